@@ -1,0 +1,347 @@
+"""ctypes view of the plain C oracle of the LCT codec (``lct_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package; the product
+path never does.  Arrays are numpy arrays; every call is serial C.
+
+Page citations are in ``lct_oracle.h``: "LCT: Losslessly Compressed Tensors
+with GPU friendly execution for Training" (abstract) and the explainer "LCT
+paper - Lossless Huffman coding of BF16 training tensors" (paragraphs on the
+byte split and codebook, on blocks and streams, and on training traffic).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lct_oracle.c")
+_LIB = os.path.join(_HERE, "liblct_oracle.so")
+
+GAUSSIAN, LAPLACE, POWERLAW = 0, 1, 2
+OK, OVF_FULL, EINVAL, EDECODE = 0, 1, -1, -2
+NSTREAM = 256
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+            "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Codebook(C.Structure):
+    _fields_ = [("len", C.c_uint8 * 256), ("esc_len", C.c_uint8),
+                ("shift", C.c_int32), ("code", C.c_uint32 * 257)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        u64, u32, i32 = C.c_uint64, C.c_uint32, C.c_int
+        L.lcto_model_survival.restype = C.c_double
+        L.lcto_model_survival.argtypes = [i32, C.c_double, C.c_double, C.c_double]
+        L.lcto_model_pmf.argtypes = [i32, C.c_double, C.c_double, P]
+        L.lcto_weights.argtypes = [P, P]
+        L.lcto_package_merge.argtypes = [i32, P, P, i32, P]
+        L.lcto_build_escape.restype = u64
+        L.lcto_build_escape.argtypes = [i32, P, i32, i32, P, P, P]
+        L.lcto_build_base.restype = u64
+        L.lcto_build_base.argtypes = [P, P, P, P]
+        L.lcto_best_shift.argtypes = [P, C.c_uint8, P, C.c_size_t]
+        L.lcto_shift_cost.restype = u64
+        L.lcto_shift_cost.argtypes = [P, C.c_uint8, P, C.c_size_t, i32]
+        L.lcto_canonical.argtypes = [P, P]
+        L.lcto_codebook_build.argtypes = [i32, C.c_double, C.c_double, P, u64, P]
+        L.lcto_codebook_from_base.argtypes = [P, C.c_uint8, i32, P]
+        L.lcto_exponent.restype = C.c_uint8
+        L.lcto_exponent.argtypes = [C.c_uint16]
+        L.lcto_signfrac.restype = C.c_uint8
+        L.lcto_signfrac.argtypes = [C.c_uint16]
+        L.lcto_join.restype = C.c_uint16
+        L.lcto_join.argtypes = [C.c_uint8, C.c_uint8]
+        L.lcto_encode_block.argtypes = [P, P, u32, u32, P, P, P, P, P]
+        L.lcto_decode_block.argtypes = [P, P, P, P, P, u32, u32, P]
+        L.lcto_encode.argtypes = [P, P, u64, u32, u32, P, P, P, P, P, u64]
+        L.lcto_decode.argtypes = [P, P, P, P, P, P, u64, u32, u32, P]
+        L.lcto_fmaf.restype = C.c_float
+        L.lcto_fmaf.argtypes = [C.c_float, C.c_float, C.c_float]
+        L.lcto_rne_bf16.restype = C.c_uint16
+        L.lcto_rne_bf16.argtypes = [C.c_float]
+        L.lcto_sgd_elem.restype = C.c_uint16
+        L.lcto_sgd_elem.argtypes = [C.c_uint16, C.c_uint16, C.c_float]
+        L.lcto_sgd.argtypes = ([P, P, P, P, P, P] + [P, P, P, P, P, P] +
+                               [C.c_float, u64, u32, u32, P, P, P, P, P, u64])
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.c_void_p)
+
+
+# ---------------------------------------------------------------- codebook
+
+@dataclass
+class Codebook:
+    """Final code: len[e] (0 = escaped), esc_len, shift, canonical codes."""
+    len: np.ndarray      # uint8[256]
+    esc_len: int
+    shift: int
+    code: np.ndarray     # uint32[257], [256] = ESC
+
+    def _c(self) -> _Codebook:
+        cb = _Codebook()
+        C.memmove(cb.len, self.len.astype(np.uint8).tobytes(), 256)
+        cb.esc_len = int(self.esc_len)
+        cb.shift = int(self.shift)
+        C.memmove(cb.code, self.code.astype(np.uint32).tobytes(), 257 * 4)
+        return cb
+
+    @staticmethod
+    def _from_c(cb: _Codebook) -> "Codebook":
+        return Codebook(np.frombuffer(bytes(cb.len), np.uint8).copy(), int(cb.esc_len),
+                        int(cb.shift), np.frombuffer(bytes(cb.code), np.uint32).copy())
+
+    def cost(self, e: int) -> int:
+        return int(self.len[e]) if self.len[e] else self.esc_len + 8
+
+
+def survival(family: int, scale: float, shape: float, t: float) -> float:
+    return lib().lcto_model_survival(family, scale, shape, t)
+
+
+def model_pmf(family: int, scale: float, shape: float = 0.0) -> np.ndarray:
+    p = np.zeros(256, np.float64)
+    rc = lib().lcto_model_pmf(family, scale, shape, _p(p))
+    if rc != OK:
+        raise ValueError("bad model")
+    return p
+
+
+def weights(p: np.ndarray) -> np.ndarray:
+    w = np.zeros(256, np.uint64)
+    lib().lcto_weights(_p(np.ascontiguousarray(p, np.float64)), _p(w))
+    return w
+
+
+def package_merge(w, L: int, ids=None) -> np.ndarray:
+    w = np.ascontiguousarray(w, np.uint64)
+    n = len(w)
+    ids = np.arange(n, dtype=np.int32) if ids is None else np.ascontiguousarray(ids, np.int32)
+    out = np.zeros(n, np.uint8)
+    rc = lib().lcto_package_merge(n, _p(w), _p(ids), L, _p(out))
+    if rc != OK:
+        raise ValueError("package_merge: bad input")
+    return out
+
+
+def build_escape(w, L: int, lit_bits: int):
+    """Returns (len[nsym], esc_len, k, cost)."""
+    w = np.ascontiguousarray(w, np.uint64)
+    n = len(w)
+    ln = np.zeros(n, np.uint8)
+    esc = C.c_uint8(0)
+    k = C.c_int(0)
+    cost = lib().lcto_build_escape(n, _p(w), L, lit_bits, _p(ln), C.byref(esc), C.byref(k))
+    if cost == 2**64 - 1:
+        raise ValueError("build_escape: bad input")
+    return ln, int(esc.value), int(k.value), int(cost)
+
+
+def build_base(w):
+    return build_escape(w, 8, 8)
+
+
+def best_shift(len_base, esc_len: int, exps) -> int:
+    e = np.ascontiguousarray(exps, np.uint8)
+    return lib().lcto_best_shift(_p(np.ascontiguousarray(len_base, np.uint8)), esc_len, _p(e), len(e))
+
+
+def shift_cost(len_base, esc_len: int, exps, k: int) -> int:
+    e = np.ascontiguousarray(exps, np.uint8)
+    return int(lib().lcto_shift_cost(_p(np.ascontiguousarray(len_base, np.uint8)), esc_len,
+                                     _p(e), len(e), k))
+
+
+def canonical(len257) -> np.ndarray:
+    code = np.zeros(257, np.uint32)
+    lib().lcto_canonical(_p(np.ascontiguousarray(len257, np.uint8)), _p(code))
+    return code
+
+
+def codebook_from_base(len_base, esc_len: int, shift: int) -> Codebook:
+    cb = _Codebook()
+    lib().lcto_codebook_from_base(_p(np.ascontiguousarray(len_base, np.uint8)), esc_len, shift,
+                                  C.byref(cb))
+    return Codebook._from_c(cb)
+
+
+def codebook_build(family: int, scale: float, shape: float, x: np.ndarray) -> Codebook:
+    x = np.ascontiguousarray(x, np.uint16)
+    cb = _Codebook()
+    rc = lib().lcto_codebook_build(family, scale, shape, _p(x), x.size, C.byref(cb))
+    if rc != OK:
+        raise ValueError("codebook_build: bad model")
+    return Codebook._from_c(cb)
+
+
+# ---------------------------------------------------------------- format
+
+def exponent(v: int) -> int:
+    return lib().lcto_exponent(v)
+
+
+def signfrac(v: int) -> int:
+    return lib().lcto_signfrac(v)
+
+
+def join(sf: int, e: int) -> int:
+    return lib().lcto_join(sf, e)
+
+
+@dataclass
+class Compressed:
+    n: int
+    block_elems: int
+    cap_words: int
+    sf: np.ndarray       # uint8[n]
+    pay: np.ndarray      # uint32[nblk*cap_words*256]
+    cnt: np.ndarray      # uint16[nblk*256]
+    obase: np.ndarray    # uint64[nblk+1]
+    ovf: np.ndarray      # uint8[ovf_cap]
+    status: int = 0
+
+    @property
+    def nblk(self) -> int:
+        return -(-self.n // self.block_elems)
+
+    @property
+    def spilled(self) -> int:
+        return int(self.obase[-1])
+
+    def nbytes(self) -> int:
+        """Compressed size: sf + payload + markers + spilled bytes."""
+        return (self.n + self.pay.nbytes + self.cnt.nbytes + self.obase.nbytes + self.spilled)
+
+    def ratio(self) -> float:
+        return 2.0 * self.n / self.nbytes() if self.n else 0.0
+
+
+def _alloc(n: int, block_elems: int, cap_words: int, ovf_cap: int) -> Compressed:
+    nblk = -(-n // block_elems)
+    return Compressed(n, block_elems, cap_words, np.zeros(n, np.uint8),
+                      np.zeros(nblk * cap_words * NSTREAM, np.uint32),
+                      np.zeros(nblk * NSTREAM, np.uint16), np.zeros(nblk + 1, np.uint64),
+                      np.zeros(max(ovf_cap, 1), np.uint8))
+
+
+def encode(cb: Codebook, x: np.ndarray, block_elems: int, cap_words: int,
+           ovf_cap: int | None = None) -> Compressed:
+    x = np.ascontiguousarray(x, np.uint16).reshape(-1)
+    n = x.size
+    ovf_cap = n if ovf_cap is None else ovf_cap
+    t = _alloc(n, block_elems, cap_words, ovf_cap)
+    c = cb._c()
+    rc = lib().lcto_encode(C.byref(c), _p(x), n, block_elems, cap_words, _p(t.sf), _p(t.pay),
+                           _p(t.cnt), _p(t.obase), _p(t.ovf), ovf_cap)
+    if rc < 0:
+        raise ValueError("encode: bad arguments")
+    t.status = rc
+    return t
+
+
+def decode(cb: Codebook, t: Compressed) -> np.ndarray:
+    y = np.zeros(t.n, np.uint16)
+    c = cb._c()
+    rc = lib().lcto_decode(C.byref(c), _p(t.sf), _p(t.pay), _p(t.cnt), _p(t.obase), _p(t.ovf),
+                           t.n, t.block_elems, t.cap_words, _p(y))
+    if rc != OK:
+        raise ValueError("decode: stream error %d" % rc)
+    return y
+
+
+def encode_block(cb: Codebook, x: np.ndarray, cap_words: int):
+    """One block: returns (sf, pay, cnt, spill bytes)."""
+    x = np.ascontiguousarray(x, np.uint16).reshape(-1)
+    nb = x.size
+    sf = np.zeros(nb, np.uint8)
+    pay = np.zeros(cap_words * NSTREAM, np.uint32)
+    cnt = np.zeros(NSTREAM, np.uint16)
+    spill = np.zeros(max(nb, 1), np.uint8)
+    ns = C.c_uint32(0)
+    c = cb._c()
+    lib().lcto_encode_block(C.byref(c), _p(x), nb, cap_words, _p(sf), _p(pay), _p(cnt),
+                            _p(spill), C.byref(ns))
+    return sf, pay, cnt, spill[:ns.value].copy()
+
+
+def decode_block(cb: Codebook, sf, pay, cnt, spill, cap_words: int) -> np.ndarray:
+    sf = np.ascontiguousarray(sf, np.uint8)
+    nb = sf.size
+    y = np.zeros(nb, np.uint16)
+    spill = np.ascontiguousarray(spill, np.uint8)
+    if spill.size == 0:
+        spill = np.zeros(1, np.uint8)
+    c = cb._c()
+    rc = lib().lcto_decode_block(C.byref(c), _p(sf), _p(np.ascontiguousarray(pay, np.uint32)),
+                                 _p(np.ascontiguousarray(cnt, np.uint16)), _p(spill), nb,
+                                 cap_words, _p(y))
+    if rc != OK:
+        raise ValueError("decode_block: stream error %d" % rc)
+    return y
+
+
+# ---------------------------------------------------------------- SGD
+
+def fmaf(a: float, b: float, c: float) -> float:
+    return lib().lcto_fmaf(a, b, c)
+
+
+def rne_bf16(r: float) -> int:
+    return lib().lcto_rne_bf16(r)
+
+
+def sgd_elem(w: int, m: int, eta: float) -> int:
+    return lib().lcto_sgd_elem(w, m, eta)
+
+
+def sgd_dense(w: np.ndarray, m: np.ndarray, eta: float) -> np.ndarray:
+    """Element-wise update on raw BF16 bit patterns (serial C, via the block path)."""
+    L = lib()
+    w = np.ascontiguousarray(w, np.uint16).reshape(-1)
+    m = np.ascontiguousarray(m, np.uint16).reshape(-1)
+    return np.fromiter((L.lcto_sgd_elem(int(a), int(b), eta) for a, b in zip(w, m)),
+                       np.uint16, count=w.size)
+
+
+def sgd(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, eta: float,
+        ovf_cap: int | None = None) -> Compressed:
+    assert (w.n, w.block_elems, w.cap_words) == (m.n, m.block_elems, m.cap_words)
+    ovf_cap = w.n if ovf_cap is None else ovf_cap
+    o = _alloc(w.n, w.block_elems, w.cap_words, ovf_cap)
+    a, b = cw._c(), cm._c()
+    rc = lib().lcto_sgd(C.byref(a), _p(w.sf), _p(w.pay), _p(w.cnt), _p(w.obase), _p(w.ovf),
+                        C.byref(b), _p(m.sf), _p(m.pay), _p(m.cnt), _p(m.obase), _p(m.ovf),
+                        eta, w.n, w.block_elems, w.cap_words, _p(o.sf), _p(o.pay), _p(o.cnt),
+                        _p(o.obase), _p(o.ovf), ovf_cap)
+    if rc < 0:
+        raise ValueError("sgd: error %d" % rc)
+    o.status = rc
+    return o
