@@ -1,0 +1,210 @@
+/*
+ * lct.h -- C ABI of the LCT lossless BF16 exponent codec for MI355X (gfx950).
+ *
+ * A BF16 tensor is stored as a raw sign-fraction byte per element plus its
+ * exponents, Huffman-coded with a precomputed, length-limited codebook (codes
+ * of at most 8 bits; rare exponents take one escape code followed by the 8-bit
+ * field).  Each block of elements is dealt round-robin into 256 streams of a
+ * fixed capacity; the exponents that do not fit spill, raw, to an overflow
+ * region whose start is recorded per block.  Sources:
+ *   "LCT: Losslessly Compressed Tensors with GPU friendly execution for
+ *    Training" (scholarbro.com), abstract;
+ *   "LCT paper - Lossless Huffman coding of BF16 training tensors"
+ *    (learnaivisually.com): the paragraph on bits (byte split, 8-bit cap,
+ *    escape, precomputed codebook and sampled shift), the paragraph on blocks
+ *    and streams (65,536 / 32,768 elements, 256 streams, fixed capacity,
+ *    overflow and its marker), and the paragraph on training traffic (the
+ *    fused SGD update W_{t+1} = W_t - eta * M_t).
+ *
+ * Conventions (common to every call):
+ *   - Every function returns lct_status (0 = LCT_OK) and never throws.
+ *   - Pointers named d_* and every pointer inside lct_tensor are DEVICE
+ *     pointers on the current HIP device; every other pointer is host memory.
+ *   - The caller allocates and frees every device buffer, sized by lct_sizes().
+ *     The library allocates no device memory of its own, except one 8 KiB
+ *     static array per device used by lct_codebook_build() for its sample.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     lct_encode, lct_decode and lct_sgd_step only enqueue work on it and
+ *     return at once; lct_codebook_build synchronises it.
+ *   - Errors found on the host (null pointer, bad size, misalignment, illegal
+ *     aliasing, wrong device) are returned before anything is enqueued.
+ *     The only data-dependent failure is a too-small overflow region: it is
+ *     reported through the device status word (LCT_ST_* bits), never by a
+ *     fault.  n == 0 is a no-op that returns LCT_OK.
+ *   - Thread-safe: no global state beyond the codebook-build sample array,
+ *     which is guarded by a lock.
+ */
+#ifndef LCT_H
+#define LCT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LCT_OK = 0,
+    LCT_EINVAL = -1,  /* null pointer, bad layout, bad model, size mismatch */
+    LCT_EALIGN = -2,  /* device pointer not aligned as documented */
+    LCT_EALIAS = -3,  /* output overlaps an input it must not overlap */
+    LCT_EHIP = -4,    /* a HIP runtime call failed (message via lct_last_hip_error) */
+    LCT_EARCH = -5    /* current device is not gfx950 */
+} lct_status;
+
+/* Device status word bits, OR-ed in by the kernels (the word is cleared at the
+ * start of every lct_encode / lct_sgd_step). */
+#define LCT_ST_OVF_FULL 0x1u   /* total spill > ovf_cap: the overflow region is incomplete;
+                                  obase[nblk] still holds the size needed */
+#define LCT_ST_LOOKBACK 0x2u   /* overflow-offset scan gave up waiting (never expected) */
+
+/* Codebook model picked by the user (explainer, paragraph on bits: a
+ * Gaussian, Laplace or power-law distribution).  scale = sigma (Gaussian),
+ * b (Laplace) or the t scale (power law = Student-t, shape = degrees of
+ * freedom). */
+typedef enum { LCT_GAUSSIAN = 0, LCT_LAPLACE = 1, LCT_POWERLAW = 2 } lct_family;
+typedef struct {
+    int32_t family;   /* lct_family */
+    double scale;
+    double shape;
+} lct_model;
+
+/* Block layouts (explainer, paragraph on blocks and streams: 65,536-element
+ * blocks in CLEAN, 32,768 in MEDIUM and HIGH).  cap_words is each stream's
+ * capacity in 32-bit words: CLEAN 25 (16 / (8 + 800/256) = 1.4382x, the
+ * bound printed for CLEAN), MEDIUM 12 (8 + 3 bits per value, 16/11), HIGH 11.
+ * Any block_elems that is a multiple of 2048 in [2048, 65536] and any
+ * cap_words in [1, 64] is accepted. */
+typedef enum { LCT_CLEAN = 0, LCT_MEDIUM = 1, LCT_HIGH = 2 } lct_mode;
+typedef struct {
+    uint32_t block_elems;
+    uint32_t cap_words;
+} lct_layout;
+
+/* Host-side codebook (plain old data, about 4 KiB).  len[e] is the code
+ * length of exponent field e, 0 when e is escaped (then it costs esc_len + 8
+ * bits: the escape code, then the field's 8 bits, least significant first).
+ * code[] holds canonical code values (ordered by length, then field; the
+ * escape symbol has id 256); codes enter a stream most significant bit first.
+ * The remaining members are lookup tables derived from len/esc_len by the
+ * library: treat them as opaque. */
+typedef struct {
+    uint8_t  len[256];
+    uint8_t  esc_len;
+    uint8_t  max_len;
+    int16_t  shift;        /* exponent offset applied to the base code */
+    uint32_t kept;         /* number of exponent fields with a code */
+    lct_model model;
+    uint32_t code[257];
+    uint32_t enc_bits[256];   /* stream bits of each field, LSB-first (code reversed, literal) */
+    uint8_t  enc_len[256];    /* bits each field costs */
+    uint16_t dec[256];        /* 8-bit peek -> field | bits << 8 | escape << 13 | invalid << 14 */
+} lct_codebook;
+
+/* A compressed tensor: every pointer is a caller-owned device buffer.
+ *   n          number of BF16 elements
+ *   layout     block_elems, cap_words;  nblk = ceil(n / block_elems)
+ *   sf         uint8[n]      sign-fraction bytes in element order (16-byte aligned)
+ *   pay        uint32[nblk * cap_words * 256]  word w of stream s of block b at
+ *              (b * cap_words + w) * 256 + s; stream bit k is bit (k mod 32) of
+ *              its word k / 32; unused bits are 0 (16-byte aligned)
+ *   cnt        uint16[nblk * 256]  coded prefix length of each stream; the rest
+ *              of the stream's elements are in the overflow region (4-byte aligned)
+ *   obase      uint64[nblk + 1]  where block b's spilled bytes start in ovf;
+ *              obase[nblk] = total spilled bytes (8-byte aligned)
+ *   ovf        uint8[ovf_cap]  spilled exponent fields, raw, in (block,
+ *              stream, position) order
+ *   status     uint32[1]  LCT_ST_* bits
+ *   scratch    lct_sizes().scratch bytes of working memory (256-byte aligned);
+ *              only lct_encode and lct_sgd_step use it.  It may be shared by
+ *              calls that do not overlap in time.
+ * Element r of block b (r < block_elems) is position r / 256 of stream r % 256. */
+typedef struct {
+    uint64_t n;
+    lct_layout layout;
+    uint8_t  *sf;
+    uint32_t *pay;
+    uint16_t *cnt;
+    uint64_t *obase;
+    uint8_t  *ovf;
+    uint64_t ovf_cap;
+    uint32_t *status;
+    void     *scratch;
+} lct_tensor;
+
+typedef struct {
+    uint64_t nblk;
+    uint64_t sf, pay, cnt, obase;   /* bytes */
+    uint64_t scratch;               /* bytes, for the given ovf_cap */
+    uint64_t fixed;                 /* sf + pay + cnt + obase: compressed size before spills */
+} lct_sizes_t;
+
+/* Layout of a mode.  Errors: LCT_EINVAL for an unknown mode or null out. */
+lct_status lct_layout_init(int32_t mode, lct_layout *out);
+
+/* Buffer sizes of an n-element tensor.  Errors: LCT_EINVAL for a layout
+ * outside the accepted range or a null pointer. */
+lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct_sizes_t *out);
+
+/* Codebook build (explainer, paragraph on bits: the codebook is
+ * precomputed from the distribution the user picks, with a small shift
+ * sampled from up to 4096 elements to follow the tensor's scale).
+ * Steps: model probability of every exponent field -> integer weights
+ * floor(p * 2^40 + 0.5) -> escape set (the k heaviest fields kept, k chosen
+ * for the least expected bits) with length-limited Huffman (package-merge,
+ * 8-bit cap) -> integer shift k minimising the coded bits of the sample
+ * d_x[floor(i * n / m)], m = min(n, 4096) (ties: smallest |k|, then the smaller
+ * k) -> final lengths len[e] = base[e - k] -> canonical codes -> lookup tables.
+ * d_x: device BF16 bit patterns, n elements (may be NULL when n == 0: shift 0).
+ * Synchronises `stream`.  Errors: LCT_EINVAL (bad model, null out),
+ * LCT_EARCH, LCT_EHIP. */
+lct_status lct_codebook_build(const lct_model *model, const uint16_t *d_x, uint64_t n,
+                              void *stream, lct_codebook *out);
+
+/* Codebook from given base lengths and shift (no model, no sampling): the
+ * final lengths are len_base[e - shift].  len_base[] must be a prefix code
+ * together with esc_len (Kraft sum <= 1, lengths <= 8, esc_len in 1..8).
+ * Errors: LCT_EINVAL. */
+lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
+                                     lct_codebook *out);
+
+/* Encode (explainer, paragraphs on bits and on blocks and streams).
+ * d_x: device BF16 bit patterns, out->n elements, 16-byte aligned.  Writes
+ * every buffer of *out (all of sf, pay, cnt, obase, status; ovf below ovf_cap).
+ * If the spill exceeds out->ovf_cap, LCT_ST_OVF_FULL is set in *out->status
+ * and obase[nblk] holds the capacity needed: allocate more and encode again.
+ * Safe bound: ovf_cap = n.  Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS (d_x
+ * overlapping an output), LCT_EARCH, LCT_EHIP. */
+lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_tensor *out,
+                      void *stream);
+
+/* Decode: the inverse of lct_encode (explainer, first paragraph: every
+ * value decodes exactly).  d_y: device uint16[in->n], 16-byte aligned, must
+ * not overlap *in.  Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS, LCT_EARCH,
+ * LCT_EHIP. */
+lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_y, void *stream);
+
+/* Fused SGD step (explainer, paragraph on training traffic: read the
+ * compressed inputs, compute, write the new exponent and sign-fraction bytes
+ * in one pass).  W' = W - eta * M, element by element as
+ * rne_bf16(fmaf(-eta, f32(m), f32(w))) with a NaN result written as 0x7FC0;
+ * W' is encoded with cw (the codebook of W).  w_in, m, w_out share n and
+ * layout.  w_out's sf, pay, cnt and obase may be w_in's own (in-place update);
+ * w_out's ovf, status and scratch must not overlap any buffer of w_in or m, and
+ * m must not overlap w_out.  If LCT_ST_OVF_FULL is set after an in-place
+ * update, W is lost: callers that cannot bound the spill update out of place.
+ * Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS, LCT_EARCH, LCT_EHIP. */
+lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in,
+                        const lct_codebook *cm, const lct_tensor *m,
+                        float eta, const lct_tensor *w_out, void *stream);
+
+/* Message for a status code (static string). */
+const char *lct_strerror(lct_status st);
+/* Text of the last HIP error seen on this thread (static per thread). */
+const char *lct_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCT_H */

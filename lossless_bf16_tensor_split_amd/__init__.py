@@ -1,0 +1,249 @@
+"""Python binding of the LCT codec's C ABI (``include/lct.h``, ``liblct.so``).
+
+Argument marshalling only: every step of the codec runs in the HIP library.
+torch provides device memory (``torch.empty`` on the GPU) and the stream
+(``torch.cuda.current_stream()``); nothing else of torch is used.  Importing
+the package needs the built library; there is no fallback.
+
+Functions keep the C names:
+    lct_layout_init(mode) -> Layout
+    lct_sizes(n, layout, ovf_cap) -> Sizes
+    lct_codebook_build(model, x) -> Codebook
+    lct_codebook_from_lengths(len_base, esc_len, shift) -> Codebook
+    lct_encode(cb, x, out)            (out: LctTensor from alloc_tensor)
+    lct_decode(cb, t, y)
+    lct_sgd_step(cw, w_in, cm, m, eta, w_out)
+plus ``alloc_tensor`` and the convenience wrappers ``encode`` / ``decode`` /
+``sgd_step`` that allocate their outputs.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblct.so")
+
+GAUSSIAN, LAPLACE, POWERLAW = 0, 1, 2
+CLEAN, MEDIUM, HIGH = 0, 1, 2
+ST_OVF_FULL, ST_LOOKBACK = 0x1, 0x2
+OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH = 0, -1, -2, -3, -4, -5
+
+EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_from_lengths",
+            "lct_encode", "lct_decode", "lct_sgd_step", "lct_strerror", "lct_last_hip_error"]
+
+
+class Model(C.Structure):
+    _fields_ = [("family", C.c_int32), ("scale", C.c_double), ("shape", C.c_double)]
+
+
+class Layout(C.Structure):
+    _fields_ = [("block_elems", C.c_uint32), ("cap_words", C.c_uint32)]
+
+
+class Codebook(C.Structure):
+    _fields_ = [("len", C.c_uint8 * 256), ("esc_len", C.c_uint8), ("max_len", C.c_uint8),
+                ("shift", C.c_int16), ("kept", C.c_uint32), ("model", Model),
+                ("code", C.c_uint32 * 257), ("enc_bits", C.c_uint32 * 256),
+                ("enc_len", C.c_uint8 * 256), ("dec", C.c_uint16 * 256)]
+
+
+class _Tensor(C.Structure):
+    _fields_ = [("n", C.c_uint64), ("layout", Layout), ("sf", C.c_void_p), ("pay", C.c_void_p),
+                ("cnt", C.c_void_p), ("obase", C.c_void_p), ("ovf", C.c_void_p),
+                ("ovf_cap", C.c_uint64), ("status", C.c_void_p), ("scratch", C.c_void_p)]
+
+
+class Sizes(C.Structure):
+    _fields_ = [("nblk", C.c_uint64), ("sf", C.c_uint64), ("pay", C.c_uint64),
+                ("cnt", C.c_uint64), ("obase", C.c_uint64), ("scratch", C.c_uint64),
+                ("fixed", C.c_uint64)]
+
+
+class LctError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblct.so is not built: run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no fallback path")
+    L = C.CDLL(LIB_PATH)
+    P, u64, i32 = C.c_void_p, C.c_uint64, C.c_int32
+    L.lct_layout_init.argtypes = [i32, C.POINTER(Layout)]
+    L.lct_sizes.argtypes = [u64, C.POINTER(Layout), u64, C.POINTER(Sizes)]
+    L.lct_codebook_build.argtypes = [C.POINTER(Model), P, u64, P, C.POINTER(Codebook)]
+    L.lct_codebook_from_lengths.argtypes = [P, C.c_uint8, i32, C.POINTER(Codebook)]
+    L.lct_encode.argtypes = [C.POINTER(Codebook), P, C.POINTER(_Tensor), P]
+    L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
+    L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
+                               C.POINTER(_Tensor), C.c_float, C.POINTER(_Tensor), P]
+    L.lct_strerror.restype = C.c_char_p
+    L.lct_strerror.argtypes = [i32]
+    L.lct_last_hip_error.restype = C.c_char_p
+    for name in EXPORTED:
+        if name not in ("lct_strerror", "lct_last_hip_error"):
+            getattr(L, name).restype = i32
+    return L
+
+
+lib = _load()
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        msg = lib.lct_strerror(rc).decode()
+        if rc == EHIP:
+            msg += " (" + lib.lct_last_hip_error().decode() + ")"
+        raise LctError("%s failed: %s [%d]" % (what, msg, rc))
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ layout, sizes
+
+def lct_layout_init(mode: int) -> Layout:
+    out = Layout()
+    _check(lib.lct_layout_init(mode, C.byref(out)), "lct_layout_init")
+    return out
+
+
+def layout(block_elems: int, cap_words: int) -> Layout:
+    return Layout(block_elems, cap_words)
+
+
+def lct_sizes(n: int, lay: Layout, ovf_cap: int = 0) -> Sizes:
+    out = Sizes()
+    _check(lib.lct_sizes(n, C.byref(lay), ovf_cap, C.byref(out)), "lct_sizes")
+    return out
+
+
+# ------------------------------------------------------------------ codebook
+
+def lct_codebook_build(model: Model, x: torch.Tensor | None, stream=None) -> Codebook:
+    """Codebook for model, shift sampled from x (BF16 or 16-bit tensor on the GPU)."""
+    out = Codebook()
+    n = 0 if x is None else x.numel()
+    if x is not None and not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    st = _stream(stream) if n else None     # no sample: nothing runs on the device
+    _check(lib.lct_codebook_build(C.byref(model), _ptr(x), n, st, C.byref(out)),
+           "lct_codebook_build")
+    return out
+
+
+def lct_codebook_from_lengths(len_base, esc_len: int, shift: int = 0) -> Codebook:
+    arr = (C.c_uint8 * 256)(*[int(v) for v in len_base])
+    out = Codebook()
+    _check(lib.lct_codebook_from_lengths(arr, esc_len, shift, C.byref(out)),
+           "lct_codebook_from_lengths")
+    return out
+
+
+# ------------------------------------------------------------------ compressed tensors
+
+class LctTensor:
+    """Device buffers of one compressed tensor (torch-owned memory)."""
+
+    def __init__(self, n: int, lay: Layout, ovf_cap: int, device="cuda", scratch=None):
+        sz = lct_sizes(n, lay, ovf_cap)
+        dev = torch.device(device)
+        u8 = torch.uint8
+        self.n, self.layout, self.ovf_cap, self.sizes = n, Layout(lay.block_elems, lay.cap_words), ovf_cap, sz
+        self.sf = torch.empty(max(sz.sf, 16), dtype=u8, device=dev)
+        self.pay = torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev)
+        self.obase = torch.empty(sz.obase // 8, dtype=torch.int64, device=dev)
+        self.ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
+        self.status = torch.zeros(4, dtype=torch.int32, device=dev)
+        if scratch is None:
+            scratch = torch.empty(sz.scratch, dtype=u8, device=dev)
+        elif scratch.numel() < sz.scratch:
+            raise ValueError("scratch too small: %d < %d" % (scratch.numel(), sz.scratch))
+        self.scratch = scratch
+
+    def c(self) -> _Tensor:
+        return _Tensor(self.n, self.layout, _ptr(self.sf), _ptr(self.pay), _ptr(self.cnt),
+                       _ptr(self.obase), _ptr(self.ovf), self.ovf_cap, _ptr(self.status),
+                       _ptr(self.scratch))
+
+    # host views (synchronise the current stream)
+    def status_word(self) -> int:
+        return int(self.status[0].item()) & 0xFFFFFFFF
+
+    def spilled(self) -> int:
+        return int(self.obase[-1].item())
+
+    def nbytes(self) -> int:
+        return int(self.sizes.fixed) + self.spilled()
+
+    def ratio(self) -> float:
+        return 2.0 * self.n / self.nbytes() if self.n else 0.0
+
+
+def alloc_tensor(n: int, lay: Layout, ovf_cap: int | None = None, device="cuda",
+                 scratch=None) -> LctTensor:
+    return LctTensor(n, lay, n if ovf_cap is None else ovf_cap, device, scratch)
+
+
+def _bits16(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("expected BF16 (or 16-bit pattern) tensor, got %s" % x.dtype)
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return x
+
+
+def lct_encode(cb: Codebook, x: torch.Tensor, out: LctTensor, stream=None) -> None:
+    _bits16(x)
+    if x.numel() != out.n:
+        raise ValueError("x has %d elements, output tensor %d" % (x.numel(), out.n))
+    t = out.c()
+    _check(lib.lct_encode(C.byref(cb), _ptr(x), C.byref(t), _stream(stream)), "lct_encode")
+
+
+def lct_decode(cb: Codebook, t: LctTensor, y: torch.Tensor, stream=None) -> None:
+    _bits16(y)
+    if y.numel() != t.n:
+        raise ValueError("y has %d elements, tensor %d" % (y.numel(), t.n))
+    ct = t.c()
+    _check(lib.lct_decode(C.byref(cb), C.byref(ct), _ptr(y), _stream(stream)), "lct_decode")
+
+
+def lct_sgd_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta: float,
+                 w_out: LctTensor, stream=None) -> None:
+    a, b, o = w_in.c(), m.c(), w_out.c()
+    _check(lib.lct_sgd_step(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta, C.byref(o),
+                            _stream(stream)), "lct_sgd_step")
+
+
+# ------------------------------------------------------------------ conveniences
+
+def encode(cb: Codebook, x: torch.Tensor, lay: Layout, ovf_cap: int | None = None,
+           scratch=None) -> LctTensor:
+    out = alloc_tensor(x.numel(), lay, ovf_cap, x.device, scratch)
+    lct_encode(cb, x, out)
+    return out
+
+
+def decode(cb: Codebook, t: LctTensor) -> torch.Tensor:
+    y = torch.empty(max(t.n, 1), dtype=torch.bfloat16, device=t.sf.device)[:t.n]
+    lct_decode(cb, t, y)
+    return y
+
+
+def sgd_step(cw: Codebook, w: LctTensor, cm: Codebook, m: LctTensor, eta: float,
+             out: LctTensor | None = None, ovf_cap: int | None = None) -> LctTensor:
+    if out is None:
+        out = alloc_tensor(w.n, w.layout, ovf_cap, w.sf.device)
+    lct_sgd_step(cw, w, cm, m, eta, out)
+    return out

@@ -1,0 +1,313 @@
+// api.cpp -- the extern "C" entry points declared in include/lct.h:
+// argument checks, size accounting and kernel launches.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "lct_internal.h"
+
+namespace lct {
+size_t encode_lds(uint32_t cap);
+size_t decode_lds(uint32_t cap);
+size_t sgd_lds(uint32_t cap);
+}  // namespace lct
+
+namespace {
+
+using namespace lct;
+
+thread_local char g_hip_msg[256] = "";
+
+lct_status hip_fail(int err, const char *what) {
+    snprintf(g_hip_msg, sizeof g_hip_msg, "%s: %s", what, hipGetErrorString((hipError_t)err));
+    return LCT_EHIP;
+}
+
+// gfx950 check, cached per device.
+lct_status check_arch() {
+    static std::mutex mu;
+    static int known[64] = {0};   // 0 unknown, 1 ok, -1 other arch
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return LCT_EARCH;
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return known[dev] == 1 ? LCT_OK : LCT_EARCH;
+}
+
+bool layout_ok(const lct_layout &l) {
+    return l.block_elems >= kMinBlock && l.block_elems <= kMaxBlock &&
+           l.block_elems % kMinBlock == 0 && l.cap_words >= 1 && l.cap_words <= kMaxCapWords;
+}
+
+uint64_t nblocks(uint64_t n, const lct_layout &l) { return (n + l.block_elems - 1) / l.block_elems; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Range rng(const void *p, uint64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+struct Parts {
+    Range sf, pay, cnt, obase, ovf, status, scratch;
+};
+
+Parts parts(const lct_tensor &t) {
+    const uint64_t nb = nblocks(t.n, t.layout);
+    Parts p;
+    p.sf = rng(t.sf, t.n);
+    p.pay = rng(t.pay, nb * t.layout.cap_words * kStreams * 4);
+    p.cnt = rng(t.cnt, nb * kStreams * 2);
+    p.obase = rng(t.obase, (nb + 1) * 8);
+    p.ovf = rng(t.ovf, t.ovf_cap);
+    p.status = rng(t.status, 4);
+    p.scratch = rng(t.scratch, scr_stage_offset(nb) + t.ovf_cap);
+    return p;
+}
+
+// Pointers a call reads or writes must be non-null and aligned.
+lct_status check_tensor(const lct_tensor *t, bool writes) {
+    if (!t || !layout_ok(t->layout)) return LCT_EINVAL;
+    if (!t->sf || !t->pay || !t->cnt || !t->obase) return LCT_EINVAL;
+    if (t->ovf_cap && !t->ovf) return LCT_EINVAL;
+    if (!aligned(t->sf, 16) || !aligned(t->pay, 16) || !aligned(t->cnt, 4) || !aligned(t->obase, 8))
+        return LCT_EALIGN;
+    if (writes) {
+        if (!t->status || !t->scratch) return LCT_EINVAL;
+        if (!aligned(t->status, 4) || !aligned(t->scratch, 256)) return LCT_EALIGN;
+        // the output's own parts must be disjoint
+        const Parts p = parts(*t);
+        const Range all[] = {p.sf, p.pay, p.cnt, p.obase, p.ovf, p.status, p.scratch};
+        for (int i = 0; i < 7; ++i)
+            for (int j = i + 1; j < 7; ++j)
+                if (overlap(all[i], all[j])) return LCT_EALIAS;
+    }
+    return LCT_OK;
+}
+
+bool overlaps_any(Range r, const Parts &p, bool with_writable = true) {
+    const Range all[] = {p.sf, p.pay, p.cnt, p.obase, p.ovf};
+    for (const Range &a : all)
+        if (overlap(r, a)) return true;
+    if (with_writable && (overlap(r, p.status) || overlap(r, p.scratch))) return true;
+    return false;
+}
+
+std::mutex g_sample_mu;
+
+}  // namespace
+
+extern "C" {
+
+lct_status lct_layout_init(int32_t mode, lct_layout *out) {
+    if (!out) return LCT_EINVAL;
+    switch (mode) {
+    case LCT_CLEAN: *out = {65536, 25}; return LCT_OK;
+    case LCT_MEDIUM: *out = {32768, 12}; return LCT_OK;
+    case LCT_HIGH: *out = {32768, 11}; return LCT_OK;
+    }
+    return LCT_EINVAL;
+}
+
+lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct_sizes_t *out) {
+    if (!layout || !out || !layout_ok(*layout)) return LCT_EINVAL;
+    const uint64_t nb = nblocks(n, *layout);
+    out->nblk = nb;
+    out->sf = n;
+    out->pay = nb * layout->cap_words * kStreams * 4;
+    out->cnt = nb * kStreams * 2;
+    out->obase = (nb + 1) * 8;
+    out->scratch = scr_stage_offset(nb) + ovf_cap;
+    out->fixed = out->sf + out->pay + out->cnt + out->obase;
+    return LCT_OK;
+}
+
+lct_status lct_codebook_build(const lct_model *model, const uint16_t *d_x, uint64_t n, void *stream,
+                              lct_codebook *out) {
+    if (!model || !out || (n > 0 && !d_x)) return LCT_EINVAL;
+    const uint32_t m = (uint32_t)std::min<uint64_t>(n, 4096);
+    uint16_t sample[4096];
+    if (m > 0) {
+        lct_status st = check_arch();
+        if (st != LCT_OK) return st;
+        std::lock_guard<std::mutex> lock(g_sample_mu);
+        const int e = launch_gather(d_x, n, m, stream, sample);
+        if (e != hipSuccess) return hip_fail(e, "sample gather");
+    }
+    return build_codebook(*model, sample, m, out);
+}
+
+lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
+                                     lct_codebook *out) {
+    return codebook_from_lengths(len_base, esc_len, shift, out);
+}
+
+lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_tensor *out,
+                      void *stream) {
+    if (!cb || !out) return LCT_EINVAL;
+    if (out->n == 0) return LCT_OK;
+    lct_status st = check_tensor(out, true);
+    if (st != LCT_OK) return st;
+    if (!d_x) return LCT_EINVAL;
+    if (!aligned(d_x, 16)) return LCT_EALIGN;
+    if (overlaps_any(rng(d_x, out->n * 2), parts(*out))) return LCT_EALIAS;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+
+    const uint64_t nb = nblocks(out->n, out->layout);
+    if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
+    EncodeParams p;
+    memset(&p, 0, sizeof p);
+    p.x = d_x;
+    p.n = out->n;
+    p.block_elems = out->layout.block_elems;
+    p.cap_words = out->layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.sf = out->sf;
+    p.pay = out->pay;
+    p.cnt = out->cnt;
+    p.obase = out->obase;
+    p.ovf = out->ovf;
+    p.ovf_cap = out->ovf_cap;
+    p.status = out->status;
+    p.scratch = (uint8_t *)out->scratch;
+    fill_enc(*cb, &p.enc);
+    int e = launch_clear(p.scratch, nb, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_encode(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+    return LCT_OK;
+}
+
+lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_y, void *stream) {
+    if (!cb || !in) return LCT_EINVAL;
+    if (in->n == 0) return LCT_OK;
+    lct_status st = check_tensor(in, false);
+    if (st != LCT_OK) return st;
+    if (!d_y) return LCT_EINVAL;
+    if (!aligned(d_y, 16)) return LCT_EALIGN;
+    if (overlaps_any(rng(d_y, in->n * 2), parts(*in), false)) return LCT_EALIAS;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+    const uint64_t nb = nblocks(in->n, in->layout);
+    if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
+    DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.sf = in->sf;
+    p.pay = in->pay;
+    p.cnt = in->cnt;
+    p.obase = in->obase;
+    p.ovf = in->ovf;
+    p.ovf_cap = in->ovf_cap;
+    p.y = d_y;
+    p.n = in->n;
+    p.block_elems = in->layout.block_elems;
+    p.cap_words = in->layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    fill_dec(*cb, &p.dec);
+    const int e = launch_decode(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return LCT_OK;
+}
+
+lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
+                        const lct_tensor *m, float eta, const lct_tensor *w_out, void *stream) {
+    if (!cw || !cm || !w_in || !m || !w_out) return LCT_EINVAL;
+    if (w_in->n != m->n || w_in->n != w_out->n) return LCT_EINVAL;
+    if (w_in->layout.block_elems != m->layout.block_elems ||
+        w_in->layout.block_elems != w_out->layout.block_elems ||
+        w_in->layout.cap_words != m->layout.cap_words ||
+        w_in->layout.cap_words != w_out->layout.cap_words)
+        return LCT_EINVAL;
+    if (w_in->n == 0) return LCT_OK;
+    lct_status st = check_tensor(w_in, false);
+    if (st == LCT_OK) st = check_tensor(m, false);
+    if (st == LCT_OK) st = check_tensor(w_out, true);
+    if (st != LCT_OK) return st;
+    const Parts pw = parts(*w_in), pm = parts(*m), po = parts(*w_out);
+    // M is read-only and must not share memory with the output
+    const Range mr[] = {pm.sf, pm.pay, pm.cnt, pm.obase, pm.ovf};
+    for (const Range &r : mr)
+        if (overlaps_any(r, po)) return LCT_EALIAS;
+    // the output's fixed side may be W's own buffers, exactly, or disjoint from W
+    const Range wf[] = {pw.sf, pw.pay, pw.cnt, pw.obase};
+    const Range of[] = {po.sf, po.pay, po.cnt, po.obase};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j) {
+            const bool same = i == j && wf[i].lo == of[j].lo;
+            if (!same && overlap(wf[i], of[j])) return LCT_EALIAS;
+        }
+        if (overlap(pw.ovf, of[i])) return LCT_EALIAS;
+    }
+    // overflow, status and scratch of the output never overlap an input
+    const Range ow[] = {po.ovf, po.status, po.scratch};
+    for (const Range &r : ow)
+        if (overlaps_any(r, pw, false) || overlaps_any(r, pm, false)) return LCT_EALIAS;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+
+    const uint64_t nb = nblocks(w_in->n, w_in->layout);
+    if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
+    SgdParams p;
+    memset(&p, 0, sizeof p);
+    p.w_sf = w_in->sf;
+    p.w_pay = w_in->pay;
+    p.w_cnt = w_in->cnt;
+    p.w_obase = w_in->obase;
+    p.w_ovf = w_in->ovf;
+    p.w_ovf_cap = w_in->ovf_cap;
+    p.m_sf = m->sf;
+    p.m_pay = m->pay;
+    p.m_cnt = m->cnt;
+    p.m_obase = m->obase;
+    p.m_ovf = m->ovf;
+    p.m_ovf_cap = m->ovf_cap;
+    p.o_sf = w_out->sf;
+    p.o_pay = w_out->pay;
+    p.o_cnt = w_out->cnt;
+    p.o_obase = w_out->obase;
+    p.o_ovf = w_out->ovf;
+    p.ovf_cap = w_out->ovf_cap;
+    p.status = w_out->status;
+    p.scratch = (uint8_t *)w_out->scratch;
+    p.n = w_in->n;
+    p.block_elems = w_in->layout.block_elems;
+    p.cap_words = w_in->layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.neg_eta = -eta;
+    fill_enc(*cw, &p.wenc);
+    fill_dec(*cw, &p.wdec);
+    fill_dec(*cm, &p.mdec);
+    int e = launch_clear(p.scratch, nb, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_sgd(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "sgd launch");
+    return LCT_OK;
+}
+
+const char *lct_strerror(lct_status st) {
+    switch (st) {
+    case LCT_OK: return "ok";
+    case LCT_EINVAL: return "invalid argument";
+    case LCT_EALIGN: return "misaligned device pointer";
+    case LCT_EALIAS: return "illegal buffer overlap";
+    case LCT_EHIP: return "HIP runtime error";
+    case LCT_EARCH: return "device is not gfx950";
+    }
+    return "unknown status";
+}
+
+const char *lct_last_hip_error(void) { return g_hip_msg; }
+
+}  // extern "C"

@@ -1,0 +1,337 @@
+// codebook.cpp -- host construction of the exponent codebook.
+//
+// Explainer "LCT paper - Lossless Huffman coding of BF16 training tensors",
+// paragraph on bits: exponents are Huffman-coded with codes of at most 8 bits;
+// rare exponents share one escape code followed by the 8-bit field; the
+// codebook is precomputed from a Gaussian, Laplace or power-law model the user
+// picks, plus a small shift sampled from up to 4096 elements.  The LCT
+// abstract names the adaptation to magnitude shifts.
+//
+// Readings taken where the passage is silent:
+//   - weights are floor(p * 2^40 + 0.5) of the model probability of each
+//     8-bit exponent field (field e in 1..254 covers |x| in [2^(e-127),
+//     2^(e-126)), field 0 zero and subnormals, field 255 nothing);
+//   - "rare" = every field but the k heaviest, k chosen for the least
+//     expected bits (an escaped field costs esc_len + 8);
+//   - the 8-bit cap is met by an optimal length-limited code (package-merge),
+//     leaves ordered by (weight, id), a leaf before a package of equal weight;
+//   - the shift is the integer exponent offset k that minimises the coded
+//     bits of the sample under the base code (ties: smallest |k|, then the
+//     smaller k);
+//   - canonical code values follow DEFLATE's convention (RFC 1951, 3.2.2).
+#include <math.h>
+#include <string.h>
+
+// The model weights must not depend on contraction of a*b+c into fma.
+#pragma clang fp contract(off)
+
+#include <algorithm>
+#include <vector>
+
+#include "lct_internal.h"
+
+namespace lct {
+namespace {
+
+constexpr int kCap = 8;          // longest code
+constexpr int kLit = 8;          // literal bits after the escape code
+constexpr int kEsc = 256;        // escape symbol id
+
+// ---------------------------------------------------------------- model
+
+double cont_frac_beta(double a, double b, double x) {
+    // 1 / (1 + d1 / (1 + d2 / (1 + ...))) for the regularized incomplete beta,
+    // with d_{2m+1} = -(a+m)(a+b+m)x / ((a+2m)(a+2m+1)) and
+    // d_{2m} = m(b-m)x / ((a+2m-1)(a+2m)); modified Lentz evaluation.
+    const double tiny = 1e-300;
+    double f = 1.0, c = 1.0, d = 0.0;
+    for (int j = 1; j <= 100000; ++j) {
+        const double m = j / 2;
+        const double num = (j & 1) ? -(a + m) * (a + b + m) * x
+                                   : m * (b - m) * x;
+        const double den = (j & 1) ? (a + 2.0 * m) * (a + 2.0 * m + 1.0)
+                                   : (a + 2.0 * m - 1.0) * (a + 2.0 * m);
+        const double dj = num / den;
+        d = 1.0 + dj * d;
+        if (fabs(d) < tiny) d = tiny;
+        d = 1.0 / d;
+        c = 1.0 + dj / c;
+        if (fabs(c) < tiny) c = tiny;
+        const double step = c * d;
+        f *= step;
+        if (fabs(step - 1.0) < 1e-16) break;
+    }
+    return f;
+}
+
+// I_x(a, b); y = 1 - x is given separately to keep its precision.
+double reg_inc_beta(double a, double b, double x, double y) {
+    if (x <= 0.0) return 0.0;
+    if (y <= 0.0) return 1.0;
+    const double lb = lgamma(a) + lgamma(b) - lgamma(a + b);
+    const double front = exp(a * log(x) + b * log(y) - lb);
+    if (x < (a + 1.0) / (a + b + 2.0)) return front / (a * cont_frac_beta(a, b, x));
+    return 1.0 - front / (b * cont_frac_beta(b, a, y));
+}
+
+// P(|X| > t) under the model.
+double tail(const lct_model &m, double t) {
+    switch (m.family) {
+    case LCT_GAUSSIAN:
+        return erfc(t / (m.scale * sqrt(2.0)));
+    case LCT_LAPLACE:
+        return exp(-t / m.scale);
+    case LCT_POWERLAW: {
+        const double u = t / m.scale;
+        const double nu = m.shape;
+        return reg_inc_beta(0.5 * nu, 0.5, nu / (nu + u * u), (u * u) / (nu + u * u));
+    }
+    }
+    return 0.0;
+}
+
+bool model_ok(const lct_model &m) {
+    if (m.family < LCT_GAUSSIAN || m.family > LCT_POWERLAW) return false;
+    if (!(m.scale > 0.0) || !std::isfinite(m.scale)) return false;
+    if (m.family == LCT_POWERLAW && (!(m.shape > 0.0) || !std::isfinite(m.shape))) return false;
+    return true;
+}
+
+void model_weights(const lct_model &m, uint64_t w[256]) {
+    double p[256];
+    p[0] = 1.0 - tail(m, ldexp(1.0, -126));
+    for (int e = 1; e <= 254; ++e) {
+        const double lo = tail(m, ldexp(1.0, e - 127));
+        const double hi = tail(m, ldexp(1.0, e - 126));
+        const double q = lo - hi;
+        p[e] = q > 0.0 ? q : 0.0;
+    }
+    p[255] = 0.0;
+    for (int e = 0; e < 256; ++e) w[e] = (uint64_t)floor(p[e] * 1099511627776.0 + 0.5);
+}
+
+// ---------------------------------------------------------------- package-merge
+//
+// Coin-collector form: level kCap holds the leaves in (weight, id) order;
+// every shallower level is the leaves merged with the pairs of consecutive
+// items of the level below.  Only each level's item kinds are kept: of the
+// first 2n-2 items of level 1, the leaves are the lightest leaves and the
+// packages expand to the first items of the next level, so a leaf's length
+// is the number of levels whose selected prefix reaches it.
+
+struct Leaf {
+    uint64_t w;
+    int id;
+};
+
+void limited_lengths(std::vector<Leaf> &leaves, std::vector<int> &len_out) {
+    const int n = (int)leaves.size();
+    std::sort(leaves.begin(), leaves.end(), [](const Leaf &a, const Leaf &b) {
+        return a.w != b.w ? a.w < b.w : a.id < b.id;
+    });
+    // kind[d][i]: true = package; levels 1..kCap (index 0 unused)
+    std::vector<std::vector<uint8_t>> kind(kCap + 1);
+    std::vector<uint64_t> cur(n), nxt;
+    for (int i = 0; i < n; ++i) cur[i] = leaves[i].w;
+    kind[kCap].assign(n, 0);
+    for (int d = kCap - 1; d >= 1; --d) {
+        const int npk = (int)cur.size() / 2;
+        nxt.clear();
+        kind[d].clear();
+        int li = 0, pi = 0;
+        while (li < n || pi < npk) {
+            const bool take_leaf =
+                li < n && (pi >= npk || leaves[li].w <= cur[2 * pi] + cur[2 * pi + 1]);
+            if (take_leaf) {
+                nxt.push_back(leaves[li++].w);
+                kind[d].push_back(0);
+            } else {
+                nxt.push_back(cur[2 * pi] + cur[2 * pi + 1]);
+                kind[d].push_back(1);
+                ++pi;
+            }
+        }
+        cur.swap(nxt);
+    }
+    std::vector<int> len_sorted(n, 0);
+    int take = 2 * n - 2;
+    for (int d = 1; d <= kCap && take > 0; ++d) {
+        int nleaf = 0, npack = 0;
+        for (int i = 0; i < take; ++i) (kind[d][i] ? npack : nleaf)++;
+        for (int i = 0; i < nleaf; ++i) ++len_sorted[i];
+        take = 2 * npack;
+    }
+    len_out.assign(n, 0);
+    for (int i = 0; i < n; ++i) len_out[i] = len_sorted[i];
+}
+
+// Base code: lengths len[256] (0 = escaped) and esc_len for the weights.
+bool base_code(const uint64_t w[256], uint8_t len[256], uint8_t *esc_len) {
+    int order[256];
+    for (int i = 0; i < 256; ++i) order[i] = i;
+    std::sort(order, order + 256, [&](int a, int b) { return w[a] != w[b] ? w[a] > w[b] : a < b; });
+    int nonzero = 0;
+    for (int i = 0; i < 256; ++i) nonzero += w[i] != 0;
+    const int kmax = std::min(255, std::max(1, nonzero));
+
+    // suffix sums of the ranked weights: weight escaped when keeping k
+    uint64_t rest[257];
+    rest[256] = 0;
+    for (int r = 255; r >= 0; --r) rest[r] = rest[r + 1] + w[order[r]];
+
+    uint64_t best = ~uint64_t(0);
+    int best_k = 0;
+    std::vector<int> best_len;
+    std::vector<Leaf> leaves;
+    std::vector<int> ln;
+    for (int k = 1; k <= kmax; ++k) {
+        leaves.clear();
+        for (int r = 0; r < k; ++r) leaves.push_back({w[order[r]], order[r]});
+        leaves.push_back({rest[k], kEsc});
+        limited_lengths(leaves, ln);   // leaves are now sorted; ln follows that order
+        uint64_t cost = 0;
+        for (size_t i = 0; i < leaves.size(); ++i) {
+            if (leaves[i].id == kEsc) {
+                cost += leaves[i].w * (uint64_t)(ln[i] + kLit);
+            } else {
+                cost += leaves[i].w * (uint64_t)ln[i];
+            }
+        }
+        if (cost < best) {
+            best = cost;
+            best_k = k;
+            best_len.assign(257, 0);
+            for (size_t i = 0; i < leaves.size(); ++i) best_len[leaves[i].id] = ln[i];
+        }
+    }
+    if (best_k == 0) return false;
+    for (int e = 0; e < 256; ++e) len[e] = (uint8_t)best_len[e];
+    *esc_len = (uint8_t)best_len[kEsc];
+    return true;
+}
+
+// Shift k minimising the sample's coded bits; the histogram of the sample's
+// exponent fields is all that matters.
+int best_shift(const uint8_t base[256], uint8_t esc_len, const uint16_t *sample, uint32_t m) {
+    uint64_t hist[256] = {0};
+    for (uint32_t i = 0; i < m; ++i) ++hist[(sample[i] >> 7) & 0xFF];
+    auto bits_for = [&](int k) {
+        uint64_t total = 0;
+        for (int e = 0; e < 256; ++e) {
+            if (!hist[e]) continue;
+            const int x = e - k;
+            const unsigned c = (x >= 0 && x < 256 && base[x]) ? base[x] : esc_len + kLit;
+            total += hist[e] * c;
+        }
+        return total;
+    };
+    int best_k = 0;
+    uint64_t best = bits_for(0);
+    // visiting 0, -1, +1, -2, +2, ... and keeping strict improvements gives
+    // the smallest |k|, then the smaller k, among equal costs
+    for (int a = 1; a <= 255; ++a) {
+        for (int k : {-a, a}) {
+            const uint64_t c = bits_for(k);
+            if (c < best) {
+                best = c;
+                best_k = k;
+            }
+        }
+    }
+    return best_k;
+}
+
+uint32_t reverse_bits(uint32_t v, int n) {
+    uint32_t r = 0;
+    for (int i = 0; i < n; ++i) r |= ((v >> i) & 1u) << (n - 1 - i);
+    return r;
+}
+
+// Canonical codes, lookup tables and summary fields from cb->len / esc_len.
+void finish(lct_codebook *cb) {
+    // symbols with a code in (length, id) order; code values count up and
+    // shift left whenever the length grows
+    std::vector<std::pair<int, int>> syms;   // (length, id)
+    for (int e = 0; e < 256; ++e)
+        if (cb->len[e]) syms.push_back({cb->len[e], e});
+    syms.push_back({cb->esc_len, kEsc});
+    std::sort(syms.begin(), syms.end());
+    memset(cb->code, 0, sizeof cb->code);
+    uint32_t c = 0;
+    for (size_t i = 0; i < syms.size(); ++i) {
+        if (i > 0) c = (c + 1) << (syms[i].first - syms[i - 1].first);
+        cb->code[syms[i].second] = c;
+    }
+    uint32_t kept = 0, maxl = cb->esc_len;
+    for (int e = 0; e < 256; ++e) {
+        if (cb->len[e]) {
+            ++kept;
+            maxl = std::max<uint32_t>(maxl, cb->len[e]);
+            cb->enc_bits[e] = reverse_bits(cb->code[e], cb->len[e]);
+            cb->enc_len[e] = cb->len[e];
+        } else {
+            cb->enc_bits[e] = reverse_bits(cb->code[kEsc], cb->esc_len) | ((uint32_t)e << cb->esc_len);
+            cb->enc_len[e] = (uint8_t)(cb->esc_len + kLit);
+        }
+    }
+    cb->kept = kept;
+    cb->max_len = (uint8_t)maxl;
+    // peek table: every 8-bit window whose low L bits are a code's stream bits
+    for (int p = 0; p < 256; ++p) cb->dec[p] = (uint16_t)((kCap << 8) | (1u << 14));
+    for (const auto &s : syms) {
+        const int L = s.first;
+        const uint32_t r = reverse_bits(cb->code[s.second], L);
+        const uint16_t ent = s.second == kEsc
+                                 ? (uint16_t)(((L + kLit) << 8) | (1u << 13))
+                                 : (uint16_t)(s.second | (L << 8));
+        for (uint32_t h = 0; h < (1u << (kCap - L)); ++h) cb->dec[r | (h << L)] = ent;
+    }
+}
+
+}  // namespace
+
+lct_status build_codebook(const lct_model &model, const uint16_t *sample, uint32_t m,
+                          lct_codebook *out) {
+    if (!model_ok(model)) return LCT_EINVAL;
+    uint64_t w[256];
+    model_weights(model, w);
+    uint8_t base[256], esc_len = 0;
+    if (!base_code(w, base, &esc_len)) return LCT_EINVAL;
+    const int k = best_shift(base, esc_len, sample, m);
+    lct_status st = codebook_from_lengths(base, esc_len, k, out);
+    out->model = model;
+    return st;
+}
+
+lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
+                                 lct_codebook *out) {
+    if (!len_base || !out || esc_len < 1 || esc_len > kCap || shift < -255 || shift > 255)
+        return LCT_EINVAL;
+    uint32_t kraft = 1u << (kCap - esc_len);
+    for (int e = 0; e < 256; ++e) {
+        if (len_base[e] > kCap) return LCT_EINVAL;
+        if (len_base[e]) kraft += 1u << (kCap - len_base[e]);
+    }
+    if (kraft > (1u << kCap)) return LCT_EINVAL;
+    memset(out, 0, sizeof *out);
+    for (int e = 0; e < 256; ++e) {
+        const int x = e - shift;
+        out->len[e] = (x >= 0 && x < 256) ? len_base[x] : 0;
+    }
+    out->esc_len = esc_len;
+    out->shift = (int16_t)shift;
+    finish(out);
+    return LCT_OK;
+}
+
+void fill_enc(const lct_codebook &cb, EncTab *t) {
+    memcpy(t->bits, cb.enc_bits, sizeof t->bits);
+    memcpy(t->len, cb.enc_len, sizeof t->len);
+}
+
+void fill_dec(const lct_codebook &cb, DecTab *t) {
+    memcpy(t->dec, cb.dec, sizeof t->dec);
+    t->esc_len = cb.esc_len;
+}
+
+}  // namespace lct

@@ -1,0 +1,113 @@
+// lct_internal.h -- parameter blocks shared by the C ABI (api.cpp) and the
+// HIP kernels (kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lct.h"
+
+namespace lct {
+
+constexpr uint32_t kStreams = 256;          // streams per block
+constexpr uint32_t kChunk = 8;              // positions per stream processed per loop step
+constexpr uint32_t kMinBlock = kStreams * kChunk;
+constexpr uint32_t kMaxBlock = 65536;
+constexpr uint32_t kMaxCapWords = 64;
+
+// Scratch layout (bytes).  The header and the look-back flags are cleared by
+// a fill kernel before each encode / SGD launch; the staging area holds
+// spilled exponent fields until the block's overflow offset is known.
+constexpr uint64_t kScrTicket = 0;    // uint32: next block to hand out
+constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the staging area
+constexpr uint64_t kScrFlags = 64;    // uint64[nblk]: look-back descriptors
+__host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) { return (kScrFlags + 8 * nblk + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) { return kScrFlags + 8 * nblk; }
+
+// Encoder tables: stream bits of each exponent field and their count.
+struct EncTab {
+    uint32_t bits[256];
+    uint8_t len[256];
+};
+
+// Decoder table: 8-bit peek -> field | bits << 8 | escape << 13 | invalid << 14.
+struct DecTab {
+    uint16_t dec[256];
+    uint32_t esc_len;
+};
+
+struct EncodeParams {
+    const uint16_t *x;
+    uint64_t n;
+    uint32_t block_elems, cap_words, nblk, pad0;
+    uint8_t *sf;
+    uint32_t *pay;
+    uint16_t *cnt;
+    uint64_t *obase;
+    uint8_t *ovf;
+    uint64_t ovf_cap;
+    uint32_t *status;
+    uint8_t *scratch;
+    EncTab enc;
+};
+
+struct DecodeParams {
+    const uint8_t *sf;
+    const uint32_t *pay;
+    const uint16_t *cnt;
+    const uint64_t *obase;
+    const uint8_t *ovf;
+    uint64_t ovf_cap;
+    uint16_t *y;
+    uint64_t n;
+    uint32_t block_elems, cap_words, nblk, pad0;
+    DecTab dec;
+};
+
+struct SgdParams {
+    // inputs: W (codebook cw) and M (codebook cm)
+    const uint8_t *w_sf;
+    const uint32_t *w_pay;
+    const uint16_t *w_cnt;
+    const uint64_t *w_obase;
+    const uint8_t *w_ovf;
+    uint64_t w_ovf_cap;
+    const uint8_t *m_sf;
+    const uint32_t *m_pay;
+    const uint16_t *m_cnt;
+    const uint64_t *m_obase;
+    const uint8_t *m_ovf;
+    uint64_t m_ovf_cap;
+    // output W'
+    uint8_t *o_sf;
+    uint32_t *o_pay;
+    uint16_t *o_cnt;
+    uint64_t *o_obase;
+    uint8_t *o_ovf;
+    uint64_t ovf_cap;
+    uint32_t *status;
+    uint8_t *scratch;
+    uint64_t n;
+    uint32_t block_elems, cap_words, nblk;
+    float neg_eta;
+    EncTab wenc;
+    DecTab wdec;
+    DecTab mdec;
+};
+
+// Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
+int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
+int launch_encode(const EncodeParams &p, void *stream);
+int launch_decode(const DecodeParams &p, void *stream);
+int launch_sgd(const SgdParams &p, void *stream);
+int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
+
+// Host codebook construction (codebook.cpp).
+lct_status build_codebook(const lct_model &model, const uint16_t *sample, uint32_t m,
+                          lct_codebook *out);
+lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
+                                 lct_codebook *out);
+void fill_enc(const lct_codebook &cb, EncTab *t);
+void fill_dec(const lct_codebook &cb, DecTab *t);
+
+}  // namespace lct

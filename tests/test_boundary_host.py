@@ -1,0 +1,210 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/lct.h declares, its structs match the header's layout,
+its host codebook builder agrees with the oracle's, and invalid arguments are
+rejected before anything reaches a device.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lct.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import lossless_bf16_tensor_split_amd as L
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lct_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    out = subprocess.check_output(["nm", "-D", "--defined-only", L.LIB_PATH]).decode()
+    exported = set(re.findall(r" T (lct_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L.lib, n)
+    assert set(L.EXPORTED) == set(names)
+
+
+def test_struct_layouts_match_header(L, tmp_path):
+    src = tmp_path / "probe.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lct.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+                   'sizeof(lct_codebook), sizeof(lct_tensor), sizeof(lct_sizes_t), sizeof(lct_model),'
+                   'offsetof(lct_codebook, code), offsetof(lct_codebook, dec),'
+                   'offsetof(lct_tensor, scratch), offsetof(lct_codebook, model));return 0;}\n')
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-I" + os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    want = [C.sizeof(L.Codebook), C.sizeof(L._Tensor), C.sizeof(L.Sizes), C.sizeof(L.Model),
+            L.Codebook.code.offset, L.Codebook.dec.offset, L._Tensor.scratch.offset,
+            L.Codebook.model.offset]
+    assert got == want
+
+
+def test_layout_modes_and_sizes(L, orc):
+    import synth
+    for mode in (L.CLEAN, L.MEDIUM, L.HIGH):
+        lay = L.lct_layout_init(mode)
+        assert (lay.block_elems, lay.cap_words) == synth.mode_layout(mode)
+    with pytest.raises(L.LctError):
+        L.lct_layout_init(7)
+    # sizes agree with the oracle's buffers
+    x = synth.draw(synth.TensorSpec("w", (3 * 32768 + 5,), 1, "normal", {"sigma": 0.02}))
+    cb = orc.codebook_build(0, 0.02, 0.0, x)
+    t = orc.encode(cb, x, 32768, 12)
+    sz = L.lct_sizes(x.size, L.layout(32768, 12), 1000)
+    assert (sz.nblk, sz.sf, sz.pay, sz.cnt, sz.obase) == (
+        t.nblk, t.sf.nbytes, t.pay.nbytes, t.cnt.nbytes, t.obase.nbytes)
+    assert sz.fixed == t.sf.nbytes + t.pay.nbytes + t.cnt.nbytes + t.obase.nbytes
+    assert sz.scratch >= 1000 + 8 * t.nblk
+    for bad in [(1024, 25), (65536 + 2048, 25), (3000, 25), (65536, 0), (65536, 65)]:
+        with pytest.raises(L.LctError):
+            L.lct_sizes(100, L.layout(*bad), 0)
+
+
+MODELS = [(0, 0.02, 0.0), (0, 1e-3, 0.0), (0, 1.0, 0.0), (1, 0.01, 0.0), (1, 0.25, 0.0),
+          (2, 0.01, 3.0), (2, 1.0, 1.0), (2, 0.05, 5.5), (0, 1e-30, 0.0), (1, 1e30, 0.0)]
+
+
+@pytest.mark.parametrize("fam,scale,shape", MODELS)
+def test_host_codebook_equals_oracle(L, orc, fam, scale, shape):
+    """Base code (no sample: shift 0): identical lengths, escape length and
+    canonical codes to the oracle's builder."""
+    cb = L.lct_codebook_build(L.Model(fam, scale, shape), None)
+    lens, esc, k, _ = orc.build_base(orc.weights(orc.model_pmf(fam, scale, shape)))
+    ocb = orc.codebook_from_base(lens, esc, 0)
+    assert np.array_equal(np.frombuffer(bytes(cb.len), np.uint8), ocb.len)
+    assert cb.esc_len == ocb.esc_len and cb.shift == 0 and cb.kept == k
+    assert np.array_equal(np.frombuffer(bytes(cb.code), np.uint32), ocb.code)
+
+
+def test_tables_follow_the_oracle_codebook(L, orc):
+    """The library's encoder bits and 8-bit peek table, checked against the
+    oracle's canonical codes (MSB-first code, LSB-first stream)."""
+    g = np.random.default_rng(4)
+    for trial in range(6):
+        fam = trial % 3
+        lens, esc, _, _ = orc.build_base(orc.weights(orc.model_pmf(fam, 0.01 * (trial + 1), 3.0)))
+        shift = int(g.integers(-30, 31))
+        cb = L.lct_codebook_from_lengths(lens, esc, shift)
+        ocb = orc.codebook_from_base(lens, esc, shift)
+        assert np.array_equal(np.frombuffer(bytes(cb.len), np.uint8), ocb.len)
+        assert np.array_equal(np.frombuffer(bytes(cb.code), np.uint32), ocb.code)
+        bits = np.frombuffer(bytes(cb.enc_bits), np.uint32)
+        blen = np.frombuffer(bytes(cb.enc_len), np.uint8)
+        dec = np.frombuffer(bytes(cb.dec), np.uint16)
+        for e in range(256):
+            if ocb.len[e]:
+                s = format(int(ocb.code[e]), "0%db" % ocb.len[e])
+            else:
+                s = format(int(ocb.code[256]), "0%db" % esc) + format(e, "08b")[::-1]
+            assert blen[e] == len(s)
+            # stream order: first bit at bit 0
+            assert int(bits[e]) == int(s[::-1], 2), e
+            # the peek table finds this field from its first 8 stream bits
+            peek = int(s[:8][::-1], 2) if len(s) >= 8 else int(s[::-1], 2)
+            for hi in range(0, 256, 37):
+                p = (peek | (hi << len(s))) & 0xFF if len(s) < 8 else peek
+                ent = int(dec[p])
+                assert not (ent >> 14) & 1
+                if ocb.len[e]:
+                    assert ent & 0xFF == e and (ent >> 8) & 0x1F == ocb.len[e]
+                else:
+                    assert (ent >> 13) & 1 and (ent >> 8) & 0x1F == esc + 8
+
+
+def test_codebook_from_lengths_rejects_bad_codes(L):
+    bad = np.zeros(256, np.uint8)
+    bad[:3] = 1                       # Kraft sum 1.5
+    with pytest.raises(L.LctError):
+        L.lct_codebook_from_lengths(bad, 1, 0)
+    ok = np.zeros(256, np.uint8)
+    ok[10] = 1
+    with pytest.raises(L.LctError):
+        L.lct_codebook_from_lengths(ok, 0, 0)   # escape length must be 1..8
+    with pytest.raises(L.LctError):
+        L.lct_codebook_from_lengths(ok, 1, 300)
+    with pytest.raises(L.LctError):
+        L.lct_codebook_build(L.Model(5, 1.0, 0.0), None)
+    with pytest.raises(L.LctError):
+        L.lct_codebook_build(L.Model(0, -1.0, 0.0), None)
+
+
+def _fake_tensor(L, n, lay, base, ovf_cap=64, **over):
+    """A descriptor with made-up, never dereferenced device addresses."""
+    sz = L.lct_sizes(n, lay, ovf_cap)
+    addr = {}
+    cur = base
+    for k, nbytes in [("sf", sz.sf), ("pay", sz.pay), ("cnt", sz.cnt), ("obase", sz.obase),
+                      ("ovf", ovf_cap), ("status", 4), ("scratch", sz.scratch)]:
+        cur = (cur + 4095) & ~4095
+        addr[k] = cur
+        cur += nbytes
+    addr.update(over)
+    return L._Tensor(n, lay, *[C.c_void_p(addr[k]) for k in ("sf", "pay", "cnt", "obase", "ovf")],
+                     ovf_cap, C.c_void_p(addr["status"]), C.c_void_p(addr["scratch"]))
+
+
+def test_invalid_arguments_rejected_on_host(L):
+    lay = L.layout(65536, 25)
+    cb = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    x = C.c_void_p(0x7000_0000_0000)
+    n = 100000
+    t = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    enc = L.lib.lct_encode
+    assert enc(C.byref(cb), None, C.byref(t), None) == L.EINVAL
+    assert enc(None, x, C.byref(t), None) == L.EINVAL
+    assert enc(C.byref(cb), C.c_void_p(0x7000_0000_0002), C.byref(t), None) == L.EALIGN
+    t_bad = _fake_tensor(L, n, lay, 0x1000_0000_0000, sf=0x1000_0000_0008)
+    assert enc(C.byref(cb), x, C.byref(t_bad), None) == L.EALIGN
+    t_bad = _fake_tensor(L, n, lay, 0x1000_0000_0000, scratch=0x2000_0000_0080)
+    assert enc(C.byref(cb), x, C.byref(t_bad), None) == L.EALIGN
+    # input overlapping an output
+    assert enc(C.byref(cb), C.c_void_p(t.pay), C.byref(t), None) == L.EALIAS
+    # two outputs overlapping each other
+    t_bad = _fake_tensor(L, n, lay, 0x1000_0000_0000, cnt=t.pay)
+    assert enc(C.byref(cb), x, C.byref(t_bad), None) == L.EALIAS
+    # bad layout
+    t_bad = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    t_bad.layout = L.layout(4096, 0)
+    assert enc(C.byref(cb), x, C.byref(t_bad), None) == L.EINVAL
+    # n == 0 is a no-op
+    t0 = _fake_tensor(L, 0, lay, 0x1000_0000_0000)
+    assert enc(C.byref(cb), None, C.byref(t0), None) == L.OK
+    # decode: output overlapping the input
+    dec = L.lib.lct_decode
+    assert dec(C.byref(cb), C.byref(t), C.c_void_p(t.sf), None) == L.EALIAS
+    assert dec(C.byref(cb), C.byref(t), None, None) == L.EINVAL
+    # SGD: aliasing rules
+    sgd = L.lib.lct_sgd_step
+    w = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    m = _fake_tensor(L, n, lay, 0x3000_0000_0000)
+    o = _fake_tensor(L, n, lay, 0x5000_0000_0000)
+    # (every descriptor below is rejected before any launch: fake addresses
+    # must never reach a kernel, even where a GPU is present)
+    # overflow of the output on the input's overflow: rejected
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, ovf=w.ovf)
+    assert sgd(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), C.c_float(1e-3), C.byref(bad), None) == L.EALIAS
+    # output on M: rejected
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, sf=m.sf)
+    assert sgd(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), C.c_float(1e-3), C.byref(bad), None) == L.EALIAS
+    # partial overlap with W's fixed side: rejected
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, sf=w.sf + 16)
+    assert sgd(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), C.c_float(1e-3), C.byref(bad), None) == L.EALIAS
+    # size mismatch
+    m2 = _fake_tensor(L, n + 1, lay, 0x3000_0000_0000)
+    assert sgd(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m2), C.c_float(1e-3), C.byref(o), None) == L.EINVAL
+    assert L.lib.lct_strerror(L.EALIAS) == b"illegal buffer overlap"

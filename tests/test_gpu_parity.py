@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, byte for
+byte on every compressed buffer and bit for bit on decoded and updated values.
+
+The bar: sf, pay, cnt, obase and the used part of ovf identical; decoded
+tensors identical to the input; the SGD output identical to the oracle's naive
+decode -> fmaf -> RNE -> encode round trip (0 ULP).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lossless_bf16_tensor_split_amd as L
+    return L
+
+
+def dev(x16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).cuda()
+
+
+def host_parts(t):
+    """Compressed buffers of a device tensor, trimmed to their sizes."""
+    sz = t.sizes
+    torch.cuda.synchronize()
+    spilled = int(t.obase[-1].item())
+    return {
+        "sf": t.sf[:sz.sf].cpu().numpy(),
+        "pay": t.pay[:sz.pay // 4].cpu().numpy().view(np.uint32),
+        "cnt": t.cnt[:sz.cnt // 2].cpu().numpy().view(np.uint16),
+        "obase": t.obase.cpu().numpy().view(np.uint64),
+        "ovf": t.ovf[:min(spilled, t.ovf_cap)].cpu().numpy(),
+        "status": int(t.status[0].item()),
+    }
+
+
+def assert_same(gpu, ref, what=""):
+    for k in ["sf", "pay", "cnt", "obase"]:
+        a, b = gpu[k], getattr(ref, k)
+        if not np.array_equal(a, b):
+            bad = np.nonzero(a != b)[0]
+            raise AssertionError("%s %s differs at %d places, first %d: gpu %s oracle %s" %
+                                 (what, k, bad.size, bad[0], a[bad[0]], b[bad[0]]))
+    n = min(ref.spilled, len(ref.ovf))
+    assert np.array_equal(gpu["ovf"][:n], ref.ovf[:n]), what + " ovf"
+
+
+def check_codebook(L, orc, model, x):
+    """Library build on the device vs oracle build on the host: same lengths,
+    escape length, shift and codes."""
+    cb = L.lct_codebook_build(L.Model(model.family, model.scale, model.shape), dev(x))
+    ocb = orc.codebook_build(model.family, model.scale, model.shape, x)
+    assert np.array_equal(np.frombuffer(bytes(cb.len), np.uint8), ocb.len)
+    assert cb.esc_len == ocb.esc_len and cb.shift == ocb.shift
+    assert np.array_equal(np.frombuffer(bytes(cb.code), np.uint32), ocb.code)
+    return cb, ocb
+
+
+def roundtrip_case(L, orc, x, model, block_elems, cap_words, ovf_cap=None, what=""):
+    cb, ocb = check_codebook(L, orc, model, x)
+    lay = L.layout(block_elems, cap_words)
+    xd = dev(x)
+    t = L.encode(cb, xd, lay, ovf_cap)
+    ref = orc.encode(ocb, x, block_elems, cap_words, ovf_cap)
+    g = host_parts(t)
+    assert_same(g, ref, what)
+    assert g["status"] == ref.status
+    y = L.decode(cb, t)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), x), what + " decode"
+    return cb, ocb, t, ref
+
+
+# ------------------------------------------------------------------ encode / decode
+
+def test_config1_gaussian_clean(L, orc):
+    spec, model = synth.config1()[0]
+    x = synth.draw(spec)
+    B, cw = synth.mode_layout(synth.CLEAN)
+    _, _, t, ref = roundtrip_case(L, orc, x, model, B, cw, what="config1")
+    assert ref.spilled == 0 and abs(t.ratio() - ref.ratio()) < 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 257, 2047, 2048, 2049, 65535, 65537, 300001])
+def test_odd_sizes(L, orc, n):
+    x = synth.draw(synth.TensorSpec("w", (n,), 500 + n % 89, "normal", {"sigma": 0.02}))
+    for B, cw in [(65536, 25), (2048, 2), (4096, 1)]:
+        roundtrip_case(L, orc, x, synth.Model(0, 0.02), B, cw, what="n=%d B=%d cw=%d" % (n, B, cw))
+
+
+@pytest.mark.parametrize("B,cw", [(2048, 1), (2048, 3), (4096, 2), (16384, 4), (32768, 11),
+                                  (65536, 8), (65536, 64)])
+def test_forced_overflow_many_blocks(L, orc, B, cw):
+    x = synth.draw(synth.TensorSpec("w", (97 * B + 1234,), 600 + cw, "laplace", {"b": 0.01}))
+    _, _, _, ref = roundtrip_case(L, orc, x, synth.Model(1, 0.01), B, cw, what="B=%d cw=%d" % (B, cw))
+    if cw < 12:
+        assert ref.spilled > 0
+
+
+def test_specials_and_uniform_bits(L, orc):
+    allpat = np.tile(np.arange(1 << 16, dtype=np.uint16), 3)
+    ub = synth.draw(synth.TensorSpec("u", (200003,), 4002, "uniform_bits"))
+    for x in [allpat, ub, np.full(70000, 0x7FC0, np.uint16), np.full(4097, 0x0001, np.uint16)]:
+        for B, cw in [(65536, 25), (32768, 12), (2048, 1)]:
+            roundtrip_case(L, orc, x, synth.Model(0, 1.0), B, cw, what="specials B=%d" % B)
+
+
+def test_repeatable_lookback(L, orc):
+    """Many small blocks with spills everywhere, encoded 20 times: identical
+    bytes every time (the cross-block offset scan has a single answer)."""
+    x = synth.draw(synth.TensorSpec("u", (2048 * 3000 + 17,), 77, "uniform_bits"))
+    cb, ocb = check_codebook(L, orc, synth.Model(0, 1.0), x)
+    ref = orc.encode(ocb, x, 2048, 2)
+    lay = L.layout(2048, 2)
+    xd = dev(x)
+    t = L.alloc_tensor(x.size, lay)
+    for _ in range(20):
+        t.obase.fill_(-1)
+        L.lct_encode(cb, xd, t)
+        assert_same(host_parts(t), ref, "repeat")
+
+
+def test_ovf_capacity_status_and_guards(L, orc):
+    x = synth.draw(synth.TensorSpec("u", (40000,), 78, "uniform_bits"))
+    cb, ocb = check_codebook(L, orc, synth.Model(0, 1.0), x)
+    full = orc.encode(ocb, x, 2048, 2)
+    need = full.spilled
+    lay = L.layout(2048, 2)
+    for cap in [0, 1, need // 2, need - 1, need]:
+        t = L.alloc_tensor(x.size, lay, ovf_cap=cap)
+        # the ovf buffer holds 4096 guard bytes past ovf_cap
+        t.ovf = torch.full((cap + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+        L.lct_encode(cb, dev(x), t)
+        g = host_parts(t)
+        assert int(g["obase"][-1]) == need
+        assert g["status"] == (0 if cap >= need else L.ST_OVF_FULL)
+        ovf = t.ovf.cpu().numpy()
+        assert np.array_equal(ovf[:cap], full.ovf[:cap])
+        assert (ovf[cap:] == 0xA5).all()
+        assert np.array_equal(g["pay"], full.pay) and np.array_equal(g["cnt"], full.cnt)
+
+
+# ------------------------------------------------------------------ larger workloads
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+@pytest.mark.parametrize("mode", [synth.MEDIUM, synth.HIGH])
+def test_config2_overflow_stress(L, orc, idx, mode):
+    spec, model = synth.config2()[idx]
+    x = synth.draw(spec)
+    B, cw = synth.mode_layout(mode)
+    _, _, _, ref = roundtrip_case(L, orc, x, model, B, cw, what="config2 %s mode %d" % (spec.name, mode))
+    if mode == synth.HIGH:
+        assert ref.spilled > 0
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_config4_activations(L, orc, idx):
+    spec, model = synth.config4()[idx]
+    x = synth.draw(spec)
+    for mode in (synth.CLEAN, synth.MEDIUM):
+        B, cw = synth.mode_layout(mode)
+        roundtrip_case(L, orc, x, model, B, cw, what="config4 %s" % spec.name)
+
+
+# ------------------------------------------------------------------ fused SGD
+
+def sgd_case(L, orc, w, m, mw, mm, eta, B, cw, inplace, what=""):
+    cbw, ocw = check_codebook(L, orc, mw, w)
+    cbm, ocm = check_codebook(L, orc, mm, m)
+    lay = L.layout(B, cw)
+    tw = L.encode(cbw, dev(w), lay)
+    tm = L.encode(cbm, dev(m), lay)
+    rw = orc.encode(ocw, w, B, cw)
+    rm = orc.encode(ocm, m, B, cw)
+    assert_same(host_parts(tw), rw, what + " W")
+    assert_same(host_parts(tm), rm, what + " M")
+    ref = orc.sgd(ocw, rw, ocm, rm, eta)
+    if inplace:
+        out = L.alloc_tensor(w.size, lay)
+        out.sf, out.pay, out.cnt, out.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+    else:
+        out = L.alloc_tensor(w.size, lay)
+    L.lct_sgd_step(cbw, tw, cbm, tm, eta, out)
+    g = host_parts(out)
+    assert_same(g, ref, what + " W'")
+    assert g["status"] == ref.status
+    y = L.decode(cbw, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), orc.decode(ocw, ref))
+    return ref
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (2048, 2), (4096, 3), (32768, 12)])
+def test_sgd_small_with_spills(L, orc, B, cw, inplace):
+    g = np.random.default_rng(B + cw)
+    n = 7 * B + 333
+    w = synth.to_bf16_bits(g.laplace(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1.0, n))
+    m[:64] = [0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x8001, 0x7F7F, 0xFF7F] * 8
+    w[100:164] = [0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x8001, 0x7F7F, 0xFF7F] * 8
+    sgd_case(L, orc, w, m, synth.Model(1, 0.02), synth.Model(0, 1.0), 0.05, B, cw, inplace,
+             what="B=%d cw=%d inplace=%s" % (B, cw, inplace))
+
+
+def test_sgd_eta_zero_identity(L, orc):
+    g = np.random.default_rng(3)
+    n = 5 * 65536 + 7
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    w[w == 0x8000] = 0
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    ref = sgd_case(L, orc, w, m, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.0, 65536, 25, False)
+    assert np.array_equal(orc.decode(orc.codebook_build(0, 0.02, 0.0, w), ref), w)
+
+
+def test_config3_gpt162m_flat(L, orc):
+    """One fused step over the flat 162M-parameter set, checked in full."""
+    ws, ms, mw, mm, eta = synth.config3()
+    w = np.concatenate([synth.draw(s) for s in ws])
+    m = np.concatenate([synth.draw(s) for s in ms])
+    B, cw = synth.mode_layout(synth.CLEAN)
+    ref = sgd_case(L, orc, w, m, mw, mm, eta, B, cw, True, what="config3")
+    assert ref.spilled == 0
