@@ -1,0 +1,335 @@
+"""Benchmark of the LCT codec's hot path on one MI355X.
+
+Workload: a Qwen3-4B-shaped parameter set (36 layers, hidden 2560, FFN 9728,
+32 q / 8 kv heads of dim 128, vocab 151936, tied embeddings) flattened to
+4,022,468,096 BF16 elements, W ~ N(0, 0.02^2) and a momentum buffer
+M ~ N(0, 1e-3^2), both resident in HBM; CLEAN layout (65,536-element blocks,
+25 words per stream); eta = 1e-3.  Inputs are synthetic and seeded: the pages'
+fine-tuning runs used trained weights and data that are not available.
+
+One step = the whole hot path over the set:
+    encode  W (dense BF16)          -> compressed W        (lct_encode)
+    update  W' = W - eta * M        on compressed W and M  (lct_sgd_step, in place)
+    decode  W' (compressed)         -> dense BF16 W        (lct_decode)
+The codebooks (lct_codebook_build) are set up once, as the pages prescribe
+(no codebook is built during training); their build time is reported apart.
+
+Prints one JSON line.  Per-op times come from HIP events recorded on the
+stream the kernels run on; `roofline` is for the op that takes longest, with
+its algorithmic bytes (what the format must move: BF16 in/out, the compressed
+sides and spilled bytes) over its mean duration.  `cpu_baseline` times the
+plain C oracle on a bounded sample of the same blocks (and checks the GPU's
+bytes for those blocks against it).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, AMD's published figure
+METRIC = "encode/decode GB/s of BF16 input, fused SGD elems/s, % HBM peak, comp. ratio"
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "lossless_bf16_tensor_split_amd", "csrc", "kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if one
+    exists for this kernel and workload and the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s_%s.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source") != kernel_source_hash():
+        return None
+    return d
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_4b", choices=["qwen3_4b", "gpt162m"])
+    ap.add_argument("--cpu-blocks", type=int, default=2048,
+                    help="blocks in the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the codec shards by blocks with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lossless_bf16_tensor_split_amd as L
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    if args.workload == "qwen3_4b":
+        wspec, mspec, mw, mm, eta = synth.config5()
+        wname = "qwen3_4b"
+        desc = ("Qwen3-4B-shaped parameter set (tied embeddings), flat, 4,022,468,096 BF16 "
+                "elements; W ~ N(0, 0.02^2), M ~ N(0, 1e-3^2); CLEAN 65536/25; eta 1e-3")
+    else:
+        ws, ms, mw, mm, eta = synth.config3()
+        n = sum(s.numel for s in ws)
+        wspec = synth.TensorSpec("W.flat", (n,), 3000, "normal", {"sigma": 0.02})
+        mspec = synth.TensorSpec("M.flat", (n,), 3001, "normal", {"sigma": 1e-3})
+        wname = "gpt162m"
+        desc = ("GPT-style 162M parameter set, flat, 162,201,600 BF16 elements; "
+                "W ~ N(0, 0.02^2), M ~ N(0, 1e-3^2); CLEAN 65536/25; eta 1e-3")
+    n = wspec.numel
+    lay = L.lct_layout_init(L.CLEAN)
+
+    # ---------------- set-up (untimed): inputs resident in HBM, codebooks, buffers
+    w_dense = synth.draw_device(wspec, dev)
+    m_dense = synth.draw_device(mspec, dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    cbw = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), w_dense)
+    t_cb = time.perf_counter() - t0
+    cbm = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), m_dense)
+    ovf_cap = max(n // 64, 1 << 20)
+    scratch = torch.empty(L.lct_sizes(n, lay, ovf_cap).scratch, dtype=torch.uint8, device=dev)
+    tw = L.alloc_tensor(n, lay, ovf_cap, dev, scratch)          # encode target
+    tm = L.alloc_tensor(n, lay, ovf_cap, dev, scratch)
+    L.lct_encode(cbm, m_dense, tm)
+    torch.cuda.synchronize()
+    assert tm.status_word() == 0, "M overflow capacity exceeded"
+    # the update writes W' in place on W's fixed side; its overflow goes to a
+    # second region (the overflow side ping-pongs)
+    tw2 = L.alloc_tensor(n, lay, ovf_cap, dev, scratch)
+    tw2.sf, tw2.pay, tw2.cnt, tw2.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+    cpu_in = None
+    if not args.no_cpu_baseline:
+        # inputs of the CPU leg, taken before anything is overwritten: the
+        # sampled blocks of W and M and the shift samples
+        blocks = sample_blocks(tw.sizes.nblk, n, lay.block_elems, args.cpu_blocks)
+        pos = torch.as_tensor(sample_positions(n), device=dev)
+        cpu_in = {"blocks": blocks,
+                  "w_blocks": host_blocks_dense(w_dense, blocks, lay.block_elems),
+                  "m_blocks": host_blocks_dense(m_dense, blocks, lay.block_elems),
+                  "w_sample": w_dense.view(torch.int16)[pos].cpu().numpy().view(np.uint16),
+                  "m_sample": m_dense.view(torch.int16)[pos].cpu().numpy().view(np.uint16)}
+    del m_dense
+    torch.cuda.empty_cache()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+          for _ in range(args.warmup + args.steps)]
+
+    def step(i):
+        e = ev[i]
+        e[0].record(stream)
+        L.lct_encode(cbw, w_dense, tw)
+        e[1].record(stream)
+        L.lct_sgd_step(cbw, tw, cbm, tm, eta, tw2)
+        e[2].record(stream)
+        L.lct_decode(cbw, tw2, w_dense)
+        e[3].record(stream)
+
+    # the first step runs op by op so that the CPU leg can check each output
+    cpu = None
+    if cpu_in is not None:
+        blocks = cpu_in["blocks"]
+        L.lct_encode(cbw, w_dense, tw)
+        torch.cuda.synchronize()
+        st_enc = tw.status_word()
+        g_enc = host_blocks_compressed(tw, blocks)
+        g_m = host_blocks_compressed(tm, blocks)
+        L.lct_sgd_step(cbw, tw, cbm, tm, eta, tw2)
+        torch.cuda.synchronize()
+        st_sgd = tw2.status_word()
+        g_sgd = host_blocks_compressed(tw2, blocks)
+        L.lct_decode(cbw, tw2, w_dense)
+        torch.cuda.synchronize()
+        g_dec = host_blocks_dense(w_dense, blocks, lay.block_elems)
+        cpu = cpu_baseline_leg(cpu_in, (g_enc, g_m, g_sgd, g_dec), cbw, cbm, mw, mm, eta, lay, n)
+    else:
+        step(0)
+        torch.cuda.synchronize()
+        st_enc, st_sgd = tw.status_word(), tw2.status_word()
+    ratio_w, ratio_m = tw.ratio(), tm.ratio()
+    spill_w, spill_m = tw.spilled(), tm.spilled()
+
+    for i in range(1, args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert tw.status_word() == 0 and tw2.status_word() == 0, "overflow capacity exceeded"
+
+    timed = ev[args.warmup:]
+    t_enc = float(np.mean([e[0].elapsed_time(e[1]) for e in timed])) / 1e3
+    t_sgd = float(np.mean([e[1].elapsed_time(e[2]) for e in timed])) / 1e3
+    t_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in timed])) / 1e3
+    t_step = float(np.mean([e[0].elapsed_time(e[3]) for e in timed])) / 1e3
+
+    fixed = tw.sizes.fixed
+    alg = {
+        "encode": 2 * n + fixed + tw.spilled(),
+        "decode": fixed + tw2.spilled() + 2 * n,
+        "sgd": fixed + tw.spilled() + fixed + tm.spilled() + fixed + tw2.spilled(),
+    }
+    times = {"encode": t_enc, "decode": t_dec, "sgd": t_sgd}
+    kname = {"encode": "k_encode", "decode": "k_decode", "sgd": "k_sgd"}
+    per_op = {}
+    for op in ("encode", "decode", "sgd"):
+        gbs = alg[op] / times[op] / 1e9
+        per_op[op] = {"ms": round(times[op] * 1e3, 4), "alg_bytes": int(alg[op]),
+                      "alg_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    per_op["encode"]["GBps_bf16_input"] = round(2 * n / t_enc / 1e9, 1)
+    per_op["decode"]["GBps_bf16_output"] = round(2 * n / t_dec / 1e9, 1)
+    per_op["sgd"]["elems_per_s"] = float("%.4g" % (n / t_sgd))
+    dom = max(times, key=times.get)
+    traffic = load_traffic(kname[dom], wname)
+    achieved = alg[dom] / times[dom] / 1e9
+    out = {
+        "metric": METRIC,
+        "value": float("%.5g" % (n / t_step)),
+        "unit": "elems/s (encode + fused SGD + decode of every element, one step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32 codec / f32 update",
+        "data": "synthetic (seeded device draws)",
+        "config": {"workload": desc, "elements": n, "block_elems": lay.block_elems,
+                   "cap_words": lay.cap_words, "eta": eta, "parallelism": "single GPU"},
+        "per_op": per_op,
+        "compression_ratio": {"W": round(ratio_w, 5), "M": round(ratio_m, 5),
+                              "payload_bound": round(16.0 / (8 + 32.0 * lay.cap_words / 256), 5)},
+        "spilled_bytes": {"W": spill_w, "M": spill_m},
+        "status": {"encode": st_enc, "sgd": st_sgd},
+        "codebook_build_ms": round(t_cb * 1e3, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": kname[dom], "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ CPU-baseline leg
+
+def sample_blocks(nblk: int, n: int, B: int, want: int):
+    """Evenly spread full blocks (the last, partial block is left out)."""
+    import numpy as np
+    full = n // B
+    want = min(want, full)
+    return np.unique(np.linspace(0, full - 1, want).round().astype(np.int64))
+
+
+def host_blocks_dense(x, blocks, B):
+    import torch
+    idx = (torch.as_tensor(blocks, device=x.device)[:, None] * B +
+           torch.arange(B, device=x.device)[None, :]).reshape(-1)
+    return x.view(torch.int16)[idx].cpu().numpy().view("uint16")
+
+
+def host_blocks_compressed(t, blocks):
+    """The sampled blocks of a device tensor as one oracle tensor (offsets rebased)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    B, cw = t.layout.block_elems, t.layout.cap_words
+    dv = t.sf.device
+    bt = torch.as_tensor(blocks, device=dv)
+
+    def rows(buf, width):
+        idx = (bt[:, None] * width + torch.arange(width, device=dv)[None, :]).reshape(-1)
+        return buf[idx].cpu().numpy()
+
+    sf = rows(t.sf, B)
+    pay = rows(t.pay, cw * 256).view(np.uint32)
+    cnt = rows(t.cnt, 256).view(np.uint16)
+    ob = t.obase.cpu().numpy().view(np.uint64)
+    spans = [(int(ob[b]), int(ob[b + 1])) for b in blocks]
+    ovf_all = t.ovf
+    parts = [ovf_all[a:b].cpu().numpy() for a, b in spans]
+    ovf = np.concatenate(parts) if parts else np.zeros(0, np.uint8)
+    obase = np.zeros(len(blocks) + 1, np.uint64)
+    obase[1:] = np.cumsum([b - a for a, b in spans])
+    return oracle.Compressed(len(blocks) * B, B, cw, sf, pay, cnt, obase,
+                             ovf if ovf.size else np.zeros(1, np.uint8))
+
+
+def sample_positions(n: int):
+    """Positions floor(i * n / m), m = min(n, 4096), of a codebook's shift sample."""
+    import numpy as np
+    m = min(n, 4096)
+    return ((np.arange(m, dtype=np.uint64) * np.uint64(n)) // np.uint64(max(m, 1))).astype(np.int64)
+
+
+def cpu_baseline_leg(cpu_in, gpu_out, cbw, cbm, mw, mm, eta, lay, n):
+    """Time the oracle on the sampled blocks for the same step (encode W,
+    naive SGD round trip, decode W') and check the GPU's bytes against it."""
+    import numpy as np
+
+    import oracle
+    B, cw = lay.block_elems, lay.cap_words
+    g_enc, g_m, g_sgd, g_dec = gpu_out
+    # the oracle's own codebooks, from the model and the shift sample
+    ocw = oracle.codebook_from_sample(mw.family, mw.scale, mw.shape, cpu_in["w_sample"])
+    ocm = oracle.codebook_from_sample(mm.family, mm.scale, mm.shape, cpu_in["m_sample"])
+    same_cb = (np.array_equal(np.frombuffer(bytes(cbw.len), np.uint8), ocw.len)
+               and cbw.shift == ocw.shift and cbm.shift == ocm.shift
+               and np.array_equal(np.frombuffer(bytes(cbm.len), np.uint8), ocm.len))
+    rm = oracle.encode(ocm, cpu_in["m_blocks"], B, cw)     # set-up of M: not timed
+    t0 = time.perf_counter()
+    rw = oracle.encode(ocw, cpu_in["w_blocks"], B, cw)
+    t1 = time.perf_counter()
+    ro = oracle.sgd(ocw, rw, ocm, rm, eta)
+    t2 = time.perf_counter()
+    rd = oracle.decode(ocw, ro)
+    t3 = time.perf_counter()
+    t_oracle = t3 - t0
+
+    def same(a, b):
+        return all(np.array_equal(getattr(a, k), getattr(b, k))
+                   for k in ("sf", "pay", "cnt", "obase")) \
+            and np.array_equal(a.ovf[:a.spilled], b.ovf[:b.spilled])
+
+    parity = {"codebooks": bool(same_cb), "encode_W": bool(same(g_enc, rw)),
+              "encode_M": bool(same(g_m, rm)), "sgd_W": bool(same(g_sgd, ro)),
+              "decode_W": bool(np.array_equal(g_dec, rd))}
+    ns = len(cpu_in["blocks"]) * B
+    return {"value": float("%.4g" % (ns / t_oracle)), "unit": "elems/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d evenly spread full blocks of %d (%d elements): encode W, naive SGD "
+                      "round trip, decode W'; serial C; encode %.2f s, sgd %.2f s, decode %.2f s"
+                      % (len(cpu_in["blocks"]), n // B, ns, t1 - t0, t2 - t1, t3 - t2),
+            "parity_on_sample": parity}
+
+
+if __name__ == "__main__":
+    main()

@@ -174,6 +174,8 @@ lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_le
  * every buffer of *out (all of sf, pay, cnt, obase, status; ovf below ovf_cap).
  * If the spill exceeds out->ovf_cap, LCT_ST_OVF_FULL is set in *out->status
  * and obase[nblk] holds the capacity needed: allocate more and encode again.
+ * The fixed side (sf, pay, cnt, obase) is complete even then; ovf is never
+ * written past ovf_cap, and its content is unspecified.
  * Safe bound: ovf_cap = n.  Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS (d_x
  * overlapping an output), LCT_EARCH, LCT_EHIP. */
 lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_tensor *out,

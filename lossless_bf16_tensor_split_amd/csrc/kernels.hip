@@ -24,6 +24,8 @@
 // position) order in one pass.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "lct_internal.h"
 
 namespace lct {
@@ -604,13 +606,18 @@ __global__ __launch_bounds__(256) void k_sgd(const SgdParams p) {
     writer_finish(st, n_s, b, cap, s_opay, ocol, s_tmp, &s_ob, o);
 }
 
-constexpr int kMaxLds = 160 * 1024;
-
+// Dynamic LDS beyond 64 KiB must be requested per kernel; remember the
+// largest size granted so far so the runtime is asked only when it grows.
 template <typename K>
-int set_lds(K kernel) {
-    return (int)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+int ensure_lds(K kernel, size_t bytes, std::atomic<size_t> &granted) {
+    if (bytes <= 64 * 1024 || bytes <= granted.load()) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) granted.store(bytes);
+    return (int)e;
 }
+
+std::atomic<size_t> g_enc_lds{0}, g_dec_lds{0}, g_sgd_lds{0};
 
 }  // namespace
 
@@ -627,21 +634,21 @@ int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream
 }
 
 int launch_encode(const EncodeParams &p, void *stream) {
-    static const int attr = set_lds(k_encode);
+    const int attr = ensure_lds(k_encode, encode_lds(p.cap_words), g_enc_lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_encode, dim3(p.nblk), dim3(NS), encode_lds(p.cap_words), (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 
 int launch_decode(const DecodeParams &p, void *stream) {
-    static const int attr = set_lds(k_decode);
+    const int attr = ensure_lds(k_decode, decode_lds(p.cap_words), g_dec_lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_decode, dim3(p.nblk), dim3(NS), decode_lds(p.cap_words), (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 
 int launch_sgd(const SgdParams &p, void *stream) {
-    static const int attr = set_lds(k_sgd);
+    const int attr = ensure_lds(k_sgd, sgd_lds(p.cap_words), g_sgd_lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_sgd, dim3(p.nblk), dim3(NS), sgd_lds(p.cap_words), (hipStream_t)stream, p);
     return (int)hipGetLastError();

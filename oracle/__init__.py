@@ -193,6 +193,20 @@ def codebook_from_base(len_base, esc_len: int, shift: int) -> Codebook:
     return Codebook._from_c(cb)
 
 
+def sample_positions(n: int) -> np.ndarray:
+    """Positions floor(i * n / m), m = min(n, 4096), of the shift sample."""
+    m = min(n, 4096)
+    return (np.arange(m, dtype=np.uint64) * np.uint64(n)) // np.uint64(max(m, 1))
+
+
+def codebook_from_sample(family: int, scale: float, shape: float, sample: np.ndarray) -> Codebook:
+    """Codebook from the model and the already gathered sample (BF16 bits at
+    sample_positions(n)); same result as codebook_build on the whole tensor."""
+    lens, esc, _, _ = build_base(weights(model_pmf(family, scale, shape)))
+    e = ((np.ascontiguousarray(sample, np.uint16) >> 7) & 0xFF).astype(np.uint8)
+    return codebook_from_base(lens, esc, best_shift(lens, esc, e))
+
+
 def codebook_build(family: int, scale: float, shape: float, x: np.ndarray) -> Codebook:
     x = np.ascontiguousarray(x, np.uint16)
     cb = _Codebook()

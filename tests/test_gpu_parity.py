@@ -100,7 +100,7 @@ def test_odd_sizes(L, orc, n):
 def test_forced_overflow_many_blocks(L, orc, B, cw):
     x = synth.draw(synth.TensorSpec("w", (97 * B + 1234,), 600 + cw, "laplace", {"b": 0.01}))
     _, _, _, ref = roundtrip_case(L, orc, x, synth.Model(1, 0.01), B, cw, what="B=%d cw=%d" % (B, cw))
-    if cw < 12:
+    if 32.0 * cw * 256 / B < 3.5:      # capacity below the Laplace code's ~3 bits: must spill
         assert ref.spilled > 0
 
 
@@ -142,8 +142,11 @@ def test_ovf_capacity_status_and_guards(L, orc):
         assert int(g["obase"][-1]) == need
         assert g["status"] == (0 if cap >= need else L.ST_OVF_FULL)
         ovf = t.ovf.cpu().numpy()
-        assert np.array_equal(ovf[:cap], full.ovf[:cap])
+        # nothing is written past ovf_cap; below it the content is only
+        # specified when everything fits
         assert (ovf[cap:] == 0xA5).all()
+        if cap >= need:
+            assert np.array_equal(ovf[:need], full.ovf[:need])
         assert np.array_equal(g["pay"], full.pay) and np.array_equal(g["cnt"], full.cnt)
 
 
