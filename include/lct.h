@@ -74,7 +74,7 @@ typedef struct {
  * blocks in CLEAN, 32,768 in MEDIUM and HIGH).  cap_words is each stream's
  * capacity in 32-bit words: CLEAN 25 (16 / (8 + 800/256) = 1.4382x, the
  * bound printed for CLEAN), MEDIUM 12 (8 + 3 bits per value, 16/11), HIGH 11.
- * Any block_elems that is a multiple of 2048 in [2048, 65536] and any
+ * Any block_elems that is a multiple of 4096 in [4096, 65536] and any
  * cap_words in [1, 64] is accepted. */
 typedef enum { LCT_CLEAN = 0, LCT_MEDIUM = 1, LCT_HIGH = 2 } lct_mode;
 typedef struct {

@@ -10,19 +10,23 @@
 namespace lct {
 
 constexpr uint32_t kStreams = 256;          // streams per block
-constexpr uint32_t kChunk = 8;              // positions per stream processed per loop step
+constexpr uint32_t kChunk = 16;             // positions per stream processed per loop step
 constexpr uint32_t kMinBlock = kStreams * kChunk;
 constexpr uint32_t kMaxBlock = 65536;
 constexpr uint32_t kMaxCapWords = 64;
 
-// Scratch layout (bytes).  The header and the look-back flags are cleared by
-// a fill kernel before each encode / SGD launch; the staging area holds
-// spilled exponent fields until the block's overflow offset is known.
-constexpr uint64_t kScrTicket = 0;    // uint32: next block to hand out
+constexpr uint32_t kMaxUnits = 4;           // workgroups a block may be split over
+
+// Scratch layout (bytes).  The header, the look-back flags and the per-block
+// reader counters are cleared by a fill kernel before each encode / SGD
+// launch; the staging area holds spilled exponent fields until their
+// overflow offset is known.
+constexpr uint64_t kScrTicket = 0;    // uint32: next unit to hand out
 constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the staging area
-constexpr uint64_t kScrFlags = 64;    // uint64[nblk]: look-back descriptors
-__host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) { return (kScrFlags + 8 * nblk + 255) & ~uint64_t(255); }
-__host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) { return kScrFlags + 8 * nblk; }
+constexpr uint64_t kScrFlags = 64;    // uint64[kMaxUnits * nblk]: look-back descriptors
+__host__ __device__ inline uint64_t scr_readers_offset(uint64_t nblk) { return kScrFlags + 8 * kMaxUnits * nblk; }
+__host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) { return scr_readers_offset(nblk) + 4 * nblk; }
+__host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) { return (scr_clear_bytes(nblk) + 255) & ~uint64_t(255); }
 
 // Encoder tables: stream bits of each exponent field and their count.
 struct EncTab {
@@ -30,7 +34,8 @@ struct EncTab {
     uint8_t len[256];
 };
 
-// Decoder table: 8-bit peek -> field | bits << 8 | escape << 13 | invalid << 14.
+// Decoder table: 8-bit peek -> field | bits << 8 | escape << 13 | invalid << 14
+// (the kernels expand it in LDS).
 struct DecTab {
     uint16_t dec[256];
     uint32_t esc_len;

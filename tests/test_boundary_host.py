@@ -70,7 +70,7 @@ def test_layout_modes_and_sizes(L, orc):
         t.nblk, t.sf.nbytes, t.pay.nbytes, t.cnt.nbytes, t.obase.nbytes)
     assert sz.fixed == t.sf.nbytes + t.pay.nbytes + t.cnt.nbytes + t.obase.nbytes
     assert sz.scratch >= 1000 + 8 * t.nblk
-    for bad in [(1024, 25), (65536 + 2048, 25), (3000, 25), (65536, 0), (65536, 65)]:
+    for bad in [(1024, 25), (2048, 25), (65536 + 4096, 25), (6000, 25), (65536, 0), (65536, 65)]:
         with pytest.raises(L.LctError):
             L.lct_sizes(100, L.layout(*bad), 0)
 

@@ -91,11 +91,11 @@ def test_config1_gaussian_clean(L, orc):
 @pytest.mark.parametrize("n", [1, 255, 256, 257, 2047, 2048, 2049, 65535, 65537, 300001])
 def test_odd_sizes(L, orc, n):
     x = synth.draw(synth.TensorSpec("w", (n,), 500 + n % 89, "normal", {"sigma": 0.02}))
-    for B, cw in [(65536, 25), (2048, 2), (4096, 1)]:
+    for B, cw in [(65536, 25), (4096, 2), (4096, 1)]:
         roundtrip_case(L, orc, x, synth.Model(0, 0.02), B, cw, what="n=%d B=%d cw=%d" % (n, B, cw))
 
 
-@pytest.mark.parametrize("B,cw", [(2048, 1), (2048, 3), (4096, 2), (16384, 4), (32768, 11),
+@pytest.mark.parametrize("B,cw", [(4096, 1), (8192, 3), (4096, 2), (16384, 4), (32768, 11),
                                   (65536, 8), (65536, 64)])
 def test_forced_overflow_many_blocks(L, orc, B, cw):
     x = synth.draw(synth.TensorSpec("w", (97 * B + 1234,), 600 + cw, "laplace", {"b": 0.01}))
@@ -108,17 +108,17 @@ def test_specials_and_uniform_bits(L, orc):
     allpat = np.tile(np.arange(1 << 16, dtype=np.uint16), 3)
     ub = synth.draw(synth.TensorSpec("u", (200003,), 4002, "uniform_bits"))
     for x in [allpat, ub, np.full(70000, 0x7FC0, np.uint16), np.full(4097, 0x0001, np.uint16)]:
-        for B, cw in [(65536, 25), (32768, 12), (2048, 1)]:
+        for B, cw in [(65536, 25), (32768, 12), (4096, 1)]:
             roundtrip_case(L, orc, x, synth.Model(0, 1.0), B, cw, what="specials B=%d" % B)
 
 
 def test_repeatable_lookback(L, orc):
     """Many small blocks with spills everywhere, encoded 20 times: identical
     bytes every time (the cross-block offset scan has a single answer)."""
-    x = synth.draw(synth.TensorSpec("u", (2048 * 3000 + 17,), 77, "uniform_bits"))
+    x = synth.draw(synth.TensorSpec("u", (4096 * 1500 + 17,), 77, "uniform_bits"))
     cb, ocb = check_codebook(L, orc, synth.Model(0, 1.0), x)
-    ref = orc.encode(ocb, x, 2048, 2)
-    lay = L.layout(2048, 2)
+    ref = orc.encode(ocb, x, 4096, 2)
+    lay = L.layout(4096, 2)
     xd = dev(x)
     t = L.alloc_tensor(x.size, lay)
     for _ in range(20):
@@ -130,9 +130,9 @@ def test_repeatable_lookback(L, orc):
 def test_ovf_capacity_status_and_guards(L, orc):
     x = synth.draw(synth.TensorSpec("u", (40000,), 78, "uniform_bits"))
     cb, ocb = check_codebook(L, orc, synth.Model(0, 1.0), x)
-    full = orc.encode(ocb, x, 2048, 2)
+    full = orc.encode(ocb, x, 4096, 2)
     need = full.spilled
-    lay = L.layout(2048, 2)
+    lay = L.layout(4096, 2)
     for cap in [0, 1, need // 2, need - 1, need]:
         t = L.alloc_tensor(x.size, lay, ovf_cap=cap)
         # the ovf buffer holds 4096 guard bytes past ovf_cap
@@ -201,7 +201,7 @@ def sgd_case(L, orc, w, m, mw, mm, eta, B, cw, inplace, what=""):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-@pytest.mark.parametrize("B,cw", [(65536, 25), (2048, 2), (4096, 3), (32768, 12)])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 2), (8192, 3), (32768, 12)])
 def test_sgd_small_with_spills(L, orc, B, cw, inplace):
     g = np.random.default_rng(B + cw)
     n = 7 * B + 333
