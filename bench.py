@@ -68,6 +68,9 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=2048,
                     help="blocks in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy a buffer of this many MiB once (a plain "
+                         "device copy whose HBM bytes are known, to scale rocprofv3 byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -181,6 +184,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     assert tw.status_word() == 0 and tw2.status_word() == 0, "overflow capacity exceeded"
+
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     timed = ev[args.warmup:]
     t_enc = float(np.mean([e[0].elapsed_time(e[1]) for e in timed])) / 1e3

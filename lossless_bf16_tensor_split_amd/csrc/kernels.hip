@@ -17,6 +17,10 @@
 // stream words are interleaved (word w of stream s at w*256 + s), so a unit's
 // payload rows move between HBM and LDS with 16-byte accesses and every lane
 // works on its own column of LDS rows (a row's lanes hit distinct banks).
+// LDS holds the code tables (after 256 bytes of small shared values) and then
+// the payload rows; kernels
+// are specialised on the stream capacity of the three modes so that every LDS
+// offset is an immediate of the instruction.
 //
 // Bit reader: a code starts at stream bit q+2; the two LDS words around q give
 // a 32-bit window by one funnel shift (v_alignbit), whose bits 2..9 are the
@@ -36,10 +40,11 @@
 // order in one pass.  Fields that spill are parked in a staging area until
 // their offset is known.
 //
-// Every loop step handles 16 positions per lane and loads the next 16 ahead.
-// Full blocks whose inputs carry no spilled fields take a path with no
-// overflow reads at all; partial blocks and inputs with spills take a general
-// path with per-element checks.
+// Every loop step handles 16 positions per lane while the next 16 are loaded
+// into a second buffer (two buffers alternate, so loads are waited for one
+// step after they were issued).  Full blocks whose inputs carry no spilled fields
+// take a path with no overflow reads at all; partial blocks and inputs with
+// spills take a general path with per-element checks.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -55,6 +60,32 @@ constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kFlagVal = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 21;
+
+extern __shared__ uint32_t lds[];
+
+// The first 256 bytes of LDS hold a workgroup's small shared values; tables
+// and rows start at 256 so that every offset is a multiple of 256 (the unit
+// of the paired LDS accesses' immediate offsets).
+constexpr uint32_t kMiscTmp = 0;      // uint32[4]: per-wave scan totals
+constexpr uint32_t kMiscTicket = 16;  // uint32: the unit's ticket
+constexpr uint32_t kMiscOb = 24;      // uint64: the unit's overflow offset
+__device__ __forceinline__ uint32_t *s_tmp_ptr() { return lds + kMiscTmp / 4; }
+__device__ __forceinline__ uint32_t *s_ticket_ptr() { return lds + kMiscTicket / 4; }
+__device__ __forceinline__ uint64_t *s_ob_ptr() { return reinterpret_cast<uint64_t *>(lds + kMiscOb / 4); }
+
+// LDS accessed by byte offset.  These kernels declare no static LDS, so the
+// dynamic region starts at LDS address 0 and an offset is an address: the
+// accesses take it (plus a constant folded into the instruction) directly.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<lds_u32 *>(off); }
+__device__ __forceinline__ uint32_t ld8(uint32_t off) { return *reinterpret_cast<lds_u8 *>(off); }
+__device__ __forceinline__ void st32(uint32_t off, uint32_t v) { *reinterpret_cast<lds_u32 *>(off) = v; }
+__device__ __forceinline__ void st8(uint32_t off, uint32_t v) {
+    *reinterpret_cast<lds_u8 *>(off) = (uint8_t)v;
+}
+
+constexpr uint32_t log2c(uint32_t v) { return v <= 1 ? 0 : 1 + log2c(v / 2); }
 
 __device__ __forceinline__ uint32_t lane() { return __lane_id(); }
 
@@ -143,55 +174,57 @@ __device__ __forceinline__ uint32_t stream_len(uint32_t nb, uint32_t s) {
     return nb > s ? (nb - s + NS - 1) / NS : 0;
 }
 
-// BF16 bits from a sign-fraction byte and an exponent in bits 30..23 of e23
-// (other bits of e23 are ignored): sign to bit 15, fraction to bits 6..0.
-__device__ __forceinline__ uint32_t join16(uint32_t sf, uint32_t e23) {
-    const uint32_t sfx = sf * 0x101u;
-    return (sfx & 0x807Fu) | ((e23 >> 16) & 0x7F80u);
+// Sign-fraction byte of BF16 bits v: sign (bit 15) to bit 7, fraction kept.
+__device__ __forceinline__ uint32_t sf_of(uint32_t v) {
+    return (v & 0x7Fu) | ((v >> 8) & ~0x7Fu);
 }
 
 // fp32 bits of the BF16 value (sf, e): sf in bytes 3 and 2, e in 30..23.
 __device__ __forceinline__ uint32_t join32(uint32_t sf, uint32_t e23) {
     const uint32_t sfx = __builtin_amdgcn_perm(0u, sf, 0x00000C0Cu);
-    return (sfx & 0x807FFFFFu) | (e23 & 0x7F800000u);
+    return (sfx & 0x807FFFFFu) | (e23 & ~0x807FFFFFu);
 }
 
 // ------------------------------------------------------------------ code tables in LDS
 
-// Decode table, indexed by peek*4: e << 23 | bits consumed, and a mask that
-// selects the literal field (escape codes).
-__device__ __forceinline__ void stage_dec(const DecTab &t, uint32_t *ent, uint32_t *msk) {
+// Decode table at byte offset `ent` (and its escape masks at `msk`), indexed
+// by peek*4: e << 23 | bits consumed; the mask selects the literal field.
+__device__ __forceinline__ void stage_dec(const DecTab &t, uint32_t ent, uint32_t msk) {
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
         const uint32_t d = t.dec[i];
-        ent[i] = ((d & 0xFFu) << 23) | ((d >> 8) & 0x1Fu);
-        msk[i] = (d >> 13) & 1u ? 0x7F800000u : 0u;
+        st32(ent + 4 * i, ((d & 0xFFu) << 23) | ((d >> 8) & 0x1Fu));
+        st32(msk + 4 * i, (d >> 13) & 1u ? 0x7F800000u : 0u);
     }
 }
 
-__device__ __forceinline__ void stage_enc(const EncTab &t, uint32_t *bits, uint8_t *len) {
+// Encode tables: stream bits (u32, at `bits`) and their count (u8, at `len`).
+__device__ __forceinline__ void stage_enc(const EncTab &t, uint32_t bits, uint32_t len) {
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
-        bits[i] = t.bits[i];
-        len[i] = t.len[i];
+        st32(bits + 4 * i, t.bits[i]);
+        st8(len + i, t.len[i]);
     }
 }
 
 // ------------------------------------------------------------------ stream reader
 
-template <uint32_t SW>
+// ROWB: bytes per LDS row.  Offsets are relative to the region's row 0.
+template <uint32_t ROWB>
 struct Reader {
+    static constexpr uint32_t kSh = log2c(ROWB) - 5;
     int32_t q;   // stream bit position of the next code, minus 2
 
     __device__ __forceinline__ void init() { q = -2; }
     // Next exponent field in bits 30..23 of the result (other bits garbage).
-    // col: this stream's word in row 0; rows -1 and `cap` are zero.
-    __device__ __forceinline__ uint32_t next(const uint32_t *col, const uint32_t *ent,
-                                             const uint32_t *msk, uint32_t litsh) {
-        const uint32_t *p = col + (q >> 5) * (int32_t)SW;
-        const uint32_t a = p[0], b = p[SW];
+    // row0: LDS offset of row 0; tcol: this lane's column (bytes); rows -1
+    // and `cap` are zero.
+    __device__ __forceinline__ uint32_t next(uint32_t row0, uint32_t tcol, uint32_t ent,
+                                             uint32_t msk, uint32_t litsh) {
+        const uint32_t off = (((uint32_t)q << kSh) & ~(ROWB - 1)) | tcol;
+        const uint32_t a = ld32(row0 + off), b = ld32(row0 + off + ROWB);
         const uint32_t win = __builtin_amdgcn_alignbit(b, a, (uint32_t)q);
         const uint32_t k = win & 0x3FCu;
-        const uint32_t en = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(ent) + k);
-        const uint32_t mk = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(msk) + k);
+        const uint32_t en = ld32(ent + k);
+        const uint32_t mk = ld32(msk + k);
         q += en & 0xFFu;
         return ((win << litsh) & mk) | en;
     }
@@ -199,21 +232,23 @@ struct Reader {
 
 // ------------------------------------------------------------------ stream writer
 
-template <uint32_t SW>
+template <uint32_t ROWB>
 struct Writer {
-    static constexpr uint32_t kRowShift = SW == 256 ? 10 : SW == 128 ? 9 : 8;   // log2(row bytes)
+    static constexpr uint32_t kSh = log2c(ROWB) - 5;
     uint64_t buf;     // pending bits, LSB first (< 32 at every store step)
     uint32_t used;    // bits in buf
-    uint32_t *wp;     // LDS word of this stream being filled
+    uint32_t woff;    // row * ROWB + this lane's column, relative to row 0
+    uint32_t tadj;    // column >> kSh, so that total() = (woff >> kSh) - tadj + used
     uint32_t live;    // no field has failed to fit yet
     uint32_t cs;      // coded prefix length
     uint32_t claimed; // staging space claimed for the spilled fields
     uint64_t soff;    // start of this stream's spilled fields in the staging area
 
-    __device__ __forceinline__ void init(uint32_t *col0, uint32_t n_s) {
+    __device__ __forceinline__ void init(uint32_t tcol, uint32_t n_s) {
         buf = 0;
         used = 0;
-        wp = col0;
+        woff = tcol;
+        tadj = tcol >> kSh;
         live = 1;
         cs = n_s;
         claimed = 0;
@@ -225,38 +260,35 @@ struct Writer {
     }
     // Store both words of the buffer at the current row and the next; move
     // on by a word when the first is full.
-    __device__ __forceinline__ void flush() {
-        wp[0] = (uint32_t)buf;
-        wp[SW] = (uint32_t)(buf >> 32);
+    __device__ __forceinline__ void flush(uint32_t row0) {
+        st32(row0 + woff, (uint32_t)buf);
+        st32(row0 + woff + ROWB, (uint32_t)(buf >> 32));
         const uint32_t t = used & 32u;
         buf >>= t;
-        wp = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(wp) + (t << (kRowShift - 5)));
+        woff += t << kSh;
         used &= 31u;
     }
-    __device__ __forceinline__ uint32_t total(const uint32_t *col0) const {
-        return (uint32_t)((reinterpret_cast<const char *>(wp) - reinterpret_cast<const char *>(col0)) >>
-                          (kRowShift - 5)) + used;
-    }
+    __device__ __forceinline__ uint32_t total() const { return (woff >> kSh) - tadj + used; }
 };
 
 // Code the CH fields e[] at positions j0..j0+CH-1; with CHECKED, positions at
 // or past n_s are absent.  One capacity test per step in the common case.
-template <uint32_t SW, bool CHECKED>
-__device__ __forceinline__ void writer_chunk(Writer<SW> &st, const uint32_t (&e)[CH], uint32_t j0,
-                                             uint32_t n_s, uint32_t capbits, const uint32_t *ebits,
-                                             const uint8_t *elen, const uint32_t *col0) {
+template <uint32_t ROWB, bool CHECKED>
+__device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&e)[CH], uint32_t j0,
+                                             uint32_t n_s, uint32_t capbits, uint32_t ebits,
+                                             uint32_t elen, uint32_t row0) {
     uint32_t cb[CH], cl[CH];
 #pragma unroll
     for (uint32_t i = 0; i < CH; ++i) {
-        cb[i] = ebits[e[i]];
-        cl[i] = elen[e[i]];
+        cb[i] = ld32(ebits + 4 * e[i]);
+        cl[i] = ld8(elen + e[i]);
         if (CHECKED && j0 + i >= n_s) {
             cb[i] = 0;
             cl[i] = 0;
         }
     }
     if (!st.live) return;
-    const uint32_t tot = st.total(col0);
+    const uint32_t tot = st.total();
     bool fits = tot + CH * 16 <= capbits;
     if (!fits) {
         uint32_t sum = 0;
@@ -269,15 +301,15 @@ __device__ __forceinline__ void writer_chunk(Writer<SW> &st, const uint32_t (&e)
         for (uint32_t k = 0; k < CH; k += 2) {
             st.put(cb[k], cl[k]);
             st.put(cb[k + 1], cl[k + 1]);
-            st.flush();
+            st.flush(row0);
         }
     } else {
 #pragma unroll
         for (uint32_t i = 0; i < CH; ++i) {
             if (st.live) {
-                if (st.total(col0) + cl[i] <= capbits) {
+                if (st.total() + cl[i] <= capbits) {
                     st.put(cb[i], cl[i]);
-                    st.flush();
+                    st.flush(row0);
                 } else {
                     st.live = 0;
                     st.cs = j0 + i;
@@ -290,8 +322,8 @@ __device__ __forceinline__ void writer_chunk(Writer<SW> &st, const uint32_t (&e)
 // Claim staging space for streams that started spilling in this step (one
 // atomic per wave), then park this step's spilled fields there.  Every lane of
 // the wave must reach it.
-template <uint32_t SW, bool CHECKED>
-__device__ __forceinline__ void writer_spill(Writer<SW> &st, const uint32_t (&e)[CH], uint32_t j0,
+template <uint32_t ROWB, bool CHECKED>
+__device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&e)[CH], uint32_t j0,
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
@@ -331,21 +363,22 @@ struct UnitOut {
     uint32_t nblk, nunits, cap;
 };
 
-// After the stream loop: the unit's payload rows, the overflow offset
-// (look-back) and the spilled fields, then counts and the block's marker.
-// `before` runs just before cnt / obase are written (the fused update waits
-// there until the block's other units have read theirs).
+// After the stream loop: the unit's payload rows (LDS rows of SW words from
+// byte offset row0), the overflow offset (look-back) and the spilled fields,
+// then counts and the block's marker.  `before` runs just before cnt / obase
+// are written (the fused update waits there until the block's other units
+// have read theirs).
 template <uint32_t SW, typename Before>
-__device__ void writer_finish(Writer<SW> &st, uint32_t n_s, uint32_t u, uint32_t b, uint32_t h,
-                              const uint32_t *s_out, uint32_t *s_tmp, uint64_t *s_ob,
+__device__ void writer_finish(uint32_t cs, uint64_t soff, uint32_t n_s, uint32_t u, uint32_t b,
+                              uint32_t h, uint32_t row0, uint32_t *s_tmp, uint64_t *s_ob,
                               const UnitOut &o, Before before) {
     const uint32_t t = threadIdx.x;
-    const uint32_t spill = n_s - st.cs;
+    const uint32_t spill = n_s - cs;
     uint32_t total;
     const uint32_t excl = group_excl_scan<SW>(spill, s_tmp, total);   // barriers: LDS rows complete
     // payload: cap rows of SW words (16-byte pieces)
     constexpr uint32_t Q = SW / 4;
-    const uint4 *src = reinterpret_cast<const uint4 *>(s_out);
+    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(lds) + row0);
     uint4 *dst = reinterpret_cast<uint4 *>(o.pay);
     for (uint32_t i = t; i < o.cap * Q; i += SW) {
         const uint32_t row = i / Q, c = i % Q;
@@ -361,12 +394,12 @@ __device__ void writer_finish(Writer<SW> &st, uint32_t n_s, uint32_t u, uint32_t
     if (spill) {
         const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
         for (uint32_t k = 0; k < spill; ++k) {
-            const uint64_t from = st.soff + k, to = ob + excl + k;
+            const uint64_t from = soff + k, to = ob + excl + k;
             if (from < o.ovf_cap && to < o.ovf_cap) o.ovf[to] = stage[from];
         }
     }
     before();
-    o.cnt[(uint64_t)b * NS + h * SW + t] = (uint16_t)st.cs;
+    o.cnt[(uint64_t)b * NS + h * SW + t] = (uint16_t)cs;
     if (t == 0) {
         if (h == 0) o.obase[b] = ob;
         if (u == o.nunits - 1) {
@@ -377,12 +410,12 @@ __device__ void writer_finish(Writer<SW> &st, uint32_t n_s, uint32_t u, uint32_t
 }
 
 // Copy rows [0, cap) of a unit's columns of a block's payload into LDS rows of
-// SW words.
+// SW words from byte offset row0.
 template <uint32_t SW>
 __device__ __forceinline__ void stage_rows(const uint32_t *pay, uint64_t b, uint32_t h, uint32_t cap,
-                                           uint32_t *dst_row0) {
+                                           uint32_t row0) {
     constexpr uint32_t Q = SW / 4;
-    uint4 *dst = reinterpret_cast<uint4 *>(dst_row0);
+    uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) + row0);
     const uint4 *src = reinterpret_cast<const uint4 *>(pay);
     for (uint32_t i = threadIdx.x; i < cap * Q; i += SW) {
         const uint32_t row = i / Q, c = i % Q;
@@ -431,60 +464,88 @@ __global__ void k_gather(const uint16_t *x, uint64_t n, uint32_t m) {
     if (i < m) g_sample[i] = x[(uint64_t)i * n / m];
 }
 
+// ------------------------------------------------------------------ step driver
+
+// Positions [j0, j0+CH) of one lane's stream from base (the lane's position 0,
+// positions NS apart); with GUARD, positions at or past n_s read as 0.
+template <bool GUARD, typename T>
+__device__ __forceinline__ void load_chunk(uint32_t (&dst)[CH], const T *base, uint32_t j0,
+                                           uint32_t n_s) {
+    const T *p = base + (size_t)j0 * NS;
+#pragma unroll
+    for (uint32_t i = 0; i < CH; ++i) dst[i] = (!GUARD || j0 + i < n_s) ? (uint32_t)p[i * NS] : 0u;
+}
+
+// Runs step(buf, j0) over the positions of a stream, CH at a time, with the
+// next step's inputs loaded (load(buf, j0)) while the current one works.  Two
+// buffers alternate, so no value is copied between steps and the waits for a
+// load fall one step after it was issued.  The load for the step past the end
+// re-reads the last step's positions.
+template <typename Buf, typename Load, typename Step>
+__device__ __forceinline__ void double_buffered(uint32_t npos, Load load, Step step) {
+    Buf a, b;
+    load(a, 0u);
+    for (uint32_t j0 = 0; j0 < npos; j0 += 2 * CH) {
+        load(b, min(j0 + CH, npos - CH));
+        step(a, j0);
+        if (j0 + CH >= npos) break;
+        load(a, min(j0 + 2 * CH, npos - CH));
+        step(b, j0 + CH);
+    }
+}
+
+struct Buf1 {
+    uint32_t v[CH];
+};
+struct Buf2 {
+    uint32_t w[CH], m[CH];
+};
+
 // ------------------------------------------------------------------ encode
 
-constexpr uint32_t kEncH = 1, kEncSW = NS / kEncH;
+constexpr uint32_t kEncH = 1, kEncSW = NS / kEncH, kEncRowB = kEncSW * 4;
+// LDS: bits table, lengths, then the output rows (cap + 2 sink rows).
+constexpr uint32_t kEncBits = 256, kEncLen = 1280, kEncRow0 = 1536;
 
-template <bool FULL>
-__device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer<kEncSW> &st,
-                                              uint32_t n_s, uint64_t r0, const uint32_t *ebits,
-                                              const uint8_t *elen, const uint32_t *col0) {
+template <uint32_t CAPT>
+__device__ __forceinline__ uint32_t cap_of(uint32_t rt) { return CAPT ? CAPT : rt; }
+
+template <bool FULL, uint32_t CAPT>
+__device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer<kEncRowB> &st,
+                                              uint32_t n_s, uint64_t r0) {
     const uint32_t s = threadIdx.x;
     const uint32_t npos = p.block_elems / NS;
-    const uint32_t capbits = 32 * p.cap_words;
+    const uint32_t capbits = 32 * cap_of<CAPT>(p.cap_words);
     const uint16_t *xs = p.x + r0 + s;
     uint8_t *sfs = p.sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    uint32_t v[CH], vn[CH];
-#pragma unroll
-    for (uint32_t i = 0; i < CH; ++i) v[i] = (FULL || i < n_s) ? xs[i * NS] : 0;
-    for (uint32_t j0 = 0; j0 < npos; j0 += CH) {
-        if (j0 + CH < npos) {
+    double_buffered<Buf1>(
+        npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FULL>(bf.v, xs, j0, n_s); },
+        [&](Buf1 &bf, uint32_t j0) {
+            uint32_t e[CH];
+            uint8_t *o = sfs + (size_t)j0 * NS;
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + CH + i;
-                vn[i] = (FULL || j < n_s) ? xs[j * NS] : 0;
+                e[i] = (bf.v[i] >> 7) & 0xFFu;
+                if (FULL || j0 + i < n_s) o[i * NS] = (uint8_t)sf_of(bf.v[i]);
             }
-        }
-        uint32_t e[CH];
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            e[i] = (v[i] >> 7) & 0xFFu;
-            if (FULL || j0 + i < n_s)
-                sfs[(j0 + i) * NS] = (uint8_t)(((v[i] >> 8) & 0x80u) | (v[i] & 0x7Fu));
-        }
-        writer_chunk<kEncSW, !FULL>(st, e, j0, n_s, capbits, ebits, elen, col0);
-        writer_spill<kEncSW, !FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) v[i] = vn[i];
-    }
+            writer_chunk<kEncRowB, !FULL>(st, e, j0, n_s, capbits, kEncBits, kEncLen, kEncRow0);
+            writer_spill<kEncRowB, !FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
+        });
 }
 
+template <uint32_t CAPT>
 __global__ __launch_bounds__(256) void k_encode(const EncodeParams p) {
-    extern __shared__ uint32_t lds[];
-    __shared__ uint32_t s_tmp[4];
-    __shared__ uint32_t s_ticket;
-    __shared__ uint64_t s_ob;
+    uint32_t *s_tmp = s_tmp_ptr();
+    uint32_t &s_ticket = *s_ticket_ptr();
+    uint64_t &s_ob = *s_ob_ptr();
     constexpr uint32_t SW = kEncSW;
     const uint32_t t = threadIdx.x;
-    const uint32_t cap = p.cap_words;
-    uint32_t *s_out = lds;                                    // cap rows + 2 sink rows
-    uint32_t *s_bits = lds + (cap + 2) * SW;                  // 256 words
-    uint8_t *s_len = reinterpret_cast<uint8_t *>(s_bits + 256);
-    stage_enc(p.enc, s_bits, s_len);
-    uint32_t *col0 = s_out + t;
-    for (uint32_t w = 0; w < cap; ++w) col0[w * SW] = 0;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    stage_enc(p.enc, kEncBits, kEncLen);
+    const uint32_t tcol = 4 * t;
+    for (uint32_t w = 0; w < cap; ++w) st32(kEncRow0 + w * kEncRowB + tcol, 0);
     if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
     __syncthreads();
     const uint32_t u = s_ticket;
@@ -494,72 +555,65 @@ __global__ __launch_bounds__(256) void k_encode(const EncodeParams p) {
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
     const uint32_t n_s = stream_len(nb, h * SW + t);
-    Writer<SW> st;
-    st.init(col0, n_s);
+    Writer<kEncRowB> st;
+    st.init(tcol, n_s);
     if (nb == p.block_elems)
-        encode_stream<true>(p, st, n_s, r0 + h * SW, s_bits, s_len, col0);
+        encode_stream<true, CAPT>(p, st, n_s, r0 + h * SW);
     else
-        encode_stream<false>(p, st, n_s, r0 + h * SW, s_bits, s_len, col0);
+        encode_stream<false, CAPT>(p, st, n_s, r0 + h * SW);
     const UnitOut o{p.pay, p.cnt, p.obase, p.ovf, p.ovf_cap, p.status, p.scratch,
                     p.nblk, nunits, cap};
-    writer_finish<SW>(st, n_s, u, b, h, s_out, s_tmp, &s_ob, o, [] {});
+    writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, kEncRow0, s_tmp, &s_ob, o, [] {});
 }
 
 // ------------------------------------------------------------------ decode
 
-template <bool FAST>
+// LDS: decode table, escape masks, zero row -1, rows 0..cap-1, zero row cap.
+constexpr uint32_t kDecRowB = NS * 4;
+constexpr uint32_t kDecEnt = 256, kDecMsk = 1280, kDecRowM1 = 2304, kDecRow0 = 2304 + kDecRowB;
+
+template <bool FAST, uint32_t CAPT>
 __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_s, uint32_t c_s,
-                                              uint64_t r0, uint64_t sp0, const uint32_t *col,
-                                              const uint32_t *ent, const uint32_t *msk) {
+                                              uint64_t r0, uint64_t sp0) {
     const uint32_t s = threadIdx.x;
+    const uint32_t tcol = 4 * s;
     const uint32_t npos = p.block_elems / NS;
-    const int32_t qmax = 32 * (int32_t)p.cap_words - 2;
+    const int32_t qmax = 32 * (int32_t)cap_of<CAPT>(p.cap_words) - 2;
     const uint32_t litsh = 21 - p.dec.esc_len;
     const uint8_t *sfs = p.sf + r0 + s;
     uint16_t *ys = p.y + r0 + s;
-    Reader<NS> rd;
+    Reader<kDecRowB> rd;
     rd.init();
-    uint32_t f[CH], fn[CH];
-#pragma unroll
-    for (uint32_t i = 0; i < CH; ++i) f[i] = (FAST || i < n_s) ? sfs[i * NS] : 0;
-    for (uint32_t j0 = 0; j0 < npos; j0 += CH) {
-        if (j0 + CH < npos) {
+    double_buffered<Buf1>(
+        npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FAST>(bf.v, sfs, j0, n_s); },
+        [&](Buf1 &bf, uint32_t j0) {
+            uint16_t *o = ys + (size_t)j0 * NS;
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + CH + i;
-                fn[i] = (FAST || j < n_s) ? sfs[j * NS] : 0;
-            }
-        }
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            const uint32_t j = j0 + i;
-            uint32_t e23 = rd.next(col, ent, msk, litsh);
-            if (!FAST) {
-                rd.q = min(rd.q, qmax);
-                if (j >= c_s && j < n_s) {
-                    const uint64_t k = sp0 + (j - c_s);
-                    e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
+                const uint32_t j = j0 + i;
+                uint32_t e23 = rd.next(kDecRow0, tcol, kDecEnt, kDecMsk, litsh);
+                if (!FAST) {
+                    rd.q = min(rd.q, qmax);
+                    if (j >= c_s && j < n_s) {
+                        const uint64_t k = sp0 + (j - c_s);
+                        e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
+                    }
                 }
+                // the BF16 value is the top half of its fp32 form
+                if (FAST || j < n_s) o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
             }
-            if (FAST || j < n_s) ys[j * NS] = (uint16_t)join16(f[i], e23);
-        }
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) f[i] = fn[i];
-    }
+        });
 }
 
+template <uint32_t CAPT>
 __global__ __launch_bounds__(256) void k_decode(const DecodeParams p) {
-    extern __shared__ uint32_t lds[];
-    __shared__ uint32_t s_tmp[4];
+    uint32_t *s_tmp = s_tmp_ptr();
     const uint32_t t = threadIdx.x, b = blockIdx.x;
-    const uint32_t cap = p.cap_words;
-    uint32_t *s_in = lds + NS;                                // row -1 at lds, rows 0..cap-1, row cap
-    uint32_t *s_ent = lds + (cap + 2) * NS;
-    uint32_t *s_msk = s_ent + 256;
-    stage_dec(p.dec, s_ent, s_msk);
-    stage_rows<NS>(p.pay, b, 0, cap, s_in);
-    lds[t] = 0;
-    s_in[cap * NS + t] = 0;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    stage_dec(p.dec, kDecEnt, kDecMsk);
+    stage_rows<NS>(p.pay, b, 0, cap, kDecRow0);
+    st32(kDecRowM1 + 4 * t, 0);
+    st32(kDecRow0 + cap * kDecRowB + 4 * t, 0);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
     const uint32_t n_s = stream_len(nb, t);
@@ -567,14 +621,34 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeParams p) {
     block_spills<NS, 1>(p.cnt + (uint64_t)b * NS, nb, 0, s_tmp, c_s, excl, total);  // barriers
     const uint64_t sp0 = p.obase[b] + excl;
     if (nb == p.block_elems && total == 0)
-        decode_stream<true>(p, n_s, c_s, r0, sp0, s_in + t, s_ent, s_msk);
+        decode_stream<true, CAPT>(p, n_s, c_s, r0, sp0);
     else
-        decode_stream<false>(p, n_s, c_s, r0, sp0, s_in + t, s_ent, s_msk);
+        decode_stream<false, CAPT>(p, n_s, c_s, r0, sp0);
 }
 
 // ------------------------------------------------------------------ fused SGD
 
-constexpr uint32_t kSgdH = 2, kSgdSW = NS / kSgdH;
+constexpr uint32_t kSgdH = 2, kSgdSW = NS / kSgdH, kSgdRowB = kSgdSW * 4;
+// LDS: W and M decode tables and masks, W encode bits and lengths, then rows.
+constexpr uint32_t kSgdWEnt = 256, kSgdWMsk = 1280, kSgdMEnt = 2304, kSgdMMsk = 3328;
+constexpr uint32_t kSgdBits = 4352, kSgdLen = 5376, kSgdRows = 5632;
+
+// Rows (kSgdRowB bytes each): the output's rows 0..cap-1 and its two sink
+// rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row cap and M's
+// row -1); M's rows; a zero row.  With cap >= 18 the output's sink rows are
+// W's row -1 and row 0: a stream's output reaches row cap-1 only after
+// 2*(cap-1) >= 34 fields, when its own W reader has left rows -1 and 0.
+struct SgdLayout {
+    uint32_t out0, z0, w0, z1, m0, z2, end;
+    __host__ __device__ constexpr SgdLayout(uint32_t cap)
+        : out0(kSgdRows),
+          z0(kSgdRows + (cap >= 18 ? cap : cap + 2) * kSgdRowB),
+          w0(z0 + kSgdRowB),
+          z1(w0 + cap * kSgdRowB),
+          m0(z1 + kSgdRowB),
+          z2(m0 + cap * kSgdRowB),
+          end(z2 + kSgdRowB) {}
+};
 
 // One element: rne_bf16(fmaf(-eta, m, w)) in bits 31..16 of the result (bits
 // 15..0 hold rounding garbage); a NaN gives 0x7FC0.
@@ -587,18 +661,16 @@ __device__ __forceinline__ uint32_t sgd_round(uint32_t wf, uint32_t mf, float ne
     return R;
 }
 
-template <bool FAST>
-__device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdSW> &st, uint32_t n_s,
+template <bool FAST, uint32_t CAPT>
+__device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdRowB> &st, uint32_t n_s,
                                            uint32_t cw_s, uint32_t cm_s, uint64_t r0, uint64_t wsp,
-                                           uint64_t msp, const uint32_t *wcol, const uint32_t *mcol,
-                                           const uint32_t *went, const uint32_t *wmsk,
-                                           const uint32_t *ment, const uint32_t *mmsk,
-                                           const uint32_t *ebits, const uint8_t *elen,
-                                           const uint32_t *ocol0) {
-    constexpr uint32_t SW = kSgdSW;
+                                           uint64_t msp) {
     const uint32_t s = threadIdx.x;
+    const uint32_t tcol = 4 * s;
     const uint32_t npos = p.block_elems / NS;
-    const uint32_t capbits = 32 * p.cap_words;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const SgdLayout lay(cap);
+    const uint32_t capbits = 32 * cap;
     const int32_t qmax = (int32_t)capbits - 2;
     const uint32_t wlit = 21 - p.wdec.esc_len, mlit = 21 - p.mdec.esc_len;
     const uint8_t *wsf = p.w_sf + r0 + s;
@@ -606,99 +678,72 @@ __device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdSW> &s
     uint8_t *osf = p.o_sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    Reader<SW> rw, rm;
+    Reader<kSgdRowB> rw, rm;
     rw.init();
     rm.init();
-    uint32_t fw[CH], fm[CH], fwn[CH], fmn[CH];
-#pragma unroll
-    for (uint32_t i = 0; i < CH; ++i) {
-        fw[i] = (FAST || i < n_s) ? wsf[i * NS] : 0;
-        fm[i] = (FAST || i < n_s) ? msf[i * NS] : 0;
-    }
-    for (uint32_t j0 = 0; j0 < npos; j0 += CH) {
-        if (j0 + CH < npos) {
+    double_buffered<Buf2>(
+        npos,
+        [&](Buf2 &bf, uint32_t j0) {
+            load_chunk<!FAST>(bf.w, wsf, j0, n_s);
+            load_chunk<!FAST>(bf.m, msf, j0, n_s);
+        },
+        [&](Buf2 &bf, uint32_t j0) {
+            uint32_t e[CH];
+            uint8_t *o = osf + (size_t)j0 * NS;
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + CH + i;
-                fwn[i] = (FAST || j < n_s) ? wsf[j * NS] : 0;
-                fmn[i] = (FAST || j < n_s) ? msf[j * NS] : 0;
-            }
-        }
-        uint32_t e[CH];
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            const uint32_t j = j0 + i;
-            uint32_t ew = rw.next(wcol, went, wmsk, wlit);
-            uint32_t em = rm.next(mcol, ment, mmsk, mlit);
-            if (!FAST) {
-                rw.q = min(rw.q, qmax);
-                rm.q = min(rm.q, qmax);
-                if (j >= cw_s && j < n_s) {
-                    const uint64_t k = wsp + (j - cw_s);
-                    ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                const uint32_t j = j0 + i;
+                uint32_t ew = rw.next(lay.w0, tcol, kSgdWEnt, kSgdWMsk, wlit);
+                uint32_t em = rm.next(lay.m0, tcol, kSgdMEnt, kSgdMMsk, mlit);
+                if (!FAST) {
+                    rw.q = min(rw.q, qmax);
+                    rm.q = min(rm.q, qmax);
+                    if (j >= cw_s && j < n_s) {
+                        const uint64_t k = wsp + (j - cw_s);
+                        ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                    }
+                    if (j >= cm_s && j < n_s) {
+                        const uint64_t k = msp + (j - cm_s);
+                        em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                    }
                 }
-                if (j >= cm_s && j < n_s) {
-                    const uint64_t k = msp + (j - cm_s);
-                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                }
+                const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.neg_eta);
+                // sign-fraction byte of the result: the sign (bit 31) goes to
+                // bit 23, then bits 23..16 are stored
+                const uint32_t sfr = (R & ~0x00800000u) | ((R >> 8) & 0x00800000u);
+                if (FAST || j < n_s) o[i * NS] = (uint8_t)(sfr >> 16);
+                e[i] = (R >> 23) & 0xFFu;
             }
-            const uint32_t R = sgd_round(join32(fw[i], ew), join32(fm[i], em), p.neg_eta);
-            // sign-fraction byte of the result: move the sign (bit 31) to bit
-            // 23, then store bits 23..16
-            const uint32_t sfr = (R & ~0x00800000u) | ((R >> 8) & 0x00800000u);
-            if (FAST || j < n_s) osf[j * NS] = (uint8_t)(sfr >> 16);
-            e[i] = (R >> 23) & 0xFFu;
-        }
-        writer_chunk<SW, !FAST>(st, e, j0, n_s, capbits, ebits, elen, ocol0);
-        writer_spill<SW, !FAST>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            fw[i] = fwn[i];
-            fm[i] = fmn[i];
-        }
-    }
+            writer_chunk<kSgdRowB, !FAST>(st, e, j0, n_s, capbits, kSgdBits, kSgdLen, lay.out0);
+            writer_spill<kSgdRowB, !FAST>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
+        });
 }
 
+template <uint32_t CAPT>
 __global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
-    extern __shared__ uint32_t lds[];
-    __shared__ uint32_t s_tmp[4];
-    __shared__ uint32_t s_ticket;
-    __shared__ uint64_t s_ob;
+    uint32_t *s_tmp = s_tmp_ptr();
+    uint32_t &s_ticket = *s_ticket_ptr();
+    uint64_t &s_ob = *s_ob_ptr();
     constexpr uint32_t SW = kSgdSW, H = kSgdH;
     const uint32_t t = threadIdx.x;
-    const uint32_t cap = p.cap_words;
-    // LDS rows (SW words each): the output's rows 0..cap-1 and its two sink
-    // rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row cap and M's
-    // row -1); M's rows; a zero row.  With cap >= 18 the output's sink rows
-    // are W's row -1 and row 0: a stream's output reaches row cap-1 only after
-    // 2*(cap-1) >= 34 fields, when its own W reader has left rows -1 and 0.
-    const bool alias = cap >= 18;
-    uint32_t *s_out = lds;
-    uint32_t *z0 = lds + (alias ? cap : cap + 2) * SW;
-    uint32_t *s_w = z0 + SW;
-    uint32_t *z1 = s_w + cap * SW;
-    uint32_t *s_m = z1 + SW;
-    uint32_t *z2 = s_m + cap * SW;
-    uint32_t *tabs = z2 + SW;
-    uint32_t *went = tabs, *wmsk = tabs + 256, *ment = tabs + 512, *mmsk = tabs + 768;
-    uint32_t *ebits = tabs + 1024;
-    uint8_t *elen = reinterpret_cast<uint8_t *>(tabs + 1280);
-    stage_dec(p.wdec, went, wmsk);
-    stage_dec(p.mdec, ment, mmsk);
-    stage_enc(p.wenc, ebits, elen);
+    const uint32_t tcol = 4 * t;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const SgdLayout lay(cap);
+    stage_dec(p.wdec, kSgdWEnt, kSgdWMsk);
+    stage_dec(p.mdec, kSgdMEnt, kSgdMMsk);
+    stage_enc(p.wenc, kSgdBits, kSgdLen);
     if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
     __syncthreads();
     const uint32_t u = s_ticket;
     const uint32_t nunits = p.nblk * H;
     if (u >= nunits) return;   // only if the scratch header was not cleared
     const uint32_t b = u / H, h = u % H;
-    stage_rows<SW>(p.w_pay, b, h, cap, s_w);
-    stage_rows<SW>(p.m_pay, b, h, cap, s_m);
-    z0[t] = 0;
-    z1[t] = 0;
-    z2[t] = 0;
-    uint32_t *ocol0 = s_out + t;
-    for (uint32_t w = 0; w < cap; ++w) ocol0[w * SW] = 0;
+    stage_rows<SW>(p.w_pay, b, h, cap, lay.w0);
+    stage_rows<SW>(p.m_pay, b, h, cap, lay.m0);
+    st32(lay.z0 + tcol, 0);
+    st32(lay.z1 + tcol, 0);
+    st32(lay.z2 + tcol, 0);
+    for (uint32_t w = 0; w < cap; ++w) st32(lay.out0 + w * kSgdRowB + tcol, 0);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
     const uint32_t n_s = stream_len(nb, h * SW + t);
@@ -710,18 +755,17 @@ __global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
     uint32_t *readers = reinterpret_cast<uint32_t *>(p.scratch + scr_readers_offset(p.nblk));
     __syncthreads();
     if (t == 0) __hip_atomic_fetch_add(&readers[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    Writer<SW> st;
-    st.init(ocol0, n_s);
+    Writer<kSgdRowB> st;
+    st.init(tcol, n_s);
     if (nb == p.block_elems && wtot == 0 && mtot == 0)
-        sgd_stream<true>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp, s_w + t, s_m + t, went,
-                         wmsk, ment, mmsk, ebits, elen, ocol0);
+        sgd_stream<true, CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
     else
-        sgd_stream<false>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp, s_w + t, s_m + t, went,
-                          wmsk, ment, mmsk, ebits, elen, ocol0);
+        sgd_stream<false, CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
     const UnitOut o{p.o_pay, p.o_cnt, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.scratch,
                     p.nblk, nunits, cap};
     uint32_t *status = p.status;
-    writer_finish<SW>(st, n_s, u, b, h, s_out, s_tmp, &s_ob, o, [readers, b, status, t] {
+    writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, lay.out0, s_tmp, &s_ob, o,
+                      [readers, b, status, t] {
         // counts and offsets of W may be this block's own buffers: wait until
         // every unit of the block has read them (they all hold tickets, so
         // they are running, and they read before anything else)
@@ -741,25 +785,52 @@ __global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
 
 // Dynamic LDS beyond 64 KiB must be requested per kernel; remember the
 // largest size granted so far so the runtime is asked only when it grows.
-template <typename K>
-int ensure_lds(K kernel, size_t bytes, std::atomic<size_t> &granted) {
+int ensure_lds(const void *kernel, size_t bytes, std::atomic<size_t> &granted) {
     if (bytes <= 64 * 1024 || bytes <= granted.load()) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)bytes);
     if (e == hipSuccess) granted.store(bytes);
     return (int)e;
 }
 
-std::atomic<size_t> g_enc_lds{0}, g_dec_lds{0}, g_sgd_lds{0};
+// The capacities of the three modes get their own kernels; others run the
+// kernel that reads the capacity at run time.
+template <template <uint32_t> class K>
+struct ByCap {
+    static const void *pick(uint32_t cap) {
+        switch (cap) {
+        case 25: return K<25>::fn();
+        case 12: return K<12>::fn();
+        case 11: return K<11>::fn();
+        default: return K<0>::fn();
+        }
+    }
+};
+template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C>); } };
+template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C>); } };
+template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C>); } };
+
+std::atomic<size_t> g_lds_granted[3][4];
+
+int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
+
+template <typename P>
+int launch(const void *fn, uint32_t grid, uint32_t block, size_t lds_bytes, const P &p, void *stream,
+           std::atomic<size_t> &granted) {
+    const int attr = ensure_lds(fn, lds_bytes, granted);
+    if (attr != hipSuccess) return attr;
+    void *args[] = {const_cast<P *>(&p)};
+    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds_bytes,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return (int)e;
+    return (int)hipGetLastError();
+}
 
 }  // namespace
 
-size_t encode_lds(uint32_t cap) { return (size_t)(cap + 2) * kEncSW * 4 + 256 * 4 + 256; }
-size_t decode_lds(uint32_t cap) { return (size_t)(cap + 2) * NS * 4 + 2 * 256 * 4; }
-size_t sgd_lds(uint32_t cap) {
-    const uint32_t rows = (cap >= 18 ? cap : cap + 2) + 1 + cap + 1 + cap + 1;
-    return (size_t)rows * kSgdSW * 4 + 1280 * 4 + 256;
-}
+size_t encode_lds(uint32_t cap) { return kEncRow0 + (size_t)(cap + 2) * kEncRowB; }
+size_t decode_lds(uint32_t cap) { return kDecRow0 + (size_t)(cap + 1) * kDecRowB; }
+size_t sgd_lds(uint32_t cap) { return SgdLayout(cap).end; }
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
@@ -770,26 +841,18 @@ int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream
 }
 
 int launch_encode(const EncodeParams &p, void *stream) {
-    const int attr = ensure_lds(k_encode, encode_lds(p.cap_words), g_enc_lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_encode, dim3(p.nblk * kEncH), dim3(kEncSW), encode_lds(p.cap_words),
-                       (hipStream_t)stream, p);
-    return (int)hipGetLastError();
+    return launch(ByCap<EncK>::pick(p.cap_words), p.nblk * kEncH, kEncSW, encode_lds(p.cap_words),
+                  p, stream, g_lds_granted[0][cap_slot(p.cap_words)]);
 }
 
 int launch_decode(const DecodeParams &p, void *stream) {
-    const int attr = ensure_lds(k_decode, decode_lds(p.cap_words), g_dec_lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_decode, dim3(p.nblk), dim3(NS), decode_lds(p.cap_words), (hipStream_t)stream, p);
-    return (int)hipGetLastError();
+    return launch(ByCap<DecK>::pick(p.cap_words), p.nblk, NS, decode_lds(p.cap_words), p, stream,
+                  g_lds_granted[1][cap_slot(p.cap_words)]);
 }
 
 int launch_sgd(const SgdParams &p, void *stream) {
-    const int attr = ensure_lds(k_sgd, sgd_lds(p.cap_words), g_sgd_lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_sgd, dim3(p.nblk * kSgdH), dim3(kSgdSW), sgd_lds(p.cap_words),
-                       (hipStream_t)stream, p);
-    return (int)hipGetLastError();
+    return launch(ByCap<SgdK>::pick(p.cap_words), p.nblk * kSgdH, kSgdSW, sgd_lds(p.cap_words), p,
+                  stream, g_lds_granted[2][cap_slot(p.cap_words)]);
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {
