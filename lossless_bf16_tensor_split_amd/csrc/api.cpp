@@ -72,7 +72,7 @@ Parts parts(const lct_tensor &t) {
     p.obase = rng(t.obase, (nb + 1) * 8);
     p.ovf = rng(t.ovf, t.ovf_cap);
     p.status = rng(t.status, 4);
-    p.scratch = rng(t.scratch, scr_stage_offset(nb) + t.ovf_cap);
+    p.scratch = rng(t.scratch, scr_bytes(nb, t.ovf_cap));
     return p;
 }
 
@@ -128,7 +128,7 @@ lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct
     out->pay = nb * layout->cap_words * kStreams * 4;
     out->cnt = nb * kStreams * 2;
     out->obase = (nb + 1) * 8;
-    out->scratch = scr_stage_offset(nb) + ovf_cap;
+    out->scratch = scr_bytes(nb, ovf_cap);
     out->fixed = out->sf + out->pay + out->cnt + out->obase;
     return LCT_OK;
 }
@@ -187,6 +187,8 @@ lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_ten
     if (e != hipSuccess) return hip_fail(e, "clear launch");
     e = launch_encode(p, stream);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
+    e = launch_scan(p.scratch, nb, kEncUnits, p.obase, p.ovf, p.ovf_cap, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
 }
 
@@ -293,6 +295,8 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
     if (e != hipSuccess) return hip_fail(e, "clear launch");
     e = launch_sgd(p, stream);
     if (e != hipSuccess) return hip_fail(e, "sgd launch");
+    e = launch_scan(p.scratch, nb, kSgdUnits, p.o_obase, p.o_ovf, p.ovf_cap, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
 }
 

@@ -24,14 +24,18 @@
 //
 // Bit reader: a code starts at stream bit q+2; the two LDS words around q give
 // a 32-bit window by one funnel shift (v_alignbit), whose bits 2..9 are the
-// 8-bit peek and index the decode table directly as a byte offset.  The
-// window is re-read for every code, so there is no refill logic.  Row -1 of
-// each input column is zero for the first codes.
+// 8-bit peek and index the decode table directly as a byte offset.  A table
+// entry holds the field (bits 30..23), the bits the code takes (bits 15..8)
+// and a shift (bits 4..0) that moves an escape's literal from the window to
+// bits 30..23 (31 for ordinary codes, which shifts everything out of that
+// range).  The window is re-read for every code, so there is no refill logic.
+// Row -1 of each input column is zero for the first codes.
 //
 // Bit writer: a 64-bit buffer; after every second code both of its words are
 // stored (ds_write2st64) at the current row and the next, and the buffer
 // advances by a word when the first one is full, so there is no final flush.
 // Two sink rows past the stream capacity absorb the stores of a full stream.
+// The encode table has one 8-byte entry per field: stream bits, bit count.
 //
 // Overflow offsets come from a scan of the per-stream spill counts over the
 // unit and a decoupled look-back across units (Merrill and Garland,
@@ -44,7 +48,10 @@
 // into a second buffer (two buffers alternate, so loads are waited for one
 // step after they were issued).  Full blocks whose inputs carry no spilled fields
 // take a path with no overflow reads at all; partial blocks and inputs with
-// spills take a general path with per-element checks.
+// spills take a general path with per-element checks.  The fused update's
+// full-block path moves the sign-fraction bytes through a per-wave LDS slab:
+// one 16-byte global access per lane covers 16 positions of 16 streams, where
+// a lane-per-stream access would move one byte per instruction.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -78,8 +85,15 @@ __device__ __forceinline__ uint64_t *s_ob_ptr() { return reinterpret_cast<uint64
 // accesses take it (plus a constant folded into the instruction) directly.
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x2 lds_u64;
+typedef __attribute__((address_space(3))) u32x4 lds_u128;
 __device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<lds_u32 *>(off); }
 __device__ __forceinline__ uint32_t ld8(uint32_t off) { return *reinterpret_cast<lds_u8 *>(off); }
+__device__ __forceinline__ u32x2 ld64(uint32_t off) { return *reinterpret_cast<lds_u64 *>(off); }
+__device__ __forceinline__ u32x4 ld128(uint32_t off) { return *reinterpret_cast<lds_u128 *>(off); }
+__device__ __forceinline__ void st128(uint32_t off, u32x4 v) { *reinterpret_cast<lds_u128 *>(off) = v; }
 __device__ __forceinline__ void st32(uint32_t off, uint32_t v) { *reinterpret_cast<lds_u32 *>(off) = v; }
 __device__ __forceinline__ void st8(uint32_t off, uint32_t v) {
     *reinterpret_cast<lds_u8 *>(off) = (uint8_t)v;
@@ -125,12 +139,12 @@ __device__ __forceinline__ uint32_t group_excl_scan(uint32_t v, uint32_t *s_tmp,
     return base + inc - v;
 }
 
-// Decoupled look-back for unit u, run by one whole wave: publishes the unit's
-// spill total, walks back over the predecessors' descriptors 64 at a time
+// Decoupled look-back for scan group u, run by one whole wave: publishes the
+// group's total, walks back over the predecessors' descriptors 64 at a time
 // until an inclusive prefix is found, publishes its own inclusive prefix and
-// returns the exclusive one.  Units come from a ticket counter, so every
+// returns the exclusive one.  Groups come from a ticket counter, so every
 // predecessor is already running and never waits on u.  The wait is bounded:
-// on time-out the status word records it and the unit goes on.
+// on time-out the status word records it and the group goes on.
 __device__ uint64_t lookback(uint64_t *flags, uint32_t u, uint64_t agg, uint32_t *status) {
     if (u == 0) {
         if (lane() == 0)
@@ -179,29 +193,35 @@ __device__ __forceinline__ uint32_t sf_of(uint32_t v) {
     return (v & 0x7Fu) | ((v >> 8) & ~0x7Fu);
 }
 
-// fp32 bits of the BF16 value (sf, e): sf in bytes 3 and 2, e in 30..23.
+// fp32 bits of the BF16 value (sf, e): sf copied to bytes 3 and 2, then the
+// exponent field (bits 30..23 of e23; its other bits are ignored) inserted.
 __device__ __forceinline__ uint32_t join32(uint32_t sf, uint32_t e23) {
     const uint32_t sfx = __builtin_amdgcn_perm(0u, sf, 0x00000C0Cu);
-    return (sfx & 0x807FFFFFu) | (e23 & ~0x807FFFFFu);
+    uint32_t r;
+    // one bit-field insert; written out because the compiler otherwise
+    // spends a mask and an and-or on it
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(0x7F800000u), "v"(e23), "v"(sfx));
+    return r;
 }
 
 // ------------------------------------------------------------------ code tables in LDS
 
-// Decode table at byte offset `ent` (and its escape masks at `msk`), indexed
-// by peek*4: e << 23 | bits consumed; the mask selects the literal field.
-__device__ __forceinline__ void stage_dec(const DecTab &t, uint32_t ent, uint32_t msk) {
+// Decode table at byte offset `tab`, indexed by peek*4 (see the bit reader).
+__device__ __forceinline__ void stage_dec(const DecTab &t, uint32_t tab) {
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
         const uint32_t d = t.dec[i];
-        st32(ent + 4 * i, ((d & 0xFFu) << 23) | ((d >> 8) & 0x1Fu));
-        st32(msk + 4 * i, (d >> 13) & 1u ? 0x7F800000u : 0u);
+        const bool esc = (d >> 13) & 1u;
+        const uint32_t field = esc ? 0u : (d & 0xFFu);
+        const uint32_t sh = esc ? 21u - t.esc_len : 31u;
+        st32(tab + 4 * i, (field << 23) | (((d >> 8) & 0x1Fu) << 8) | sh);
     }
 }
 
-// Encode tables: stream bits (u32, at `bits`) and their count (u8, at `len`).
-__device__ __forceinline__ void stage_enc(const EncTab &t, uint32_t bits, uint32_t len) {
+// Encode table at byte offset `tab`: 8-byte entries {stream bits, bit count}.
+__device__ __forceinline__ void stage_enc(const EncTab &t, uint32_t tab) {
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
-        st32(bits + 4 * i, t.bits[i]);
-        st8(len + i, t.len[i]);
+        st32(tab + 8 * i, t.bits[i]);
+        st32(tab + 8 * i + 4, t.len[i]);
     }
 }
 
@@ -214,19 +234,43 @@ struct Reader {
     int32_t q;   // stream bit position of the next code, minus 2
 
     __device__ __forceinline__ void init() { q = -2; }
-    // Next exponent field in bits 30..23 of the result (other bits garbage).
+    // The 32-bit window at q: stream bits q .. q+31 (the code at bit 2).
     // row0: LDS offset of row 0; tcol: this lane's column (bytes); rows -1
     // and `cap` are zero.
-    __device__ __forceinline__ uint32_t next(uint32_t row0, uint32_t tcol, uint32_t ent,
-                                             uint32_t msk, uint32_t litsh) {
+    __device__ __forceinline__ uint32_t window(uint32_t row0, uint32_t tcol) const {
         const uint32_t off = (((uint32_t)q << kSh) & ~(ROWB - 1)) | tcol;
         const uint32_t a = ld32(row0 + off), b = ld32(row0 + off + ROWB);
-        const uint32_t win = __builtin_amdgcn_alignbit(b, a, (uint32_t)q);
-        const uint32_t k = win & 0x3FCu;
-        const uint32_t en = ld32(ent + k);
-        const uint32_t mk = ld32(msk + k);
-        q += en & 0xFFu;
-        return ((win << litsh) & mk) | en;
+        return __builtin_amdgcn_alignbit(b, a, (uint32_t)q);
+    }
+    // Next exponent field in bits 30..23 of the result (other bits garbage);
+    // tab: the decode table.
+    __device__ __forceinline__ uint32_t next(uint32_t row0, uint32_t tcol, uint32_t tab) {
+        const uint32_t win = window(row0, tcol);
+        const uint32_t en = ld32(tab + (win & 0x3FCu));
+        q += (en >> 8) & 0xFFu;
+        return (win << (en & 31u)) | en;
+    }
+    // The next N fields from one window: field k is read from the window
+    // shifted by the bits of fields 0..k-1.  The window holds 30 bits past the
+    // first code, so the results are exact when all N fields (codes and
+    // literals) take at most 30 bits together; the bits they take are
+    // returned, and a caller that gets more than 30 must decode the same
+    // fields again with next().  q is kept at most qmax so that a bad group
+    // never addresses past the stream's zero row.
+    template <uint32_t N>
+    __device__ __forceinline__ uint32_t next_n(uint32_t row0, uint32_t tcol, uint32_t tab,
+                                               int32_t qmax, uint32_t (&e23)[N]) {
+        const uint32_t win = window(row0, tcol);
+        uint32_t c = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < N; ++k) {
+            const uint32_t wk = win >> c;
+            const uint32_t en = ld32(tab + (wk & 0x3FCu));
+            e23[k] = (wk << (en & 31u)) | en;
+            c += (en >> 8) & 0xFFu;
+        }
+        q = min(q + (int32_t)c, qmax);
+        return c;
     }
 };
 
@@ -271,17 +315,19 @@ struct Writer {
     __device__ __forceinline__ uint32_t total() const { return (woff >> kSh) - tadj + used; }
 };
 
-// Code the CH fields e[] at positions j0..j0+CH-1; with CHECKED, positions at
-// or past n_s are absent.  One capacity test per step in the common case.
+// Code the CH fields at positions j0..j0+CH-1, given as encode-table offsets
+// e8[] (8 * field); with CHECKED, positions at or past n_s are absent.  One
+// capacity test per step in the common case.
 template <uint32_t ROWB, bool CHECKED>
-__device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&e)[CH], uint32_t j0,
-                                             uint32_t n_s, uint32_t capbits, uint32_t ebits,
-                                             uint32_t elen, uint32_t row0) {
+__device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&e8)[CH], uint32_t j0,
+                                             uint32_t n_s, uint32_t capbits, uint32_t etab,
+                                             uint32_t row0) {
     uint32_t cb[CH], cl[CH];
 #pragma unroll
     for (uint32_t i = 0; i < CH; ++i) {
-        cb[i] = ld32(ebits + 4 * e[i]);
-        cl[i] = ld8(elen + e[i]);
+        const u32x2 c = ld64(etab + e8[i]);
+        cb[i] = c.x;
+        cl[i] = c.y;
         if (CHECKED && j0 + i >= n_s) {
             cb[i] = 0;
             cl[i] = 0;
@@ -320,10 +366,10 @@ __device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&
 }
 
 // Claim staging space for streams that started spilling in this step (one
-// atomic per wave), then park this step's spilled fields there.  Every lane of
-// the wave must reach it.
+// atomic per wave), then park this step's spilled fields (e8[] = 8 * field)
+// there.  Every lane of the wave must reach it.
 template <uint32_t ROWB, bool CHECKED>
-__device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&e)[CH], uint32_t j0,
+__device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&e8)[CH], uint32_t j0,
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
@@ -345,7 +391,7 @@ __device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&
             const uint32_t j = j0 + i;
             if (j >= st.cs && (!CHECKED || j < n_s)) {
                 const uint64_t k = st.soff + (j - st.cs);
-                if (k < stage_cap) stage[k] = (uint8_t)e[i];
+                if (k < stage_cap) stage[k] = (uint8_t)(e8[i] >> 3);
             }
         }
     }
@@ -355,22 +401,21 @@ __device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&
 struct UnitOut {
     uint32_t *pay;       // whole array
     uint16_t *cnt;       // whole array
-    uint64_t *obase;     // whole array
-    uint8_t *ovf;
-    uint64_t ovf_cap;
-    uint32_t *status;
     uint8_t *scratch;
-    uint32_t nblk, nunits, cap;
+    uint64_t nblk, ovf_cap;
+    uint32_t cap;
 };
 
 // After the stream loop: the unit's payload rows (LDS rows of SW words from
-// byte offset row0), the overflow offset (look-back) and the spilled fields,
-// then counts and the block's marker.  `before` runs just before cnt / obase
-// are written (the fused update waits there until the block's other units
-// have read theirs).
+// byte offset row0) go out; spilled fields, if any, are gathered from the
+// per-stream staging pieces into one piece of the second staging area in
+// (stream, position) order, and the unit's record says where; then the
+// counts.  `before` runs just before cnt is written (the fused update waits
+// there until the block's other units have read theirs).  The overflow
+// offsets and the fields' final places are the scan kernel's work.
 template <uint32_t SW, typename Before>
 __device__ void writer_finish(uint32_t cs, uint64_t soff, uint32_t n_s, uint32_t u, uint32_t b,
-                              uint32_t h, uint32_t row0, uint32_t *s_tmp, uint64_t *s_ob,
+                              uint32_t h, uint32_t row0, uint32_t *s_tmp, uint64_t *s_base,
                               const UnitOut &o, Before before) {
     const uint32_t t = threadIdx.x;
     const uint32_t spill = n_s - cs;
@@ -378,48 +423,65 @@ __device__ void writer_finish(uint32_t cs, uint64_t soff, uint32_t n_s, uint32_t
     const uint32_t excl = group_excl_scan<SW>(spill, s_tmp, total);   // barriers: LDS rows complete
     // payload: cap rows of SW words (16-byte pieces)
     constexpr uint32_t Q = SW / 4;
-    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(lds) + row0);
-    uint4 *dst = reinterpret_cast<uint4 *>(o.pay);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(lds) + row0);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(o.pay);
     for (uint32_t i = t; i < o.cap * Q; i += SW) {
         const uint32_t row = i / Q, c = i % Q;
         dst[(((uint64_t)b * o.cap + row) * NS + h * SW) / 4 + c] = src[i];
     }
-    if (t < 64) {
-        uint64_t *flags = reinterpret_cast<uint64_t *>(o.scratch + kScrFlags);
-        const uint64_t ob = lookback(flags, u, total, o.status);
-        if (t == 0) *s_ob = ob;
-    }
-    __syncthreads();
-    const uint64_t ob = *s_ob;
-    if (spill) {
+    uint64_t base = 0;
+    if (total) {
+        if (t == 0)
+            *s_base = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
+                                (unsigned long long)total);
+        __syncthreads();
+        base = *s_base;
         const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
+        uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
         for (uint32_t k = 0; k < spill; ++k) {
-            const uint64_t from = soff + k, to = ob + excl + k;
-            if (from < o.ovf_cap && to < o.ovf_cap) o.ovf[to] = stage[from];
+            const uint64_t from = soff + k, to = base + excl + k;
+            if (from < o.ovf_cap && to < o.ovf_cap) stage2[to] = stage[from];
         }
+    }
+    if (t == 0) {
+        UnitRec *rec = reinterpret_cast<UnitRec *>(o.scratch + scr_rec_offset(o.nblk));
+        rec[u] = UnitRec{total, base};
     }
     before();
     o.cnt[(uint64_t)b * NS + h * SW + t] = (uint16_t)cs;
-    if (t == 0) {
-        if (h == 0) o.obase[b] = ob;
-        if (u == o.nunits - 1) {
-            o.obase[o.nblk] = ob + total;
-            if (ob + total > o.ovf_cap) atomicOr(o.status, LCT_ST_OVF_FULL);
-        }
-    }
 }
 
 // Copy rows [0, cap) of a unit's columns of a block's payload into LDS rows of
-// SW words from byte offset row0.
+// SW words from byte offset row0; with a second source (pay2 != nullptr) its
+// rows go to row2 as well.  Up to 8 pieces per source are loaded before any is
+// stored, so the copy waits for memory a few times rather than once per piece.
 template <uint32_t SW>
-__device__ __forceinline__ void stage_rows(const uint32_t *pay, uint64_t b, uint32_t h, uint32_t cap,
-                                           uint32_t row0) {
+__device__ __forceinline__ void stage_rows(const uint32_t *pay, uint32_t row0, const uint32_t *pay2,
+                                           uint32_t row2, uint64_t b, uint32_t h, uint32_t cap) {
     constexpr uint32_t Q = SW / 4;
-    uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) + row0);
-    const uint4 *src = reinterpret_cast<const uint4 *>(pay);
-    for (uint32_t i = threadIdx.x; i < cap * Q; i += SW) {
-        const uint32_t row = i / Q, c = i % Q;
-        dst[i] = src[((b * cap + row) * NS + h * SW) / 4 + c];
+    constexpr uint32_t K = 8;
+    const uint32_t total = cap * Q;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(pay);
+    const u32x4 *src2 = reinterpret_cast<const u32x4 *>(pay2);
+    for (uint32_t base = 0; base < total; base += K * SW) {
+        u32x4 v[K], v2[K];
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k) {
+            const uint32_t i = base + k * SW + threadIdx.x;
+            const uint64_t g = ((b * cap + i / Q) * NS + h * SW) / 4 + i % Q;
+            if (i < total) {
+                v[k] = src[g];
+                if (pay2) v2[k] = src2[g];
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k) {
+            const uint32_t i = base + k * SW + threadIdx.x;
+            if (i < total) {
+                st128(row0 + 16 * i, v[k]);
+                if (pay2) st128(row2 + 16 * i, v2[k]);
+            }
+        }
     }
 }
 
@@ -455,6 +517,67 @@ __global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nwords) words[i] = 0;
     if (i == 0) *status = 0;
+}
+
+// Overflow offsets: an exclusive scan of the units' spill totals in unit
+// order (block, then its units), one unit per thread, groups chained by the
+// look-back.  Writes obase, flags a too-small overflow region, then copies
+// each of its units' spilled fields from the second staging area to their
+// place in the overflow region.
+__global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t nblk, uint32_t H,
+                                                     uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
+                                                     uint32_t *status) {
+    __shared__ uint32_t s_g;
+    __shared__ uint64_t s_wave[kScanGroup / 64], s_excl;
+    __shared__ uint64_t s_tot[kScanGroup], s_from[kScanGroup], s_to[kScanGroup];
+    const uint32_t t = threadIdx.x;
+    if (t == 0) s_g = atomicAdd(reinterpret_cast<uint32_t *>(scratch + kScrTicket2), 1u);
+    __syncthreads();
+    const uint32_t g = s_g;
+    const uint64_t nunits = nblk * H;
+    const uint64_t u = (uint64_t)g * kScanGroup + t;
+    const UnitRec *rec = reinterpret_cast<const UnitRec *>(scratch + scr_rec_offset(nblk));
+    const UnitRec r = u < nunits ? rec[u] : UnitRec{0, 0};
+    // group scan of 64-bit totals
+    uint64_t inc = r.total;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t x = __shfl_up(inc, d, 64);
+        if ((int)lane() >= d) inc += x;
+    }
+    if (lane() == 63) s_wave[t >> 6] = inc;
+    __syncthreads();
+    uint64_t before = 0, agg = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kScanGroup / 64; ++k) {
+        before += k < (t >> 6) ? s_wave[k] : 0;
+        agg += s_wave[k];
+    }
+    inc += before;
+    if (t < 64) {
+        uint64_t *flags = reinterpret_cast<uint64_t *>(scratch + scr_flags_offset(nblk));
+        const uint64_t ex = lookback(flags, g, agg, status);
+        if (t == 0) s_excl = ex;
+    }
+    __syncthreads();
+    const uint64_t ex = s_excl + inc - r.total;
+    if (u < nunits && u % H == 0) obase[u / H] = ex;
+    if (u + 1 == nunits) {
+        obase[nblk] = ex + r.total;
+        if (ex + r.total > ovf_cap) atomicOr(status, LCT_ST_OVF_FULL);
+    }
+    s_tot[t] = r.total;
+    s_from[t] = r.base;
+    s_to[t] = ex;
+    __syncthreads();
+    const uint8_t *stage2 = scratch + scr_stage2_offset(nblk, ovf_cap);
+    for (uint32_t k = 0; k < kScanGroup; ++k) {
+        const uint64_t n = s_tot[k];
+        if (n == 0) continue;
+        const uint64_t from = s_from[k], to = s_to[k];
+        for (uint64_t i = t; i < n; i += kScanGroup)
+            if (from + i < ovf_cap && to + i < ovf_cap) ovf[to + i] = stage2[from + i];
+    }
 }
 
 __device__ uint16_t g_sample[4096];
@@ -503,9 +626,9 @@ struct Buf2 {
 
 // ------------------------------------------------------------------ encode
 
-constexpr uint32_t kEncH = 1, kEncSW = NS / kEncH, kEncRowB = kEncSW * 4;
-// LDS: bits table, lengths, then the output rows (cap + 2 sink rows).
-constexpr uint32_t kEncBits = 256, kEncLen = 1280, kEncRow0 = 1536;
+constexpr uint32_t kEncH = kEncUnits, kEncSW = NS / kEncH, kEncRowB = kEncSW * 4;
+// LDS: encode table, then the output rows (cap + 2 sink rows).
+constexpr uint32_t kEncTab = 256, kEncRow0 = 2304;
 
 template <uint32_t CAPT>
 __device__ __forceinline__ uint32_t cap_of(uint32_t rt) { return CAPT ? CAPT : rt; }
@@ -527,10 +650,10 @@ __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer<kEnc
             uint8_t *o = sfs + (size_t)j0 * NS;
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
-                e[i] = (bf.v[i] >> 7) & 0xFFu;
+                e[i] = (bf.v[i] >> 4) & 0x7F8u;   // 8 * exponent field
                 if (FULL || j0 + i < n_s) o[i * NS] = (uint8_t)sf_of(bf.v[i]);
             }
-            writer_chunk<kEncRowB, !FULL>(st, e, j0, n_s, capbits, kEncBits, kEncLen, kEncRow0);
+            writer_chunk<kEncRowB, !FULL>(st, e, j0, n_s, capbits, kEncTab, kEncRow0);
             writer_spill<kEncRowB, !FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
 }
@@ -543,7 +666,7 @@ __global__ __launch_bounds__(256) void k_encode(const EncodeParams p) {
     constexpr uint32_t SW = kEncSW;
     const uint32_t t = threadIdx.x;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    stage_enc(p.enc, kEncBits, kEncLen);
+    stage_enc(p.enc, kEncTab);
     const uint32_t tcol = 4 * t;
     for (uint32_t w = 0; w < cap; ++w) st32(kEncRow0 + w * kEncRowB + tcol, 0);
     if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
@@ -561,16 +684,15 @@ __global__ __launch_bounds__(256) void k_encode(const EncodeParams p) {
         encode_stream<true, CAPT>(p, st, n_s, r0 + h * SW);
     else
         encode_stream<false, CAPT>(p, st, n_s, r0 + h * SW);
-    const UnitOut o{p.pay, p.cnt, p.obase, p.ovf, p.ovf_cap, p.status, p.scratch,
-                    p.nblk, nunits, cap};
+    const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap};
     writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, kEncRow0, s_tmp, &s_ob, o, [] {});
 }
 
 // ------------------------------------------------------------------ decode
 
-// LDS: decode table, escape masks, zero row -1, rows 0..cap-1, zero row cap.
+// LDS: decode table, zero row -1, rows 0..cap-1, zero row cap.
 constexpr uint32_t kDecRowB = NS * 4;
-constexpr uint32_t kDecEnt = 256, kDecMsk = 1280, kDecRowM1 = 2304, kDecRow0 = 2304 + kDecRowB;
+constexpr uint32_t kDecTab = 256, kDecRowM1 = 1280, kDecRow0 = 1280 + kDecRowB;
 
 template <bool FAST, uint32_t CAPT>
 __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_s, uint32_t c_s,
@@ -579,7 +701,6 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_
     const uint32_t tcol = 4 * s;
     const uint32_t npos = p.block_elems / NS;
     const int32_t qmax = 32 * (int32_t)cap_of<CAPT>(p.cap_words) - 2;
-    const uint32_t litsh = 21 - p.dec.esc_len;
     const uint8_t *sfs = p.sf + r0 + s;
     uint16_t *ys = p.y + r0 + s;
     Reader<kDecRowB> rd;
@@ -588,19 +709,41 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_
         npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FAST>(bf.v, sfs, j0, n_s); },
         [&](Buf1 &bf, uint32_t j0) {
             uint16_t *o = ys + (size_t)j0 * NS;
+            if (FAST) {
+                // four fields per window; a chunk where some window ran out
+                // (long escapes) is decoded again one field per window
+                const int32_t q0 = rd.q;
+                uint32_t cmax = 0;
+#pragma unroll
+                for (uint32_t g = 0; g < CH; g += 4) {
+                    uint32_t e23[4];
+                    cmax = max(cmax, rd.next_n<4>(kDecRow0, tcol, kDecTab, qmax, e23));
+#pragma unroll
+                    for (uint32_t k = 0; k < 4; ++k)
+                        o[(g + k) * NS] = (uint16_t)(join32(bf.v[g + k], e23[k]) >> 16);
+                }
+                if (__builtin_expect(!__all(cmax <= 30), 0)) {
+                    rd.q = q0;
+#pragma unroll
+                    for (uint32_t i = 0; i < CH; ++i) {
+                        const uint32_t e23 = rd.next(kDecRow0, tcol, kDecTab);
+                        rd.q = min(rd.q, qmax);
+                        o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
                 const uint32_t j = j0 + i;
-                uint32_t e23 = rd.next(kDecRow0, tcol, kDecEnt, kDecMsk, litsh);
-                if (!FAST) {
-                    rd.q = min(rd.q, qmax);
-                    if (j >= c_s && j < n_s) {
-                        const uint64_t k = sp0 + (j - c_s);
-                        e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
-                    }
+                uint32_t e23 = rd.next(kDecRow0, tcol, kDecTab);
+                rd.q = min(rd.q, qmax);
+                if (j >= c_s && j < n_s) {
+                    const uint64_t k = sp0 + (j - c_s);
+                    e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
                 }
                 // the BF16 value is the top half of its fp32 form
-                if (FAST || j < n_s) o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
+                if (j < n_s) o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
             }
         });
 }
@@ -610,8 +753,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeParams p) {
     uint32_t *s_tmp = s_tmp_ptr();
     const uint32_t t = threadIdx.x, b = blockIdx.x;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    stage_dec(p.dec, kDecEnt, kDecMsk);
-    stage_rows<NS>(p.pay, b, 0, cap, kDecRow0);
+    stage_dec(p.dec, kDecTab);
+    stage_rows<NS>(p.pay, kDecRow0, nullptr, 0, b, 0, cap);
     st32(kDecRowM1 + 4 * t, 0);
     st32(kDecRow0 + cap * kDecRowB + 4 * t, 0);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
@@ -628,10 +771,16 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeParams p) {
 
 // ------------------------------------------------------------------ fused SGD
 
-constexpr uint32_t kSgdH = 2, kSgdSW = NS / kSgdH, kSgdRowB = kSgdSW * 4;
-// LDS: W and M decode tables and masks, W encode bits and lengths, then rows.
-constexpr uint32_t kSgdWEnt = 256, kSgdWMsk = 1280, kSgdMEnt = 2304, kSgdMMsk = 3328;
-constexpr uint32_t kSgdBits = 4352, kSgdLen = 5376, kSgdRows = 5632;
+constexpr uint32_t kSgdH = kSgdUnits, kSgdSW = NS / kSgdH, kSgdRowB = kSgdSW * 4;
+constexpr uint32_t kSgdWaves = kSgdSW / 64;
+// Sign-fraction slabs of the full-block path: per wave, kSlabPos positions of
+// its 64 streams for W (also the result's bytes, written in place) and for M.
+constexpr uint32_t kSlabPos = 2 * CH;
+constexpr uint32_t kSlabB = kSlabPos * 64;
+// LDS: W and M decode tables, the W encode table, the slabs, then rows.
+constexpr uint32_t kSgdWTab = 256, kSgdMTab = 1280, kSgdETab = 2304, kSgdSlab = 4352;
+constexpr uint32_t kSgdRows = kSgdSlab + kSgdWaves * 2 * kSlabB;
+static_assert(kSgdRows % 256 == 0, "rows must start on a 256-byte boundary");
 
 // Rows (kSgdRowB bytes each): the output's rows 0..cap-1 and its two sink
 // rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row cap and M's
@@ -655,16 +804,34 @@ struct SgdLayout {
 __device__ __forceinline__ uint32_t sgd_round(uint32_t wf, uint32_t mf, float neg_eta) {
     const float r = __builtin_fmaf(neg_eta, __uint_as_float(mf), __uint_as_float(wf));
     const uint32_t u = __float_as_uint(r);
-    uint32_t R = u + 0x7FFFu + ((u >> 16) & 1u);
-    const bool nan = r != r;
-    if (__builtin_expect(__any(nan), 0)) R = nan ? 0x7FC00000u : R;
-    return R;
+    const uint32_t R = u + 0x7FFFu + ((u >> 16) & 1u);
+    return r != r ? 0x7FC00000u : R;
 }
 
-template <bool FAST, uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdRowB> &st, uint32_t n_s,
-                                           uint32_t cw_s, uint32_t cm_s, uint64_t r0, uint64_t wsp,
-                                           uint64_t msp) {
+// Sign-fraction byte of the rounded result R in bits 23..16: the sign moves
+// from bit 31 to bit 23, the fraction stays in bits 22..16.
+__device__ __forceinline__ uint32_t sgd_sf16(uint32_t R) {
+    return (R & ~0x00800000u) | ((R >> 8) & 0x00800000u);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even BF16 by the hardware conversion
+// (a in bits 15..0, b in bits 31..16).  It agrees with the integer rounding of
+// sgd_round for every value but NaN, whose sign and payload it keeps: callers
+// check for NaN and take sgd_round where one occurs.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// General path: partial blocks and inputs with spilled fields; byte-wide
+// accesses with per-element checks.
+template <uint32_t CAPT>
+__device__ __forceinline__ void sgd_stream_general(const SgdParams &p, Writer<kSgdRowB> &st,
+                                                   uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
+                                                   uint64_t r0, uint64_t wsp, uint64_t msp) {
     const uint32_t s = threadIdx.x;
     const uint32_t tcol = 4 * s;
     const uint32_t npos = p.block_elems / NS;
@@ -672,7 +839,6 @@ __device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdRowB> 
     const SgdLayout lay(cap);
     const uint32_t capbits = 32 * cap;
     const int32_t qmax = (int32_t)capbits - 2;
-    const uint32_t wlit = 21 - p.wdec.esc_len, mlit = 21 - p.mdec.esc_len;
     const uint8_t *wsf = p.w_sf + r0 + s;
     const uint8_t *msf = p.m_sf + r0 + s;
     uint8_t *osf = p.o_sf + r0 + s;
@@ -684,8 +850,8 @@ __device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdRowB> 
     double_buffered<Buf2>(
         npos,
         [&](Buf2 &bf, uint32_t j0) {
-            load_chunk<!FAST>(bf.w, wsf, j0, n_s);
-            load_chunk<!FAST>(bf.m, msf, j0, n_s);
+            load_chunk<true>(bf.w, wsf, j0, n_s);
+            load_chunk<true>(bf.m, msf, j0, n_s);
         },
         [&](Buf2 &bf, uint32_t j0) {
             uint32_t e[CH];
@@ -693,30 +859,208 @@ __device__ __forceinline__ void sgd_stream(const SgdParams &p, Writer<kSgdRowB> 
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
                 const uint32_t j = j0 + i;
-                uint32_t ew = rw.next(lay.w0, tcol, kSgdWEnt, kSgdWMsk, wlit);
-                uint32_t em = rm.next(lay.m0, tcol, kSgdMEnt, kSgdMMsk, mlit);
-                if (!FAST) {
-                    rw.q = min(rw.q, qmax);
-                    rm.q = min(rm.q, qmax);
-                    if (j >= cw_s && j < n_s) {
-                        const uint64_t k = wsp + (j - cw_s);
-                        ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
-                    }
-                    if (j >= cm_s && j < n_s) {
-                        const uint64_t k = msp + (j - cm_s);
-                        em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                    }
+                uint32_t ew = rw.next(lay.w0, tcol, kSgdWTab);
+                uint32_t em = rm.next(lay.m0, tcol, kSgdMTab);
+                rw.q = min(rw.q, qmax);
+                rm.q = min(rm.q, qmax);
+                if (j >= cw_s && j < n_s) {
+                    const uint64_t k = wsp + (j - cw_s);
+                    ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                }
+                if (j >= cm_s && j < n_s) {
+                    const uint64_t k = msp + (j - cm_s);
+                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
                 }
                 const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.neg_eta);
-                // sign-fraction byte of the result: the sign (bit 31) goes to
-                // bit 23, then bits 23..16 are stored
-                const uint32_t sfr = (R & ~0x00800000u) | ((R >> 8) & 0x00800000u);
-                if (FAST || j < n_s) o[i * NS] = (uint8_t)(sfr >> 16);
-                e[i] = (R >> 23) & 0xFFu;
+                if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
+                e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
             }
-            writer_chunk<kSgdRowB, !FAST>(st, e, j0, n_s, capbits, kSgdBits, kSgdLen, lay.out0);
-            writer_spill<kSgdRowB, !FAST>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
+            writer_chunk<kSgdRowB, true>(st, e, j0, n_s, capbits, kSgdETab, lay.out0);
+            writer_spill<kSgdRowB, true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
+}
+
+// Full-block path (every stream has npos elements and no input field spilled).
+// The sign-fraction bytes of W and M arrive through per-wave LDS slabs: lane l
+// moves the 16 bytes of position l/4, streams 16*(l%4).. of its wave, twice
+// per slab (positions +0 and +CH), with one 16-byte load each; the result's
+// bytes overwrite W's in the slab and leave with one 16-byte store each.  The
+// next slab's loads are in flight while the current one is worked on.
+struct SlabRegs {
+    u32x4 w0, w1, m0, m1;
+};
+
+template <uint32_t CAPT>
+__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdRowB> &st,
+                                                uint64_t r0) {
+    const uint32_t t = threadIdx.x, l = lane(), wv = t >> 6;
+    const uint32_t tcol = 4 * t;
+    const uint32_t npos = p.block_elems / NS;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const SgdLayout lay(cap);
+    const uint32_t capbits = 32 * cap;
+    const int32_t qmax = (int32_t)capbits - 2;
+    const uint32_t sw = kSgdSlab + wv * 2 * kSlabB, sm = sw + kSlabB;
+    const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a slab
+    const uint32_t col = l;                       // this lane's byte in a slab row
+    const uint64_t g = r0 + 64 * wv + (uint64_t)(l >> 2) * NS + 16 * (l & 3);
+    const uint8_t *gw = p.w_sf + g;
+    const uint8_t *gm = p.m_sf + g;
+    uint8_t *go = p.o_sf + g;
+    constexpr uint64_t kHalf = (uint64_t)CH * NS;   // bytes between the slab's halves
+    uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
+    uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
+    Reader<kSgdRowB> rw, rm;
+    rw.init();
+    rm.init();
+    // Always four loads (a slab that is only half inside the block loads its
+    // first half twice), so that the number of loads in flight is the same on
+    // every path and the wait for one slab never includes the next one's.
+    auto load = [&](SlabRegs &r, uint32_t j0) {
+        const uint64_t o = (uint64_t)j0 * NS;
+        const uint64_t o1 = j0 + CH < npos ? o + kHalf : o;
+        r.w0 = *reinterpret_cast<const u32x4 *>(gw + o);
+        r.m0 = *reinterpret_cast<const u32x4 *>(gm + o);
+        r.w1 = *reinterpret_cast<const u32x4 *>(gw + o1);
+        r.m1 = *reinterpret_cast<const u32x4 *>(gm + o1);
+    };
+    // The slab bytes are read before and written after the decode loop, so no
+    // LDS store sits between one field's table read and the next field's
+    // window read: the two W/M reader chains then overlap the arithmetic.
+    auto half = [&](uint32_t j0, uint32_t row) {
+        uint32_t ws[CH], ms[CH], H[CH / 2], e[CH];
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) {
+            ws[i] = ld8(sw + (row + i) * 64 + col);
+            ms[i] = ld8(sm + (row + i) * 64 + col);
+        }
+        // Four fields per window and reader, software-pipelined: step k of a
+        // group issues both readers' k-th table lookups, and the arithmetic of
+        // the previous group's k-th element fills their latency.  The
+        // scheduling barriers keep that order (left alone, the two reader
+        // chains are scheduled one after the other).  Results are rounded in
+        // pairs by the hardware conversion; a chunk holding a NaN, or one
+        // where some window ran out (long escapes), is done again with one
+        // field per window and the integer rounding.
+        const int32_t qw0 = rw.q, qm0 = rm.q;
+        uint32_t cmax = 0;
+        bool nan = false;
+        uint32_t ew[CH], em[CH];
+        float r[CH];
+#pragma unroll
+        for (uint32_t g = 0; g <= CH; g += 4) {
+            uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
+            if (g < CH) {
+                winw = rw.window(lay.w0, tcol);
+                winm = rm.window(lay.m0, tcol);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
+                if (g < CH) {
+                    wkw = winw >> cw;
+                    wkm = winm >> cm;
+                    enw = ld32(kSgdWTab + (wkw & 0x3FCu));
+                    enm = ld32(kSgdMTab + (wkm & 0x3FCu));
+                }
+                if (g > 0) {
+                    const uint32_t i = g - 4 + k;
+                    r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32(ms[i], em[i])),
+                                          __uint_as_float(join32(ws[i], ew[i])));
+                    nan |= r[i] != r[i];
+                    if (k & 1) H[i / 2] = cvt_bf16x2(r[i - 1], r[i]);
+                }
+                if (g < CH) {
+                    ew[g + k] = (wkw << (enw & 31u)) | enw;
+                    em[g + k] = (wkm << (enm & 31u)) | enm;
+                    cw += (enw >> 8) & 0xFFu;
+                    cm += (enm >> 8) & 0xFFu;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (g < CH) {
+                rw.q = min(rw.q + (int32_t)cw, qmax);
+                rm.q = min(rm.q + (int32_t)cm, qmax);
+                cmax = max(cmax, max(cw, cm));
+            }
+        }
+        if (__builtin_expect(!__all(cmax <= 30 && !nan), 0)) {
+            if (!__all(cmax <= 30)) {
+                rw.q = qw0;
+                rm.q = qm0;
+#pragma unroll
+                for (uint32_t i = 0; i < CH; ++i) {
+                    ew[i] = rw.next(lay.w0, tcol, kSgdWTab);
+                    em[i] = rm.next(lay.m0, tcol, kSgdMTab);
+                    rw.q = min(rw.q, qmax);
+                    rm.q = min(rm.q, qmax);
+                }
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < CH; i += 2) {
+                const uint32_t R0 = sgd_round(join32(ws[i], ew[i]), join32(ms[i], em[i]), p.neg_eta);
+                const uint32_t R1 =
+                    sgd_round(join32(ws[i + 1], ew[i + 1]), join32(ms[i + 1], em[i + 1]), p.neg_eta);
+                H[i / 2] = (R0 >> 16) | (R1 & 0xFFFF0000u);
+            }
+        }
+        // split the pairs: exponent field (as an encode-table offset) and the
+        // sign-fraction byte of each result, the latter back into the slab
+#pragma unroll
+        for (uint32_t i = 0; i < CH; i += 2) {
+            const uint32_t h = H[i / 2], t = h >> 8;
+            e[i] = (h >> 4) & 0x7F8u;
+            e[i + 1] = (h >> 20) & 0x7F8u;
+            st8(sw + (row + i) * 64 + col, (h & 0x7Fu) | (t & 0x80u));
+            st8(sw + (row + i + 1) * 64 + col, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
+        }
+        writer_chunk<kSgdRowB, false>(st, e, j0, npos, capbits, kSgdETab, lay.out0);
+        writer_spill<kSgdRowB, false>(st, e, j0, npos, stage_ctr, stage, p.ovf_cap);
+    };
+    // A slab's result bytes are read into registers at the end of its step
+    // and stored after the next slab has been staged: the memory-counter wait
+    // that stages a slab then never includes stores issued just before it,
+    // and a store's registers (which may only be reused once it completes)
+    // stay untouched for a whole step.  Staging and stores are unconditional:
+    // a slab only half inside the block repeats its first half.  The first
+    // step stores W's own bytes to the result's first slab, overwritten by
+    // the real result a step later (same wave, same addresses, in order).
+    u32x4 out0, out1;
+    uint64_t dst0, dst1;
+    auto step = [&](SlabRegs &r, uint32_t j0) {
+        const bool two = j0 + CH < npos;
+        st128(sw + mine, r.w0);
+        st128(sm + mine, r.m0);
+        st128(sw + kSlabB / 2 + mine, r.w1);
+        st128(sm + kSlabB / 2 + mine, r.m1);
+        *reinterpret_cast<u32x4 *>(dst0) = out0;
+        *reinterpret_cast<u32x4 *>(dst1) = out1;
+        half(j0, 0);
+        if (two) half(j0 + CH, CH);
+        const uint64_t o = (uint64_t)j0 * NS;
+        dst0 = reinterpret_cast<uint64_t>(go + o);
+        dst1 = reinterpret_cast<uint64_t>(go + (two ? o + kHalf : o));
+        out0 = ld128(sw + mine);
+        out1 = ld128(sw + (two ? kSlabB / 2 : 0) + mine);
+    };
+    SlabRegs a, b;
+    load(a, 0u);
+    out0 = a.w0;
+    out1 = a.w1;
+    dst0 = reinterpret_cast<uint64_t>(go);
+    dst1 = reinterpret_cast<uint64_t>(go + (CH < npos ? kHalf : 0));
+    for (uint32_t j0 = 0; j0 < npos; j0 += 2 * kSlabPos) {
+        const uint32_t j1 = j0 + kSlabPos;
+        load(b, j1 < npos ? j1 : j0);
+        step(a, j0);
+        if (j1 >= npos) break;
+        const uint32_t j2 = j1 + kSlabPos;
+        load(a, j2 < npos ? j2 : j1);
+        step(b, j1);
+    }
+    *reinterpret_cast<u32x4 *>(dst0) = out0;
+    *reinterpret_cast<u32x4 *>(dst1) = out1;
 }
 
 template <uint32_t CAPT>
@@ -729,17 +1073,16 @@ __global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
     const uint32_t tcol = 4 * t;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const SgdLayout lay(cap);
-    stage_dec(p.wdec, kSgdWEnt, kSgdWMsk);
-    stage_dec(p.mdec, kSgdMEnt, kSgdMMsk);
-    stage_enc(p.wenc, kSgdBits, kSgdLen);
+    stage_dec(p.wdec, kSgdWTab);
+    stage_dec(p.mdec, kSgdMTab);
+    stage_enc(p.wenc, kSgdETab);
     if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
     __syncthreads();
     const uint32_t u = s_ticket;
     const uint32_t nunits = p.nblk * H;
     if (u >= nunits) return;   // only if the scratch header was not cleared
     const uint32_t b = u / H, h = u % H;
-    stage_rows<SW>(p.w_pay, b, h, cap, lay.w0);
-    stage_rows<SW>(p.m_pay, b, h, cap, lay.m0);
+    stage_rows<SW>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
     st32(lay.z0 + tcol, 0);
     st32(lay.z1 + tcol, 0);
     st32(lay.z2 + tcol, 0);
@@ -752,17 +1095,16 @@ __global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
     block_spills<SW, H>(p.m_cnt + (uint64_t)b * NS, nb, h, s_tmp, cm_s, mex, mtot);
     const uint64_t wsp = p.w_obase[b] + wex, msp = p.m_obase[b] + mex;
     // this unit has read what the block's other units may overwrite in place
-    uint32_t *readers = reinterpret_cast<uint32_t *>(p.scratch + scr_readers_offset(p.nblk));
+    uint32_t *readers = reinterpret_cast<uint32_t *>(p.scratch + kScrReaders);
     __syncthreads();
     if (t == 0) __hip_atomic_fetch_add(&readers[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     Writer<kSgdRowB> st;
     st.init(tcol, n_s);
     if (nb == p.block_elems && wtot == 0 && mtot == 0)
-        sgd_stream<true, CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
+        sgd_stream_full<CAPT>(p, st, r0 + h * SW);
     else
-        sgd_stream<false, CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
-    const UnitOut o{p.o_pay, p.o_cnt, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.scratch,
-                    p.nblk, nunits, cap};
+        sgd_stream_general<CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
+    const UnitOut o{p.o_pay, p.o_cnt, p.scratch, p.nblk, p.ovf_cap, cap};
     uint32_t *status = p.status;
     writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, lay.out0, s_tmp, &s_ob, o,
                       [readers, b, status, t] {
@@ -831,6 +1173,14 @@ int launch(const void *fn, uint32_t grid, uint32_t block, size_t lds_bytes, cons
 size_t encode_lds(uint32_t cap) { return kEncRow0 + (size_t)(cap + 2) * kEncRowB; }
 size_t decode_lds(uint32_t cap) { return kDecRow0 + (size_t)(cap + 1) * kDecRowB; }
 size_t sgd_lds(uint32_t cap) { return SgdLayout(cap).end; }
+
+int launch_scan(uint8_t *scratch, uint64_t nblk, uint32_t units_per_block, uint64_t *obase,
+                uint8_t *ovf, uint64_t ovf_cap, uint32_t *status, void *stream) {
+    const uint64_t groups = (nblk * units_per_block + kScanGroup - 1) / kScanGroup;
+    hipLaunchKernelGGL(k_scan, dim3((uint32_t)groups), dim3(kScanGroup), 0, (hipStream_t)stream,
+                       scratch, nblk, units_per_block, obase, ovf, ovf_cap, status);
+    return (int)hipGetLastError();
+}
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;

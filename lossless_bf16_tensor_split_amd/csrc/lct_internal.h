@@ -16,17 +16,42 @@ constexpr uint32_t kMaxBlock = 65536;
 constexpr uint32_t kMaxCapWords = 64;
 
 constexpr uint32_t kMaxUnits = 4;           // workgroups a block may be split over
+constexpr uint32_t kEncUnits = 1;           // encode: one workgroup per block
+constexpr uint32_t kSgdUnits = 2;           // fused update: two workgroups per block
 
-// Scratch layout (bytes).  The header, the look-back flags and the per-block
-// reader counters are cleared by a fill kernel before each encode / SGD
-// launch; the staging area holds spilled exponent fields until their
-// overflow offset is known.
-constexpr uint64_t kScrTicket = 0;    // uint32: next unit to hand out
-constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the staging area
-constexpr uint64_t kScrFlags = 64;    // uint64[kMaxUnits * nblk]: look-back descriptors
-__host__ __device__ inline uint64_t scr_readers_offset(uint64_t nblk) { return kScrFlags + 8 * kMaxUnits * nblk; }
-__host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) { return scr_readers_offset(nblk) + 4 * nblk; }
-__host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) { return (scr_clear_bytes(nblk) + 255) & ~uint64_t(255); }
+// Scratch layout (bytes).  The header, the per-block reader counters and the
+// scan's look-back flags are cleared by a fill kernel before each encode / SGD
+// launch.  Every unit of the main kernel writes its record (spilled bytes,
+// where they sit in the second staging area).  Spilled exponent fields are
+// parked per stream in the first staging area while a unit runs, copied into
+// one contiguous piece per unit at its end, and placed in the overflow region
+// by the scan kernel once every unit's offset is known.
+constexpr uint64_t kScrTicket = 0;    // uint32: next unit of the main kernel
+constexpr uint64_t kScrTicket2 = 4;   // uint32: next group of the scan kernel
+constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the first staging area
+constexpr uint64_t kScrStage2 = 16;   // uint64: bytes claimed in the second
+constexpr uint64_t kScrReaders = 64;  // uint32[nblk]: units of a block that have read it
+constexpr uint32_t kScanGroup = 256;  // units per scan workgroup
+__host__ __device__ inline uint64_t scr_max_units(uint64_t nblk) { return kMaxUnits * nblk; }
+__host__ __device__ inline uint64_t scr_flags_offset(uint64_t nblk) { return (kScrReaders + 4 * nblk + 7) & ~uint64_t(7); }
+__host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) {
+    return scr_flags_offset(nblk) + 8 * ((scr_max_units(nblk) + kScanGroup - 1) / kScanGroup + 1);
+}
+__host__ __device__ inline uint64_t scr_rec_offset(uint64_t nblk) { return (scr_clear_bytes(nblk) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) {
+    return (scr_rec_offset(nblk) + 16 * scr_max_units(nblk) + 255) & ~uint64_t(255);
+}
+__host__ __device__ inline uint64_t scr_stage2_offset(uint64_t nblk, uint64_t ovf_cap) {
+    return (scr_stage_offset(nblk) + ovf_cap + 255) & ~uint64_t(255);
+}
+__host__ __device__ inline uint64_t scr_bytes(uint64_t nblk, uint64_t ovf_cap) {
+    return scr_stage2_offset(nblk, ovf_cap) + ovf_cap;
+}
+
+// A unit's record: spilled bytes and where they start in the second staging area.
+struct UnitRec {
+    uint64_t total, base;
+};
 
 // Encoder tables: stream bits of each exponent field and their count.
 struct EncTab {
@@ -102,6 +127,8 @@ struct SgdParams {
 
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
+int launch_scan(uint8_t *scratch, uint64_t nblk, uint32_t units_per_block, uint64_t *obase,
+                uint8_t *ovf, uint64_t ovf_cap, uint32_t *status, void *stream);
 int launch_encode(const EncodeParams &p, void *stream);
 int launch_decode(const DecodeParams &p, void *stream);
 int launch_sgd(const SgdParams &p, void *stream);
