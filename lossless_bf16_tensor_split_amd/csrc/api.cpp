@@ -187,7 +187,7 @@ lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_ten
     if (e != hipSuccess) return hip_fail(e, "clear launch");
     e = launch_encode(p, stream);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
-    e = launch_scan(p.scratch, nb, kEncUnits, p.obase, p.ovf, p.ovf_cap, p.status, stream);
+    e = launch_scan(p.scratch, nb, p.obase, p.ovf, p.ovf_cap, p.status, p.cnt, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
 }
@@ -288,6 +288,7 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
     p.cap_words = w_in->layout.cap_words;
     p.nblk = (uint32_t)nb;
     p.neg_eta = -eta;
+    p.park_cnt = p.o_cnt == p.w_cnt;
     fill_enc(*cw, &p.wenc);
     fill_dec(*cw, &p.wdec);
     fill_dec(*cm, &p.mdec);
@@ -295,7 +296,7 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
     if (e != hipSuccess) return hip_fail(e, "clear launch");
     e = launch_sgd(p, stream);
     if (e != hipSuccess) return hip_fail(e, "sgd launch");
-    e = launch_scan(p.scratch, nb, kSgdUnits, p.o_obase, p.o_ovf, p.ovf_cap, p.status, stream);
+    e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
 }

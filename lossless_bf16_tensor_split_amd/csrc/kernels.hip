@@ -11,16 +11,17 @@
 // follows the paragraph on training traffic: read the compressed W and M,
 // compute W - eta * M, write the new bytes in one pass.
 //
-// Mapping.  One lane per stream, so at step j lane s touches element
-// j*256 + s of its block and a wave's accesses cover contiguous bytes.  A
-// workgroup ("unit") owns SW = 256/H streams of one block.  The block's
-// stream words are interleaved (word w of stream s at w*256 + s), so a unit's
-// payload rows move between HBM and LDS with 16-byte accesses and every lane
-// works on its own column of LDS rows (a row's lanes hit distinct banks).
-// LDS holds the code tables (after 256 bytes of small shared values) and then
-// the payload rows; kernels
-// are specialised on the stream capacity of the three modes so that every LDS
-// offset is an immediate of the instruction.
+// Mapping.  A "unit" is 64 streams of one block and one wave does it, one
+// lane per stream, so at step j lane s touches element j*256 + s of its block
+// and a wave's accesses cover contiguous bytes.  The waves of a workgroup
+// share the code tables in LDS and nothing else, so no wave ever waits for
+// another.  Encode and decode run one unit per wave (a workgroup is a block's
+// four units); the fused update's waves are persistent and take units
+// round-robin, so its three tables are staged once per workgroup.  The block's stream words are interleaved (word w of stream s at
+// w*256 + s): a unit's payload rows move between HBM and LDS with 16-byte
+// accesses and every lane works on its own column of the wave's LDS rows
+// (a row's lanes hit distinct banks).  Kernels are specialised on the stream
+// capacity of the three modes, so row counts and table offsets are constants.
 //
 // Bit reader: a code starts at stream bit q+2; the two LDS words around q give
 // a 32-bit window by one funnel shift (v_alignbit), whose bits 2..9 are the
@@ -28,7 +29,7 @@
 // entry holds the field (bits 30..23), the bits the code takes (bits 15..8)
 // and a shift (bits 4..0) that moves an escape's literal from the window to
 // bits 30..23 (31 for ordinary codes, which shifts everything out of that
-// range).  The window is re-read for every code, so there is no refill logic.
+// range).  Several codes are read from one window; there is no refill logic.
 // Row -1 of each input column is zero for the first codes.
 //
 // Bit writer: a 64-bit buffer; after every second code both of its words are
@@ -37,21 +38,21 @@
 // Two sink rows past the stream capacity absorb the stores of a full stream.
 // The encode table has one 8-byte entry per field: stream bits, bit count.
 //
-// Overflow offsets come from a scan of the per-stream spill counts over the
-// unit and a decoupled look-back across units (Merrill and Garland,
-// "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016); units
-// take tickets in order, so spilled fields land in (block, stream, position)
-// order in one pass.  Fields that spill are parked in a staging area until
-// their offset is known.
+// Overflow offsets: spilled fields are parked per stream in a staging area,
+// gathered per unit at its end, and placed by a separate scan kernel, an
+// exclusive scan over the units' spill totals with a decoupled look-back
+// across its workgroups (Merrill and Garland, "Single-pass Parallel Prefix
+// Scan with Decoupled Look-back", 2016), so that the fields land in (block,
+// stream, position) order.
 //
 // Every loop step handles 16 positions per lane while the next 16 are loaded
 // into a second buffer (two buffers alternate, so loads are waited for one
-// step after they were issued).  Full blocks whose inputs carry no spilled fields
-// take a path with no overflow reads at all; partial blocks and inputs with
-// spills take a general path with per-element checks.  The fused update's
-// full-block path moves the sign-fraction bytes through a per-wave LDS slab:
-// one 16-byte global access per lane covers 16 positions of 16 streams, where
-// a lane-per-stream access would move one byte per instruction.
+// step after they were issued).  Full blocks whose inputs carry no spilled
+// fields take a path with no overflow reads at all; partial blocks and inputs
+// with spills take a general path with per-element checks.  The fused
+// update's full-block path moves the sign-fraction bytes through a per-wave
+// LDS slab: one 16-byte global access per lane covers 16 positions of 16
+// streams, where a lane-per-stream access would move one byte per instruction.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -69,16 +70,6 @@ constexpr uint64_t kFlagVal = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 21;
 
 extern __shared__ uint32_t lds[];
-
-// The first 256 bytes of LDS hold a workgroup's small shared values; tables
-// and rows start at 256 so that every offset is a multiple of 256 (the unit
-// of the paired LDS accesses' immediate offsets).
-constexpr uint32_t kMiscTmp = 0;      // uint32[4]: per-wave scan totals
-constexpr uint32_t kMiscTicket = 16;  // uint32: the unit's ticket
-constexpr uint32_t kMiscOb = 24;      // uint64: the unit's overflow offset
-__device__ __forceinline__ uint32_t *s_tmp_ptr() { return lds + kMiscTmp / 4; }
-__device__ __forceinline__ uint32_t *s_ticket_ptr() { return lds + kMiscTicket / 4; }
-__device__ __forceinline__ uint64_t *s_ob_ptr() { return reinterpret_cast<uint64_t *>(lds + kMiscOb / 4); }
 
 // LDS accessed by byte offset.  These kernels declare no static LDS, so the
 // dynamic region starts at LDS address 0 and an offset is an address: the
@@ -116,27 +107,6 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
     return v;
-}
-
-// Exclusive scan over the SW threads of the workgroup; the total too.  Every
-// thread must call it (it holds two barriers).
-template <uint32_t SW>
-__device__ __forceinline__ uint32_t group_excl_scan(uint32_t v, uint32_t *s_tmp, uint32_t &total) {
-    constexpr uint32_t NW = SW / 64;
-    const uint32_t inc = wave_incl_scan(v);
-    const uint32_t wid = threadIdx.x >> 6;
-    if (lane() == 63) s_tmp[wid] = inc;
-    __syncthreads();
-    uint32_t base = 0, tot = 0;
-#pragma unroll
-    for (uint32_t k = 0; k < NW; ++k) {
-        const uint32_t t = s_tmp[k];
-        base += k < wid ? t : 0;
-        tot += t;
-    }
-    __syncthreads();
-    total = tot;
-    return base + inc - v;
 }
 
 // Decoupled look-back for scan group u, run by one whole wave: publishes the
@@ -227,25 +197,34 @@ __device__ __forceinline__ void stage_enc(const EncTab &t, uint32_t tab) {
 
 // ------------------------------------------------------------------ stream reader
 
-// ROWB: bytes per LDS row.  Offsets are relative to the region's row 0.
-template <uint32_t ROWB>
-struct Reader {
-    static constexpr uint32_t kSh = log2c(ROWB) - 5;
-    int32_t q;   // stream bit position of the next code, minus 2
+// Rows are one wave's: 64 streams of 4 bytes.
+constexpr uint32_t US = kUnitStreams;
+constexpr uint32_t ROWB = US * 4;
+static_assert(ROWB == 256, "a unit row is 256 bytes: paired LDS accesses step one row per unit");
 
-    __device__ __forceinline__ void init() { q = -2; }
-    // The 32-bit window at q: stream bits q .. q+31 (the code at bit 2).
-    // row0: LDS offset of row 0; tcol: this lane's column (bytes); rows -1
-    // and `cap` are zero.
-    __device__ __forceinline__ uint32_t window(uint32_t row0, uint32_t tcol) const {
-        const uint32_t off = (((uint32_t)q << kSh) & ~(ROWB - 1)) | tcol;
-        const uint32_t a = ld32(row0 + off), b = ld32(row0 + off + ROWB);
+struct Reader {
+    // q: stream bit position of the next code, minus 2, plus 32 times the
+    // index of the stream's row 0 in LDS (row0 / ROWB), so that q / 32 is
+    // the LDS row to read and q % 32 the bit within it.
+    int32_t q;
+    uint32_t tcol;   // this lane's byte in a row
+
+    __device__ __forceinline__ static int32_t bias(uint32_t row0) { return (int32_t)(row0 / ROWB) * 32; }
+    __device__ __forceinline__ void init(uint32_t row0, uint32_t lane_) {
+        q = bias(row0) - 2;
+        tcol = 4 * lane_;
+    }
+    // The 32-bit window at q: stream bits q .. q+31 (the code at bit 2).  Rows
+    // -1 and `cap` are zero.
+    __device__ __forceinline__ uint32_t window() const {
+        const uint32_t off = (((uint32_t)q << 3) & ~(ROWB - 1)) | tcol;
+        const uint32_t a = ld32(off), b = ld32(off + ROWB);
         return __builtin_amdgcn_alignbit(b, a, (uint32_t)q);
     }
     // Next exponent field in bits 30..23 of the result (other bits garbage);
     // tab: the decode table.
-    __device__ __forceinline__ uint32_t next(uint32_t row0, uint32_t tcol, uint32_t tab) {
-        const uint32_t win = window(row0, tcol);
+    __device__ __forceinline__ uint32_t next(uint32_t tab) {
+        const uint32_t win = window();
         const uint32_t en = ld32(tab + (win & 0x3FCu));
         q += (en >> 8) & 0xFFu;
         return (win << (en & 31u)) | en;
@@ -258,9 +237,8 @@ struct Reader {
     // fields again with next().  q is kept at most qmax so that a bad group
     // never addresses past the stream's zero row.
     template <uint32_t N>
-    __device__ __forceinline__ uint32_t next_n(uint32_t row0, uint32_t tcol, uint32_t tab,
-                                               int32_t qmax, uint32_t (&e23)[N]) {
-        const uint32_t win = window(row0, tcol);
+    __device__ __forceinline__ uint32_t next_n(uint32_t tab, int32_t qmax, uint32_t (&e23)[N]) {
+        const uint32_t win = window();
         uint32_t c = 0;
 #pragma unroll
         for (uint32_t k = 0; k < N; ++k) {
@@ -276,23 +254,23 @@ struct Reader {
 
 // ------------------------------------------------------------------ stream writer
 
-template <uint32_t ROWB>
 struct Writer {
     static constexpr uint32_t kSh = log2c(ROWB) - 5;
     uint64_t buf;     // pending bits, LSB first (< 32 at every store step)
     uint32_t used;    // bits in buf
-    uint32_t woff;    // row * ROWB + this lane's column, relative to row 0
-    uint32_t tadj;    // column >> kSh, so that total() = (woff >> kSh) - tadj + used
+    uint32_t woff;    // LDS address: current row of this lane's column
+    uint32_t tadj;    // column address >> kSh, so that total() = (woff >> kSh) - tadj + used
     uint32_t live;    // no field has failed to fit yet
     uint32_t cs;      // coded prefix length
     uint32_t claimed; // staging space claimed for the spilled fields
     uint64_t soff;    // start of this stream's spilled fields in the staging area
 
-    __device__ __forceinline__ void init(uint32_t tcol, uint32_t n_s) {
+    // row0: LDS address of the output's row 0 (a multiple of ROWB).
+    __device__ __forceinline__ void init(uint32_t row0, uint32_t lane_, uint32_t n_s) {
         buf = 0;
         used = 0;
-        woff = tcol;
-        tadj = tcol >> kSh;
+        woff = row0 + 4 * lane_;
+        tadj = woff >> kSh;
         live = 1;
         cs = n_s;
         claimed = 0;
@@ -304,9 +282,9 @@ struct Writer {
     }
     // Store both words of the buffer at the current row and the next; move
     // on by a word when the first is full.
-    __device__ __forceinline__ void flush(uint32_t row0) {
-        st32(row0 + woff, (uint32_t)buf);
-        st32(row0 + woff + ROWB, (uint32_t)(buf >> 32));
+    __device__ __forceinline__ void flush() {
+        st32(woff, (uint32_t)buf);
+        st32(woff + ROWB, (uint32_t)(buf >> 32));
         const uint32_t t = used & 32u;
         buf >>= t;
         woff += t << kSh;
@@ -318,10 +296,9 @@ struct Writer {
 // Code the CH fields at positions j0..j0+CH-1, given as encode-table offsets
 // e8[] (8 * field); with CHECKED, positions at or past n_s are absent.  One
 // capacity test per step in the common case.
-template <uint32_t ROWB, bool CHECKED>
-__device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&e8)[CH], uint32_t j0,
-                                             uint32_t n_s, uint32_t capbits, uint32_t etab,
-                                             uint32_t row0) {
+template <bool CHECKED>
+__device__ __forceinline__ void writer_chunk(Writer &st, const uint32_t (&e8)[CH], uint32_t j0,
+                                             uint32_t n_s, uint32_t capbits, uint32_t etab) {
     uint32_t cb[CH], cl[CH];
 #pragma unroll
     for (uint32_t i = 0; i < CH; ++i) {
@@ -347,7 +324,7 @@ __device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&
         for (uint32_t k = 0; k < CH; k += 2) {
             st.put(cb[k], cl[k]);
             st.put(cb[k + 1], cl[k + 1]);
-            st.flush(row0);
+            st.flush();
         }
     } else {
 #pragma unroll
@@ -355,7 +332,7 @@ __device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&
             if (st.live) {
                 if (st.total() + cl[i] <= capbits) {
                     st.put(cb[i], cl[i]);
-                    st.flush(row0);
+                    st.flush();
                 } else {
                     st.live = 0;
                     st.cs = j0 + i;
@@ -368,8 +345,8 @@ __device__ __forceinline__ void writer_chunk(Writer<ROWB> &st, const uint32_t (&
 // Claim staging space for streams that started spilling in this step (one
 // atomic per wave), then park this step's spilled fields (e8[] = 8 * field)
 // there.  Every lane of the wave must reach it.
-template <uint32_t ROWB, bool CHECKED>
-__device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&e8)[CH], uint32_t j0,
+template <bool CHECKED>
+__device__ __forceinline__ void writer_spill(Writer &st, const uint32_t (&e8)[CH], uint32_t j0,
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
@@ -397,118 +374,118 @@ __device__ __forceinline__ void writer_spill(Writer<ROWB> &st, const uint32_t (&
     }
 }
 
-// Where a unit's results go.
-struct UnitOut {
-    uint32_t *pay;       // whole array
-    uint16_t *cnt;       // whole array
-    uint8_t *scratch;
-    uint64_t nblk, ovf_cap;
-    uint32_t cap;
-};
+// ------------------------------------------------------------------ units
 
-// After the stream loop: the unit's payload rows (LDS rows of SW words from
-// byte offset row0) go out; spilled fields, if any, are gathered from the
-// per-stream staging pieces into one piece of the second staging area in
-// (stream, position) order, and the unit's record says where; then the
-// counts.  `before` runs just before cnt is written (the fused update waits
-// there until the block's other units have read theirs).  The overflow
-// offsets and the fields' final places are the scan kernel's work.
-template <uint32_t SW, typename Before>
-__device__ void writer_finish(uint32_t cs, uint64_t soff, uint32_t n_s, uint32_t u, uint32_t b,
-                              uint32_t h, uint32_t row0, uint32_t *s_tmp, uint64_t *s_base,
-                              const UnitOut &o, Before before) {
-    const uint32_t t = threadIdx.x;
-    const uint32_t spill = n_s - cs;
-    uint32_t total;
-    const uint32_t excl = group_excl_scan<SW>(spill, s_tmp, total);   // barriers: LDS rows complete
-    // payload: cap rows of SW words (16-byte pieces)
-    constexpr uint32_t Q = SW / 4;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(lds) + row0);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(o.pay);
-    for (uint32_t i = t; i < o.cap * Q; i += SW) {
-        const uint32_t row = i / Q, c = i % Q;
-        dst[(((uint64_t)b * o.cap + row) * NS + h * SW) / 4 + c] = src[i];
-    }
-    uint64_t base = 0;
-    if (total) {
-        if (t == 0)
-            *s_base = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
-                                (unsigned long long)total);
-        __syncthreads();
-        base = *s_base;
-        const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
-        uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
-        for (uint32_t k = 0; k < spill; ++k) {
-            const uint64_t from = soff + k, to = base + excl + k;
-            if (from < o.ovf_cap && to < o.ovf_cap) stage2[to] = stage[from];
-        }
-    }
-    if (t == 0) {
-        UnitRec *rec = reinterpret_cast<UnitRec *>(o.scratch + scr_rec_offset(o.nblk));
-        rec[u] = UnitRec{total, base};
-    }
-    before();
-    o.cnt[(uint64_t)b * NS + h * SW + t] = (uint16_t)cs;
+// Unit u is streams (u % kMaxUnits) * US .. +US of block u / kMaxUnits.
+__device__ __forceinline__ uint32_t unit_block(uint32_t u) { return u / kMaxUnits; }
+__device__ __forceinline__ uint32_t unit_part(uint32_t u) { return u % kMaxUnits; }
+
+// Wave g of the grid does unit g; persistent waves then take units g + S,
+// g + 2S, ... with S the number of waves in the grid (units are alike in
+// work, so round-robin spreads them evenly).
+__device__ __forceinline__ uint32_t first_unit(uint32_t waves) {
+    return blockIdx.x * waves + (threadIdx.x >> 6);
 }
 
-// Copy rows [0, cap) of a unit's columns of a block's payload into LDS rows of
-// SW words from byte offset row0; with a second source (pay2 != nullptr) its
-// rows go to row2 as well.  Up to 8 pieces per source are loaded before any is
-// stored, so the copy waits for memory a few times rather than once per piece.
-template <uint32_t SW>
-__device__ __forceinline__ void stage_rows(const uint32_t *pay, uint32_t row0, const uint32_t *pay2,
-                                           uint32_t row2, uint64_t b, uint32_t h, uint32_t cap) {
-    constexpr uint32_t Q = SW / 4;
-    constexpr uint32_t K = 8;
-    const uint32_t total = cap * Q;
+// Copy a unit's payload rows (cap rows of 64 words: cap * 16 pieces of 16
+// bytes, piece p of row p / 16) to LDS from row0; with a second source (pay2)
+// its rows go to row2 as well.  Up to 8 pieces per lane and source are loaded
+// before any is stored, so a unit's start waits for memory about once.  The
+// loads are unconditional (a lane past the last piece loads the last piece
+// again) so that no branch splits them; only the stores are skipped.
+__device__ __forceinline__ void rows_to_lds(const uint32_t *pay, uint32_t row0, const uint32_t *pay2,
+                                            uint32_t row2, uint32_t b, uint32_t h, uint32_t cap) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(pay);
     const u32x4 *src2 = reinterpret_cast<const u32x4 *>(pay2);
-    for (uint32_t base = 0; base < total; base += K * SW) {
-        u32x4 v[K], v2[K];
+    const uint32_t np = cap * 16;
+    for (uint32_t base = 0; base < np; base += 8 * 64) {
+        u32x4 v[8], v2[8];
 #pragma unroll
-        for (uint32_t k = 0; k < K; ++k) {
-            const uint32_t i = base + k * SW + threadIdx.x;
-            const uint64_t g = ((b * cap + i / Q) * NS + h * SW) / 4 + i % Q;
-            if (i < total) {
+        for (uint32_t k = 0; k < 8; ++k) {
+            const uint32_t p = min(base + k * 64 + lane(), np - 1);
+            const uint64_t g = (((uint64_t)b * cap + p / 16) * NS + h * US) / 4 + p % 16;
+            if (base + k * 64 < np) {
                 v[k] = src[g];
                 if (pay2) v2[k] = src2[g];
             }
         }
 #pragma unroll
-        for (uint32_t k = 0; k < K; ++k) {
-            const uint32_t i = base + k * SW + threadIdx.x;
-            if (i < total) {
-                st128(row0 + 16 * i, v[k]);
-                if (pay2) st128(row2 + 16 * i, v2[k]);
+        for (uint32_t k = 0; k < 8; ++k) {
+            const uint32_t p = base + k * 64 + lane();
+            if (p < np) {
+                st128(row0 + 16 * p, v[k]);
+                if (pay2) st128(row2 + 16 * p, v2[k]);
             }
         }
     }
 }
 
-// Spill layout of a block as unit h sees it: this stream's coded count, the
-// number of spilled fields of the block's streams before it, the block total.
-template <uint32_t SW, uint32_t H>
-__device__ __forceinline__ void block_spills(const uint16_t *cnt_b, uint32_t nb, uint32_t h,
-                                             uint32_t *s_tmp, uint32_t &c_own, uint32_t &excl,
-                                             uint32_t &block_total) {
-    uint32_t base = 0, mine = 0, all = 0;
+// Spill layout of a block (general paths): this lane's stream's coded count
+// and the number of spilled fields of the block's streams before it.
+__device__ __forceinline__ void unit_spills(const uint16_t *cnt_b, uint32_t nb, uint32_t h,
+                                            uint32_t &c_own, uint32_t &excl) {
+    uint32_t before = 0;
     c_own = 0;
+    excl = 0;
 #pragma unroll
-    for (uint32_t k = 0; k < H; ++k) {
-        const uint32_t s = k * SW + threadIdx.x;
+    for (uint32_t k = 0; k < kMaxUnits; ++k) {
+        const uint32_t s = k * US + lane();
         const uint32_t n_s = stream_len(nb, s);
         const uint32_t c = min<uint32_t>(cnt_b[s], n_s);
-        uint32_t tot;
-        const uint32_t ex = group_excl_scan<SW>(n_s - c, s_tmp, tot);
-        if (k < h) base += tot;
+        const uint32_t sp = n_s - c;
+        const uint32_t inc = wave_incl_scan(sp);
+        if (k < h) before += __shfl(inc, 63, 64);
         if (k == h) {
-            mine = ex;
             c_own = c;
+            excl = inc - sp;
         }
-        all += tot;
     }
-    excl = base + mine;
-    block_total = all;
+    excl += before;
+}
+
+// Where a unit's results go.
+struct UnitOut {
+    uint32_t *pay;       // whole array
+    uint16_t *cnt;       // whole array (or the parking area in scratch)
+    uint8_t *scratch;
+    uint64_t nblk, ovf_cap;
+    uint32_t cap, parked;
+};
+
+// After a unit's stream loop: its payload rows (the wave's LDS rows from
+// address row0) go out; its spilled fields, if any, are gathered from the
+// per-stream staging pieces into one piece of the second staging area in
+// (stream, position) order; its record says where; then its counts.  The
+// overflow offsets and the fields' final places are the scan kernel's work.
+__device__ void unit_finish(const Writer &st, uint32_t n_s, uint32_t u, uint32_t b, uint32_t h,
+                            uint32_t row0, const UnitOut &o) {
+    const uint32_t l = lane();
+    const uint32_t spill = n_s - st.cs;
+    const uint32_t inc = wave_incl_scan(spill);
+    const uint32_t total = __shfl(inc, 63, 64);
+    const uint32_t excl = inc - spill;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(o.pay);
+    for (uint32_t p = l; p < o.cap * 16; p += 64)
+        dst[(((uint64_t)b * o.cap + p / 16) * NS + h * US) / 4 + p % 16] = ld128(row0 + 16 * p);
+    uint64_t base = 0;
+    if (total) {
+        unsigned long long t = 0;
+        if (l == 0)
+            t = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
+                          (unsigned long long)total);
+        base = __shfl(t, 0, 64);
+        const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
+        uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
+        for (uint32_t k = 0; k < spill; ++k) {
+            const uint64_t from = st.soff + k, to = base + excl + k;
+            if (from < o.ovf_cap && to < o.ovf_cap) stage2[to] = stage[from];
+        }
+    }
+    if (l == 0) {
+        UnitRec *rec = reinterpret_cast<UnitRec *>(o.scratch + scr_rec_offset(o.nblk));
+        rec[u] = UnitRec{base, total, o.parked};
+    }
+    o.cnt[(uint64_t)b * NS + h * US + l] = (uint16_t)st.cs;
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -521,24 +498,25 @@ __global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
 
 // Overflow offsets: an exclusive scan of the units' spill totals in unit
 // order (block, then its units), one unit per thread, groups chained by the
-// look-back.  Writes obase, flags a too-small overflow region, then copies
-// each of its units' spilled fields from the second staging area to their
-// place in the overflow region.
-__global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t nblk, uint32_t H,
-                                                     uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
-                                                     uint32_t *status) {
+// look-back.  Writes obase, flags a too-small overflow region, copies each of
+// its units' spilled fields from the second staging area to their place in
+// the overflow region, and puts parked counts in place.
+__global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase,
+                                                     uint8_t *ovf, uint64_t ovf_cap, uint32_t *status,
+                                                     uint16_t *cnt) {
     __shared__ uint32_t s_g;
     __shared__ uint64_t s_wave[kScanGroup / 64], s_excl;
-    __shared__ uint64_t s_tot[kScanGroup], s_from[kScanGroup], s_to[kScanGroup];
+    __shared__ uint64_t s_from[kScanGroup], s_to[kScanGroup];
+    __shared__ uint32_t s_tot[kScanGroup], s_flags[kScanGroup];
     const uint32_t t = threadIdx.x;
     if (t == 0) s_g = atomicAdd(reinterpret_cast<uint32_t *>(scratch + kScrTicket2), 1u);
     __syncthreads();
     const uint32_t g = s_g;
-    const uint64_t nunits = nblk * H;
+    const uint64_t nunits = nblk * kMaxUnits;
     const uint64_t u = (uint64_t)g * kScanGroup + t;
     const UnitRec *rec = reinterpret_cast<const UnitRec *>(scratch + scr_rec_offset(nblk));
-    const UnitRec r = u < nunits ? rec[u] : UnitRec{0, 0};
-    // group scan of 64-bit totals
+    const UnitRec r = u < nunits ? rec[u] : UnitRec{0, 0, 0};
+    // group scan of the totals (64-bit sums)
     uint64_t inc = r.total;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -555,13 +533,13 @@ __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t 
     }
     inc += before;
     if (t < 64) {
-        uint64_t *flags = reinterpret_cast<uint64_t *>(scratch + scr_flags_offset(nblk));
+        uint64_t *flags = reinterpret_cast<uint64_t *>(scratch + kScrFlags);
         const uint64_t ex = lookback(flags, g, agg, status);
         if (t == 0) s_excl = ex;
     }
     __syncthreads();
     const uint64_t ex = s_excl + inc - r.total;
-    if (u < nunits && u % H == 0) obase[u / H] = ex;
+    if (u < nunits && u % kMaxUnits == 0) obase[u / kMaxUnits] = ex;
     if (u + 1 == nunits) {
         obase[nblk] = ex + r.total;
         if (ex + r.total > ovf_cap) atomicOr(status, LCT_ST_OVF_FULL);
@@ -569,9 +547,17 @@ __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t 
     s_tot[t] = r.total;
     s_from[t] = r.base;
     s_to[t] = ex;
+    s_flags[t] = r.flags;
     __syncthreads();
     const uint8_t *stage2 = scratch + scr_stage2_offset(nblk, ovf_cap);
+    const uint16_t *parked = reinterpret_cast<const uint16_t *>(scratch + scr_cnt_offset(nblk));
     for (uint32_t k = 0; k < kScanGroup; ++k) {
+        const uint64_t uk = (uint64_t)g * kScanGroup + k;
+        if (uk >= nunits) break;
+        if (s_flags[k] & 1u) {
+            const uint64_t at = (uk / kMaxUnits) * NS + (uk % kMaxUnits) * US;
+            if (t < US) cnt[at + t] = parked[at + t];
+        }
         const uint64_t n = s_tot[k];
         if (n == 0) continue;
         const uint64_t from = s_from[k], to = s_to[k];
@@ -591,12 +577,19 @@ __global__ void k_gather(const uint16_t *x, uint64_t n, uint32_t m) {
 
 // Positions [j0, j0+CH) of one lane's stream from base (the lane's position 0,
 // positions NS apart); with GUARD, positions at or past n_s read as 0.
+// The second half of a chunk is addressed from its own base, so that every
+// access's offset fits the instruction's immediate (16 positions of 2-byte
+// values span 7.5 KiB).
 template <bool GUARD, typename T>
 __device__ __forceinline__ void load_chunk(uint32_t (&dst)[CH], const T *base, uint32_t j0,
                                            uint32_t n_s) {
     const T *p = base + (size_t)j0 * NS;
+    const T *p2 = p + (CH / 2) * NS;
 #pragma unroll
-    for (uint32_t i = 0; i < CH; ++i) dst[i] = (!GUARD || j0 + i < n_s) ? (uint32_t)p[i * NS] : 0u;
+    for (uint32_t i = 0; i < CH; ++i) {
+        const T *q = i < CH / 2 ? p + i * NS : p2 + (i - CH / 2) * NS;
+        dst[i] = (!GUARD || j0 + i < n_s) ? (uint32_t)*q : 0u;
+    }
 }
 
 // Runs step(buf, j0) over the positions of a stream, CH at a time, with the
@@ -624,19 +617,20 @@ struct Buf2 {
     uint32_t w[CH], m[CH];
 };
 
-// ------------------------------------------------------------------ encode
-
-constexpr uint32_t kEncH = kEncUnits, kEncSW = NS / kEncH, kEncRowB = kEncSW * 4;
-// LDS: encode table, then the output rows (cap + 2 sink rows).
-constexpr uint32_t kEncTab = 256, kEncRow0 = 2304;
-
 template <uint32_t CAPT>
 __device__ __forceinline__ uint32_t cap_of(uint32_t rt) { return CAPT ? CAPT : rt; }
 
+// ------------------------------------------------------------------ encode
+
+// LDS: encode table, then per wave the output rows (cap + 2 sink rows).
+constexpr uint32_t kEncWaves = 4;
+constexpr uint32_t kEncTab = 256, kEncWave0 = 2304;
+__host__ __device__ constexpr uint32_t enc_wave_bytes(uint32_t cap) { return (cap + 2) * ROWB; }
+
 template <bool FULL, uint32_t CAPT>
-__device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer<kEncRowB> &st,
-                                              uint32_t n_s, uint64_t r0) {
-    const uint32_t s = threadIdx.x;
+__device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer &st, uint32_t n_s,
+                                              uint64_t r0) {
+    const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t capbits = 32 * cap_of<CAPT>(p.cap_words);
     const uint16_t *xs = p.x + r0 + s;
@@ -653,62 +647,58 @@ __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer<kEnc
                 e[i] = (bf.v[i] >> 4) & 0x7F8u;   // 8 * exponent field
                 if (FULL || j0 + i < n_s) o[i * NS] = (uint8_t)sf_of(bf.v[i]);
             }
-            writer_chunk<kEncRowB, !FULL>(st, e, j0, n_s, capbits, kEncTab, kEncRow0);
-            writer_spill<kEncRowB, !FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
+            writer_chunk<!FULL>(st, e, j0, n_s, capbits, kEncTab);
+            writer_spill<!FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
 }
 
 template <uint32_t CAPT>
-__global__ __launch_bounds__(256) void k_encode(const EncodeParams p) {
-    uint32_t *s_tmp = s_tmp_ptr();
-    uint32_t &s_ticket = *s_ticket_ptr();
-    uint64_t &s_ob = *s_ob_ptr();
-    constexpr uint32_t SW = kEncSW;
-    const uint32_t t = threadIdx.x;
-    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+__global__ __launch_bounds__(64 * kEncWaves) void k_encode(const EncodeParams p) {
     stage_enc(p.enc, kEncTab);
-    const uint32_t tcol = 4 * t;
-    for (uint32_t w = 0; w < cap; ++w) st32(kEncRow0 + w * kEncRowB + tcol, 0);
-    if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
     __syncthreads();
-    const uint32_t u = s_ticket;
-    const uint32_t nunits = p.nblk * kEncH;
-    if (u >= nunits) return;   // only if the scratch header was not cleared
-    const uint32_t b = u / kEncH, h = u % kEncH;
+    const uint32_t l = lane();
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const uint32_t out0 = kEncWave0 + (threadIdx.x >> 6) * enc_wave_bytes(cap);
+    const uint32_t u = first_unit(kEncWaves);
+    if (u >= p.nblk * kMaxUnits) return;
+    const uint32_t b = unit_block(u), h = unit_part(u);
+    for (uint32_t w = 0; w < cap; ++w) st32(out0 + w * ROWB + 4 * l, 0);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
-    const uint32_t n_s = stream_len(nb, h * SW + t);
-    Writer<kEncRowB> st;
-    st.init(tcol, n_s);
+    const uint32_t n_s = stream_len(nb, h * US + l);
+    Writer st;
+    st.init(out0, l, n_s);
     if (nb == p.block_elems)
-        encode_stream<true, CAPT>(p, st, n_s, r0 + h * SW);
+        encode_stream<true, CAPT>(p, st, n_s, r0 + h * US);
     else
-        encode_stream<false, CAPT>(p, st, n_s, r0 + h * SW);
-    const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap};
-    writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, kEncRow0, s_tmp, &s_ob, o, [] {});
+        encode_stream<false, CAPT>(p, st, n_s, r0 + h * US);
+    const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0};
+    unit_finish(st, n_s, u, b, h, out0, o);
 }
 
 // ------------------------------------------------------------------ decode
 
-// LDS: decode table, zero row -1, rows 0..cap-1, zero row cap.
-constexpr uint32_t kDecRowB = NS * 4;
-constexpr uint32_t kDecTab = 256, kDecRowM1 = 1280, kDecRow0 = 1280 + kDecRowB;
+// LDS: decode table, then per wave: zero row -1, rows 0..cap-1, zero row cap.
+constexpr uint32_t kDecWaves = 4;
+constexpr uint32_t kDecTab = 256, kDecWave0 = 1280;
+__host__ __device__ constexpr uint32_t dec_wave_bytes(uint32_t cap) { return (cap + 2) * ROWB; }
 
 template <bool FAST, uint32_t CAPT>
-__device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_s, uint32_t c_s,
-                                              uint64_t r0, uint64_t sp0) {
-    const uint32_t s = threadIdx.x;
-    const uint32_t tcol = 4 * s;
+__device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t row0, uint32_t n_s,
+                                              uint32_t c_s, uint64_t r0, uint64_t sp0) {
+    const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
-    const int32_t qmax = 32 * (int32_t)cap_of<CAPT>(p.cap_words) - 2;
+    const int32_t qmax = Reader::bias(row0) + 32 * (int32_t)cap_of<CAPT>(p.cap_words) - 2;
     const uint8_t *sfs = p.sf + r0 + s;
     uint16_t *ys = p.y + r0 + s;
-    Reader<kDecRowB> rd;
-    rd.init();
+    Reader rd;
+    rd.init(row0, s);
     double_buffered<Buf1>(
         npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FAST>(bf.v, sfs, j0, n_s); },
         [&](Buf1 &bf, uint32_t j0) {
             uint16_t *o = ys + (size_t)j0 * NS;
+            uint16_t *o2 = o + (CH / 2) * NS;
+            auto out = [&](uint32_t i) -> uint16_t & { return i < CH / 2 ? o[i * NS] : o2[(i - CH / 2) * NS]; };
             if (FAST) {
                 // four fields per window; a chunk where some window ran out
                 // (long escapes) is decoded again one field per window
@@ -717,18 +707,18 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_
 #pragma unroll
                 for (uint32_t g = 0; g < CH; g += 4) {
                     uint32_t e23[4];
-                    cmax = max(cmax, rd.next_n<4>(kDecRow0, tcol, kDecTab, qmax, e23));
+                    cmax = max(cmax, rd.next_n<4>(kDecTab, qmax, e23));
 #pragma unroll
                     for (uint32_t k = 0; k < 4; ++k)
-                        o[(g + k) * NS] = (uint16_t)(join32(bf.v[g + k], e23[k]) >> 16);
+                        out(g + k) = (uint16_t)(join32(bf.v[g + k], e23[k]) >> 16);
                 }
                 if (__builtin_expect(!__all(cmax <= 30), 0)) {
                     rd.q = q0;
 #pragma unroll
                     for (uint32_t i = 0; i < CH; ++i) {
-                        const uint32_t e23 = rd.next(kDecRow0, tcol, kDecTab);
+                        const uint32_t e23 = rd.next(kDecTab);
                         rd.q = min(rd.q, qmax);
-                        o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
+                        out(i) = (uint16_t)(join32(bf.v[i], e23) >> 16);
                     }
                 }
                 return;
@@ -736,68 +726,75 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t n_
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
                 const uint32_t j = j0 + i;
-                uint32_t e23 = rd.next(kDecRow0, tcol, kDecTab);
+                uint32_t e23 = rd.next(kDecTab);
                 rd.q = min(rd.q, qmax);
                 if (j >= c_s && j < n_s) {
                     const uint64_t k = sp0 + (j - c_s);
                     e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
                 }
                 // the BF16 value is the top half of its fp32 form
-                if (j < n_s) o[i * NS] = (uint16_t)(join32(bf.v[i], e23) >> 16);
+                if (j < n_s) out(i) = (uint16_t)(join32(bf.v[i], e23) >> 16);
             }
         });
 }
 
 template <uint32_t CAPT>
-__global__ __launch_bounds__(256) void k_decode(const DecodeParams p) {
-    uint32_t *s_tmp = s_tmp_ptr();
-    const uint32_t t = threadIdx.x, b = blockIdx.x;
-    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+__global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p) {
     stage_dec(p.dec, kDecTab);
-    stage_rows<NS>(p.pay, kDecRow0, nullptr, 0, b, 0, cap);
-    st32(kDecRowM1 + 4 * t, 0);
-    st32(kDecRow0 + cap * kDecRowB + 4 * t, 0);
+    __syncthreads();
+    const uint32_t l = lane();
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const uint32_t base = kDecWave0 + (threadIdx.x >> 6) * dec_wave_bytes(cap);
+    const uint32_t row0 = base + ROWB;
+    st32(base + 4 * l, 0);                      // row -1
+    st32(row0 + cap * ROWB + 4 * l, 0);         // row cap
+    const uint32_t u = first_unit(kDecWaves);
+    if (u >= p.nblk * kMaxUnits) return;
+    const uint32_t b = unit_block(u), h = unit_part(u);
+    rows_to_lds(p.pay, row0, nullptr, 0, b, h, cap);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
-    const uint32_t n_s = stream_len(nb, t);
-    uint32_t c_s, excl, total;
-    block_spills<NS, 1>(p.cnt + (uint64_t)b * NS, nb, 0, s_tmp, c_s, excl, total);  // barriers
-    const uint64_t sp0 = p.obase[b] + excl;
-    if (nb == p.block_elems && total == 0)
-        decode_stream<true, CAPT>(p, n_s, c_s, r0, sp0);
-    else
-        decode_stream<false, CAPT>(p, n_s, c_s, r0, sp0);
+    const uint32_t n_s = stream_len(nb, h * US + l);
+    const uint64_t ob0 = p.obase[b], ob1 = p.obase[b + 1];
+    if (nb == p.block_elems && ob0 == ob1) {
+        decode_stream<true, CAPT>(p, row0, n_s, n_s, r0 + h * US, 0);
+    } else {
+        uint32_t c_s, excl;
+        unit_spills(p.cnt + (uint64_t)b * NS, nb, h, c_s, excl);
+        decode_stream<false, CAPT>(p, row0, n_s, c_s, r0 + h * US, ob0 + excl);
+    }
 }
 
 // ------------------------------------------------------------------ fused SGD
 
-constexpr uint32_t kSgdH = kSgdUnits, kSgdSW = NS / kSgdH, kSgdRowB = kSgdSW * 4;
-constexpr uint32_t kSgdWaves = kSgdSW / 64;
+constexpr uint32_t kSgdWaves = 2;
 // Sign-fraction slabs of the full-block path: per wave, kSlabPos positions of
 // its 64 streams for W (also the result's bytes, written in place) and for M.
 constexpr uint32_t kSlabPos = 2 * CH;
-constexpr uint32_t kSlabB = kSlabPos * 64;
-// LDS: W and M decode tables, the W encode table, the slabs, then rows.
-constexpr uint32_t kSgdWTab = 256, kSgdMTab = 1280, kSgdETab = 2304, kSgdSlab = 4352;
-constexpr uint32_t kSgdRows = kSgdSlab + kSgdWaves * 2 * kSlabB;
-static_assert(kSgdRows % 256 == 0, "rows must start on a 256-byte boundary");
+constexpr uint32_t kSlabB = kSlabPos * US;
+// LDS: W and M decode tables, the W encode table, then per wave the slabs and
+// the rows.
+constexpr uint32_t kSgdWTab = 256, kSgdMTab = 1280, kSgdETab = 2304, kSgdWave0 = 4352;
 
-// Rows (kSgdRowB bytes each): the output's rows 0..cap-1 and its two sink
-// rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row cap and M's
-// row -1); M's rows; a zero row.  With cap >= 18 the output's sink rows are
-// W's row -1 and row 0: a stream's output reaches row cap-1 only after
-// 2*(cap-1) >= 34 fields, when its own W reader has left rows -1 and 0.
+// A wave's region (from `base`): the slabs; the output's rows 0..cap-1 and
+// its two sink rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row
+// cap and M's row -1); M's rows; a zero row.  With cap >= 18 the output's
+// sink rows are W's row -1 and row 0: a stream's output reaches row cap-1 only
+// after 2*(cap-1) >= 34 fields, when its own W reader has left rows -1 and 0.
 struct SgdLayout {
-    uint32_t out0, z0, w0, z1, m0, z2, end;
-    __host__ __device__ constexpr SgdLayout(uint32_t cap)
-        : out0(kSgdRows),
-          z0(kSgdRows + (cap >= 18 ? cap : cap + 2) * kSgdRowB),
-          w0(z0 + kSgdRowB),
-          z1(w0 + cap * kSgdRowB),
-          m0(z1 + kSgdRowB),
-          z2(m0 + cap * kSgdRowB),
-          end(z2 + kSgdRowB) {}
+    uint32_t sw, sm, out0, z0, w0, z1, m0, z2, end;
+    __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base)
+        : sw(base),
+          sm(base + kSlabB),
+          out0(base + 2 * kSlabB),
+          z0(base + 2 * kSlabB + (cap >= 18 ? cap : cap + 2) * ROWB),
+          w0(z0 + ROWB),
+          z1(w0 + cap * ROWB),
+          m0(z1 + ROWB),
+          z2(m0 + cap * ROWB),
+          end(z2 + ROWB) {}
 };
+__host__ __device__ constexpr uint32_t sgd_wave_bytes(uint32_t cap) { return SgdLayout(cap, 0).end; }
 
 // One element: rne_bf16(fmaf(-eta, m, w)) in bits 31..16 of the result (bits
 // 15..0 hold rounding garbage); a NaN gives 0x7FC0.
@@ -829,24 +826,23 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 // General path: partial blocks and inputs with spilled fields; byte-wide
 // accesses with per-element checks.
 template <uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream_general(const SgdParams &p, Writer<kSgdRowB> &st,
+__device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, Writer &st,
                                                    uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
                                                    uint64_t r0, uint64_t wsp, uint64_t msp) {
-    const uint32_t s = threadIdx.x;
-    const uint32_t tcol = 4 * s;
+    const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap);
     const uint32_t capbits = 32 * cap;
-    const int32_t qmax = (int32_t)capbits - 2;
+    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
+    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
     const uint8_t *wsf = p.w_sf + r0 + s;
     const uint8_t *msf = p.m_sf + r0 + s;
     uint8_t *osf = p.o_sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    Reader<kSgdRowB> rw, rm;
-    rw.init();
-    rm.init();
+    Reader rw, rm;
+    rw.init(lay.w0, s);
+    rm.init(lay.m0, s);
     double_buffered<Buf2>(
         npos,
         [&](Buf2 &bf, uint32_t j0) {
@@ -859,10 +855,10 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, Writer<kS
 #pragma unroll
             for (uint32_t i = 0; i < CH; ++i) {
                 const uint32_t j = j0 + i;
-                uint32_t ew = rw.next(lay.w0, tcol, kSgdWTab);
-                uint32_t em = rm.next(lay.m0, tcol, kSgdMTab);
-                rw.q = min(rw.q, qmax);
-                rm.q = min(rm.q, qmax);
+                uint32_t ew = rw.next(kSgdWTab);
+                uint32_t em = rm.next(kSgdMTab);
+                rw.q = min(rw.q, qwmax);
+                rm.q = min(rm.q, qmmax);
                 if (j >= cw_s && j < n_s) {
                     const uint64_t k = wsp + (j - cw_s);
                     ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
@@ -875,14 +871,14 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, Writer<kS
                 if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
                 e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
             }
-            writer_chunk<kSgdRowB, true>(st, e, j0, n_s, capbits, kSgdETab, lay.out0);
-            writer_spill<kSgdRowB, true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
+            writer_chunk<true>(st, e, j0, n_s, capbits, kSgdETab);
+            writer_spill<true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
 }
 
 // Full-block path (every stream has npos elements and no input field spilled).
-// The sign-fraction bytes of W and M arrive through per-wave LDS slabs: lane l
-// moves the 16 bytes of position l/4, streams 16*(l%4).. of its wave, twice
+// The sign-fraction bytes of W and M arrive through the wave's LDS slabs: lane
+// l moves the 16 bytes of position l/4, streams 16*(l%4).. of the unit, twice
 // per slab (positions +0 and +CH), with one 16-byte load each; the result's
 // bytes overwrite W's in the slab and leave with one 16-byte store each.  The
 // next slab's loads are in flight while the current one is worked on.
@@ -891,28 +887,26 @@ struct SlabRegs {
 };
 
 template <uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdRowB> &st,
+__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, Writer &st,
                                                 uint64_t r0) {
-    const uint32_t t = threadIdx.x, l = lane(), wv = t >> 6;
-    const uint32_t tcol = 4 * t;
+    const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap);
     const uint32_t capbits = 32 * cap;
-    const int32_t qmax = (int32_t)capbits - 2;
-    const uint32_t sw = kSgdSlab + wv * 2 * kSlabB, sm = sw + kSlabB;
+    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
+    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    const uint32_t sw = lay.sw, sm = lay.sm;
     const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a slab
-    const uint32_t col = l;                       // this lane's byte in a slab row
-    const uint64_t g = r0 + 64 * wv + (uint64_t)(l >> 2) * NS + 16 * (l & 3);
+    const uint64_t g = r0 + (uint64_t)(l >> 2) * NS + 16 * (l & 3);
     const uint8_t *gw = p.w_sf + g;
     const uint8_t *gm = p.m_sf + g;
     uint8_t *go = p.o_sf + g;
     constexpr uint64_t kHalf = (uint64_t)CH * NS;   // bytes between the slab's halves
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    Reader<kSgdRowB> rw, rm;
-    rw.init();
-    rm.init();
+    Reader rw, rm;
+    rw.init(lay.w0, l);
+    rm.init(lay.m0, l);
     // Always four loads (a slab that is only half inside the block loads its
     // first half twice), so that the number of loads in flight is the same on
     // every path and the wait for one slab never includes the next one's.
@@ -924,15 +918,12 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdR
         r.w1 = *reinterpret_cast<const u32x4 *>(gw + o1);
         r.m1 = *reinterpret_cast<const u32x4 *>(gm + o1);
     };
-    // The slab bytes are read before and written after the decode loop, so no
-    // LDS store sits between one field's table read and the next field's
-    // window read: the two W/M reader chains then overlap the arithmetic.
     auto half = [&](uint32_t j0, uint32_t row) {
         uint32_t ws[CH], ms[CH], H[CH / 2], e[CH];
 #pragma unroll
         for (uint32_t i = 0; i < CH; ++i) {
-            ws[i] = ld8(sw + (row + i) * 64 + col);
-            ms[i] = ld8(sm + (row + i) * 64 + col);
+            ws[i] = ld8(sw + (row + i) * US + l);
+            ms[i] = ld8(sm + (row + i) * US + l);
         }
         // Four fields per window and reader, software-pipelined: step k of a
         // group issues both readers' k-th table lookups, and the arithmetic of
@@ -948,40 +939,40 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdR
         uint32_t ew[CH], em[CH];
         float r[CH];
 #pragma unroll
-        for (uint32_t g = 0; g <= CH; g += 4) {
+        for (uint32_t gi = 0; gi <= CH; gi += 4) {
             uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
-            if (g < CH) {
-                winw = rw.window(lay.w0, tcol);
-                winm = rm.window(lay.m0, tcol);
+            if (gi < CH) {
+                winw = rw.window();
+                winm = rm.window();
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
                 uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
-                if (g < CH) {
+                if (gi < CH) {
                     wkw = winw >> cw;
                     wkm = winm >> cm;
                     enw = ld32(kSgdWTab + (wkw & 0x3FCu));
                     enm = ld32(kSgdMTab + (wkm & 0x3FCu));
                 }
-                if (g > 0) {
-                    const uint32_t i = g - 4 + k;
+                if (gi > 0) {
+                    const uint32_t i = gi - 4 + k;
                     r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32(ms[i], em[i])),
                                           __uint_as_float(join32(ws[i], ew[i])));
                     nan |= r[i] != r[i];
                     if (k & 1) H[i / 2] = cvt_bf16x2(r[i - 1], r[i]);
                 }
-                if (g < CH) {
-                    ew[g + k] = (wkw << (enw & 31u)) | enw;
-                    em[g + k] = (wkm << (enm & 31u)) | enm;
+                if (gi < CH) {
+                    ew[gi + k] = (wkw << (enw & 31u)) | enw;
+                    em[gi + k] = (wkm << (enm & 31u)) | enm;
                     cw += (enw >> 8) & 0xFFu;
                     cm += (enm >> 8) & 0xFFu;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (g < CH) {
-                rw.q = min(rw.q + (int32_t)cw, qmax);
-                rm.q = min(rm.q + (int32_t)cm, qmax);
+            if (gi < CH) {
+                rw.q = min(rw.q + (int32_t)cw, qwmax);
+                rm.q = min(rm.q + (int32_t)cm, qmmax);
                 cmax = max(cmax, max(cw, cm));
             }
         }
@@ -991,10 +982,10 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdR
                 rm.q = qm0;
 #pragma unroll
                 for (uint32_t i = 0; i < CH; ++i) {
-                    ew[i] = rw.next(lay.w0, tcol, kSgdWTab);
-                    em[i] = rm.next(lay.m0, tcol, kSgdMTab);
-                    rw.q = min(rw.q, qmax);
-                    rm.q = min(rm.q, qmax);
+                    ew[i] = rw.next(kSgdWTab);
+                    em[i] = rm.next(kSgdMTab);
+                    rw.q = min(rw.q, qwmax);
+                    rm.q = min(rm.q, qmmax);
                 }
             }
 #pragma unroll
@@ -1012,11 +1003,11 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdR
             const uint32_t h = H[i / 2], t = h >> 8;
             e[i] = (h >> 4) & 0x7F8u;
             e[i + 1] = (h >> 20) & 0x7F8u;
-            st8(sw + (row + i) * 64 + col, (h & 0x7Fu) | (t & 0x80u));
-            st8(sw + (row + i + 1) * 64 + col, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
+            st8(sw + (row + i) * US + l, (h & 0x7Fu) | (t & 0x80u));
+            st8(sw + (row + i + 1) * US + l, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
         }
-        writer_chunk<kSgdRowB, false>(st, e, j0, npos, capbits, kSgdETab, lay.out0);
-        writer_spill<kSgdRowB, false>(st, e, j0, npos, stage_ctr, stage, p.ovf_cap);
+        writer_chunk<false>(st, e, j0, npos, capbits, kSgdETab);
+        writer_spill<false>(st, e, j0, npos, stage_ctr, stage, p.ovf_cap);
     };
     // A slab's result bytes are read into registers at the end of its step
     // and stored after the next slab has been staged: the memory-counter wait
@@ -1064,66 +1055,50 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, Writer<kSgdR
 }
 
 template <uint32_t CAPT>
-__global__ __launch_bounds__(128) void k_sgd(const SgdParams p) {
-    uint32_t *s_tmp = s_tmp_ptr();
-    uint32_t &s_ticket = *s_ticket_ptr();
-    uint64_t &s_ob = *s_ob_ptr();
-    constexpr uint32_t SW = kSgdSW, H = kSgdH;
-    const uint32_t t = threadIdx.x;
-    const uint32_t tcol = 4 * t;
-    const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap);
+__global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
     stage_dec(p.wdec, kSgdWTab);
     stage_dec(p.mdec, kSgdMTab);
     stage_enc(p.wenc, kSgdETab);
-    if (t == 0) s_ticket = atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrTicket), 1u);
     __syncthreads();
-    const uint32_t u = s_ticket;
-    const uint32_t nunits = p.nblk * H;
-    if (u >= nunits) return;   // only if the scratch header was not cleared
-    const uint32_t b = u / H, h = u % H;
-    stage_rows<SW>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
-    st32(lay.z0 + tcol, 0);
-    st32(lay.z1 + tcol, 0);
-    st32(lay.z2 + tcol, 0);
-    for (uint32_t w = 0; w < cap; ++w) st32(lay.out0 + w * kSgdRowB + tcol, 0);
-    const uint64_t r0 = (uint64_t)b * p.block_elems;
-    const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
-    const uint32_t n_s = stream_len(nb, h * SW + t);
-    uint32_t cw_s, cm_s, wex, mex, wtot, mtot;
-    block_spills<SW, H>(p.w_cnt + (uint64_t)b * NS, nb, h, s_tmp, cw_s, wex, wtot);   // barriers
-    block_spills<SW, H>(p.m_cnt + (uint64_t)b * NS, nb, h, s_tmp, cm_s, mex, mtot);
-    const uint64_t wsp = p.w_obase[b] + wex, msp = p.m_obase[b] + mex;
-    // this unit has read what the block's other units may overwrite in place
-    uint32_t *readers = reinterpret_cast<uint32_t *>(p.scratch + kScrReaders);
-    __syncthreads();
-    if (t == 0) __hip_atomic_fetch_add(&readers[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    Writer<kSgdRowB> st;
-    st.init(tcol, n_s);
-    if (nb == p.block_elems && wtot == 0 && mtot == 0)
-        sgd_stream_full<CAPT>(p, st, r0 + h * SW);
-    else
-        sgd_stream_general<CAPT>(p, st, n_s, cw_s, cm_s, r0 + h * SW, wsp, msp);
-    const UnitOut o{p.o_pay, p.o_cnt, p.scratch, p.nblk, p.ovf_cap, cap};
-    uint32_t *status = p.status;
-    writer_finish<SW>(st.cs, st.soff, n_s, u, b, h, lay.out0, s_tmp, &s_ob, o,
-                      [readers, b, status, t] {
-        // counts and offsets of W may be this block's own buffers: wait until
-        // every unit of the block has read them (they all hold tickets, so
-        // they are running, and they read before anything else)
-        if (t == 0) {
-            uint32_t spins = 0;
-            while (__hip_atomic_load(&readers[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < H) {
-                if (++spins > kSpinLimit) {
-                    atomicOr(status, LCT_ST_LOOKBACK);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
+    const uint32_t l = lane();
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const SgdLayout lay(cap, kSgdWave0 + (threadIdx.x >> 6) * sgd_wave_bytes(cap));
+    st32(lay.z1 + 4 * l, 0);
+    st32(lay.z2 + 4 * l, 0);
+    const uint32_t nunits = p.nblk * kMaxUnits;
+    uint16_t *cnt_out = p.park_cnt ? reinterpret_cast<uint16_t *>(p.scratch + scr_cnt_offset(p.nblk))
+                                   : p.o_cnt;
+    const uint32_t stride = gridDim.x * kSgdWaves;
+    for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
+        const uint32_t b = unit_block(u), h = unit_part(u);
+        rows_to_lds(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        st32(lay.z0 + 4 * l, 0);   // W's row -1 (a sink row of the output for cap >= 18)
+        for (uint32_t w = 0; w < cap; ++w) st32(lay.out0 + w * ROWB + 4 * l, 0);
+        const uint64_t r0 = (uint64_t)b * p.block_elems;
+        const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+        const uint32_t n_s = stream_len(nb, h * US + l);
+        const uint64_t wob = p.w_obase[b], mob = p.m_obase[b];
+        const bool fast = nb == p.block_elems && wob == p.w_obase[b + 1] && mob == p.m_obase[b + 1];
+        Writer st;
+        st.init(lay.out0, l, n_s);
+        if (fast) {
+            sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
+        } else {
+            uint32_t cw_s, cm_s, wex, mex;
+            unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
+            unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
+            sgd_stream_general<CAPT>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
         }
-        __syncthreads();
-    });
+        // The result's counts overwrite W's when the update is in place:
+        // other units of this block may still read W's (general path), so
+        // they are parked and put in place by the scan kernel.
+        const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
+                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
+        unit_finish(st, n_s, u, b, h, lay.out0, o);
+    }
 }
+
+// ------------------------------------------------------------------ launches
 
 // Dynamic LDS beyond 64 KiB must be requested per kernel; remember the
 // largest size granted so far so the runtime is asked only when it grows.
@@ -1156,31 +1131,37 @@ std::atomic<size_t> g_lds_granted[3][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
+// One wave per unit, or (persistent) as many workgroups as the device holds
+// at once, never more than there are units to go round.
 template <typename P>
-int launch(const void *fn, uint32_t grid, uint32_t block, size_t lds_bytes, const P &p, void *stream,
-           std::atomic<size_t> &granted) {
+int launch(const void *fn, uint64_t nunits, uint32_t waves, bool persistent, size_t lds_bytes,
+           const P &p, void *stream, std::atomic<size_t> &granted) {
     const int attr = ensure_lds(fn, lds_bytes, granted);
     if (attr != hipSuccess) return attr;
+    const uint64_t want = (nunits + waves - 1) / waves;
+    uint32_t grid = (uint32_t)want;
+    hipError_t e = hipSuccess;
+    if (persistent) {
+        int dev = 0, cus = 0, per_cu = 0;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, (int)(64 * waves), lds_bytes);
+        if (e != hipSuccess) return (int)e;
+        if (per_cu < 1) return (int)hipErrorInvalidConfiguration;
+        grid = (uint32_t)std::min<uint64_t>(want, (uint64_t)per_cu * cus);
+    }
     void *args[] = {const_cast<P *>(&p)};
-    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds_bytes,
-                                         (hipStream_t)stream);
+    e = hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), args, lds_bytes, (hipStream_t)stream);
     if (e != hipSuccess) return (int)e;
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-size_t encode_lds(uint32_t cap) { return kEncRow0 + (size_t)(cap + 2) * kEncRowB; }
-size_t decode_lds(uint32_t cap) { return kDecRow0 + (size_t)(cap + 1) * kDecRowB; }
-size_t sgd_lds(uint32_t cap) { return SgdLayout(cap).end; }
-
-int launch_scan(uint8_t *scratch, uint64_t nblk, uint32_t units_per_block, uint64_t *obase,
-                uint8_t *ovf, uint64_t ovf_cap, uint32_t *status, void *stream) {
-    const uint64_t groups = (nblk * units_per_block + kScanGroup - 1) / kScanGroup;
-    hipLaunchKernelGGL(k_scan, dim3((uint32_t)groups), dim3(kScanGroup), 0, (hipStream_t)stream,
-                       scratch, nblk, units_per_block, obase, ovf, ovf_cap, status);
-    return (int)hipGetLastError();
-}
+size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wave_bytes(cap); }
+size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
+size_t sgd_lds(uint32_t cap) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap); }
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
@@ -1190,19 +1171,27 @@ int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream
     return (int)hipGetLastError();
 }
 
+int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
+                uint32_t *status, uint16_t *cnt, void *stream) {
+    const uint64_t groups = (nblk * kMaxUnits + kScanGroup - 1) / kScanGroup;
+    hipLaunchKernelGGL(k_scan, dim3((uint32_t)groups), dim3(kScanGroup), 0, (hipStream_t)stream,
+                       scratch, nblk, obase, ovf, ovf_cap, status, cnt);
+    return (int)hipGetLastError();
+}
+
 int launch_encode(const EncodeParams &p, void *stream) {
-    return launch(ByCap<EncK>::pick(p.cap_words), p.nblk * kEncH, kEncSW, encode_lds(p.cap_words),
-                  p, stream, g_lds_granted[0][cap_slot(p.cap_words)]);
+    return launch(ByCap<EncK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kEncWaves, false,
+                  encode_lds(p.cap_words), p, stream, g_lds_granted[0][cap_slot(p.cap_words)]);
 }
 
 int launch_decode(const DecodeParams &p, void *stream) {
-    return launch(ByCap<DecK>::pick(p.cap_words), p.nblk, NS, decode_lds(p.cap_words), p, stream,
-                  g_lds_granted[1][cap_slot(p.cap_words)]);
+    return launch(ByCap<DecK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kDecWaves, false,
+                  decode_lds(p.cap_words), p, stream, g_lds_granted[1][cap_slot(p.cap_words)]);
 }
 
 int launch_sgd(const SgdParams &p, void *stream) {
-    return launch(ByCap<SgdK>::pick(p.cap_words), p.nblk * kSgdH, kSgdSW, sgd_lds(p.cap_words), p,
-                  stream, g_lds_granted[2][cap_slot(p.cap_words)]);
+    return launch(ByCap<SgdK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true,
+                  sgd_lds(p.cap_words), p, stream, g_lds_granted[2][cap_slot(p.cap_words)]);
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {

@@ -15,42 +15,48 @@ constexpr uint32_t kMinBlock = kStreams * kChunk;
 constexpr uint32_t kMaxBlock = 65536;
 constexpr uint32_t kMaxCapWords = 64;
 
-constexpr uint32_t kMaxUnits = 4;           // workgroups a block may be split over
-constexpr uint32_t kEncUnits = 1;           // encode: one workgroup per block
-constexpr uint32_t kSgdUnits = 2;           // fused update: two workgroups per block
+constexpr uint32_t kMaxUnits = 4;           // units a block is split into
+constexpr uint32_t kUnitStreams = kStreams / kMaxUnits;   // streams per unit: one wave's lanes
 
-// Scratch layout (bytes).  The header, the per-block reader counters and the
-// scan's look-back flags are cleared by a fill kernel before each encode / SGD
-// launch.  Every unit of the main kernel writes its record (spilled bytes,
-// where they sit in the second staging area).  Spilled exponent fields are
+// Scratch layout (bytes).  The header and the scan's look-back flags are
+// cleared by a fill kernel before each encode / SGD launch.  Every unit of the
+// main kernel writes its record (spilled bytes, where they sit in the second
+// staging area, whether its counts were parked).  Spilled exponent fields are
 // parked per stream in the first staging area while a unit runs, copied into
 // one contiguous piece per unit at its end, and placed in the overflow region
-// by the scan kernel once every unit's offset is known.
+// by the scan kernel once every unit's offset is known.  An in-place update
+// parks its counts too, so that no unit overwrites counts another unit of the
+// same block has yet to read; the scan kernel puts them in place.
 constexpr uint64_t kScrTicket = 0;    // uint32: next unit of the main kernel
 constexpr uint64_t kScrTicket2 = 4;   // uint32: next group of the scan kernel
 constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the first staging area
 constexpr uint64_t kScrStage2 = 16;   // uint64: bytes claimed in the second
-constexpr uint64_t kScrReaders = 64;  // uint32[nblk]: units of a block that have read it
+constexpr uint64_t kScrFlags = 64;    // uint64[groups + 1]: the scan's look-back flags
 constexpr uint32_t kScanGroup = 256;  // units per scan workgroup
-__host__ __device__ inline uint64_t scr_max_units(uint64_t nblk) { return kMaxUnits * nblk; }
-__host__ __device__ inline uint64_t scr_flags_offset(uint64_t nblk) { return (kScrReaders + 4 * nblk + 7) & ~uint64_t(7); }
+__host__ __device__ inline uint64_t scr_units(uint64_t nblk) { return kMaxUnits * nblk; }
 __host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) {
-    return scr_flags_offset(nblk) + 8 * ((scr_max_units(nblk) + kScanGroup - 1) / kScanGroup + 1);
+    return kScrFlags + 8 * ((scr_units(nblk) + kScanGroup - 1) / kScanGroup + 1);
 }
-__host__ __device__ inline uint64_t scr_rec_offset(uint64_t nblk) { return (scr_clear_bytes(nblk) + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t scr_rec_offset(uint64_t nblk) { return align256(scr_clear_bytes(nblk)); }
+__host__ __device__ inline uint64_t scr_cnt_offset(uint64_t nblk) {
+    return align256(scr_rec_offset(nblk) + 16 * scr_units(nblk));
+}
 __host__ __device__ inline uint64_t scr_stage_offset(uint64_t nblk) {
-    return (scr_rec_offset(nblk) + 16 * scr_max_units(nblk) + 255) & ~uint64_t(255);
+    return align256(scr_cnt_offset(nblk) + 2 * kStreams * nblk);
 }
 __host__ __device__ inline uint64_t scr_stage2_offset(uint64_t nblk, uint64_t ovf_cap) {
-    return (scr_stage_offset(nblk) + ovf_cap + 255) & ~uint64_t(255);
+    return align256(scr_stage_offset(nblk) + ovf_cap);
 }
 __host__ __device__ inline uint64_t scr_bytes(uint64_t nblk, uint64_t ovf_cap) {
     return scr_stage2_offset(nblk, ovf_cap) + ovf_cap;
 }
 
-// A unit's record: spilled bytes and where they start in the second staging area.
+// A unit's record: where its spilled bytes sit in the second staging area,
+// how many there are, and flags (bit 0: its counts are parked in scratch).
 struct UnitRec {
-    uint64_t total, base;
+    uint64_t base;
+    uint32_t total, flags;
 };
 
 // Encoder tables: stream bits of each exponent field and their count.
@@ -120,6 +126,8 @@ struct SgdParams {
     uint64_t n;
     uint32_t block_elems, cap_words, nblk;
     float neg_eta;
+    uint32_t park_cnt;   // the result's counts overwrite W's: park them in scratch
+    uint32_t pad1;
     EncTab wenc;
     DecTab wdec;
     DecTab mdec;
@@ -127,8 +135,8 @@ struct SgdParams {
 
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
-int launch_scan(uint8_t *scratch, uint64_t nblk, uint32_t units_per_block, uint64_t *obase,
-                uint8_t *ovf, uint64_t ovf_cap, uint32_t *status, void *stream);
+int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
+                uint32_t *status, uint16_t *cnt, void *stream);
 int launch_encode(const EncodeParams &p, void *stream);
 int launch_decode(const DecodeParams &p, void *stream);
 int launch_sgd(const SgdParams &p, void *stream);
