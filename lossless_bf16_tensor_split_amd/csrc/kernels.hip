@@ -457,8 +457,8 @@ struct UnitOut {
 // per-stream staging pieces into one piece of the second staging area in
 // (stream, position) order; its record says where; then its counts.  The
 // overflow offsets and the fields' final places are the scan kernel's work.
-__device__ void unit_finish(const Writer &st, uint32_t n_s, uint32_t u, uint32_t b, uint32_t h,
-                            uint32_t row0, const UnitOut &o) {
+__device__ __forceinline__ void unit_finish(const Writer &st, uint32_t n_s, uint32_t u, uint32_t b, uint32_t h,
+                                            uint32_t row0, const UnitOut &o) {
     const uint32_t l = lane();
     const uint32_t spill = n_s - st.cs;
     const uint32_t inc = wave_incl_scan(spill);
@@ -1069,7 +1069,15 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
     uint16_t *cnt_out = p.park_cnt ? reinterpret_cast<uint16_t *>(p.scratch + scr_cnt_offset(p.nblk))
                                    : p.o_cnt;
     const uint32_t stride = gridDim.x * kSgdWaves;
+    // The two waves of a workgroup take units 2i and 2i+1 of one block, whose
+    // sign-fraction bytes share every 128-byte line.  Left free, the waves
+    // drift apart over many units and the second read of a line misses L2, so
+    // they meet at the start of each unit (an execution barrier only: they
+    // share no data).  Both take the same number of trips, the unit count
+    // being even.
+    static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
+        __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
         rows_to_lds(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
         st32(lay.z0 + 4 * l, 0);   // W's row -1 (a sink row of the output for cap >= 18)
