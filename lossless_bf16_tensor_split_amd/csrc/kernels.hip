@@ -343,10 +343,10 @@ __device__ __forceinline__ void writer_chunk(Writer &st, const uint32_t (&e8)[CH
 }
 
 // Claim staging space for streams that started spilling in this step (one
-// atomic per wave), then park this step's spilled fields (e8[] = 8 * field)
+// atomic per wave), then park this step's N spilled fields (e8[] = 8 * field)
 // there.  Every lane of the wave must reach it.
-template <bool CHECKED>
-__device__ __forceinline__ void writer_spill(Writer &st, const uint32_t (&e8)[CH], uint32_t j0,
+template <bool CHECKED, uint32_t N>
+__device__ __forceinline__ void writer_spill(Writer &st, const uint32_t (&e8)[N], uint32_t j0,
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
@@ -364,7 +364,7 @@ __device__ __forceinline__ void writer_spill(Writer &st, const uint32_t (&e8)[CH
     }
     if (!st.live) {
 #pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
+        for (uint32_t i = 0; i < N; ++i) {
             const uint32_t j = j0 + i;
             if (j >= st.cs && (!CHECKED || j < n_s)) {
                 const uint64_t k = st.soff + (j - st.cs);
@@ -774,7 +774,10 @@ constexpr uint32_t kSlabPos = 2 * CH;
 constexpr uint32_t kSlabB = kSlabPos * US;
 // LDS: W and M decode tables, the W encode table, then per wave the slabs and
 // the rows.
-constexpr uint32_t kSgdWTab = 256, kSgdMTab = 1280, kSgdETab = 2304, kSgdWave0 = 4352;
+constexpr uint32_t kSgdETab = 0, kSgdNone = 2048, kSgdWTab = 2304, kSgdMTab = 3328, kSgdWave0 = 4352;
+// kSgdNone: an encode-table entry of no bits and length 0 (a field that codes
+// to nothing), as an offset from kSgdETab
+constexpr uint32_t kSgdNoField = kSgdNone - kSgdETab;
 
 // A wave's region (from `base`): the slabs; the output's rows 0..cap-1 and
 // its two sink rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row
@@ -918,32 +921,71 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         r.w1 = *reinterpret_cast<const u32x4 *>(gw + o1);
         r.m1 = *reinterpret_cast<const u32x4 *>(gm + o1);
     };
-    auto half = [&](uint32_t j0, uint32_t row) {
-        uint32_t ws[CH], ms[CH], H[CH / 2], e[CH];
+    // The writer runs one half behind the readers: the fields of a half are
+    // coded while the next half is decoded, four per group, so that their
+    // table lookups and bit packing fill the latency of the readers' lookups.
+    // Before the first half, ep holds fields that code to nothing.
+    uint32_t ep[CH];      // fields of the half not yet coded (8 * field)
+    uint32_t jp = 0;      // position of ep[0]
 #pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            ws[i] = ld8(sw + (row + i) * US + l);
-            ms[i] = ld8(sm + (row + i) * US + l);
-        }
+    for (uint32_t i = 0; i < CH; ++i) ep[i] = kSgdNoField;
+    auto half = [&](uint32_t j0, uint32_t row) {
+        uint32_t ws[CH], ms[CH], ew[CH], em[CH], H[CH / 2], e[CH];
+        u32x2 wc[CH];
+        float r[CH];
+        // sign-fraction bytes of a group and encode-table entries of the
+        // writer's group, each read one group before it is used
+        auto fetch = [&](uint32_t g) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                ws[g + k] = ld8(sw + (row + g + k) * US + l);
+                ms[g + k] = ld8(sm + (row + g + k) * US + l);
+                wc[g + k] = ld64(kSgdETab + ep[g + k]);
+            }
+        };
+        fetch(0);
         // Four fields per window and reader, software-pipelined: step k of a
-        // group issues both readers' k-th table lookups, and the arithmetic of
-        // the previous group's k-th element fills their latency.  The
-        // scheduling barriers keep that order (left alone, the two reader
-        // chains are scheduled one after the other).  Results are rounded in
-        // pairs by the hardware conversion; a chunk holding a NaN, or one
-        // where some window ran out (long escapes), is done again with one
-        // field per window and the integer rounding.
+        // group issues both readers' k-th table lookups; the arithmetic of
+        // the previous group's k-th element and the writer's k-th field fill
+        // their latency.  The scheduling barriers keep that order (left
+        // alone, the two reader chains are scheduled one after the other).
+        // Results are rounded in pairs by the hardware conversion; a half
+        // holding a NaN, or one where some window ran out (long escapes), is
+        // decoded again with one field per window and the integer rounding.
+        // The writer codes a group in the pipeline when every stream is live
+        // and has room for four fields of the longest kind; otherwise the
+        // group is coded with checks before the pipeline step and its fields
+        // are replaced by ones that code to nothing.  Nothing in the pipeline
+        // step branches (a branch there lets the compiler move the arithmetic
+        // past it), and each rounded pair is pinned where it is made.
         const int32_t qw0 = rw.q, qm0 = rm.q;
         uint32_t cmax = 0;
         bool nan = false;
-        uint32_t ew[CH], em[CH];
-        float r[CH];
+        const bool wall = __all(st.live && st.total() + CH * 16 <= capbits);
 #pragma unroll
         for (uint32_t gi = 0; gi <= CH; gi += 4) {
             uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
             if (gi < CH) {
                 winw = rw.window();
                 winm = rm.window();
+            }
+            if (gi + 4 < CH) fetch(gi + 4);
+            if (gi < CH && !wall && !__all(st.live && st.total() + 4 * 16 <= capbits)) {
+                const uint32_t eg[4] = {ep[gi], ep[gi + 1], ep[gi + 2], ep[gi + 3]};
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) {
+                    if (st.live) {
+                        if (st.total() + wc[gi + k].y <= capbits) {
+                            st.put(wc[gi + k].x, wc[gi + k].y);
+                            st.flush();
+                        } else {
+                            st.live = 0;
+                            st.cs = jp + gi + k;
+                        }
+                    }
+                    wc[gi + k] = u32x2{0u, 0u};
+                }
+                writer_spill<false>(st, eg, jp + gi, npos, stage_ctr, stage, p.ovf_cap);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -960,7 +1002,14 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                     r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32(ms[i], em[i])),
                                           __uint_as_float(join32(ws[i], ew[i])));
                     nan |= r[i] != r[i];
-                    if (k & 1) H[i / 2] = cvt_bf16x2(r[i - 1], r[i]);
+                    if (k & 1) {
+                        H[i / 2] = cvt_bf16x2(r[i - 1], r[i]);
+                        asm volatile("" : "+v"(H[i / 2]));
+                    }
+                }
+                if (gi < CH) {
+                    st.put(wc[gi + k].x, wc[gi + k].y);
+                    if (k & 1) st.flush();
                 }
                 if (gi < CH) {
                     ew[gi + k] = (wkw << (enw & 31u)) | enw;
@@ -977,23 +1026,20 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             }
         }
         if (__builtin_expect(!__all(cmax <= 30 && !nan), 0)) {
-            if (!__all(cmax <= 30)) {
-                rw.q = qw0;
-                rm.q = qm0;
-#pragma unroll
-                for (uint32_t i = 0; i < CH; ++i) {
-                    ew[i] = rw.next(kSgdWTab);
-                    em[i] = rm.next(kSgdMTab);
-                    rw.q = min(rw.q, qwmax);
-                    rm.q = min(rm.q, qmmax);
-                }
-            }
+            rw.q = qw0;
+            rm.q = qm0;
 #pragma unroll
             for (uint32_t i = 0; i < CH; i += 2) {
-                const uint32_t R0 = sgd_round(join32(ws[i], ew[i]), join32(ms[i], em[i]), p.neg_eta);
-                const uint32_t R1 =
-                    sgd_round(join32(ws[i + 1], ew[i + 1]), join32(ms[i + 1], em[i + 1]), p.neg_eta);
-                H[i / 2] = (R0 >> 16) | (R1 & 0xFFFF0000u);
+                uint32_t R[2];
+#pragma unroll
+                for (uint32_t t = 0; t < 2; ++t) {
+                    const uint32_t fw = rw.next(kSgdWTab), fm = rm.next(kSgdMTab);
+                    rw.q = min(rw.q, qwmax);
+                    rm.q = min(rm.q, qmmax);
+                    R[t] = sgd_round(join32(ld8(sw + (row + i + t) * US + l), fw),
+                                     join32(ld8(sm + (row + i + t) * US + l), fm), p.neg_eta);
+                }
+                H[i / 2] = (R[0] >> 16) | (R[1] & 0xFFFF0000u);
             }
         }
         // split the pairs: exponent field (as an encode-table offset) and the
@@ -1006,8 +1052,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             st8(sw + (row + i) * US + l, (h & 0x7Fu) | (t & 0x80u));
             st8(sw + (row + i + 1) * US + l, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
         }
-        writer_chunk<false>(st, e, j0, npos, capbits, kSgdETab);
-        writer_spill<false>(st, e, j0, npos, stage_ctr, stage, p.ovf_cap);
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) ep[i] = e[i];
+        jp = j0;
     };
     // A slab's result bytes are read into registers at the end of its step
     // and stored after the next slab has been staged: the memory-counter wait
@@ -1050,6 +1097,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         load(a, j2 < npos ? j2 : j1);
         step(b, j1);
     }
+    writer_chunk<false>(st, ep, jp, npos, capbits, kSgdETab);
+    writer_spill<false>(st, ep, jp, npos, stage_ctr, stage, p.ovf_cap);
     *reinterpret_cast<u32x4 *>(dst0) = out0;
     *reinterpret_cast<u32x4 *>(dst1) = out1;
 }
@@ -1059,6 +1108,7 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
     stage_dec(p.wdec, kSgdWTab);
     stage_dec(p.mdec, kSgdMTab);
     stage_enc(p.wenc, kSgdETab);
+    if (threadIdx.x < 2) st32(kSgdNone + 4 * threadIdx.x, 0);
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
