@@ -930,7 +930,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 #pragma unroll
     for (uint32_t i = 0; i < CH; ++i) ep[i] = kSgdNoField;
     auto half = [&](uint32_t j0, uint32_t row) {
-        uint32_t ws[CH], ms[CH], ew[CH], em[CH], H[CH / 2], e[CH];
+        uint32_t ws[CH], ms[CH], ew[CH], em[CH];
         u32x2 wc[CH];
         float r[CH];
         // sign-fraction bytes of a group and encode-table entries of the
@@ -942,6 +942,16 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                 ms[g + k] = ld8(sm + (row + g + k) * US + l);
                 wc[g + k] = ld64(kSgdETab + ep[g + k]);
             }
+        };
+        // a rounded pair (elements i, i+1 in bits 15..0, 31..16): its fields,
+        // as encode-table offsets, replace the coded ones in ep (read a group
+        // earlier) and its sign-fraction bytes go back into the slab
+        auto split = [&](uint32_t h, uint32_t i) {
+            const uint32_t t = h >> 8;
+            ep[i] = (h >> 4) & 0x7F8u;
+            ep[i + 1] = (h >> 20) & 0x7F8u;
+            st8(sw + (row + i) * US + l, (h & 0x7Fu) | (t & 0x80u));
+            st8(sw + (row + i + 1) * US + l, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
         };
         fetch(0);
         // Four fields per window and reader, software-pipelined: step k of a
@@ -1003,8 +1013,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                                           __uint_as_float(join32(ws[i], ew[i])));
                     nan |= r[i] != r[i];
                     if (k & 1) {
-                        H[i / 2] = cvt_bf16x2(r[i - 1], r[i]);
-                        asm volatile("" : "+v"(H[i / 2]));
+                        uint32_t h = cvt_bf16x2(r[i - 1], r[i]);
+                        asm volatile("" : "+v"(h));
+                        split(h, i - 1);
                     }
                 }
                 if (gi < CH) {
@@ -1026,6 +1037,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             }
         }
         if (__builtin_expect(!__all(cmax <= 30 && !nan), 0)) {
+            // W's bytes in the slab are already results: take them from
+            // memory, which the result reaches only a step later
+            const uint8_t *wsrc = p.w_sf + r0 + (uint64_t)j0 * NS + l;
             rw.q = qw0;
             rm.q = qm0;
 #pragma unroll
@@ -1036,24 +1050,12 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                     const uint32_t fw = rw.next(kSgdWTab), fm = rm.next(kSgdMTab);
                     rw.q = min(rw.q, qwmax);
                     rm.q = min(rm.q, qmmax);
-                    R[t] = sgd_round(join32(ld8(sw + (row + i + t) * US + l), fw),
+                    R[t] = sgd_round(join32(wsrc[(i + t) * NS], fw),
                                      join32(ld8(sm + (row + i + t) * US + l), fm), p.neg_eta);
                 }
-                H[i / 2] = (R[0] >> 16) | (R[1] & 0xFFFF0000u);
+                split((R[0] >> 16) | (R[1] & 0xFFFF0000u), i);
             }
         }
-        // split the pairs: exponent field (as an encode-table offset) and the
-        // sign-fraction byte of each result, the latter back into the slab
-#pragma unroll
-        for (uint32_t i = 0; i < CH; i += 2) {
-            const uint32_t h = H[i / 2], t = h >> 8;
-            e[i] = (h >> 4) & 0x7F8u;
-            e[i + 1] = (h >> 20) & 0x7F8u;
-            st8(sw + (row + i) * US + l, (h & 0x7Fu) | (t & 0x80u));
-            st8(sw + (row + i + 1) * US + l, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
-        }
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) ep[i] = e[i];
         jp = j0;
     };
     // A slab's result bytes are read into registers at the end of its step

@@ -213,6 +213,36 @@ def test_sgd_small_with_spills(L, orc, B, cw, inplace):
              what="B=%d cw=%d inplace=%s" % (B, cw, inplace))
 
 
+@pytest.mark.parametrize("inplace", [False, True])
+def test_sgd_full_blocks_escapes_and_nans(L, orc, inplace):
+    """Full blocks with no spilled input field (the update's full-block path):
+    runs of escaped exponents that overrun a four-field window, and NaNs in
+    either operand at several places of a slab, send single halves through
+    the path's re-decode with the integer rounding."""
+    g = np.random.default_rng(77)
+    B = 65536
+    n = 4 * B
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    tiny = synth.to_bf16_bits(np.array([1e-30, -3e-33, 2e-35, -1e-36]))
+    for blk, s, j in [(0, 5, 40), (1, 130, 0), (2, 255, 252), (3, 64, 17), (0, 200, 128)]:
+        for t in range(4):                    # four escapes in one window of stream s
+            w[blk * B + (j + t) * 256 + s] = tiny[t]
+    for blk, s, j in [(1, 7, 30), (2, 100, 161), (3, 250, 9)]:
+        for t in range(2):                    # two escapes in one window of M
+            m[blk * B + (j + t) * 256 + s] = tiny[t]
+    w[1 * B + 100 * 256 + 3] = 0x7FC0          # NaN in W, second half of a slab
+    m[2 * B + 201 * 256 + 66] = 0xFFC1          # NaN in M (negative, payload)
+    w[3 * B + 255 * 256 + 255] = 0x7F81         # signalling-pattern NaN, last element
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-3)
+    lay_b, lay_c = B, 25
+    ocw = orc.codebook_build(0, 0.02, 0.0, w)
+    ocm = orc.codebook_build(0, 1e-3, 0.0, m)
+    assert orc.encode(ocw, w, lay_b, lay_c).spilled == 0
+    assert orc.encode(ocm, m, lay_b, lay_c).spilled == 0
+    sgd_case(L, orc, w, m, mw, mm, 1e-3, lay_b, lay_c, inplace, what="escapes/nans inplace=%s" % inplace)
+
+
 def test_sgd_eta_zero_identity(L, orc):
     g = np.random.default_rng(3)
     n = 5 * 65536 + 7
