@@ -86,6 +86,10 @@ __device__ __forceinline__ u32x2 ld64(uint32_t off) { return *reinterpret_cast<l
 __device__ __forceinline__ u32x4 ld128(uint32_t off) { return *reinterpret_cast<lds_u128 *>(off); }
 __device__ __forceinline__ void st128(uint32_t off, u32x4 v) { *reinterpret_cast<lds_u128 *>(off) = v; }
 __device__ __forceinline__ void st32(uint32_t off, uint32_t v) { *reinterpret_cast<lds_u32 *>(off) = v; }
+// byte 2 of v
+__device__ __forceinline__ void st8hi(uint32_t off, uint32_t v) {
+    *reinterpret_cast<lds_u8 *>(off) = (uint8_t)(v >> 16);
+}
 __device__ __forceinline__ void st8(uint32_t off, uint32_t v) {
     *reinterpret_cast<lds_u8 *>(off) = (uint8_t)v;
 }
@@ -170,6 +174,14 @@ __device__ __forceinline__ uint32_t join32(uint32_t sf, uint32_t e23) {
     uint32_t r;
     // one bit-field insert; written out because the compiler otherwise
     // spends a mask and an and-or on it
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(0x7F800000u), "v"(e23), "v"(sfx));
+    return r;
+}
+// The same with the sign-fraction byte as byte s of word w, sel being
+// s * 0x01010000 | 0x0C0C.
+__device__ __forceinline__ uint32_t join32s(uint32_t w, uint32_t e23, uint32_t sel) {
+    const uint32_t sfx = __builtin_amdgcn_perm(0u, w, sel);
+    uint32_t r;
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(0x7F800000u), "v"(e23), "v"(sfx));
     return r;
 }
@@ -900,6 +912,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
     const uint32_t sw = lay.sw, sm = lay.sm;
     const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a slab
+    const uint32_t lw = l & ~3u;                  // its sign-fraction byte's word in a slab row
+    const uint32_t jsel = (l & 3u) * 0x01010000u | 0x0C0Cu;
     const uint64_t g = r0 + (uint64_t)(l >> 2) * NS + 16 * (l & 3);
     const uint8_t *gw = p.w_sf + g;
     const uint8_t *gm = p.m_sf + g;
@@ -933,13 +947,14 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         uint32_t ws[CH], ms[CH], ew[CH], em[CH];
         u32x2 wc[CH];
         float r[CH];
-        // sign-fraction bytes of a group and encode-table entries of the
-        // writer's group, each read one group before it is used
+        // sign-fraction bytes of a group (each as the aligned word holding
+        // it, whose byte l % 4 the join picks) and encode-table entries of
+        // the writer's group, each read one group before it is used
         auto fetch = [&](uint32_t g) {
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
-                ws[g + k] = ld8(sw + (row + g + k) * US + l);
-                ms[g + k] = ld8(sm + (row + g + k) * US + l);
+                ws[g + k] = ld32(sw + (row + g + k) * US + lw);
+                ms[g + k] = ld32(sm + (row + g + k) * US + lw);
                 wc[g + k] = ld64(kSgdETab + ep[g + k]);
             }
         };
@@ -947,11 +962,14 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         // as encode-table offsets, replace the coded ones in ep (read a group
         // earlier) and its sign-fraction bytes go back into the slab
         auto split = [&](uint32_t h, uint32_t i) {
-            const uint32_t t = h >> 8;
             ep[i] = (h >> 4) & 0x7F8u;
             ep[i + 1] = (h >> 20) & 0x7F8u;
-            st8(sw + (row + i) * US + l, (h & 0x7Fu) | (t & 0x80u));
-            st8(sw + (row + i + 1) * US + l, ((h & ~0x00800000u) | (t & 0x00800000u)) >> 16);
+            // each sign (bits 15, 31) moves down next to its fraction: bytes
+            // 0 and 2 of b are the two sign-fraction bytes
+            uint32_t b;
+            asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b) : "s"(0x00800080u), "v"(h >> 8), "v"(h));
+            st8(sw + (row + i) * US + l, b);
+            st8hi(sw + (row + i + 1) * US + l, b);
         };
         fetch(0);
         // Four fields per window and reader, software-pipelined: step k of a
@@ -1009,8 +1027,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                 }
                 if (gi > 0) {
                     const uint32_t i = gi - 4 + k;
-                    r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32(ms[i], em[i])),
-                                          __uint_as_float(join32(ws[i], ew[i])));
+                    r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32s(ms[i], em[i], jsel)),
+                                          __uint_as_float(join32s(ws[i], ew[i], jsel)));
                     nan |= r[i] != r[i];
                     if (k & 1) {
                         uint32_t h = cvt_bf16x2(r[i - 1], r[i]);
