@@ -32,11 +32,16 @@
 // range).  Several codes are read from one window; there is no refill logic.
 // Row -1 of each input column is zero for the first codes.
 //
-// Bit writer: a 64-bit buffer; after every second code both of its words are
-// stored (ds_write2st64) at the current row and the next, and the buffer
-// advances by a word when the first one is full, so there is no final flush.
-// Two sink rows past the stream capacity absorb the stores of a full stream.
-// The encode table has one 8-byte entry per field: stream bits, bit count.
+// Bit writer: a 64-bit buffer; after every second code it is stored at the
+// current row, and it advances by a word when the first one is full.  The
+// encoder's rows are the wave's LDS rows (both words stored, by ds_write2st64,
+// so there is no final flush; two sink rows past the stream capacity absorb
+// the stores of a full stream), copied out at the unit's end.  The fused
+// update writes the first word straight to the payload array through a buffer
+// resource spanning the unit's rows (its range check drops the stores of a
+// full stream past the last row), stores the last word at the unit's end and
+// clears the rows after it; that keeps its LDS to the inputs' rows.  The
+// encode table has one 8-byte entry per field: stream bits, bit count.
 //
 // Overflow offsets: spilled fields are parked per stream in a staging area,
 // gathered per unit at its end, and placed by a separate scan kernel, an
@@ -266,18 +271,49 @@ struct Reader {
 
 // ------------------------------------------------------------------ stream writer
 
-struct Writer {
-    static constexpr uint32_t kSh = log2c(ROWB) - 5;
+// Where a writer's rows go.  LdsRows: the wave's LDS rows (ROWB bytes apart),
+// both words of the buffer stored at each step (the second is overwritten
+// until complete).  PayRows: the unit's rows of the payload array in memory
+// (4 * NS bytes apart), through a buffer resource spanning exactly the unit's
+// cap rows; only the first word is stored at each step (each word is stored
+// again until it is complete, and the last one once more at the end), and a
+// store past the last row, left by a full stream, is dropped by the range
+// check.
+struct LdsRows {
+    static constexpr uint32_t kStride = ROWB;
+    __device__ __forceinline__ void store(uint32_t woff, uint64_t buf) const {
+        st32(woff, (uint32_t)buf);
+        st32(woff + ROWB, (uint32_t)(buf >> 32));
+    }
+};
+struct PayRows {
+    static constexpr uint32_t kStride = 4 * NS;
+    __amdgpu_buffer_rsrc_t r;
+    // rows of unit h of block b (cap rows of the payload array)
+    __device__ __forceinline__ void init(uint32_t *pay, uint32_t b, uint32_t h, uint32_t cap) {
+        uint32_t *base = pay + ((uint64_t)b * cap * NS + h * US);
+        r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)((cap - 1) * kStride + 4 * US),
+                                             0x00020000);
+    }
+    __device__ __forceinline__ void store(uint32_t woff, uint64_t buf) const {
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)buf, r, woff, 0, 0);
+    }
+};
+
+template <class Rows>
+struct WriterT {
+    static constexpr uint32_t kSh = log2c(Rows::kStride) - 5;
     uint64_t buf;     // pending bits, LSB first (< 32 at every store step)
     uint32_t used;    // bits in buf
-    uint32_t woff;    // LDS address: current row of this lane's column
+    uint32_t woff;    // address of the current row of this lane's column
     uint32_t tadj;    // column address >> kSh, so that total() = (woff >> kSh) - tadj + used
     uint32_t live;    // no field has failed to fit yet
     uint32_t cs;      // coded prefix length
     uint32_t claimed; // staging space claimed for the spilled fields
     uint64_t soff;    // start of this stream's spilled fields in the staging area
+    Rows rows;
 
-    // row0: LDS address of the output's row 0 (a multiple of ROWB).
+    // row0: address of the output's row 0 (a multiple of the row stride).
     __device__ __forceinline__ void init(uint32_t row0, uint32_t lane_, uint32_t n_s) {
         buf = 0;
         used = 0;
@@ -292,11 +328,10 @@ struct Writer {
         buf |= (uint64_t)bits << used;
         used += len;
     }
-    // Store both words of the buffer at the current row and the next; move
-    // on by a word when the first is full.
+    // Store the buffer at the current row; move on by a word when the first
+    // is full.
     __device__ __forceinline__ void flush() {
-        st32(woff, (uint32_t)buf);
-        st32(woff + ROWB, (uint32_t)(buf >> 32));
+        rows.store(woff, buf);
         const uint32_t t = used & 32u;
         buf >>= t;
         woff += t << kSh;
@@ -304,12 +339,14 @@ struct Writer {
     }
     __device__ __forceinline__ uint32_t total() const { return (woff >> kSh) - tadj + used; }
 };
+using Writer = WriterT<LdsRows>;
+using PayWriter = WriterT<PayRows>;
 
 // Code the CH fields at positions j0..j0+CH-1, given as encode-table offsets
 // e8[] (8 * field); with CHECKED, positions at or past n_s are absent.  One
 // capacity test per step in the common case.
-template <bool CHECKED>
-__device__ __forceinline__ void writer_chunk(Writer &st, const uint32_t (&e8)[CH], uint32_t j0,
+template <bool CHECKED, class W>
+__device__ __forceinline__ void writer_chunk(W &st, const uint32_t (&e8)[CH], uint32_t j0,
                                              uint32_t n_s, uint32_t capbits, uint32_t etab) {
     uint32_t cb[CH], cl[CH];
 #pragma unroll
@@ -357,8 +394,8 @@ __device__ __forceinline__ void writer_chunk(Writer &st, const uint32_t (&e8)[CH
 // Claim staging space for streams that started spilling in this step (one
 // atomic per wave), then park this step's N spilled fields (e8[] = 8 * field)
 // there.  Every lane of the wave must reach it.
-template <bool CHECKED, uint32_t N>
-__device__ __forceinline__ void writer_spill(Writer &st, const uint32_t (&e8)[N], uint32_t j0,
+template <bool CHECKED, uint32_t N, class W>
+__device__ __forceinline__ void writer_spill(W &st, const uint32_t (&e8)[N], uint32_t j0,
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
@@ -464,21 +501,29 @@ struct UnitOut {
     uint32_t cap, parked;
 };
 
-// After a unit's stream loop: its payload rows (the wave's LDS rows from
-// address row0) go out; its spilled fields, if any, are gathered from the
+// After a unit's stream loop: its payload rows go out (LdsRows: the wave's
+// LDS rows from address row0 are copied; PayRows: the last word is stored
+// and the rows after it are cleared); its spilled fields, if any, are gathered from the
 // per-stream staging pieces into one piece of the second staging area in
 // (stream, position) order; its record says where; then its counts.  The
 // overflow offsets and the fields' final places are the scan kernel's work.
-__device__ __forceinline__ void unit_finish(const Writer &st, uint32_t n_s, uint32_t u, uint32_t b, uint32_t h,
-                                            uint32_t row0, const UnitOut &o) {
+template <class Rows>
+__device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_s, uint32_t u, uint32_t b,
+                                            uint32_t h, uint32_t row0, const UnitOut &o) {
     const uint32_t l = lane();
     const uint32_t spill = n_s - st.cs;
     const uint32_t inc = wave_incl_scan(spill);
     const uint32_t total = __shfl(inc, 63, 64);
     const uint32_t excl = inc - spill;
-    u32x4 *dst = reinterpret_cast<u32x4 *>(o.pay);
-    for (uint32_t p = l; p < o.cap * 16; p += 64)
-        dst[(((uint64_t)b * o.cap + p / 16) * NS + h * US) / 4 + p % 16] = ld128(row0 + 16 * p);
+    if constexpr (Rows::kStride == ROWB) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(o.pay);
+        for (uint32_t p = l; p < o.cap * 16; p += 64)
+            dst[(((uint64_t)b * o.cap + p / 16) * NS + h * US) / 4 + p % 16] = ld128(row0 + 16 * p);
+    } else {
+        st.rows.store(st.woff, st.buf);
+        for (uint32_t w = st.woff + Rows::kStride; w < o.cap * Rows::kStride; w += Rows::kStride)
+            st.rows.store(w, 0);
+    }
     uint64_t base = 0;
     if (total) {
         unsigned long long t = 0;
@@ -791,18 +836,15 @@ constexpr uint32_t kSgdETab = 0, kSgdNone = 2048, kSgdWTab = 2304, kSgdMTab = 33
 // to nothing), as an offset from kSgdETab
 constexpr uint32_t kSgdNoField = kSgdNone - kSgdETab;
 
-// A wave's region (from `base`): the slabs; the output's rows 0..cap-1 and
-// its two sink rows; W's zero row -1 and rows 0..cap-1; a zero row (W's row
-// cap and M's row -1); M's rows; a zero row.  With cap >= 18 the output's
-// sink rows are W's row -1 and row 0: a stream's output reaches row cap-1 only
-// after 2*(cap-1) >= 34 fields, when its own W reader has left rows -1 and 0.
+// A wave's region (from `base`): the slabs; W's zero row -1 and rows
+// 0..cap-1; a zero row (W's row cap and M's row -1); M's rows; a zero row.
+// The result's rows are not staged: they go to memory as they fill.
 struct SgdLayout {
-    uint32_t sw, sm, out0, z0, w0, z1, m0, z2, end;
+    uint32_t sw, sm, z0, w0, z1, m0, z2, end;
     __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base)
         : sw(base),
           sm(base + kSlabB),
-          out0(base + 2 * kSlabB),
-          z0(base + 2 * kSlabB + (cap >= 18 ? cap : cap + 2) * ROWB),
+          z0(base + 2 * kSlabB),
           w0(z0 + ROWB),
           z1(w0 + cap * ROWB),
           m0(z1 + ROWB),
@@ -841,7 +883,7 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 // General path: partial blocks and inputs with spilled fields; byte-wide
 // accesses with per-element checks.
 template <uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, Writer &st,
+__device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                    uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
                                                    uint64_t r0, uint64_t wsp, uint64_t msp) {
     const uint32_t s = lane();
@@ -902,7 +944,7 @@ struct SlabRegs {
 };
 
 template <uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, Writer &st,
+__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                 uint64_t r0) {
     const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
@@ -1133,6 +1175,7 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const SgdLayout lay(cap, kSgdWave0 + (threadIdx.x >> 6) * sgd_wave_bytes(cap));
+    st32(lay.z0 + 4 * l, 0);
     st32(lay.z1 + 4 * l, 0);
     st32(lay.z2 + 4 * l, 0);
     const uint32_t nunits = p.nblk * kMaxUnits;
@@ -1150,15 +1193,16 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
         rows_to_lds(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
-        st32(lay.z0 + 4 * l, 0);   // W's row -1 (a sink row of the output for cap >= 18)
-        for (uint32_t w = 0; w < cap; ++w) st32(lay.out0 + w * ROWB + 4 * l, 0);
         const uint64_t r0 = (uint64_t)b * p.block_elems;
         const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
         const uint32_t n_s = stream_len(nb, h * US + l);
         const uint64_t wob = p.w_obase[b], mob = p.m_obase[b];
         const bool fast = nb == p.block_elems && wob == p.w_obase[b + 1] && mob == p.m_obase[b + 1];
-        Writer st;
-        st.init(lay.out0, l, n_s);
+        // The result's rows go straight to memory: W's rows, which an update
+        // in place overwrites, are all in LDS by now.
+        PayWriter st;
+        st.init(0, l, n_s);
+        st.rows.init(p.o_pay, b, h, cap);
         if (fast) {
             sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
         } else {
@@ -1172,7 +1216,7 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
         // they are parked and put in place by the scan kernel.
         const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
                         p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
-        unit_finish(st, n_s, u, b, h, lay.out0, o);
+        unit_finish(st, n_s, u, b, h, 0, o);
     }
 }
 
