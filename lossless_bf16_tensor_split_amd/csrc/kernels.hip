@@ -956,11 +956,19 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a slab
     const uint32_t lw = l & ~3u;                  // its sign-fraction byte's word in a slab row
     const uint32_t jsel = (l & 3u) * 0x01010000u | 0x0C0Cu;
-    const uint64_t g = r0 + (uint64_t)(l >> 2) * NS + 16 * (l & 3);
-    const uint8_t *gw = p.w_sf + g;
-    const uint8_t *gm = p.m_sf + g;
-    uint8_t *go = p.o_sf + g;
-    constexpr uint64_t kHalf = (uint64_t)CH * NS;   // bytes between the slab's halves
+    // The unit's sign-fraction bytes of W, M and the result through buffer
+    // resources spanning them: 32-bit offsets, and an offset past the range
+    // makes a store that the hardware drops.
+    const uint32_t span = (npos - 1) * NS + US;
+    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(p.w_sf) + r0, (short)0, (int)span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rms = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(p.m_sf) + r0, (short)0, (int)span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ros = __builtin_amdgcn_make_buffer_rsrc(p.o_sf + r0, (short)0, (int)span,
+                                                                         0x00020000);
+    constexpr uint32_t kNoStore = 0x80000000u;
+    const uint32_t g = (l >> 2) * NS + 16 * (l & 3);
+    constexpr uint32_t kHalf = CH * NS;   // bytes between the slab's halves
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
     Reader rw, rm;
@@ -970,12 +978,12 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // first half twice), so that the number of loads in flight is the same on
     // every path and the wait for one slab never includes the next one's.
     auto load = [&](SlabRegs &r, uint32_t j0) {
-        const uint64_t o = (uint64_t)j0 * NS;
-        const uint64_t o1 = j0 + CH < npos ? o + kHalf : o;
-        r.w0 = *reinterpret_cast<const u32x4 *>(gw + o);
-        r.m0 = *reinterpret_cast<const u32x4 *>(gm + o);
-        r.w1 = *reinterpret_cast<const u32x4 *>(gw + o1);
-        r.m1 = *reinterpret_cast<const u32x4 *>(gm + o1);
+        const uint32_t o = j0 * NS + g;
+        const uint32_t o1 = j0 + CH < npos ? o + kHalf : o;
+        r.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
+        r.m0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
+        r.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o1, 0, 0));
+        r.m1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o1, 0, 0));
     };
     // The writer runs one half behind the readers: the fields of a half are
     // coded while the next half is decoded, four per group, so that their
@@ -1124,23 +1132,24 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // and a store's registers (which may only be reused once it completes)
     // stay untouched for a whole step.  Staging and stores are unconditional:
     // a slab only half inside the block repeats its first half.  The first
-    // step stores W's own bytes to the result's first slab, overwritten by
-    // the real result a step later (same wave, same addresses, in order).
+    // step's stores have nothing to store and go past the range.
     u32x4 out0, out1;
-    uint64_t dst0, dst1;
+    uint32_t dst0, dst1;
+    auto put_out = [&]() {
+        __builtin_amdgcn_raw_buffer_store_b128(out0, ros, dst0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(out1, ros, dst1, 0, 0);
+    };
     auto step = [&](SlabRegs &r, uint32_t j0) {
         const bool two = j0 + CH < npos;
         st128(sw + mine, r.w0);
         st128(sm + mine, r.m0);
         st128(sw + kSlabB / 2 + mine, r.w1);
         st128(sm + kSlabB / 2 + mine, r.m1);
-        *reinterpret_cast<u32x4 *>(dst0) = out0;
-        *reinterpret_cast<u32x4 *>(dst1) = out1;
+        put_out();
         half(j0, 0);
         if (two) half(j0 + CH, CH);
-        const uint64_t o = (uint64_t)j0 * NS;
-        dst0 = reinterpret_cast<uint64_t>(go + o);
-        dst1 = reinterpret_cast<uint64_t>(go + (two ? o + kHalf : o));
+        dst0 = j0 * NS + g;
+        dst1 = two ? dst0 + kHalf : dst0;
         out0 = ld128(sw + mine);
         out1 = ld128(sw + (two ? kSlabB / 2 : 0) + mine);
     };
@@ -1148,8 +1157,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     load(a, 0u);
     out0 = a.w0;
     out1 = a.w1;
-    dst0 = reinterpret_cast<uint64_t>(go);
-    dst1 = reinterpret_cast<uint64_t>(go + (CH < npos ? kHalf : 0));
+    dst0 = kNoStore;
+    dst1 = kNoStore;
     for (uint32_t j0 = 0; j0 < npos; j0 += 2 * kSlabPos) {
         const uint32_t j1 = j0 + kSlabPos;
         load(b, j1 < npos ? j1 : j0);
@@ -1161,8 +1170,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     }
     writer_chunk<false>(st, ep, jp, npos, capbits, kSgdETab);
     writer_spill<false>(st, ep, jp, npos, stage_ctr, stage, p.ovf_cap);
-    *reinterpret_cast<u32x4 *>(dst0) = out0;
-    *reinterpret_cast<u32x4 *>(dst1) = out1;
+    put_out();
 }
 
 template <uint32_t CAPT>
