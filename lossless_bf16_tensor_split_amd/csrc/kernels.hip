@@ -270,6 +270,20 @@ struct Reader {
 };
 
 // ------------------------------------------------------------------ stream writer
+// A buffer resource over `bytes` bytes from p, which must be the same in
+// every lane: its registers are taken as the wave's scalars (the compiler
+// cannot see that a unit's base is uniform, and a resource in vector
+// registers makes every access a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p, uint32_t bytes) {
+    // (the builtin returns a signed int: widen each half through uint32_t,
+    // or a low half with bit 31 set would fill the high half with ones)
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t s = ((uint64_t)hi << 32) | lo;
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(s), (short)0, (int)bytes, 0x00020000);
+}
+
 
 // Where a writer's rows go.  LdsRows: the wave's LDS rows (ROWB bytes apart),
 // both words of the buffer stored at each step (the second is overwritten
@@ -291,9 +305,7 @@ struct PayRows {
     __amdgpu_buffer_rsrc_t r;
     // rows of unit h of block b (cap rows of the payload array)
     __device__ __forceinline__ void init(uint32_t *pay, uint32_t b, uint32_t h, uint32_t cap) {
-        uint32_t *base = pay + ((uint64_t)b * cap * NS + h * US);
-        r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)((cap - 1) * kStride + 4 * US),
-                                             0x00020000);
+        r = wave_rsrc(pay + ((uint64_t)b * cap * NS + h * US), (cap - 1) * kStride + 4 * US);
     }
     __device__ __forceinline__ void store(uint32_t woff, uint64_t buf) const {
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)buf, r, woff, 0, 0);
@@ -432,9 +444,9 @@ __device__ __forceinline__ uint32_t unit_part(uint32_t u) { return u % kMaxUnits
 // Wave g of the grid does unit g; persistent waves then take units g + S,
 // g + 2S, ... with S the number of waves in the grid (units are alike in
 // work, so round-robin spreads them evenly).
-__device__ __forceinline__ uint32_t first_unit(uint32_t waves) {
-    return blockIdx.x * waves + (threadIdx.x >> 6);
-}
+__device__ __forceinline__ uint32_t wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ uint32_t first_unit(uint32_t waves) { return blockIdx.x * waves + wave_id(); }
+
 
 // Copy a unit's payload rows (cap rows of 64 words: cap * 16 pieces of 16
 // bytes, piece p of row p / 16) to LDS from row0; with a second source (pay2)
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode(const EncodeParams p)
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const uint32_t out0 = kEncWave0 + (threadIdx.x >> 6) * enc_wave_bytes(cap);
+    const uint32_t out0 = kEncWave0 + wave_id() * enc_wave_bytes(cap);
     const uint32_t u = first_unit(kEncWaves);
     if (u >= p.nblk * kMaxUnits) return;
     const uint32_t b = unit_block(u), h = unit_part(u);
@@ -801,7 +813,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p)
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const uint32_t base = kDecWave0 + (threadIdx.x >> 6) * dec_wave_bytes(cap);
+    const uint32_t base = kDecWave0 + wave_id() * dec_wave_bytes(cap);
     const uint32_t row0 = base + ROWB;
     st32(base + 4 * l, 0);                      // row -1
     st32(row0 + cap * ROWB + 4 * l, 0);         // row cap
@@ -960,12 +972,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // resources spanning them: 32-bit offsets, and an offset past the range
     // makes a store that the hardware drops.
     const uint32_t span = (npos - 1) * NS + US;
-    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(p.w_sf) + r0, (short)0, (int)span, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rms = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(p.m_sf) + r0, (short)0, (int)span, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ros = __builtin_amdgcn_make_buffer_rsrc(p.o_sf + r0, (short)0, (int)span,
-                                                                         0x00020000);
+    const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rms = wave_rsrc(p.m_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t ros = wave_rsrc(p.o_sf + r0, span);
     constexpr uint32_t kNoStore = 0x80000000u;
     const uint32_t g = (l >> 2) * NS + 16 * (l & 3);
     constexpr uint32_t kHalf = CH * NS;   // bytes between the slab's halves
@@ -1174,7 +1183,10 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 }
 
 template <uint32_t CAPT>
-__global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
+// Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
+// a lane, AGPRs included.
+__global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void k_sgd(const SgdParams p) {
     stage_dec(p.wdec, kSgdWTab);
     stage_dec(p.mdec, kSgdMTab);
     stage_enc(p.wenc, kSgdETab);
@@ -1182,7 +1194,7 @@ __global__ __launch_bounds__(64 * kSgdWaves) void k_sgd(const SgdParams p) {
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap, kSgdWave0 + (threadIdx.x >> 6) * sgd_wave_bytes(cap));
+    const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap));
     st32(lay.z0 + 4 * l, 0);
     st32(lay.z1 + 4 * l, 0);
     st32(lay.z2 + 4 * l, 0);

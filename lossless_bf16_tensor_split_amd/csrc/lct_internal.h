@@ -27,7 +27,6 @@ constexpr uint32_t kUnitStreams = kStreams / kMaxUnits;   // streams per unit: o
 // by the scan kernel once every unit's offset is known.  An in-place update
 // parks its counts too, so that no unit overwrites counts another unit of the
 // same block has yet to read; the scan kernel puts them in place.
-constexpr uint64_t kScrTicket = 0;    // uint32: next unit of the main kernel
 constexpr uint64_t kScrTicket2 = 4;   // uint32: next group of the scan kernel
 constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the first staging area
 constexpr uint64_t kScrStage2 = 16;   // uint64: bytes claimed in the second
