@@ -1095,9 +1095,11 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                         split(h, i - 1);
                     }
                 }
-                if (gi < CH) {
-                    st.put(wc[gi + k].x, wc[gi + k].y);
-                    if (k & 1) st.flush();
+                if (gi < CH && (k & 1)) {
+                    // a pair of codes (at most 16 bits each) as one put
+                    const u32x2 c0 = wc[gi + k - 1], c1 = wc[gi + k];
+                    st.put(c0.x | (c1.x << c0.y), c0.y + c1.y);
+                    st.flush();
                 }
                 if (gi < CH) {
                     ew[gi + k] = (wkw << (enw & 31u)) | enw;
