@@ -449,25 +449,29 @@ __device__ __forceinline__ uint32_t first_unit(uint32_t waves) { return blockIdx
 
 
 // Copy a unit's payload rows (cap rows of 64 words: cap * 16 pieces of 16
-// bytes, piece p of row p / 16) to LDS from row0; with a second source (pay2)
-// its rows go to row2 as well.  Up to 8 pieces per lane and source are loaded
-// before any is stored, so a unit's start waits for memory about once.  The
-// loads are unconditional (a lane past the last piece loads the last piece
-// again) so that no branch splits them; only the stores are skipped.
+// bytes, piece p of row p / 16) to LDS from row0; with TWO, the rows of a
+// second array (pay2) go to row2 as well.  Up to 8 pieces per lane and source
+// are loaded before any is stored, so a unit's start waits for memory about
+// once.  The loads go through buffer resources spanning the unit's rows; a
+// lane past the last piece loads from past the range (nothing, no traffic),
+// so no branch splits the loads; only the stores are skipped.
+template <bool TWO>
 __device__ __forceinline__ void rows_to_lds(const uint32_t *pay, uint32_t row0, const uint32_t *pay2,
                                             uint32_t row2, uint32_t b, uint32_t h, uint32_t cap) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(pay);
-    const u32x4 *src2 = reinterpret_cast<const u32x4 *>(pay2);
     const uint32_t np = cap * 16;
+    const uint64_t u0 = (uint64_t)b * cap * NS + h * US;
+    const uint32_t span = (cap - 1) * 4 * NS + 4 * US;
+    const __amdgpu_buffer_rsrc_t r1 = wave_rsrc(pay + u0, span);
+    const __amdgpu_buffer_rsrc_t r2 = wave_rsrc((TWO ? pay2 : pay) + u0, span);
     for (uint32_t base = 0; base < np; base += 8 * 64) {
         u32x4 v[8], v2[8];
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k) {
-            const uint32_t p = min(base + k * 64 + lane(), np - 1);
-            const uint64_t g = (((uint64_t)b * cap + p / 16) * NS + h * US) / 4 + p % 16;
+            const uint32_t p = base + k * 64 + lane();
+            const uint32_t off = p < np ? (p / 16) * (4 * NS) + (p % 16) * 16 : 0x80000000u;
             if (base + k * 64 < np) {
-                v[k] = src[g];
-                if (pay2) v2[k] = src2[g];
+                v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, 0));
+                if (TWO) v2[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, 0));
             }
         }
 #pragma unroll
@@ -475,7 +479,7 @@ __device__ __forceinline__ void rows_to_lds(const uint32_t *pay, uint32_t row0, 
             const uint32_t p = base + k * 64 + lane();
             if (p < np) {
                 st128(row0 + 16 * p, v[k]);
-                if (pay2) st128(row2 + 16 * p, v2[k]);
+                if (TWO) st128(row2 + 16 * p, v2[k]);
             }
         }
     }
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p)
     const uint32_t u = first_unit(kDecWaves);
     if (u >= p.nblk * kMaxUnits) return;
     const uint32_t b = unit_block(u), h = unit_part(u);
-    rows_to_lds(p.pay, row0, nullptr, 0, b, h, cap);
+    rows_to_lds<false>(p.pay, row0, nullptr, 0, b, h, cap);
     const uint64_t r0 = (uint64_t)b * p.block_elems;
     const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
     const uint32_t n_s = stream_len(nb, h * US + l);
@@ -1214,12 +1218,15 @@ void k_sgd(const SgdParams p) {
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
-        rows_to_lds(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        // the block's overflow offsets are read along with the rows (one
+        // memory round trip for both)
+        const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
+        const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
+        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
         const uint64_t r0 = (uint64_t)b * p.block_elems;
         const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
         const uint32_t n_s = stream_len(nb, h * US + l);
-        const uint64_t wob = p.w_obase[b], mob = p.m_obase[b];
-        const bool fast = nb == p.block_elems && wob == p.w_obase[b + 1] && mob == p.m_obase[b + 1];
+        const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
         // The result's rows go straight to memory: W's rows, which an update
         // in place overwrites, are all in LDS by now.
         PayWriter st;
