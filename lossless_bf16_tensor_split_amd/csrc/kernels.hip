@@ -841,10 +841,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p)
 // ------------------------------------------------------------------ fused SGD
 
 constexpr uint32_t kSgdWaves = 2;
-// Sign-fraction slabs of the full-block path: per wave, kSlabPos positions of
-// its 64 streams for W (also the result's bytes, written in place) and for M.
-constexpr uint32_t kSlabPos = 2 * CH;
-constexpr uint32_t kSlabB = kSlabPos * US;
+// Sign-fraction regions of the full-block path: per wave and tensor, two
+// regions of one half (CH positions of its 64 streams) each; W's also take
+// the result's bytes, written in place.
+constexpr uint32_t kRegB = CH * US;
+constexpr uint32_t kSlabB = 2 * kRegB;
 // LDS: W and M decode tables, the W encode table, then per wave the slabs and
 // the rows.
 constexpr uint32_t kSgdETab = 0, kSgdNone = 2048, kSgdWTab = 2304, kSgdMTab = 3328, kSgdWave0 = 4352;
@@ -950,13 +951,23 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
 }
 
 // Full-block path (every stream has npos elements and no input field spilled).
-// The sign-fraction bytes of W and M arrive through the wave's LDS slabs: lane
-// l moves the 16 bytes of position l/4, streams 16*(l%4).. of the unit, twice
-// per slab (positions +0 and +CH), with one 16-byte load each; the result's
-// bytes overwrite W's in the slab and leave with one 16-byte store each.  The
-// next slab's loads are in flight while the current one is worked on.
-struct SlabRegs {
-    u32x4 w0, w1, m0, m1;
+//
+// One software pipeline over the unit's groups of four positions: stage s
+// decodes group s (both readers, four fields per window), does the
+// arithmetic of group s-1 and splits its results, and codes the fields of
+// group s-2.  Nothing goes back: a group whose window ran out (long escapes)
+// is decoded again right after its own decode, and a NaN result, which the
+// hardware conversion rounds to the same exponent field as the integer
+// rounding, only has its sign-fraction byte made again right after its
+// arithmetic; so the writer can follow two groups behind.
+//
+// The sign-fraction bytes of W and M move through two LDS regions per
+// tensor, one per half (16 positions) in turn: lane l carries the 16 bytes of
+// position l/4, streams 16*(l%4).. of the unit, with one 16-byte load per
+// tensor and half, issued two halves ahead; the result's bytes overwrite W's
+// in the region and leave with one 16-byte store, half a half later.
+struct HalfRegs {
+    u32x4 w, m;
 };
 
 template <uint32_t CAPT>
@@ -964,233 +975,228 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                                                 uint64_t r0) {
     const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
+    const uint32_t nh = npos / CH;                // halves (the block size is a multiple of 4096)
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const uint32_t capbits = 32 * cap;
     const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
     const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
-    const uint32_t sw = lay.sw, sm = lay.sm;
-    const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a slab
-    const uint32_t lw = l & ~3u;                  // its sign-fraction byte's word in a slab row
+    const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a region
+    const uint32_t lw = l & ~3u;                  // its sign-fraction byte's word in a region row
     const uint32_t jsel = (l & 3u) * 0x01010000u | 0x0C0Cu;
     // The unit's sign-fraction bytes of W, M and the result through buffer
     // resources spanning them: 32-bit offsets, and an offset past the range
-    // makes a store that the hardware drops.
+    // makes a load that returns nothing (no traffic) or a store that is
+    // dropped.
     const uint32_t span = (npos - 1) * NS + US;
     const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
     const __amdgpu_buffer_rsrc_t rms = wave_rsrc(p.m_sf + r0, span);
     const __amdgpu_buffer_rsrc_t ros = wave_rsrc(p.o_sf + r0, span);
-    constexpr uint32_t kNoStore = 0x80000000u;
+    constexpr uint32_t kNone = 0x80000000u;
+    constexpr uint32_t kHalfB = CH * NS;          // sign-fraction bytes of a half
     const uint32_t g = (l >> 2) * NS + 16 * (l & 3);
-    constexpr uint32_t kHalf = CH * NS;   // bytes between the slab's halves
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
     Reader rw, rm;
     rw.init(lay.w0, l);
     rm.init(lay.m0, l);
-    // Always four loads (a slab that is only half inside the block loads its
-    // first half twice), so that the number of loads in flight is the same on
-    // every path and the wait for one slab never includes the next one's.
-    auto load = [&](SlabRegs &r, uint32_t j0) {
-        const uint32_t o = j0 * NS + g;
-        const uint32_t o1 = j0 + CH < npos ? o + kHalf : o;
-        r.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
-        r.m0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
-        r.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o1, 0, 0));
-        r.m1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o1, 0, 0));
+
+    auto load = [&](HalfRegs &r, uint32_t h) {
+        const uint32_t o = h < nh ? h * kHalfB + g : kNone;
+        r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
+        r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
     };
-    // The writer runs one half behind the readers: the fields of a half are
-    // coded while the next half is decoded, four per group, so that their
-    // table lookups and bit packing fill the latency of the readers' lookups.
-    // Before the first half, ep holds fields that code to nothing.
-    uint32_t ep[CH];      // fields of the half not yet coded (8 * field)
-    uint32_t jp = 0;      // position of ep[0]
+    auto region = [&](uint32_t h) { return (h & 1u) * kRegB; };
+
+    // Carried from stage to stage: the inputs of the group whose arithmetic
+    // comes next (sign-fraction words and decoded fields), the codes (and
+    // fields) of the group the writer codes next, the result bytes of the
+    // half that leaves next.  Before the first group they stand for a group
+    // that codes to nothing.
+    uint32_t wsP[4] = {0, 0, 0, 0}, msP[4] = {0, 0, 0, 0}, ewP[4] = {0, 0, 0, 0}, emP[4] = {0, 0, 0, 0};
+    u32x2 wc[4] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+    uint32_t ew8[4] = {kSgdNoField, kSgdNoField, kSgdNoField, kSgdNoField};
+    uint32_t jw = 0;                              // position of the writer's group
+    u32x4 outv = {0u, 0u, 0u, 0u};
+    bool wall = true;
+
+    // The writer's group coded with a check per field (a stream near its end
+    // may run out of room); its codes are then spent.
+    auto code_checked = [&]() {
 #pragma unroll
-    for (uint32_t i = 0; i < CH; ++i) ep[i] = kSgdNoField;
-    auto half = [&](uint32_t j0, uint32_t row) {
-        uint32_t ws[CH], ms[CH], ew[CH], em[CH];
-        u32x2 wc[CH];
-        float r[CH];
-        // sign-fraction bytes of a group (each as the aligned word holding
-        // it, whose byte l % 4 the join picks) and encode-table entries of
-        // the writer's group, each read one group before it is used
-        auto fetch = [&](uint32_t g) {
+        for (uint32_t k = 0; k < 4; ++k) {
+            if (st.live) {
+                if (st.total() + wc[k].y <= capbits) {
+                    st.put(wc[k].x, wc[k].y);
+                    st.flush();
+                } else {
+                    st.live = 0;
+                    st.cs = jw + k;
+                }
+            }
+            wc[k] = u32x2{0u, 0u};
+        }
+        writer_spill<false>(st, ew8, jw, npos, stage_ctr, stage, p.ovf_cap);
+    };
+
+    // One stage.  DEC: group s exists (decode it).  GS = s % 4; h = s / 4.
+    // The arithmetic is for group s-1 (in half (s-1)/4, region of that half),
+    // the writer codes group s-2 (its codes in wc, fields in ew8, positions
+    // jw..).
+    auto stage_fn = [&](auto DEC_, auto GS_, uint32_t h) {
+        constexpr bool DEC = decltype(DEC_)::value;
+        constexpr uint32_t GS = decltype(GS_)::value;
+        const uint32_t rc = region(h) + GS * 4 * US;                       // group s's rows
+        const uint32_t rp = (GS ? region(h) : region(h + 1)) + ((GS + 3) % 4) * 4 * US;   // group s-1's rows
+        uint32_t wsC[4], msC[4], ewC[4], emC[4];
+        uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
+        const int32_t qw0 = rw.q, qm0 = rm.q;
+        if (DEC) {
+            winw = rw.window();
+            winm = rm.window();
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
-                ws[g + k] = ld32(sw + (row + g + k) * US + lw);
-                ms[g + k] = ld32(sm + (row + g + k) * US + lw);
-                wc[g + k] = ld64(kSgdETab + ep[g + k]);
+                wsC[k] = ld32(lay.sw + rc + k * US + lw);
+                msC[k] = ld32(lay.sm + rc + k * US + lw);
             }
-        };
-        // a rounded pair (elements i, i+1 in bits 15..0, 31..16): its fields,
-        // as encode-table offsets, replace the coded ones in ep (read a group
-        // earlier) and its sign-fraction bytes go back into the slab
-        auto split = [&](uint32_t h, uint32_t i) {
-            ep[i] = (h >> 4) & 0x7F8u;
-            ep[i + 1] = (h >> 20) & 0x7F8u;
-            // each sign (bits 15, 31) moves down next to its fraction: bytes
-            // 0 and 2 of b are the two sign-fraction bytes
-            uint32_t b;
-            asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b) : "s"(0x00800080u), "v"(h >> 8), "v"(h));
-            st8(sw + (row + i) * US + l, b);
-            st8hi(sw + (row + i + 1) * US + l, b);
-        };
-        fetch(0);
-        // Four fields per window and reader, software-pipelined: step k of a
-        // group issues both readers' k-th table lookups; the arithmetic of
-        // the previous group's k-th element and the writer's k-th field fill
-        // their latency.  The scheduling barriers keep that order (left
-        // alone, the two reader chains are scheduled one after the other).
-        // Results are rounded in pairs by the hardware conversion; a half
-        // holding a NaN, or one where some window ran out (long escapes), is
-        // decoded again with one field per window and the integer rounding.
-        // The writer codes a group in the pipeline when every stream is live
-        // and has room for four fields of the longest kind; otherwise the
-        // group is coded with checks before the pipeline step and its fields
-        // are replaced by ones that code to nothing.  Nothing in the pipeline
-        // step branches (a branch there lets the compiler move the arithmetic
-        // past it), and each rounded pair is pinned where it is made.
-        const int32_t qw0 = rw.q, qm0 = rm.q;
-        uint32_t cmax = 0;
+        }
+        // the writer's group, with checks when some stream is near its end
+        if (!wall && !__all(st.live && st.total() + 4 * 16 <= capbits)) code_checked();
+        uint32_t ep[4];
+        float r[4];
         bool nan = false;
-        const bool wall = __all(st.live && st.total() + CH * 16 <= capbits);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (uint32_t gi = 0; gi <= CH; gi += 4) {
-            uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
-            if (gi < CH) {
-                winw = rw.window();
-                winm = rm.window();
+        for (uint32_t k = 0; k < 4; ++k) {
+            uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
+            if (DEC) {
+                wkw = winw >> cw;
+                wkm = winm >> cm;
+                enw = ld32(kSgdWTab + (wkw & 0x3FCu));
+                enm = ld32(kSgdMTab + (wkm & 0x3FCu));
             }
-            if (gi + 4 < CH) fetch(gi + 4);
-            if (gi < CH && !wall && !__all(st.live && st.total() + 4 * 16 <= capbits)) {
-                const uint32_t eg[4] = {ep[gi], ep[gi + 1], ep[gi + 2], ep[gi + 3]};
-#pragma unroll
-                for (uint32_t k = 0; k < 4; ++k) {
-                    if (st.live) {
-                        if (st.total() + wc[gi + k].y <= capbits) {
-                            st.put(wc[gi + k].x, wc[gi + k].y);
-                            st.flush();
-                        } else {
-                            st.live = 0;
-                            st.cs = jp + gi + k;
-                        }
-                    }
-                    wc[gi + k] = u32x2{0u, 0u};
-                }
-                writer_spill<false>(st, eg, jp + gi, npos, stage_ctr, stage, p.ovf_cap);
+            r[k] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32s(msP[k], emP[k], jsel)),
+                                  __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
+            nan |= r[k] != r[k];
+            if (k & 1) {
+                uint32_t hh = cvt_bf16x2(r[k - 1], r[k]);
+                asm volatile("" : "+v"(hh));
+                ep[k - 1] = (hh >> 4) & 0x7F8u;
+                ep[k] = (hh >> 20) & 0x7F8u;
+                uint32_t b;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b) : "s"(0x00800080u), "v"(hh >> 8), "v"(hh));
+                st8(lay.sw + rp + (k - 1) * US + l, b);
+                st8hi(lay.sw + rp + k * US + l, b);
+                // a pair of codes (at most 16 bits each) as one put
+                st.put(wc[k - 1].x | (wc[k].x << wc[k - 1].y), wc[k - 1].y + wc[k].y);
+                st.flush();
+            }
+            if (DEC) {
+                ewC[k] = (wkw << (enw & 31u)) | enw;
+                emC[k] = (wkm << (enm & 31u)) | enm;
+                cw += (enw >> 8) & 0xFFu;
+                cm += (enm >> 8) & 0xFFu;
             }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) {
-                uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
-                if (gi < CH) {
-                    wkw = winw >> cw;
-                    wkm = winm >> cm;
-                    enw = ld32(kSgdWTab + (wkw & 0x3FCu));
-                    enm = ld32(kSgdMTab + (wkm & 0x3FCu));
-                }
-                if (gi > 0) {
-                    const uint32_t i = gi - 4 + k;
-                    r[i] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32s(ms[i], em[i], jsel)),
-                                          __uint_as_float(join32s(ws[i], ew[i], jsel)));
-                    nan |= r[i] != r[i];
-                    if (k & 1) {
-                        uint32_t h = cvt_bf16x2(r[i - 1], r[i]);
-                        asm volatile("" : "+v"(h));
-                        split(h, i - 1);
-                    }
-                }
-                if (gi < CH && (k & 1)) {
-                    // a pair of codes (at most 16 bits each) as one put
-                    const u32x2 c0 = wc[gi + k - 1], c1 = wc[gi + k];
-                    st.put(c0.x | (c1.x << c0.y), c0.y + c1.y);
-                    st.flush();
-                }
-                if (gi < CH) {
-                    ew[gi + k] = (wkw << (enw & 31u)) | enw;
-                    em[gi + k] = (wkm << (enm & 31u)) | enm;
-                    cw += (enw >> 8) & 0xFFu;
-                    cm += (enm >> 8) & 0xFFu;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (gi < CH) {
-                rw.q = min(rw.q + (int32_t)cw, qwmax);
-                rm.q = min(rm.q + (int32_t)cm, qmmax);
-                cmax = max(cmax, max(cw, cm));
-            }
         }
-        if (__builtin_expect(!__all(cmax <= 30 && !nan), 0)) {
-            // W's bytes in the slab are already results: take them from
-            // memory, which the result reaches only a step later
-            const uint8_t *wsrc = p.w_sf + r0 + (uint64_t)j0 * NS + l;
-            rw.q = qw0;
-            rm.q = qm0;
+        if (DEC) {
+            rw.q = min(rw.q + (int32_t)cw, qwmax);
+            rm.q = min(rm.q + (int32_t)cm, qmmax);
+        }
+        if (__builtin_expect(!__all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
+            if (DEC && !__all(max(cw, cm) <= 30)) {
+                // a window ran out: group s again, one field per window
+                rw.q = qw0;
+                rm.q = qm0;
 #pragma unroll
-            for (uint32_t i = 0; i < CH; i += 2) {
-                uint32_t R[2];
-#pragma unroll
-                for (uint32_t t = 0; t < 2; ++t) {
-                    const uint32_t fw = rw.next(kSgdWTab), fm = rm.next(kSgdMTab);
+                for (uint32_t k = 0; k < 4; ++k) {
+                    ewC[k] = rw.next(kSgdWTab);
+                    emC[k] = rm.next(kSgdMTab);
                     rw.q = min(rw.q, qwmax);
                     rm.q = min(rm.q, qmmax);
-                    R[t] = sgd_round(join32(wsrc[(i + t) * NS], fw),
-                                     join32(ld8(sm + (row + i + t) * US + l), fm), p.neg_eta);
                 }
-                split((R[0] >> 16) | (R[1] & 0xFFFF0000u), i);
+            }
+            // group s-1 with the integer rounding (same fields; a NaN's byte
+            // becomes the canonical one's)
+#pragma unroll
+            for (uint32_t k = 0; k < 4; k += 2) {
+                const uint32_t R0 = sgd_round(join32s(wsP[k], ewP[k], jsel), join32s(msP[k], emP[k], jsel), p.neg_eta);
+                const uint32_t R1 =
+                    sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel), join32s(msP[k + 1], emP[k + 1], jsel), p.neg_eta);
+                const uint32_t hh = (R0 >> 16) | (R1 & 0xFFFF0000u);
+                ep[k] = (hh >> 4) & 0x7F8u;
+                ep[k + 1] = (hh >> 20) & 0x7F8u;
+                uint32_t b;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(b) : "s"(0x00800080u), "v"(hh >> 8), "v"(hh));
+                st8(lay.sw + rp + k * US + l, b);
+                st8hi(lay.sw + rp + (k + 1) * US + l, b);
             }
         }
-        jp = j0;
+        // the writer codes group s-1 next stage
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            wc[k] = ld64(kSgdETab + ep[k]);
+            ew8[k] = ep[k];
+        }
+        jw = 4 * (4 * h + GS) - 4;
+        if (DEC) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                wsP[k] = wsC[k];
+                msP[k] = msC[k];
+                ewP[k] = ewC[k];
+                emP[k] = emC[k];
+            }
+        }
     };
-    // A slab's result bytes are read into registers at the end of its step
-    // and stored after the next slab has been staged: the memory-counter wait
-    // that stages a slab then never includes stores issued just before it,
-    // and a store's registers (which may only be reused once it completes)
-    // stay untouched for a whole step.  Staging and stores are unconditional:
-    // a slab only half inside the block repeats its first half.  The first
-    // step's stores have nothing to store and go past the range.
-    u32x4 out0, out1;
-    uint32_t dst0, dst1;
-    auto put_out = [&]() {
-        __builtin_amdgcn_raw_buffer_store_b128(out0, ros, dst0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(out1, ros, dst1, 0, 0);
+    // Half h: its four stages.  At the end of its first stage the last group
+    // of half h-1 has been split: that half's bytes are read out, its region
+    // takes half h+1 (loaded two halves earlier into `next`), and the loads
+    // of half h+3 go out into the same registers.  Half h-1's bytes leave in
+    // the third stage.
+    auto half = [&](uint32_t h, HalfRegs &next) {
+        wall = __all(st.live && st.total() + CH * 16 <= capbits);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 0>{}, h);
+        if (h == 0) {
+            // the group before the first codes to nothing
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                wc[k] = u32x2{0u, 0u};
+                ew8[k] = kSgdNoField;
+            }
+            jw = 0;
+        } else {
+            outv = ld128(lay.sw + region(h - 1) + mine);
+        }
+        st128(lay.sw + region(h + 1) + mine, next.w);
+        st128(lay.sm + region(h + 1) + mine, next.m);
+        load(next, h + 3);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 1>{}, h);
+        if (h != 0) __builtin_amdgcn_raw_buffer_store_b128(outv, ros, (h - 1) * kHalfB + g, 0, 0);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 2>{}, h);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 3>{}, h);
     };
-    auto step = [&](SlabRegs &r, uint32_t j0) {
-        const bool two = j0 + CH < npos;
-        st128(sw + mine, r.w0);
-        st128(sm + mine, r.m0);
-        st128(sw + kSlabB / 2 + mine, r.w1);
-        st128(sm + kSlabB / 2 + mine, r.m1);
-        put_out();
-        half(j0, 0);
-        if (two) half(j0 + CH, CH);
-        dst0 = j0 * NS + g;
-        dst1 = two ? dst0 + kHalf : dst0;
-        out0 = ld128(sw + mine);
-        out1 = ld128(sw + (two ? kSlabB / 2 : 0) + mine);
-    };
-    SlabRegs a, b;
-    load(a, 0u);
-    out0 = a.w0;
-    out1 = a.w1;
-    dst0 = kNoStore;
-    dst1 = kNoStore;
-    for (uint32_t j0 = 0; j0 < npos; j0 += 2 * kSlabPos) {
-        const uint32_t j1 = j0 + kSlabPos;
-        load(b, j1 < npos ? j1 : j0);
-        step(a, j0);
-        if (j1 >= npos) break;
-        const uint32_t j2 = j1 + kSlabPos;
-        load(a, j2 < npos ? j2 : j1);
-        step(b, j1);
+    HalfRegs a, b;
+    load(a, 0);
+    load(b, 1);
+    st128(lay.sw + mine, a.w);
+    st128(lay.sm + mine, a.m);
+    load(a, 2);
+    for (uint32_t h = 0; h < nh; h += 2) {
+        half(h, b);
+        if (h + 1 < nh) half(h + 1, a);
     }
-    writer_chunk<false>(st, ep, jp, npos, capbits, kSgdETab);
-    writer_spill<false>(st, ep, jp, npos, stage_ctr, stage, p.ovf_cap);
-    put_out();
+    // the last group's arithmetic, the writer's last two groups, the last
+    // half's bytes
+    wall = false;
+    stage_fn(std::false_type{}, std::integral_constant<uint32_t, 0>{}, nh);
+    code_checked();
+    outv = ld128(lay.sw + region(nh - 1) + mine);
+    __builtin_amdgcn_raw_buffer_store_b128(outv, ros, (nh - 1) * kHalfB + g, 0, 0);
 }
 
-template <uint32_t CAPT>
 // Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
 // a lane, AGPRs included.
+template <uint32_t CAPT>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
     stage_dec(p.wdec, kSgdWTab);
