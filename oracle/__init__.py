@@ -87,6 +87,12 @@ def lib():
         L.lcto_sgd_elem.argtypes = [C.c_uint16, C.c_uint16, C.c_float]
         L.lcto_sgd.argtypes = ([P, P, P, P, P, P] + [P, P, P, P, P, P] +
                                [C.c_float, u64, u32, u32, P, P, P, P, P, u64])
+        L.lcto_momentum_elem.restype = None
+        L.lcto_momentum_elem.argtypes = [C.c_uint16, C.c_uint16, C.c_uint16, C.c_float, C.c_float,
+                                         C.POINTER(C.c_uint16), C.POINTER(C.c_uint16)]
+        L.lcto_momentum.argtypes = ([P, P, P, P, P, P] + [P, P, P, P, P, P] +
+                                    [P, C.c_float, C.c_float, u64, u32, u32] +
+                                    [P, P, P, P, P, u64] + [P, P, P, P, P, u64])
         _lib = L
     return _lib
 
@@ -359,3 +365,47 @@ def sgd(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, eta: float,
         raise ValueError("sgd: error %d" % rc)
     o.status = rc
     return o
+
+
+# ---------------------------------------------------------------- momentum step
+
+def momentum_elem(w: int, m: int, g: int, mu: float, eta: float):
+    """(w', m') of one element: m' = rne(fmaf(mu, m, g)), w' = rne(fmaf(-eta, m', w))."""
+    wo, mo = C.c_uint16(), C.c_uint16()
+    lib().lcto_momentum_elem(w, m, g, mu, eta, C.byref(wo), C.byref(mo))
+    return wo.value, mo.value
+
+
+def momentum_dense(w: np.ndarray, m: np.ndarray, g: np.ndarray, mu: float, eta: float):
+    """Element-wise momentum step on raw BF16 bit patterns (serial C)."""
+    w = np.ascontiguousarray(w, np.uint16).reshape(-1)
+    m = np.ascontiguousarray(m, np.uint16).reshape(-1)
+    g = np.ascontiguousarray(g, np.uint16).reshape(-1)
+    wo = np.empty_like(w)
+    mo = np.empty_like(m)
+    for i in range(w.size):
+        wo[i], mo[i] = momentum_elem(int(w[i]), int(m[i]), int(g[i]), mu, eta)
+    return wo, mo
+
+
+def momentum(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, g: np.ndarray,
+             mu: float, eta: float, ovf_cap: int | None = None):
+    """Naive round trip of one momentum step on compressed W and M and dense g:
+    returns (W', M') encoded with cw and cm."""
+    assert (w.n, w.block_elems, w.cap_words) == (m.n, m.block_elems, m.cap_words)
+    g = np.ascontiguousarray(g, np.uint16).reshape(-1)
+    assert g.size == w.n
+    ovf_cap = w.n if ovf_cap is None else ovf_cap
+    ow = _alloc(w.n, w.block_elems, w.cap_words, ovf_cap)
+    om = _alloc(w.n, w.block_elems, w.cap_words, ovf_cap)
+    a, b = cw._c(), cm._c()
+    rc = lib().lcto_momentum(C.byref(a), _p(w.sf), _p(w.pay), _p(w.cnt), _p(w.obase), _p(w.ovf),
+                             C.byref(b), _p(m.sf), _p(m.pay), _p(m.cnt), _p(m.obase), _p(m.ovf),
+                             _p(g), mu, eta, w.n, w.block_elems, w.cap_words,
+                             _p(ow.sf), _p(ow.pay), _p(ow.cnt), _p(ow.obase), _p(ow.ovf), ovf_cap,
+                             _p(om.sf), _p(om.pay), _p(om.cnt), _p(om.obase), _p(om.ovf), ovf_cap)
+    if rc < 0:
+        raise ValueError("momentum: error %d" % rc)
+    ow.status = int(ow.obase[-1] > ovf_cap)
+    om.status = int(om.obase[-1] > ovf_cap)
+    return ow, om

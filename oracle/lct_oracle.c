@@ -21,6 +21,8 @@
  *                 update W_{t+1} = W_t - eta * M_t.
  *   [EXP-ideal]   same page, paragraph with the idealized arithmetic (16/11,
  *                 1.4382x for CLEAN).
+ *   [EXP-jargon]  same page, jargon entry "Optimizer state": the momentum
+ *                 buffer of SGD with momentum, kept for every weight.
  */
 #include "lct_oracle.h"
 
@@ -620,4 +622,76 @@ int lcto_sgd(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay
     free(spill);
     if (rc != LCTO_OK) return rc;
     return o_obase[nblk] > ovf_cap ? LCTO_OVF_FULL : LCTO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Momentum step ([EXP-jargon], [EXP-train]).  The pages name the momentum   */
+/* buffer of SGD with momentum as optimizer state stored compressed, but no  */
+/* update rule; this is the plain heavy-ball form M' = mu*M + g, then        */
+/* W' = W - eta*M', each a single fused multiply-add rounded to fp32, then   */
+/* to BF16 (a NaN written as 0x7FC0); the W update uses M' as stored.        */
+/* ------------------------------------------------------------------------ */
+void lcto_momentum_elem(uint16_t w, uint16_t m, uint16_t g, float mu, float eta,
+                        uint16_t *w_out, uint16_t *m_out)
+{
+    uint16_t m2 = lcto_rne_bf16(fmaf(mu, bf16_to_f32(m), bf16_to_f32(g)));
+    *m_out = m2;
+    *w_out = lcto_rne_bf16(fmaf(-eta, bf16_to_f32(m2), bf16_to_f32(w)));
+}
+
+/* Encode one block's values and append its spilled bytes to ovf at obase[b]. */
+static void encode_block_out(const lcto_codebook *cb, const uint16_t *x, uint32_t nb, uint32_t cap_words,
+                             uint64_t b, uint64_t r0, uint64_t po, uint8_t *spill,
+                             uint8_t *sf, uint32_t *pay, uint16_t *cnt, uint64_t *obase,
+                             uint8_t *ovf, uint64_t ovf_cap)
+{
+    uint32_t ns = 0;
+    lcto_encode_block(cb, x, nb, cap_words, sf + r0, pay + po, cnt + b * NSTREAM, spill, &ns);
+    for (uint32_t i = 0; i < ns; i++)
+        if (obase[b] + i < ovf_cap) ovf[obase[b] + i] = spill[i];
+    obase[b + 1] = obase[b] + ns;
+}
+
+int lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay,
+                  const uint16_t *w_cnt, const uint64_t *w_obase, const uint8_t *w_ovf,
+                  const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
+                  const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
+                  const uint16_t *g, float mu, float eta,
+                  uint64_t n, uint32_t block_elems, uint32_t cap_words,
+                  uint8_t *ow_sf, uint32_t *ow_pay, uint16_t *ow_cnt, uint64_t *ow_obase,
+                  uint8_t *ow_ovf, uint64_t ow_ovf_cap,
+                  uint8_t *om_sf, uint32_t *om_pay, uint16_t *om_cnt, uint64_t *om_obase,
+                  uint8_t *om_ovf, uint64_t om_ovf_cap)
+{
+    if (!layout_ok(block_elems, cap_words)) return LCTO_EINVAL;
+    uint64_t nblk = (n + block_elems - 1) / block_elems;
+    uint16_t *wd = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
+    uint16_t *md = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
+    uint8_t *spill = (uint8_t *)malloc(block_elems);
+    int rc = LCTO_OK;
+    if (!wd || !md || !spill) rc = LCTO_EINVAL;
+    if (rc == LCTO_OK) {
+        ow_obase[0] = 0;
+        om_obase[0] = 0;
+    }
+    for (uint64_t b = 0; b < nblk && rc == LCTO_OK; b++) {
+        uint64_t r0 = b * block_elems, po = b * (uint64_t)cap_words * NSTREAM;
+        uint32_t nb = (uint32_t)((n - r0) < block_elems ? (n - r0) : block_elems);
+        rc = lcto_decode_block(cw, w_sf + r0, w_pay + po, w_cnt + b * NSTREAM, w_ovf + w_obase[b],
+                               nb, cap_words, wd);
+        if (rc != LCTO_OK) break;
+        rc = lcto_decode_block(cm, m_sf + r0, m_pay + po, m_cnt + b * NSTREAM, m_ovf + m_obase[b],
+                               nb, cap_words, md);
+        if (rc != LCTO_OK) break;
+        for (uint32_t r = 0; r < nb; r++) lcto_momentum_elem(wd[r], md[r], g[r0 + r], mu, eta, &wd[r], &md[r]);
+        encode_block_out(cw, wd, nb, cap_words, b, r0, po, spill, ow_sf, ow_pay, ow_cnt, ow_obase, ow_ovf,
+                         ow_ovf_cap);
+        encode_block_out(cm, md, nb, cap_words, b, r0, po, spill, om_sf, om_pay, om_cnt, om_obase, om_ovf,
+                         om_ovf_cap);
+    }
+    free(wd);
+    free(md);
+    free(spill);
+    if (rc != LCTO_OK) return rc;
+    return (ow_obase[nblk] > ow_ovf_cap || om_obase[nblk] > om_ovf_cap) ? LCTO_OVF_FULL : LCTO_OK;
 }

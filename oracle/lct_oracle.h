@@ -142,6 +142,28 @@ int  lcto_sgd(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pa
               uint8_t *o_sf, uint32_t *o_pay, uint16_t *o_cnt, uint64_t *o_obase,
               uint8_t *o_ovf, uint64_t ovf_cap);
 
+/* ---- Momentum step ([EXP-jargon], [EXP-train]) ---------------------------- */
+
+/* One element of SGD with momentum: m' = rne(fmaf(mu, f32(m), f32(g))), then
+ * w' = rne(fmaf(-eta, f32(m'), f32(w))) with m' as stored (BF16). */
+void lcto_momentum_elem(uint16_t w, uint16_t m, uint16_t g, float mu, float eta,
+                        uint16_t *w_out, uint16_t *m_out);
+
+/* Naive round trip of one momentum step: decode W (codebook cw) and M (cm)
+ * fully, update densely with the dense gradient g, re-encode W' with cw and
+ * M' with cm.  Inputs and outputs share n, block_elems and cap_words.
+ * Returns LCTO_OVF_FULL if either output's spill exceeds its ovf_cap. */
+int  lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay,
+                   const uint16_t *w_cnt, const uint64_t *w_obase, const uint8_t *w_ovf,
+                   const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
+                   const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
+                   const uint16_t *g, float mu, float eta,
+                   uint64_t n, uint32_t block_elems, uint32_t cap_words,
+                   uint8_t *ow_sf, uint32_t *ow_pay, uint16_t *ow_cnt, uint64_t *ow_obase,
+                   uint8_t *ow_ovf, uint64_t ow_ovf_cap,
+                   uint8_t *om_sf, uint32_t *om_pay, uint16_t *om_cnt, uint64_t *om_obase,
+                   uint8_t *om_ovf, uint64_t om_ovf_cap);
+
 #ifdef __cplusplus
 }
 #endif
