@@ -24,7 +24,8 @@
  *     The library allocates no device memory of its own, except one 8 KiB
  *     static array per device used by lct_codebook_build() for its sample.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     lct_encode, lct_decode and lct_sgd_step only enqueue work on it and
+ *     lct_encode, lct_decode, lct_sgd_step and lct_momentum_step only enqueue
+ *     work on it and
  *     return at once; lct_codebook_build synchronises it.
  *   - Errors found on the host (null pointer, bad size, misalignment, illegal
  *     aliasing, wrong device) are returned before anything is enqueued.
@@ -54,7 +55,7 @@ typedef enum {
 } lct_status;
 
 /* Device status word bits, OR-ed in by the kernels (the word is cleared at the
- * start of every lct_encode / lct_sgd_step). */
+ * start of every lct_encode / lct_sgd_step / lct_momentum_step). */
 #define LCT_ST_OVF_FULL 0x1u   /* total spill > ovf_cap: the overflow region is incomplete;
                                   obase[nblk] still holds the size needed */
 #define LCT_ST_LOOKBACK 0x2u   /* overflow-offset scan gave up waiting (never expected) */
@@ -117,7 +118,8 @@ typedef struct {
  *              stream, position) order
  *   status     uint32[1]  LCT_ST_* bits
  *   scratch    lct_sizes().scratch bytes of working memory (256-byte aligned);
- *              only lct_encode and lct_sgd_step use it.  It may be shared by
+ *              only lct_encode and the output of lct_sgd_step and
+ *              lct_momentum_step use it.  It may be shared by
  *              calls that do not overlap in time.
  * Element r of block b (r < block_elems) is position r / 256 of stream r % 256. */
 typedef struct {
@@ -200,6 +202,24 @@ lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_
 lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in,
                         const lct_codebook *cm, const lct_tensor *m,
                         float eta, const lct_tensor *w_out, void *stream);
+
+/* Momentum step (explainer, jargon entry "Optimizer state": the momentum
+ * buffer of SGD with momentum is stored compressed like the weights; paragraph
+ * on training traffic: decode, update, re-encode in one pass).  Element by
+ * element, m' = rne_bf16(fmaf(mu, f32(m), f32(g))), then
+ * w' = rne_bf16(fmaf(-eta, f32(m'), f32(w))) with m' as stored; a NaN result
+ * is written as 0x7FC0.  W' is encoded with cw, M' with cm.
+ * d_g: the dense gradient, device BF16 bit patterns, n elements, 16-byte
+ * aligned, overlapping no output.  w_in, m_in, w_out, m_out share n and
+ * layout.  Each output's sf, pay, cnt and obase may be its own input's
+ * (in-place step) or disjoint from every input; its ovf, status and scratch
+ * must not overlap any input, and the two outputs must not overlap each other.
+ * Each output has its own status word (LCT_ST_OVF_FULL as for lct_encode).
+ * Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS, LCT_EARCH, LCT_EHIP. */
+lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in,
+                             const lct_codebook *cm, const lct_tensor *m_in,
+                             const uint16_t *d_g, float mu, float eta,
+                             const lct_tensor *w_out, const lct_tensor *m_out, void *stream);
 
 /* Message for a status code (static string). */
 const char *lct_strerror(lct_status st);

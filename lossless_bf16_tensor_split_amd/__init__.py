@@ -13,8 +13,9 @@ Functions keep the C names:
     lct_encode(cb, x, out)            (out: LctTensor from alloc_tensor)
     lct_decode(cb, t, y)
     lct_sgd_step(cw, w_in, cm, m, eta, w_out)
+    lct_momentum_step(cw, w_in, cm, m_in, g, mu, eta, w_out, m_out)
 plus ``alloc_tensor`` and the convenience wrappers ``encode`` / ``decode`` /
-``sgd_step`` that allocate their outputs.
+``sgd_step`` / ``momentum_step`` that allocate their outputs.
 """
 from __future__ import annotations
 
@@ -32,7 +33,8 @@ ST_OVF_FULL, ST_LOOKBACK = 0x1, 0x2
 OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_from_lengths",
-            "lct_encode", "lct_decode", "lct_sgd_step", "lct_strerror", "lct_last_hip_error"]
+            "lct_encode", "lct_decode", "lct_sgd_step", "lct_momentum_step", "lct_strerror",
+            "lct_last_hip_error"]
 
 
 class Model(C.Structure):
@@ -80,6 +82,9 @@ def _load():
     L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
     L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
                                C.POINTER(_Tensor), C.c_float, C.POINTER(_Tensor), P]
+    L.lct_momentum_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
+                                    C.POINTER(_Tensor), P, C.c_float, C.c_float, C.POINTER(_Tensor),
+                                    C.POINTER(_Tensor), P]
     L.lct_strerror.restype = C.c_char_p
     L.lct_strerror.argtypes = [i32]
     L.lct_last_hip_error.restype = C.c_char_p
@@ -226,6 +231,13 @@ def lct_sgd_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta:
                             _stream(stream)), "lct_sgd_step")
 
 
+def lct_momentum_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: LctTensor, g: torch.Tensor,
+                      mu: float, eta: float, w_out: LctTensor, m_out: LctTensor, stream=None) -> None:
+    a, b, ow, om = w_in.c(), m_in.c(), w_out.c(), m_out.c()
+    _check(lib.lct_momentum_step(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), _ptr(g), mu, eta,
+                                 C.byref(ow), C.byref(om), _stream(stream)), "lct_momentum_step")
+
+
 # ------------------------------------------------------------------ conveniences
 
 def encode(cb: Codebook, x: torch.Tensor, lay: Layout, ovf_cap: int | None = None,
@@ -247,3 +259,14 @@ def sgd_step(cw: Codebook, w: LctTensor, cm: Codebook, m: LctTensor, eta: float,
         out = alloc_tensor(w.n, w.layout, ovf_cap, w.sf.device)
     lct_sgd_step(cw, w, cm, m, eta, out)
     return out
+
+
+def momentum_step(cw: Codebook, w: LctTensor, cm: Codebook, m: LctTensor, g: torch.Tensor,
+                  mu: float, eta: float, w_out: LctTensor | None = None, m_out: LctTensor | None = None,
+                  ovf_cap: int | None = None):
+    if w_out is None:
+        w_out = alloc_tensor(w.n, w.layout, ovf_cap, w.sf.device)
+    if m_out is None:
+        m_out = alloc_tensor(m.n, m.layout, ovf_cap, m.sf.device)
+    lct_momentum_step(cw, w, cm, m, g, mu, eta, w_out, m_out)
+    return w_out, m_out

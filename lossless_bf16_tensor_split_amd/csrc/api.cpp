@@ -301,6 +301,108 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
     return LCT_OK;
 }
 
+lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
+                             const lct_tensor *m_in, const uint16_t *d_g, float mu, float eta,
+                             const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
+    if (!cw || !cm || !w_in || !m_in || !w_out || !m_out) return LCT_EINVAL;
+    const lct_tensor *all[] = {w_in, m_in, w_out, m_out};
+    for (const lct_tensor *t : all)
+        if (t->n != w_in->n || t->layout.block_elems != w_in->layout.block_elems ||
+            t->layout.cap_words != w_in->layout.cap_words)
+            return LCT_EINVAL;
+    if (w_in->n == 0) return LCT_OK;
+    if (!d_g) return LCT_EINVAL;
+    if (!aligned(d_g, 16)) return LCT_EALIGN;
+    lct_status st = check_tensor(w_in, false);
+    if (st == LCT_OK) st = check_tensor(m_in, false);
+    if (st == LCT_OK) st = check_tensor(w_out, true);
+    if (st == LCT_OK) st = check_tensor(m_out, true);
+    if (st != LCT_OK) return st;
+    const Parts pw = parts(*w_in), pm = parts(*m_in), qw = parts(*w_out), qm = parts(*m_out);
+    const Range g = rng(d_g, w_in->n * 2);
+    // the gradient is read only: no output may overlap it
+    if (overlaps_any(g, qw) || overlaps_any(g, qm)) return LCT_EALIAS;
+    // the outputs are disjoint from each other
+    const Range qws[] = {qw.sf, qw.pay, qw.cnt, qw.obase, qw.ovf, qw.status, qw.scratch};
+    for (const Range &r : qws)
+        if (overlaps_any(r, qm)) return LCT_EALIAS;
+    // each output's fixed side is its own input's buffers, exactly, or disjoint
+    // from every input; its overflow, status and scratch overlap no input
+    auto check_out = [&](const Parts &own, const Parts &other, const Parts &q) {
+        const Range in[] = {own.sf, own.pay, own.cnt, own.obase};
+        const Range out[] = {q.sf, q.pay, q.cnt, q.obase};
+        for (int i = 0; i < 4; ++i) {
+            for (int j = 0; j < 4; ++j) {
+                const bool same = i == j && in[i].lo == out[j].lo;
+                if (!same && overlap(in[i], out[j])) return false;
+            }
+            if (overlap(own.ovf, out[i])) return false;
+            if (overlaps_any(out[i], other, false)) return false;
+        }
+        const Range rest[] = {q.ovf, q.status, q.scratch};
+        for (const Range &r : rest)
+            if (overlaps_any(r, own, false) || overlaps_any(r, other, false)) return false;
+        return true;
+    };
+    if (!check_out(pw, pm, qw) || !check_out(pm, pw, qm)) return LCT_EALIAS;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+
+    const uint64_t nb = nblocks(w_in->n, w_in->layout);
+    if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
+    MomParams p;
+    memset(&p, 0, sizeof p);
+    p.w_sf = w_in->sf;
+    p.w_pay = w_in->pay;
+    p.w_cnt = w_in->cnt;
+    p.w_obase = w_in->obase;
+    p.w_ovf = w_in->ovf;
+    p.w_ovf_cap = w_in->ovf_cap;
+    p.m_sf = m_in->sf;
+    p.m_pay = m_in->pay;
+    p.m_cnt = m_in->cnt;
+    p.m_obase = m_in->obase;
+    p.m_ovf = m_in->ovf;
+    p.m_ovf_cap = m_in->ovf_cap;
+    p.g = d_g;
+    auto out = [](const lct_tensor &t, const lct_tensor &in) {
+        MomOut o;
+        memset(&o, 0, sizeof o);
+        o.sf = t.sf;
+        o.pay = t.pay;
+        o.cnt = t.cnt;
+        o.obase = t.obase;
+        o.ovf = t.ovf;
+        o.ovf_cap = t.ovf_cap;
+        o.status = t.status;
+        o.scratch = (uint8_t *)t.scratch;
+        o.park_cnt = t.cnt == in.cnt;
+        return o;
+    };
+    p.ow = out(*w_out, *w_in);
+    p.om = out(*m_out, *m_in);
+    p.n = w_in->n;
+    p.block_elems = w_in->layout.block_elems;
+    p.cap_words = w_in->layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.mu = mu;
+    p.neg_eta = -eta;
+    fill_enc(*cw, &p.wenc);
+    fill_enc(*cm, &p.menc);
+    fill_dec(*cw, &p.wdec);
+    fill_dec(*cm, &p.mdec);
+    int e = launch_clear(p.ow.scratch, nb, p.ow.status, stream);
+    if (e == hipSuccess) e = launch_clear(p.om.scratch, nb, p.om.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_momentum(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "momentum launch");
+    e = launch_scan(p.ow.scratch, nb, p.ow.obase, p.ow.ovf, p.ow.ovf_cap, p.ow.status, p.ow.cnt, stream);
+    if (e == hipSuccess)
+        e = launch_scan(p.om.scratch, nb, p.om.obase, p.om.ovf, p.om.ovf_cap, p.om.status, p.om.cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return LCT_OK;
+}
+
 const char *lct_strerror(lct_status st) {
     switch (st) {
     case LCT_OK: return "ok";

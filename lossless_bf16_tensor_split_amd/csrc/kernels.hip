@@ -1255,6 +1255,149 @@ void k_sgd(const SgdParams p) {
     }
 }
 
+// ------------------------------------------------------------------ momentum step
+
+// SGD with momentum on compressed W and M (explainer, jargon entry "Optimizer
+// state": the momentum buffer is stored compressed like the weights; paragraph
+// on training traffic: decode, update, re-encode in one pass), with a dense
+// BF16 gradient g: m' = rne(fmaf(mu, m, g)), w' = rne(fmaf(-eta, m', w)).  Two
+// writers per lane (W' with W's code, M' with M's), each to its own payload
+// rows in memory and its own overflow staging; the units and the pairing of
+// waves are the update's.  Byte-wide accesses with per-element checks (the
+// update's general path, twice over).
+constexpr uint32_t kMomWaves = 2;
+constexpr uint32_t kMomWEnc = 0, kMomMEnc = 2048, kMomWDec = 4096, kMomMDec = 5120, kMomWave0 = 6144;
+
+// A wave's region: W's zero row -1 and rows 0..cap-1; a zero row (W's row cap
+// and M's row -1); M's rows; a zero row.
+struct MomLayout {
+    uint32_t z0, w0, z1, m0, z2, end;
+    __host__ __device__ constexpr MomLayout(uint32_t cap, uint32_t base)
+        : z0(base), w0(base + ROWB), z1(w0 + cap * ROWB), m0(z1 + ROWB), z2(m0 + cap * ROWB), end(z2 + ROWB) {}
+};
+__host__ __device__ constexpr uint32_t mom_wave_bytes(uint32_t cap) { return MomLayout(cap, 0).end; }
+
+struct Buf3 {
+    uint32_t w[CH], m[CH], g[CH];
+};
+
+template <uint32_t CAPT>
+__device__ __forceinline__ void mom_stream(const MomParams &p, const MomLayout &lay, PayWriter &stw,
+                                           PayWriter &stm, uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
+                                           uint64_t r0, uint64_t wsp, uint64_t msp) {
+    const uint32_t s = lane();
+    const uint32_t npos = p.block_elems / NS;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const uint32_t capbits = 32 * cap;
+    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
+    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    const uint8_t *wsf = p.w_sf + r0 + s;
+    const uint8_t *msf = p.m_sf + r0 + s;
+    const uint16_t *gs = p.g + r0 + s;
+    uint8_t *owsf = p.ow.sf + r0 + s;
+    uint8_t *omsf = p.om.sf + r0 + s;
+    uint64_t *wctr = reinterpret_cast<uint64_t *>(p.ow.scratch + kScrStage);
+    uint8_t *wstage = p.ow.scratch + scr_stage_offset(p.nblk);
+    uint64_t *mctr = reinterpret_cast<uint64_t *>(p.om.scratch + kScrStage);
+    uint8_t *mstage = p.om.scratch + scr_stage_offset(p.nblk);
+    Reader rw, rm;
+    rw.init(lay.w0, s);
+    rm.init(lay.m0, s);
+    double_buffered<Buf3>(
+        npos,
+        [&](Buf3 &bf, uint32_t j0) {
+            load_chunk<true>(bf.w, wsf, j0, n_s);
+            load_chunk<true>(bf.m, msf, j0, n_s);
+            load_chunk<true>(bf.g, gs, j0, n_s);
+        },
+        [&](Buf3 &bf, uint32_t j0) {
+            uint32_t ew8[CH], em8[CH];
+            uint8_t *ow = owsf + (size_t)j0 * NS;
+            uint8_t *om = omsf + (size_t)j0 * NS;
+#pragma unroll
+            for (uint32_t i = 0; i < CH; ++i) {
+                const uint32_t j = j0 + i;
+                uint32_t ew = rw.next(kMomWDec);
+                uint32_t em = rm.next(kMomMDec);
+                rw.q = min(rw.q, qwmax);
+                rm.q = min(rm.q, qmmax);
+                if (j >= cw_s && j < n_s) {
+                    const uint64_t k = wsp + (j - cw_s);
+                    ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                }
+                if (j >= cm_s && j < n_s) {
+                    const uint64_t k = msp + (j - cm_s);
+                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                }
+                // m' = rne(fmaf(mu, m, g)), then w' = rne(fmaf(-eta, m', w)) with m'
+                // as stored (results in bits 31..16)
+                const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], em), p.mu);
+                const uint32_t Rw = sgd_round(join32(bf.w[i], ew), Rm & 0xFFFF0000u, p.neg_eta);
+                if (j < n_s) {
+                    ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
+                    om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
+                }
+                ew8[i] = (Rw >> 20) & 0x7F8u;   // 8 * exponent field
+                em8[i] = (Rm >> 20) & 0x7F8u;
+            }
+            writer_chunk<true>(stw, ew8, j0, n_s, capbits, kMomWEnc);
+            writer_spill<true>(stw, ew8, j0, n_s, wctr, wstage, p.ow.ovf_cap);
+            writer_chunk<true>(stm, em8, j0, n_s, capbits, kMomMEnc);
+            writer_spill<true>(stm, em8, j0, n_s, mctr, mstage, p.om.ovf_cap);
+        });
+}
+
+template <uint32_t CAPT>
+__global__ __launch_bounds__(64 * kMomWaves) void k_momentum(const MomParams p) {
+    stage_dec(p.wdec, kMomWDec);
+    stage_dec(p.mdec, kMomMDec);
+    stage_enc(p.wenc, kMomWEnc);
+    stage_enc(p.menc, kMomMEnc);
+    __syncthreads();
+    const uint32_t l = lane();
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const MomLayout lay(cap, kMomWave0 + wave_id() * mom_wave_bytes(cap));
+    st32(lay.z0 + 4 * l, 0);
+    st32(lay.z1 + 4 * l, 0);
+    st32(lay.z2 + 4 * l, 0);
+    const uint32_t nunits = p.nblk * kMaxUnits;
+    // An output in place over its input overwrites counts that other units of
+    // the block still read: they are parked and put in place by the scan.
+    uint16_t *wcnt = p.ow.park_cnt ? reinterpret_cast<uint16_t *>(p.ow.scratch + scr_cnt_offset(p.nblk))
+                                   : p.ow.cnt;
+    uint16_t *mcnt = p.om.park_cnt ? reinterpret_cast<uint16_t *>(p.om.scratch + scr_cnt_offset(p.nblk))
+                                   : p.om.cnt;
+    const uint32_t stride = gridDim.x * kMomWaves;
+    // the two waves of a workgroup take units 2i and 2i+1 of one block (whose
+    // sign-fraction bytes share lines) and meet at every unit; both take the
+    // same number of trips
+    static_assert(kMomWaves == 2 && kMaxUnits % kMomWaves == 0, "pairs of units per workgroup");
+    for (uint32_t u = first_unit(kMomWaves); u < nunits; u += stride) {
+        __builtin_amdgcn_s_barrier();
+        const uint32_t b = unit_block(u), h = unit_part(u);
+        const uint64_t wob = p.w_obase[b], mob = p.m_obase[b];
+        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        const uint64_t r0 = (uint64_t)b * p.block_elems;
+        const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+        const uint32_t n_s = stream_len(nb, h * US + l);
+        uint32_t cw_s, cm_s, wex, mex;
+        unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
+        unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
+        // the results' rows go straight to memory: the inputs' rows, which a
+        // step in place overwrites, are all in LDS by now
+        PayWriter stw, stm;
+        stw.init(0, l, n_s);
+        stw.rows.init(p.ow.pay, b, h, cap);
+        stm.init(0, l, n_s);
+        stm.rows.init(p.om.pay, b, h, cap);
+        mom_stream<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
+        const UnitOut ow{p.ow.pay, wcnt, p.ow.scratch, p.nblk, p.ow.ovf_cap, cap, p.ow.park_cnt};
+        unit_finish(stw, n_s, u, b, h, 0, ow);
+        const UnitOut om{p.om.pay, mcnt, p.om.scratch, p.nblk, p.om.ovf_cap, cap, p.om.park_cnt};
+        unit_finish(stm, n_s, u, b, h, 0, om);
+    }
+}
+
 // ------------------------------------------------------------------ launches
 
 // Dynamic LDS beyond 64 KiB must be requested per kernel; remember the
@@ -1283,8 +1426,9 @@ struct ByCap {
 template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C>); } };
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C>); } };
 template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C>); } };
+template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_momentum<C>); } };
 
-std::atomic<size_t> g_lds_granted[3][4];
+std::atomic<size_t> g_lds_granted[4][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
@@ -1319,6 +1463,7 @@ int launch(const void *fn, uint64_t nunits, uint32_t waves, bool persistent, siz
 size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wave_bytes(cap); }
 size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
 size_t sgd_lds(uint32_t cap) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap); }
+size_t mom_lds(uint32_t cap) { return kMomWave0 + (size_t)kMomWaves * mom_wave_bytes(cap); }
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
@@ -1349,6 +1494,11 @@ int launch_decode(const DecodeParams &p, void *stream) {
 int launch_sgd(const SgdParams &p, void *stream) {
     return launch(ByCap<SgdK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true,
                   sgd_lds(p.cap_words), p, stream, g_lds_granted[2][cap_slot(p.cap_words)]);
+}
+
+int launch_momentum(const MomParams &p, void *stream) {
+    return launch(ByCap<MomK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kMomWaves, true,
+                  mom_lds(p.cap_words), p, stream, g_lds_granted[3][cap_slot(p.cap_words)]);
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {

@@ -208,3 +208,47 @@ def test_invalid_arguments_rejected_on_host(L):
     m2 = _fake_tensor(L, n + 1, lay, 0x3000_0000_0000)
     assert sgd(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m2), C.c_float(1e-3), C.byref(o), None) == L.EINVAL
     assert L.lib.lct_strerror(L.EALIAS) == b"illegal buffer overlap"
+
+
+def test_momentum_arguments_rejected_on_host(L):
+    """Every descriptor below is rejected before any launch (fake addresses
+    never reach a kernel)."""
+    lay = L.layout(65536, 25)
+    cb = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    n = 100000
+    mom = L.lib.lct_momentum_step
+    w = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    m = _fake_tensor(L, n, lay, 0x3000_0000_0000)
+    ow = _fake_tensor(L, n, lay, 0x5000_0000_0000)
+    om = _fake_tensor(L, n, lay, 0x6000_0000_0000)
+    g = C.c_void_p(0x7000_0000_0000)
+
+    def call(g_, w_=w, m_=m, ow_=ow, om_=om):
+        return mom(C.byref(cb), C.byref(w_), C.byref(cb), C.byref(m_), g_, C.c_float(0.9), C.c_float(1e-3),
+                   C.byref(ow_), C.byref(om_), None)
+
+    assert call(None) == L.EINVAL
+    assert call(C.c_void_p(0x7000_0000_0002)) == L.EALIGN
+    # gradient on an output
+    assert call(C.c_void_p(ow.pay)) == L.EALIAS
+    assert call(C.c_void_p(om.scratch)) == L.EALIAS
+    # the two outputs overlapping
+    bad = _fake_tensor(L, n, lay, 0x6000_0000_0000, ovf=ow.ovf)
+    assert call(g, om_=bad) == L.EALIAS
+    # W' on M's buffers, M' on W's
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, sf=m.sf)
+    assert call(g, ow_=bad) == L.EALIAS
+    bad = _fake_tensor(L, n, lay, 0x6000_0000_0000, pay=w.pay)
+    assert call(g, om_=bad) == L.EALIAS
+    # an output's overflow on its input's overflow; a partial overlap of the fixed side
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, ovf=w.ovf)
+    assert call(g, ow_=bad) == L.EALIAS
+    bad = _fake_tensor(L, n, lay, 0x6000_0000_0000, cnt=m.cnt + 8)
+    assert call(g, om_=bad) == L.EALIAS
+    # size mismatch
+    m2 = _fake_tensor(L, n + 1, lay, 0x3000_0000_0000)
+    assert call(g, m_=m2) == L.EINVAL
+    # n == 0 is a no-op
+    z = [_fake_tensor(L, 0, lay, base) for base in (0x1000_0000_0000, 0x3000_0000_0000,
+                                                    0x5000_0000_0000, 0x6000_0000_0000)]
+    assert call(None, *z) == L.OK

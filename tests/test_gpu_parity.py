@@ -261,3 +261,75 @@ def test_config3_gpt162m_flat(L, orc):
     B, cw = synth.mode_layout(synth.CLEAN)
     ref = sgd_case(L, orc, w, m, mw, mm, eta, B, cw, True, what="config3")
     assert ref.spilled == 0
+
+
+# ------------------------------------------------------------------ momentum step
+
+def momentum_case(L, orc, w, m, gr, mw, mm, mu, eta, B, cw, inplace, what=""):
+    cbw, ocw = check_codebook(L, orc, mw, w)
+    cbm, ocm = check_codebook(L, orc, mm, m)
+    lay = L.layout(B, cw)
+    tw = L.encode(cbw, dev(w), lay)
+    tm = L.encode(cbm, dev(m), lay)
+    rw = orc.encode(ocw, w, B, cw)
+    rm = orc.encode(ocm, m, B, cw)
+    assert_same(host_parts(tw), rw, what + " W")
+    assert_same(host_parts(tm), rm, what + " M")
+    ref_w, ref_m = orc.momentum(ocw, rw, ocm, rm, gr, mu, eta)
+    ow = L.alloc_tensor(w.size, lay)
+    om = L.alloc_tensor(w.size, lay)
+    if inplace:
+        ow.sf, ow.pay, ow.cnt, ow.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+        om.sf, om.pay, om.cnt, om.obase = tm.sf, tm.pay, tm.cnt, tm.obase
+    L.lct_momentum_step(cbw, tw, cbm, tm, dev(gr), mu, eta, ow, om)
+    for out, ref, cb, ocb, name in ((ow, ref_w, cbw, ocw, " W'"), (om, ref_m, cbm, ocm, " M'")):
+        g = host_parts(out)
+        assert_same(g, ref, what + name)
+        assert g["status"] == ref.status
+        y = L.decode(cb, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), orc.decode(ocb, ref))
+    return ref_w, ref_m
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 1), (8192, 3), (32768, 12)])
+def test_momentum_small_with_spills(L, orc, B, cw, inplace):
+    g = np.random.default_rng(B + 3 * cw)
+    n = 5 * B + 531
+    w = synth.to_bf16_bits(g.laplace(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-2, n))
+    gr = synth.to_bf16_bits(g.normal(0, 0.1, n))
+    specials = [0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x8001, 0x7F7F, 0xFF7F]
+    m[:64] = specials * 8
+    w[100:164] = specials * 8
+    gr[300:364] = specials * 8
+    ref_w, ref_m = momentum_case(L, orc, w, m, gr, synth.Model(1, 0.02), synth.Model(0, 1e-2), 0.9, 0.05,
+                                 B, cw, inplace, what="B=%d cw=%d inplace=%s" % (B, cw, inplace))
+    if cw == 1:
+        assert ref_w.spilled > 0 and ref_m.spilled > 0
+
+
+def test_momentum_zero_rates(L, orc):
+    """mu = 0 makes M' the gradient; eta = 0 keeps W (no -0 in W, no zero in g)."""
+    g = np.random.default_rng(5)
+    n = 3 * 65536 + 17
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    w[w == 0x8000] = 0
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr[(gr & 0x7FFF) == 0] = 0x3A83
+    ref_w, ref_m = momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.0, 0.0,
+                                 65536, 25, True, what="zero rates")
+    assert np.array_equal(orc.decode(orc.codebook_build(0, 1e-3, 0.0, m), ref_m), gr)
+    assert np.array_equal(orc.decode(orc.codebook_build(0, 0.02, 0.0, w), ref_w), w)
+
+
+def test_momentum_gpt162m_flat(L, orc):
+    """One momentum step over the flat 162M-parameter set, checked in full."""
+    ws, ms, mw, mm, eta = synth.config3()
+    w = np.concatenate([synth.draw(s) for s in ws])
+    m = np.concatenate([synth.draw(s) for s in ms])
+    gr = synth.draw(synth.TensorSpec("g.flat", (w.size,), 3100, "normal", {"sigma": 1e-3}))
+    B, cw = synth.mode_layout(synth.CLEAN)
+    momentum_case(L, orc, w, m, gr, mw, mm, 0.9, eta, B, cw, True, what="momentum config3")
