@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -68,6 +69,8 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=2048,
                     help="blocks in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the momentum step timed after the headline step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a buffer of this many MiB once (a plain "
                          "device copy whose HBM bytes are known, to scale rocprofv3 byte counters)")
@@ -218,6 +221,59 @@ def main():
     dom = max(times, key=times.get)
     traffic = load_traffic(kname[dom], wname)
     achieved = alg[dom] / times[dom] / 1e9
+    # The momentum step (SGD with momentum) on the same workload, timed after
+    # the headline step and outside `value`: W (the update's output; the
+    # headline step's byte counts are taken above, before these calls rewrite
+    # the offsets) and M compressed and resident, a dense BF16 gradient; W' and M' are written in
+    # place on the fixed sides while the overflow regions ping-pong between
+    # two sets, so every call reads a consistent (W, M) pair.  Each call gets a
+    # fresh gradient g ~ N(0, s^2 (1 - mu^2)) with s the spread of M, drawn
+    # untimed: then M' = mu*M + g keeps M's distribution (the stationary spread
+    # of heavy-ball momentum under independent gradients), as in a run whose
+    # momentum has settled.
+    next_ops = None
+    if not args.no_next:
+        mu, reps = 0.9, 6
+        g_sigma = mspec.args["sigma"] * math.sqrt(1.0 - mu * mu)
+        scratch2 = torch.empty(L.lct_sizes(n, lay, ovf_cap).scratch, dtype=torch.uint8, device=dev)
+        tm.scratch = scratch2
+        sets = [(tw2, tm)]
+        bw = L.alloc_tensor(n, lay, ovf_cap, dev, scratch)
+        bm = L.alloc_tensor(n, lay, ovf_cap, dev, scratch2)
+        bw.sf, bw.pay, bw.cnt, bw.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+        bm.sf, bm.pay, bm.cnt, bm.obase = tm.sf, tm.pay, tm.cnt, tm.obase
+        sets.append((bw, bm))
+        torch.cuda.empty_cache()
+        alg_mom, mom_status = [], 0
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps + 1):
+            (wi, mi), (wo, mo) = sets[i % 2], sets[(i + 1) % 2]
+            spill_in = wi.spilled() + mi.spilled()
+            g_dense = synth.draw_device(synth.TensorSpec("g.flat", (n,), wspec.seed + 100 + i, "normal",
+                                                         {"sigma": g_sigma}), dev)
+            torch.cuda.synchronize()
+            if i:
+                mev[i - 1][0].record(stream)
+            L.lct_momentum_step(cbw, wi, cbm, mi, g_dense, mu, eta, wo, mo)
+            if i:
+                mev[i - 1][1].record(stream)
+            torch.cuda.synchronize()
+            mom_status = max(mom_status, wo.status_word(), mo.status_word())
+            del g_dense
+            if i:
+                alg_mom.append(4 * tw.sizes.fixed + 2 * n + spill_in + wo.spilled() + mo.spilled())
+        t_mom = float(np.mean([e[0].elapsed_time(e[1]) for e in mev])) / 1e3
+        bytes_mom = float(np.mean(alg_mom))
+        gbs = bytes_mom / t_mom / 1e9
+        mtraffic = load_traffic("k_momentum", wname)
+        next_ops = {"momentum": {"ms": round(t_mom * 1e3, 4), "alg_bytes": int(bytes_mom),
+                                 "alg_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "elems_per_s": float("%.4g" % (n / t_mom)), "mu": mu,
+                                 "g_sigma": float("%.4g" % g_sigma),
+                                 "status": mom_status,
+                                 "traffic": None if mtraffic is None else mtraffic.get("bytes_per_launch")}}
+        del sets, bw, bm
+
     out = {
         "metric": METRIC,
         "value": float("%.5g" % (n / t_step)),
@@ -245,6 +301,7 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
         "cpu_baseline": cpu,
+        "next_ops": next_ops,
     }
     print(json.dumps(out), flush=True)
 
