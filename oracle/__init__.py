@@ -40,7 +40,7 @@ def build(force: bool = True) -> str:
 
 class _Codebook(C.Structure):
     _fields_ = [("len", C.c_uint8 * 256), ("esc_len", C.c_uint8),
-                ("shift", C.c_int32), ("code", C.c_uint32 * 257)]
+                ("shift", C.c_int32), ("code", C.c_uint32 * 257), ("len_base", C.c_uint8 * 256)]
 
 
 _lib = None
@@ -86,13 +86,14 @@ def lib():
         L.lcto_sgd_elem.restype = C.c_uint16
         L.lcto_sgd_elem.argtypes = [C.c_uint16, C.c_uint16, C.c_float]
         L.lcto_sgd.argtypes = ([P, P, P, P, P, P] + [P, P, P, P, P, P] +
-                               [C.c_float, u64, u32, u32, P, P, P, P, P, u64])
+                               [C.c_float, P, u64, u32, u32, P, P, P, P, P, u64])
         L.lcto_momentum_elem.restype = None
         L.lcto_momentum_elem.argtypes = [C.c_uint16, C.c_uint16, C.c_uint16, C.c_float, C.c_float,
                                          C.POINTER(C.c_uint16), C.POINTER(C.c_uint16)]
         L.lcto_momentum.argtypes = ([P, P, P, P, P, P] + [P, P, P, P, P, P] +
-                                    [P, C.c_float, C.c_float, u64, u32, u32] +
+                                    [P, C.c_float, C.c_float, P, P, u64, u32, u32] +
                                     [P, P, P, P, P, u64] + [P, P, P, P, P, u64])
+        L.lcto_reshift.argtypes = [P, P, P, P, P, P, u64, u32, u32, P]
         _lib = L
     return _lib
 
@@ -106,11 +107,13 @@ def _p(a: np.ndarray):
 
 @dataclass
 class Codebook:
-    """Final code: len[e] (0 = escaped), esc_len, shift, canonical codes."""
+    """Final code: len[e] (0 = escaped), esc_len, shift, canonical codes, and
+    the base code len_base the shift was applied to."""
     len: np.ndarray      # uint8[256]
     esc_len: int
     shift: int
     code: np.ndarray     # uint32[257], [256] = ESC
+    len_base: np.ndarray  # uint8[256]
 
     def _c(self) -> _Codebook:
         cb = _Codebook()
@@ -118,12 +121,14 @@ class Codebook:
         cb.esc_len = int(self.esc_len)
         cb.shift = int(self.shift)
         C.memmove(cb.code, self.code.astype(np.uint32).tobytes(), 257 * 4)
+        C.memmove(cb.len_base, self.len_base.astype(np.uint8).tobytes(), 256)
         return cb
 
     @staticmethod
     def _from_c(cb: _Codebook) -> "Codebook":
         return Codebook(np.frombuffer(bytes(cb.len), np.uint8).copy(), int(cb.esc_len),
-                        int(cb.shift), np.frombuffer(bytes(cb.code), np.uint32).copy())
+                        int(cb.shift), np.frombuffer(bytes(cb.code), np.uint32).copy(),
+                        np.frombuffer(bytes(cb.len_base), np.uint8).copy())
 
     def cost(self, e: int) -> int:
         return int(self.len[e]) if self.len[e] else self.esc_len + 8
@@ -351,15 +356,20 @@ def sgd_dense(w: np.ndarray, m: np.ndarray, eta: float) -> np.ndarray:
                        np.uint16, count=w.size)
 
 
+def _cb_ref(cb: Codebook | None):
+    return None if cb is None else C.byref(cb._c())
+
+
 def sgd(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, eta: float,
-        ovf_cap: int | None = None) -> Compressed:
+        ovf_cap: int | None = None, cw_out: Codebook | None = None) -> Compressed:
+    """Naive round trip of one SGD step; W' is encoded with cw_out (cw if None)."""
     assert (w.n, w.block_elems, w.cap_words) == (m.n, m.block_elems, m.cap_words)
     ovf_cap = w.n if ovf_cap is None else ovf_cap
     o = _alloc(w.n, w.block_elems, w.cap_words, ovf_cap)
     a, b = cw._c(), cm._c()
     rc = lib().lcto_sgd(C.byref(a), _p(w.sf), _p(w.pay), _p(w.cnt), _p(w.obase), _p(w.ovf),
                         C.byref(b), _p(m.sf), _p(m.pay), _p(m.cnt), _p(m.obase), _p(m.ovf),
-                        eta, w.n, w.block_elems, w.cap_words, _p(o.sf), _p(o.pay), _p(o.cnt),
+                        eta, _cb_ref(cw_out), w.n, w.block_elems, w.cap_words, _p(o.sf), _p(o.pay), _p(o.cnt),
                         _p(o.obase), _p(o.ovf), ovf_cap)
     if rc < 0:
         raise ValueError("sgd: error %d" % rc)
@@ -389,9 +399,10 @@ def momentum_dense(w: np.ndarray, m: np.ndarray, g: np.ndarray, mu: float, eta: 
 
 
 def momentum(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, g: np.ndarray,
-             mu: float, eta: float, ovf_cap: int | None = None):
+             mu: float, eta: float, ovf_cap: int | None = None,
+             cw_out: Codebook | None = None, cm_out: Codebook | None = None):
     """Naive round trip of one momentum step on compressed W and M and dense g:
-    returns (W', M') encoded with cw and cm."""
+    returns (W', M') encoded with cw_out and cm_out (cw and cm if None)."""
     assert (w.n, w.block_elems, w.cap_words) == (m.n, m.block_elems, m.cap_words)
     g = np.ascontiguousarray(g, np.uint16).reshape(-1)
     assert g.size == w.n
@@ -401,7 +412,7 @@ def momentum(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, g: np.nda
     a, b = cw._c(), cm._c()
     rc = lib().lcto_momentum(C.byref(a), _p(w.sf), _p(w.pay), _p(w.cnt), _p(w.obase), _p(w.ovf),
                              C.byref(b), _p(m.sf), _p(m.pay), _p(m.cnt), _p(m.obase), _p(m.ovf),
-                             _p(g), mu, eta, w.n, w.block_elems, w.cap_words,
+                             _p(g), mu, eta, _cb_ref(cw_out), _cb_ref(cm_out), w.n, w.block_elems, w.cap_words,
                              _p(ow.sf), _p(ow.pay), _p(ow.cnt), _p(ow.obase), _p(ow.ovf), ovf_cap,
                              _p(om.sf), _p(om.pay), _p(om.cnt), _p(om.obase), _p(om.ovf), ovf_cap)
     if rc < 0:
@@ -409,3 +420,16 @@ def momentum(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, g: np.nda
     ow.status = int(ow.obase[-1] > ovf_cap)
     om.status = int(om.obase[-1] > ovf_cap)
     return ow, om
+
+
+# ---------------------------------------------------------------- shift re-estimation
+
+def reshift(cb: Codebook, t: Compressed) -> Codebook:
+    """cb's base code with the shift re-estimated from the compressed tensor t
+    (decoded with cb; sample at sample_positions(t.n))."""
+    out = _Codebook()
+    rc = lib().lcto_reshift(C.byref(cb._c()), _p(t.sf), _p(t.pay), _p(t.cnt), _p(t.obase),
+                            _p(t.ovf), t.n, t.block_elems, t.cap_words, C.byref(out))
+    if rc != OK:
+        raise ValueError("reshift: error %d" % rc)
+    return Codebook._from_c(out)

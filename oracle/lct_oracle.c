@@ -349,6 +349,7 @@ void lcto_codebook_from_base(const uint8_t len_base[256], uint8_t esc_len, int s
         cb->len[e] = l[e];
     }
     l[256] = esc_len;
+    memcpy(cb->len_base, len_base, 256);
     cb->esc_len = esc_len;
     cb->shift = shift;
     lcto_canonical(l, cb->code);
@@ -558,6 +559,33 @@ int lcto_decode(const lcto_codebook *cb, const uint8_t *sf, const uint32_t *pay,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Shift re-estimation ([LCT-abs]: adaptation to magnitude shifts;           */
+/* [EXP-split]: the shift is sampled from up to 4096 elements; [EXP-limits]: */
+/* a distribution that no longer fits the tensor raises storage).  The       */
+/* tensor is decoded in full, the sample is taken at the build's positions,  */
+/* and only the shift changes: the base code is kept as it is.               */
+/* ------------------------------------------------------------------------ */
+int lcto_reshift(const lcto_codebook *cb, const uint8_t *sf, const uint32_t *pay,
+                 const uint16_t *cnt, const uint64_t *obase, const uint8_t *ovf,
+                 uint64_t n, uint32_t block_elems, uint32_t cap_words, lcto_codebook *out)
+{
+    if (!layout_ok(block_elems, cap_words)) return LCTO_EINVAL;
+    uint16_t *y = (uint16_t *)malloc(sizeof(uint16_t) * (n ? n : 1));
+    size_t m = n < 4096 ? (size_t)n : 4096;
+    uint8_t *smp = (uint8_t *)malloc(m ? m : 1);
+    int rc = (y && smp) ? LCTO_OK : LCTO_EINVAL;
+    if (rc == LCTO_OK) rc = lcto_decode(cb, sf, pay, cnt, obase, ovf, n, block_elems, cap_words, y);
+    if (rc == LCTO_OK) {
+        for (size_t i = 0; i < m; i++) smp[i] = lcto_exponent(y[(uint64_t)i * n / m]);
+        int shift = lcto_best_shift(cb->len_base, cb->esc_len, smp, m);
+        lcto_codebook_from_base(cb->len_base, cb->esc_len, shift, out);
+    }
+    free(y);
+    free(smp);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* SGD update ([EXP-train]): W_{t+1} = W_t - eta * M_t, read as one fp32     */
 /* fused multiply-add fmaf(-eta, m, w), rounded to nearest-even BF16.  A NaN */
 /* result is written as the canonical quiet NaN 0x7FC0.                      */
@@ -589,11 +617,12 @@ int lcto_sgd(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay
              const uint16_t *w_cnt, const uint64_t *w_obase, const uint8_t *w_ovf,
              const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
              const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
-             float eta, uint64_t n, uint32_t block_elems, uint32_t cap_words,
-             uint8_t *o_sf, uint32_t *o_pay, uint16_t *o_cnt, uint64_t *o_obase,
+             float eta, const lcto_codebook *cw_out, uint64_t n, uint32_t block_elems,
+             uint32_t cap_words, uint8_t *o_sf, uint32_t *o_pay, uint16_t *o_cnt, uint64_t *o_obase,
              uint8_t *o_ovf, uint64_t ovf_cap)
 {
     if (!layout_ok(block_elems, cap_words)) return LCTO_EINVAL;
+    if (!cw_out) cw_out = cw;
     uint64_t nblk = (n + block_elems - 1) / block_elems;
     uint16_t *wd = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
     uint16_t *md = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
@@ -612,7 +641,7 @@ int lcto_sgd(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay
         if (rc != LCTO_OK) break;
         for (uint32_t r = 0; r < nb; r++) wd[r] = lcto_sgd_elem(wd[r], md[r], eta);
         uint32_t ns = 0;
-        lcto_encode_block(cw, wd, nb, cap_words, o_sf + r0, o_pay + po, o_cnt + b * NSTREAM, spill, &ns);
+        lcto_encode_block(cw_out, wd, nb, cap_words, o_sf + r0, o_pay + po, o_cnt + b * NSTREAM, spill, &ns);
         for (uint32_t i = 0; i < ns; i++)
             if (o_obase[b] + i < ovf_cap) o_ovf[o_obase[b] + i] = spill[i];
         o_obase[b + 1] = o_obase[b] + ns;
@@ -657,6 +686,7 @@ int lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *
                   const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
                   const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
                   const uint16_t *g, float mu, float eta,
+                  const lcto_codebook *cw_out, const lcto_codebook *cm_out,
                   uint64_t n, uint32_t block_elems, uint32_t cap_words,
                   uint8_t *ow_sf, uint32_t *ow_pay, uint16_t *ow_cnt, uint64_t *ow_obase,
                   uint8_t *ow_ovf, uint64_t ow_ovf_cap,
@@ -664,6 +694,8 @@ int lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *
                   uint8_t *om_ovf, uint64_t om_ovf_cap)
 {
     if (!layout_ok(block_elems, cap_words)) return LCTO_EINVAL;
+    if (!cw_out) cw_out = cw;
+    if (!cm_out) cm_out = cm;
     uint64_t nblk = (n + block_elems - 1) / block_elems;
     uint16_t *wd = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
     uint16_t *md = (uint16_t *)malloc(sizeof(uint16_t) * block_elems);
@@ -684,9 +716,9 @@ int lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *
                                nb, cap_words, md);
         if (rc != LCTO_OK) break;
         for (uint32_t r = 0; r < nb; r++) lcto_momentum_elem(wd[r], md[r], g[r0 + r], mu, eta, &wd[r], &md[r]);
-        encode_block_out(cw, wd, nb, cap_words, b, r0, po, spill, ow_sf, ow_pay, ow_cnt, ow_obase, ow_ovf,
+        encode_block_out(cw_out, wd, nb, cap_words, b, r0, po, spill, ow_sf, ow_pay, ow_cnt, ow_obase, ow_ovf,
                          ow_ovf_cap);
-        encode_block_out(cm, md, nb, cap_words, b, r0, po, spill, om_sf, om_pay, om_cnt, om_obase, om_ovf,
+        encode_block_out(cm_out, md, nb, cap_words, b, r0, po, spill, om_sf, om_pay, om_cnt, om_obase, om_ovf,
                          om_ovf_cap);
     }
     free(wd);

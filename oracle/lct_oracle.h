@@ -14,6 +14,9 @@
  *   [EXP-streams] same page, paragraph on blocks of 65,536 / 32,768 and 256 streams.
  *   [EXP-train]   same page, paragraph on training traffic and the fused SGD update.
  *   [EXP-ideal]   same page, paragraph "Here is the idealized arithmetic ...".
+ *   [EXP-limits]  same page, paragraph on the longer-context claim and the limits
+ *                 (a distribution that does not fit the tensor raises storage).
+ *   [EXP-jargon]  same page, jargon entry "Optimizer state".
  *
  * Conventions fixed where the pages are silent are listed, with the reading
  * taken, in the design notes; every function below names the one it uses.
@@ -50,6 +53,7 @@ typedef struct {
     uint8_t  esc_len;
     int32_t  shift;
     uint32_t code[257];     /* canonical code values, MSB-first; [256] = ESC */
+    uint8_t  len_base[256]; /* the base code the shift was applied to */
 } lcto_codebook;
 
 /* ---- model and codebook construction ([EXP-split]) ---------------------- */
@@ -94,6 +98,17 @@ int  lcto_codebook_build(int family, double scale, double shape,
 void lcto_codebook_from_base(const uint8_t len_base[256], uint8_t esc_len, int shift,
                              lcto_codebook *cb);
 
+/* ---- shift re-estimation ([LCT-abs], [EXP-split], [EXP-limits]) ----------- */
+
+/* New shift for a compressed tensor, keeping the base code: decode the tensor
+ * (codebook cb), take its sample x[floor(i*n/m)], m = min(n, 4096), pick the
+ * shift that minimises the sample's coded bits under cb's base code (same
+ * search and tie rule as the build), and apply it: out has cb's base code and
+ * escape length with the new shift.  No Huffman code is rebuilt. */
+int  lcto_reshift(const lcto_codebook *cb, const uint8_t *sf, const uint32_t *pay,
+                  const uint16_t *cnt, const uint64_t *obase, const uint8_t *ovf,
+                  uint64_t n, uint32_t block_elems, uint32_t cap_words, lcto_codebook *out);
+
 /* ---- the format ([EXP-split], [EXP-streams]) ----------------------------- */
 
 /* Split / join of one BF16 bit pattern. */
@@ -132,13 +147,13 @@ uint16_t lcto_rne_bf16(float r);
 uint16_t lcto_sgd_elem(uint16_t w, uint16_t m, float eta);
 
 /* Naive round trip of one SGD step: decode W (codebook cw) and M (cm) fully,
- * update densely, re-encode W' with cw.  Input and output compressed tensors
- * share n, block_elems and cap_words. */
+ * update densely, re-encode W' with cw_out (cw when NULL).  Input and output
+ * compressed tensors share n, block_elems and cap_words. */
 int  lcto_sgd(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay,
               const uint16_t *w_cnt, const uint64_t *w_obase, const uint8_t *w_ovf,
               const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
               const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
-              float eta, uint64_t n, uint32_t block_elems, uint32_t cap_words,
+              float eta, const lcto_codebook *cw_out, uint64_t n, uint32_t block_elems, uint32_t cap_words,
               uint8_t *o_sf, uint32_t *o_pay, uint16_t *o_cnt, uint64_t *o_obase,
               uint8_t *o_ovf, uint64_t ovf_cap);
 
@@ -150,14 +165,16 @@ void lcto_momentum_elem(uint16_t w, uint16_t m, uint16_t g, float mu, float eta,
                         uint16_t *w_out, uint16_t *m_out);
 
 /* Naive round trip of one momentum step: decode W (codebook cw) and M (cm)
- * fully, update densely with the dense gradient g, re-encode W' with cw and
- * M' with cm.  Inputs and outputs share n, block_elems and cap_words.
+ * fully, update densely with the dense gradient g, re-encode W' with cw_out
+ * and M' with cm_out (cw and cm when NULL).  Inputs and outputs share n,
+ * block_elems and cap_words.
  * Returns LCTO_OVF_FULL if either output's spill exceeds its ovf_cap. */
 int  lcto_momentum(const lcto_codebook *cw, const uint8_t *w_sf, const uint32_t *w_pay,
                    const uint16_t *w_cnt, const uint64_t *w_obase, const uint8_t *w_ovf,
                    const lcto_codebook *cm, const uint8_t *m_sf, const uint32_t *m_pay,
                    const uint16_t *m_cnt, const uint64_t *m_obase, const uint8_t *m_ovf,
                    const uint16_t *g, float mu, float eta,
+                   const lcto_codebook *cw_out, const lcto_codebook *cm_out,
                    uint64_t n, uint32_t block_elems, uint32_t cap_words,
                    uint8_t *ow_sf, uint32_t *ow_pay, uint16_t *ow_cnt, uint64_t *ow_obase,
                    uint8_t *ow_ovf, uint64_t ow_ovf_cap,
