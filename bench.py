@@ -272,7 +272,18 @@ def main():
                                  "g_sigma": float("%.4g" % g_sigma),
                                  "status": mom_status,
                                  "traffic": None if mtraffic is None else mtraffic.get("bytes_per_launch")}}
-        del sets, bw, bm
+        # shift re-estimation on the momentum step's last W': 4096 elements
+        # decoded from the compressed form on the device, the shift search and
+        # the new tables on the host (a synchronising call, timed on the host)
+        L.lct_codebook_reshift(cbw, wo)
+        tr = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            new = L.lct_codebook_reshift(cbw, wo)
+            tr.append(time.perf_counter() - t0)
+        next_ops["reshift"] = {"ms": round(1e3 * float(np.median(tr)), 4), "sample": 4096,
+                               "shift_before": int(cbw.shift), "shift_after": int(new.shift)}
+        del sets, bw, bm, wi, mi, wo, mo
 
     out = {
         "metric": METRIC,

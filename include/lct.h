@@ -13,8 +13,11 @@
  *    (learnaivisually.com): the paragraph on bits (byte split, 8-bit cap,
  *    escape, precomputed codebook and sampled shift), the paragraph on blocks
  *    and streams (65,536 / 32,768 elements, 256 streams, fixed capacity,
- *    overflow and its marker), and the paragraph on training traffic (the
- *    fused SGD update W_{t+1} = W_t - eta * M_t).
+ *    overflow and its marker), the paragraph on training traffic (the
+ *    fused SGD update W_{t+1} = W_t - eta * M_t), the jargon entry
+ *    "Optimizer state" (the momentum buffer is stored compressed too) and the
+ *    paragraph on the limits (a distribution that does not fit the tensor
+ *    raises storage).
  *
  * Conventions (common to every call):
  *   - Every function returns lct_status (0 = LCT_OK) and never throws.
@@ -22,18 +25,20 @@
  *     pointers on the current HIP device; every other pointer is host memory.
  *   - The caller allocates and frees every device buffer, sized by lct_sizes().
  *     The library allocates no device memory of its own, except one 8 KiB
- *     static array per device used by lct_codebook_build() for its sample.
+ *     static array per device used by lct_codebook_build() and
+ *     lct_codebook_reshift() for their sample.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     lct_encode, lct_decode, lct_sgd_step and lct_momentum_step only enqueue
- *     work on it and
- *     return at once; lct_codebook_build synchronises it.
+ *     lct_encode, lct_decode and the update calls (lct_sgd_step*,
+ *     lct_momentum_step*) only enqueue work on it and return at once;
+ *     lct_codebook_build, lct_codebook_reshift and lct_codebook_adapt
+ *     synchronise it.
  *   - Errors found on the host (null pointer, bad size, misalignment, illegal
  *     aliasing, wrong device) are returned before anything is enqueued.
  *     The only data-dependent failure is a too-small overflow region: it is
  *     reported through the device status word (LCT_ST_* bits), never by a
  *     fault.  n == 0 is a no-op that returns LCT_OK.
- *   - Thread-safe: no global state beyond the codebook-build sample array,
- *     which is guarded by a lock.
+ *   - Thread-safe: no global state beyond the sample array, which is guarded
+ *     by a lock.
  */
 #ifndef LCT_H
 #define LCT_H
@@ -55,7 +60,7 @@ typedef enum {
 } lct_status;
 
 /* Device status word bits, OR-ed in by the kernels (the word is cleared at the
- * start of every lct_encode / lct_sgd_step / lct_momentum_step). */
+ * start of every lct_encode and every update call that writes the tensor). */
 #define LCT_ST_OVF_FULL 0x1u   /* total spill > ovf_cap: the overflow region is incomplete;
                                   obase[nblk] still holds the size needed */
 #define LCT_ST_LOOKBACK 0x2u   /* overflow-offset scan gave up waiting (never expected) */
@@ -88,8 +93,10 @@ typedef struct {
  * bits: the escape code, then the field's 8 bits, least significant first).
  * code[] holds canonical code values (ordered by length, then field; the
  * escape symbol has id 256); codes enter a stream most significant bit first.
- * The remaining members are lookup tables derived from len/esc_len by the
- * library: treat them as opaque. */
+ * len_base[] is the base code the shift was applied to: len[e] =
+ * len_base[e - shift] where 0 <= e - shift <= 255, else 0; shift re-estimation
+ * keeps it.  The remaining members are lookup tables derived from
+ * len/esc_len by the library: treat them as opaque. */
 typedef struct {
     uint8_t  len[256];
     uint8_t  esc_len;
@@ -101,6 +108,7 @@ typedef struct {
     uint32_t enc_bits[256];   /* stream bits of each field, LSB-first (code reversed, literal) */
     uint8_t  enc_len[256];    /* bits each field costs */
     uint16_t dec[256];        /* 8-bit peek -> field | bits << 8 | escape << 13 | invalid << 14 */
+    uint8_t  len_base[256];   /* base code lengths before the shift */
 } lct_codebook;
 
 /* A compressed tensor: every pointer is a caller-owned device buffer.
@@ -171,6 +179,38 @@ lct_status lct_codebook_build(const lct_model *model, const uint16_t *d_x, uint6
 lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
                                      lct_codebook *out);
 
+/* Shift re-estimation (abstract: adaptation to magnitude shifts; explainer,
+ * paragraph on bits: a small shift sampled from up to 4096 elements follows
+ * the tensor's scale; paragraph on the limits: a distribution that no longer
+ * fits the tensor raises storage).  Takes the current values of the
+ * compressed tensor *t (decoded with *cb) at positions floor(i * n / m),
+ * m = min(n, 4096), as lct_codebook_build does, and picks the shift that
+ * minimises their coded bits under cb's base code (same search and ties).
+ * *out gets cb's base code, escape length and model with the new shift; no
+ * Huffman code is rebuilt.  n == 0 gives shift 0.  The tensor keeps its
+ * encoding: it moves to *out when it is next written (lct_encode, or an
+ * update call with *out as its output codebook).  Synchronises `stream`.
+ * Errors: LCT_EINVAL, LCT_EALIGN, LCT_EARCH, LCT_EHIP. */
+lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, void *stream,
+                                lct_codebook *out);
+
+/* The shift sample of a compressed tensor, as lct_codebook_reshift takes it:
+ * out[i] = element floor(i * n / m) of *t (decoded with *cb), i < m =
+ * min(n, 4096), as BF16 bit patterns in host memory (out holds 4096 values);
+ * *m_out (may be NULL) gets m.  Synchronises `stream`.  Errors: as
+ * lct_codebook_reshift. */
+lct_status lct_tensor_sample(const lct_codebook *cb, const lct_tensor *t, void *stream,
+                             uint16_t *out, uint32_t *m_out);
+
+/* Re-estimation when the spill has grown: reads t's spilled total
+ * (obase[nblk]); if it exceeds max_spill_per_elem * n bytes, *out is
+ * lct_codebook_reshift(cb, t), else a copy of *cb.  *changed (may be NULL)
+ * is set to 1 when out's shift differs from cb's, else 0.  Synchronises
+ * `stream`.  Errors: as lct_codebook_reshift; LCT_EINVAL for a negative or
+ * NaN limit. */
+lct_status lct_codebook_adapt(const lct_codebook *cb, const lct_tensor *t, double max_spill_per_elem,
+                              void *stream, lct_codebook *out, int32_t *changed);
+
 /* Encode (explainer, paragraphs on bits and on blocks and streams).
  * d_x: device BF16 bit patterns, out->n elements, 16-byte aligned.  Writes
  * every buffer of *out (all of sf, pay, cnt, obase, status; ovf below ovf_cap).
@@ -203,6 +243,13 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in,
                         const lct_codebook *cm, const lct_tensor *m,
                         float eta, const lct_tensor *w_out, void *stream);
 
+/* lct_sgd_step with W' encoded with cw_out instead of cw (W is still decoded
+ * with cw): the step that moves W onto a codebook from lct_codebook_reshift.
+ * Same arguments, rules and errors otherwise; cw_out == cw is lct_sgd_step. */
+lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in,
+                               const lct_codebook *cm, const lct_tensor *m, float eta,
+                               const lct_codebook *cw_out, const lct_tensor *w_out, void *stream);
+
 /* Momentum step (explainer, jargon entry "Optimizer state": the momentum
  * buffer of SGD with momentum is stored compressed like the weights; paragraph
  * on training traffic: decode, update, re-encode in one pass).  Element by
@@ -220,6 +267,15 @@ lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in,
                              const lct_codebook *cm, const lct_tensor *m_in,
                              const uint16_t *d_g, float mu, float eta,
                              const lct_tensor *w_out, const lct_tensor *m_out, void *stream);
+
+/* lct_momentum_step with W' encoded with cw_out and M' with cm_out (W and M
+ * are still decoded with cw and cm).  Same arguments, rules and errors
+ * otherwise. */
+lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_in,
+                                    const lct_codebook *cm, const lct_tensor *m_in,
+                                    const uint16_t *d_g, float mu, float eta,
+                                    const lct_codebook *cw_out, const lct_codebook *cm_out,
+                                    const lct_tensor *w_out, const lct_tensor *m_out, void *stream);
 
 /* Message for a status code (static string). */
 const char *lct_strerror(lct_status st);

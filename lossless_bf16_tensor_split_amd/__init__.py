@@ -10,10 +10,15 @@ Functions keep the C names:
     lct_sizes(n, layout, ovf_cap) -> Sizes
     lct_codebook_build(model, x) -> Codebook
     lct_codebook_from_lengths(len_base, esc_len, shift) -> Codebook
+    lct_tensor_sample(cb, t) -> numpy uint16 array (the shift sample)
+    lct_codebook_reshift(cb, t) -> Codebook
+    lct_codebook_adapt(cb, t, max_spill_per_elem) -> (Codebook, changed)
     lct_encode(cb, x, out)            (out: LctTensor from alloc_tensor)
     lct_decode(cb, t, y)
     lct_sgd_step(cw, w_in, cm, m, eta, w_out)
+    lct_sgd_step_recode(cw, w_in, cm, m, eta, cw_out, w_out)
     lct_momentum_step(cw, w_in, cm, m_in, g, mu, eta, w_out, m_out)
+    lct_momentum_step_recode(cw, w_in, cm, m_in, g, mu, eta, cw_out, cm_out, w_out, m_out)
 plus ``alloc_tensor`` and the convenience wrappers ``encode`` / ``decode`` /
 ``sgd_step`` / ``momentum_step`` that allocate their outputs.
 """
@@ -33,8 +38,9 @@ ST_OVF_FULL, ST_LOOKBACK = 0x1, 0x2
 OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_from_lengths",
-            "lct_encode", "lct_decode", "lct_sgd_step", "lct_momentum_step", "lct_strerror",
-            "lct_last_hip_error"]
+            "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_adapt", "lct_encode", "lct_decode",
+            "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
+            "lct_strerror", "lct_last_hip_error"]
 
 
 class Model(C.Structure):
@@ -49,7 +55,8 @@ class Codebook(C.Structure):
     _fields_ = [("len", C.c_uint8 * 256), ("esc_len", C.c_uint8), ("max_len", C.c_uint8),
                 ("shift", C.c_int16), ("kept", C.c_uint32), ("model", Model),
                 ("code", C.c_uint32 * 257), ("enc_bits", C.c_uint32 * 256),
-                ("enc_len", C.c_uint8 * 256), ("dec", C.c_uint16 * 256)]
+                ("enc_len", C.c_uint8 * 256), ("dec", C.c_uint16 * 256),
+                ("len_base", C.c_uint8 * 256)]
 
 
 class _Tensor(C.Structure):
@@ -78,6 +85,12 @@ def _load():
     L.lct_sizes.argtypes = [u64, C.POINTER(Layout), u64, C.POINTER(Sizes)]
     L.lct_codebook_build.argtypes = [C.POINTER(Model), P, u64, P, C.POINTER(Codebook)]
     L.lct_codebook_from_lengths.argtypes = [P, C.c_uint8, i32, C.POINTER(Codebook)]
+    CB, T = C.POINTER(Codebook), C.POINTER(_Tensor)
+    L.lct_tensor_sample.argtypes = [CB, T, P, P, C.POINTER(C.c_uint32)]
+    L.lct_codebook_reshift.argtypes = [CB, T, P, CB]
+    L.lct_codebook_adapt.argtypes = [CB, T, C.c_double, P, CB, C.POINTER(i32)]
+    L.lct_sgd_step_recode.argtypes = [CB, T, CB, T, C.c_float, CB, T, P]
+    L.lct_momentum_step_recode.argtypes = [CB, T, CB, T, P, C.c_float, C.c_float, CB, CB, T, T, P]
     L.lct_encode.argtypes = [C.POINTER(Codebook), P, C.POINTER(_Tensor), P]
     L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
     L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
@@ -152,6 +165,39 @@ def lct_codebook_from_lengths(len_base, esc_len: int, shift: int = 0) -> Codeboo
     _check(lib.lct_codebook_from_lengths(arr, esc_len, shift, C.byref(out)),
            "lct_codebook_from_lengths")
     return out
+
+
+def lct_tensor_sample(cb: Codebook, t: "LctTensor", stream=None):
+    """BF16 bit patterns (numpy uint16) of the shift sample of t."""
+    import numpy as np
+    out = np.zeros(4096, np.uint16)
+    m = C.c_uint32(0)
+    ct = t.c()
+    st = _stream(stream) if t.n else None
+    _check(lib.lct_tensor_sample(C.byref(cb), C.byref(ct), st, out.ctypes.data_as(C.c_void_p),
+                                 C.byref(m)), "lct_tensor_sample")
+    return out[:m.value].copy()
+
+
+def lct_codebook_reshift(cb: Codebook, t: "LctTensor", stream=None) -> Codebook:
+    """cb's base code with the shift re-estimated from the compressed tensor t."""
+    out = Codebook()
+    ct = t.c()
+    st = _stream(stream) if t.n else None
+    _check(lib.lct_codebook_reshift(C.byref(cb), C.byref(ct), st, C.byref(out)),
+           "lct_codebook_reshift")
+    return out
+
+
+def lct_codebook_adapt(cb: Codebook, t: "LctTensor", max_spill_per_elem: float, stream=None):
+    """(codebook, changed): re-estimated when t spills more than the limit."""
+    out = Codebook()
+    changed = C.c_int32(0)
+    ct = t.c()
+    st = _stream(stream) if t.n else None
+    _check(lib.lct_codebook_adapt(C.byref(cb), C.byref(ct), max_spill_per_elem, st, C.byref(out),
+                                  C.byref(changed)), "lct_codebook_adapt")
+    return out, bool(changed.value)
 
 
 # ------------------------------------------------------------------ compressed tensors
@@ -229,6 +275,24 @@ def lct_sgd_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta:
     a, b, o = w_in.c(), m.c(), w_out.c()
     _check(lib.lct_sgd_step(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta, C.byref(o),
                             _stream(stream)), "lct_sgd_step")
+
+
+def lct_sgd_step_recode(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta: float,
+                        cw_out: Codebook, w_out: LctTensor, stream=None) -> None:
+    a, b, o = w_in.c(), m.c(), w_out.c()
+    _check(lib.lct_sgd_step_recode(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta,
+                                   C.byref(cw_out), C.byref(o), _stream(stream)),
+           "lct_sgd_step_recode")
+
+
+def lct_momentum_step_recode(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: LctTensor,
+                             g: torch.Tensor, mu: float, eta: float, cw_out: Codebook,
+                             cm_out: Codebook, w_out: LctTensor, m_out: LctTensor,
+                             stream=None) -> None:
+    a, b, ow, om = w_in.c(), m_in.c(), w_out.c(), m_out.c()
+    _check(lib.lct_momentum_step_recode(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), _ptr(g),
+                                        mu, eta, C.byref(cw_out), C.byref(cm_out), C.byref(ow),
+                                        C.byref(om), _stream(stream)), "lct_momentum_step_recode")
 
 
 def lct_momentum_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: LctTensor, g: torch.Tensor,

@@ -153,6 +153,75 @@ lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_le
     return codebook_from_lengths(len_base, esc_len, shift, out);
 }
 
+lct_status lct_tensor_sample(const lct_codebook *cb, const lct_tensor *t, void *stream,
+                             uint16_t *sample, uint32_t *m_out) {
+    if (!cb || !t || !sample) return LCT_EINVAL;
+    const uint32_t m = (uint32_t)std::min<uint64_t>(t->n, 4096);
+    if (m > 0) {
+        lct_status st = check_tensor(t, false);
+        if (st != LCT_OK) return st;
+        if (t->n >= (1ull << 52)) return LCT_EINVAL;   // i * n stays within 64 bits
+        st = check_arch();
+        if (st != LCT_OK) return st;
+        SampleParams p;
+        memset(&p, 0, sizeof p);
+        p.sf = t->sf;
+        p.pay = t->pay;
+        p.cnt = t->cnt;
+        p.obase = t->obase;
+        p.ovf = t->ovf;
+        p.ovf_cap = t->ovf_cap;
+        p.n = t->n;
+        p.block_elems = t->layout.block_elems;
+        p.cap_words = t->layout.cap_words;
+        p.m = m;
+        fill_dec(*cb, &p.dec);
+        std::lock_guard<std::mutex> lock(g_sample_mu);
+        const int e = launch_sample(p, stream, sample);
+        if (e != hipSuccess) return hip_fail(e, "compressed sample");
+    }
+    if (m_out) *m_out = m;
+    return LCT_OK;
+}
+
+lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, void *stream,
+                                lct_codebook *out) {
+    if (!cb || !t || !out) return LCT_EINVAL;
+    uint16_t sample[4096];
+    uint32_t m = 0;
+    const lct_status st = lct_tensor_sample(cb, t, stream, sample, &m);
+    if (st != LCT_OK) return st;
+    return reshift_codebook(*cb, sample, m, out);
+}
+
+lct_status lct_codebook_adapt(const lct_codebook *cb, const lct_tensor *t, double max_spill_per_elem,
+                              void *stream, lct_codebook *out, int32_t *changed) {
+    if (!cb || !t || !out || !(max_spill_per_elem >= 0)) return LCT_EINVAL;
+    const lct_codebook in = *cb;   // out may be cb
+    bool reshift = false;
+    if (t->n > 0) {
+        lct_status st = check_tensor(t, false);
+        if (st != LCT_OK) return st;
+        st = check_arch();
+        if (st != LCT_OK) return st;
+        uint64_t spilled = 0;
+        hipStream_t hs = (hipStream_t)stream;
+        hipError_t e = hipMemcpyAsync(&spilled, t->obase + nblocks(t->n, t->layout), sizeof spilled,
+                                      hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip_fail(e, "spill total read");
+        reshift = (double)spilled > max_spill_per_elem * (double)t->n;
+    }
+    if (reshift) {
+        lct_status st = lct_codebook_reshift(&in, t, stream, out);
+        if (st != LCT_OK) return st;
+    } else {
+        *out = in;
+    }
+    if (changed) *changed = out->shift != in.shift;
+    return LCT_OK;
+}
+
 lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_tensor *out,
                       void *stream) {
     if (!cb || !out) return LCT_EINVAL;
@@ -225,7 +294,13 @@ lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_
 
 lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
                         const lct_tensor *m, float eta, const lct_tensor *w_out, void *stream) {
-    if (!cw || !cm || !w_in || !m || !w_out) return LCT_EINVAL;
+    return lct_sgd_step_recode(cw, w_in, cm, m, eta, cw, w_out, stream);
+}
+
+lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
+                               const lct_tensor *m, float eta, const lct_codebook *cw_out,
+                               const lct_tensor *w_out, void *stream) {
+    if (!cw || !cm || !cw_out || !w_in || !m || !w_out) return LCT_EINVAL;
     if (w_in->n != m->n || w_in->n != w_out->n) return LCT_EINVAL;
     if (w_in->layout.block_elems != m->layout.block_elems ||
         w_in->layout.block_elems != w_out->layout.block_elems ||
@@ -289,7 +364,7 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
     p.nblk = (uint32_t)nb;
     p.neg_eta = -eta;
     p.park_cnt = p.o_cnt == p.w_cnt;
-    fill_enc(*cw, &p.wenc);
+    fill_enc(*cw_out, &p.wenc);
     fill_dec(*cw, &p.wdec);
     fill_dec(*cm, &p.mdec);
     int e = launch_clear(p.scratch, nb, p.status, stream);
@@ -304,7 +379,15 @@ lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in, const lc
 lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
                              const lct_tensor *m_in, const uint16_t *d_g, float mu, float eta,
                              const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
-    if (!cw || !cm || !w_in || !m_in || !w_out || !m_out) return LCT_EINVAL;
+    return lct_momentum_step_recode(cw, w_in, cm, m_in, d_g, mu, eta, cw, cm, w_out, m_out, stream);
+}
+
+lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_in,
+                                    const lct_codebook *cm, const lct_tensor *m_in,
+                                    const uint16_t *d_g, float mu, float eta,
+                                    const lct_codebook *cw_out, const lct_codebook *cm_out,
+                                    const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
+    if (!cw || !cm || !cw_out || !cm_out || !w_in || !m_in || !w_out || !m_out) return LCT_EINVAL;
     const lct_tensor *all[] = {w_in, m_in, w_out, m_out};
     for (const lct_tensor *t : all)
         if (t->n != w_in->n || t->layout.block_elems != w_in->layout.block_elems ||
@@ -387,8 +470,8 @@ lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in, con
     p.nblk = (uint32_t)nb;
     p.mu = mu;
     p.neg_eta = -eta;
-    fill_enc(*cw, &p.wenc);
-    fill_enc(*cm, &p.menc);
+    fill_enc(*cw_out, &p.wenc);
+    fill_enc(*cm_out, &p.menc);
     fill_dec(*cw, &p.wdec);
     fill_dec(*cm, &p.mdec);
     int e = launch_clear(p.ow.scratch, nb, p.ow.status, stream);

@@ -18,7 +18,11 @@
 //   - the shift is the integer exponent offset k that minimises the coded
 //     bits of the sample under the base code (ties: smallest |k|, then the
 //     smaller k);
-//   - canonical code values follow DEFLATE's convention (RFC 1951, 3.2.2).
+//   - canonical code values follow DEFLATE's convention (RFC 1951, 3.2.2);
+//   - re-estimating the shift during training keeps the base code and runs
+//     the same shift search over a sample of the tensor's current values
+//     (explainer, paragraph on the limits: a model that no longer fits the
+//     tensor raises storage).
 #include <math.h>
 #include <string.h>
 
@@ -318,10 +322,20 @@ lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, i
         const int x = e - shift;
         out->len[e] = (x >= 0 && x < 256) ? len_base[x] : 0;
     }
+    memcpy(out->len_base, len_base, sizeof out->len_base);
     out->esc_len = esc_len;
     out->shift = (int16_t)shift;
     finish(out);
     return LCT_OK;
+}
+
+lct_status reshift_codebook(const lct_codebook &cb, const uint16_t *sample, uint32_t m,
+                            lct_codebook *out) {
+    const lct_codebook in = cb;   // out may be &cb
+    const int k = best_shift(in.len_base, in.esc_len, sample, m);
+    lct_status st = codebook_from_lengths(in.len_base, in.esc_len, k, out);
+    if (st == LCT_OK) out->model = in.model;
+    return st;
 }
 
 void fill_enc(const lct_codebook &cb, EncTab *t) {

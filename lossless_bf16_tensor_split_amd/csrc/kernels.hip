@@ -646,6 +646,53 @@ __global__ void k_gather(const uint16_t *x, uint64_t n, uint32_t m) {
     if (i < m) g_sample[i] = x[(uint64_t)i * n / m];
 }
 
+// Shift re-estimation sample of a compressed tensor: thread i < m takes
+// element floor(i * n / m).  Its stream's words are copied to the thread's
+// LDS column first (independent loads, no barrier: a thread reads only its own
+// column), then the stream is walked one code at a time up to the element's
+// position; a spilled element is read from the overflow region, whose bytes
+// are in (block, stream, position) order.  The decode table sits below the
+// columns.
+constexpr uint32_t kSampleDec = 0, kSampleCols = 1024;
+
+__global__ __launch_bounds__(64) void k_sample(const SampleParams p) {
+    for (uint32_t k = threadIdx.x; k < 256; k += 64) st32(kSampleDec + 4 * k, p.dec.dec[k]);
+    __syncthreads();
+    const uint32_t l = threadIdx.x;
+    const uint32_t i = blockIdx.x * 64 + l;
+    if (i >= p.m) return;
+    const uint64_t r = (uint64_t)i * p.n / p.m;
+    const uint64_t b = r / p.block_elems;
+    const uint32_t j = (uint32_t)(r - b * p.block_elems);
+    const uint32_t s = j % NS, pos = j / NS;
+    const uint32_t cap = p.cap_words;
+    const uint32_t c = p.cnt[b * NS + s];
+    uint32_t e = 0;
+    if (pos < c) {
+        const uint32_t *col = p.pay + b * cap * NS + s;
+        for (uint32_t w = 0; w < cap; ++w) st32(kSampleCols + (w * 64 + l) * 4, col[(size_t)w * NS]);
+        uint32_t q = 0;
+        for (uint32_t k = 0; k <= pos; ++k) {
+            const uint32_t w = q >> 5;
+            if (w >= cap) break;     // never for a valid stream: its first c codes fit
+            const uint32_t lo = ld32(kSampleCols + (w * 64 + l) * 4);
+            const uint32_t hi = w + 1 < cap ? ld32(kSampleCols + ((w + 1) * 64 + l) * 4) : 0u;
+            const uint32_t win = (uint32_t)((((uint64_t)hi << 32) | lo) >> (q & 31));
+            const uint32_t ent = ld32(kSampleDec + 4 * (win & 0xFFu));
+            if (ent & (1u << 14)) break;   // no code word: not a valid stream
+            e = (ent & (1u << 13)) ? (win >> p.dec.esc_len) & 0xFFu : ent & 0xFFu;
+            q += (ent >> 8) & 0x1Fu;
+        }
+    } else {
+        const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - b * p.block_elems);
+        uint64_t k = p.obase[b] + (pos - c);
+        for (uint32_t t = 0; t < s; ++t) k += stream_len(nb, t) - p.cnt[b * NS + t];
+        e = k < p.ovf_cap ? p.ovf[k] : 0u;
+    }
+    const uint32_t sf = p.sf[r];
+    g_sample[i] = (uint16_t)(((sf & 0x80u) << 8) | (e << 7) | (sf & 0x7Fu));
+}
+
 // ------------------------------------------------------------------ step driver
 
 // Positions [j0, j0+CH) of one lane's stream from base (the lane's position 0,
@@ -1499,6 +1546,19 @@ int launch_sgd(const SgdParams &p, void *stream) {
 int launch_momentum(const MomParams &p, void *stream) {
     return launch(ByCap<MomK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kMomWaves, true,
                   mom_lds(p.cap_words), p, stream, g_lds_granted[3][cap_slot(p.cap_words)]);
+}
+
+int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out) {
+    hipStream_t st = (hipStream_t)stream;
+    if (p.m == 0) return hipSuccess;
+    const size_t lds_bytes = kSampleCols + (size_t)p.cap_words * 64 * 4;
+    hipLaunchKernelGGL(k_sample, dim3((p.m + 63) / 64), dim3(64), lds_bytes, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    e = hipMemcpyFromSymbolAsync(host_out, HIP_SYMBOL(g_sample), p.m * sizeof(uint16_t), 0,
+                                 hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return (int)e;
+    return (int)hipStreamSynchronize(st);
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {

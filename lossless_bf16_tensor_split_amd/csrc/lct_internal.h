@@ -171,6 +171,19 @@ struct SgdParams {
     DecTab mdec;
 };
 
+// Shift sample of a compressed tensor: the values at floor(i * n / m), i < m.
+struct SampleParams {
+    const uint8_t *sf;
+    const uint32_t *pay;
+    const uint16_t *cnt;
+    const uint64_t *obase;
+    const uint8_t *ovf;
+    uint64_t ovf_cap;
+    uint64_t n;
+    uint32_t block_elems, cap_words, m, pad0;
+    DecTab dec;
+};
+
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
@@ -180,12 +193,17 @@ int launch_decode(const DecodeParams &p, void *stream);
 int launch_sgd(const SgdParams &p, void *stream);
 int launch_momentum(const MomParams &p, void *stream);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
+// The shift sample of a compressed tensor, copied to host_out; synchronises.
+int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);
 
 // Host codebook construction (codebook.cpp).
 lct_status build_codebook(const lct_model &model, const uint16_t *sample, uint32_t m,
                           lct_codebook *out);
 lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,
                                  lct_codebook *out);
+// cb's base code with the shift that minimises the sample's coded bits.
+lct_status reshift_codebook(const lct_codebook &cb, const uint16_t *sample, uint32_t m,
+                            lct_codebook *out);
 void fill_enc(const lct_codebook &cb, EncTab *t);
 void fill_dec(const lct_codebook &cb, DecTab *t);
 

@@ -41,16 +41,17 @@ def test_exports_every_declared_function(L):
 def test_struct_layouts_match_header(L, tmp_path):
     src = tmp_path / "probe.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lct.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
                    'sizeof(lct_codebook), sizeof(lct_tensor), sizeof(lct_sizes_t), sizeof(lct_model),'
                    'offsetof(lct_codebook, code), offsetof(lct_codebook, dec),'
-                   'offsetof(lct_tensor, scratch), offsetof(lct_codebook, model));return 0;}\n')
+                   'offsetof(lct_tensor, scratch), offsetof(lct_codebook, model),'
+                   'offsetof(lct_codebook, len_base));return 0;}\n')
     exe = tmp_path / "probe"
     subprocess.check_call(["gcc", "-I" + os.path.dirname(HEADER), str(src), "-o", str(exe)])
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     want = [C.sizeof(L.Codebook), C.sizeof(L._Tensor), C.sizeof(L.Sizes), C.sizeof(L.Model),
             L.Codebook.code.offset, L.Codebook.dec.offset, L._Tensor.scratch.offset,
-            L.Codebook.model.offset]
+            L.Codebook.model.offset, L.Codebook.len_base.offset]
     assert got == want
 
 
@@ -252,3 +253,63 @@ def test_momentum_arguments_rejected_on_host(L):
     z = [_fake_tensor(L, 0, lay, base) for base in (0x1000_0000_0000, 0x3000_0000_0000,
                                                     0x5000_0000_0000, 0x6000_0000_0000)]
     assert call(None, *z) == L.OK
+
+
+def test_reshift_and_recode_arguments_rejected_on_host(L):
+    """Shift re-estimation and the updates with output codebooks: bad
+    descriptors are rejected before any launch; an empty tensor needs no
+    device and gives shift 0 with the base code kept."""
+    lay = L.layout(65536, 25)
+    base = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    cb = L.lct_codebook_from_lengths(list(base.len_base), base.esc_len, 5)
+    assert cb.shift == 5 and list(cb.len_base) == list(base.len_base)
+    n = 100000
+    t = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    out = L.Codebook()
+    rs = L.lib.lct_codebook_reshift
+    assert rs(None, C.byref(t), None, C.byref(out)) == L.EINVAL
+    assert rs(C.byref(cb), None, None, C.byref(out)) == L.EINVAL
+    assert rs(C.byref(cb), C.byref(t), None, None) == L.EINVAL
+    bad = _fake_tensor(L, n, lay, 0x1000_0000_0000, sf=0x1000_0000_0008)
+    assert rs(C.byref(cb), C.byref(bad), None, C.byref(out)) == L.EALIGN
+    bad = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    bad.layout = L.layout(4096, 65)
+    assert rs(C.byref(cb), C.byref(bad), None, C.byref(out)) == L.EINVAL
+    big = _fake_tensor(L, 1 << 52, lay, 0x1000_0000_0000)
+    assert rs(C.byref(cb), C.byref(big), None, C.byref(out)) == L.EINVAL
+    t0 = _fake_tensor(L, 0, lay, 0x1000_0000_0000)
+    assert rs(C.byref(cb), C.byref(t0), None, C.byref(out)) == L.OK
+    assert out.shift == 0 and list(out.len_base) == list(base.len_base)
+    assert bytes(out.dec) == bytes(base.dec) and bytes(out.enc_bits) == bytes(base.enc_bits)
+    smp = (C.c_uint16 * 4096)()
+    mm = C.c_uint32(9)
+    assert L.lib.lct_tensor_sample(C.byref(cb), C.byref(bad), None, smp, C.byref(mm)) == L.EINVAL
+    assert L.lib.lct_tensor_sample(C.byref(cb), C.byref(t), None, None, C.byref(mm)) == L.EINVAL
+    assert L.lib.lct_tensor_sample(C.byref(cb), C.byref(t0), None, smp, C.byref(mm)) == L.OK
+    assert mm.value == 0
+    # adapt: the limit must be a number >= 0; an empty tensor spills nothing
+    ad = L.lib.lct_codebook_adapt
+    changed = C.c_int32(7)
+    assert ad(C.byref(cb), C.byref(t), C.c_double(-1.0), None, C.byref(out), C.byref(changed)) == L.EINVAL
+    assert ad(C.byref(cb), C.byref(t), C.c_double(float("nan")), None, C.byref(out), None) == L.EINVAL
+    assert ad(C.byref(cb), C.byref(bad), C.c_double(0.01), None, C.byref(out), None) == L.EINVAL
+    assert ad(C.byref(cb), C.byref(t0), C.c_double(0.0), None, C.byref(out), C.byref(changed)) == L.OK
+    assert changed.value == 0 and out.shift == 5
+    # updates with output codebooks
+    w = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    m = _fake_tensor(L, n, lay, 0x3000_0000_0000)
+    o = _fake_tensor(L, n, lay, 0x5000_0000_0000)
+    om = _fake_tensor(L, n, lay, 0x6000_0000_0000)
+    g = C.c_void_p(0x7000_0000_0000)
+    sr = L.lib.lct_sgd_step_recode
+    eta = C.c_float(1e-3)
+    assert sr(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), eta, None, C.byref(o), None) == L.EINVAL
+    bad = _fake_tensor(L, n, lay, 0x5000_0000_0000, ovf=w.ovf)
+    assert sr(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), eta, C.byref(base), C.byref(bad),
+              None) == L.EALIAS
+    mr = L.lib.lct_momentum_step_recode
+    mu = C.c_float(0.9)
+    assert mr(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), g, mu, eta, C.byref(base), None,
+              C.byref(o), C.byref(om), None) == L.EINVAL
+    assert mr(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), C.c_void_p(om.pay), mu, eta,
+              C.byref(base), C.byref(base), C.byref(o), C.byref(om), None) == L.EALIAS
