@@ -284,6 +284,8 @@ def main():
         next_ops["reshift"] = {"ms": round(1e3 * float(np.median(tr)), 4), "sample": 4096,
                                "shift_before": int(cbw.shift), "shift_after": int(new.shift)}
         del sets, bw, bm, wi, mi, wo, mo
+        torch.cuda.empty_cache()
+        next_ops["activations"] = activation_leg(L, dev)
 
     out = {
         "metric": METRIC,
@@ -315,6 +317,76 @@ def main():
         "next_ops": next_ops,
     }
     print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ saved activations
+
+def activation_leg(L, dev, seq=3500, hid=2560, ffn=9728, reps=5):
+    """One Qwen3-4B-shaped MLP block with its residual at batch 1 and the given
+    sequence length, x + down(silu(gate(x)) * up(x)), random weights (std
+    0.02) and inputs: forward and backward timed with autograd's saved tensors
+    kept as they are, then kept compressed (encoded when saved, decoded when
+    backward reads them)."""
+    import numpy as np
+    import torch
+    from lossless_bf16_tensor_split_amd.activations import compressed_activations
+
+    f = torch.nn.functional
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9000)
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device=dev) * scale).to(torch.bfloat16)
+
+    x = randn(seq, hid).requires_grad_()
+    ws = [randn(ffn, hid, scale=0.02).requires_grad_(), randn(ffn, hid, scale=0.02).requires_grad_(),
+          randn(hid, ffn, scale=0.02).requires_grad_()]
+
+    def step():
+        y = x + f.linear(f.silu(f.linear(x, ws[0])) * f.linear(x, ws[1]), ws[2])
+        y.float().square().mean().backward()
+
+    def grads(compress):
+        for t in [x] + ws:
+            t.grad = None
+        if compress:
+            with compressed_activations(L.Model(L.GAUSSIAN, 1.0, 0.0)):
+                step()
+        else:
+            step()
+        torch.cuda.synchronize()
+        return [t.grad.clone() for t in [x] + ws]
+
+    def timed(compress):
+        codec, ms = None, []
+        for i in range(reps + 2):
+            for t in [x] + ws:
+                t.grad = None
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if compress:
+                with compressed_activations(L.Model(L.GAUSSIAN, 1.0, 0.0)) as codec:
+                    step()
+            else:
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms)), codec
+
+    g_plain, g_again, g_lct = grads(False), grads(False), grads(True)
+    same = all(torch.equal(a, b) for a, b in zip(g_plain, g_lct))
+    repro = all(torch.equal(a, b) for a, b in zip(g_plain, g_again))
+    del g_plain, g_again, g_lct
+    t_plain, _ = timed(False)
+    t_lct, codec = timed(True)
+    return {"workload": "Qwen3-4B-shaped MLP block, seq %d, hidden %d, FFN %d, BF16" % (seq, hid, ffn),
+            "ms_plain": round(t_plain, 3), "ms_compressed": round(t_lct, 3),
+            "step_time_increase": round(t_lct / t_plain - 1.0, 4),
+            "saved_tensors": codec.saved, "saved_raw_bytes": codec.raw_bytes,
+            "saved_stored_bytes": codec.stored_bytes, "ratio": round(codec.ratio(), 5),
+            "grads_identical": same, "plain_grads_reproducible": repro}
 
 
 # ------------------------------------------------------------------ CPU-baseline leg

@@ -202,6 +202,17 @@ lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, voi
 lct_status lct_tensor_sample(const lct_codebook *cb, const lct_tensor *t, void *stream,
                              uint16_t *out, uint32_t *m_out);
 
+/* Shift re-estimation from a dense tensor: d_x (device BF16 bit patterns, n
+ * elements) sampled at floor(i * n / m), m = min(n, 4096), as
+ * lct_codebook_build does, and cb's base code, escape length and model kept
+ * with the shift that minimises the sample's coded bits.  For a codebook
+ * built from a model this equals lct_codebook_build(model, d_x) without
+ * building the Huffman code again: the per-tensor codebook of a saved
+ * activation (abstract: activations are compressed too).  n == 0 gives shift
+ * 0.  Synchronises `stream`.  Errors: LCT_EINVAL, LCT_EARCH, LCT_EHIP. */
+lct_status lct_codebook_reshift_dense(const lct_codebook *cb, const uint16_t *d_x, uint64_t n,
+                                      void *stream, lct_codebook *out);
+
 /* Re-estimation when the spill has grown: reads t's spilled total
  * (obase[nblk]); if it exceeds max_spill_per_elem * n bytes, *out is
  * lct_codebook_reshift(cb, t), else a copy of *cb.  *changed (may be NULL)

@@ -12,6 +12,7 @@ Functions keep the C names:
     lct_codebook_from_lengths(len_base, esc_len, shift) -> Codebook
     lct_tensor_sample(cb, t) -> numpy uint16 array (the shift sample)
     lct_codebook_reshift(cb, t) -> Codebook
+    lct_codebook_reshift_dense(cb, x) -> Codebook
     lct_codebook_adapt(cb, t, max_spill_per_elem) -> (Codebook, changed)
     lct_encode(cb, x, out)            (out: LctTensor from alloc_tensor)
     lct_decode(cb, t, y)
@@ -38,7 +39,8 @@ ST_OVF_FULL, ST_LOOKBACK = 0x1, 0x2
 OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_from_lengths",
-            "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_adapt", "lct_encode", "lct_decode",
+            "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_reshift_dense",
+            "lct_codebook_adapt", "lct_encode", "lct_decode",
             "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
             "lct_strerror", "lct_last_hip_error"]
 
@@ -88,6 +90,7 @@ def _load():
     CB, T = C.POINTER(Codebook), C.POINTER(_Tensor)
     L.lct_tensor_sample.argtypes = [CB, T, P, P, C.POINTER(C.c_uint32)]
     L.lct_codebook_reshift.argtypes = [CB, T, P, CB]
+    L.lct_codebook_reshift_dense.argtypes = [CB, P, u64, P, CB]
     L.lct_codebook_adapt.argtypes = [CB, T, C.c_double, P, CB, C.POINTER(i32)]
     L.lct_sgd_step_recode.argtypes = [CB, T, CB, T, C.c_float, CB, T, P]
     L.lct_momentum_step_recode.argtypes = [CB, T, CB, T, P, C.c_float, C.c_float, CB, CB, T, T, P]
@@ -189,6 +192,18 @@ def lct_codebook_reshift(cb: Codebook, t: "LctTensor", stream=None) -> Codebook:
     return out
 
 
+def lct_codebook_reshift_dense(cb: Codebook, x: torch.Tensor, stream=None) -> Codebook:
+    """cb's base code with the shift re-estimated from the dense tensor x."""
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    out = Codebook()
+    n = x.numel()
+    st = _stream(stream) if n else None
+    _check(lib.lct_codebook_reshift_dense(C.byref(cb), _ptr(x), n, st, C.byref(out)),
+           "lct_codebook_reshift_dense")
+    return out
+
+
 def lct_codebook_adapt(cb: Codebook, t: "LctTensor", max_spill_per_elem: float, stream=None):
     """(codebook, changed): re-estimated when t spills more than the limit."""
     out = Codebook()
@@ -205,7 +220,7 @@ def lct_codebook_adapt(cb: Codebook, t: "LctTensor", max_spill_per_elem: float, 
 class LctTensor:
     """Device buffers of one compressed tensor (torch-owned memory)."""
 
-    def __init__(self, n: int, lay: Layout, ovf_cap: int, device="cuda", scratch=None):
+    def __init__(self, n: int, lay: Layout, ovf_cap: int, device="cuda", scratch=None, ovf=None):
         sz = lct_sizes(n, lay, ovf_cap)
         dev = torch.device(device)
         u8 = torch.uint8
@@ -214,7 +229,11 @@ class LctTensor:
         self.pay = torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev)
         self.cnt = torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev)
         self.obase = torch.empty(sz.obase // 8, dtype=torch.int64, device=dev)
-        self.ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
+        if ovf is None:
+            ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
+        elif ovf.numel() < ovf_cap:
+            raise ValueError("ovf too small: %d < %d" % (ovf.numel(), ovf_cap))
+        self.ovf = ovf
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
         if scratch is None:
             scratch = torch.empty(sz.scratch, dtype=u8, device=dev)
@@ -242,8 +261,8 @@ class LctTensor:
 
 
 def alloc_tensor(n: int, lay: Layout, ovf_cap: int | None = None, device="cuda",
-                 scratch=None) -> LctTensor:
-    return LctTensor(n, lay, n if ovf_cap is None else ovf_cap, device, scratch)
+                 scratch=None, ovf=None) -> LctTensor:
+    return LctTensor(n, lay, n if ovf_cap is None else ovf_cap, device, scratch, ovf)
 
 
 def _bits16(x: torch.Tensor) -> torch.Tensor:

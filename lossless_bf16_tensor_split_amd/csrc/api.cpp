@@ -194,6 +194,22 @@ lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, voi
     return reshift_codebook(*cb, sample, m, out);
 }
 
+lct_status lct_codebook_reshift_dense(const lct_codebook *cb, const uint16_t *d_x, uint64_t n,
+                                      void *stream, lct_codebook *out) {
+    if (!cb || !out || (n > 0 && !d_x)) return LCT_EINVAL;
+    const uint32_t m = (uint32_t)std::min<uint64_t>(n, 4096);
+    uint16_t sample[4096];
+    if (m > 0) {
+        if (n >= (1ull << 52)) return LCT_EINVAL;
+        lct_status st = check_arch();
+        if (st != LCT_OK) return st;
+        std::lock_guard<std::mutex> lock(g_sample_mu);
+        const int e = launch_gather(d_x, n, m, stream, sample);
+        if (e != hipSuccess) return hip_fail(e, "sample gather");
+    }
+    return reshift_codebook(*cb, sample, m, out);
+}
+
 lct_status lct_codebook_adapt(const lct_codebook *cb, const lct_tensor *t, double max_spill_per_elem,
                               void *stream, lct_codebook *out, int32_t *changed) {
     if (!cb || !t || !out || !(max_spill_per_elem >= 0)) return LCT_EINVAL;
