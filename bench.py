@@ -386,6 +386,8 @@ def activation_leg(L, dev, seq=3500, hid=2560, ffn=9728, reps=5):
             "step_time_increase": round(t_lct / t_plain - 1.0, 4),
             "saved_tensors": codec.saved, "saved_raw_bytes": codec.raw_bytes,
             "saved_stored_bytes": codec.stored_bytes, "ratio": round(codec.ratio(), 5),
+            "host_ms_in_save_hooks": round(1e3 * codec.pack_s, 3),
+            "host_ms_in_restore_hooks": round(1e3 * codec.unpack_s, 3),
             "grads_identical": same, "plain_grads_reproducible": repro}
 
 

@@ -13,8 +13,11 @@ Per saved tensor:
     the shift re-estimated from the tensor's own 4096-element sample
     (lct_codebook_reshift_dense, no Huffman rebuild);
   - buffers: the fixed side at its exact size; the spilled bytes land in a
-    staging region shared by the context and are then copied into a buffer
-    of exactly their size.
+    staging region shared by the context, large enough for every element to
+    spill, and are then copied into a buffer of exactly their size.
+
+A save waits twice for the device: for the sample that sets the shift, and
+for the spilled total that sizes the kept overflow buffer.
 
 Tensors that are not BF16, not on the GPU, not contiguous, smaller than
 `min_elems`, or leaves that require grad (parameters, which autograd saves by
@@ -22,12 +25,13 @@ reference at no cost) are saved as they are.
 """
 from __future__ import annotations
 
+import time
 from contextlib import contextmanager
 from dataclasses import dataclass
 
 import torch
 
-from . import (CLEAN, GAUSSIAN, Codebook, LctTensor, Model, ST_OVF_FULL, alloc_tensor,
+from . import (CLEAN, GAUSSIAN, Codebook, LctTensor, Model, alloc_tensor,
                lct_codebook_build, lct_codebook_reshift_dense, lct_decode, lct_encode,
                lct_layout_init, lct_sizes)
 
@@ -53,6 +57,8 @@ class ActivationCodec:
         self.passed = 0          # tensors kept as they are
         self.raw_bytes = 0       # BF16 bytes of the encoded tensors
         self.stored_bytes = 0    # their fixed sides plus spilled bytes
+        self.pack_s = 0.0        # host time spent in pack (waits for the device included)
+        self.unpack_s = 0.0      # host time spent in unpack
 
     def _wants(self, x: torch.Tensor) -> bool:
         return (x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
@@ -69,18 +75,15 @@ class ActivationCodec:
         if not self._wants(x):
             self.passed += 1
             return x
+        t0 = time.perf_counter()
         n = x.numel()
         xd = x.detach()
         cb = lct_codebook_reshift_dense(self.base, xd.view(-1))
-        cap = max(n // 16, 1 << 16)
-        while True:
-            self._staging(n, cap, x.device)
-            t = alloc_tensor(n, self.layout, cap, x.device, self._scratch, self._ovf)
-            lct_encode(cb, xd.view(-1), t)
-            spilled = t.spilled()            # synchronises
-            if not (t.status_word() & ST_OVF_FULL):
-                break
-            cap = spilled                    # the size needed is known: encode again
+        # a staging region of n bytes holds every possible spill: one encode
+        self._staging(n, n, x.device)
+        t = alloc_tensor(n, self.layout, n, x.device, self._scratch, self._ovf)
+        lct_encode(cb, xd.view(-1), t)
+        spilled = t.spilled()                # synchronises
         # keep the spilled bytes in a buffer of their own size
         t.ovf = self._ovf[:max(spilled, 16)].clone()
         t.ovf_cap = spilled
@@ -88,13 +91,16 @@ class ActivationCodec:
         self.saved += 1
         self.raw_bytes += 2 * n
         self.stored_bytes += int(t.sizes.fixed) + spilled
+        self.pack_s += time.perf_counter() - t0
         return _Saved(t, cb, x.shape)
 
     def unpack(self, h):
         if not isinstance(h, _Saved):
             return h
+        t0 = time.perf_counter()
         y = torch.empty(h.shape, dtype=torch.bfloat16, device=h.t.sf.device)
         lct_decode(h.cb, h.t, y.view(-1))
+        self.unpack_s += time.perf_counter() - t0
         return y
 
     def ratio(self) -> float:

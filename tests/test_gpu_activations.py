@@ -43,7 +43,7 @@ def test_config4_saved_tensors_round_trip(L, orc, idx):
     if spec.kind != "uniform_bits":
         assert codec.ratio() > 1.2
     else:
-        assert h.t.spilled() > x.size // 16      # the staging region grew: encoded twice
+        assert h.t.spilled() > x.size // 2       # expands: most exponents spill
 
 
 def test_saved_bytes_are_the_oracles(L, orc):
