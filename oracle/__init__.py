@@ -433,3 +433,55 @@ def reshift(cb: Codebook, t: Compressed) -> Codebook:
     if rc != OK:
         raise ValueError("reshift: error %d" % rc)
     return Codebook._from_c(out)
+
+
+# ---------------------------------------------------------------- tensor groups
+
+def group(ts, ovf_cap: int | None = None) -> Compressed:
+    """Tensors laid side by side with one shared overflow region (explainer,
+    paragraph on the idealized arithmetic: the shared overflow buffer).  Tensor
+    k's blocks follow tensor k-1's; its sign-fraction bytes start at the sum of
+    the earlier sizes, each rounded up to a multiple of 256 (the padding is
+    zero); its spilled bytes follow the earlier tensors' in the shared region
+    and its block offsets are shifted by their total.  Every tensor is encoded
+    on its own (each with every spilled byte kept); this only places them.
+    The result's n is the sf array's length."""
+    B, cw = ts[0].block_elems, ts[0].cap_words
+    assert all((t.block_elems, t.cap_words) == (B, cw) for t in ts)
+    sf, pay, cnt, ob, ovf = [], [], [], [], []
+    base = 0
+    for t in ts:
+        assert t.spilled <= len(t.ovf), "encode each tensor with room for every spill"
+        pad = -(-t.n // 256) * 256
+        sf.append(np.concatenate([t.sf[:t.n], np.zeros(pad - t.n, np.uint8)]))
+        pay.append(t.pay)
+        cnt.append(t.cnt)
+        ob.append(t.obase[:-1] + np.uint64(base))
+        ovf.append(t.ovf[:t.spilled])
+        base += t.spilled
+    ob.append(np.array([base], np.uint64))
+    total = base
+    ovf_cap = total if ovf_cap is None else ovf_cap
+    region = np.zeros(max(ovf_cap, 1), np.uint8)
+    keep = min(total, ovf_cap)
+    region[:keep] = np.concatenate(ovf)[:keep] if ovf else region[:0]
+    g = Compressed(sum(len(a) for a in sf), B, cw, np.concatenate(sf), np.concatenate(pay),
+                   np.concatenate(cnt), np.concatenate(ob), region)
+    g.status = int(total > ovf_cap)
+    return g
+
+
+def group_member(g: Compressed, ns, k: int) -> Compressed:
+    """Tensor k of a group (sizes ns) as a tensor whose block offsets index
+    the group's shared overflow region."""
+    B, cw = g.block_elems, g.cap_words
+    b0 = sum(-(-n // B) for n in ns[:k])
+    e0 = sum(-(-n // 256) * 256 for n in ns[:k])
+    nb = -(-ns[k] // B)
+    return Compressed(ns[k], B, cw, g.sf[e0:e0 + ns[k]], g.pay[b0 * cw * NSTREAM:(b0 + nb) * cw * NSTREAM],
+                      g.cnt[b0 * NSTREAM:(b0 + nb) * NSTREAM], g.obase[b0:b0 + nb + 1], g.ovf)
+
+
+def encode_group(cbs, xs, block_elems: int, cap_words: int, ovf_cap: int | None = None) -> Compressed:
+    """Every tensor encoded with its own codebook, then placed as a group."""
+    return group([encode(cb, x, block_elems, cap_words) for cb, x in zip(cbs, xs)], ovf_cap)
