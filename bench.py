@@ -286,6 +286,8 @@ def main():
         del sets, bw, bm, wi, mi, wo, mo
         torch.cuda.empty_cache()
         next_ops["activations"] = activation_leg(L, dev)
+        if args.workload == "qwen3_4b":
+            next_ops["group"] = group_leg(L, dev, stream, w_dense, mspec, mw, mm, eta, lay)
 
     out = {
         "metric": METRIC,
@@ -317,6 +319,79 @@ def main():
         "next_ops": next_ops,
     }
     print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ tensor groups
+
+def group_leg(L, dev, stream, w_dense, mspec, mw, mm, eta, lay, reps=5):
+    """The same step on the Qwen3-4B parameter set as its 398 tensors (each
+    with its own codebook: the model's base code, the shift from its own
+    sample), one group launch per op and one shared overflow region, against
+    the same tensors one call each."""
+    import numpy as np
+    import torch
+    import synth
+
+    ns = [int(np.prod(s)) for _, s in synth.qwen3_4b_shapes()]
+    offs = np.concatenate([[0], np.cumsum(ns)])
+    assert offs[-1] == w_dense.numel() and all(o % 8 == 0 for o in offs)   # 16-byte aligned slices
+    m_dense = synth.draw_device(mspec, dev)
+    wv = [w_dense[offs[k]:offs[k + 1]] for k in range(len(ns))]
+    mv = [m_dense[offs[k]:offs[k + 1]] for k in range(len(ns))]
+    basew = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), None)
+    basem = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), None)
+    t0 = time.perf_counter()
+    cw = [L.lct_codebook_reshift_dense(basew, v) for v in wv]
+    t_cb = time.perf_counter() - t0
+    cm = [L.lct_codebook_reshift_dense(basem, v) for v in mv]
+    gw = L.LctGroup(ns, lay, cw, wv)
+    gm = L.LctGroup(ns, lay, cm, mv)
+    cap = sum(ns) // 64
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gm, m_all)
+    w_out = gw.alloc_storage(cap, scratch=w_all.scratch)
+    w_out.sf, w_out.pay, w_out.cnt, w_out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+
+    def group_step(e):
+        e[0].record(stream)
+        L.lct_encode_group(gw, w_all)
+        e[1].record(stream)
+        L.lct_sgd_step_group(gw, w_all, gm, m_all, eta, w_out)
+        e[2].record(stream)
+        L.lct_decode_group(gw, w_out)
+        e[3].record(stream)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 2)]
+    for e in ev:
+        group_step(e)
+    torch.cuda.synchronize()
+    status = [w_all.status_word(), w_out.status_word(), m_all.status_word()]
+    timed = ev[2:]
+    ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in timed]))
+          for i, name in enumerate(["encode", "sgd", "decode"])}
+    ms["step"] = float(np.mean([e[0].elapsed_time(e[3]) for e in timed]))
+    spilled = [w_all.spilled(), m_all.spilled(), w_out.spilled()]
+    # the same encodes as one call per tensor (each tensor its own storage)
+    singles = [L.alloc_tensor(n, lay, max(n // 64, 1024), dev) for n in ns]
+    for k in range(len(ns)):
+        L.lct_encode(cw[k], wv[k], singles[k])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(len(ns)):
+        L.lct_encode(cw[k], wv[k], singles[k])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_singles = e0.elapsed_time(e1)
+    nblk = int(gw.g.nblk)
+    del singles, m_dense, w_all, m_all, w_out, gw, gm
+    torch.cuda.empty_cache()
+    return {"workload": "Qwen3-4B-shaped parameter set as %d tensors (%d blocks), one group each for W and M"
+                        % (len(ns), nblk),
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "elems_per_s": float("%.4g" % (sum(ns) / (ms["step"] / 1e3))),
+            "encode_one_call_per_tensor_ms": round(t_singles, 4),
+            "codebooks_ms": round(1e3 * t_cb, 2), "spilled_bytes": spilled, "status": status}
 
 
 # ------------------------------------------------------------------ saved activations

@@ -288,6 +288,74 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
                                     const lct_codebook *cw_out, const lct_codebook *cm_out,
                                     const lct_tensor *w_out, const lct_tensor *m_out, void *stream);
 
+/* ---- tensor groups ---------------------------------------------------------
+ * Many tensors in one launch, with one shared overflow region (explainer,
+ * paragraph on the idealized arithmetic: measured memory includes the shared
+ * overflow buffer).  A group lays its tensors side by side: tensor k's blocks
+ * follow tensor k-1's in one set of arrays (pay, cnt and obase indexed by the
+ * group's block number), its sign-fraction bytes start at a multiple of 256 in
+ * one sf array, and every spilled byte goes to one overflow region, in tensor
+ * order; obase values are offsets into that shared region.  Each tensor keeps
+ * its own codebook and its own dense buffer.  Tensor k alone is an ordinary
+ * lct_tensor (lct_group_tensor) that every other call accepts.
+ *
+ * The group's storage is one lct_tensor whose n is the group's sf_bytes and
+ * whose arrays are sized by lct_group_sizes; its status word and scratch
+ * serve the whole group. */
+typedef struct {
+    uint32_t count;              /* tensors */
+    lct_layout layout;
+    uint64_t nblk;               /* blocks of all tensors */
+    uint64_t sf_bytes;           /* sf array: every n[k] rounded up to a multiple of 256 */
+    uint64_t shape_hash;         /* fingerprint of (layout, n[]) */
+    const uint64_t *n;           /* host, caller-owned, count entries, alive while the group is used */
+    uint16_t *const *d_dense;    /* host array of device pointers, caller-owned (may be NULL) */
+    void *d_table;               /* device descriptor table */
+} lct_group;
+
+/* Bytes of the device descriptor table of a group (count tensors of n[k]
+ * elements in `layout`).  Errors: LCT_EINVAL. */
+lct_status lct_group_table_bytes(uint32_t count, const uint64_t *n, const lct_layout *layout,
+                                 uint64_t *bytes);
+
+/* Set up a group: tensor k has n[k] elements (0 allowed), codebook cbs[k]
+ * (used to encode and decode it; for a group used as M in an update, to
+ * decode it) and dense buffer d_dense[k] (device BF16, 16-byte aligned, the
+ * source of lct_encode_group and the target of lct_decode_group; d_dense may
+ * be NULL for a group that is only updated).  Dense buffers must not overlap
+ * each other.  Writes the descriptor table to d_table (device,
+ * lct_group_table_bytes bytes, 256-byte aligned) with a blocking copy and
+ * fills *out, which keeps the n and d_dense pointers.  Errors: LCT_EINVAL,
+ * LCT_EALIGN, LCT_EALIAS, LCT_EARCH, LCT_EHIP. */
+lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *layout,
+                          const lct_codebook *cbs, uint16_t *const *d_dense, void *d_table,
+                          lct_group *out);
+
+/* Sizes of a group's storage arrays (as lct_sizes for one tensor). */
+lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out);
+
+/* Tensor k of a group as an lct_tensor: views into the storage `all` (its
+ * ovf, ovf_cap, status and scratch are all's). */
+lct_status lct_group_tensor(const lct_group *g, const lct_tensor *all, uint32_t k, lct_tensor *out);
+
+/* Encode every tensor of the group from its dense buffer, in one launch
+ * (plus the clear and the overflow scan).  As lct_encode otherwise: the
+ * status word reports a too-small shared overflow region.  Errors:
+ * LCT_EINVAL (no dense buffers, storage not sized for g), LCT_EALIGN,
+ * LCT_EALIAS (a dense buffer overlapping the storage), LCT_EARCH, LCT_EHIP. */
+lct_status lct_encode_group(const lct_group *g, const lct_tensor *all, void *stream);
+
+/* Decode every tensor of the group into its dense buffer, in one launch. */
+lct_status lct_decode_group(const lct_group *g, const lct_tensor *all, void *stream);
+
+/* Fused SGD step on a group, in one launch: W' = W - eta * M per tensor as
+ * lct_sgd_step, with gw's codebooks for W and W' and gm's for M.  gw and gm
+ * must have the same layout and sizes.  Storage aliasing rules as
+ * lct_sgd_step (w_out may be w_all in place).  Errors: as lct_sgd_step. */
+lct_status lct_sgd_step_group(const lct_group *gw, const lct_tensor *w_all, const lct_group *gm,
+                              const lct_tensor *m_all, float eta, const lct_tensor *w_out,
+                              void *stream);
+
 /* Message for a status code (static string). */
 const char *lct_strerror(lct_status st);
 /* Text of the last HIP error seen on this thread (static per thread). */

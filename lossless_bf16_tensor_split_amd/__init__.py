@@ -20,6 +20,9 @@ Functions keep the C names:
     lct_sgd_step_recode(cw, w_in, cm, m, eta, cw_out, w_out)
     lct_momentum_step(cw, w_in, cm, m_in, g, mu, eta, w_out, m_out)
     lct_momentum_step_recode(cw, w_in, cm, m_in, g, mu, eta, cw_out, cm_out, w_out, m_out)
+    LctGroup(ns, layout, codebooks, dense)  (lct_group_table_bytes + lct_group_bind)
+    lct_encode_group(g, all) / lct_decode_group(g, all)
+    lct_sgd_step_group(gw, w_all, gm, m_all, eta, w_out)
 plus ``alloc_tensor`` and the convenience wrappers ``encode`` / ``decode`` /
 ``sgd_step`` / ``momentum_step`` that allocate their outputs.
 """
@@ -42,6 +45,8 @@ EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_
             "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_reshift_dense",
             "lct_codebook_adapt", "lct_encode", "lct_decode",
             "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
+            "lct_group_table_bytes", "lct_group_bind", "lct_group_sizes", "lct_group_tensor",
+            "lct_encode_group", "lct_decode_group", "lct_sgd_step_group",
             "lct_strerror", "lct_last_hip_error"]
 
 
@@ -73,6 +78,12 @@ class Sizes(C.Structure):
                 ("fixed", C.c_uint64)]
 
 
+class Group(C.Structure):
+    _fields_ = [("count", C.c_uint32), ("layout", Layout), ("nblk", C.c_uint64),
+                ("sf_bytes", C.c_uint64), ("shape_hash", C.c_uint64), ("n", C.c_void_p),
+                ("d_dense", C.c_void_p), ("d_table", C.c_void_p)]
+
+
 class LctError(RuntimeError):
     pass
 
@@ -94,6 +105,14 @@ def _load():
     L.lct_codebook_adapt.argtypes = [CB, T, C.c_double, P, CB, C.POINTER(i32)]
     L.lct_sgd_step_recode.argtypes = [CB, T, CB, T, C.c_float, CB, T, P]
     L.lct_momentum_step_recode.argtypes = [CB, T, CB, T, P, C.c_float, C.c_float, CB, CB, T, T, P]
+    G = C.POINTER(Group)
+    L.lct_group_table_bytes.argtypes = [C.c_uint32, P, C.POINTER(Layout), C.POINTER(u64)]
+    L.lct_group_bind.argtypes = [C.c_uint32, P, C.POINTER(Layout), P, P, P, G]
+    L.lct_group_sizes.argtypes = [G, u64, C.POINTER(Sizes)]
+    L.lct_group_tensor.argtypes = [G, T, C.c_uint32, T]
+    L.lct_encode_group.argtypes = [G, T, P]
+    L.lct_decode_group.argtypes = [G, T, P]
+    L.lct_sgd_step_group.argtypes = [G, T, G, T, C.c_float, T, P]
     L.lct_encode.argtypes = [C.POINTER(Codebook), P, C.POINTER(_Tensor), P]
     L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
     L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
@@ -241,6 +260,15 @@ class LctTensor:
             raise ValueError("scratch too small: %d < %d" % (scratch.numel(), sz.scratch))
         self.scratch = scratch
 
+    @classmethod
+    def wrap(cls, n: int, lay: Layout, ovf_cap: int, sizes: Sizes, sf, pay, cnt, obase, ovf, status,
+             scratch) -> "LctTensor":
+        """A descriptor over existing buffers (views of a group's storage)."""
+        t = cls.__new__(cls)
+        t.n, t.layout, t.ovf_cap, t.sizes = n, Layout(lay.block_elems, lay.cap_words), ovf_cap, sizes
+        t.sf, t.pay, t.cnt, t.obase, t.ovf, t.status, t.scratch = sf, pay, cnt, obase, ovf, status, scratch
+        return t
+
     def c(self) -> _Tensor:
         return _Tensor(self.n, self.layout, _ptr(self.sf), _ptr(self.pay), _ptr(self.cnt),
                        _ptr(self.obase), _ptr(self.ovf), self.ovf_cap, _ptr(self.status),
@@ -353,3 +381,84 @@ def momentum_step(cw: Codebook, w: LctTensor, cm: Codebook, m: LctTensor, g: tor
         m_out = alloc_tensor(m.n, m.layout, ovf_cap, m.sf.device)
     lct_momentum_step(cw, w, cm, m, g, mu, eta, w_out, m_out)
     return w_out, m_out
+
+
+# ------------------------------------------------------------------ tensor groups
+
+class LctGroup:
+    """A bound group: the device table, the host arrays the C struct points
+    at (kept alive here), the codebooks and the dense tensors."""
+
+    def __init__(self, ns, lay: Layout, codebooks, dense=None, device="cuda"):
+        count = len(ns)
+        if len(codebooks) != count or (dense is not None and len(dense) != count):
+            raise ValueError("one codebook (and one dense tensor) per size")
+        self.count, self.layout = count, Layout(lay.block_elems, lay.cap_words)
+        self.ns = (C.c_uint64 * count)(*[int(v) for v in ns])
+        self.codebooks = (Codebook * count)(*codebooks)
+        self.dense = list(dense) if dense is not None else None
+        self.dense_ptrs = None
+        if dense is not None:
+            for t in dense:
+                _bits16(t)
+            self.dense_ptrs = (C.c_void_p * count)(*[t.data_ptr() for t in dense])
+        nbytes = C.c_uint64(0)
+        _check(lib.lct_group_table_bytes(count, self.ns, C.byref(self.layout), C.byref(nbytes)),
+               "lct_group_table_bytes")
+        self.table = torch.empty(max(int(nbytes.value), 256), dtype=torch.uint8, device=device)
+        self.g = Group()
+        _check(lib.lct_group_bind(count, self.ns, C.byref(self.layout), self.codebooks,
+                                  self.dense_ptrs, _ptr(self.table), C.byref(self.g)), "lct_group_bind")
+
+    def sizes(self, ovf_cap: int = 0) -> Sizes:
+        out = Sizes()
+        _check(lib.lct_group_sizes(C.byref(self.g), ovf_cap, C.byref(out)), "lct_group_sizes")
+        return out
+
+    def alloc_storage(self, ovf_cap: int, device="cuda", scratch=None) -> LctTensor:
+        sz = self.sizes(ovf_cap)
+        dev = torch.device(device)
+        u8 = torch.uint8
+        if scratch is None:
+            scratch = torch.empty(sz.scratch, dtype=u8, device=dev)
+        return LctTensor.wrap(int(self.g.sf_bytes), self.layout, ovf_cap, sz,
+                              torch.empty(max(sz.sf, 16), dtype=u8, device=dev),
+                              torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev),
+                              torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev),
+                              torch.empty(sz.obase // 8, dtype=torch.int64, device=dev),
+                              torch.empty(max(ovf_cap, 16), dtype=u8, device=dev),
+                              torch.zeros(4, dtype=torch.int32, device=dev), scratch)
+
+    def tensor(self, all_: LctTensor, k: int) -> LctTensor:
+        """Tensor k as views of the storage (its obase values index the shared
+        overflow region; read it with any call, write the group with the
+        group calls)."""
+        t = _Tensor()
+        a = all_.c()
+        _check(lib.lct_group_tensor(C.byref(self.g), C.byref(a), k, C.byref(t)), "lct_group_tensor")
+        n = int(self.ns[k])
+        sz = lct_sizes(n, self.layout, all_.ovf_cap)
+        sf0 = (t.sf or 0) - all_.sf.data_ptr()
+        pay0 = ((t.pay or 0) - all_.pay.data_ptr()) // 4
+        cnt0 = ((t.cnt or 0) - all_.cnt.data_ptr()) // 2
+        ob0 = ((t.obase or 0) - all_.obase.data_ptr()) // 8
+        return LctTensor.wrap(n, self.layout, all_.ovf_cap, sz, all_.sf[sf0:sf0 + max(n, 1)],
+                              all_.pay[pay0:pay0 + sz.pay // 4], all_.cnt[cnt0:cnt0 + sz.cnt // 2],
+                              all_.obase[ob0:ob0 + sz.obase // 8], all_.ovf, all_.status, all_.scratch)
+
+
+def lct_encode_group(g: LctGroup, all_: LctTensor, stream=None) -> None:
+    a = all_.c()
+    _check(lib.lct_encode_group(C.byref(g.g), C.byref(a), _stream(stream)), "lct_encode_group")
+
+
+def lct_decode_group(g: LctGroup, all_: LctTensor, stream=None) -> None:
+    a = all_.c()
+    _check(lib.lct_decode_group(C.byref(g.g), C.byref(a), _stream(stream)), "lct_decode_group")
+
+
+def lct_sgd_step_group(gw: LctGroup, w_all: LctTensor, gm: LctGroup, m_all: LctTensor, eta: float,
+                       w_out: LctTensor, stream=None) -> None:
+    a, b, o = w_all.c(), m_all.c(), w_out.c()
+    _check(lib.lct_sgd_step_group(C.byref(gw.g), C.byref(a), C.byref(gm.g), C.byref(b), eta,
+                                  C.byref(o), _stream(stream)), "lct_sgd_step_group")

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "lct_internal.h"
 
@@ -63,8 +64,10 @@ struct Parts {
     Range sf, pay, cnt, obase, ovf, status, scratch;
 };
 
-Parts parts(const lct_tensor &t) {
-    const uint64_t nb = nblocks(t.n, t.layout);
+// The ranges of a tensor's buffers; nb overrides the block count (a group's
+// storage has more blocks than its n implies).
+Parts parts(const lct_tensor &t, uint64_t nb = ~0ull) {
+    if (nb == ~0ull) nb = nblocks(t.n, t.layout);
     Parts p;
     p.sf = rng(t.sf, t.n);
     p.pay = rng(t.pay, nb * t.layout.cap_words * kStreams * 4);
@@ -77,7 +80,7 @@ Parts parts(const lct_tensor &t) {
 }
 
 // Pointers a call reads or writes must be non-null and aligned.
-lct_status check_tensor(const lct_tensor *t, bool writes) {
+lct_status check_tensor(const lct_tensor *t, bool writes, uint64_t nb = ~0ull) {
     if (!t || !layout_ok(t->layout)) return LCT_EINVAL;
     if (!t->sf || !t->pay || !t->cnt || !t->obase) return LCT_EINVAL;
     if (t->ovf_cap && !t->ovf) return LCT_EINVAL;
@@ -87,7 +90,7 @@ lct_status check_tensor(const lct_tensor *t, bool writes) {
         if (!t->status || !t->scratch) return LCT_EINVAL;
         if (!aligned(t->status, 4) || !aligned(t->scratch, 256)) return LCT_EALIGN;
         // the output's own parts must be disjoint
-        const Parts p = parts(*t);
+        const Parts p = parts(*t, nb);
         const Range all[] = {p.sf, p.pay, p.cnt, p.obase, p.ovf, p.status, p.scratch};
         for (int i = 0; i < 7; ++i)
             for (int j = i + 1; j < 7; ++j)
@@ -105,6 +108,131 @@ bool overlaps_any(Range r, const Parts &p, bool with_writable = true) {
 }
 
 std::mutex g_sample_mu;
+
+// ---- groups
+
+uint64_t shape_hash(uint32_t count, const uint64_t *n, const lct_layout &l) {
+    uint64_t h = 1469598103934665603ull;   // FNV-1a over the layout and sizes
+    auto mix = [&](uint64_t v) {
+        for (int i = 0; i < 8; ++i) {
+            h ^= (v >> (8 * i)) & 0xFF;
+            h *= 1099511628211ull;
+        }
+    };
+    mix(l.block_elems);
+    mix(l.cap_words);
+    mix(count);
+    for (uint32_t k = 0; k < count; ++k) mix(n[k]);
+    return h;
+}
+
+uint64_t round256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// The group's block count and sf bytes; false on overflow of the 32-bit block index.
+bool group_extent(uint32_t count, const uint64_t *n, const lct_layout &l, uint64_t *nblk, uint64_t *sf) {
+    uint64_t nb = 0, s = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        if (n[k] >= (1ull << 48)) return false;
+        nb += nblocks(n[k], l);
+        s += round256(n[k]);
+    }
+    if (nb > 0xFFFFFFFFull) return false;
+    *nblk = nb;
+    *sf = s;
+    return true;
+}
+
+GroupRef group_ref(const lct_group &g) {
+    const GroupTableLayout t = group_table_layout(g.count, g.nblk);
+    const uint8_t *base = static_cast<const uint8_t *>(g.d_table);
+    return {reinterpret_cast<const GroupEntry *>(base + t.ent), reinterpret_cast<const EncTab *>(base + t.enc),
+            reinterpret_cast<const DecTab *>(base + t.dec), reinterpret_cast<const uint32_t *>(base + t.blk_tensor)};
+}
+
+// A bound group and storage sized for it.
+lct_status check_group(const lct_group *g, const lct_tensor *all, bool writes) {
+    if (!g || !all || !g->d_table || !g->n || g->count == 0 || !layout_ok(g->layout)) return LCT_EINVAL;
+    if (all->n != g->sf_bytes || all->layout.block_elems != g->layout.block_elems ||
+        all->layout.cap_words != g->layout.cap_words)
+        return LCT_EINVAL;
+    uint64_t nb = 0, sf = 0;
+    if (!group_extent(g->count, g->n, g->layout, &nb, &sf) || nb != g->nblk || sf != g->sf_bytes ||
+        shape_hash(g->count, g->n, g->layout) != g->shape_hash)
+        return LCT_EINVAL;
+    return check_tensor(all, writes, g->nblk);
+}
+
+// Every dense buffer of the group, disjoint from the storage's parts.
+lct_status check_group_dense(const lct_group &g, const Parts &p) {
+    if (!g.d_dense) return LCT_EINVAL;
+    for (uint32_t k = 0; k < g.count; ++k) {
+        if (g.n[k] == 0) continue;
+        if (!g.d_dense[k]) return LCT_EINVAL;
+        if (!aligned(g.d_dense[k], 16)) return LCT_EALIGN;
+        if (overlaps_any(rng(g.d_dense[k], g.n[k] * 2), p)) return LCT_EALIAS;
+    }
+    return LCT_OK;
+}
+
+// Aliasing rules, parameters and launches of an update (a tensor, or a
+// group's storage when `group`); p's tables (or group references) are set.
+lct_status sgd_run(SgdParams &p, const lct_tensor &w_in, const lct_tensor &m, const lct_tensor &w_out,
+                   uint64_t nb, float eta, bool group, void *stream) {
+    const Parts pw = parts(w_in, nb), pm = parts(m, nb), po = parts(w_out, nb);
+    // M is read-only and must not share memory with the output
+    const Range mr[] = {pm.sf, pm.pay, pm.cnt, pm.obase, pm.ovf};
+    for (const Range &r : mr)
+        if (overlaps_any(r, po)) return LCT_EALIAS;
+    // the output's fixed side may be W's own buffers, exactly, or disjoint from W
+    const Range wf[] = {pw.sf, pw.pay, pw.cnt, pw.obase};
+    const Range of[] = {po.sf, po.pay, po.cnt, po.obase};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j) {
+            const bool same = i == j && wf[i].lo == of[j].lo;
+            if (!same && overlap(wf[i], of[j])) return LCT_EALIAS;
+        }
+        if (overlap(pw.ovf, of[i])) return LCT_EALIAS;
+    }
+    // overflow, status and scratch of the output never overlap an input
+    const Range ow[] = {po.ovf, po.status, po.scratch};
+    for (const Range &r : ow)
+        if (overlaps_any(r, pw, false) || overlaps_any(r, pm, false)) return LCT_EALIAS;
+    lct_status st = check_arch();
+    if (st != LCT_OK) return st;
+    p.w_sf = w_in.sf;
+    p.w_pay = w_in.pay;
+    p.w_cnt = w_in.cnt;
+    p.w_obase = w_in.obase;
+    p.w_ovf = w_in.ovf;
+    p.w_ovf_cap = w_in.ovf_cap;
+    p.m_sf = m.sf;
+    p.m_pay = m.pay;
+    p.m_cnt = m.cnt;
+    p.m_obase = m.obase;
+    p.m_ovf = m.ovf;
+    p.m_ovf_cap = m.ovf_cap;
+    p.o_sf = w_out.sf;
+    p.o_pay = w_out.pay;
+    p.o_cnt = w_out.cnt;
+    p.o_obase = w_out.obase;
+    p.o_ovf = w_out.ovf;
+    p.ovf_cap = w_out.ovf_cap;
+    p.status = w_out.status;
+    p.scratch = (uint8_t *)w_out.scratch;
+    p.n = w_in.n;
+    p.block_elems = w_in.layout.block_elems;
+    p.cap_words = w_in.layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.neg_eta = -eta;
+    p.park_cnt = p.o_cnt == p.w_cnt;
+    int e = launch_clear(p.scratch, nb, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_sgd(p, stream, group);
+    if (e != hipSuccess) return hip_fail(e, "sgd launch");
+    e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return LCT_OK;
+}
 
 }  // namespace
 
@@ -328,68 +456,14 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in, c
     if (st == LCT_OK) st = check_tensor(m, false);
     if (st == LCT_OK) st = check_tensor(w_out, true);
     if (st != LCT_OK) return st;
-    const Parts pw = parts(*w_in), pm = parts(*m), po = parts(*w_out);
-    // M is read-only and must not share memory with the output
-    const Range mr[] = {pm.sf, pm.pay, pm.cnt, pm.obase, pm.ovf};
-    for (const Range &r : mr)
-        if (overlaps_any(r, po)) return LCT_EALIAS;
-    // the output's fixed side may be W's own buffers, exactly, or disjoint from W
-    const Range wf[] = {pw.sf, pw.pay, pw.cnt, pw.obase};
-    const Range of[] = {po.sf, po.pay, po.cnt, po.obase};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 4; ++j) {
-            const bool same = i == j && wf[i].lo == of[j].lo;
-            if (!same && overlap(wf[i], of[j])) return LCT_EALIAS;
-        }
-        if (overlap(pw.ovf, of[i])) return LCT_EALIAS;
-    }
-    // overflow, status and scratch of the output never overlap an input
-    const Range ow[] = {po.ovf, po.status, po.scratch};
-    for (const Range &r : ow)
-        if (overlaps_any(r, pw, false) || overlaps_any(r, pm, false)) return LCT_EALIAS;
-    st = check_arch();
-    if (st != LCT_OK) return st;
-
     const uint64_t nb = nblocks(w_in->n, w_in->layout);
     if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
     SgdParams p;
     memset(&p, 0, sizeof p);
-    p.w_sf = w_in->sf;
-    p.w_pay = w_in->pay;
-    p.w_cnt = w_in->cnt;
-    p.w_obase = w_in->obase;
-    p.w_ovf = w_in->ovf;
-    p.w_ovf_cap = w_in->ovf_cap;
-    p.m_sf = m->sf;
-    p.m_pay = m->pay;
-    p.m_cnt = m->cnt;
-    p.m_obase = m->obase;
-    p.m_ovf = m->ovf;
-    p.m_ovf_cap = m->ovf_cap;
-    p.o_sf = w_out->sf;
-    p.o_pay = w_out->pay;
-    p.o_cnt = w_out->cnt;
-    p.o_obase = w_out->obase;
-    p.o_ovf = w_out->ovf;
-    p.ovf_cap = w_out->ovf_cap;
-    p.status = w_out->status;
-    p.scratch = (uint8_t *)w_out->scratch;
-    p.n = w_in->n;
-    p.block_elems = w_in->layout.block_elems;
-    p.cap_words = w_in->layout.cap_words;
-    p.nblk = (uint32_t)nb;
-    p.neg_eta = -eta;
-    p.park_cnt = p.o_cnt == p.w_cnt;
     fill_enc(*cw_out, &p.wenc);
     fill_dec(*cw, &p.wdec);
     fill_dec(*cm, &p.mdec);
-    int e = launch_clear(p.scratch, nb, p.status, stream);
-    if (e != hipSuccess) return hip_fail(e, "clear launch");
-    e = launch_sgd(p, stream);
-    if (e != hipSuccess) return hip_fail(e, "sgd launch");
-    e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
-    if (e != hipSuccess) return hip_fail(e, "scan launch");
-    return LCT_OK;
+    return sgd_run(p, *w_in, *m, *w_out, nb, eta, false, stream);
 }
 
 lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
@@ -500,6 +574,178 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
         e = launch_scan(p.om.scratch, nb, p.om.obase, p.om.ovf, p.om.ovf_cap, p.om.status, p.om.cnt, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
+}
+
+// ---- groups
+
+lct_status lct_group_table_bytes(uint32_t count, const uint64_t *n, const lct_layout *layout,
+                                 uint64_t *bytes) {
+    if (!layout || !bytes || !layout_ok(*layout) || (count > 0 && !n)) return LCT_EINVAL;
+    uint64_t nb = 0, sf = 0;
+    if (!group_extent(count, n, *layout, &nb, &sf)) return LCT_EINVAL;
+    *bytes = group_table_layout(count, nb).bytes;
+    return LCT_OK;
+}
+
+lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *layout,
+                          const lct_codebook *cbs, uint16_t *const *d_dense, void *d_table,
+                          lct_group *out) {
+    if (!layout || !out || !cbs || !n || !d_table || count == 0 || !layout_ok(*layout))
+        return LCT_EINVAL;
+    if (!aligned(d_table, 256)) return LCT_EALIGN;
+    uint64_t nb = 0, sf = 0;
+    if (!group_extent(count, n, *layout, &nb, &sf)) return LCT_EINVAL;
+    if (d_dense) {
+        std::vector<Range> rs;
+        for (uint32_t k = 0; k < count; ++k) {
+            if (n[k] == 0) continue;
+            if (!d_dense[k]) return LCT_EINVAL;
+            if (!aligned(d_dense[k], 16)) return LCT_EALIGN;
+            rs.push_back(rng(d_dense[k], n[k] * 2));
+        }
+        std::sort(rs.begin(), rs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+        for (size_t i = 1; i < rs.size(); ++i)
+            if (rs[i].lo < rs[i - 1].hi) return LCT_EALIAS;
+    }
+    lct_status st = check_arch();
+    if (st != LCT_OK) return st;
+    const GroupTableLayout t = group_table_layout(count, nb);
+    std::vector<uint8_t> host(t.bytes, 0);
+    auto *ent = reinterpret_cast<GroupEntry *>(host.data() + t.ent);
+    auto *enc = reinterpret_cast<EncTab *>(host.data() + t.enc);
+    auto *dec = reinterpret_cast<DecTab *>(host.data() + t.dec);
+    auto *owner = reinterpret_cast<uint32_t *>(host.data() + t.blk_tensor);
+    uint64_t b0 = 0, e0 = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        const uint64_t nbk = nblocks(n[k], *layout);
+        ent[k].dense = d_dense ? d_dense[k] : nullptr;
+        ent[k].n = n[k];
+        ent[k].e0 = e0;
+        ent[k].blk0 = (uint32_t)b0;
+        ent[k].nblk = (uint32_t)nbk;
+        fill_enc(cbs[k], &enc[k]);
+        fill_dec(cbs[k], &dec[k]);
+        for (uint64_t j = 0; j < nbk; ++j) owner[b0 + j] = k;
+        b0 += nbk;
+        e0 += round256(n[k]);
+    }
+    const hipError_t e = hipMemcpy(d_table, host.data(), t.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "group table copy");
+    out->count = count;
+    out->layout = *layout;
+    out->nblk = nb;
+    out->sf_bytes = sf;
+    out->shape_hash = shape_hash(count, n, *layout);
+    out->n = n;
+    out->d_dense = d_dense;
+    out->d_table = d_table;
+    return LCT_OK;
+}
+
+lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out) {
+    if (!g || !out || !layout_ok(g->layout)) return LCT_EINVAL;
+    out->nblk = g->nblk;
+    out->sf = g->sf_bytes;
+    out->pay = g->nblk * g->layout.cap_words * kStreams * 4;
+    out->cnt = g->nblk * kStreams * 2;
+    out->obase = (g->nblk + 1) * 8;
+    out->scratch = scr_bytes(g->nblk, ovf_cap);
+    out->fixed = out->sf + out->pay + out->cnt + out->obase;
+    return LCT_OK;
+}
+
+lct_status lct_group_tensor(const lct_group *g, const lct_tensor *all, uint32_t k, lct_tensor *out) {
+    if (!g || !all || !out || !g->n || k >= g->count) return LCT_EINVAL;
+    uint64_t b0 = 0, e0 = 0;
+    for (uint32_t j = 0; j < k; ++j) {
+        b0 += nblocks(g->n[j], g->layout);
+        e0 += round256(g->n[j]);
+    }
+    *out = *all;
+    out->n = g->n[k];
+    out->sf = all->sf + e0;
+    out->pay = all->pay + b0 * g->layout.cap_words * kStreams;
+    out->cnt = all->cnt + b0 * kStreams;
+    out->obase = all->obase + b0;
+    return LCT_OK;
+}
+
+lct_status lct_encode_group(const lct_group *g, const lct_tensor *all, void *stream) {
+    lct_status st = check_group(g, all, true);
+    if (st != LCT_OK) return st;
+    st = check_group_dense(*g, parts(*all, g->nblk));
+    if (st != LCT_OK) return st;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+    if (g->nblk == 0) return LCT_OK;
+    EncodeParams p;
+    memset(&p, 0, sizeof p);
+    p.n = all->n;
+    p.block_elems = g->layout.block_elems;
+    p.cap_words = g->layout.cap_words;
+    p.nblk = (uint32_t)g->nblk;
+    p.sf = all->sf;
+    p.pay = all->pay;
+    p.cnt = all->cnt;
+    p.obase = all->obase;
+    p.ovf = all->ovf;
+    p.ovf_cap = all->ovf_cap;
+    p.status = all->status;
+    p.scratch = (uint8_t *)all->scratch;
+    p.grp = group_ref(*g);
+    int e = launch_clear(p.scratch, g->nblk, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_encode(p, stream, true);
+    if (e != hipSuccess) return hip_fail(e, "group encode launch");
+    e = launch_scan(p.scratch, g->nblk, p.obase, p.ovf, p.ovf_cap, p.status, p.cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return LCT_OK;
+}
+
+lct_status lct_decode_group(const lct_group *g, const lct_tensor *all, void *stream) {
+    lct_status st = check_group(g, all, false);
+    if (st != LCT_OK) return st;
+    st = check_group_dense(*g, parts(*all, g->nblk));
+    if (st != LCT_OK) return st;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+    if (g->nblk == 0) return LCT_OK;
+    DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.sf = all->sf;
+    p.pay = all->pay;
+    p.cnt = all->cnt;
+    p.obase = all->obase;
+    p.ovf = all->ovf;
+    p.ovf_cap = all->ovf_cap;
+    p.n = all->n;
+    p.block_elems = g->layout.block_elems;
+    p.cap_words = g->layout.cap_words;
+    p.nblk = (uint32_t)g->nblk;
+    p.grp = group_ref(*g);
+    const int e = launch_decode(p, stream, true);
+    if (e != hipSuccess) return hip_fail(e, "group decode launch");
+    return LCT_OK;
+}
+
+lct_status lct_sgd_step_group(const lct_group *gw, const lct_tensor *w_all, const lct_group *gm,
+                              const lct_tensor *m_all, float eta, const lct_tensor *w_out,
+                              void *stream) {
+    lct_status st = check_group(gw, w_all, false);
+    if (st == LCT_OK) st = check_group(gm, m_all, false);
+    if (st == LCT_OK) st = check_group(gw, w_out, true);
+    if (st != LCT_OK) return st;
+    if (gm->shape_hash != gw->shape_hash || gm->count != gw->count || gm->nblk != gw->nblk ||
+        gm->sf_bytes != gw->sf_bytes)
+        return LCT_EINVAL;
+    for (uint32_t k = 0; k < gw->count; ++k)
+        if (gw->n[k] != gm->n[k]) return LCT_EINVAL;
+    if (gw->nblk == 0) return LCT_OK;
+    SgdParams p;
+    memset(&p, 0, sizeof p);
+    p.gw = group_ref(*gw);
+    p.gm = group_ref(*gm);
+    return sgd_run(p, *w_all, *m_all, *w_out, gw->nblk, eta, true, stream);
 }
 
 const char *lct_strerror(lct_status st) {

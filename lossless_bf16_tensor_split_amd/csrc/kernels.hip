@@ -747,14 +747,16 @@ constexpr uint32_t kEncWaves = 4;
 constexpr uint32_t kEncTab = 256, kEncWave0 = 2304;
 __host__ __device__ constexpr uint32_t enc_wave_bytes(uint32_t cap) { return (cap + 2) * ROWB; }
 
+// One lane's stream of a unit; xu and sfu point at the unit's first element
+// (stream 0, position 0) in the values and in the sign-fraction bytes.
 template <bool FULL, uint32_t CAPT>
 __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer &st, uint32_t n_s,
-                                              uint64_t r0) {
+                                              const uint16_t *xu, uint8_t *sfu) {
     const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t capbits = 32 * cap_of<CAPT>(p.cap_words);
-    const uint16_t *xs = p.x + r0 + s;
-    uint8_t *sfs = p.sf + r0 + s;
+    const uint16_t *xs = xu + s;
+    uint8_t *sfs = sfu + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
     double_buffered<Buf1>(
@@ -772,26 +774,48 @@ __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer &st,
         });
 }
 
-template <uint32_t CAPT>
+// Where a block's elements live: its values (encode source, decode target),
+// the offset of its sign-fraction bytes, and its length.  A flat tensor's
+// block b starts at element b * block_elems; in a group, block b belongs to
+// tensor blk_tensor[b] and starts (b - blk0) * block_elems into that tensor.
+struct BlockSpan {
+    uint16_t *dense;
+    uint64_t sf0;
+    uint32_t nb;
+};
+__device__ __forceinline__ BlockSpan flat_span(uint16_t *dense, uint64_t n, uint32_t block_elems, uint32_t b) {
+    const uint64_t r0 = (uint64_t)b * block_elems;
+    return {dense + r0, r0, (uint32_t)min<uint64_t>(block_elems, n - r0)};
+}
+__device__ __forceinline__ BlockSpan group_span(const GroupRef &g, uint32_t k, uint32_t block_elems, uint32_t b) {
+    const GroupEntry e = g.ent[k];
+    const uint64_t loc = (uint64_t)(b - e.blk0) * block_elems;
+    return {e.dense + loc, e.e0 + loc, (uint32_t)min<uint64_t>(block_elems, e.n - loc)};
+}
+
+template <uint32_t CAPT, bool GROUP>
 __global__ __launch_bounds__(64 * kEncWaves) void k_encode(const EncodeParams p) {
-    stage_enc(p.enc, kEncTab);
+    const uint32_t u = first_unit(kEncWaves);
+    const uint32_t b = unit_block(u), h = unit_part(u);
+    // a workgroup is one block, so one tensor of a group
+    const uint32_t k = GROUP ? p.grp.blk_tensor[min(b, p.nblk - 1)] : 0u;
+    stage_enc(GROUP ? p.grp.enc[k] : p.enc, kEncTab);
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const uint32_t out0 = kEncWave0 + wave_id() * enc_wave_bytes(cap);
-    const uint32_t u = first_unit(kEncWaves);
     if (u >= p.nblk * kMaxUnits) return;
-    const uint32_t b = unit_block(u), h = unit_part(u);
     for (uint32_t w = 0; w < cap; ++w) st32(out0 + w * ROWB + 4 * l, 0);
-    const uint64_t r0 = (uint64_t)b * p.block_elems;
-    const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+    const BlockSpan sp = GROUP ? group_span(p.grp, k, p.block_elems, b)
+                               : flat_span(const_cast<uint16_t *>(p.x), p.n, p.block_elems, b);
+    const uint32_t nb = sp.nb;
     const uint32_t n_s = stream_len(nb, h * US + l);
     Writer st;
     st.init(out0, l, n_s);
     if (nb == p.block_elems)
-        encode_stream<true, CAPT>(p, st, n_s, r0 + h * US);
+        encode_stream<true, CAPT>(p, st, n_s, sp.dense + h * US, p.sf + sp.sf0 + h * US);
     else
-        encode_stream<false, CAPT>(p, st, n_s, r0 + h * US);
+        encode_stream<false, CAPT>(p, st, n_s, sp.dense + h * US, p.sf + sp.sf0 + h * US);
     const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0};
     unit_finish(st, n_s, u, b, h, out0, o);
 }
@@ -805,12 +829,13 @@ __host__ __device__ constexpr uint32_t dec_wave_bytes(uint32_t cap) { return (ca
 
 template <bool FAST, uint32_t CAPT>
 __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t row0, uint32_t n_s,
-                                              uint32_t c_s, uint64_t r0, uint64_t sp0) {
+                                              uint32_t c_s, const uint8_t *sfu, uint16_t *yu,
+                                              uint64_t sp0) {
     const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const int32_t qmax = Reader::bias(row0) + 32 * (int32_t)cap_of<CAPT>(p.cap_words) - 2;
-    const uint8_t *sfs = p.sf + r0 + s;
-    uint16_t *ys = p.y + r0 + s;
+    const uint8_t *sfs = sfu + s;
+    uint16_t *ys = yu + s;
     Reader rd;
     rd.init(row0, s);
     double_buffered<Buf1>(
@@ -858,9 +883,12 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t ro
         });
 }
 
-template <uint32_t CAPT>
+template <uint32_t CAPT, bool GROUP>
 __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p) {
-    stage_dec(p.dec, kDecTab);
+    const uint32_t u = first_unit(kDecWaves);
+    const uint32_t b = unit_block(u), h = unit_part(u);
+    const uint32_t k = GROUP ? p.grp.blk_tensor[min(b, p.nblk - 1)] : 0u;
+    stage_dec(GROUP ? p.grp.dec[k] : p.dec, kDecTab);
     __syncthreads();
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
@@ -868,20 +896,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p)
     const uint32_t row0 = base + ROWB;
     st32(base + 4 * l, 0);                      // row -1
     st32(row0 + cap * ROWB + 4 * l, 0);         // row cap
-    const uint32_t u = first_unit(kDecWaves);
     if (u >= p.nblk * kMaxUnits) return;
-    const uint32_t b = unit_block(u), h = unit_part(u);
     rows_to_lds<false>(p.pay, row0, nullptr, 0, b, h, cap);
-    const uint64_t r0 = (uint64_t)b * p.block_elems;
-    const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+    const BlockSpan sp = GROUP ? group_span(p.grp, k, p.block_elems, b)
+                               : flat_span(p.y, p.n, p.block_elems, b);
+    const uint32_t nb = sp.nb;
     const uint32_t n_s = stream_len(nb, h * US + l);
     const uint64_t ob0 = p.obase[b], ob1 = p.obase[b + 1];
+    const uint8_t *sfu = p.sf + sp.sf0 + h * US;
+    uint16_t *yu = sp.dense + h * US;
     if (nb == p.block_elems && ob0 == ob1) {
-        decode_stream<true, CAPT>(p, row0, n_s, n_s, r0 + h * US, 0);
+        decode_stream<true, CAPT>(p, row0, n_s, n_s, sfu, yu, 0);
     } else {
         uint32_t c_s, excl;
         unit_spills(p.cnt + (uint64_t)b * NS, nb, h, c_s, excl);
-        decode_stream<false, CAPT>(p, row0, n_s, c_s, r0 + h * US, ob0 + excl);
+        decode_stream<false, CAPT>(p, row0, n_s, c_s, sfu, yu, ob0 + excl);
     }
 }
 
@@ -1243,14 +1272,17 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 
 // Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
 // a lane, AGPRs included.
-template <uint32_t CAPT>
+template <uint32_t CAPT, bool GROUP>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
-    stage_dec(p.wdec, kSgdWTab);
-    stage_dec(p.mdec, kSgdMTab);
-    stage_enc(p.wenc, kSgdETab);
+    if (!GROUP) {
+        stage_dec(p.wdec, kSgdWTab);
+        stage_dec(p.mdec, kSgdMTab);
+        stage_enc(p.wenc, kSgdETab);
+    }
     if (threadIdx.x < 2) st32(kSgdNone + 4 * threadIdx.x, 0);
     __syncthreads();
+    uint32_t staged = ~0u;   // the group tensor whose tables are in LDS
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap));
@@ -1271,13 +1303,34 @@ void k_sgd(const SgdParams p) {
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
+        uint32_t k = 0;
+        if (GROUP) {
+            // both waves work on one block, so on one tensor; the barrier
+            // above means neither still reads the tables being replaced
+            k = p.gw.blk_tensor[b];
+            if (k != staged) {
+                stage_dec(p.gw.dec[k], kSgdWTab);
+                stage_dec(p.gm.dec[k], kSgdMTab);
+                stage_enc(p.gw.enc[k], kSgdETab);
+                __syncthreads();
+                staged = k;
+            }
+        }
         // the block's overflow offsets are read along with the rows (one
         // memory round trip for both)
         const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
         const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
         rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
-        const uint64_t r0 = (uint64_t)b * p.block_elems;
-        const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+        uint64_t r0;
+        uint32_t nb;
+        if (GROUP) {
+            const BlockSpan sp = group_span(p.gw, k, p.block_elems, b);
+            r0 = sp.sf0;
+            nb = sp.nb;
+        } else {
+            r0 = (uint64_t)b * p.block_elems;
+            nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+        }
         const uint32_t n_s = stream_len(nb, h * US + l);
         const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
         // The result's rows go straight to memory: W's rows, which an update
@@ -1470,12 +1523,17 @@ struct ByCap {
         }
     }
 };
-template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C>); } };
-template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C>); } };
-template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C>); } };
+template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, false>); } };
+template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
+template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false>); } };
+template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
+template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
+template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true>); } };
 template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_momentum<C>); } };
 
-std::atomic<size_t> g_lds_granted[4][4];
+// per kernel (encode, decode, update, momentum, then the group encode, decode
+// and update) and capacity slot
+std::atomic<size_t> g_lds_granted[7][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
@@ -1528,19 +1586,22 @@ int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, 
     return (int)hipGetLastError();
 }
 
-int launch_encode(const EncodeParams &p, void *stream) {
-    return launch(ByCap<EncK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kEncWaves, false,
-                  encode_lds(p.cap_words), p, stream, g_lds_granted[0][cap_slot(p.cap_words)]);
+int launch_encode(const EncodeParams &p, void *stream, bool group) {
+    const void *fn = group ? ByCap<EncGK>::pick(p.cap_words) : ByCap<EncK>::pick(p.cap_words);
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kEncWaves, false, encode_lds(p.cap_words), p, stream,
+                  g_lds_granted[group ? 4 : 0][cap_slot(p.cap_words)]);
 }
 
-int launch_decode(const DecodeParams &p, void *stream) {
-    return launch(ByCap<DecK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kDecWaves, false,
-                  decode_lds(p.cap_words), p, stream, g_lds_granted[1][cap_slot(p.cap_words)]);
+int launch_decode(const DecodeParams &p, void *stream, bool group) {
+    const void *fn = group ? ByCap<DecGK>::pick(p.cap_words) : ByCap<DecK>::pick(p.cap_words);
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kDecWaves, false, decode_lds(p.cap_words), p, stream,
+                  g_lds_granted[group ? 5 : 1][cap_slot(p.cap_words)]);
 }
 
-int launch_sgd(const SgdParams &p, void *stream) {
-    return launch(ByCap<SgdK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true,
-                  sgd_lds(p.cap_words), p, stream, g_lds_granted[2][cap_slot(p.cap_words)]);
+int launch_sgd(const SgdParams &p, void *stream, bool group) {
+    const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+                  g_lds_granted[group ? 6 : 2][cap_slot(p.cap_words)]);
 }
 
 int launch_momentum(const MomParams &p, void *stream) {

@@ -71,6 +71,38 @@ struct DecTab {
     uint32_t esc_len;
 };
 
+// Tensor groups: tensor k's blocks follow tensor k-1's in one set of arrays
+// (pay, cnt, obase indexed by the group's block number; sf at the tensor's
+// own offset e0, a multiple of 256), one overflow region for all.  The device
+// table holds a record per tensor, the tensor of every block and every
+// tensor's code tables.
+struct GroupEntry {
+    uint16_t *dense;      // encode source and decode target (null: none)
+    uint64_t n;           // elements
+    uint64_t e0;          // first sign-fraction byte in the group's sf array
+    uint32_t blk0, nblk;  // first block in the group, blocks
+};
+struct GroupRef {
+    const GroupEntry *ent;
+    const EncTab *enc;
+    const DecTab *dec;
+    const uint32_t *blk_tensor;
+};
+// Offsets of the parts of a group's device table.
+struct GroupTableLayout {
+    uint64_t ent, enc, dec, blk_tensor, bytes;
+};
+inline GroupTableLayout group_table_layout(uint64_t count, uint64_t nblk) {
+    auto up = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    GroupTableLayout t;
+    t.ent = 0;
+    t.enc = up(t.ent + count * sizeof(GroupEntry));
+    t.dec = up(t.enc + count * sizeof(EncTab));
+    t.blk_tensor = up(t.dec + count * sizeof(DecTab));
+    t.bytes = up(t.blk_tensor + nblk * sizeof(uint32_t));
+    return t;
+}
+
 struct EncodeParams {
     const uint16_t *x;
     uint64_t n;
@@ -83,6 +115,7 @@ struct EncodeParams {
     uint64_t ovf_cap;
     uint32_t *status;
     uint8_t *scratch;
+    GroupRef grp;         // used by the group kernels only
     EncTab enc;
 };
 
@@ -96,6 +129,7 @@ struct DecodeParams {
     uint16_t *y;
     uint64_t n;
     uint32_t block_elems, cap_words, nblk, pad0;
+    GroupRef grp;         // used by the group kernels only
     DecTab dec;
 };
 
@@ -166,6 +200,7 @@ struct SgdParams {
     float neg_eta;
     uint32_t park_cnt;   // the result's counts overwrite W's: park them in scratch
     uint32_t pad1;
+    GroupRef gw, gm;     // used by the group kernel only (W's codes for W and W')
     EncTab wenc;
     DecTab wdec;
     DecTab mdec;
@@ -188,9 +223,9 @@ struct SampleParams {
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
                 uint32_t *status, uint16_t *cnt, void *stream);
-int launch_encode(const EncodeParams &p, void *stream);
-int launch_decode(const DecodeParams &p, void *stream);
-int launch_sgd(const SgdParams &p, void *stream);
+int launch_encode(const EncodeParams &p, void *stream, bool group = false);
+int launch_decode(const DecodeParams &p, void *stream, bool group = false);
+int launch_sgd(const SgdParams &p, void *stream, bool group = false);
 int launch_momentum(const MomParams &p, void *stream);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.

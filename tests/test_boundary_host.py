@@ -313,3 +313,60 @@ def test_reshift_and_recode_arguments_rejected_on_host(L):
               C.byref(o), C.byref(om), None) == L.EINVAL
     assert mr(C.byref(cb), C.byref(w), C.byref(cb), C.byref(m), C.c_void_p(om.pay), mu, eta,
               C.byref(base), C.byref(base), C.byref(o), C.byref(om), None) == L.EALIAS
+
+
+def test_group_host_side(L):
+    """Group sizes, member views and argument checks, all on the host (a fake
+    table address is never dereferenced: every call below fails its checks
+    before any launch, or launches nothing)."""
+    lay = L.layout(4096, 2)
+    ns = [3 * 4096 + 5, 0, 1, 255, 4097]
+    arr = (C.c_uint64 * len(ns))(*ns)
+    nbytes = C.c_uint64(0)
+    assert L.lib.lct_group_table_bytes(len(ns), arr, C.byref(lay), C.byref(nbytes)) == L.OK
+    nblk = sum(-(-n // 4096) for n in ns)
+    sf_bytes = sum(-(-n // 256) * 256 for n in ns)
+    assert nbytes.value % 256 == 0 and nbytes.value >= nblk * 4 + len(ns) * (32 + 1280 + 516)
+    assert L.lib.lct_group_table_bytes(1, None, C.byref(lay), C.byref(nbytes)) == L.EINVAL
+    bad_lay = L.layout(4096, 0)
+    assert L.lib.lct_group_table_bytes(1, arr, C.byref(bad_lay), C.byref(nbytes)) == L.EINVAL
+    cb = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    cbs = (L.Codebook * len(ns))(*([cb] * len(ns)))
+    out = L.Group()
+    table = C.c_void_p(0x2000_0000_0000)
+    bind = L.lib.lct_group_bind
+    assert bind(0, arr, C.byref(lay), cbs, None, table, C.byref(out)) == L.EINVAL
+    assert bind(len(ns), arr, C.byref(lay), cbs, None, C.c_void_p(0x2000_0000_0010), C.byref(out)) == L.EALIGN
+    dense = (C.c_void_p * len(ns))(*[0x3000_0000_0000 + k * 0x100000 for k in range(len(ns))])
+    dense[3] = dense[0] + 16                                     # overlaps tensor 0
+    assert bind(len(ns), arr, C.byref(lay), cbs, dense, table, C.byref(out)) == L.EALIAS
+    dense[3] = dense[0] + 0x80008                                # not 16-byte aligned
+    assert bind(len(ns), arr, C.byref(lay), cbs, dense, table, C.byref(out)) == L.EALIGN
+    # a group descriptor filled by hand, as bind would (its hash taken from a
+    # real bind is not available without a device: the checks that need it fail)
+    g = L.Group(len(ns), lay, nblk, sf_bytes, 0, C.cast(arr, C.c_void_p), None, table)
+    sz = L.Sizes()
+    assert L.lib.lct_group_sizes(C.byref(g), 100, C.byref(sz)) == L.OK
+    assert (sz.nblk, sz.sf, sz.pay, sz.cnt, sz.obase) == (nblk, sf_bytes, nblk * 2 * 1024, nblk * 512,
+                                                         (nblk + 1) * 8)
+    base = 0x1000_0000_0000
+    all_ = L._Tensor(sf_bytes, lay, C.c_void_p(base), C.c_void_p(base + 0x1000000),
+                     C.c_void_p(base + 0x2000000), C.c_void_p(base + 0x3000000), C.c_void_p(base + 0x4000000),
+                     100, C.c_void_p(base + 0x5000000), C.c_void_p(base + 0x6000000))
+    view = L._Tensor()
+    b0 = e0 = 0
+    for k, n in enumerate(ns):
+        assert L.lib.lct_group_tensor(C.byref(g), C.byref(all_), k, C.byref(view)) == L.OK
+        assert view.n == n and (view.sf or 0) == base + e0
+        assert (view.pay or 0) == base + 0x1000000 + b0 * 2 * 1024
+        assert (view.cnt or 0) == base + 0x2000000 + b0 * 512
+        assert (view.obase or 0) == base + 0x3000000 + b0 * 8
+        assert (view.ovf or 0) == base + 0x4000000 and view.ovf_cap == 100
+        b0 += -(-n // 4096)
+        e0 += -(-n // 256) * 256
+    assert L.lib.lct_group_tensor(C.byref(g), C.byref(all_), len(ns), C.byref(view)) == L.EINVAL
+    # the hand-made descriptor's fingerprint is wrong: every group call refuses it
+    assert L.lib.lct_encode_group(C.byref(g), C.byref(all_), None) == L.EINVAL
+    assert L.lib.lct_decode_group(C.byref(g), C.byref(all_), None) == L.EINVAL
+    assert L.lib.lct_sgd_step_group(C.byref(g), C.byref(all_), C.byref(g), C.byref(all_), C.c_float(1e-3),
+                                    C.byref(all_), None) == L.EINVAL
