@@ -10,12 +10,6 @@
 
 #include "lct_internal.h"
 
-namespace lct {
-size_t encode_lds(uint32_t cap);
-size_t decode_lds(uint32_t cap);
-size_t sgd_lds(uint32_t cap);
-}  // namespace lct
-
 namespace {
 
 using namespace lct;
@@ -174,6 +168,52 @@ lct_status check_group_dense(const lct_group &g, const Parts &p) {
     return LCT_OK;
 }
 
+// The buffers of an update: W (decoded, the product's other factor for a
+// dense operand), M (decoded second operand; null with a dense one), the
+// result.
+void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const lct_tensor &w_out,
+                uint64_t nb, float mul) {
+    p.w_sf = w_in.sf;
+    p.w_pay = w_in.pay;
+    p.w_cnt = w_in.cnt;
+    p.w_obase = w_in.obase;
+    p.w_ovf = w_in.ovf;
+    p.w_ovf_cap = w_in.ovf_cap;
+    if (m) {
+        p.m_sf = m->sf;
+        p.m_pay = m->pay;
+        p.m_cnt = m->cnt;
+        p.m_obase = m->obase;
+        p.m_ovf = m->ovf;
+        p.m_ovf_cap = m->ovf_cap;
+    }
+    p.o_sf = w_out.sf;
+    p.o_pay = w_out.pay;
+    p.o_cnt = w_out.cnt;
+    p.o_obase = w_out.obase;
+    p.o_ovf = w_out.ovf;
+    p.ovf_cap = w_out.ovf_cap;
+    p.status = w_out.status;
+    p.scratch = (uint8_t *)w_out.scratch;
+    p.n = w_in.n;
+    p.block_elems = w_in.layout.block_elems;
+    p.cap_words = w_in.layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.mul = mul;
+    p.park_cnt = p.o_cnt == p.w_cnt;
+}
+
+// Clear, update, scan.
+lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream) {
+    int e = launch_clear(p.scratch, nb, p.status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_sgd(p, stream, group);
+    if (e != hipSuccess) return hip_fail(e, "sgd launch");
+    e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return LCT_OK;
+}
+
 // Aliasing rules, parameters and launches of an update (a tensor, or a
 // group's storage when `group`); p's tables (or group references) are set.
 lct_status sgd_run(SgdParams &p, const lct_tensor &w_in, const lct_tensor &m, const lct_tensor &w_out,
@@ -199,39 +239,8 @@ lct_status sgd_run(SgdParams &p, const lct_tensor &w_in, const lct_tensor &m, co
         if (overlaps_any(r, pw, false) || overlaps_any(r, pm, false)) return LCT_EALIAS;
     lct_status st = check_arch();
     if (st != LCT_OK) return st;
-    p.w_sf = w_in.sf;
-    p.w_pay = w_in.pay;
-    p.w_cnt = w_in.cnt;
-    p.w_obase = w_in.obase;
-    p.w_ovf = w_in.ovf;
-    p.w_ovf_cap = w_in.ovf_cap;
-    p.m_sf = m.sf;
-    p.m_pay = m.pay;
-    p.m_cnt = m.cnt;
-    p.m_obase = m.obase;
-    p.m_ovf = m.ovf;
-    p.m_ovf_cap = m.ovf_cap;
-    p.o_sf = w_out.sf;
-    p.o_pay = w_out.pay;
-    p.o_cnt = w_out.cnt;
-    p.o_obase = w_out.obase;
-    p.o_ovf = w_out.ovf;
-    p.ovf_cap = w_out.ovf_cap;
-    p.status = w_out.status;
-    p.scratch = (uint8_t *)w_out.scratch;
-    p.n = w_in.n;
-    p.block_elems = w_in.layout.block_elems;
-    p.cap_words = w_in.layout.cap_words;
-    p.nblk = (uint32_t)nb;
-    p.neg_eta = -eta;
-    p.park_cnt = p.o_cnt == p.w_cnt;
-    int e = launch_clear(p.scratch, nb, p.status, stream);
-    if (e != hipSuccess) return hip_fail(e, "clear launch");
-    e = launch_sgd(p, stream, group);
-    if (e != hipSuccess) return hip_fail(e, "sgd launch");
-    e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
-    if (e != hipSuccess) return hip_fail(e, "scan launch");
-    return LCT_OK;
+    sgd_params(p, w_in, &m, w_out, nb, -eta);
+    return sgd_launch(p, nb, group, stream);
 }
 
 }  // namespace
@@ -523,57 +532,24 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
 
     const uint64_t nb = nblocks(w_in->n, w_in->layout);
     if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
-    MomParams p;
-    memset(&p, 0, sizeof p);
-    p.w_sf = w_in->sf;
-    p.w_pay = w_in->pay;
-    p.w_cnt = w_in->cnt;
-    p.w_obase = w_in->obase;
-    p.w_ovf = w_in->ovf;
-    p.w_ovf_cap = w_in->ovf_cap;
-    p.m_sf = m_in->sf;
-    p.m_pay = m_in->pay;
-    p.m_cnt = m_in->cnt;
-    p.m_obase = m_in->obase;
-    p.m_ovf = m_in->ovf;
-    p.m_ovf_cap = m_in->ovf_cap;
-    p.g = d_g;
-    auto out = [](const lct_tensor &t, const lct_tensor &in) {
-        MomOut o;
-        memset(&o, 0, sizeof o);
-        o.sf = t.sf;
-        o.pay = t.pay;
-        o.cnt = t.cnt;
-        o.obase = t.obase;
-        o.ovf = t.ovf;
-        o.ovf_cap = t.ovf_cap;
-        o.status = t.status;
-        o.scratch = (uint8_t *)t.scratch;
-        o.park_cnt = t.cnt == in.cnt;
-        return o;
-    };
-    p.ow = out(*w_out, *w_in);
-    p.om = out(*m_out, *m_in);
-    p.n = w_in->n;
-    p.block_elems = w_in->layout.block_elems;
-    p.cap_words = w_in->layout.cap_words;
-    p.nblk = (uint32_t)nb;
-    p.mu = mu;
-    p.neg_eta = -eta;
-    fill_enc(*cw_out, &p.wenc);
-    fill_enc(*cm_out, &p.menc);
-    fill_dec(*cw, &p.wdec);
-    fill_dec(*cm, &p.mdec);
-    int e = launch_clear(p.ow.scratch, nb, p.ow.status, stream);
-    if (e == hipSuccess) e = launch_clear(p.om.scratch, nb, p.om.status, stream);
-    if (e != hipSuccess) return hip_fail(e, "clear launch");
-    e = launch_momentum(p, stream);
-    if (e != hipSuccess) return hip_fail(e, "momentum launch");
-    e = launch_scan(p.ow.scratch, nb, p.ow.obase, p.ow.ovf, p.ow.ovf_cap, p.ow.status, p.ow.cnt, stream);
-    if (e == hipSuccess)
-        e = launch_scan(p.om.scratch, nb, p.om.obase, p.om.ovf, p.om.ovf_cap, p.om.status, p.om.cnt, stream);
-    if (e != hipSuccess) return hip_fail(e, "scan launch");
-    return LCT_OK;
+    // Two passes of the update kernel: M' = rne(mu * M + g) with the dense
+    // gradient as the second operand (M' encoded with cm_out), then
+    // W' = rne(W - eta * M') reading M' as stored.
+    SgdParams p1;
+    memset(&p1, 0, sizeof p1);
+    sgd_params(p1, *m_in, nullptr, *m_out, nb, mu);
+    p1.dense = d_g;
+    fill_enc(*cm_out, &p1.wenc);
+    fill_dec(*cm, &p1.wdec);
+    st = sgd_launch(p1, nb, false, stream);
+    if (st != LCT_OK) return st;
+    SgdParams p2;
+    memset(&p2, 0, sizeof p2);
+    sgd_params(p2, *w_in, m_out, *w_out, nb, -eta);
+    fill_enc(*cw_out, &p2.wenc);
+    fill_dec(*cw, &p2.wdec);
+    fill_dec(*cm_out, &p2.mdec);
+    return sgd_launch(p2, nb, false, stream);
 }
 
 // ---- groups

@@ -81,12 +81,14 @@ extern __shared__ uint32_t lds[];
 // accesses take it (plus a constant folded into the instruction) directly.
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x2 lds_u64;
 typedef __attribute__((address_space(3))) u32x4 lds_u128;
 __device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<lds_u32 *>(off); }
 __device__ __forceinline__ uint32_t ld8(uint32_t off) { return *reinterpret_cast<lds_u8 *>(off); }
+__device__ __forceinline__ uint32_t ld16(uint32_t off) { return *reinterpret_cast<lds_u16 *>(off); }
 __device__ __forceinline__ u32x2 ld64(uint32_t off) { return *reinterpret_cast<lds_u64 *>(off); }
 __device__ __forceinline__ u32x4 ld128(uint32_t off) { return *reinterpret_cast<lds_u128 *>(off); }
 __device__ __forceinline__ void st128(uint32_t off, u32x4 v) { *reinterpret_cast<lds_u128 *>(off) = v; }
@@ -931,25 +933,29 @@ constexpr uint32_t kSgdNoField = kSgdNone - kSgdETab;
 
 // A wave's region (from `base`): the slabs; W's zero row -1 and rows
 // 0..cap-1; a zero row (W's row cap and M's row -1); M's rows; a zero row.
-// The result's rows are not staged: they go to memory as they fill.
+// The result's rows are not staged: they go to memory as they fill.  With a
+// dense second operand (DENSE) its slab holds 2-byte values (twice the size)
+// and there are no M rows.
 struct SgdLayout {
     uint32_t sw, sm, z0, w0, z1, m0, z2, end;
-    __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base)
+    __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base, bool dense = false)
         : sw(base),
           sm(base + kSlabB),
-          z0(base + 2 * kSlabB),
+          z0(base + (dense ? 3 : 2) * kSlabB),
           w0(z0 + ROWB),
           z1(w0 + cap * ROWB),
           m0(z1 + ROWB),
-          z2(m0 + cap * ROWB),
+          z2(dense ? z1 : m0 + cap * ROWB),
           end(z2 + ROWB) {}
 };
-__host__ __device__ constexpr uint32_t sgd_wave_bytes(uint32_t cap) { return SgdLayout(cap, 0).end; }
+__host__ __device__ constexpr uint32_t sgd_wave_bytes(uint32_t cap, bool dense = false) {
+    return SgdLayout(cap, 0, dense).end;
+}
 
 // One element: rne_bf16(fmaf(-eta, m, w)) in bits 31..16 of the result (bits
 // 15..0 hold rounding garbage); a NaN gives 0x7FC0.
-__device__ __forceinline__ uint32_t sgd_round(uint32_t wf, uint32_t mf, float neg_eta) {
-    const float r = __builtin_fmaf(neg_eta, __uint_as_float(mf), __uint_as_float(wf));
+__device__ __forceinline__ uint32_t sgd_round(uint32_t wf, uint32_t mf, float a) {
+    const float r = __builtin_fmaf(a, __uint_as_float(mf), __uint_as_float(wf));
     const uint32_t u = __float_as_uint(r);
     const uint32_t R = u + 0x7FFFu + ((u >> 16) & 1u);
     return r != r ? 0x7FC00000u : R;
@@ -975,7 +981,7 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 
 // General path: partial blocks and inputs with spilled fields; byte-wide
 // accesses with per-element checks.
-template <uint32_t CAPT>
+template <uint32_t CAPT, bool DENSE>
 __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                    uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
                                                    uint64_t r0, uint64_t wsp, uint64_t msp) {
@@ -987,6 +993,7 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
     const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
     const uint8_t *wsf = p.w_sf + r0 + s;
     const uint8_t *msf = p.m_sf + r0 + s;
+    const uint16_t *gs = p.dense + r0 + s;
     uint8_t *osf = p.o_sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
@@ -997,7 +1004,10 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
         npos,
         [&](Buf2 &bf, uint32_t j0) {
             load_chunk<true>(bf.w, wsf, j0, n_s);
-            load_chunk<true>(bf.m, msf, j0, n_s);
+            if (DENSE)
+                load_chunk<true>(bf.m, gs, j0, n_s);
+            else
+                load_chunk<true>(bf.m, msf, j0, n_s);
         },
         [&](Buf2 &bf, uint32_t j0) {
             uint32_t e[CH];
@@ -1006,18 +1016,24 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
             for (uint32_t i = 0; i < CH; ++i) {
                 const uint32_t j = j0 + i;
                 uint32_t ew = rw.next(kSgdWTab);
-                uint32_t em = rm.next(kSgdMTab);
                 rw.q = min(rw.q, qwmax);
-                rm.q = min(rm.q, qmmax);
                 if (j >= cw_s && j < n_s) {
                     const uint64_t k = wsp + (j - cw_s);
                     ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
                 }
-                if (j >= cm_s && j < n_s) {
-                    const uint64_t k = msp + (j - cm_s);
-                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                uint32_t R;
+                if (DENSE) {
+                    // mu * M + g: the decoded tensor multiplies, the dense one adds
+                    R = sgd_round(bf.m[i] << 16, join32(bf.w[i], ew), p.mul);
+                } else {
+                    uint32_t em = rm.next(kSgdMTab);
+                    rm.q = min(rm.q, qmmax);
+                    if (j >= cm_s && j < n_s) {
+                        const uint64_t k = msp + (j - cm_s);
+                        em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                    }
+                    R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.mul);
                 }
-                const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.neg_eta);
                 if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
                 e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
             }
@@ -1042,11 +1058,13 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
 // position l/4, streams 16*(l%4).. of the unit, with one 16-byte load per
 // tensor and half, issued two halves ahead; the result's bytes overwrite W's
 // in the region and leave with one 16-byte store, half a half later.
+// A half's inputs on their way to LDS: W's sign-fraction bytes, and M's (or,
+// with a dense second operand, the first 16 of its 32 bytes, g1 the rest).
 struct HalfRegs {
-    u32x4 w, m;
+    u32x4 w, m, g1;
 };
 
-template <uint32_t CAPT>
+template <uint32_t CAPT, bool DENSE>
 __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                 uint64_t r0) {
     const uint32_t l = lane();
@@ -1065,7 +1083,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // dropped.
     const uint32_t span = (npos - 1) * NS + US;
     const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
-    const __amdgpu_buffer_rsrc_t rms = wave_rsrc(p.m_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rms =
+        DENSE ? wave_rsrc(p.dense + r0, 2 * span) : wave_rsrc(p.m_sf + r0, span);
     const __amdgpu_buffer_rsrc_t ros = wave_rsrc(p.o_sf + r0, span);
     constexpr uint32_t kNone = 0x80000000u;
     constexpr uint32_t kHalfB = CH * NS;          // sign-fraction bytes of a half
@@ -1079,9 +1098,26 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     auto load = [&](HalfRegs &r, uint32_t h) {
         const uint32_t o = h < nh ? h * kHalfB + g : kNone;
         r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
-        r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
+        if (DENSE) {
+            // the same elements' 2-byte values: 32 bytes (kNone stays out of range)
+            const uint32_t o2 = h < nh ? 2 * (h * kHalfB + g) : kNone;
+            r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o2, 0, 0));
+            r.g1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o2 + 16, 0, 0));
+        } else {
+            r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
+        }
     };
     auto region = [&](uint32_t h) { return (h & 1u) * kRegB; };
+    // a half's inputs into the region of half h
+    auto to_lds = [&](const HalfRegs &r, uint32_t h) {
+        st128(lay.sw + region(h) + mine, r.w);
+        if (DENSE) {
+            st128(lay.sm + 2 * region(h) + 2 * mine, r.m);
+            st128(lay.sm + 2 * region(h) + 2 * mine + 16, r.g1);
+        } else {
+            st128(lay.sm + region(h) + mine, r.m);
+        }
+    };
 
     // Carried from stage to stage: the inputs of the group whose arithmetic
     // comes next (sign-fraction words and decoded fields), the codes (and
@@ -1123,16 +1159,17 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         constexpr uint32_t GS = decltype(GS_)::value;
         const uint32_t rc = region(h) + GS * 4 * US;                       // group s's rows
         const uint32_t rp = (GS ? region(h) : region(h + 1)) + ((GS + 3) % 4) * 4 * US;   // group s-1's rows
-        uint32_t wsC[4], msC[4], ewC[4], emC[4];
+        uint32_t wsC[4], msC[4], ewC[4], emC[4] = {0u, 0u, 0u, 0u};
         uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
         const int32_t qw0 = rw.q, qm0 = rm.q;
         if (DEC) {
             winw = rw.window();
-            winm = rm.window();
+            if (!DENSE) winm = rm.window();
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
                 wsC[k] = ld32(lay.sw + rc + k * US + lw);
-                msC[k] = ld32(lay.sm + rc + k * US + lw);
+                // the dense operand's 2-byte value, or M's sign-fraction word
+                msC[k] = DENSE ? ld16(lay.sm + 2 * rc + 2 * k * US + 2 * l) : ld32(lay.sm + rc + k * US + lw);
             }
         }
         // the writer's group, with checks when some stream is near its end
@@ -1146,12 +1183,18 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
             if (DEC) {
                 wkw = winw >> cw;
-                wkm = winm >> cm;
                 enw = ld32(kSgdWTab + (wkw & 0x3FCu));
-                enm = ld32(kSgdMTab + (wkm & 0x3FCu));
+                if (!DENSE) {
+                    wkm = winm >> cm;
+                    enm = ld32(kSgdMTab + (wkm & 0x3FCu));
+                }
             }
-            r[k] = __builtin_fmaf(p.neg_eta, __uint_as_float(join32s(msP[k], emP[k], jsel)),
-                                  __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
+            if (DENSE)
+                r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(wsP[k], ewP[k], jsel)),
+                                      __uint_as_float(msP[k] << 16));
+            else
+                r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(msP[k], emP[k], jsel)),
+                                      __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
             nan |= r[k] != r[k];
             if (k & 1) {
                 uint32_t hh = cvt_bf16x2(r[k - 1], r[k]);
@@ -1168,36 +1211,46 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             }
             if (DEC) {
                 ewC[k] = (wkw << (enw & 31u)) | enw;
-                emC[k] = (wkm << (enm & 31u)) | enm;
                 cw += (enw >> 8) & 0xFFu;
-                cm += (enm >> 8) & 0xFFu;
+                if (!DENSE) {
+                    emC[k] = (wkm << (enm & 31u)) | enm;
+                    cm += (enm >> 8) & 0xFFu;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         if (DEC) {
             rw.q = min(rw.q + (int32_t)cw, qwmax);
-            rm.q = min(rm.q + (int32_t)cm, qmmax);
+            if (!DENSE) rm.q = min(rm.q + (int32_t)cm, qmmax);
         }
         if (__builtin_expect(!__all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
             if (DEC && !__all(max(cw, cm) <= 30)) {
                 // a window ran out: group s again, one field per window
                 rw.q = qw0;
-                rm.q = qm0;
+                if (!DENSE) rm.q = qm0;
 #pragma unroll
                 for (uint32_t k = 0; k < 4; ++k) {
                     ewC[k] = rw.next(kSgdWTab);
-                    emC[k] = rm.next(kSgdMTab);
                     rw.q = min(rw.q, qwmax);
-                    rm.q = min(rm.q, qmmax);
+                    if (!DENSE) {
+                        emC[k] = rm.next(kSgdMTab);
+                        rm.q = min(rm.q, qmmax);
+                    }
                 }
             }
             // group s-1 with the integer rounding (same fields; a NaN's byte
             // becomes the canonical one's)
 #pragma unroll
             for (uint32_t k = 0; k < 4; k += 2) {
-                const uint32_t R0 = sgd_round(join32s(wsP[k], ewP[k], jsel), join32s(msP[k], emP[k], jsel), p.neg_eta);
-                const uint32_t R1 =
-                    sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel), join32s(msP[k + 1], emP[k + 1], jsel), p.neg_eta);
+                uint32_t R0, R1;
+                if (DENSE) {
+                    R0 = sgd_round(msP[k] << 16, join32s(wsP[k], ewP[k], jsel), p.mul);
+                    R1 = sgd_round(msP[k + 1] << 16, join32s(wsP[k + 1], ewP[k + 1], jsel), p.mul);
+                } else {
+                    R0 = sgd_round(join32s(wsP[k], ewP[k], jsel), join32s(msP[k], emP[k], jsel), p.mul);
+                    R1 = sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel), join32s(msP[k + 1], emP[k + 1], jsel),
+                                   p.mul);
+                }
                 const uint32_t hh = (R0 >> 16) | (R1 & 0xFFFF0000u);
                 ep[k] = (hh >> 4) & 0x7F8u;
                 ep[k + 1] = (hh >> 20) & 0x7F8u;
@@ -1243,8 +1296,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         } else {
             outv = ld128(lay.sw + region(h - 1) + mine);
         }
-        st128(lay.sw + region(h + 1) + mine, next.w);
-        st128(lay.sm + region(h + 1) + mine, next.m);
+        to_lds(next, h + 1);
         load(next, h + 3);
         stage_fn(std::true_type{}, std::integral_constant<uint32_t, 1>{}, h);
         if (h != 0) __builtin_amdgcn_raw_buffer_store_b128(outv, ros, (h - 1) * kHalfB + g, 0, 0);
@@ -1254,8 +1306,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     HalfRegs a, b;
     load(a, 0);
     load(b, 1);
-    st128(lay.sw + mine, a.w);
-    st128(lay.sm + mine, a.m);
+    to_lds(a, 0);
     load(a, 2);
     for (uint32_t h = 0; h < nh; h += 2) {
         half(h, b);
@@ -1272,12 +1323,15 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 
 // Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
 // a lane, AGPRs included.
-template <uint32_t CAPT, bool GROUP>
+// DENSE: the second operand is the dense BF16 tensor p.dense and the result
+// is p.mul * W + dense (the momentum step's first pass, W standing for M).
+template <uint32_t CAPT, bool GROUP, bool DENSE>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
+    static_assert(!(GROUP && DENSE), "no dense operand in groups");
     if (!GROUP) {
         stage_dec(p.wdec, kSgdWTab);
-        stage_dec(p.mdec, kSgdMTab);
+        if (!DENSE) stage_dec(p.mdec, kSgdMTab);
         stage_enc(p.wenc, kSgdETab);
     }
     if (threadIdx.x < 2) st32(kSgdNone + 4 * threadIdx.x, 0);
@@ -1285,7 +1339,7 @@ void k_sgd(const SgdParams p) {
     uint32_t staged = ~0u;   // the group tensor whose tables are in LDS
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap));
+    const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap, DENSE), DENSE);
     st32(lay.z0 + 4 * l, 0);
     st32(lay.z1 + 4 * l, 0);
     st32(lay.z2 + 4 * l, 0);
@@ -1319,8 +1373,11 @@ void k_sgd(const SgdParams p) {
         // the block's overflow offsets are read along with the rows (one
         // memory round trip for both)
         const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
-        const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
-        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        const uint64_t mob = DENSE ? 0 : p.m_obase[b], mob1 = DENSE ? 0 : p.m_obase[b + 1];
+        if (DENSE)
+            rows_to_lds<false>(p.w_pay, lay.w0, nullptr, 0, b, h, cap);
+        else
+            rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
         uint64_t r0;
         uint32_t nb;
         if (GROUP) {
@@ -1339,12 +1396,12 @@ void k_sgd(const SgdParams p) {
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
         if (fast) {
-            sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
+            sgd_stream_full<CAPT, DENSE>(p, lay, st, r0 + h * US);
         } else {
-            uint32_t cw_s, cm_s, wex, mex;
+            uint32_t cw_s, cm_s = 0, wex, mex = 0;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
-            unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
-            sgd_stream_general<CAPT>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
+            if (!DENSE) unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
+            sgd_stream_general<CAPT, DENSE>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
         }
         // The result's counts overwrite W's when the update is in place:
         // other units of this block may still read W's (general path), so
@@ -1352,149 +1409,6 @@ void k_sgd(const SgdParams p) {
         const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
                         p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
         unit_finish(st, n_s, u, b, h, 0, o);
-    }
-}
-
-// ------------------------------------------------------------------ momentum step
-
-// SGD with momentum on compressed W and M (explainer, jargon entry "Optimizer
-// state": the momentum buffer is stored compressed like the weights; paragraph
-// on training traffic: decode, update, re-encode in one pass), with a dense
-// BF16 gradient g: m' = rne(fmaf(mu, m, g)), w' = rne(fmaf(-eta, m', w)).  Two
-// writers per lane (W' with W's code, M' with M's), each to its own payload
-// rows in memory and its own overflow staging; the units and the pairing of
-// waves are the update's.  Byte-wide accesses with per-element checks (the
-// update's general path, twice over).
-constexpr uint32_t kMomWaves = 2;
-constexpr uint32_t kMomWEnc = 0, kMomMEnc = 2048, kMomWDec = 4096, kMomMDec = 5120, kMomWave0 = 6144;
-
-// A wave's region: W's zero row -1 and rows 0..cap-1; a zero row (W's row cap
-// and M's row -1); M's rows; a zero row.
-struct MomLayout {
-    uint32_t z0, w0, z1, m0, z2, end;
-    __host__ __device__ constexpr MomLayout(uint32_t cap, uint32_t base)
-        : z0(base), w0(base + ROWB), z1(w0 + cap * ROWB), m0(z1 + ROWB), z2(m0 + cap * ROWB), end(z2 + ROWB) {}
-};
-__host__ __device__ constexpr uint32_t mom_wave_bytes(uint32_t cap) { return MomLayout(cap, 0).end; }
-
-struct Buf3 {
-    uint32_t w[CH], m[CH], g[CH];
-};
-
-template <uint32_t CAPT>
-__device__ __forceinline__ void mom_stream(const MomParams &p, const MomLayout &lay, PayWriter &stw,
-                                           PayWriter &stm, uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
-                                           uint64_t r0, uint64_t wsp, uint64_t msp) {
-    const uint32_t s = lane();
-    const uint32_t npos = p.block_elems / NS;
-    const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const uint32_t capbits = 32 * cap;
-    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
-    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
-    const uint8_t *wsf = p.w_sf + r0 + s;
-    const uint8_t *msf = p.m_sf + r0 + s;
-    const uint16_t *gs = p.g + r0 + s;
-    uint8_t *owsf = p.ow.sf + r0 + s;
-    uint8_t *omsf = p.om.sf + r0 + s;
-    uint64_t *wctr = reinterpret_cast<uint64_t *>(p.ow.scratch + kScrStage);
-    uint8_t *wstage = p.ow.scratch + scr_stage_offset(p.nblk);
-    uint64_t *mctr = reinterpret_cast<uint64_t *>(p.om.scratch + kScrStage);
-    uint8_t *mstage = p.om.scratch + scr_stage_offset(p.nblk);
-    Reader rw, rm;
-    rw.init(lay.w0, s);
-    rm.init(lay.m0, s);
-    double_buffered<Buf3>(
-        npos,
-        [&](Buf3 &bf, uint32_t j0) {
-            load_chunk<true>(bf.w, wsf, j0, n_s);
-            load_chunk<true>(bf.m, msf, j0, n_s);
-            load_chunk<true>(bf.g, gs, j0, n_s);
-        },
-        [&](Buf3 &bf, uint32_t j0) {
-            uint32_t ew8[CH], em8[CH];
-            uint8_t *ow = owsf + (size_t)j0 * NS;
-            uint8_t *om = omsf + (size_t)j0 * NS;
-#pragma unroll
-            for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + i;
-                uint32_t ew = rw.next(kMomWDec);
-                uint32_t em = rm.next(kMomMDec);
-                rw.q = min(rw.q, qwmax);
-                rm.q = min(rm.q, qmmax);
-                if (j >= cw_s && j < n_s) {
-                    const uint64_t k = wsp + (j - cw_s);
-                    ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
-                }
-                if (j >= cm_s && j < n_s) {
-                    const uint64_t k = msp + (j - cm_s);
-                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                }
-                // m' = rne(fmaf(mu, m, g)), then w' = rne(fmaf(-eta, m', w)) with m'
-                // as stored (results in bits 31..16)
-                const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], em), p.mu);
-                const uint32_t Rw = sgd_round(join32(bf.w[i], ew), Rm & 0xFFFF0000u, p.neg_eta);
-                if (j < n_s) {
-                    ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
-                    om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
-                }
-                ew8[i] = (Rw >> 20) & 0x7F8u;   // 8 * exponent field
-                em8[i] = (Rm >> 20) & 0x7F8u;
-            }
-            writer_chunk<true>(stw, ew8, j0, n_s, capbits, kMomWEnc);
-            writer_spill<true>(stw, ew8, j0, n_s, wctr, wstage, p.ow.ovf_cap);
-            writer_chunk<true>(stm, em8, j0, n_s, capbits, kMomMEnc);
-            writer_spill<true>(stm, em8, j0, n_s, mctr, mstage, p.om.ovf_cap);
-        });
-}
-
-template <uint32_t CAPT>
-__global__ __launch_bounds__(64 * kMomWaves) void k_momentum(const MomParams p) {
-    stage_dec(p.wdec, kMomWDec);
-    stage_dec(p.mdec, kMomMDec);
-    stage_enc(p.wenc, kMomWEnc);
-    stage_enc(p.menc, kMomMEnc);
-    __syncthreads();
-    const uint32_t l = lane();
-    const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const MomLayout lay(cap, kMomWave0 + wave_id() * mom_wave_bytes(cap));
-    st32(lay.z0 + 4 * l, 0);
-    st32(lay.z1 + 4 * l, 0);
-    st32(lay.z2 + 4 * l, 0);
-    const uint32_t nunits = p.nblk * kMaxUnits;
-    // An output in place over its input overwrites counts that other units of
-    // the block still read: they are parked and put in place by the scan.
-    uint16_t *wcnt = p.ow.park_cnt ? reinterpret_cast<uint16_t *>(p.ow.scratch + scr_cnt_offset(p.nblk))
-                                   : p.ow.cnt;
-    uint16_t *mcnt = p.om.park_cnt ? reinterpret_cast<uint16_t *>(p.om.scratch + scr_cnt_offset(p.nblk))
-                                   : p.om.cnt;
-    const uint32_t stride = gridDim.x * kMomWaves;
-    // the two waves of a workgroup take units 2i and 2i+1 of one block (whose
-    // sign-fraction bytes share lines) and meet at every unit; both take the
-    // same number of trips
-    static_assert(kMomWaves == 2 && kMaxUnits % kMomWaves == 0, "pairs of units per workgroup");
-    for (uint32_t u = first_unit(kMomWaves); u < nunits; u += stride) {
-        __builtin_amdgcn_s_barrier();
-        const uint32_t b = unit_block(u), h = unit_part(u);
-        const uint64_t wob = p.w_obase[b], mob = p.m_obase[b];
-        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
-        const uint64_t r0 = (uint64_t)b * p.block_elems;
-        const uint32_t nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
-        const uint32_t n_s = stream_len(nb, h * US + l);
-        uint32_t cw_s, cm_s, wex, mex;
-        unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
-        unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
-        // the results' rows go straight to memory: the inputs' rows, which a
-        // step in place overwrites, are all in LDS by now
-        PayWriter stw, stm;
-        stw.init(0, l, n_s);
-        stw.rows.init(p.ow.pay, b, h, cap);
-        stm.init(0, l, n_s);
-        stm.rows.init(p.om.pay, b, h, cap);
-        mom_stream<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
-        const UnitOut ow{p.ow.pay, wcnt, p.ow.scratch, p.nblk, p.ow.ovf_cap, cap, p.ow.park_cnt};
-        unit_finish(stw, n_s, u, b, h, 0, ow);
-        const UnitOut om{p.om.pay, mcnt, p.om.scratch, p.nblk, p.om.ovf_cap, cap, p.om.park_cnt};
-        unit_finish(stm, n_s, u, b, h, 0, om);
     }
 }
 
@@ -1525,14 +1439,14 @@ struct ByCap {
 };
 template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, false>); } };
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
-template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false>); } };
+template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, false>); } };
+template <uint32_t C> struct SgdDK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, true>); } };
 template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
 template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
-template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true>); } };
-template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_momentum<C>); } };
+template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, false>); } };
 
-// per kernel (encode, decode, update, momentum, then the group encode, decode
-// and update) and capacity slot
+// per kernel (encode, decode, update, the group encode, decode and update,
+// the update with a dense operand) and capacity slot
 std::atomic<size_t> g_lds_granted[7][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
@@ -1567,8 +1481,7 @@ int launch(const void *fn, uint64_t nunits, uint32_t waves, bool persistent, siz
 
 size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wave_bytes(cap); }
 size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
-size_t sgd_lds(uint32_t cap) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap); }
-size_t mom_lds(uint32_t cap) { return kMomWave0 + (size_t)kMomWaves * mom_wave_bytes(cap); }
+size_t sgd_lds(uint32_t cap, bool dense) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap, dense); }
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
@@ -1589,25 +1502,25 @@ int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, 
 int launch_encode(const EncodeParams &p, void *stream, bool group) {
     const void *fn = group ? ByCap<EncGK>::pick(p.cap_words) : ByCap<EncK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kEncWaves, false, encode_lds(p.cap_words), p, stream,
-                  g_lds_granted[group ? 4 : 0][cap_slot(p.cap_words)]);
+                  g_lds_granted[group ? 3 : 0][cap_slot(p.cap_words)]);
 }
 
 int launch_decode(const DecodeParams &p, void *stream, bool group) {
     const void *fn = group ? ByCap<DecGK>::pick(p.cap_words) : ByCap<DecK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kDecWaves, false, decode_lds(p.cap_words), p, stream,
-                  g_lds_granted[group ? 5 : 1][cap_slot(p.cap_words)]);
+                  g_lds_granted[group ? 4 : 1][cap_slot(p.cap_words)]);
 }
 
 int launch_sgd(const SgdParams &p, void *stream, bool group) {
-    const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
-    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
-                  g_lds_granted[group ? 6 : 2][cap_slot(p.cap_words)]);
+    const bool dense = p.dense != nullptr;
+    if (group && dense) return (int)hipErrorInvalidValue;
+    const void *fn = group   ? ByCap<SgdGK>::pick(p.cap_words)
+                     : dense ? ByCap<SgdDK>::pick(p.cap_words)
+                             : ByCap<SgdK>::pick(p.cap_words);
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words, dense), p, stream,
+                  g_lds_granted[group ? 5 : dense ? 6 : 2][cap_slot(p.cap_words)]);
 }
 
-int launch_momentum(const MomParams &p, void *stream) {
-    return launch(ByCap<MomK>::pick(p.cap_words), (uint64_t)p.nblk * kMaxUnits, kMomWaves, true,
-                  mom_lds(p.cap_words), p, stream, g_lds_granted[3][cap_slot(p.cap_words)]);
-}
 
 int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out) {
     hipStream_t st = (hipStream_t)stream;

@@ -133,45 +133,6 @@ struct DecodeParams {
     DecTab dec;
 };
 
-// One compressed output of the momentum step.
-struct MomOut {
-    uint8_t *sf;
-    uint32_t *pay;
-    uint16_t *cnt;
-    uint64_t *obase;
-    uint8_t *ovf;
-    uint64_t ovf_cap;
-    uint32_t *status;
-    uint8_t *scratch;
-    uint32_t park_cnt;   // the output's counts overwrite its input's: park them in scratch
-    uint32_t pad;
-};
-
-struct MomParams {
-    // inputs: W (codebook cw), M (codebook cm), dense gradient g
-    const uint8_t *w_sf;
-    const uint32_t *w_pay;
-    const uint16_t *w_cnt;
-    const uint64_t *w_obase;
-    const uint8_t *w_ovf;
-    uint64_t w_ovf_cap;
-    const uint8_t *m_sf;
-    const uint32_t *m_pay;
-    const uint16_t *m_cnt;
-    const uint64_t *m_obase;
-    const uint8_t *m_ovf;
-    uint64_t m_ovf_cap;
-    const uint16_t *g;
-    MomOut ow, om;       // outputs W' (codebook cw) and M' (codebook cm)
-    uint64_t n;
-    uint32_t block_elems, cap_words, nblk;
-    float mu, neg_eta;
-    uint32_t pad0;
-    EncTab wenc, menc;
-    DecTab wdec, mdec;
-};
-static_assert(sizeof(MomParams) <= 4096, "kernel arguments");
-
 struct SgdParams {
     // inputs: W (codebook cw) and M (codebook cm)
     const uint8_t *w_sf;
@@ -197,7 +158,11 @@ struct SgdParams {
     uint8_t *scratch;
     uint64_t n;
     uint32_t block_elems, cap_words, nblk;
-    float neg_eta;
+    // The product's factor: -eta for W - eta*M; mu for mu*M + g, where the
+    // decoded tensor (the W fields above) is M and the dense BF16 values
+    // below are g (the first pass of the momentum step).
+    float mul;
+    const uint16_t *dense;
     uint32_t park_cnt;   // the result's counts overwrite W's: park them in scratch
     uint32_t pad1;
     GroupRef gw, gm;     // used by the group kernel only (W's codes for W and W')
@@ -226,7 +191,6 @@ int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, 
 int launch_encode(const EncodeParams &p, void *stream, bool group = false);
 int launch_decode(const DecodeParams &p, void *stream, bool group = false);
 int launch_sgd(const SgdParams &p, void *stream, bool group = false);
-int launch_momentum(const MomParams &p, void *stream);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.
 int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);
