@@ -335,7 +335,11 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
 lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out);
 
 /* Tensor k of a group as an lct_tensor: views into the storage `all` (its
- * ovf, ovf_cap, status and scratch are all's). */
+ * ovf, ovf_cap, status and scratch are all's; its obase values point into
+ * the shared overflow region, so its spilled bytes are obase[nblk] -
+ * obase[0]).  Use it as the input of any call (decode, sample, an update's
+ * input); write a group only with the group calls, since a single-tensor
+ * output rewrites the overflow region from its start. */
 lct_status lct_group_tensor(const lct_group *g, const lct_tensor *all, uint32_t k, lct_tensor *out);
 
 /* Encode every tensor of the group from its dense buffer, in one launch

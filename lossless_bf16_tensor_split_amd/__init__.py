@@ -279,7 +279,12 @@ class LctTensor:
         return int(self.status[0].item()) & 0xFFFFFFFF
 
     def spilled(self) -> int:
-        return int(self.obase[-1].item())
+        """Spilled bytes of this tensor (a group member's offsets start where
+        the earlier members' spills end)."""
+        if self.obase.numel() == 1:
+            return 0
+        ends = self.obase[[0, -1]].cpu()
+        return int(ends[1]) - int(ends[0])
 
     def nbytes(self) -> int:
         return int(self.sizes.fixed) + self.spilled()

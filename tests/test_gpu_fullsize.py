@@ -1,0 +1,152 @@
+"""GPU parity at the full sizes of the largest workloads, in the launch
+configuration the benchmark times.
+
+- The 4.02B-element Qwen3-4B-shaped set (flat, CLEAN): codebooks, encode of W
+  and M, the fused update in place and the decode, checked against the oracle
+  on evenly spread sampled blocks (the last, partial block included) and by
+  properties that hold at any size.
+- The 162M-parameter GPT-style set as a group of its 50 tensors, each with its
+  own codebook, one step checked in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from test_gpu_group import storage_equal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lossless_bf16_tensor_split_amd as L
+    return L
+
+
+def dense_blocks(x, blocks, B, n):
+    """BF16 bits of the given blocks of a flat device tensor (the last may be partial)."""
+    out = []
+    v = x.view(torch.int16)
+    for b in blocks:
+        out.append(v[b * B:min((b + 1) * B, n)].cpu().numpy().view(np.uint16))
+    return out
+
+
+def block_of(t, b, n):
+    """Block b of a device tensor as a one-block oracle tensor (offset rebased)."""
+    import oracle
+    B, cw = t.layout.block_elems, t.layout.cap_words
+    nb = min(B, n - b * B)
+    ob = t.obase[b:b + 2].cpu().numpy().view(np.uint64)
+    spill = t.ovf[int(ob[0]):int(ob[1])].cpu().numpy()
+    return oracle.Compressed(nb, B, cw, t.sf[b * B:b * B + nb].cpu().numpy(),
+                             t.pay[b * cw * 256:(b + 1) * cw * 256].cpu().numpy().view(np.uint32),
+                             t.cnt[b * 256:(b + 1) * 256].cpu().numpy().view(np.uint16),
+                             np.array([0, ob[1] - ob[0]], np.uint64),
+                             spill if spill.size else np.zeros(1, np.uint8))
+
+
+def same_block(got, ref, what):
+    for f in ("sf", "pay", "cnt", "obase"):
+        assert np.array_equal(getattr(got, f), getattr(ref, f)), "%s %s" % (what, f)
+    assert np.array_equal(got.ovf[:got.spilled], ref.ovf[:ref.spilled]), what + " ovf"
+
+
+def test_qwen3_4b_flat_sampled(L, orc):
+    wspec, mspec, mw, mm, eta = synth.config5()
+    n = wspec.numel
+    dev = torch.device("cuda", 0)
+    lay = L.lct_layout_init(L.CLEAN)
+    B = lay.block_elems
+    w = synth.draw_device(wspec, dev)
+    m = synth.draw_device(mspec, dev)
+    cbw = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), w)
+    cbm = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), m)
+    pos = torch.as_tensor(orc.sample_positions(n).astype(np.int64), device=dev)
+    ocw = orc.codebook_from_sample(mw.family, mw.scale, mw.shape,
+                                   w.view(torch.int16)[pos].cpu().numpy().view(np.uint16))
+    ocm = orc.codebook_from_sample(mm.family, mm.scale, mm.shape,
+                                   m.view(torch.int16)[pos].cpu().numpy().view(np.uint16))
+    assert cbw.shift == ocw.shift and cbm.shift == ocm.shift
+    assert np.array_equal(np.frombuffer(bytes(cbw.code), np.uint32), ocw.code)
+    ovf_cap = n // 64
+    tw = L.alloc_tensor(n, lay, ovf_cap, dev)
+    tm = L.alloc_tensor(n, lay, ovf_cap, dev)
+    L.lct_encode(cbw, w, tw)
+    L.lct_encode(cbm, m, tm)
+    nblk = -(-n // B)
+    blocks = sorted(set(np.linspace(0, nblk - 1, 24).round().astype(int).tolist()))
+    assert blocks[-1] == nblk - 1 and n % B != 0           # the partial last block is in
+    wb, mb = dense_blocks(w, blocks, B, n), dense_blocks(m, blocks, B, n)
+    del m
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    assert tw.status_word() == 0 and tm.status_word() == 0
+    for t in (tw, tm):
+        ob = t.obase.cpu().numpy().view(np.uint64)
+        assert ob[0] == 0 and (np.diff(ob.astype(np.int64)) >= 0).all()
+    # encode, block by block
+    rw, rm = {}, {}
+    for b, xw, xm in zip(blocks, wb, mb):
+        rw[b] = orc.encode(ocw, xw, B, lay.cap_words)
+        rm[b] = orc.encode(ocm, xm, B, lay.cap_words)
+        same_block(block_of(tw, b, n), rw[b], "W block %d" % b)
+        same_block(block_of(tm, b, n), rm[b], "M block %d" % b)
+    # the update in place (overflow to a region of its own), block by block
+    out = L.alloc_tensor(n, lay, ovf_cap, dev, tw.scratch)
+    out.sf, out.pay, out.cnt, out.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+    L.lct_sgd_step(cbw, tw, cbm, tm, eta, out)
+    torch.cuda.synchronize()
+    assert out.status_word() == 0
+    for b in blocks:
+        ref = orc.sgd(ocw, rw[b], ocm, rm[b], eta)
+        same_block(block_of(out, b, n), ref, "W' block %d" % b)
+    # the decode
+    L.lct_decode(cbw, out, w)
+    for b, y in zip(blocks, dense_blocks(w, blocks, B, n)):
+        ref = orc.sgd(ocw, rw[b], ocm, rm[b], eta)
+        assert np.array_equal(y, orc.decode(ocw, ref)), "decode block %d" % b
+
+
+def test_gpt162m_as_a_group(L, orc):
+    """One step over every tensor of the 162M-parameter set as its own tensor
+    (50 tensors, each with its own codebook: the model's base code, the shift
+    from the tensor's sample), checked in full."""
+    ws, ms, mw, mm, eta = synth.config3()
+    wx = [synth.draw(s) for s in ws]
+    mx = [synth.draw(s) for s in ms]
+    ns = [len(x) for x in wx]
+    B, cw = synth.mode_layout(synth.CLEAN)
+    lay = L.layout(B, cw)
+    ocw = [orc.codebook_build(mw.family, mw.scale, mw.shape, x) for x in wx]
+    ocm = [orc.codebook_build(mm.family, mm.scale, mm.shape, x) for x in mx]
+    wd = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in wx]
+    md = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in mx]
+    basew = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), None)
+    basem = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), None)
+    cbw = [L.lct_codebook_reshift_dense(basew, t) for t in wd]
+    cbm = [L.lct_codebook_reshift_dense(basem, t) for t in md]
+    for c, o in zip(cbw + cbm, ocw + ocm):
+        assert c.shift == o.shift
+    gw = L.LctGroup(ns, lay, cbw, wd)
+    gm = L.LctGroup(ns, lay, cbm, md)
+    cap = sum(ns) // 64
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    rw = [orc.encode(c, x, B, cw) for c, x in zip(ocw, wx)]
+    rm = [orc.encode(c, x, B, cw) for c, x in zip(ocm, mx)]
+    storage_equal(L, gw, w_all, orc.group(rw, cap), ns, "W")
+    storage_equal(L, gm, m_all, orc.group(rm, cap), ns, "M")
+    out = gw.alloc_storage(cap, scratch=w_all.scratch)
+    out.sf, out.pay, out.cnt, out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+    L.lct_sgd_step_group(gw, w_all, gm, m_all, eta, out)
+    ref = [orc.sgd(ocw[k], rw[k], ocm[k], rm[k], eta) for k in range(len(ns))]
+    storage_equal(L, gw, out, orc.group(ref, cap), ns, "W'")
+    L.lct_decode_group(gw, out)
+    torch.cuda.synchronize()
+    for k, d in enumerate(wd):
+        assert np.array_equal(d.view(torch.int16).cpu().numpy().view(np.uint16), orc.decode(ocw[k], ref[k])), k
