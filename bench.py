@@ -371,6 +371,26 @@ def group_leg(L, dev, stream, w_dense, mspec, mw, mm, eta, lay, reps=5):
           for i, name in enumerate(["encode", "sgd", "decode"])}
     ms["step"] = float(np.mean([e[0].elapsed_time(e[3]) for e in timed]))
     spilled = [w_all.spilled(), m_all.spilled(), w_out.spilled()]
+    # the momentum step on the groups: the gradients bound as a third group's
+    # dense buffers, W' and M' in place with overflow regions of their own
+    g_dense = synth.draw_device(synth.TensorSpec("g.flat", (sum(ns),), 5300, "normal",
+                                                 {"sigma": mspec.args["sigma"] * math.sqrt(1 - 0.81)}), dev)
+    gg = L.LctGroup(ns, lay, cm, [g_dense[offs[k]:offs[k + 1]] for k in range(len(ns))])
+    m_out = gm.alloc_storage(cap)
+    m_out.sf, m_out.pay, m_out.cnt, m_out.obase = m_all.sf, m_all.pay, m_all.cnt, m_all.obase
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+    L.lct_encode_group(gw, w_all)
+    for e in mev:
+        # each call reads the previous call's results (W' and M' in place)
+        e[0].record(stream)
+        L.lct_momentum_step_group(gw, w_all, gm, m_all, gg, 0.9, eta, w_out, m_out)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        w_all, w_out = w_out, w_all
+        m_all, m_out = m_out, m_all
+    t_mom = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+    mom_status = [w_all.status_word(), m_all.status_word()]
+    del g_dense, gg, m_out
     # the same encodes as one call per tensor (each tensor its own storage)
     singles = [L.alloc_tensor(n, lay, max(n // 64, 1024), dev) for n in ns]
     for k in range(len(ns)):
@@ -390,6 +410,7 @@ def group_leg(L, dev, stream, w_dense, mspec, mw, mm, eta, lay, reps=5):
                         % (len(ns), nblk),
             "ms": {k: round(v, 4) for k, v in ms.items()},
             "elems_per_s": float("%.4g" % (sum(ns) / (ms["step"] / 1e3))),
+            "momentum_ms": round(t_mom, 4), "momentum_status": mom_status,
             "encode_one_call_per_tensor_ms": round(t_singles, 4),
             "codebooks_ms": round(1e3 * t_cb, 2), "spilled_bytes": spilled, "status": status}
 
@@ -524,6 +545,7 @@ def cpu_baseline_leg(cpu_in, gpu_out, cbw, cbm, mw, mm, eta, lay, n):
     import numpy as np
 
     import oracle
+    import synth
     B, cw = lay.block_elems, lay.cap_words
     g_enc, g_m, g_sgd, g_dec = gpu_out
     # the oracle's own codebooks, from the model and the shift sample
@@ -547,6 +569,17 @@ def cpu_baseline_leg(cpu_in, gpu_out, cbw, cbm, mw, mm, eta, lay, n):
                    for k in ("sf", "pay", "cnt", "obase")) \
             and np.array_equal(a.ovf[:a.spilled], b.ovf[:b.spilled])
 
+    # the momentum step's oracle on the first 512 sampled blocks (naive round
+    # trip: decode W and M, dense update, encode W' and M'), with a seeded
+    # host gradient of the spread the GPU leg uses
+    nm = min(512, len(cpu_in["blocks"])) * B
+    gm = synth.to_bf16_bits(np.random.default_rng(5100).normal(0.0, 1e-3 * (1 - 0.81) ** 0.5, nm))
+    mw_ = oracle.encode(ocw, cpu_in["w_blocks"][:nm], B, cw)
+    mm_ = oracle.encode(ocm, cpu_in["m_blocks"][:nm], B, cw)
+    t4 = time.perf_counter()
+    oracle.momentum(ocw, mw_, ocm, mm_, gm, 0.9, eta)
+    t_mom = time.perf_counter() - t4
+
     parity = {"codebooks": bool(same_cb), "encode_W": bool(same(g_enc, rw)),
               "encode_M": bool(same(g_m, rm)), "sgd_W": bool(same(g_sgd, ro)),
               "decode_W": bool(np.array_equal(g_dec, rd))}
@@ -556,7 +589,10 @@ def cpu_baseline_leg(cpu_in, gpu_out, cbw, cbm, mw, mm, eta, lay, n):
             "sample": "%d evenly spread full blocks of %d (%d elements): encode W, naive SGD "
                       "round trip, decode W'; serial C; encode %.2f s, sgd %.2f s, decode %.2f s"
                       % (len(cpu_in["blocks"]), n // B, ns, t1 - t0, t2 - t1, t3 - t2),
-            "parity_on_sample": parity}
+            "parity_on_sample": parity,
+            "next_ops": {"momentum": {"value": float("%.4g" % (nm / t_mom)), "unit": "elems/s",
+                                      "sample": "the first %d sampled blocks (%d elements), %.2f s"
+                                                % (nm // B, nm, t_mom)}}}
 
 
 if __name__ == "__main__":

@@ -360,6 +360,16 @@ lct_status lct_sgd_step_group(const lct_group *gw, const lct_tensor *w_all, cons
                               const lct_tensor *m_all, float eta, const lct_tensor *w_out,
                               void *stream);
 
+/* Momentum step on groups (lct_momentum_step per tensor, two launches of the
+ * update kernel): gw's codebooks for W and W', gm's for M and M', and the
+ * gradients are gg's dense buffers (gg's codebooks are not used).  The three
+ * groups must have the same layout and sizes; the gradients must not overlap
+ * an output.  Storage aliasing rules as lct_momentum_step.  Errors: as
+ * lct_momentum_step. */
+lct_status lct_momentum_step_group(const lct_group *gw, const lct_tensor *w_all, const lct_group *gm,
+                                   const lct_tensor *m_all, const lct_group *gg, float mu, float eta,
+                                   const lct_tensor *w_out, const lct_tensor *m_out, void *stream);
+
 /* Message for a status code (static string). */
 const char *lct_strerror(lct_status st);
 /* Text of the last HIP error seen on this thread (static per thread). */

@@ -23,6 +23,7 @@ Functions keep the C names:
     LctGroup(ns, layout, codebooks, dense)  (lct_group_table_bytes + lct_group_bind)
     lct_encode_group(g, all) / lct_decode_group(g, all)
     lct_sgd_step_group(gw, w_all, gm, m_all, eta, w_out)
+    lct_momentum_step_group(gw, w_all, gm, m_all, gg, mu, eta, w_out, m_out)
 plus ``alloc_tensor`` and the convenience wrappers ``encode`` / ``decode`` /
 ``sgd_step`` / ``momentum_step`` that allocate their outputs.
 """
@@ -46,7 +47,7 @@ EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_
             "lct_codebook_adapt", "lct_encode", "lct_decode",
             "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
             "lct_group_table_bytes", "lct_group_bind", "lct_group_sizes", "lct_group_tensor",
-            "lct_encode_group", "lct_decode_group", "lct_sgd_step_group",
+            "lct_encode_group", "lct_decode_group", "lct_sgd_step_group", "lct_momentum_step_group",
             "lct_strerror", "lct_last_hip_error"]
 
 
@@ -113,6 +114,7 @@ def _load():
     L.lct_encode_group.argtypes = [G, T, P]
     L.lct_decode_group.argtypes = [G, T, P]
     L.lct_sgd_step_group.argtypes = [G, T, G, T, C.c_float, T, P]
+    L.lct_momentum_step_group.argtypes = [G, T, G, T, G, C.c_float, C.c_float, T, T, P]
     L.lct_encode.argtypes = [C.POINTER(Codebook), P, C.POINTER(_Tensor), P]
     L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
     L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
@@ -467,3 +469,12 @@ def lct_sgd_step_group(gw: LctGroup, w_all: LctTensor, gm: LctGroup, m_all: LctT
     a, b, o = w_all.c(), m_all.c(), w_out.c()
     _check(lib.lct_sgd_step_group(C.byref(gw.g), C.byref(a), C.byref(gm.g), C.byref(b), eta,
                                   C.byref(o), _stream(stream)), "lct_sgd_step_group")
+
+
+def lct_momentum_step_group(gw: LctGroup, w_all: LctTensor, gm: LctGroup, m_all: LctTensor,
+                            gg: LctGroup, mu: float, eta: float, w_out: LctTensor, m_out: LctTensor,
+                            stream=None) -> None:
+    a, b, ow, om = w_all.c(), m_all.c(), w_out.c(), m_out.c()
+    _check(lib.lct_momentum_step_group(C.byref(gw.g), C.byref(a), C.byref(gm.g), C.byref(b), C.byref(gg.g),
+                                       mu, eta, C.byref(ow), C.byref(om), _stream(stream)),
+           "lct_momentum_step_group")

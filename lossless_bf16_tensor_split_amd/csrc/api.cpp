@@ -204,14 +204,43 @@ void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const
 }
 
 // Clear, update, scan.
-lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream) {
+lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream, bool dense = false) {
     int e = launch_clear(p.scratch, nb, p.status, stream);
     if (e != hipSuccess) return hip_fail(e, "clear launch");
-    e = launch_sgd(p, stream, group);
+    e = launch_sgd(p, stream, group, dense);
     if (e != hipSuccess) return hip_fail(e, "sgd launch");
     e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     return LCT_OK;
+}
+
+// The momentum step's aliasing rules (nb: the block count, ~0 for n's): the
+// outputs are disjoint from each other; each output's fixed side is its own
+// input's buffers, exactly, or disjoint from every input; its overflow,
+// status and scratch overlap no input.
+bool momentum_alias_ok(const lct_tensor &w_in, const lct_tensor &m_in, const lct_tensor &w_out,
+                       const lct_tensor &m_out, uint64_t nb) {
+    const Parts pw = parts(w_in, nb), pm = parts(m_in, nb), qw = parts(w_out, nb), qm = parts(m_out, nb);
+    const Range qws[] = {qw.sf, qw.pay, qw.cnt, qw.obase, qw.ovf, qw.status, qw.scratch};
+    for (const Range &r : qws)
+        if (overlaps_any(r, qm)) return false;
+    auto check_out = [&](const Parts &own, const Parts &other, const Parts &q) {
+        const Range in[] = {own.sf, own.pay, own.cnt, own.obase};
+        const Range out[] = {q.sf, q.pay, q.cnt, q.obase};
+        for (int i = 0; i < 4; ++i) {
+            for (int j = 0; j < 4; ++j) {
+                const bool same = i == j && in[i].lo == out[j].lo;
+                if (!same && overlap(in[i], out[j])) return false;
+            }
+            if (overlap(own.ovf, out[i])) return false;
+            if (overlaps_any(out[i], other, false)) return false;
+        }
+        const Range rest[] = {q.ovf, q.status, q.scratch};
+        for (const Range &r : rest)
+            if (overlaps_any(r, own, false) || overlaps_any(r, other, false)) return false;
+        return true;
+    };
+    return check_out(pw, pm, qw) && check_out(pm, pw, qm);
 }
 
 // Aliasing rules, parameters and launches of an update (a tensor, or a
@@ -500,33 +529,9 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
     if (st == LCT_OK) st = check_tensor(w_out, true);
     if (st == LCT_OK) st = check_tensor(m_out, true);
     if (st != LCT_OK) return st;
-    const Parts pw = parts(*w_in), pm = parts(*m_in), qw = parts(*w_out), qm = parts(*m_out);
-    const Range g = rng(d_g, w_in->n * 2);
-    // the gradient is read only: no output may overlap it
-    if (overlaps_any(g, qw) || overlaps_any(g, qm)) return LCT_EALIAS;
-    // the outputs are disjoint from each other
-    const Range qws[] = {qw.sf, qw.pay, qw.cnt, qw.obase, qw.ovf, qw.status, qw.scratch};
-    for (const Range &r : qws)
-        if (overlaps_any(r, qm)) return LCT_EALIAS;
-    // each output's fixed side is its own input's buffers, exactly, or disjoint
-    // from every input; its overflow, status and scratch overlap no input
-    auto check_out = [&](const Parts &own, const Parts &other, const Parts &q) {
-        const Range in[] = {own.sf, own.pay, own.cnt, own.obase};
-        const Range out[] = {q.sf, q.pay, q.cnt, q.obase};
-        for (int i = 0; i < 4; ++i) {
-            for (int j = 0; j < 4; ++j) {
-                const bool same = i == j && in[i].lo == out[j].lo;
-                if (!same && overlap(in[i], out[j])) return false;
-            }
-            if (overlap(own.ovf, out[i])) return false;
-            if (overlaps_any(out[i], other, false)) return false;
-        }
-        const Range rest[] = {q.ovf, q.status, q.scratch};
-        for (const Range &r : rest)
-            if (overlaps_any(r, own, false) || overlaps_any(r, other, false)) return false;
-        return true;
-    };
-    if (!check_out(pw, pm, qw) || !check_out(pm, pw, qm)) return LCT_EALIAS;
+    if (overlaps_any(rng(d_g, w_in->n * 2), parts(*w_out)) || overlaps_any(rng(d_g, w_in->n * 2), parts(*m_out)))
+        return LCT_EALIAS;   // the gradient is read only: no output may overlap it
+    if (!momentum_alias_ok(*w_in, *m_in, *w_out, *m_out, ~0ull)) return LCT_EALIAS;
     st = check_arch();
     if (st != LCT_OK) return st;
 
@@ -541,7 +546,7 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
     p1.dense = d_g;
     fill_enc(*cm_out, &p1.wenc);
     fill_dec(*cm, &p1.wdec);
-    st = sgd_launch(p1, nb, false, stream);
+    st = sgd_launch(p1, nb, false, stream, true);
     if (st != LCT_OK) return st;
     SgdParams p2;
     memset(&p2, 0, sizeof p2);
@@ -722,6 +727,46 @@ lct_status lct_sgd_step_group(const lct_group *gw, const lct_tensor *w_all, cons
     p.gw = group_ref(*gw);
     p.gm = group_ref(*gm);
     return sgd_run(p, *w_all, *m_all, *w_out, gw->nblk, eta, true, stream);
+}
+
+lct_status lct_momentum_step_group(const lct_group *gw, const lct_tensor *w_all, const lct_group *gm,
+                                   const lct_tensor *m_all, const lct_group *gg, float mu, float eta,
+                                   const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
+    lct_status st = check_group(gw, w_all, false);
+    if (st == LCT_OK) st = check_group(gm, m_all, false);
+    if (st == LCT_OK) st = check_group(gw, w_out, true);
+    if (st == LCT_OK) st = check_group(gm, m_out, true);
+    if (st != LCT_OK) return st;
+    if (!gg || !gg->d_table || !gg->n) return LCT_EINVAL;
+    for (const lct_group *o : {gm, gg}) {
+        if (o->shape_hash != gw->shape_hash || o->count != gw->count || o->nblk != gw->nblk ||
+            o->sf_bytes != gw->sf_bytes)
+            return LCT_EINVAL;
+        for (uint32_t k = 0; k < gw->count; ++k)
+            if (o->n[k] != gw->n[k]) return LCT_EINVAL;
+    }
+    // the gradients (gg's dense buffers) are read only: no output may overlap them
+    st = check_group_dense(*gg, parts(*w_out, gw->nblk));
+    if (st == LCT_OK) st = check_group_dense(*gg, parts(*m_out, gw->nblk));
+    if (st != LCT_OK) return st;
+    if (!momentum_alias_ok(*w_all, *m_all, *w_out, *m_out, gw->nblk)) return LCT_EALIAS;
+    st = check_arch();
+    if (st != LCT_OK) return st;
+    if (gw->nblk == 0) return LCT_OK;
+    const uint64_t nb = gw->nblk;
+    SgdParams p1;
+    memset(&p1, 0, sizeof p1);
+    sgd_params(p1, *m_all, nullptr, *m_out, nb, mu);
+    p1.gw = group_ref(*gm);
+    p1.gm = group_ref(*gg);
+    st = sgd_launch(p1, nb, true, stream, true);
+    if (st != LCT_OK) return st;
+    SgdParams p2;
+    memset(&p2, 0, sizeof p2);
+    sgd_params(p2, *w_all, m_out, *w_out, nb, -eta);
+    p2.gw = group_ref(*gw);
+    p2.gm = group_ref(*gm);
+    return sgd_launch(p2, nb, true, stream);
 }
 
 const char *lct_strerror(lct_status st) {

@@ -984,7 +984,8 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 template <uint32_t CAPT, bool DENSE>
 __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                    uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
-                                                   uint64_t r0, uint64_t wsp, uint64_t msp) {
+                                                   uint64_t r0, const uint16_t *gu, uint64_t wsp,
+                                                   uint64_t msp) {
     const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
@@ -993,7 +994,7 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
     const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
     const uint8_t *wsf = p.w_sf + r0 + s;
     const uint8_t *msf = p.m_sf + r0 + s;
-    const uint16_t *gs = p.dense + r0 + s;
+    const uint16_t *gs = gu + s;
     uint8_t *osf = p.o_sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
@@ -1066,7 +1067,7 @@ struct HalfRegs {
 
 template <uint32_t CAPT, bool DENSE>
 __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
-                                                uint64_t r0) {
+                                                uint64_t r0, const uint16_t *gu) {
     const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t nh = npos / CH;                // halves (the block size is a multiple of 4096)
@@ -1084,7 +1085,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     const uint32_t span = (npos - 1) * NS + US;
     const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
     const __amdgpu_buffer_rsrc_t rms =
-        DENSE ? wave_rsrc(p.dense + r0, 2 * span) : wave_rsrc(p.m_sf + r0, span);
+        DENSE ? wave_rsrc(gu, 2 * span) : wave_rsrc(p.m_sf + r0, span);
     const __amdgpu_buffer_rsrc_t ros = wave_rsrc(p.o_sf + r0, span);
     constexpr uint32_t kNone = 0x80000000u;
     constexpr uint32_t kHalfB = CH * NS;          // sign-fraction bytes of a half
@@ -1328,7 +1329,6 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 template <uint32_t CAPT, bool GROUP, bool DENSE>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
-    static_assert(!(GROUP && DENSE), "no dense operand in groups");
     if (!GROUP) {
         stage_dec(p.wdec, kSgdWTab);
         if (!DENSE) stage_dec(p.mdec, kSgdMTab);
@@ -1364,7 +1364,7 @@ void k_sgd(const SgdParams p) {
             k = p.gw.blk_tensor[b];
             if (k != staged) {
                 stage_dec(p.gw.dec[k], kSgdWTab);
-                stage_dec(p.gm.dec[k], kSgdMTab);
+                if (!DENSE) stage_dec(p.gm.dec[k], kSgdMTab);
                 stage_enc(p.gw.enc[k], kSgdETab);
                 __syncthreads();
                 staged = k;
@@ -1380,13 +1380,17 @@ void k_sgd(const SgdParams p) {
             rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
         uint64_t r0;
         uint32_t nb;
+        const uint16_t *gu = nullptr;   // the dense operand's unit (DENSE)
         if (GROUP) {
             const BlockSpan sp = group_span(p.gw, k, p.block_elems, b);
             r0 = sp.sf0;
             nb = sp.nb;
+            // a group's dense operand: the buffers bound to p.gm, same sizes
+            if (DENSE) gu = group_span(p.gm, k, p.block_elems, b).dense + h * US;
         } else {
             r0 = (uint64_t)b * p.block_elems;
             nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+            if (DENSE) gu = p.dense + r0 + h * US;
         }
         const uint32_t n_s = stream_len(nb, h * US + l);
         const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
@@ -1396,12 +1400,12 @@ void k_sgd(const SgdParams p) {
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
         if (fast) {
-            sgd_stream_full<CAPT, DENSE>(p, lay, st, r0 + h * US);
+            sgd_stream_full<CAPT, DENSE>(p, lay, st, r0 + h * US, gu);
         } else {
             uint32_t cw_s, cm_s = 0, wex, mex = 0;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
             if (!DENSE) unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
-            sgd_stream_general<CAPT, DENSE>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
+            sgd_stream_general<CAPT, DENSE>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
         }
         // The result's counts overwrite W's when the update is in place:
         // other units of this block may still read W's (general path), so
@@ -1441,13 +1445,14 @@ template <uint32_t C> struct EncK { static const void *fn() { return reinterpret
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
 template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, false>); } };
 template <uint32_t C> struct SgdDK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, true>); } };
+template <uint32_t C> struct SgdGDK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, true>); } };
 template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
 template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
 template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, false>); } };
 
 // per kernel (encode, decode, update, the group encode, decode and update,
-// the update with a dense operand) and capacity slot
-std::atomic<size_t> g_lds_granted[7][4];
+// the update with a dense operand, alone and in a group) and capacity slot
+std::atomic<size_t> g_lds_granted[8][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
@@ -1511,14 +1516,12 @@ int launch_decode(const DecodeParams &p, void *stream, bool group) {
                   g_lds_granted[group ? 4 : 1][cap_slot(p.cap_words)]);
 }
 
-int launch_sgd(const SgdParams &p, void *stream, bool group) {
-    const bool dense = p.dense != nullptr;
-    if (group && dense) return (int)hipErrorInvalidValue;
-    const void *fn = group   ? ByCap<SgdGK>::pick(p.cap_words)
-                     : dense ? ByCap<SgdDK>::pick(p.cap_words)
-                             : ByCap<SgdK>::pick(p.cap_words);
+int launch_sgd(const SgdParams &p, void *stream, bool group, bool dense) {
+    const void *fn = group ? (dense ? ByCap<SgdGDK>::pick(p.cap_words) : ByCap<SgdGK>::pick(p.cap_words))
+                           : (dense ? ByCap<SgdDK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words));
+    const int slot = group ? (dense ? 7 : 5) : (dense ? 6 : 2);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words, dense), p, stream,
-                  g_lds_granted[group ? 5 : dense ? 6 : 2][cap_slot(p.cap_words)]);
+                  g_lds_granted[slot][cap_slot(p.cap_words)]);
 }
 
 

@@ -165,7 +165,8 @@ struct SgdParams {
     const uint16_t *dense;
     uint32_t park_cnt;   // the result's counts overwrite W's: park them in scratch
     uint32_t pad1;
-    GroupRef gw, gm;     // used by the group kernel only (W's codes for W and W')
+    GroupRef gw, gm;     // used by the group kernels only (W's codes for W and W';
+                         // M's for M, or the dense operand's buffers)
     EncTab wenc;
     DecTab wdec;
     DecTab mdec;
@@ -190,7 +191,9 @@ int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, 
                 uint32_t *status, uint16_t *cnt, void *stream);
 int launch_encode(const EncodeParams &p, void *stream, bool group = false);
 int launch_decode(const DecodeParams &p, void *stream, bool group = false);
-int launch_sgd(const SgdParams &p, void *stream, bool group = false);
+// dense: the second operand is dense (p.dense, or in a group the buffers
+// bound to p.gm); the product is p.mul * W + dense
+int launch_sgd(const SgdParams &p, void *stream, bool group = false, bool dense = false);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.
 int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);

@@ -370,3 +370,6 @@ def test_group_host_side(L):
     assert L.lib.lct_decode_group(C.byref(g), C.byref(all_), None) == L.EINVAL
     assert L.lib.lct_sgd_step_group(C.byref(g), C.byref(all_), C.byref(g), C.byref(all_), C.c_float(1e-3),
                                     C.byref(all_), None) == L.EINVAL
+    assert L.lib.lct_momentum_step_group(C.byref(g), C.byref(all_), C.byref(g), C.byref(all_), C.byref(g),
+                                         C.c_float(0.9), C.c_float(1e-3), C.byref(all_), C.byref(all_),
+                                         None) == L.EINVAL

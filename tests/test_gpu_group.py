@@ -136,3 +136,41 @@ def test_group_sgd(L, orc, B, cw, inplace):
     other = L.LctGroup(ns[:-1] + [ns[-1] + 1], lay, [lib_cb(c) for c in ocm], None)
     with pytest.raises(L.LctError):
         L.lct_sgd_step_group(gw, w_all, other, other.alloc_storage(cap), 1e-3, out)
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (8192, 3)])
+def test_group_momentum(L, orc, B, cw, inplace):
+    """Momentum step on groups: W and M with per-tensor codebooks, the
+    gradients bound as a third group's dense buffers."""
+    ns = [65536 + 300, 2 * 65536, 7, 0, 100000]
+    g = np.random.default_rng(9700 + cw)
+    ws = [synth.to_bf16_bits(g.normal(0, 0.02 * (k + 1), n)) for k, n in enumerate(ns)]
+    ms = [synth.to_bf16_bits(g.normal(0, 1e-3 * (k + 1), n)) for k, n in enumerate(ns)]
+    gs = [synth.to_bf16_bits(g.normal(0, 4e-4 * (k + 1), n)) for k, n in enumerate(ns)]
+    ocw = [orc.codebook_build(0, 0.02 * (k + 1), 0.0, w) for k, w in enumerate(ws)]
+    ocm = [orc.codebook_build(0, 1e-3 * (k + 1), 0.0, m) for k, m in enumerate(ms)]
+    lib_cb = lambda c: L.lct_codebook_from_lengths(list(c.len_base), c.esc_len, c.shift)
+    lay = L.layout(B, cw)
+    todev = lambda x: (dev(x).view(torch.bfloat16) if len(x)
+                       else torch.empty(8, dtype=torch.bfloat16, device="cuda"))
+    wd, md, gd = [todev(x) for x in ws], [todev(x) for x in ms], [todev(x) for x in gs]
+    gw = L.LctGroup(ns, lay, [lib_cb(c) for c in ocw], wd)
+    gm = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], md)
+    gg = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], gd)
+    cap = sum(ns)
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    rw = [orc.encode(c, x, B, cw) for c, x in zip(ocw, ws)]
+    rm = [orc.encode(c, x, B, cw) for c, x in zip(ocm, ms)]
+    refs = [orc.momentum(ocw[k], rw[k], ocm[k], rm[k], gs[k], 0.9, 1e-3) for k in range(len(ns))]
+    w_out, m_out = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    if inplace:
+        w_out.sf, w_out.pay, w_out.cnt, w_out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+        m_out.sf, m_out.pay, m_out.cnt, m_out.obase = m_all.sf, m_all.pay, m_all.cnt, m_all.obase
+    L.lct_momentum_step_group(gw, w_all, gm, m_all, gg, 0.9, 1e-3, w_out, m_out)
+    storage_equal(L, gw, w_out, orc.group([r[0] for r in refs], cap), ns, "W' inplace=%s" % inplace)
+    storage_equal(L, gm, m_out, orc.group([r[1] for r in refs], cap), ns, "M' inplace=%s" % inplace)
+    if cw == 3:
+        assert sum(r[1].spilled for r in refs) > 0
