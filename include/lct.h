@@ -331,6 +331,21 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
                           const lct_codebook *cbs, uint16_t *const *d_dense, void *d_table,
                           lct_group *out);
 
+/* A one-tensor group whose codebook is fitted on the device, for callers
+ * that must not wait for it (a tensor saved for backward): the shift of the
+ * dense tensor's sample over base's base code is chosen on the device, as
+ * lct_codebook_reshift_dense chooses it, and the shifted code's tables are
+ * built there and written to d_table (lct_group_table_bytes(1, n, layout)
+ * bytes, 256-byte aligned) with the tensor's record.  n and d_dense are
+ * one-element host arrays owned by the caller (kept in *out); d_shift (device
+ * int32, may be NULL) receives the shift, so that the host codebook
+ * (lct_codebook_from_lengths(base->len_base, base->esc_len, shift)) can be
+ * made once it is read.  Enqueues only.  Errors: LCT_EINVAL, LCT_EALIGN,
+ * LCT_EARCH, LCT_EHIP. */
+lct_status lct_group_fit(const lct_codebook *base, const uint64_t *n, uint16_t *const *d_dense,
+                         const lct_layout *layout, void *d_table, int32_t *d_shift, void *stream,
+                         lct_group *out);
+
 /* Sizes of a group's storage arrays (as lct_sizes for one tensor). */
 lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out);
 

@@ -46,7 +46,7 @@ EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_
             "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_reshift_dense",
             "lct_codebook_adapt", "lct_encode", "lct_decode",
             "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
-            "lct_group_table_bytes", "lct_group_bind", "lct_group_sizes", "lct_group_tensor",
+            "lct_group_table_bytes", "lct_group_bind", "lct_group_fit", "lct_group_sizes", "lct_group_tensor",
             "lct_encode_group", "lct_decode_group", "lct_sgd_step_group", "lct_momentum_step_group",
             "lct_strerror", "lct_last_hip_error"]
 
@@ -109,6 +109,7 @@ def _load():
     G = C.POINTER(Group)
     L.lct_group_table_bytes.argtypes = [C.c_uint32, P, C.POINTER(Layout), C.POINTER(u64)]
     L.lct_group_bind.argtypes = [C.c_uint32, P, C.POINTER(Layout), P, P, P, G]
+    L.lct_group_fit.argtypes = [CB, P, P, C.POINTER(Layout), P, P, P, G]
     L.lct_group_sizes.argtypes = [G, u64, C.POINTER(Sizes)]
     L.lct_group_tensor.argtypes = [G, T, C.c_uint32, T]
     L.lct_encode_group.argtypes = [G, T, P]
@@ -396,7 +397,11 @@ class LctGroup:
     """A bound group: the device table, the host arrays the C struct points
     at (kept alive here), the codebooks and the dense tensors."""
 
-    def __init__(self, ns, lay: Layout, codebooks, dense=None, device="cuda"):
+    def __init__(self, ns, lay: Layout, codebooks, dense=None, device="cuda", fit=False, shift=None,
+                 stream=None):
+        """fit: one tensor (ns[0] elements, dense[0]) whose codebook is fitted
+        on the device from codebooks[0]'s base code (lct_group_fit); the shift
+        goes to the device int32 tensor `shift`."""
         count = len(ns)
         if len(codebooks) != count or (dense is not None and len(dense) != count):
             raise ValueError("one codebook (and one dense tensor) per size")
@@ -414,27 +419,39 @@ class LctGroup:
                "lct_group_table_bytes")
         self.table = torch.empty(max(int(nbytes.value), 256), dtype=torch.uint8, device=device)
         self.g = Group()
-        _check(lib.lct_group_bind(count, self.ns, C.byref(self.layout), self.codebooks,
-                                  self.dense_ptrs, _ptr(self.table), C.byref(self.g)), "lct_group_bind")
+        if fit:
+            if count != 1 or dense is None:
+                raise ValueError("a fitted group holds one tensor with its dense buffer")
+            _check(lib.lct_group_fit(C.byref(self.codebooks[0]), self.ns, self.dense_ptrs, C.byref(self.layout),
+                                     _ptr(self.table), _ptr(shift), _stream(stream), C.byref(self.g)),
+                   "lct_group_fit")
+        else:
+            _check(lib.lct_group_bind(count, self.ns, C.byref(self.layout), self.codebooks,
+                                      self.dense_ptrs, _ptr(self.table), C.byref(self.g)), "lct_group_bind")
 
     def sizes(self, ovf_cap: int = 0) -> Sizes:
         out = Sizes()
         _check(lib.lct_group_sizes(C.byref(self.g), ovf_cap, C.byref(out)), "lct_group_sizes")
         return out
 
-    def alloc_storage(self, ovf_cap: int, device="cuda", scratch=None) -> LctTensor:
+    def alloc_storage(self, ovf_cap: int, device="cuda", scratch=None, ovf=None) -> LctTensor:
         sz = self.sizes(ovf_cap)
         dev = torch.device(device)
         u8 = torch.uint8
         if scratch is None:
             scratch = torch.empty(sz.scratch, dtype=u8, device=dev)
+        elif scratch.numel() < sz.scratch:
+            raise ValueError("scratch too small: %d < %d" % (scratch.numel(), sz.scratch))
+        if ovf is None:
+            ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
+        elif ovf.numel() < ovf_cap:
+            raise ValueError("ovf too small: %d < %d" % (ovf.numel(), ovf_cap))
         return LctTensor.wrap(int(self.g.sf_bytes), self.layout, ovf_cap, sz,
                               torch.empty(max(sz.sf, 16), dtype=u8, device=dev),
                               torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev),
                               torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev),
                               torch.empty(sz.obase // 8, dtype=torch.int64, device=dev),
-                              torch.empty(max(ovf_cap, 16), dtype=u8, device=dev),
-                              torch.zeros(4, dtype=torch.int32, device=dev), scratch)
+                              ovf, torch.zeros(4, dtype=torch.int32, device=dev), scratch)
 
     def tensor(self, all_: LctTensor, k: int) -> LctTensor:
         """Tensor k as views of the storage (its obase values index the shared

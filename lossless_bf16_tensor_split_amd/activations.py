@@ -5,19 +5,22 @@ during training, next to weights and optimizer state; the explainer's results
 paragraph credits part of NanoGPT's memory saving to them.  Here autograd's
 saved-tensor hooks do it: a BF16 tensor on the GPU that autograd saves for
 backward is encoded when it is saved and decoded when backward asks for it.
-The encode, the decode and the per-tensor shift sample all run in the HIP
+The encode, the decode and the per-tensor codebook fit all run in the HIP
 library; this module only decides what to encode and owns the buffers.
 
 Per saved tensor:
   - codebook: the context's base code (from the model the user picks) with
-    the shift re-estimated from the tensor's own 4096-element sample
-    (lct_codebook_reshift_dense, no Huffman rebuild);
+    the shift chosen from the tensor's own 4096-element sample, the same
+    choice as lct_codebook_reshift_dense, made and turned into tables on the
+    device (lct_group_fit), so a save never waits for the device;
   - buffers: the fixed side at its exact size; the spilled bytes land in a
-    staging region shared by the context, large enough for every element to
-    spill, and are then copied into a buffer of exactly their size.
-
-A save waits twice for the device: for the sample that sets the shift, and
-for the spilled total that sizes the kept overflow buffer.
+    staging region (large enough for every element to spill) taken from a
+    small pool.  The shift and the spilled total are copied to pinned host
+    memory behind an event; once the event has passed, the spilled bytes move
+    to a buffer of exactly their size, the staging region returns to the
+    pool, and the host codebook for the decode is made from the shift.  A
+    save that finds the pool empty waits for the oldest save's event; the
+    block's end and a backward read of a save still in flight wait for it.
 
 Tensors that are not BF16, not on the GPU, not contiguous, smaller than
 `min_elems`, or leaves that require grad (parameters, which autograd saves by
@@ -26,33 +29,41 @@ reference at no cost) are saved as they are.
 from __future__ import annotations
 
 import time
+from collections import deque
 from contextlib import contextmanager
 from dataclasses import dataclass
 
 import torch
 
-from . import (CLEAN, GAUSSIAN, Codebook, LctTensor, Model, alloc_tensor,
-               lct_codebook_build, lct_codebook_reshift_dense, lct_decode, lct_encode,
-               lct_layout_init, lct_sizes)
+from . import (CLEAN, GAUSSIAN, Codebook, LctGroup, LctTensor, Model, lct_codebook_build,
+               lct_codebook_from_lengths, lct_decode, lct_encode_group, lct_layout_init, lct_sizes)
 
 
 @dataclass
 class _Saved:
-    t: LctTensor
-    cb: Codebook
+    t: LctTensor                 # the tensor (n elements) over the group storage's buffers
+    grp: LctGroup | None         # its one-tensor group (device tables), until the encode is done
     shape: torch.Size
+    cb: Codebook | None = None   # host codebook, once the shift is known
 
 
 class ActivationCodec:
     """pack/unpack hooks with their staging buffers and byte counts."""
 
-    def __init__(self, model: Model | None = None, mode: int = CLEAN, min_elems: int = 1 << 16):
+    def __init__(self, model: Model | None = None, mode: int = CLEAN, min_elems: int = 1 << 16,
+                 pool: int = 3):
         self.model = Model(GAUSSIAN, 1.0, 0.0) if model is None else model
         self.base = lct_codebook_build(self.model, None)
+        self.len_base = list(self.base.len_base)
         self.layout = lct_layout_init(mode)
         self.min_elems = int(min_elems)
         self._scratch = None
-        self._ovf = None
+        self._stage = [None] * pool          # staging regions
+        self._free = list(range(pool))
+        self._shift = None                   # device int32 per slot: the fitted shift
+        self._pin_shift = None               # pinned host copies: shift (int32) and
+        self._pin_spill = None               # spilled total (int64) per slot
+        self._pending = deque()              # (handle, slot, event, stream), oldest first
         self.saved = 0           # tensors encoded
         self.passed = 0          # tensors kept as they are
         self.raw_bytes = 0       # BF16 bytes of the encoded tensors
@@ -64,44 +75,87 @@ class ActivationCodec:
         return (x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
                 and x.numel() >= self.min_elems and not (x.is_leaf and x.requires_grad))
 
-    def _staging(self, n: int, need_ovf: int, device):
-        sz = lct_sizes(n, self.layout, need_ovf)
-        if self._scratch is None or self._scratch.numel() < sz.scratch or self._scratch.device != device:
-            self._scratch = torch.empty(sz.scratch, dtype=torch.uint8, device=device)
-        if self._ovf is None or self._ovf.numel() < need_ovf or self._ovf.device != device:
-            self._ovf = torch.empty(max(need_ovf, 16), dtype=torch.uint8, device=device)
+    def _finish(self, entry):
+        """A save whose event has passed: its shift and spilled total are in
+        pinned memory; trim its spills, make its host codebook, free its slot."""
+        h, slot, _, stream = entry
+        shift, spilled = int(self._pin_shift[slot]), int(self._pin_spill[slot])
+        h.grp = None                         # its table and the reference to the input go
+        with torch.cuda.stream(stream):
+            h.t.ovf = self._stage[slot][:max(spilled, 16)].clone()
+        h.t.ovf_cap = spilled
+        h.cb = lct_codebook_from_lengths(self.len_base, self.base.esc_len, shift)
+        self.stored_bytes += int(h.t.sizes.fixed) + spilled
+        self._free.append(slot)
+
+    def _reap(self, wait_one: bool = False):
+        """Finish every save whose event has passed, in order; with wait_one,
+        wait for the oldest if none has."""
+        while self._pending:
+            e = self._pending[0][2]
+            if not e.query():
+                if not wait_one:
+                    break
+                e.synchronize()
+            wait_one = False
+            self._finish(self._pending.popleft())
 
     def pack(self, x: torch.Tensor):
         if not self._wants(x):
             self.passed += 1
             return x
         t0 = time.perf_counter()
+        dev = x.device
         n = x.numel()
-        xd = x.detach()
-        cb = lct_codebook_reshift_dense(self.base, xd.view(-1))
-        # a staging region of n bytes holds every possible spill: one encode
-        self._staging(n, n, x.device)
-        t = alloc_tensor(n, self.layout, n, x.device, self._scratch, self._ovf)
-        lct_encode(cb, xd.view(-1), t)
-        spilled = t.spilled()                # synchronises
-        # keep the spilled bytes in a buffer of their own size
-        t.ovf = self._ovf[:max(spilled, 16)].clone()
-        t.ovf_cap = spilled
-        t.scratch = None
+        xd = x.detach().view(-1)
+        stream = torch.cuda.current_stream(dev)
+        self._reap()
+        if not self._free:
+            self._reap(wait_one=True)
+        slot = self._free.pop()
+        if self._shift is None:
+            self._pin_shift = torch.zeros(len(self._stage), dtype=torch.int32, pin_memory=True)
+            self._pin_spill = torch.zeros(len(self._stage), dtype=torch.int64, pin_memory=True)
+            self._shift = torch.zeros(len(self._stage), dtype=torch.int32, device=dev)
+        st = self._stage[slot]
+        if st is None or st.numel() < n or st.device != dev:
+            self._stage[slot] = st = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        sz = lct_sizes(n, self.layout, n)
+        if self._scratch is None or self._scratch.numel() < sz.scratch or self._scratch.device != dev:
+            self._scratch = torch.empty(sz.scratch, dtype=torch.uint8, device=dev)
+        # the codebook fitted on the device, then the encode with its tables
+        grp = LctGroup([n], self.layout, [self.base], [xd], device=dev, fit=True,
+                       shift=self._shift[slot:slot + 1], stream=stream)
+        all_ = grp.alloc_storage(n, dev, self._scratch, st)
+        lct_encode_group(grp, all_, stream)
+        self._pin_shift[slot:slot + 1].copy_(self._shift[slot:slot + 1], non_blocking=True)
+        self._pin_spill[slot:slot + 1].copy_(all_.obase[-1:], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        t = LctTensor.wrap(n, self.layout, n, lct_sizes(n, self.layout, n), all_.sf, all_.pay, all_.cnt,
+                           all_.obase, st, all_.status, None)
+        h = _Saved(t, grp, x.shape)
+        self._pending.append((h, slot, ev, stream))
         self.saved += 1
         self.raw_bytes += 2 * n
-        self.stored_bytes += int(t.sizes.fixed) + spilled
         self.pack_s += time.perf_counter() - t0
-        return _Saved(t, cb, x.shape)
+        return h
 
     def unpack(self, h):
         if not isinstance(h, _Saved):
             return h
         t0 = time.perf_counter()
+        while h.cb is None:                  # still in flight: finish saves up to it
+            self._reap(wait_one=True)
         y = torch.empty(h.shape, dtype=torch.bfloat16, device=h.t.sf.device)
         lct_decode(h.cb, h.t, y.view(-1))
         self.unpack_s += time.perf_counter() - t0
         return y
+
+    def close(self):
+        """Finish every save still in flight (waits for their events)."""
+        while self._pending:
+            self._reap(wait_one=True)
 
     def ratio(self) -> float:
         return self.raw_bytes / self.stored_bytes if self.stored_bytes else 0.0
@@ -112,5 +166,8 @@ def compressed_activations(model: Model | None = None, mode: int = CLEAN, min_el
     """Within the block, tensors autograd saves for backward are stored
     compressed (see the module docstring); yields the codec for its counts."""
     codec = ActivationCodec(model, mode, min_elems)
-    with torch.autograd.graph.saved_tensors_hooks(codec.pack, codec.unpack):
-        yield codec
+    try:
+        with torch.autograd.graph.saved_tensors_hooks(codec.pack, codec.unpack):
+            yield codec
+    finally:
+        codec.close()

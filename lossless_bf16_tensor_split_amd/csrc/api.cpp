@@ -623,6 +623,45 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
     return LCT_OK;
 }
 
+lct_status lct_group_fit(const lct_codebook *base, const uint64_t *n, uint16_t *const *d_dense,
+                         const lct_layout *layout, void *d_table, int32_t *d_shift, void *stream,
+                         lct_group *out) {
+    if (!base || !n || !d_dense || !layout || !d_table || !out || !layout_ok(*layout)) return LCT_EINVAL;
+    if (n[0] > 0 && !d_dense[0]) return LCT_EINVAL;
+    if (!aligned(d_table, 256) || (n[0] > 0 && !aligned(d_dense[0], 16)) || (d_shift && !aligned(d_shift, 4)))
+        return LCT_EALIGN;
+    uint64_t nb = 0, sf = 0;
+    if (!group_extent(1, n, *layout, &nb, &sf)) return LCT_EINVAL;
+    lct_status st = check_arch();
+    if (st != LCT_OK) return st;
+    const GroupTableLayout t = group_table_layout(1, nb);
+    uint8_t *tab = static_cast<uint8_t *>(d_table);
+    FitParams p;
+    memset(&p, 0, sizeof p);
+    p.x = d_dense[0];
+    p.n = n[0];
+    p.m = (uint32_t)std::min<uint64_t>(n[0], 4096);
+    p.nblk = (uint32_t)nb;
+    p.esc_len = base->esc_len;
+    memcpy(p.base, base->len_base, sizeof p.base);
+    p.ent = reinterpret_cast<GroupEntry *>(tab + t.ent);
+    p.enc = reinterpret_cast<EncTab *>(tab + t.enc);
+    p.dec = reinterpret_cast<DecTab *>(tab + t.dec);
+    p.blk_tensor = reinterpret_cast<uint32_t *>(tab + t.blk_tensor);
+    p.shift_out = d_shift;
+    const int e = launch_fit(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "fit launch");
+    out->count = 1;
+    out->layout = *layout;
+    out->nblk = nb;
+    out->sf_bytes = sf;
+    out->shape_hash = shape_hash(1, n, *layout);
+    out->n = n;
+    out->d_dense = d_dense;
+    out->d_table = d_table;
+    return LCT_OK;
+}
+
 lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out) {
     if (!g || !out || !layout_ok(g->layout)) return LCT_EINVAL;
     out->nblk = g->nblk;

@@ -695,6 +695,98 @@ __global__ __launch_bounds__(64) void k_sample(const SampleParams p) {
     g_sample[i] = (uint16_t)(((sf & 0x80u) << 8) | (e << 7) | (sf & 0x7Fu));
 }
 
+// Codebook fit on the device, for callers that must not wait for it: one
+// workgroup takes x's 4096-element sample (positions floor(i * n / m)), costs
+// every shift k in -255..255 over the base code (a field e costs base[e - k],
+// or the escape plus its 8-bit literal), keeps the cheapest (ties: smaller
+// |k|, then negative k), and builds the shifted code's canonical codes
+// (RFC 1951 order: by length, then field, the escape last as id 256), its
+// encode table and its 8-bit peek decode table, as the host builder does.
+__global__ __launch_bounds__(256) void k_fit(const FitParams p) {
+    __shared__ uint32_t hist[256], base[256], lenf[256], code[257], cnt[16], key[4];
+    const uint32_t t = threadIdx.x;
+    hist[t] = 0;
+    base[t] = p.base[t];
+    if (t < 16) cnt[t] = 0;
+    __syncthreads();
+    for (uint32_t i = t; i < p.m; i += 256) {
+        const uint32_t e = (p.x[(uint64_t)i * p.n / p.m] >> 7) & 0xFFu;
+        atomicAdd(&hist[e], 1u);
+    }
+    __syncthreads();
+    const uint32_t esc_cost = p.esc_len + 8;
+    auto cost_key = [&](int32_t k) {
+        uint32_t c = 0;
+        for (int32_t e = 0; e < 256; ++e) {
+            const uint32_t h = hist[e];
+            const int32_t x = e - k;
+            const uint32_t b = (x >= 0 && x < 256) ? base[x] : 0u;
+            c += h * (b ? b : esc_cost);
+        }
+        // cost first, then |k|, then the negative of a pair
+        return (c << 10) | ((uint32_t)(k < 0 ? -k : k) << 1) | (k > 0 ? 1u : 0u);
+    };
+    uint32_t best = cost_key((int32_t)t - 255);
+    if (t < 255) best = min(best, cost_key((int32_t)t + 1));
+    for (uint32_t o = 32; o > 0; o >>= 1) best = min(best, (uint32_t)__shfl_xor((int)best, (int)o));
+    if ((t & 63) == 0) key[t >> 6] = best;
+    __syncthreads();
+    best = min(min(key[0], key[1]), min(key[2], key[3]));
+    const uint32_t mag = (best >> 1) & 511u;
+    const int32_t k = (best & 1u) ? (int32_t)mag : -(int32_t)mag;
+    // the shifted code: lengths, counts per length, canonical codes
+    const int32_t x = (int32_t)t - k;
+    const uint32_t L = (x >= 0 && x < 256) ? base[x] : 0u;
+    lenf[t] = L;
+    if (L) atomicAdd(&cnt[L], 1u);
+    if (t == 0) atomicAdd(&cnt[p.esc_len], 1u);
+    __syncthreads();
+    if (t == 0) {
+        uint32_t c = 0;
+        cnt[0] = 0;
+        for (uint32_t bits = 1; bits <= 8; ++bits) {
+            c = (c + cnt[bits - 1]) << 1;
+            cnt[8 + bits - 1] = c;      // first code of each length, in cnt[8..15]
+        }
+    }
+    __syncthreads();
+    auto first_code = [&](uint32_t len) { return cnt[8 + len - 1]; };
+    if (L) {
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < t; ++j) rank += lenf[j] == L;
+        code[t] = first_code(L) + rank;
+    }
+    if (t == 0) {
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < 256; ++j) rank += lenf[j] == p.esc_len;
+        code[256] = first_code(p.esc_len) + rank;
+    }
+    __syncthreads();
+    auto rev = [](uint32_t v, uint32_t n) { return __brev(v) >> (32 - n); };
+    // encode table: stream bits (code reversed; an escape then the literal)
+    if (L) {
+        p.enc->bits[t] = rev(code[t], L);
+        p.enc->len[t] = (uint8_t)L;
+    } else {
+        p.enc->bits[t] = rev(code[256], p.esc_len) | (t << p.esc_len);
+        p.enc->len[t] = (uint8_t)(p.esc_len + 8);
+    }
+    // decode table: the symbol whose reversed code the peek starts with
+    uint32_t d = (8u << 8) | (1u << 14);
+    for (uint32_t s = 0; s <= 256; ++s) {
+        const uint32_t ls = s < 256 ? lenf[s] : p.esc_len;
+        if (ls && (t & ((1u << ls) - 1)) == rev(code[s], ls))
+            d = s < 256 ? (s | (ls << 8)) : (((ls + 8) << 8) | (1u << 13));
+    }
+    p.dec->dec[t] = (uint16_t)d;
+    if (t == 0) {
+        p.dec->esc_len = p.esc_len;
+        *p.ent = GroupEntry{p.x, p.n, 0, 0, p.nblk};
+        if (p.shift_out) *p.shift_out = k;
+    }
+    for (uint32_t b = t; b < p.nblk; b += 256) p.blk_tensor[b] = 0;
+}
+
 // ------------------------------------------------------------------ step driver
 
 // Positions [j0, j0+CH) of one lane's stream from base (the lane's position 0,
@@ -1536,6 +1628,11 @@ int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out) {
                                  hipMemcpyDeviceToHost, st);
     if (e != hipSuccess) return (int)e;
     return (int)hipStreamSynchronize(st);
+}
+
+int launch_fit(const FitParams &p, void *stream) {
+    hipLaunchKernelGGL(k_fit, dim3(1), dim3(256), 0, (hipStream_t)stream, p);
+    return (int)hipGetLastError();
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {

@@ -185,6 +185,22 @@ struct SampleParams {
     DecTab dec;
 };
 
+// Fit of a codebook on the device: the shift of x's sample over the base
+// code, the shifted code's tables, and x's record, written as a one-tensor
+// group table.
+struct FitParams {
+    uint16_t *x;
+    uint64_t n;
+    uint32_t m, nblk;        // sample size min(n, 4096); x's blocks
+    uint32_t esc_len, pad0;
+    uint8_t base[256];       // base code lengths (0: escaped)
+    GroupEntry *ent;
+    EncTab *enc;
+    DecTab *dec;
+    uint32_t *blk_tensor;
+    int32_t *shift_out;      // may be null
+};
+
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
@@ -197,6 +213,8 @@ int launch_sgd(const SgdParams &p, void *stream, bool group = false, bool dense 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.
 int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);
+// The device fit (enqueues only).
+int launch_fit(const FitParams &p, void *stream);
 
 // Host codebook construction (codebook.cpp).
 lct_status build_codebook(const lct_model &model, const uint16_t *sample, uint32_t m,

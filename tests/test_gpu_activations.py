@@ -57,6 +57,7 @@ def test_saved_bytes_are_the_oracles(L, orc):
     x = synth.to_bf16_bits(v / (1 + np.exp(-v)) * 3.0)           # SiLU at a larger scale
     codec = ActivationCodec(L.Model(1, 0.25, 0.0), min_elems=1)
     h = codec.pack(dev(x).view(torch.bfloat16))
+    codec.close()
     ocb = orc.codebook_build(1, 0.25, 0.0, x)
     assert h.cb.shift == ocb.shift and h.cb.shift != 0
     assert np.array_equal(np.frombuffer(bytes(h.cb.code), np.uint32), ocb.code)
@@ -104,3 +105,25 @@ def test_mlp_backward_is_unchanged(L, orc):
     else:                         # the library GEMMs were not reproducible run to run
         for a, b in zip(g0, g2):
             assert torch.allclose(a.float(), b.float(), rtol=1e-2, atol=1e-3)
+
+
+def test_consecutive_saves_trim_in_turn(L, orc):
+    """Saves take staging regions from a pool of three and are finished as
+    their events pass (at the latest when the pool runs out): many saves of
+    tensors that spill, every one read back after the last."""
+    from lossless_bf16_tensor_split_amd.activations import ActivationCodec
+    codec = ActivationCodec(L.Model(0, 1.0, 0.0), min_elems=1)
+    g = np.random.default_rng(9110)
+    def mixture(n):         # two scales 2^6 apart: no one shift fits both, so both spill
+        return synth.to_bf16_bits(g.normal(0, 1.0, n) * np.where(g.random(n) < 0.5, 1.0, 64.0))
+    xs = [mixture(70000 + 999 * k) for k in range(7)]
+    xs.append(g.integers(0, 1 << 16, 50000, dtype=np.uint64).astype(np.uint16))   # expands
+    hs = [codec.pack(dev(x).view(torch.bfloat16)) for x in xs]
+    for h in hs[:-3]:                            # the pool holds three saves in flight
+        assert h.cb is not None and h.t.ovf_cap == h.t.spilled()
+    codec.close()
+    spills = [h.t.spilled() for h in hs]
+    assert min(spills) > 0
+    for x, h in reversed(list(zip(xs, hs))):     # the last save is read first, as in backward
+        assert np.array_equal(as_bits(codec.unpack(h)), x)
+    assert all(h.t.ovf_cap == h.t.spilled() for h in hs)

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import synth
+from test_gpu_group import storage_equal
 from test_gpu_parity import assert_same, check_codebook, dev, host_parts
 
 pytestmark = pytest.mark.gpu
@@ -184,3 +185,53 @@ def test_momentum_step_recode(L, orc, inplace):
         assert_same(gp, ref, "momentum recode %s inplace=%s" % (name, inplace))
         assert gp["status"] == ref.status
     assert ref_w.spilled > 0 and ref_m.spilled > 0
+
+
+# ------------------------------------------------------------------ fit on the device
+
+@pytest.mark.parametrize("case", ["gauss", "gauss_x64", "laplace_small", "uniform_bits", "one", "mixture"])
+def test_device_fit_matches_the_host(L, orc, case):
+    """lct_group_fit chooses the shift and builds the tables on the device:
+    the same shift, encode table and peek table as the host's
+    lct_codebook_reshift_dense, and an encode equal to the oracle's."""
+    g = np.random.default_rng(8600)
+    if case == "gauss":
+        x = synth.to_bf16_bits(g.normal(0, 0.02, 300001))
+    elif case == "gauss_x64":
+        x = synth.to_bf16_bits(g.normal(0, 0.02 * 64, 70000))
+    elif case == "laplace_small":
+        x = synth.to_bf16_bits(g.laplace(0, 3.0, 1000))
+    elif case == "uniform_bits":
+        x = g.integers(0, 1 << 16, 131072, dtype=np.uint64).astype(np.uint16)
+    elif case == "one":
+        x = np.array([0x3F80], np.uint16)
+    else:
+        n = 90000
+        x = synth.to_bf16_bits(g.normal(0, 1.0, n) * np.where(g.random(n) < 0.5, 1.0, 2.0 ** -9))
+    base = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    xd = dev(x).view(torch.bfloat16)
+    shift = torch.full((4,), -999, dtype=torch.int32, device="cuda")
+    lay = L.layout(65536, 25)
+    grp = L.LctGroup([x.size], lay, [base], [xd], fit=True, shift=shift)
+    host = L.lct_codebook_reshift_dense(base, xd)
+    torch.cuda.synchronize()
+    assert int(shift[0].item()) == host.shift
+    tab = grp.table.cpu().numpy()
+    enc0, dec0 = 256, 1536                       # the table's parts for one tensor
+    assert np.array_equal(tab[enc0:enc0 + 1024].view(np.uint32), np.frombuffer(bytes(host.enc_bits), np.uint32))
+    assert np.array_equal(tab[enc0 + 1024:enc0 + 1280], np.frombuffer(bytes(host.enc_len), np.uint8))
+    assert np.array_equal(tab[dec0:dec0 + 512].view(np.uint16), np.frombuffer(bytes(host.dec), np.uint16))
+    assert int(tab[dec0 + 512:dec0 + 516].view(np.uint32)[0]) == host.esc_len
+    ent = tab[0:32].view(np.uint64)
+    assert int(ent[0]) == xd.data_ptr() and int(ent[1]) == x.size and int(ent[2]) == 0
+    # the encode with the device tables is the oracle's with the same shift
+    ob = orc.codebook_build(0, 0.02, 0.0, x)
+    assert ob.shift == host.shift
+    all_ = grp.alloc_storage(x.size)
+    L.lct_encode_group(grp, all_)
+    ref = orc.encode(ob, x, 65536, 25)
+    storage_equal(L, grp, all_, ref, [x.size], "fit " + case)
+    y = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
+    L.lct_decode(host, grp.tensor(all_, 0), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), x)
