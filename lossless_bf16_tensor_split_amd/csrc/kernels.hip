@@ -44,10 +44,11 @@
 // encode table has one 8-byte entry per field: stream bits, bit count.
 //
 // Overflow offsets: spilled fields are parked per stream in a staging area,
-// gathered per unit at its end, and placed by a separate scan kernel, an
-// exclusive scan over the units' spill totals with a decoupled look-back
-// across its workgroups (Merrill and Garland, "Single-pass Parallel Prefix
-// Scan with Decoupled Look-back", 2016), so that the fields land in (block,
+// gathered per unit at its end, then given their offsets by a separate scan
+// kernel, an exclusive scan over the units' spill totals with a decoupled
+// look-back across its workgroups (Merrill and Garland, "Single-pass Parallel
+// Prefix Scan with Decoupled Look-back", 2016), and copied to their place by
+// a placing kernel, a wave per unit, so that the fields land in (block,
 // stream, position) order.
 //
 // Every loop step handles 16 positions per lane while the next 16 are loaded
@@ -524,7 +525,8 @@ struct UnitOut {
 // and the rows after it are cleared); its spilled fields, if any, are gathered from the
 // per-stream staging pieces into one piece of the second staging area in
 // (stream, position) order; its record says where; then its counts.  The
-// overflow offsets and the fields' final places are the scan kernel's work.
+// overflow offsets are the scan kernel's work, the fields' final places the
+// placing kernel's.
 template <class Rows>
 __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_s, uint32_t u, uint32_t b,
                                             uint32_t h, uint32_t row0, const UnitOut &o) {
@@ -573,16 +575,11 @@ __global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
 
 // Overflow offsets: an exclusive scan of the units' spill totals in unit
 // order (block, then its units), one unit per thread, groups chained by the
-// look-back.  Writes obase, flags a too-small overflow region, copies each of
-// its units' spilled fields from the second staging area to their place in
-// the overflow region, and puts parked counts in place.
+// look-back.  Writes obase and flags a too-small overflow region.
 __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase,
-                                                     uint8_t *ovf, uint64_t ovf_cap, uint32_t *status,
-                                                     uint16_t *cnt) {
+                                                     uint64_t ovf_cap, uint32_t *status) {
     __shared__ uint32_t s_g;
     __shared__ uint64_t s_wave[kScanGroup / 64], s_excl;
-    __shared__ uint64_t s_from[kScanGroup], s_to[kScanGroup];
-    __shared__ uint32_t s_tot[kScanGroup], s_flags[kScanGroup];
     const uint32_t t = threadIdx.x;
     if (t == 0) s_g = atomicAdd(reinterpret_cast<uint32_t *>(scratch + kScrTicket2), 1u);
     __syncthreads();
@@ -619,25 +616,37 @@ __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t 
         obase[nblk] = ex + r.total;
         if (ex + r.total > ovf_cap) atomicOr(status, LCT_ST_OVF_FULL);
     }
-    s_tot[t] = r.total;
-    s_from[t] = r.base;
-    s_to[t] = ex;
-    s_flags[t] = r.flags;
-    __syncthreads();
+    // parked counts are put in place by the placing kernel: tell it
+    if (__any(u < nunits && (r.flags & 1u)) && lane() == 0)
+        atomicOr(reinterpret_cast<uint32_t *>(scratch + kScrParked), 1u);
+}
+
+// After the scan: every unit's spilled bytes go from the second staging area
+// to the overflow region at its block's offset plus the spills of the block's
+// earlier units, and parked counts go in place.  One wave per unit, the
+// workgroups taking units round-robin; nothing to do (no spills, nothing
+// parked) ends every wave at once.
+__global__ __launch_bounds__(256) void k_place(const uint8_t *scratch, uint64_t nblk, const uint64_t *obase,
+                                               uint8_t *ovf, uint64_t ovf_cap, uint16_t *cnt) {
+    const uint32_t parked = *reinterpret_cast<const uint32_t *>(scratch + kScrParked);
+    if (obase[nblk] == 0 && parked == 0) return;
+    const uint64_t nunits = nblk * kMaxUnits;
+    const UnitRec *rec = reinterpret_cast<const UnitRec *>(scratch + scr_rec_offset(nblk));
     const uint8_t *stage2 = scratch + scr_stage2_offset(nblk, ovf_cap);
-    const uint16_t *parked = reinterpret_cast<const uint16_t *>(scratch + scr_cnt_offset(nblk));
-    for (uint32_t k = 0; k < kScanGroup; ++k) {
-        const uint64_t uk = (uint64_t)g * kScanGroup + k;
-        if (uk >= nunits) break;
-        if (s_flags[k] & 1u) {
-            const uint64_t at = (uk / kMaxUnits) * NS + (uk % kMaxUnits) * US;
-            if (t < US) cnt[at + t] = parked[at + t];
+    const uint16_t *parked_cnt = reinterpret_cast<const uint16_t *>(scratch + scr_cnt_offset(nblk));
+    const uint32_t l = lane();
+    for (uint64_t u = (uint64_t)blockIdx.x * 4 + wave_id(); u < nunits; u += (uint64_t)gridDim.x * 4) {
+        const UnitRec r = rec[u];
+        const uint64_t b = u / kMaxUnits;
+        if (r.flags & 1u) {
+            const uint64_t at = b * NS + (u % kMaxUnits) * US;
+            cnt[at + l] = parked_cnt[at + l];
         }
-        const uint64_t n = s_tot[k];
-        if (n == 0) continue;
-        const uint64_t from = s_from[k], to = s_to[k];
-        for (uint64_t i = t; i < n; i += kScanGroup)
-            if (from + i < ovf_cap && to + i < ovf_cap) ovf[to + i] = stage2[from + i];
+        if (r.total == 0) continue;
+        uint64_t to = obase[b];
+        for (uint64_t v = b * kMaxUnits; v < u; ++v) to += rec[v].total;
+        for (uint64_t i = l; i < r.total; i += 64)
+            if (r.base + i < ovf_cap && to + i < ovf_cap) ovf[to + i] = stage2[r.base + i];
     }
 }
 
@@ -709,10 +718,16 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     base[t] = p.base[t];
     if (t < 16) cnt[t] = 0;
     __syncthreads();
-    for (uint32_t i = t; i < p.m; i += 256) {
-        const uint32_t e = (p.x[(uint64_t)i * p.n / p.m] >> 7) & 0xFFu;
-        atomicAdd(&hist[e], 1u);
+    // the sample's 16 loads per thread all go out before any is counted
+    uint32_t es[16];
+#pragma unroll
+    for (uint32_t j = 0; j < 16; ++j) {
+        const uint32_t i = t + 256 * j;
+        es[j] = i < p.m ? (p.x[(uint64_t)i * p.n / p.m] >> 7) & 0xFFu : 256u;
     }
+#pragma unroll
+    for (uint32_t j = 0; j < 16; ++j)
+        if (es[j] < 256) atomicAdd(&hist[es[j]], 1u);
     __syncthreads();
     const uint32_t esc_cost = p.esc_len + 8;
     auto cost_key = [&](int32_t k) {
@@ -1501,7 +1516,7 @@ void k_sgd(const SgdParams p) {
         }
         // The result's counts overwrite W's when the update is in place:
         // other units of this block may still read W's (general path), so
-        // they are parked and put in place by the scan kernel.
+        // they are parked and put in place by the placing kernel.
         const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
                         p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
         unit_finish(st, n_s, u, b, h, 0, o);
@@ -1592,7 +1607,12 @@ int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, 
                 uint32_t *status, uint16_t *cnt, void *stream) {
     const uint64_t groups = (nblk * kMaxUnits + kScanGroup - 1) / kScanGroup;
     hipLaunchKernelGGL(k_scan, dim3((uint32_t)groups), dim3(kScanGroup), 0, (hipStream_t)stream,
-                       scratch, nblk, obase, ovf, ovf_cap, status, cnt);
+                       scratch, nblk, obase, ovf_cap, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const uint32_t place = (uint32_t)std::min<uint64_t>(nblk, 2048);
+    hipLaunchKernelGGL(k_place, dim3(place), dim3(256), 0, (hipStream_t)stream, scratch, nblk, obase, ovf,
+                       ovf_cap, cnt);
     return (int)hipGetLastError();
 }
 

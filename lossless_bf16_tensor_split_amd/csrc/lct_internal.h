@@ -24,12 +24,14 @@ constexpr uint32_t kUnitStreams = kStreams / kMaxUnits;   // streams per unit: o
 // staging area, whether its counts were parked).  Spilled exponent fields are
 // parked per stream in the first staging area while a unit runs, copied into
 // one contiguous piece per unit at its end, and placed in the overflow region
-// by the scan kernel once every unit's offset is known.  An in-place update
-// parks its counts too, so that no unit overwrites counts another unit of the
-// same block has yet to read; the scan kernel puts them in place.
+// by the placing kernel once the scan has given every block its offset.  An
+// in-place update parks its counts too, so that no unit overwrites counts
+// another unit of the same block has yet to read; the placing kernel puts
+// them in place.
 constexpr uint64_t kScrTicket2 = 4;   // uint32: next group of the scan kernel
 constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the first staging area
 constexpr uint64_t kScrStage2 = 16;   // uint64: bytes claimed in the second
+constexpr uint64_t kScrParked = 24;   // uint32: nonzero when some unit parked its counts
 constexpr uint64_t kScrFlags = 64;    // uint64[groups + 1]: the scan's look-back flags
 constexpr uint32_t kScanGroup = 256;  // units per scan workgroup
 __host__ __device__ inline uint64_t scr_units(uint64_t nblk) { return kMaxUnits * nblk; }
