@@ -839,6 +839,25 @@ __device__ __forceinline__ void double_buffered(uint32_t npos, Load load, Step s
     }
 }
 
+// The same with the loads two chunks ahead (three buffers): a wave's stream
+// waits less on memory when few waves share a compute unit (small tensors).
+template <typename Buf, typename Load, typename Step>
+__device__ __forceinline__ void triple_buffered(uint32_t npos, Load load, Step step) {
+    Buf a, b, c;
+    load(a, 0u);
+    load(b, min(CH, npos - CH));
+    for (uint32_t j0 = 0; j0 < npos; j0 += 3 * CH) {
+        load(c, min(j0 + 2 * CH, npos - CH));
+        step(a, j0);
+        if (j0 + CH >= npos) break;
+        load(a, min(j0 + 3 * CH, npos - CH));
+        step(b, j0 + CH);
+        if (j0 + 2 * CH >= npos) break;
+        load(b, min(j0 + 4 * CH, npos - CH));
+        step(c, j0 + 2 * CH);
+    }
+}
+
 struct Buf1 {
     uint32_t v[CH];
 };
@@ -868,7 +887,7 @@ __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer &st,
     uint8_t *sfs = sfu + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    double_buffered<Buf1>(
+    triple_buffered<Buf1>(
         npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FULL>(bf.v, xs, j0, n_s); },
         [&](Buf1 &bf, uint32_t j0) {
             uint32_t e[CH];
@@ -947,7 +966,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t ro
     uint16_t *ys = yu + s;
     Reader rd;
     rd.init(row0, s);
-    double_buffered<Buf1>(
+    triple_buffered<Buf1>(
         npos, [&](Buf1 &bf, uint32_t j0) { load_chunk<!FAST>(bf.v, sfs, j0, n_s); },
         [&](Buf1 &bf, uint32_t j0) {
             uint16_t *o = ys + (size_t)j0 * NS;
