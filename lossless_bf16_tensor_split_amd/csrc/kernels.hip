@@ -712,7 +712,8 @@ __global__ __launch_bounds__(64) void k_sample(const SampleParams p) {
 // (RFC 1951 order: by length, then field, the escape last as id 256), its
 // encode table and its 8-bit peek decode table, as the host builder does.
 __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
-    __shared__ uint32_t hist[256], base[256], lenf[256], code[257], cnt[16], key[4];
+    __shared__ uint32_t hist[256], base[256], lenf[256], code[257], cnt[16], key[4], wcount[4];
+    __shared__ uint32_t bins[256], syms[256], nbins, nsyms;
     const uint32_t t = threadIdx.x;
     hist[t] = 0;
     base[t] = p.base[t];
@@ -729,14 +730,28 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     for (uint32_t j = 0; j < 16; ++j)
         if (es[j] < 256) atomicAdd(&hist[es[j]], 1u);
     __syncthreads();
+    // keep the entries t with flag set, in order of t, in out[0..*count)
+    auto compact = [&](bool flag, uint32_t value, uint32_t *out, uint32_t *count) {
+        const uint64_t m = __ballot(flag);
+        const uint32_t l = t & 63, w = t >> 6;
+        if (l == 0) wcount[w] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t off = (uint32_t)__popcll(m & ((1ull << l) - 1));
+        for (uint32_t v = 0; v < w; ++v) off += wcount[v];
+        if (flag) out[off] = value;
+        if (t == 0) *count = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+        __syncthreads();
+    };
+    // the sample's fields (few for a tensor the model fits): field | count << 8
+    compact(hist[t] != 0, t | (hist[t] << 8), bins, &nbins);
     const uint32_t esc_cost = p.esc_len + 8;
     auto cost_key = [&](int32_t k) {
         uint32_t c = 0;
-        for (int32_t e = 0; e < 256; ++e) {
-            const uint32_t h = hist[e];
-            const int32_t x = e - k;
+        for (uint32_t j = 0; j < nbins; ++j) {
+            const uint32_t v = bins[j];
+            const int32_t x = (int32_t)(v & 0xFFu) - k;
             const uint32_t b = (x >= 0 && x < 256) ? base[x] : 0u;
-            c += h * (b ? b : esc_cost);
+            c += (v >> 8) * (b ? b : esc_cost);
         }
         // cost first, then |k|, then the negative of a pair
         return (c << 10) | ((uint32_t)(k < 0 ? -k : k) << 1) | (k > 0 ? 1u : 0u);
@@ -755,7 +770,7 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     lenf[t] = L;
     if (L) atomicAdd(&cnt[L], 1u);
     if (t == 0) atomicAdd(&cnt[p.esc_len], 1u);
-    __syncthreads();
+    compact(L != 0, t | (L << 9), syms, &nsyms);      // the coded fields, by field
     if (t == 0) {
         uint32_t c = 0;
         cnt[0] = 0;
@@ -766,14 +781,16 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     }
     __syncthreads();
     auto first_code = [&](uint32_t len) { return cnt[8 + len - 1]; };
+    // a code is its length's first code plus the coded fields before it of
+    // that length; the escape comes after every field of its length
     if (L) {
         uint32_t rank = 0;
-        for (uint32_t j = 0; j < t; ++j) rank += lenf[j] == L;
+        for (uint32_t j = 0; j < nsyms; ++j) rank += (syms[j] & 0x1FFu) < t && (syms[j] >> 9) == L;
         code[t] = first_code(L) + rank;
     }
     if (t == 0) {
         uint32_t rank = 0;
-        for (uint32_t j = 0; j < 256; ++j) rank += lenf[j] == p.esc_len;
+        for (uint32_t j = 0; j < nsyms; ++j) rank += (syms[j] >> 9) == p.esc_len;
         code[256] = first_code(p.esc_len) + rank;
     }
     __syncthreads();
@@ -788,10 +805,11 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     }
     // decode table: the symbol whose reversed code the peek starts with
     uint32_t d = (8u << 8) | (1u << 14);
-    for (uint32_t s = 0; s <= 256; ++s) {
-        const uint32_t ls = s < 256 ? lenf[s] : p.esc_len;
-        if (ls && (t & ((1u << ls) - 1)) == rev(code[s], ls))
-            d = s < 256 ? (s | (ls << 8)) : (((ls + 8) << 8) | (1u << 13));
+    for (uint32_t j = 0; j <= nsyms; ++j) {
+        const uint32_t sj = j < nsyms ? (syms[j] & 0x1FFu) : 256u;
+        const uint32_t ls = j < nsyms ? (syms[j] >> 9) : p.esc_len;
+        if ((t & ((1u << ls) - 1)) == rev(code[sj], ls))
+            d = sj < 256 ? (sj | (ls << 8)) : (((ls + 8) << 8) | (1u << 13));
     }
     p.dec->dec[t] = (uint16_t)d;
     if (t == 0) {
