@@ -333,3 +333,19 @@ def test_momentum_gpt162m_flat(L, orc):
     gr = synth.draw(synth.TensorSpec("g.flat", (w.size,), 3100, "normal", {"sigma": 1e-3}))
     B, cw = synth.mode_layout(synth.CLEAN)
     momentum_case(L, orc, w, m, gr, mw, mm, 0.9, eta, B, cw, True, what="momentum config3")
+
+
+@pytest.mark.parametrize("n", [1, 255, 4096, 65535, 65536, 65537, 3 * 65536 + 4097])
+def test_updates_at_odd_sizes(L, orc, n):
+    """The update and the momentum step on tensors of every size class (a
+    single element, a partial stream, exactly one block, one element past a
+    block), out of place and in place."""
+    g = np.random.default_rng(9800 + n % 1000)
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr = synth.to_bf16_bits(g.normal(0, 4e-4, n))
+    for inplace in (False, True):
+        sgd_case(L, orc, w, m, synth.Model(0, 0.02), synth.Model(0, 1e-3), 1e-3, 65536, 25, inplace,
+                 what="n=%d inplace=%s" % (n, inplace))
+        momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.9, 1e-3, 65536, 25,
+                      inplace, what="n=%d inplace=%s" % (n, inplace))
