@@ -77,9 +77,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the codec shards by blocks with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the codec would shard by blocks, with one exchange of spilled totals "
+              "for the overflow offsets). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
