@@ -10,16 +10,17 @@
  *   [LCT-abs]     "LCT: Losslessly Compressed Tensors with GPU friendly execution
  *                 for Training" (scholarbro.com), abstract.
  *   [EXP-split]   "LCT paper - Lossless Huffman coding of BF16 training tensors"
- *                 (learnaivisually.com), paragraph "In bits, a BF16 value is ...".
+ *                 (learnaivisually.com), the paragraph on the bits of a BF16 value
+ *                 (byte split, exponent entropy, capped Huffman codes, escape).
  *   [EXP-streams] same page, paragraph on blocks of 65,536 / 32,768 and 256 streams.
  *   [EXP-train]   same page, paragraph on training traffic and the fused SGD update.
- *   [EXP-ideal]   same page, paragraph "Here is the idealized arithmetic ...".
+ *   [EXP-ideal]   same page, the paragraph on idealized arithmetic (16/11; 1.4382).
  *   [EXP-limits]  same page, paragraph on the longer-context claim and the limits
  *                 (a distribution that does not fit the tensor raises storage).
  *   [EXP-jargon]  same page, jargon entry "Optimizer state".
  *
- * Conventions fixed where the pages are silent are listed, with the reading
- * taken, in the design notes; every function below names the one it uses.
+ * Where the pages are silent, a convention had to be fixed; every function
+ * below states the reading it takes.
  *
  * Parity status: every function here is pinned by tests/test_oracle_*.py,
  * except the model probability mass (lcto_model_pmf), whose floating CDFs are
