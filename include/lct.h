@@ -157,9 +157,10 @@ lct_status lct_layout_init(int32_t mode, lct_layout *out);
  * outside the accepted range or a null pointer. */
 lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct_sizes_t *out);
 
-/* Codebook build (explainer, paragraph on bits: the codebook is
- * precomputed from the distribution the user picks, with a small shift
- * sampled from up to 4096 elements to follow the tensor's scale).
+/* Codebook build (explainer, paragraph on bits: the code is fixed ahead of
+ * training from a model distribution chosen by the user, and an exponent
+ * offset estimated on at most 4096 sampled values adapts it to the tensor's
+ * magnitude).
  * Steps: model probability of every exponent field -> integer weights
  * floor(p * 2^40 + 0.5) -> escape set (the k heaviest fields kept, k chosen
  * for the least expected bits) with length-limited Huffman (package-merge,
@@ -180,9 +181,9 @@ lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_le
                                      lct_codebook *out);
 
 /* Shift re-estimation (abstract: adaptation to magnitude shifts; explainer,
- * paragraph on bits: a small shift sampled from up to 4096 elements follows
- * the tensor's scale; paragraph on the limits: a distribution that no longer
- * fits the tensor raises storage).  Takes the current values of the
+ * paragraph on bits: an exponent offset estimated on at most 4096 sampled
+ * values adapts the code to the tensor's magnitude; paragraph on the limits:
+ * a distribution that no longer fits the tensor raises storage).  Takes the current values of the
  * compressed tensor *t (decoded with *cb) at positions floor(i * n / m),
  * m = min(n, 4096), as lct_codebook_build does, and picks the shift that
  * minimises their coded bits under cb's base code (same search and ties).
@@ -241,8 +242,8 @@ lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_ten
 lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_y, void *stream);
 
 /* Fused SGD step (explainer, paragraph on training traffic: read the
- * compressed inputs, compute, write the new exponent and sign-fraction bytes
- * in one pass).  W' = W - eta * M, element by element as
+ * compressed operands once, do the arithmetic, and store the re-encoded
+ * result, all in a single pass).  W' = W - eta * M, element by element as
  * rne_bf16(fmaf(-eta, f32(m), f32(w))) with a NaN result written as 0x7FC0;
  * W' is encoded with cw (the codebook of W).  w_in, m, w_out share n and
  * layout.  w_out's sf, pay, cnt and obase may be w_in's own (in-place update);

@@ -3,8 +3,9 @@
 // Explainer "LCT paper - Lossless Huffman coding of BF16 training tensors",
 // paragraph on bits: exponents are Huffman-coded with codes of at most 8 bits;
 // rare exponents share one escape code followed by the 8-bit field; the
-// codebook is precomputed from a Gaussian, Laplace or power-law model the user
-// picks, plus a small shift sampled from up to 4096 elements.  The LCT
+// code is fixed ahead of training from a Gaussian, Laplace or power-law model
+// chosen by the user, with an exponent offset estimated on at most 4096
+// sampled values.  The LCT
 // abstract names the adaptation to magnitude shifts.
 //
 // Readings taken where the passage is silent:

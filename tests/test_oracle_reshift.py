@@ -3,8 +3,9 @@ with another codebook.
 
 Passages followed: LCT abstract (adaptation to magnitude shifts); explainer
 "LCT paper - Lossless Huffman coding of BF16 training tensors", paragraph on
-bits (the codebook is precomputed; a small shift sampled from up to 4096
-elements follows the tensor's scale; no codebook is built during training)
+bits (the code is fixed ahead of training; an exponent offset estimated on
+at most 4096 sampled values adapts it to the tensor's magnitude; training
+builds no new code)
 and paragraph on the limits (a distribution that no longer fits the tensor
 raises storage).  Reading: re-estimating keeps the base code and picks a new
 shift from the tensor's current values, sampled at the build's positions.
