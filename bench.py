@@ -446,7 +446,7 @@ def activation_leg(L, dev, seq=3500, hid=2560, ffn=9728, reps=5):
         for t in [x] + ws:
             t.grad = None
         if compress:
-            with compressed_activations(L.Model(L.GAUSSIAN, 1.0, 0.0)):
+            with compressed_activations(L.Model(L.POWERLAW, 1.0, 3.0)):
                 step()
         else:
             step()
@@ -461,7 +461,7 @@ def activation_leg(L, dev, seq=3500, hid=2560, ffn=9728, reps=5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             if compress:
-                with compressed_activations(L.Model(L.GAUSSIAN, 1.0, 0.0)) as codec:
+                with compressed_activations(L.Model(L.POWERLAW, 1.0, 3.0)) as codec:
                     step()
             else:
                 step()

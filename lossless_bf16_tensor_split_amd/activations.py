@@ -35,7 +35,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (CLEAN, GAUSSIAN, Codebook, LctGroup, LctTensor, Model, lct_codebook_build,
+from . import (CLEAN, POWERLAW, Codebook, LctGroup, LctTensor, Model, lct_codebook_build,
                lct_codebook_from_lengths, lct_decode, lct_encode_group, lct_layout_init, lct_sizes)
 
 
@@ -52,7 +52,11 @@ class ActivationCodec:
 
     def __init__(self, model: Model | None = None, mode: int = CLEAN, min_elems: int = 1 << 16,
                  pool: int = 3):
-        self.model = Model(GAUSSIAN, 1.0, 0.0) if model is None else model
+        # Default: Student-t with 3 degrees of freedom.  Products of activations
+        # (a gated MLP's silu(g) * u) have heavy tails that a Gaussian code sends
+        # to the escape and, past a stream's capacity, to the overflow region;
+        # the t code keeps near-Gaussian tensors at the same size.
+        self.model = Model(POWERLAW, 1.0, 3.0) if model is None else model
         self.base = lct_codebook_build(self.model, None)
         self.len_base = list(self.base.len_base)
         self.layout = lct_layout_init(mode)
