@@ -7,7 +7,7 @@ configuration the benchmark times.
   properties that hold at any size.
 - The same set's momentum step, in place, on sampled blocks.
 - The 162M-parameter GPT-style set as a group of its 50 tensors, each with its
-  own codebook, one step checked in full.
+  own codebook: one step, and one momentum step, checked in full.
 """
 import numpy as np
 import pytest
@@ -202,3 +202,40 @@ def test_qwen3_4b_momentum_sampled(L, orc):
         refw, refm = orc.momentum(ocw, rw, ocm, rm, xg, 0.9, eta)
         same_block(block_of(ow, b, n), refw, "W' block %d" % b)
         same_block(block_of(om, b, n), refm, "M' block %d" % b)
+
+
+def test_gpt162m_group_momentum(L, orc):
+    """The momentum step over the 162M-parameter set's 50 tensors as groups
+    (per-tensor codebooks; the gradients bound as a third group's dense
+    buffers), in place, checked in full against the oracle's momentum step of
+    each tensor."""
+    ws, ms, mw, mm, eta = synth.config3()
+    wx = [synth.draw(s) for s in ws]
+    mx = [synth.draw(s) for s in ms]
+    gr = np.random.default_rng(3100)
+    gx = [synth.to_bf16_bits(gr.normal(0, 4.359e-4, len(x))) for x in wx]
+    ns = [len(x) for x in wx]
+    B, cw = synth.mode_layout(synth.CLEAN)
+    lay = L.layout(B, cw)
+    ocw = [orc.codebook_build(mw.family, mw.scale, mw.shape, x) for x in wx]
+    ocm = [orc.codebook_build(mm.family, mm.scale, mm.shape, x) for x in mx]
+    todev = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wd, md, gd = [todev(x) for x in wx], [todev(x) for x in mx], [todev(x) for x in gx]
+    lib_cb = lambda c: L.lct_codebook_from_lengths(list(c.len_base), c.esc_len, c.shift)
+    gw = L.LctGroup(ns, lay, [lib_cb(c) for c in ocw], wd)
+    gm = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], md)
+    gg = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], gd)
+    cap = sum(ns) // 64
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    rw = [orc.encode(c, x, B, cw) for c, x in zip(ocw, wx)]
+    rm = [orc.encode(c, x, B, cw) for c, x in zip(ocm, mx)]
+    w_out = gw.alloc_storage(cap, scratch=w_all.scratch)
+    m_out = gm.alloc_storage(cap, scratch=m_all.scratch)
+    w_out.sf, w_out.pay, w_out.cnt, w_out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+    m_out.sf, m_out.pay, m_out.cnt, m_out.obase = m_all.sf, m_all.pay, m_all.cnt, m_all.obase
+    L.lct_momentum_step_group(gw, w_all, gm, m_all, gg, 0.9, eta, w_out, m_out)
+    refs = [orc.momentum(ocw[k], rw[k], ocm[k], rm[k], gx[k], 0.9, eta) for k in range(len(ns))]
+    storage_equal(L, gw, w_out, orc.group([r[0] for r in refs], cap), ns, "W'")
+    storage_equal(L, gm, m_out, orc.group([r[1] for r in refs], cap), ns, "M'")
