@@ -6,6 +6,8 @@ configuration the benchmark times.
   on evenly spread sampled blocks (the last, partial block included) and by
   properties that hold at any size.
 - The same set's momentum step, in place, on sampled blocks.
+- The same set's shift sample and re-estimated shift, as built and scaled by
+  2^4 (most of it spilled), against the dense values and the oracle's search.
 - The 162M-parameter GPT-style set as a group of its 50 tensors, each with its
   own codebook: one step, and one momentum step, checked in full.
 """
@@ -239,3 +241,33 @@ def test_gpt162m_group_momentum(L, orc):
     refs = [orc.momentum(ocw[k], rw[k], ocm[k], rm[k], gx[k], 0.9, eta) for k in range(len(ns))]
     storage_equal(L, gw, w_out, orc.group([r[0] for r in refs], cap), ns, "W'")
     storage_equal(L, gm, m_out, orc.group([r[1] for r in refs], cap), ns, "M'")
+
+
+def test_qwen3_4b_sample_and_reshift(L, orc):
+    """Shift re-estimation at the full 4.02B-element size: the sample read
+    back from the compressed tensor is the dense tensor at the build's
+    positions, and the new shift is the oracle's search over that sample, for
+    the tensor as built and for the tensor scaled by 2^4 (its exponents moved
+    by four against a code that no longer fits, most of it spilled)."""
+    wspec, _, mw, _, _ = synth.config5()
+    n = wspec.numel
+    dev = torch.device("cuda", 0)
+    lay = L.lct_layout_init(L.CLEAN)
+    w = synth.draw_device(wspec, dev)
+    cbw = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), w)
+    pos = torch.as_tensor(orc.sample_positions(n).astype(np.int64), device=dev)
+    t = L.alloc_tensor(n, lay, n, dev)
+    for k, x in enumerate((w, (w.float() * 16.0).to(torch.bfloat16))):
+        L.lct_encode(cbw, x, t)
+        torch.cuda.synchronize()
+        assert t.status_word() == 0
+        want = x.view(torch.int16)[pos].cpu().numpy().view(np.uint16)
+        got = L.lct_tensor_sample(cbw, t)
+        assert np.array_equal(got, want), "sample of tensor %d" % k
+        r = L.lct_codebook_reshift(cbw, t)
+        ref = orc.codebook_from_sample(mw.family, mw.scale, mw.shape, want)
+        assert r.shift == ref.shift, (k, r.shift, ref.shift)
+        assert np.array_equal(np.frombuffer(bytes(r.code), np.uint32), ref.code), k
+        if k == 1:
+            assert t.spilled() > n // 4 and r.shift == cbw.shift + 4
+        del x
