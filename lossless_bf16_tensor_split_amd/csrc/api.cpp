@@ -203,9 +203,10 @@ void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const
     p.park_cnt = p.o_cnt == p.w_cnt;
 }
 
-// Clear, update, scan.
-lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream, bool dense = false) {
-    int e = launch_clear(p.scratch, nb, p.status, stream);
+// Clear, update, scan.  carry: see launch_clear.
+lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream, bool dense = false,
+                      const uint32_t *carry = nullptr) {
+    int e = launch_clear(p.scratch, nb, p.status, stream, carry);
     if (e != hipSuccess) return hip_fail(e, "clear launch");
     e = launch_sgd(p, stream, group, dense);
     if (e != hipSuccess) return hip_fail(e, "sgd launch");
@@ -554,7 +555,8 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
     fill_enc(*cw_out, &p2.wenc);
     fill_dec(*cw, &p2.wdec);
     fill_dec(*cm_out, &p2.mdec);
-    return sgd_launch(p2, nb, false, stream);
+    // W' is computed from M' as stored: if M' lost spilled fields, so did W'
+    return sgd_launch(p2, nb, false, stream, false, m_out->status);
 }
 
 // ---- groups
@@ -805,7 +807,7 @@ lct_status lct_momentum_step_group(const lct_group *gw, const lct_tensor *w_all,
     sgd_params(p2, *w_all, m_out, *w_out, nb, -eta);
     p2.gw = group_ref(*gw);
     p2.gm = group_ref(*gm);
-    return sgd_launch(p2, nb, true, stream);
+    return sgd_launch(p2, nb, true, stream, false, m_out->status);
 }
 
 const char *lct_strerror(lct_status st) {

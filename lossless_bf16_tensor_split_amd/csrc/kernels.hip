@@ -567,10 +567,13 @@ __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_
 
 // ------------------------------------------------------------------ small kernels
 
-__global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
+// carry (may be null): a status word whose overflow bit the cleared word
+// starts with (an output computed from a tensor whose overflow region ran
+// out is marked invalid too)
+__global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status, const uint32_t *carry) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nwords) words[i] = 0;
-    if (i == 0) *status = 0;
+    if (i == 0) *status = carry ? (*carry & LCT_ST_OVF_FULL) : 0u;
 }
 
 // Overflow offsets: an exclusive scan of the units' spill totals in unit
@@ -1632,11 +1635,11 @@ size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wav
 size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
 size_t sgd_lds(uint32_t cap, bool dense) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap, dense); }
 
-int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
+int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream, const uint32_t *carry) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
     const uint32_t grid = (uint32_t)((words + 255) / 256);
     hipLaunchKernelGGL(k_clear, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                       reinterpret_cast<uint64_t *>(scratch), words, status);
+                       reinterpret_cast<uint64_t *>(scratch), words, status, carry);
     return (int)hipGetLastError();
 }
 

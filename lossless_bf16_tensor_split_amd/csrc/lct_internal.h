@@ -204,7 +204,9 @@ struct FitParams {
 };
 
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
-int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
+// carry (may be null): the cleared status word starts with carry's overflow bit
+int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream,
+                 const uint32_t *carry = nullptr);
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
                 uint32_t *status, uint16_t *cnt, void *stream);
 int launch_encode(const EncodeParams &p, void *stream, bool group = false);

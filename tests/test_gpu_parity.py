@@ -325,6 +325,43 @@ def test_momentum_zero_rates(L, orc):
     assert np.array_equal(orc.decode(orc.codebook_build(0, 0.02, 0.0, w), ref_w), w)
 
 
+@pytest.mark.parametrize("inplace", [False, True])
+def test_momentum_m_overflow_marks_both_outputs(L, orc, inplace):
+    """M' spills past m_out's overflow region: W' is computed from M' as
+    stored, so w_out's status word carries the overflow bit as well, while
+    M''s fixed side and offsets are still complete."""
+    g = np.random.default_rng(41)
+    B, cw = 4096, 1
+    n = 6 * B + 77
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-2, n))
+    gr = synth.to_bf16_bits(g.normal(0, 0.1, n))
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-2)
+    cbw, ocw = check_codebook(L, orc, mw, w)
+    cbm, ocm = check_codebook(L, orc, mm, m)
+    lay = L.layout(B, cw)
+    tw, tm = L.encode(cbw, dev(w), lay), L.encode(cbm, dev(m), lay)
+    rw, rm = orc.encode(ocw, w, B, cw), orc.encode(ocm, m, B, cw)
+    ref_w, ref_m = orc.momentum(ocw, rw, ocm, rm, gr, 0.9, 0.05)
+    assert ref_m.spilled > 16
+    ow = L.alloc_tensor(n, lay)                      # W' has room for every spill
+    om = L.alloc_tensor(n, lay, ovf_cap=ref_m.spilled // 2)
+    if inplace:
+        ow.sf, ow.pay, ow.cnt, ow.obase = tw.sf, tw.pay, tw.cnt, tw.obase
+        om.sf, om.pay, om.cnt, om.obase = tm.sf, tm.pay, tm.cnt, tm.obase
+    L.lct_momentum_step(cbw, tw, cbm, tm, dev(gr), 0.9, 0.05, ow, om)
+    gm_ = host_parts(om)
+    assert gm_["status"] == L.ST_OVF_FULL
+    assert ow.status_word() & L.ST_OVF_FULL
+    for k in ["sf", "pay", "cnt", "obase"]:
+        assert np.array_equal(gm_[k], getattr(ref_m, k)), "M' " + k
+    # with room for both, neither is marked
+    ow2, om2 = L.alloc_tensor(n, lay), L.alloc_tensor(n, lay)
+    L.lct_momentum_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), dev(gr), 0.9, 0.05,
+                        ow2, om2)
+    assert ow2.status_word() == 0 and om2.status_word() == 0
+
+
 def test_momentum_gpt162m_flat(L, orc):
     """One momentum step over the flat 162M-parameter set, checked in full."""
     ws, ms, mw, mm, eta = synth.config3()
