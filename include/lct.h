@@ -24,9 +24,10 @@
  *   - Pointers named d_* and every pointer inside lct_tensor are DEVICE
  *     pointers on the current HIP device; every other pointer is host memory.
  *   - The caller allocates and frees every device buffer, sized by lct_sizes().
- *     The library allocates no device memory of its own, except one 8 KiB
- *     static array per device used by lct_codebook_build() and
- *     lct_codebook_reshift() for their sample.
+ *     The library allocates no device memory of its own, except two static
+ *     arrays per device: 8 KiB used by lct_codebook_build() and
+ *     lct_codebook_reshift() for their sample, and the working memory of
+ *     lct_sgd_step_noalloc() (LCT_NOALLOC_SCRATCH_BYTES).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     lct_encode, lct_decode and the update calls (lct_sgd_step*,
  *     lct_momentum_step*) only enqueue work on it and return at once;
@@ -56,7 +57,9 @@ typedef enum {
     LCT_EALIGN = -2,  /* device pointer not aligned as documented */
     LCT_EALIAS = -3,  /* output overlaps an input it must not overlap */
     LCT_EHIP = -4,    /* a HIP runtime call failed (message via lct_last_hip_error) */
-    LCT_EARCH = -5    /* current device is not gfx950 */
+    LCT_EARCH = -5,   /* current device is not gfx950 */
+    LCT_ESIZE = -6    /* lct_sgd_step_noalloc: the tensor needs more working memory
+                         than its static scratch holds */
 } lct_status;
 
 /* Device status word bits, OR-ed in by the kernels (the word is cleared at the
@@ -254,6 +257,26 @@ lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_
 lct_status lct_sgd_step(const lct_codebook *cw, const lct_tensor *w_in,
                         const lct_codebook *cm, const lct_tensor *m,
                         float eta, const lct_tensor *w_out, void *stream);
+
+/* lct_sgd_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step, arguments, rules and errors, except that w_out->scratch is
+ * ignored (it may be NULL) and the library's own static working memory is used
+ * instead: one array of LCT_NOALLOC_SCRATCH_BYTES per device, reserved when the
+ * library is loaded and held until the process ends.  The call allocates
+ * nothing.  The working memory needed is lct_sizes(n, layout,
+ * w_out->ovf_cap).scratch; more than LCT_NOALLOC_SCRATCH_BYTES returns
+ * LCT_ESIZE before anything is enqueued (16 MiB holds, e.g., a 2^24-element
+ * tensor with ovf_cap up to 8,314,624 bytes, or ovf_cap = n up to about 8.3M
+ * elements).  Every call on a device shares
+ * that device's array: calls that overlap in time on one device (on
+ * different streams, or from several host threads without ordering) race and
+ * give undefined results.  The array keeps the last call's contents; what must
+ * start at zero is cleared by a kernel on `stream` at the start of each call. */
+#define LCT_NOALLOC_SCRATCH_BYTES (16u << 20)
+lct_status lct_sgd_step_noalloc(const lct_codebook *cw, const lct_tensor *w_in,
+                                const lct_codebook *cm, const lct_tensor *m,
+                                float eta, const lct_tensor *w_out, void *stream);
 
 /* lct_sgd_step with W' encoded with cw_out instead of cw (W is still decoded
  * with cw): the step that moves W onto a codebook from lct_codebook_reshift.

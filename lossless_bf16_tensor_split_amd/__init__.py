@@ -18,6 +18,7 @@ Functions keep the C names:
     lct_decode(cb, t, y)
     lct_sgd_step(cw, w_in, cm, m, eta, w_out)
     lct_sgd_step_recode(cw, w_in, cm, m, eta, cw_out, w_out)
+    lct_sgd_step_noalloc(cw, w_in, cm, m, eta, w_out)   (static working memory)
     lct_momentum_step(cw, w_in, cm, m_in, g, mu, eta, w_out, m_out)
     lct_momentum_step_recode(cw, w_in, cm, m_in, g, mu, eta, cw_out, cm_out, w_out, m_out)
     LctGroup(ns, layout, codebooks, dense)  (lct_group_table_bytes + lct_group_bind)
@@ -40,12 +41,13 @@ LIB_PATH = os.path.join(_HERE, "liblct.so")
 GAUSSIAN, LAPLACE, POWERLAW = 0, 1, 2
 CLEAN, MEDIUM, HIGH = 0, 1, 2
 ST_OVF_FULL, ST_LOOKBACK = 0x1, 0x2
-OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EALIAS, EHIP, EARCH, ESIZE = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ["lct_layout_init", "lct_sizes", "lct_codebook_build", "lct_codebook_from_lengths",
             "lct_tensor_sample", "lct_codebook_reshift", "lct_codebook_reshift_dense",
             "lct_codebook_adapt", "lct_encode", "lct_decode",
-            "lct_sgd_step", "lct_sgd_step_recode", "lct_momentum_step", "lct_momentum_step_recode",
+            "lct_sgd_step", "lct_sgd_step_recode", "lct_sgd_step_noalloc", "lct_momentum_step", "lct_momentum_step_recode",
             "lct_group_table_bytes", "lct_group_bind", "lct_group_fit", "lct_group_sizes", "lct_group_tensor",
             "lct_encode_group", "lct_decode_group", "lct_sgd_step_group", "lct_momentum_step_group",
             "lct_strerror", "lct_last_hip_error"]
@@ -120,6 +122,8 @@ def _load():
     L.lct_decode.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), P, P]
     L.lct_sgd_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
                                C.POINTER(_Tensor), C.c_float, C.POINTER(_Tensor), P]
+    L.lct_sgd_step_noalloc.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
+                                       C.POINTER(_Tensor), C.c_float, C.POINTER(_Tensor), P]
     L.lct_momentum_step.argtypes = [C.POINTER(Codebook), C.POINTER(_Tensor), C.POINTER(Codebook),
                                     C.POINTER(_Tensor), P, C.c_float, C.c_float, C.POINTER(_Tensor),
                                     C.POINTER(_Tensor), P]
@@ -330,6 +334,15 @@ def lct_sgd_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta:
     a, b, o = w_in.c(), m.c(), w_out.c()
     _check(lib.lct_sgd_step(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta, C.byref(o),
                             _stream(stream)), "lct_sgd_step")
+
+
+def lct_sgd_step_noalloc(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta: float,
+                         w_out: LctTensor, stream=None) -> None:
+    """lct_sgd_step with the library's static working memory (w_out's
+    scratch is not used)."""
+    a, b, o = w_in.c(), m.c(), w_out.c()
+    _check(lib.lct_sgd_step_noalloc(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta, C.byref(o),
+                                    _stream(stream)), "lct_sgd_step_noalloc")
 
 
 def lct_sgd_step_recode(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTensor, eta: float,

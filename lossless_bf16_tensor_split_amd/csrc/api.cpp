@@ -505,6 +505,22 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in, c
     return sgd_run(p, *w_in, *m, *w_out, nb, eta, false, stream);
 }
 
+lct_status lct_sgd_step_noalloc(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
+                                const lct_tensor *m, float eta, const lct_tensor *w_out, void *stream) {
+    if (!cw || !cm || !w_in || !m || !w_out) return LCT_EINVAL;
+    if (w_out->n == 0) return lct_sgd_step(cw, w_in, cm, m, eta, w_out, stream);
+    if (!layout_ok(w_out->layout)) return LCT_EINVAL;
+    if (scr_bytes(nblocks(w_out->n, w_out->layout), w_out->ovf_cap) > kNoAllocScratch) return LCT_ESIZE;
+    lct_status st = check_arch();
+    if (st != LCT_OK) return st;
+    uint8_t *scr = nullptr;
+    const int e = noalloc_scratch(&scr);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    lct_tensor out = *w_out;
+    out.scratch = scr;
+    return lct_sgd_step(cw, w_in, cm, m, eta, &out, stream);
+}
+
 lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
                              const lct_tensor *m_in, const uint16_t *d_g, float mu, float eta,
                              const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
@@ -818,6 +834,7 @@ const char *lct_strerror(lct_status st) {
     case LCT_EALIAS: return "illegal buffer overlap";
     case LCT_EHIP: return "HIP runtime error";
     case LCT_EARCH: return "device is not gfx950";
+    case LCT_ESIZE: return "working memory needed exceeds the static scratch of the allocation-free call";
     }
     return "unknown status";
 }

@@ -62,6 +62,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "lct_internal.h"
 
@@ -1693,6 +1694,33 @@ int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out) {
 int launch_fit(const FitParams &p, void *stream) {
     hipLaunchKernelGGL(k_fit, dim3(1), dim3(256), 0, (hipStream_t)stream, p);
     return (int)hipGetLastError();
+}
+
+// The allocation-free update's working memory: one static array per device,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol); the device address is
+// taken once per device with hipGetSymbolAddress and kept.
+namespace noalloc {
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+std::mutex g_mu;
+void *g_ptr[kMaxDevices];
+}  // namespace noalloc
+
+int noalloc_scratch(uint8_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(noalloc::g_mu);
+    if (!noalloc::g_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        noalloc::g_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(noalloc::g_ptr[dev]);
+    return hipSuccess;
 }
 
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out) {

@@ -203,6 +203,13 @@ struct FitParams {
     int32_t *shift_out;      // may be null
 };
 
+// The allocation-free update's static working memory (per device).
+constexpr uint64_t kNoAllocScratch = LCT_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+// Device address of the current device's static working memory, looked up
+// once per device (hipGetSymbolAddress).  Returns a hipError_t.
+int noalloc_scratch(uint8_t **out);
+
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
 // carry (may be null): the cleared status word starts with carry's overflow bit
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream,
