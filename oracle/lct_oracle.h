@@ -22,10 +22,12 @@
  * Where the pages are silent, a convention had to be fixed; every function
  * below states the reading it takes.
  *
- * Parity status: every function here is pinned by tests/test_oracle_*.py,
- * except the model probability mass (lcto_model_pmf), whose floating CDFs are
- * only checked loosely (mass sums to one, Monte Carlo histogram, closed forms
- * for Student-t with 1 and 3 degrees of freedom): "parity unpinned" beyond that.
+ * Parity status: every function here is pinned by tests/test_oracle_*.py.
+ * The model probability mass (lcto_model_pmf) and the integer weights
+ * (lcto_weights) are pinned bin by bin against 50-digit evaluations of the
+ * survival functions written from their definitions (erfc, exp, the
+ * regularized incomplete beta), for Gaussian, Laplace and Student-t models
+ * with 1, 2, 3 and 5.5 degrees of freedom at several scales.
  */
 #ifndef LCT_ORACLE_H
 #define LCT_ORACLE_H
