@@ -330,7 +330,10 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
  *
  * The group's storage is one lct_tensor whose n is the group's sf_bytes and
  * whose arrays are sized by lct_group_sizes; its status word and scratch
- * serve the whole group. */
+ * serve the whole group.  The sf bytes between one member's last element and
+ * the next member's start (the padding to a multiple of 256) are never read
+ * or written by any call: storage whose sf array was zeroed once keeps zero
+ * padding, as the format's reference layout has it. */
 typedef struct {
     uint32_t count;              /* tensors */
     lct_layout layout;

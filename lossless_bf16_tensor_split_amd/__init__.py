@@ -293,6 +293,12 @@ class LctTensor:
         ends = self.obase[[0, -1]].cpu()
         return int(ends[1]) - int(ends[0])
 
+    def full_path_units(self) -> int:
+        """Units (64 streams of a block) that the last update writing this
+        tensor ran on its full-block path: a counter the update keeps in the
+        header of its working memory (byte offset 28), for tests."""
+        return int(self.scratch[28:32].view(torch.int32).item())
+
     def nbytes(self) -> int:
         return int(self.sizes.fixed) + self.spilled()
 
@@ -459,8 +465,15 @@ class LctGroup:
             ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
         elif ovf.numel() < ovf_cap:
             raise ValueError("ovf too small: %d < %d" % (ovf.numel(), ovf_cap))
-        return LctTensor.wrap(int(self.g.sf_bytes), self.layout, ovf_cap, sz,
-                              torch.empty(max(sz.sf, 16), dtype=u8, device=dev),
+        # the padding after each member is zeroed once: no call writes it,
+        # so it stays zero
+        sf = torch.empty(max(sz.sf, 16), dtype=u8, device=dev)
+        if self.count == 1:
+            if int(self.ns[0]) % 256:
+                sf[int(self.ns[0]):].zero_()
+        else:
+            sf.zero_()
+        return LctTensor.wrap(int(self.g.sf_bytes), self.layout, ovf_cap, sz, sf,
                               torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev),
                               torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev),
                               torch.empty(sz.obase // 8, dtype=torch.int64, device=dev),

@@ -1502,6 +1502,7 @@ void k_sgd(const SgdParams p) {
     // share no data).  Both take the same number of trips, the unit count
     // being even.
     static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
+    uint32_t nfull = 0;   // units done on the full-block path
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
@@ -1549,6 +1550,7 @@ void k_sgd(const SgdParams p) {
         st.rows.init(p.o_pay, b, h, cap);
         if (fast) {
             sgd_stream_full<CAPT, DENSE>(p, lay, st, r0 + h * US, gu);
+            ++nfull;
         } else {
             uint32_t cw_s, cm_s = 0, wex, mex = 0;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
@@ -1562,6 +1564,7 @@ void k_sgd(const SgdParams p) {
                         p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
         unit_finish(st, n_s, u, b, h, 0, o);
     }
+    if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
 }
 
 // ------------------------------------------------------------------ launches

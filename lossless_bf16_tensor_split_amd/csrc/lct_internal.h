@@ -32,6 +32,8 @@ constexpr uint64_t kScrTicket2 = 4;   // uint32: next group of the scan kernel
 constexpr uint64_t kScrStage = 8;     // uint64: bytes claimed in the first staging area
 constexpr uint64_t kScrStage2 = 16;   // uint64: bytes claimed in the second
 constexpr uint64_t kScrParked = 24;   // uint32: nonzero when some unit parked its counts
+constexpr uint64_t kScrFullUnits = 28;  // uint32: units the update ran on its full-block path
+                                        // (read by tests to show which path ran)
 constexpr uint64_t kScrFlags = 64;    // uint64[groups + 1]: the scan's look-back flags
 constexpr uint32_t kScanGroup = 256;  // units per scan workgroup
 __host__ __device__ inline uint64_t scr_units(uint64_t nblk) { return kMaxUnits * nblk; }

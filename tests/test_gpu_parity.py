@@ -201,7 +201,7 @@ def sgd_case(L, orc, w, m, mw, mm, eta, B, cw, inplace, what=""):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 2), (8192, 3), (32768, 12)])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 2), (8192, 3), (32768, 12), (32768, 11)])
 def test_sgd_small_with_spills(L, orc, B, cw, inplace):
     g = np.random.default_rng(B + cw)
     n = 7 * B + 333
@@ -241,6 +241,54 @@ def test_sgd_full_blocks_escapes_and_nans(L, orc, inplace):
     assert orc.encode(ocw, w, lay_b, lay_c).spilled == 0
     assert orc.encode(ocm, m, lay_b, lay_c).spilled == 0
     sgd_case(L, orc, w, m, mw, mm, 1e-3, lay_b, lay_c, inplace, what="escapes/nans inplace=%s" % inplace)
+
+
+def narrow_values(orc, g, sigma, n, extra=0.01):
+    """BF16 values whose exponent fields are the two with the shortest codes
+    of the Gaussian(sigma) codebook (a share `extra` takes the third
+    shortest), with random signs and fractions: about two bits a field, so
+    even HIGH's 2.75 bits a field hold every stream without a spill."""
+    base = orc.codebook_build(0, sigma, 0.0, synth.to_bf16_bits(g.normal(0, sigma, 65536)))
+    order = np.argsort(np.where(base.len == 0, 99, base.len), kind="stable")
+    e = np.where(g.random(n) < extra, order[2], order[g.integers(0, 2, n)]).astype(np.uint16)
+    return ((g.integers(0, 2, n).astype(np.uint16) << 15) | (e << 7)
+            | g.integers(0, 128, n).astype(np.uint16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (32768, 12), (32768, 11)])
+def test_full_block_path_in_every_mode(L, orc, B, cw, inplace):
+    """Full blocks whose inputs spill nothing in CLEAN, MEDIUM and HIGH: every
+    unit of the update takes the full-block path (its own counter says so),
+    and W' equals the oracle's round trip; the momentum step's two passes
+    likewise."""
+    g = np.random.default_rng(B + 7 * cw)
+    nblk = 6
+    n = nblk * B
+    w = narrow_values(orc, g, 0.02, n)
+    m = narrow_values(orc, g, 1e-3, n)
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-3)
+    ocw, ocm = orc.codebook_build(0, 0.02, 0.0, w), orc.codebook_build(0, 1e-3, 0.0, m)
+    rw, rm = orc.encode(ocw, w, B, cw), orc.encode(ocm, m, B, cw)
+    assert rw.spilled == 0 and rm.spilled == 0
+    sgd_case(L, orc, w, m, mw, mm, 1e-3, B, cw, inplace, what="full path B=%d cw=%d" % (B, cw))
+    # sgd_case's output: run again to read its counter
+    cbw = L.lct_codebook_build(L.Model(0, 0.02, 0.0), dev(w))
+    cbm = L.lct_codebook_build(L.Model(0, 1e-3, 0.0), dev(m))
+    lay = L.layout(B, cw)
+    tw, tm = L.encode(cbw, dev(w), lay), L.encode(cbm, dev(m), lay)
+    out = L.alloc_tensor(n, lay)
+    L.lct_sgd_step(cbw, tw, cbm, tm, 1e-3, out)
+    assert out.full_path_units() == 4 * nblk
+    # momentum: M' = 0.9 M + g keeps M's fields within its short codes
+    gr = synth.to_bf16_bits(g.normal(0, 1e-6, n))
+    ref_w, ref_m = momentum_case(L, orc, w, m, gr, mw, mm, 0.9, 1e-3, B, cw, inplace,
+                                 what="full path momentum B=%d cw=%d" % (B, cw))
+    assert ref_m.spilled == 0
+    ow, om = L.alloc_tensor(n, lay), L.alloc_tensor(n, lay)
+    L.lct_momentum_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), dev(gr), 0.9, 1e-3,
+                        ow, om)
+    assert om.full_path_units() == 4 * nblk and ow.full_path_units() == 4 * nblk
 
 
 def test_sgd_eta_zero_identity(L, orc):
@@ -293,7 +341,7 @@ def momentum_case(L, orc, w, m, gr, mw, mm, mu, eta, B, cw, inplace, what=""):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 1), (8192, 3), (32768, 12)])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 1), (8192, 3), (32768, 12), (32768, 11)])
 def test_momentum_small_with_spills(L, orc, B, cw, inplace):
     g = np.random.default_rng(B + 3 * cw)
     n = 5 * B + 531

@@ -66,7 +66,7 @@ def reshift_case(L, orc, x, ocb, B, cw, what=""):
 
 
 @pytest.mark.parametrize("j", [-2, 0, 3, 6])
-@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 1), (32768, 12)])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 1), (32768, 12), (32768, 11)])
 def test_reshift_after_a_drift(L, orc, B, cw, j):
     """Values scaled by 2^j, encoded with the stale codebook (spilled fields
     fall in the sample), re-estimated from the compressed form."""
@@ -128,7 +128,7 @@ def test_adapt_moves_a_drifted_tensor_back(L, orc):
 # ------------------------------------------------------------------ updates with output codebooks
 
 @pytest.mark.parametrize("inplace", [False, True])
-@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 2)])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (4096, 2), (32768, 11)])
 def test_sgd_step_recode(L, orc, B, cw, inplace):
     """W decoded with its codebook, W' encoded with a re-estimated one; the
     CLEAN case has no spilled input field (the full-block path)."""
@@ -159,9 +159,9 @@ def test_sgd_step_recode(L, orc, B, cw, inplace):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-def test_momentum_step_recode(L, orc, inplace):
-    B, cw = 8192, 3
-    g = np.random.default_rng(8500)
+@pytest.mark.parametrize("B,cw", [(8192, 3), (32768, 11)])
+def test_momentum_step_recode(L, orc, B, cw, inplace):
+    g = np.random.default_rng(8500 + cw)
     n = 5 * B + 77
     w = synth.to_bf16_bits(g.normal(0, 0.02, n))
     m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
@@ -229,7 +229,7 @@ def test_device_fit_matches_the_host(L, orc, case):
     assert ob.shift == host.shift
     all_ = grp.alloc_storage(x.size)
     L.lct_encode_group(grp, all_)
-    ref = orc.encode(ob, x, 65536, 25)
+    ref = orc.group([orc.encode(ob, x, 65536, 25)], x.size)
     storage_equal(L, grp, all_, ref, [x.size], "fit " + case)
     y = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
     L.lct_decode(host, grp.tensor(all_, 0), y)
