@@ -288,6 +288,9 @@ def main():
         next_ops["activations"] = activation_leg(L, dev)
         if args.workload == "qwen3_4b":
             next_ops["group"] = group_leg(L, dev, stream, w_dense, mspec, mw, mm, eta, lay)
+            del w_dense, tw, tw2, tm, scratch, scratch2
+            torch.cuda.empty_cache()
+            next_ops["configs"] = configs_leg(L, dev, stream)
 
     out = {
         "metric": METRIC,
@@ -319,6 +322,109 @@ def main():
         "next_ops": next_ops,
     }
     print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ the other workloads
+
+def configs_leg(L, dev, stream, reps=5):
+    """Per-op throughput on the smaller workloads, each op timed alone with
+    HIP events (median of `reps`) after a 1 GiB write that evicts the 256 MB
+    last-level cache, so that every input comes from HBM:
+      - the 2^20-element Gaussian tensor (CLEAN): encode, decode;
+      - the three 2^26-element tensors (Laplace, Student-t(3), N(0,1) scaled by
+        2^k per 2^20 chunk) in MEDIUM and HIGH, whose streams overflow:
+        encode, decode;
+      - the flat 162M-parameter GPT-style set (CLEAN): encode W, the fused
+        update, decode W';
+      - the Qwen3-4B layer's activations (post-SiLU gate, residual with
+        outliers, uniform random bits) in CLEAN and MEDIUM: encode, decode.
+    Each entry gives GB/s of BF16 input (output for decode), the algorithmic
+    bytes (BF16 side, compressed sides, spilled bytes) over the time as a
+    fraction of 8 TB/s, the compression ratio, the overflow fraction (spilled
+    fields per element) and the allocated bits per exponent ((payload +
+    overflow bits) / n)."""
+    import numpy as np
+    import torch
+    import synth
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        ms = []
+        for _ in range(reps):
+            flush.fill_(7)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms)) / 1e3
+
+    def entry(t, s, alg, n, inout):
+        gbs = alg / s / 1e9
+        return {"ms": round(s * 1e3, 4), inout: round(2 * n / s / 1e9, 1),
+                "alg_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    def codec(x16, model, mode, sgd_with=None):
+        n = x16.numel()
+        lay = L.lct_layout_init(mode)
+        cb = L.lct_codebook_build(L.Model(model.family, model.scale, model.shape), x16)
+        t = L.alloc_tensor(n, lay, n, dev)
+        y = torch.empty_like(x16)
+        t_enc = timed(lambda: L.lct_encode(cb, x16, t))
+        st = t.status_word()
+        sp = t.spilled()
+        t_dec = timed(lambda: L.lct_decode(cb, t, y))
+        same = bool(torch.equal(y.view(torch.int16), x16.view(torch.int16)))
+        fixed = t.sizes.fixed
+        out = {"n": n, "mode": {0: "CLEAN", 1: "MEDIUM", 2: "HIGH"}[mode],
+               "layout": [lay.block_elems, lay.cap_words],
+               "encode": entry(t, t_enc, 2 * n + fixed + sp, n, "GBps_bf16_input"),
+               "decode": entry(t, t_dec, 2 * n + fixed + sp, n, "GBps_bf16_output"),
+               "ratio": round(t.ratio(), 5), "overflow_fraction": round(sp / n, 6),
+               "bits_per_exponent": round(8.0 * (t.sizes.pay + sp) / n, 4),
+               "status": st, "decoded_identical": same}
+        return out, cb, t
+
+    res = {"cache_flush": "1 GiB written before every timed op"}
+    x = torch.from_numpy(synth.draw(synth.config1()[0][0]).view(np.int16)).to(dev)
+    res["gauss_2^20"], _, _ = codec(x, synth.config1()[0][1], L.CLEAN)
+    for spec, model in synth.config2():
+        x = torch.from_numpy(synth.draw(spec).view(np.int16)).to(dev)
+        for mode in (L.MEDIUM, L.HIGH):
+            res["%s_2^26_%s" % (spec.name, {1: "medium", 2: "high"}[mode])], _, t = codec(x, model, mode)
+            del t
+        del x
+        torch.cuda.empty_cache()
+    # the 162M-parameter set: the step's three ops
+    ws, ms, mw, mm, eta = synth.config3()
+    n = sum(s.numel for s in ws)
+    w = synth.draw_device(synth.TensorSpec("W.flat", (n,), 3000, "normal", {"sigma": 0.02}), dev)
+    m = synth.draw_device(synth.TensorSpec("M.flat", (n,), 3001, "normal", {"sigma": 1e-3}), dev)
+    e, cbw, tw = codec(w, mw, L.CLEAN)
+    cbm = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), m)
+    tm = L.alloc_tensor(n, tw.layout, n, dev)
+    L.lct_encode(cbm, m, tm)
+    out = L.alloc_tensor(n, tw.layout, n, dev)
+    t_sgd = timed(lambda: L.lct_sgd_step(cbw, tw, cbm, tm, eta, out))
+    fixed = tw.sizes.fixed
+    alg = 3 * fixed + tw.spilled() + tm.spilled() + out.spilled()
+    e["sgd"] = {"ms": round(t_sgd * 1e3, 4), "elems_per_s": float("%.4g" % (n / t_sgd)),
+                "alg_GBps": round(alg / t_sgd / 1e9, 1), "hbm_frac": round(alg / t_sgd / 1e9 / PEAK_HBM_GBS, 4),
+                "status": out.status_word()}
+    res["gpt162m_flat"] = e
+    del w, m, tw, tm, out
+    torch.cuda.empty_cache()
+    for spec, model in synth.config4():
+        x = torch.from_numpy(synth.draw(spec).view(np.int16)).to(dev)
+        for mode in (L.CLEAN, L.MEDIUM):
+            res["act_%s_%s" % (spec.name, {0: "clean", 1: "medium"}[mode])], _, t = codec(x, model, mode)
+            del t
+        del x
+    del flush
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ tensor groups

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -140,7 +141,8 @@ GroupRef group_ref(const lct_group &g) {
     const GroupTableLayout t = group_table_layout(g.count, g.nblk);
     const uint8_t *base = static_cast<const uint8_t *>(g.d_table);
     return {reinterpret_cast<const GroupEntry *>(base + t.ent), reinterpret_cast<const EncTab *>(base + t.enc),
-            reinterpret_cast<const DecTab *>(base + t.dec), reinterpret_cast<const uint32_t *>(base + t.blk_tensor)};
+            reinterpret_cast<const DecTab *>(base + t.dec), reinterpret_cast<const uint32_t *>(base + t.blk_tensor),
+            reinterpret_cast<const uint32_t *>(base + t.blk_tab)};
 }
 
 // A bound group and storage sized for it.
@@ -614,6 +616,9 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
     auto *enc = reinterpret_cast<EncTab *>(host.data() + t.enc);
     auto *dec = reinterpret_cast<DecTab *>(host.data() + t.dec);
     auto *owner = reinterpret_cast<uint32_t *>(host.data() + t.blk_tensor);
+    auto *tabs = reinterpret_cast<uint32_t *>(host.data() + t.blk_tab);
+    // tensors whose tables are byte-identical share the first one's index
+    std::map<std::vector<uint8_t>, uint32_t> first_with;
     uint64_t b0 = 0, e0 = 0;
     for (uint32_t k = 0; k < count; ++k) {
         const uint64_t nbk = nblocks(n[k], *layout);
@@ -624,7 +629,14 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
         ent[k].nblk = (uint32_t)nbk;
         fill_enc(cbs[k], &enc[k]);
         fill_dec(cbs[k], &dec[k]);
-        for (uint64_t j = 0; j < nbk; ++j) owner[b0 + j] = k;
+        std::vector<uint8_t> key(sizeof(EncTab) + sizeof(DecTab));
+        memcpy(key.data(), &enc[k], sizeof(EncTab));
+        memcpy(key.data() + sizeof(EncTab), &dec[k], sizeof(DecTab));
+        const uint32_t tab = first_with.emplace(std::move(key), k).first->second;
+        for (uint64_t j = 0; j < nbk; ++j) {
+            owner[b0 + j] = k;
+            tabs[b0 + j] = tab;
+        }
         b0 += nbk;
         e0 += round256(n[k]);
     }
@@ -666,6 +678,7 @@ lct_status lct_group_fit(const lct_codebook *base, const uint64_t *n, uint16_t *
     p.enc = reinterpret_cast<EncTab *>(tab + t.enc);
     p.dec = reinterpret_cast<DecTab *>(tab + t.dec);
     p.blk_tensor = reinterpret_cast<uint32_t *>(tab + t.blk_tensor);
+    p.blk_tab = reinterpret_cast<uint32_t *>(tab + t.blk_tab);
     p.shift_out = d_shift;
     const int e = launch_fit(p, stream);
     if (e != hipSuccess) return hip_fail(e, "fit launch");

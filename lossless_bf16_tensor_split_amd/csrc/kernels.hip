@@ -821,7 +821,10 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
         *p.ent = GroupEntry{p.x, p.n, 0, 0, p.nblk};
         if (p.shift_out) *p.shift_out = k;
     }
-    for (uint32_t b = t; b < p.nblk; b += 256) p.blk_tensor[b] = 0;
+    for (uint32_t b = t; b < p.nblk; b += 256) {
+        p.blk_tensor[b] = 0;
+        p.blk_tab[b] = 0;
+    }
 }
 
 // ------------------------------------------------------------------ step driver
@@ -1484,7 +1487,7 @@ void k_sgd(const SgdParams p) {
     }
     if (threadIdx.x < 2) st32(kSgdNone + 4 * threadIdx.x, 0);
     __syncthreads();
-    uint32_t staged = ~0u;   // the group tensor whose tables are in LDS
+    uint64_t staged = ~0ull;   // the group tables in LDS: W's (and W''s) and M's, as table indices
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap, DENSE), DENSE);
@@ -1509,14 +1512,18 @@ void k_sgd(const SgdParams p) {
         uint32_t k = 0;
         if (GROUP) {
             // both waves work on one block, so on one tensor; the barrier
-            // above means neither still reads the tables being replaced
+            // above means neither still reads the tables being replaced.
+            // Tensors with identical tables share an index: a pair that moves
+            // to another tensor stages tables only when they differ.
             k = p.gw.blk_tensor[b];
-            if (k != staged) {
-                stage_dec(p.gw.dec[k], kSgdWTab);
-                if (!DENSE) stage_dec(p.gm.dec[k], kSgdMTab);
-                stage_enc(p.gw.enc[k], kSgdETab);
+            const uint32_t tw = p.gw.blk_tab[b], tm = DENSE ? 0u : p.gm.blk_tab[b];
+            const uint64_t key = ((uint64_t)tm << 32) | tw;
+            if (key != staged) {
+                stage_dec(p.gw.dec[tw], kSgdWTab);
+                if (!DENSE) stage_dec(p.gm.dec[tm], kSgdMTab);
+                stage_enc(p.gw.enc[tw], kSgdETab);
                 __syncthreads();
-                staged = k;
+                staged = key;
             }
         }
         // the block's overflow offsets are read along with the rows (one

@@ -86,15 +86,19 @@ struct GroupEntry {
     uint64_t e0;          // first sign-fraction byte in the group's sf array
     uint32_t blk0, nblk;  // first block in the group, blocks
 };
+// blk_tab[b]: the first tensor whose code tables are byte-identical to those
+// of block b's tensor (tensors with one model and one shift share tables, so
+// an update that walks many tensors stages them only when they change).
 struct GroupRef {
     const GroupEntry *ent;
     const EncTab *enc;
     const DecTab *dec;
     const uint32_t *blk_tensor;
+    const uint32_t *blk_tab;
 };
 // Offsets of the parts of a group's device table.
 struct GroupTableLayout {
-    uint64_t ent, enc, dec, blk_tensor, bytes;
+    uint64_t ent, enc, dec, blk_tensor, blk_tab, bytes;
 };
 inline GroupTableLayout group_table_layout(uint64_t count, uint64_t nblk) {
     auto up = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
@@ -103,7 +107,8 @@ inline GroupTableLayout group_table_layout(uint64_t count, uint64_t nblk) {
     t.enc = up(t.ent + count * sizeof(GroupEntry));
     t.dec = up(t.enc + count * sizeof(EncTab));
     t.blk_tensor = up(t.dec + count * sizeof(DecTab));
-    t.bytes = up(t.blk_tensor + nblk * sizeof(uint32_t));
+    t.blk_tab = up(t.blk_tensor + nblk * sizeof(uint32_t));
+    t.bytes = up(t.blk_tab + nblk * sizeof(uint32_t));
     return t;
 }
 
@@ -202,6 +207,7 @@ struct FitParams {
     EncTab *enc;
     DecTab *dec;
     uint32_t *blk_tensor;
+    uint32_t *blk_tab;
     int32_t *shift_out;      // may be null
 };
 

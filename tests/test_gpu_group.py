@@ -173,3 +173,50 @@ def test_group_momentum(L, orc, B, cw, inplace):
     storage_equal(L, gm, m_out, orc.group([r[1] for r in refs], cap), ns, "M' inplace=%s" % inplace)
     if cw == 3:
         assert sum(r[1].spilled for r in refs) > 0
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_group_sgd_shared_tables(L, orc, inplace):
+    """Tensors that share code tables (same model and shift) share one table
+    index in the group's device table, and the update, which stages tables
+    only when the index pair changes, still matches the oracle when the
+    tensors' tables alternate."""
+    B, cw = 65536, 25
+    ns = [2 * B] * 6 + [B + 999]
+    g = np.random.default_rng(9800)
+    wsig = [0.02, 0.08, 0.02, 0.02, 0.08, 0.02, 0.02]       # two W codebooks (shifts 0 and 2)
+    msig = [1e-3, 1e-3, 4e-3, 1e-3, 4e-3, 4e-3, 1e-3]       # two M codebooks
+    ws = [synth.to_bf16_bits(g.normal(0, s, n)) for s, n in zip(wsig, ns)]
+    ms = [synth.to_bf16_bits(g.normal(0, s, n)) for s, n in zip(msig, ns)]
+    ocw = [orc.codebook_build(0, 0.02, 0.0, w) for w in ws]
+    ocm = [orc.codebook_build(0, 1e-3, 0.0, m) for m in ms]
+    assert len({int(c.shift) for c in ocw}) == 2 and len({int(c.shift) for c in ocm}) == 2
+    lib_cb = lambda c: L.lct_codebook_from_lengths(list(c.len_base), c.esc_len, c.shift)
+    lay = L.layout(B, cw)
+    gw = L.LctGroup(ns, lay, [lib_cb(c) for c in ocw], [dev(w).view(torch.bfloat16) for w in ws])
+    gm = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], [dev(m).view(torch.bfloat16) for m in ms])
+    # the table index of every block: the first tensor with the same tables
+    for grp, ocs in ((gw, ocw), (gm, ocm)):
+        nblk = int(grp.g.nblk)
+        tab = grp.table.cpu().numpy()
+        owner_at = len(tab) - 4 * nblk                      # blk_tab is the last part (256-aligned)
+        owner_at -= owner_at % 256
+        blk_tab = tab[owner_at:owner_at + 4 * nblk].view(np.uint32)
+        want = []
+        for k, c in enumerate(ocs):
+            first = next(j for j in range(k + 1) if ocs[j].shift == c.shift)
+            want += [first] * (-(-ns[k] // B))
+        assert blk_tab.tolist() == want
+    rw = [orc.encode(c, w, B, cw) for c, w in zip(ocw, ws)]
+    rm = [orc.encode(c, m, B, cw) for c, m in zip(ocm, ms)]
+    cap = sum(ns)
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    storage_equal(L, gw, w_all, orc.group(rw, cap), ns, "W")
+    ref = orc.group([orc.sgd(ocw[k], rw[k], ocm[k], rm[k], 1e-3) for k in range(len(ns))], cap)
+    out = gw.alloc_storage(cap)
+    if inplace:
+        out.sf, out.pay, out.cnt, out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+    L.lct_sgd_step_group(gw, w_all, gm, m_all, 1e-3, out)
+    storage_equal(L, gw, out, ref, ns, "W' shared tables inplace=%s" % inplace)
