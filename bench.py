@@ -69,6 +69,8 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=2048,
                     help="blocks in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-whole-set", action="store_true",
+                    help="skip the threaded oracle's check of every block (CPU leg)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the momentum step timed after the headline step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -138,8 +140,12 @@ def main():
                   "m_blocks": host_blocks_dense(m_dense, blocks, lay.block_elems),
                   "w_sample": w_dense.view(torch.int16)[pos].cpu().numpy().view(np.uint16),
                   "m_sample": m_dense.view(torch.int16)[pos].cpu().numpy().view(np.uint16)}
-    del m_dense
-    torch.cuda.empty_cache()
+    whole = None
+    if cpu_in is not None and not args.no_whole_set:
+        whole = WholeSet(cpu_in, mw, mm, eta, lay, n)
+    else:
+        del m_dense
+        torch.cuda.empty_cache()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
           for _ in range(args.warmup + args.steps)]
@@ -163,14 +169,25 @@ def main():
         st_enc = tw.status_word()
         g_enc = host_blocks_compressed(tw, blocks)
         g_m = host_blocks_compressed(tm, blocks)
+        if whole is not None:
+            whole.encode(w_dense, m_dense, tw, tm)
+            del m_dense
+            torch.cuda.empty_cache()
         L.lct_sgd_step(cbw, tw, cbm, tm, eta, tw2)
         torch.cuda.synchronize()
         st_sgd = tw2.status_word()
         g_sgd = host_blocks_compressed(tw2, blocks)
+        if whole is not None:
+            whole.sgd(tw2)
         L.lct_decode(cbw, tw2, w_dense)
         torch.cuda.synchronize()
         g_dec = host_blocks_dense(w_dense, blocks, lay.block_elems)
+        if whole is not None:
+            whole.decode(w_dense)
         cpu = cpu_baseline_leg(cpu_in, (g_enc, g_m, g_sgd, g_dec), cbw, cbm, mw, mm, eta, lay, n)
+        if whole is not None:
+            cpu["threaded"] = whole.result()
+            del whole
     else:
         step(0)
         torch.cuda.synchronize()
@@ -594,6 +611,93 @@ def activation_leg(L, dev, seq=3500, hid=2560, ffn=9728, reps=5):
 
 
 # ------------------------------------------------------------------ CPU-baseline leg
+
+class WholeSet:
+    """Every block of the step checked against the oracle run over ranges of
+    whole blocks on the host's threads (its bytes equal the serial oracle's),
+    op by op between the GPU's untimed first step; the oracle's time for the
+    same step (encode W, naive SGD round trip, decode W') is the threaded
+    baseline.  Works through 4096 blocks at a time."""
+
+    CHUNK = 4096
+
+    def __init__(self, cpu_in, mw, mm, eta, lay, n):
+        import oracle
+        self.orc = oracle
+        self.threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        self.ocw = oracle.codebook_from_sample(mw.family, mw.scale, mw.shape, cpu_in["w_sample"])
+        self.ocm = oracle.codebook_from_sample(mm.family, mm.scale, mm.shape, cpu_in["m_sample"])
+        self.eta, self.lay, self.n = eta, lay, n
+        self.B = lay.block_elems
+        self.nblk = -(-n // self.B)
+        self.ranges = [(b0, min(self.nblk, b0 + self.CHUNK)) for b0 in range(0, self.nblk, self.CHUNK)]
+        self.rw, self.rm, self.ro = [], [], []
+        self.ok = {"encode_W": True, "encode_M": True, "sgd_W": True, "decode_W": True}
+        self.t = {"encode": 0.0, "sgd": 0.0, "decode": 0.0}
+
+    def _chunk(self, t, b0, b1):
+        import numpy as np
+        B, cw = self.B, self.lay.cap_words
+        e0, e1 = b0 * B, min(b1 * B, self.n)
+        ob = t.obase[b0:b1 + 1].cpu().numpy().view(np.uint64)
+        spill = t.ovf[int(ob[0]):int(ob[-1])].cpu().numpy()
+        return self.orc.Compressed(e1 - e0, B, cw, t.sf[e0:e1].cpu().numpy(),
+                                   t.pay[b0 * cw * 256:b1 * cw * 256].cpu().numpy().view(np.uint32),
+                                   t.cnt[b0 * 256:b1 * 256].cpu().numpy().view(np.uint16),
+                                   (ob - ob[0]).astype(np.uint64), spill if spill.size else np.zeros(1, np.uint8))
+
+    @staticmethod
+    def _same(a, b):
+        import numpy as np
+        return (all(np.array_equal(getattr(a, k), getattr(b, k)) for k in ("sf", "pay", "cnt", "obase"))
+                and np.array_equal(a.ovf[:a.spilled], b.ovf[:b.spilled]))
+
+    def _dense(self, x, b0, b1):
+        import numpy as np
+        import torch
+        return x.view(torch.int16)[b0 * self.B:min(b1 * self.B, self.n)].cpu().numpy().view(np.uint16)
+
+    def encode(self, w, m, tw, tm):
+        cw, th = self.lay.cap_words, self.threads
+        for b0, b1 in self.ranges:
+            xw, xm = self._dense(w, b0, b1), self._dense(m, b0, b1)
+            t0 = time.perf_counter()
+            rw = self.orc.encode_threads(self.ocw, xw, self.B, cw, th)
+            self.t["encode"] += time.perf_counter() - t0
+            rm = self.orc.encode_threads(self.ocm, xm, self.B, cw, th)     # M's set-up: not timed
+            self.ok["encode_W"] &= self._same(self._chunk(tw, b0, b1), rw)
+            self.ok["encode_M"] &= self._same(self._chunk(tm, b0, b1), rm)
+            self.rw.append(rw)
+            self.rm.append(rm)
+
+    def sgd(self, out):
+        for (b0, b1), rw, rm in zip(self.ranges, self.rw, self.rm):
+            t0 = time.perf_counter()
+            ro = self.orc.sgd_threads(self.ocw, rw, self.ocm, rm, self.eta, self.threads)
+            self.t["sgd"] += time.perf_counter() - t0
+            self.ok["sgd_W"] &= self._same(self._chunk(out, b0, b1), ro)
+            self.ro.append(ro)
+        self.rw, self.rm = [], []
+
+    def decode(self, y):
+        import numpy as np
+        for (b0, b1), ro in zip(self.ranges, self.ro):
+            t0 = time.perf_counter()
+            ry = self.orc.decode_threads(self.ocw, ro, self.threads)
+            self.t["decode"] += time.perf_counter() - t0
+            self.ok["decode_W"] &= bool(np.array_equal(self._dense(y, b0, b1), ry))
+        self.ro = []
+
+    def result(self):
+        tot = sum(self.t.values())
+        return {"value": float("%.4g" % (self.n / tot)), "unit": "elems/s", "cores": self.threads,
+                "kind": "oracle",
+                "sample": "every block (%d, %d elements): encode W, naive SGD round trip, decode W'; "
+                          "the serial C routines over ranges of whole blocks on %d host threads, offsets "
+                          "stitched serially; encode %.2f s, sgd %.2f s, decode %.2f s"
+                          % (self.nblk, self.n, self.threads, self.t["encode"], self.t["sgd"], self.t["decode"]),
+                "parity_whole_set": {k: bool(v) for k, v in self.ok.items()}}
+
 
 def sample_blocks(nblk: int, n: int, B: int, want: int):
     """Evenly spread full blocks (the last, partial block is left out)."""

@@ -107,6 +107,11 @@ constexpr uint32_t log2c(uint32_t v) { return v <= 1 ? 0 : 1 + log2c(v / 2); }
 
 __device__ __forceinline__ uint32_t lane() { return __lane_id(); }
 
+// True when c holds in every active lane (one ballot compared with exec).
+__device__ __forceinline__ bool wave_all(bool c) {
+    return __builtin_amdgcn_ballot_w64(c) == __builtin_amdgcn_read_exec();
+}
+
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -1371,12 +1376,15 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // All fields of a full block are valid: a window that held its four
+        // fields moves the reader at most to the stream's end, so no clamp is
+        // needed here; a window that ran out is decoded again (with clamps).
         if (DEC) {
-            rw.q = min(rw.q + (int32_t)cw, qwmax);
-            if (!DENSE) rm.q = min(rm.q + (int32_t)cm, qmmax);
+            rw.q += (int32_t)cw;
+            if (!DENSE) rm.q += (int32_t)cm;
         }
-        if (__builtin_expect(!__all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
-            if (DEC && !__all(max(cw, cm) <= 30)) {
+        if (__builtin_expect(!wave_all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
+            if (DEC && !wave_all(max(cw, cm) <= 30)) {
                 // a window ran out: group s again, one field per window
                 rw.q = qw0;
                 if (!DENSE) rm.q = qm0;

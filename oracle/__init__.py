@@ -485,3 +485,123 @@ def group_member(g: Compressed, ns, k: int) -> Compressed:
 def encode_group(cbs, xs, block_elems: int, cap_words: int, ovf_cap: int | None = None) -> Compressed:
     """Every tensor encoded with its own codebook, then placed as a group."""
     return group([encode(cb, x, block_elems, cap_words) for cb, x in zip(cbs, xs)], ovf_cap)
+
+
+# ---------------------------------------------------------------- block-range driver
+
+def _at(a: np.ndarray, i: int) -> C.c_void_p:
+    """Pointer to element i of a contiguous numpy array."""
+    return C.c_void_p(a.ctypes.data + int(i) * a.itemsize)
+
+
+def _ranges(nblk: int, pieces: int):
+    pieces = max(1, min(pieces, nblk))
+    cuts = [nblk * i // pieces for i in range(pieces + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(pieces) if cuts[i + 1] > cuts[i]]
+
+
+def _in_view(t: Compressed, b0: int, b1: int):
+    """Blocks [b0, b1) of t as the serial routines take a tensor: element
+    range, pointers into t's arrays and offsets rebased to the range."""
+    B, cw = t.block_elems, t.cap_words
+    e0, e1 = b0 * B, min(b1 * B, t.n)
+    ob = (t.obase[b0:b1 + 1] - t.obase[b0]).astype(np.uint64)
+    ovf = _at(t.ovf, int(t.obase[b0])) if int(t.obase[b0]) < t.ovf.size else _at(t.ovf, 0)
+    return e0, e1, (_at(t.sf, e0), _at(t.pay, b0 * cw * NSTREAM), _at(t.cnt, b0 * NSTREAM), _p(ob), ovf), ob
+
+
+def _stitch(out: Compressed, ranges, parts, ovf_cap: int):
+    """Offsets and spilled bytes of the block ranges, placed in block order
+    (the serial scan over the ranges' totals)."""
+    base = 0
+    for (b0, b1), (ob, ov) in zip(ranges, parts):
+        out.obase[b0:b1] = ob[:-1] + np.uint64(base)
+        tot = int(ob[-1])
+        keep = max(0, min(tot, ovf_cap - base))
+        if keep:
+            out.ovf[base:base + keep] = ov[:keep]
+        base += tot
+    out.obase[out.nblk] = base
+    out.status = int(base > ovf_cap)
+    return out
+
+
+def _run(fn, ranges, threads: int):
+    """fn over the block ranges on `threads` host threads (the C calls release
+    the interpreter lock, so the ranges run in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    if threads <= 1:
+        return [fn(r) for r in ranges]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, ranges))
+
+
+def encode_threads(cb: Codebook, x: np.ndarray, block_elems: int, cap_words: int,
+                   threads: int, ovf_cap: int | None = None, pieces: int | None = None) -> Compressed:
+    """lcto_encode over ranges of whole blocks on several host threads, then
+    the overflow offsets by a serial scan over the ranges: the same bytes as
+    encode() (blocks are coded independently; only the offsets chain)."""
+    x = np.ascontiguousarray(x, np.uint16).reshape(-1)
+    n = x.size
+    ovf_cap = n if ovf_cap is None else ovf_cap
+    out = _alloc(n, block_elems, cap_words, ovf_cap)
+    ranges = _ranges(out.nblk, pieces or 4 * threads)
+    c = cb._c()
+
+    def work(r):
+        b0, b1 = r
+        e0, e1 = b0 * block_elems, min(b1 * block_elems, n)
+        ob = np.zeros(b1 - b0 + 1, np.uint64)
+        ov = np.zeros(max(e1 - e0, 1), np.uint8)
+        rc = lib().lcto_encode(C.byref(c), _at(x, e0), e1 - e0, block_elems, cap_words, _at(out.sf, e0),
+                               _at(out.pay, b0 * cap_words * NSTREAM), _at(out.cnt, b0 * NSTREAM), _p(ob),
+                               _p(ov), e1 - e0)
+        if rc < 0:
+            raise ValueError("encode: bad arguments")
+        return ob, ov
+
+    return _stitch(out, ranges, _run(work, ranges, threads), ovf_cap)
+
+
+def sgd_threads(cw: Codebook, w: Compressed, cm: Codebook, m: Compressed, eta: float, threads: int,
+                ovf_cap: int | None = None, pieces: int | None = None) -> Compressed:
+    """sgd() over ranges of whole blocks on several host threads (each range
+    the naive round trip on its own), offsets stitched serially."""
+    assert (w.n, w.block_elems, w.cap_words) == (m.n, m.block_elems, m.cap_words)
+    B, cwd = w.block_elems, w.cap_words
+    ovf_cap = w.n if ovf_cap is None else ovf_cap
+    out = _alloc(w.n, B, cwd, ovf_cap)
+    ranges = _ranges(out.nblk, pieces or 4 * threads)
+    a, b = cw._c(), cm._c()
+
+    def work(r):
+        b0, b1 = r
+        e0, e1, wp, wob = _in_view(w, b0, b1)
+        _, _, mp, mob = _in_view(m, b0, b1)
+        ob = np.zeros(b1 - b0 + 1, np.uint64)
+        ov = np.zeros(max(e1 - e0, 1), np.uint8)
+        rc = lib().lcto_sgd(C.byref(a), *wp, C.byref(b), *mp, eta, None, e1 - e0, B, cwd,
+                            _at(out.sf, e0), _at(out.pay, b0 * cwd * NSTREAM), _at(out.cnt, b0 * NSTREAM),
+                            _p(ob), _p(ov), e1 - e0)
+        if rc < 0:
+            raise ValueError("sgd: error %d" % rc)
+        return ob, ov
+
+    return _stitch(out, ranges, _run(work, ranges, threads), ovf_cap)
+
+
+def decode_threads(cb: Codebook, t: Compressed, threads: int, pieces: int | None = None) -> np.ndarray:
+    """decode() over ranges of whole blocks on several host threads."""
+    y = np.zeros(t.n, np.uint16)
+    ranges = _ranges(t.nblk, pieces or 4 * threads)
+    c = cb._c()
+
+    def work(r):
+        b0, b1 = r
+        e0, e1, tp, _ = _in_view(t, b0, b1)
+        rc = lib().lcto_decode(C.byref(c), *tp, e1 - e0, t.block_elems, t.cap_words, _at(y, e0))
+        if rc != OK:
+            raise ValueError("decode: stream error %d" % rc)
+
+    _run(work, ranges, threads)
+    return y

@@ -2,9 +2,9 @@
 configuration the benchmark times.
 
 - The 4.02B-element Qwen3-4B-shaped set (flat, CLEAN): codebooks, encode of W
-  and M, the fused update in place and the decode, checked against the oracle
-  on evenly spread sampled blocks (the last, partial block included) and by
-  properties that hold at any size.
+  and M, the fused update and the decode, checked against the oracle on every
+  block (out of place), and in place on evenly spread sampled blocks (the
+  last, partial block included) and by properties that hold at any size.
 - The same set's momentum step, in place, on sampled blocks.
 - The same set's shift sample and re-estimated shift, as built and scaled by
   2^4 (most of it spilled), against the dense values and the oracle's search.
@@ -56,6 +56,73 @@ def same_block(got, ref, what):
     for f in ("sf", "pay", "cnt", "obase"):
         assert np.array_equal(getattr(got, f), getattr(ref, f)), "%s %s" % (what, f)
     assert np.array_equal(got.ovf[:got.spilled], ref.ovf[:ref.spilled]), what + " ovf"
+
+
+def host_threads():
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def chunk_of(t, b0, b1, n):
+    """Blocks [b0, b1) of a device tensor as an oracle tensor (offsets rebased)."""
+    import oracle
+    B, cw = t.layout.block_elems, t.layout.cap_words
+    e0, e1 = b0 * B, min(b1 * B, n)
+    ob = t.obase[b0:b1 + 1].cpu().numpy().view(np.uint64)
+    spill = t.ovf[int(ob[0]):int(ob[-1])].cpu().numpy()
+    return oracle.Compressed(e1 - e0, B, cw, t.sf[e0:e1].cpu().numpy(),
+                             t.pay[b0 * cw * 256:b1 * cw * 256].cpu().numpy().view(np.uint32),
+                             t.cnt[b0 * 256:b1 * 256].cpu().numpy().view(np.uint16),
+                             (ob - ob[0]).astype(np.uint64), spill if spill.size else np.zeros(1, np.uint8))
+
+
+def test_qwen3_4b_flat_every_block(L, orc):
+    """Every one of the 61,378 blocks of the 4.02B-element set, in ranges of
+    4096 blocks: the encodes of W and M, the fused update (out of place) and
+    the decode of W', byte for byte against the oracle run over whole blocks
+    on the host's threads (its bytes equal the serial oracle's)."""
+    wspec, mspec, mw, mm, eta = synth.config5()
+    n = wspec.numel
+    dev = torch.device("cuda", 0)
+    lay = L.lct_layout_init(L.CLEAN)
+    B, cwd = lay.block_elems, lay.cap_words
+    w = synth.draw_device(wspec, dev)
+    m = synth.draw_device(mspec, dev)
+    cbw = L.lct_codebook_build(L.Model(mw.family, mw.scale, mw.shape), w)
+    cbm = L.lct_codebook_build(L.Model(mm.family, mm.scale, mm.shape), m)
+    pos = torch.as_tensor(orc.sample_positions(n).astype(np.int64), device=dev)
+    ocw = orc.codebook_from_sample(mw.family, mw.scale, mw.shape,
+                                   w.view(torch.int16)[pos].cpu().numpy().view(np.uint16))
+    ocm = orc.codebook_from_sample(mm.family, mm.scale, mm.shape,
+                                   m.view(torch.int16)[pos].cpu().numpy().view(np.uint16))
+    ovf_cap = n // 64
+    tw, tm, out = (L.alloc_tensor(n, lay, ovf_cap, dev) for _ in range(3))
+    L.lct_encode(cbw, w, tw)
+    L.lct_encode(cbm, m, tm)
+    L.lct_sgd_step(cbw, tw, cbm, tm, eta, out)
+    y = torch.empty_like(w)
+    L.lct_decode(cbw, out, y)
+    torch.cuda.synchronize()
+    assert tw.status_word() == 0 and tm.status_word() == 0 and out.status_word() == 0
+    nblk = -(-n // B)
+    th = host_threads()
+    checked = 0
+    for b0 in range(0, nblk, 4096):
+        b1 = min(nblk, b0 + 4096)
+        e0, e1 = b0 * B, min(b1 * B, n)
+        xw = w.view(torch.int16)[e0:e1].cpu().numpy().view(np.uint16)
+        xm = m.view(torch.int16)[e0:e1].cpu().numpy().view(np.uint16)
+        rw = orc.encode_threads(ocw, xw, B, cwd, th)
+        rm = orc.encode_threads(ocm, xm, B, cwd, th)
+        same_block(chunk_of(tw, b0, b1, n), rw, "W blocks %d..%d" % (b0, b1))
+        same_block(chunk_of(tm, b0, b1, n), rm, "M blocks %d..%d" % (b0, b1))
+        ro = orc.sgd_threads(ocw, rw, ocm, rm, eta, th)
+        same_block(chunk_of(out, b0, b1, n), ro, "W' blocks %d..%d" % (b0, b1))
+        got = y.view(torch.int16)[e0:e1].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, orc.decode_threads(ocw, ro, th)), "decode blocks %d..%d" % (b0, b1)
+        checked += b1 - b0
+        print("checked blocks %d..%d" % (b0, b1), flush=True)
+    assert checked == nblk == 61378
 
 
 def test_qwen3_4b_flat_sampled(L, orc):
