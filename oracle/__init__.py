@@ -21,6 +21,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lct_oracle.c")
 _LIB = os.path.join(_HERE, "liblct_oracle.so")
+# A different build of the same source (the sanitizer test's) may be loaded
+# instead; build() still writes the default one.
+_LOAD = os.environ.get("LCT_ORACLE_LIB") or _LIB
 
 GAUSSIAN, LAPLACE, POWERLAW = 0, 1, 2
 OK, OVF_FULL, EINVAL, EDECODE = 0, 1, -1, -2
@@ -49,9 +52,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _LOAD == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        L = C.CDLL(_LIB)
+        L = C.CDLL(_LOAD)
         P = C.c_void_p
         u64, u32, i32 = C.c_uint64, C.c_uint32, C.c_int
         L.lcto_model_survival.restype = C.c_double
