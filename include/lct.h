@@ -297,11 +297,11 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in,
  * (in-place step) or disjoint from every input; its ovf, status and scratch
  * must not overlap any input, and the two outputs must not overlap each other.
  * Each output has its own status word (LCT_ST_OVF_FULL as for lct_encode).
- * W' is computed from M' as stored, so when M' overflows m_out's region its
- * missing fields make W' invalid as well: w_out's status word then carries
- * LCT_ST_OVF_FULL too (whatever w_out's own spill), and after an in-place step
- * both W and M are lost.  Callers that cannot bound the spill step out of
- * place or size ovf_cap = n.
+ * The step is one pass: W' is computed from M' as rounded, not from M''s
+ * stored form, so an overflow of m_out's region leaves W' complete and
+ * w_out's status clean (and the other way round).  After an in-place step
+ * whose output overflowed, that input is lost: callers that cannot bound the
+ * spill step out of place or size ovf_cap = n.
  * Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS, LCT_EARCH, LCT_EHIP. */
 lct_status lct_momentum_step(const lct_codebook *cw, const lct_tensor *w_in,
                              const lct_codebook *cm, const lct_tensor *m_in,

@@ -217,6 +217,63 @@ lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream,
     return LCT_OK;
 }
 
+// The buffers of a fused momentum step.
+void mom_params(MomParams &p, const lct_tensor &w_in, const lct_tensor &m_in, const uint16_t *g,
+                const lct_tensor &w_out, const lct_tensor &m_out, uint64_t nb, float mu, float eta) {
+    p.w_sf = w_in.sf;
+    p.w_pay = w_in.pay;
+    p.w_cnt = w_in.cnt;
+    p.w_obase = w_in.obase;
+    p.w_ovf = w_in.ovf;
+    p.w_ovf_cap = w_in.ovf_cap;
+    p.m_sf = m_in.sf;
+    p.m_pay = m_in.pay;
+    p.m_cnt = m_in.cnt;
+    p.m_obase = m_in.obase;
+    p.m_ovf = m_in.ovf;
+    p.m_ovf_cap = m_in.ovf_cap;
+    p.g = g;
+    p.ow_sf = w_out.sf;
+    p.ow_pay = w_out.pay;
+    p.ow_cnt = w_out.cnt;
+    p.ow_obase = w_out.obase;
+    p.ow_ovf = w_out.ovf;
+    p.ow_ovf_cap = w_out.ovf_cap;
+    p.ow_status = w_out.status;
+    p.ow_scratch = (uint8_t *)w_out.scratch;
+    p.om_sf = m_out.sf;
+    p.om_pay = m_out.pay;
+    p.om_cnt = m_out.cnt;
+    p.om_obase = m_out.obase;
+    p.om_ovf = m_out.ovf;
+    p.om_ovf_cap = m_out.ovf_cap;
+    p.om_status = m_out.status;
+    p.om_scratch = (uint8_t *)m_out.scratch;
+    p.n = w_in.n;
+    p.block_elems = w_in.layout.block_elems;
+    p.cap_words = w_in.layout.cap_words;
+    p.nblk = (uint32_t)nb;
+    p.mu = mu;
+    p.neg_eta = -eta;
+    p.park_w = p.ow_cnt == p.w_cnt;
+    p.park_m = p.om_cnt == p.m_cnt;
+}
+
+// Clear both outputs' scratch headers and status words, the fused kernel,
+// both outputs' overflow scans.
+lct_status mom_launch(const MomParams &p, uint64_t nb, bool group, void *stream) {
+    int e = launch_clear(p.ow_scratch, nb, p.ow_status, stream);
+    if (e == hipSuccess) e = launch_clear(p.om_scratch, nb, p.om_status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+    e = launch_mom(p, stream, group);
+    if (e != hipSuccess) return hip_fail(e, "momentum launch");
+    e = launch_scan(p.ow_scratch, nb, p.ow_obase, p.ow_ovf, p.ow_ovf_cap, p.ow_status, p.ow_cnt, stream);
+    if (e == hipSuccess)
+        e = launch_scan(p.om_scratch, nb, p.om_obase, p.om_ovf, p.om_ovf_cap, p.om_status, p.om_cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return LCT_OK;
+}
+
 // The momentum step's aliasing rules (nb: the block count, ~0 for n's): the
 // outputs are disjoint from each other; each output's fixed side is its own
 // input's buffers, exactly, or disjoint from every input; its overflow,
@@ -556,25 +613,16 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
 
     const uint64_t nb = nblocks(w_in->n, w_in->layout);
     if (nb > 0xFFFFFFFFull) return LCT_EINVAL;
-    // Two passes of the update kernel: M' = rne(mu * M + g) with the dense
-    // gradient as the second operand (M' encoded with cm_out), then
-    // W' = rne(W - eta * M') reading M' as stored.
-    SgdParams p1;
-    memset(&p1, 0, sizeof p1);
-    sgd_params(p1, *m_in, nullptr, *m_out, nb, mu);
-    p1.dense = d_g;
-    fill_enc(*cm_out, &p1.wenc);
-    fill_dec(*cm, &p1.wdec);
-    st = sgd_launch(p1, nb, false, stream, true);
-    if (st != LCT_OK) return st;
-    SgdParams p2;
-    memset(&p2, 0, sizeof p2);
-    sgd_params(p2, *w_in, m_out, *w_out, nb, -eta);
-    fill_enc(*cw_out, &p2.wenc);
-    fill_dec(*cw, &p2.wdec);
-    fill_dec(*cm_out, &p2.mdec);
-    // W' is computed from M' as stored: if M' lost spilled fields, so did W'
-    return sgd_launch(p2, nb, false, stream, false, m_out->status);
+    // One pass: W and M decoded, M' = rne(mu * M + g) and W' = rne(W - eta * M')
+    // with M' as rounded, both re-encoded by the fused kernel.
+    MomParams p;
+    memset(&p, 0, sizeof p);
+    mom_params(p, *w_in, *m_in, d_g, *w_out, *m_out, nb, mu, eta);
+    fill_enc_packed(*cw_out, p.wenc);
+    fill_enc_packed(*cm_out, p.menc);
+    fill_dec(*cw, &p.wdec);
+    fill_dec(*cm, &p.mdec);
+    return mom_launch(p, nb, false, stream);
 }
 
 // ---- groups
@@ -824,19 +872,13 @@ lct_status lct_momentum_step_group(const lct_group *gw, const lct_tensor *w_all,
     if (st != LCT_OK) return st;
     if (gw->nblk == 0) return LCT_OK;
     const uint64_t nb = gw->nblk;
-    SgdParams p1;
-    memset(&p1, 0, sizeof p1);
-    sgd_params(p1, *m_all, nullptr, *m_out, nb, mu);
-    p1.gw = group_ref(*gm);
-    p1.gm = group_ref(*gg);
-    st = sgd_launch(p1, nb, true, stream, true);
-    if (st != LCT_OK) return st;
-    SgdParams p2;
-    memset(&p2, 0, sizeof p2);
-    sgd_params(p2, *w_all, m_out, *w_out, nb, -eta);
-    p2.gw = group_ref(*gw);
-    p2.gm = group_ref(*gm);
-    return sgd_launch(p2, nb, true, stream, false, m_out->status);
+    MomParams p;
+    memset(&p, 0, sizeof p);
+    mom_params(p, *w_all, *m_all, nullptr, *w_out, *m_out, nb, mu, eta);
+    p.gw = group_ref(*gw);
+    p.gm = group_ref(*gm);
+    p.gg = group_ref(*gg);
+    return mom_launch(p, nb, true, stream);
 }
 
 const char *lct_strerror(lct_status st) {

@@ -344,6 +344,10 @@ void fill_enc(const lct_codebook &cb, EncTab *t) {
     memcpy(t->len, cb.enc_len, sizeof t->len);
 }
 
+void fill_enc_packed(const lct_codebook &cb, uint32_t t[256]) {
+    for (int e = 0; e < 256; ++e) t[e] = cb.enc_bits[e] | ((uint32_t)cb.enc_len[e] << 24);
+}
+
 void fill_dec(const lct_codebook &cb, DecTab *t) {
     memcpy(t->dec, cb.dec, sizeof t->dec);
     t->esc_len = cb.esc_len;

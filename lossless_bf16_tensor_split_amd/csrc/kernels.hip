@@ -1582,6 +1582,446 @@ void k_sgd(const SgdParams p) {
     if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
 }
 
+// ------------------------------------------------------------------ fused momentum step
+
+// One pass for the momentum step (explainer, jargon entry "Optimizer state":
+// the momentum buffer is kept compressed like the weights; paragraph on
+// training traffic: decode, update and re-encode in one pass): W and M are
+// decoded, g is read dense, and per element m' = rne(fmaf(mu, m, g)) and
+// w' = rne(fmaf(-eta, m', w)) with m' as rounded, each NaN written as 0x7FC0;
+// M' is coded with M's output code and W' with W's, each by its own writer
+// into its own output.  The update's pipeline carries both: stage s decodes
+// group s of W and M (and loads its g values), does both products of group
+// s-1 and splits both results, and codes both outputs' fields of group s-2.
+// M''s sign-fraction bytes take the place of M's in M's LDS regions, W''s
+// those of W, and each leaves with its own 16-byte stores.
+//
+// Four waves per workgroup, the four units of a block, share the four code
+// tables (two waves per SIMD, eight per CU); units 2i and 2i+1 share their
+// sign-fraction lines, so the workgroup meets at every block.
+constexpr uint32_t kMomWaves = 4;
+constexpr uint32_t kMWE = 0, kMME = 2048, kMNone = 4096, kMWD = 4352, kMMD = 5376, kMWave0 = 6400;
+constexpr uint32_t kMWNoField = kMNone - kMWE, kMMNoField = kMNone - kMME;
+
+// Encode table from its packed form (bits | len << 24) into 8-byte entries.
+__device__ __forceinline__ void stage_enc_packed(const uint32_t *t, uint32_t tab) {
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
+        const uint32_t e = t[i];
+        st32(tab + 8 * i, e & 0xFFFFFFu);
+        st32(tab + 8 * i + 4, e >> 24);
+    }
+}
+
+// General path (partial blocks and inputs with spilled fields): byte-wide
+// accesses with per-element checks.
+template <uint32_t CAPT>
+__device__ __forceinline__ void mom_stream_general(const MomParams &p, const SgdLayout &lay, PayWriter &stw,
+                                                   PayWriter &stm, uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
+                                                   uint64_t r0, const uint16_t *gu, uint64_t wsp, uint64_t msp) {
+    const uint32_t s = lane();
+    const uint32_t npos = p.block_elems / NS;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const uint32_t capbits = 32 * cap;
+    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
+    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    const uint8_t *wsf = p.w_sf + r0 + s;
+    const uint8_t *msf = p.m_sf + r0 + s;
+    const uint16_t *gs = gu + s;
+    uint8_t *owsf = p.ow_sf + r0 + s;
+    uint8_t *omsf = p.om_sf + r0 + s;
+    uint64_t *wctr = reinterpret_cast<uint64_t *>(p.ow_scratch + kScrStage);
+    uint8_t *wstage = p.ow_scratch + scr_stage_offset(p.nblk);
+    uint64_t *mctr = reinterpret_cast<uint64_t *>(p.om_scratch + kScrStage);
+    uint8_t *mstage = p.om_scratch + scr_stage_offset(p.nblk);
+    Reader rw, rm;
+    rw.init(lay.w0, s);
+    rm.init(lay.m0, s);
+    struct Buf3 {
+        uint32_t w[CH], m[CH], g[CH];
+    };
+    double_buffered<Buf3>(
+        npos,
+        [&](Buf3 &bf, uint32_t j0) {
+            load_chunk<true>(bf.w, wsf, j0, n_s);
+            load_chunk<true>(bf.m, msf, j0, n_s);
+            load_chunk<true>(bf.g, gs, j0, n_s);
+        },
+        [&](Buf3 &bf, uint32_t j0) {
+            uint32_t ew[CH], em[CH];
+            uint8_t *ow = owsf + (size_t)j0 * NS;
+            uint8_t *om = omsf + (size_t)j0 * NS;
+#pragma unroll
+            for (uint32_t i = 0; i < CH; ++i) {
+                const uint32_t j = j0 + i;
+                uint32_t fw = rw.next(kMWD);
+                rw.q = min(rw.q, qwmax);
+                if (j >= cw_s && j < n_s) {
+                    const uint64_t k = wsp + (j - cw_s);
+                    fw = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                }
+                uint32_t fm = rm.next(kMMD);
+                rm.q = min(rm.q, qmmax);
+                if (j >= cm_s && j < n_s) {
+                    const uint64_t k = msp + (j - cm_s);
+                    fm = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                }
+                const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], fm), p.mu);
+                const uint32_t Rw = sgd_round(join32(bf.w[i], fw), Rm & 0xFFFF0000u, p.neg_eta);
+                if (j < n_s) {
+                    ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
+                    om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
+                }
+                ew[i] = (Rw >> 20) & 0x7F8u;
+                em[i] = (Rm >> 20) & 0x7F8u;
+            }
+            writer_chunk<true>(stw, ew, j0, n_s, capbits, kMWE);
+            writer_spill<true>(stw, ew, j0, n_s, wctr, wstage, p.ow_ovf_cap);
+            writer_chunk<true>(stm, em, j0, n_s, capbits, kMME);
+            writer_spill<true>(stm, em, j0, n_s, mctr, mstage, p.om_ovf_cap);
+        });
+}
+
+// Full-block path (every stream has npos elements and no input field
+// spilled): the update's pipeline with both products and both writers.
+template <uint32_t CAPT>
+__device__ __forceinline__ void mom_stream_full(const MomParams &p, const SgdLayout &lay, PayWriter &stw,
+                                                PayWriter &stm, uint64_t r0, const uint16_t *gu) {
+    const uint32_t l = lane();
+    const uint32_t npos = p.block_elems / NS;
+    const uint32_t nh = npos / CH;
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const uint32_t capbits = 32 * cap;
+    const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
+    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    const uint32_t mine = 16 * l;
+    const uint32_t lw = l & ~3u;
+    const uint32_t jsel = (l & 3u) * 0x01010000u | 0x0C0Cu;
+    const uint32_t span = (npos - 1) * NS + US;
+    const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rms = wave_rsrc(p.m_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rows_ = wave_rsrc(p.ow_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t roms = wave_rsrc(p.om_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rg = wave_rsrc(gu, 2 * span);
+    constexpr uint32_t kNone = 0x80000000u;
+    constexpr uint32_t kHalfB = CH * NS;
+    const uint32_t piece = (l >> 2) * NS + 16 * (l & 3);
+    uint64_t *wctr = reinterpret_cast<uint64_t *>(p.ow_scratch + kScrStage);
+    uint8_t *wstage = p.ow_scratch + scr_stage_offset(p.nblk);
+    uint64_t *mctr = reinterpret_cast<uint64_t *>(p.om_scratch + kScrStage);
+    uint8_t *mstage = p.om_scratch + scr_stage_offset(p.nblk);
+    Reader rw, rm;
+    rw.init(lay.w0, l);
+    rm.init(lay.m0, l);
+
+    struct Halves {
+        u32x4 w, m;
+    };
+    auto load = [&](Halves &r, uint32_t h) {
+        const uint32_t o = h < nh ? h * kHalfB + piece : kNone;
+        r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
+        r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
+    };
+    auto region = [&](uint32_t h) { return (h & 1u) * kRegB; };
+    auto to_lds = [&](const Halves &r, uint32_t h) {
+        st128(lay.sw + region(h) + mine, r.w);
+        st128(lay.sm + region(h) + mine, r.m);
+    };
+    // g of group s (positions 4s..4s+3 of this lane's stream), as BF16 bits
+    auto gload = [&](uint32_t s, uint32_t (&gv)[4]) {
+        const uint32_t o = 2 * (4 * s * NS + l);
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k)
+            gv[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rg, o + 2 * k * NS, 0, 0);
+    };
+
+    uint32_t wsP[4] = {0, 0, 0, 0}, msP[4] = {0, 0, 0, 0}, ewP[4] = {0, 0, 0, 0}, emP[4] = {0, 0, 0, 0};
+    uint32_t gP[4] = {0, 0, 0, 0}, gC[4] = {0, 0, 0, 0};
+    u32x2 wcw[4] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}}, wcm[4] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+    uint32_t ew8[4] = {kMWNoField, kMWNoField, kMWNoField, kMWNoField};
+    uint32_t em8[4] = {kMMNoField, kMMNoField, kMMNoField, kMMNoField};
+    uint32_t jw = 0;
+    u32x4 outw = {0u, 0u, 0u, 0u}, outm = {0u, 0u, 0u, 0u};
+    bool wall = true;
+
+    // a writer's group coded with a check per field; its codes are then spent
+    auto checked = [&](PayWriter &st, u32x2 (&wc)[4], const uint32_t (&e8)[4], uint64_t *ctr, uint8_t *stg,
+                       uint64_t stg_cap) {
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            if (st.live) {
+                if (st.total() + wc[k].y <= capbits) {
+                    st.put(wc[k].x, wc[k].y);
+                    st.flush();
+                } else {
+                    st.live = 0;
+                    st.cs = jw + k;
+                }
+            }
+            wc[k] = u32x2{0u, 0u};
+        }
+        writer_spill<false>(st, e8, jw, npos, ctr, stg, stg_cap);
+    };
+    auto code_checked = [&]() {
+        checked(stw, wcw, ew8, wctr, wstage, p.ow_ovf_cap);
+        checked(stm, wcm, em8, mctr, mstage, p.om_ovf_cap);
+    };
+
+    auto stage_fn = [&](auto DEC_, auto GS_, uint32_t h) {
+        constexpr bool DEC = decltype(DEC_)::value;
+        constexpr uint32_t GS = decltype(GS_)::value;
+        const uint32_t rc = region(h) + GS * 4 * US;
+        const uint32_t rp = (GS ? region(h) : region(h + 1)) + ((GS + 3) % 4) * 4 * US;
+        uint32_t wsC[4], msC[4], ewC[4], emC[4];
+        uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
+        const int32_t qw0 = rw.q, qm0 = rm.q;
+        if (DEC) {
+            winw = rw.window();
+            winm = rm.window();
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                wsC[k] = ld32(lay.sw + rc + k * US + lw);
+                msC[k] = ld32(lay.sm + rc + k * US + lw);
+            }
+            gload(4 * h + GS, gC);
+        }
+        if (!wall && !wave_all(stw.live && stw.total() + 4 * 16 <= capbits &&
+                               stm.live && stm.total() + 4 * 16 <= capbits))
+            code_checked();
+        uint32_t epw[4], epm[4];
+        float rmv[4], rwv[4];
+        bool nan = false;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
+            if (DEC) {
+                wkw = winw >> cw;
+                enw = ld32(kMWD + (wkw & 0x3FCu));
+                wkm = winm >> cm;
+                enm = ld32(kMMD + (wkm & 0x3FCu));
+            }
+            rmv[k] = __builtin_fmaf(p.mu, __uint_as_float(join32s(msP[k], emP[k], jsel)),
+                                    __uint_as_float(gP[k] << 16));
+            if (k & 1) {
+                // M' of the pair, rounded; W' from M' as rounded
+                uint32_t hm = cvt_bf16x2(rmv[k - 1], rmv[k]);
+                asm volatile("" : "+v"(hm));
+                rwv[k - 1] = __builtin_fmaf(p.neg_eta, __uint_as_float(hm << 16),
+                                            __uint_as_float(join32s(wsP[k - 1], ewP[k - 1], jsel)));
+                rwv[k] = __builtin_fmaf(p.neg_eta, __uint_as_float(hm & 0xFFFF0000u),
+                                        __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
+                uint32_t hw = cvt_bf16x2(rwv[k - 1], rwv[k]);
+                asm volatile("" : "+v"(hw));
+                nan |= (rmv[k - 1] != rmv[k - 1]) | (rmv[k] != rmv[k]) | (rwv[k - 1] != rwv[k - 1]) |
+                       (rwv[k] != rwv[k]);
+                epm[k - 1] = (hm >> 4) & 0x7F8u;
+                epm[k] = (hm >> 20) & 0x7F8u;
+                epw[k - 1] = (hw >> 4) & 0x7F8u;
+                epw[k] = (hw >> 20) & 0x7F8u;
+                uint32_t bm, bw;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(bm) : "s"(0x00800080u), "v"(hm >> 8), "v"(hm));
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(bw) : "s"(0x00800080u), "v"(hw >> 8), "v"(hw));
+                st8(lay.sm + rp + (k - 1) * US + l, bm);
+                st8hi(lay.sm + rp + k * US + l, bm);
+                st8(lay.sw + rp + (k - 1) * US + l, bw);
+                st8hi(lay.sw + rp + k * US + l, bw);
+                stw.put(wcw[k - 1].x | (wcw[k].x << wcw[k - 1].y), wcw[k - 1].y + wcw[k].y);
+                stw.flush();
+                stm.put(wcm[k - 1].x | (wcm[k].x << wcm[k - 1].y), wcm[k - 1].y + wcm[k].y);
+                stm.flush();
+            }
+            if (DEC) {
+                ewC[k] = (wkw << (enw & 31u)) | enw;
+                cw += (enw >> 8) & 0xFFu;
+                emC[k] = (wkm << (enm & 31u)) | enm;
+                cm += (enm >> 8) & 0xFFu;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // every field of a full block is valid: a window that held its four
+        // fields moves a reader at most to its stream's end (no clamp)
+        if (DEC) {
+            rw.q += (int32_t)cw;
+            rm.q += (int32_t)cm;
+        }
+        if (__builtin_expect(!wave_all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
+            if (DEC && !wave_all(max(cw, cm) <= 30)) {
+                // a window ran out: group s again, one field per window
+                rw.q = qw0;
+                rm.q = qm0;
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) {
+                    ewC[k] = rw.next(kMWD);
+                    rw.q = min(rw.q, qwmax);
+                    emC[k] = rm.next(kMMD);
+                    rm.q = min(rm.q, qmmax);
+                }
+            }
+            // group s-1 with the integer rounding (same fields; a NaN's byte
+            // becomes the canonical one's)
+#pragma unroll
+            for (uint32_t k = 0; k < 4; k += 2) {
+                const uint32_t Rm0 = sgd_round(gP[k] << 16, join32s(msP[k], emP[k], jsel), p.mu);
+                const uint32_t Rm1 = sgd_round(gP[k + 1] << 16, join32s(msP[k + 1], emP[k + 1], jsel), p.mu);
+                const uint32_t Rw0 = sgd_round(join32s(wsP[k], ewP[k], jsel), Rm0 & 0xFFFF0000u, p.neg_eta);
+                const uint32_t Rw1 = sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel), Rm1 & 0xFFFF0000u,
+                                               p.neg_eta);
+                const uint32_t hm = (Rm0 >> 16) | (Rm1 & 0xFFFF0000u);
+                const uint32_t hw = (Rw0 >> 16) | (Rw1 & 0xFFFF0000u);
+                epm[k] = (hm >> 4) & 0x7F8u;
+                epm[k + 1] = (hm >> 20) & 0x7F8u;
+                epw[k] = (hw >> 4) & 0x7F8u;
+                epw[k + 1] = (hw >> 20) & 0x7F8u;
+                uint32_t bm, bw;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(bm) : "s"(0x00800080u), "v"(hm >> 8), "v"(hm));
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(bw) : "s"(0x00800080u), "v"(hw >> 8), "v"(hw));
+                st8(lay.sm + rp + k * US + l, bm);
+                st8hi(lay.sm + rp + (k + 1) * US + l, bm);
+                st8(lay.sw + rp + k * US + l, bw);
+                st8hi(lay.sw + rp + (k + 1) * US + l, bw);
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            wcw[k] = ld64(kMWE + epw[k]);
+            ew8[k] = epw[k];
+            wcm[k] = ld64(kMME + epm[k]);
+            em8[k] = epm[k];
+        }
+        jw = 4 * (4 * h + GS) - 4;
+        if (DEC) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                wsP[k] = wsC[k];
+                msP[k] = msC[k];
+                ewP[k] = ewC[k];
+                emP[k] = emC[k];
+                gP[k] = gC[k];
+            }
+        }
+    };
+    auto half = [&](uint32_t h, Halves &next) {
+        wall = wave_all(stw.live && stw.total() + CH * 16 <= capbits && stm.live &&
+                        stm.total() + CH * 16 <= capbits);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 0>{}, h);
+        if (h == 0) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                wcw[k] = u32x2{0u, 0u};
+                wcm[k] = u32x2{0u, 0u};
+                ew8[k] = kMWNoField;
+                em8[k] = kMMNoField;
+            }
+            jw = 0;
+        } else {
+            outw = ld128(lay.sw + region(h - 1) + mine);
+            outm = ld128(lay.sm + region(h - 1) + mine);
+        }
+        to_lds(next, h + 1);
+        load(next, h + 2);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 1>{}, h);
+        if (h != 0) {
+            __builtin_amdgcn_raw_buffer_store_b128(outw, rows_, (h - 1) * kHalfB + piece, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(outm, roms, (h - 1) * kHalfB + piece, 0, 0);
+        }
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 2>{}, h);
+        stage_fn(std::true_type{}, std::integral_constant<uint32_t, 3>{}, h);
+    };
+    Halves a;
+    load(a, 0);
+    to_lds(a, 0);
+    load(a, 1);
+    for (uint32_t h = 0; h < nh; ++h) half(h, a);
+    wall = false;
+    stage_fn(std::false_type{}, std::integral_constant<uint32_t, 0>{}, nh);
+    code_checked();
+    outw = ld128(lay.sw + region(nh - 1) + mine);
+    outm = ld128(lay.sm + region(nh - 1) + mine);
+    __builtin_amdgcn_raw_buffer_store_b128(outw, rows_, (nh - 1) * kHalfB + piece, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(outm, roms, (nh - 1) * kHalfB + piece, 0, 0);
+}
+
+template <uint32_t CAPT, bool GROUP>
+__global__ __launch_bounds__(64 * kMomWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void k_mom(const MomParams p) {
+    if (!GROUP) {
+        stage_dec(p.wdec, kMWD);
+        stage_dec(p.mdec, kMMD);
+        stage_enc_packed(p.wenc, kMWE);
+        stage_enc_packed(p.menc, kMME);
+    }
+    if (threadIdx.x < 2) st32(kMNone + 4 * threadIdx.x, 0);
+    __syncthreads();
+    uint64_t staged = ~0ull;
+    const uint32_t l = lane();
+    const uint32_t cap = cap_of<CAPT>(p.cap_words);
+    const SgdLayout lay(cap, kMWave0 + wave_id() * sgd_wave_bytes(cap), false);
+    st32(lay.z0 + 4 * l, 0);
+    st32(lay.z1 + 4 * l, 0);
+    st32(lay.z2 + 4 * l, 0);
+    uint16_t *wcnt_out = p.park_w ? reinterpret_cast<uint16_t *>(p.ow_scratch + scr_cnt_offset(p.nblk)) : p.ow_cnt;
+    uint16_t *mcnt_out = p.park_m ? reinterpret_cast<uint16_t *>(p.om_scratch + scr_cnt_offset(p.nblk)) : p.om_cnt;
+    static_assert(kMomWaves == kMaxUnits, "a workgroup is one block's units");
+    // Workgroups take blocks round-robin; the four waves meet at every block
+    // (the units share sign-fraction lines and, in a group, the tables).
+    for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
+        __builtin_amdgcn_s_barrier();
+        const uint32_t h = wave_id();
+        const uint32_t u = b * kMaxUnits + h;
+        uint32_t k = 0;
+        if (GROUP) {
+            k = p.gw.blk_tensor[b];
+            const uint32_t tw = p.gw.blk_tab[b], tm = p.gm.blk_tab[b];
+            const uint64_t key = ((uint64_t)tm << 32) | tw;
+            if (key != staged) {
+                stage_dec(p.gw.dec[tw], kMWD);
+                stage_dec(p.gm.dec[tm], kMMD);
+                stage_enc(p.gw.enc[tw], kMWE);
+                stage_enc(p.gm.enc[tm], kMME);
+                __syncthreads();
+                staged = key;
+            }
+        }
+        const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
+        const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
+        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        uint64_t r0;
+        uint32_t nb;
+        const uint16_t *gu;
+        if (GROUP) {
+            const BlockSpan sp = group_span(p.gw, k, p.block_elems, b);
+            r0 = sp.sf0;
+            nb = sp.nb;
+            gu = group_span(p.gg, k, p.block_elems, b).dense + h * US;
+        } else {
+            r0 = (uint64_t)b * p.block_elems;
+            nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+            gu = p.g + r0 + h * US;
+        }
+        const uint32_t n_s = stream_len(nb, h * US + l);
+        const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
+        PayWriter stw, stm;
+        stw.init(0, l, n_s);
+        stw.rows.init(p.ow_pay, b, h, cap);
+        stm.init(0, l, n_s);
+        stm.rows.init(p.om_pay, b, h, cap);
+        if (fast) {
+            mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
+        } else {
+            uint32_t cw_s, cm_s, wex, mex;
+            unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
+            unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
+            mom_stream_general<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
+        }
+        const UnitOut ow{p.ow_pay, (!fast && p.park_w) ? wcnt_out : p.ow_cnt, p.ow_scratch, p.nblk,
+                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w)};
+        unit_finish(stw, n_s, u, b, h, 0, ow);
+        const UnitOut om{p.om_pay, (!fast && p.park_m) ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
+                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m)};
+        unit_finish(stm, n_s, u, b, h, 0, om);
+    }
+}
+
 // ------------------------------------------------------------------ launches
 
 // Dynamic LDS beyond 64 KiB must be requested per kernel; remember the
@@ -1679,6 +2119,18 @@ int launch_encode(const EncodeParams &p, void *stream, bool group) {
     const void *fn = group ? ByCap<EncGK>::pick(p.cap_words) : ByCap<EncK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kEncWaves, false, encode_lds(p.cap_words), p, stream,
                   g_lds_granted[group ? 3 : 0][cap_slot(p.cap_words)]);
+}
+
+template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, false>); } };
+template <uint32_t C> struct MomGK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, true>); } };
+std::atomic<size_t> g_mom_lds_granted[2][4];
+
+int launch_mom(const MomParams &p, void *stream, bool group) {
+    const void *fn = group ? ByCap<MomGK>::pick(p.cap_words) : ByCap<MomK>::pick(p.cap_words);
+    const size_t lds = kMWave0 + (size_t)kMomWaves * sgd_wave_bytes(p.cap_words);
+    // persistent: one workgroup is one block at a time
+    return launch(fn, (uint64_t)p.nblk * kMomWaves, kMomWaves, true, lds, p, stream,
+                  g_mom_lds_granted[group ? 1 : 0][cap_slot(p.cap_words)]);
 }
 
 int launch_decode(const DecodeParams &p, void *stream, bool group) {

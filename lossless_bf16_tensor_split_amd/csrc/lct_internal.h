@@ -181,6 +181,51 @@ struct SgdParams {
     DecTab mdec;
 };
 
+// The fused momentum step: W and M decoded, g dense; M' = rne(mu*M + g) and
+// W' = rne(W - eta*M') (M' as rounded), both re-encoded in one pass.  Encode
+// tables travel packed (stream bits | bit count << 24) to keep the arguments
+// small.
+struct MomParams {
+    const uint8_t *w_sf;
+    const uint32_t *w_pay;
+    const uint16_t *w_cnt;
+    const uint64_t *w_obase;
+    const uint8_t *w_ovf;
+    uint64_t w_ovf_cap;
+    const uint8_t *m_sf;
+    const uint32_t *m_pay;
+    const uint16_t *m_cnt;
+    const uint64_t *m_obase;
+    const uint8_t *m_ovf;
+    uint64_t m_ovf_cap;
+    const uint16_t *g;
+    // outputs W' (ow_*) and M' (om_*), each with its own overflow side
+    uint8_t *ow_sf;
+    uint32_t *ow_pay;
+    uint16_t *ow_cnt;
+    uint64_t *ow_obase;
+    uint8_t *ow_ovf;
+    uint64_t ow_ovf_cap;
+    uint32_t *ow_status;
+    uint8_t *ow_scratch;
+    uint8_t *om_sf;
+    uint32_t *om_pay;
+    uint16_t *om_cnt;
+    uint64_t *om_obase;
+    uint8_t *om_ovf;
+    uint64_t om_ovf_cap;
+    uint32_t *om_status;
+    uint8_t *om_scratch;
+    uint64_t n;
+    uint32_t block_elems, cap_words, nblk;
+    float mu, neg_eta;
+    uint32_t park_w, park_m;   // an output's counts overwrite its input's: park them
+    uint32_t pad0;
+    GroupRef gw, gm, gg;       // group kernels: W's and M's codes, the gradients' buffers
+    uint32_t wenc[256], menc[256];   // packed: bits | len << 24 (W' and M')
+    DecTab wdec, mdec;
+};
+
 // Shift sample of a compressed tensor: the values at floor(i * n / m), i < m.
 struct SampleParams {
     const uint8_t *sf;
@@ -229,6 +274,7 @@ int launch_decode(const DecodeParams &p, void *stream, bool group = false);
 // dense: the second operand is dense (p.dense, or in a group the buffers
 // bound to p.gm); the product is p.mul * W + dense
 int launch_sgd(const SgdParams &p, void *stream, bool group = false, bool dense = false);
+int launch_mom(const MomParams &p, void *stream, bool group = false);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.
 int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);
@@ -244,6 +290,7 @@ lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, i
 lct_status reshift_codebook(const lct_codebook &cb, const uint16_t *sample, uint32_t m,
                             lct_codebook *out);
 void fill_enc(const lct_codebook &cb, EncTab *t);
+void fill_enc_packed(const lct_codebook &cb, uint32_t t[256]);
 void fill_dec(const lct_codebook &cb, DecTab *t);
 
 }  // namespace lct

@@ -374,10 +374,11 @@ def test_momentum_zero_rates(L, orc):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-def test_momentum_m_overflow_marks_both_outputs(L, orc, inplace):
-    """M' spills past m_out's overflow region: W' is computed from M' as
-    stored, so w_out's status word carries the overflow bit as well, while
-    M''s fixed side and offsets are still complete."""
+def test_momentum_m_overflow_leaves_w_valid(L, orc, inplace):
+    """M' spills past m_out's overflow region: m_out's status says so and its
+    fixed side and offsets are complete; W' is computed from M' as rounded
+    (one pass), so W' is complete, w_out's status is clean and W' equals the
+    oracle's (which computes W' from M' as rounded too)."""
     g = np.random.default_rng(41)
     B, cw = 4096, 1
     n = 6 * B + 77
@@ -391,7 +392,7 @@ def test_momentum_m_overflow_marks_both_outputs(L, orc, inplace):
     tw, tm = L.encode(cbw, dev(w), lay), L.encode(cbm, dev(m), lay)
     rw, rm = orc.encode(ocw, w, B, cw), orc.encode(ocm, m, B, cw)
     ref_w, ref_m = orc.momentum(ocw, rw, ocm, rm, gr, 0.9, 0.05)
-    assert ref_m.spilled > 16
+    assert ref_m.spilled > 16 and ref_w.spilled > 0
     ow = L.alloc_tensor(n, lay)                      # W' has room for every spill
     om = L.alloc_tensor(n, lay, ovf_cap=ref_m.spilled // 2)
     if inplace:
@@ -400,14 +401,11 @@ def test_momentum_m_overflow_marks_both_outputs(L, orc, inplace):
     L.lct_momentum_step(cbw, tw, cbm, tm, dev(gr), 0.9, 0.05, ow, om)
     gm_ = host_parts(om)
     assert gm_["status"] == L.ST_OVF_FULL
-    assert ow.status_word() & L.ST_OVF_FULL
     for k in ["sf", "pay", "cnt", "obase"]:
         assert np.array_equal(gm_[k], getattr(ref_m, k)), "M' " + k
-    # with room for both, neither is marked
-    ow2, om2 = L.alloc_tensor(n, lay), L.alloc_tensor(n, lay)
-    L.lct_momentum_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), dev(gr), 0.9, 0.05,
-                        ow2, om2)
-    assert ow2.status_word() == 0 and om2.status_word() == 0
+    gw_ = host_parts(ow)
+    assert gw_["status"] == 0
+    assert_same(gw_, ref_w, "W' beside an overflowing M'")
 
 
 def test_momentum_gpt162m_flat(L, orc):
