@@ -205,12 +205,11 @@ void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const
     p.park_cnt = p.o_cnt == p.w_cnt;
 }
 
-// Clear, update, scan.  carry: see launch_clear.
-lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream, bool dense = false,
-                      const uint32_t *carry = nullptr) {
-    int e = launch_clear(p.scratch, nb, p.status, stream, carry);
+// Clear, update, scan.
+lct_status sgd_launch(const SgdParams &p, uint64_t nb, bool group, void *stream) {
+    int e = launch_clear(p.scratch, nb, p.status, stream);
     if (e != hipSuccess) return hip_fail(e, "clear launch");
-    e = launch_sgd(p, stream, group, dense);
+    e = launch_sgd(p, stream, group);
     if (e != hipSuccess) return hip_fail(e, "sgd launch");
     e = launch_scan(p.scratch, nb, p.o_obase, p.o_ovf, p.ovf_cap, p.status, p.o_cnt, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");

@@ -573,13 +573,12 @@ __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_
 
 // ------------------------------------------------------------------ small kernels
 
-// carry (may be null): a status word whose overflow bit the cleared word
-// starts with (an output computed from a tensor whose overflow region ran
-// out is marked invalid too)
-__global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status, const uint32_t *carry) {
+// A scratch header and the status word, cleared by a fill kernel (no
+// memset node if a caller captures the call in a graph).
+__global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nwords) words[i] = 0;
-    if (i == 0) *status = carry ? (*carry & LCT_ST_OVF_FULL) : 0u;
+    if (i == 0) *status = 0u;
 }
 
 // Overflow offsets: an exclusive scan of the units' spill totals in unit
@@ -1089,24 +1088,20 @@ constexpr uint32_t kSgdNoField = kSgdNone - kSgdETab;
 
 // A wave's region (from `base`): the slabs; W's zero row -1 and rows
 // 0..cap-1; a zero row (W's row cap and M's row -1); M's rows; a zero row.
-// The result's rows are not staged: they go to memory as they fill.  With a
-// dense second operand (DENSE) its slab holds 2-byte values (twice the size)
-// and there are no M rows.
+// The result's rows are not staged: they go to memory as they fill.
 struct SgdLayout {
     uint32_t sw, sm, z0, w0, z1, m0, z2, end;
-    __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base, bool dense = false)
+    __host__ __device__ constexpr SgdLayout(uint32_t cap, uint32_t base)
         : sw(base),
           sm(base + kSlabB),
-          z0(base + (dense ? 3 : 2) * kSlabB),
+          z0(base + 2 * kSlabB),
           w0(z0 + ROWB),
           z1(w0 + cap * ROWB),
           m0(z1 + ROWB),
-          z2(dense ? z1 : m0 + cap * ROWB),
+          z2(m0 + cap * ROWB),
           end(z2 + ROWB) {}
 };
-__host__ __device__ constexpr uint32_t sgd_wave_bytes(uint32_t cap, bool dense = false) {
-    return SgdLayout(cap, 0, dense).end;
-}
+__host__ __device__ constexpr uint32_t sgd_wave_bytes(uint32_t cap) { return SgdLayout(cap, 0).end; }
 
 // One element: rne_bf16(fmaf(-eta, m, w)) in bits 31..16 of the result (bits
 // 15..0 hold rounding garbage); a NaN gives 0x7FC0.
@@ -1137,11 +1132,10 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 
 // General path: partial blocks and inputs with spilled fields; byte-wide
 // accesses with per-element checks.
-template <uint32_t CAPT, bool DENSE>
+template <uint32_t CAPT>
 __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
                                                    uint32_t n_s, uint32_t cw_s, uint32_t cm_s,
-                                                   uint64_t r0, const uint16_t *gu, uint64_t wsp,
-                                                   uint64_t msp) {
+                                                   uint64_t r0, uint64_t wsp, uint64_t msp) {
     const uint32_t s = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
@@ -1150,7 +1144,6 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
     const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
     const uint8_t *wsf = p.w_sf + r0 + s;
     const uint8_t *msf = p.m_sf + r0 + s;
-    const uint16_t *gs = gu + s;
     uint8_t *osf = p.o_sf + r0 + s;
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
@@ -1161,10 +1154,7 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
         npos,
         [&](Buf2 &bf, uint32_t j0) {
             load_chunk<true>(bf.w, wsf, j0, n_s);
-            if (DENSE)
-                load_chunk<true>(bf.m, gs, j0, n_s);
-            else
-                load_chunk<true>(bf.m, msf, j0, n_s);
+            load_chunk<true>(bf.m, msf, j0, n_s);
         },
         [&](Buf2 &bf, uint32_t j0) {
             uint32_t e[CH];
@@ -1178,19 +1168,13 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
                     const uint64_t k = wsp + (j - cw_s);
                     ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
                 }
-                uint32_t R;
-                if (DENSE) {
-                    // mu * M + g: the decoded tensor multiplies, the dense one adds
-                    R = sgd_round(bf.m[i] << 16, join32(bf.w[i], ew), p.mul);
-                } else {
-                    uint32_t em = rm.next(kSgdMTab);
-                    rm.q = min(rm.q, qmmax);
-                    if (j >= cm_s && j < n_s) {
-                        const uint64_t k = msp + (j - cm_s);
-                        em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                    }
-                    R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.mul);
+                uint32_t em = rm.next(kSgdMTab);
+                rm.q = min(rm.q, qmmax);
+                if (j >= cm_s && j < n_s) {
+                    const uint64_t k = msp + (j - cm_s);
+                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
                 }
+                const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.mul);
                 if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
                 e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
             }
@@ -1215,15 +1199,14 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
 // position l/4, streams 16*(l%4).. of the unit, with one 16-byte load per
 // tensor and half, issued two halves ahead; the result's bytes overwrite W's
 // in the region and leave with one 16-byte store, half a half later.
-// A half's inputs on their way to LDS: W's sign-fraction bytes, and M's (or,
-// with a dense second operand, the first 16 of its 32 bytes, g1 the rest).
+// A half's inputs on their way to LDS: W's sign-fraction bytes and M's.
 struct HalfRegs {
-    u32x4 w, m, g1;
+    u32x4 w, m;
 };
 
-template <uint32_t CAPT, bool DENSE>
+template <uint32_t CAPT>
 __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
-                                                uint64_t r0, const uint16_t *gu) {
+                                                uint64_t r0) {
     const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t nh = npos / CH;                // halves (the block size is a multiple of 4096)
@@ -1240,8 +1223,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // dropped.
     const uint32_t span = (npos - 1) * NS + US;
     const __amdgpu_buffer_rsrc_t rws = wave_rsrc(p.w_sf + r0, span);
-    const __amdgpu_buffer_rsrc_t rms =
-        DENSE ? wave_rsrc(gu, 2 * span) : wave_rsrc(p.m_sf + r0, span);
+    const __amdgpu_buffer_rsrc_t rms = wave_rsrc(p.m_sf + r0, span);
     const __amdgpu_buffer_rsrc_t ros = wave_rsrc(p.o_sf + r0, span);
     constexpr uint32_t kNone = 0x80000000u;
     constexpr uint32_t kHalfB = CH * NS;          // sign-fraction bytes of a half
@@ -1255,25 +1237,13 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     auto load = [&](HalfRegs &r, uint32_t h) {
         const uint32_t o = h < nh ? h * kHalfB + g : kNone;
         r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
-        if (DENSE) {
-            // the same elements' 2-byte values: 32 bytes (kNone stays out of range)
-            const uint32_t o2 = h < nh ? 2 * (h * kHalfB + g) : kNone;
-            r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o2, 0, 0));
-            r.g1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o2 + 16, 0, 0));
-        } else {
-            r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
-        }
+        r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
     };
     auto region = [&](uint32_t h) { return (h & 1u) * kRegB; };
     // a half's inputs into the region of half h
     auto to_lds = [&](const HalfRegs &r, uint32_t h) {
         st128(lay.sw + region(h) + mine, r.w);
-        if (DENSE) {
-            st128(lay.sm + 2 * region(h) + 2 * mine, r.m);
-            st128(lay.sm + 2 * region(h) + 2 * mine + 16, r.g1);
-        } else {
-            st128(lay.sm + region(h) + mine, r.m);
-        }
+        st128(lay.sm + region(h) + mine, r.m);
     };
 
     // Carried from stage to stage: the inputs of the group whose arithmetic
@@ -1316,17 +1286,16 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         constexpr uint32_t GS = decltype(GS_)::value;
         const uint32_t rc = region(h) + GS * 4 * US;                       // group s's rows
         const uint32_t rp = (GS ? region(h) : region(h + 1)) + ((GS + 3) % 4) * 4 * US;   // group s-1's rows
-        uint32_t wsC[4], msC[4], ewC[4], emC[4] = {0u, 0u, 0u, 0u};
+        uint32_t wsC[4], msC[4], ewC[4], emC[4];
         uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
         const int32_t qw0 = rw.q, qm0 = rm.q;
         if (DEC) {
             winw = rw.window();
-            if (!DENSE) winm = rm.window();
+            winm = rm.window();
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
                 wsC[k] = ld32(lay.sw + rc + k * US + lw);
-                // the dense operand's 2-byte value, or M's sign-fraction word
-                msC[k] = DENSE ? ld16(lay.sm + 2 * rc + 2 * k * US + 2 * l) : ld32(lay.sm + rc + k * US + lw);
+                msC[k] = ld32(lay.sm + rc + k * US + lw);
             }
         }
         // the writer's group, with checks when some stream is near its end
@@ -1341,17 +1310,11 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             if (DEC) {
                 wkw = winw >> cw;
                 enw = ld32(kSgdWTab + (wkw & 0x3FCu));
-                if (!DENSE) {
-                    wkm = winm >> cm;
-                    enm = ld32(kSgdMTab + (wkm & 0x3FCu));
-                }
+                wkm = winm >> cm;
+                enm = ld32(kSgdMTab + (wkm & 0x3FCu));
             }
-            if (DENSE)
-                r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(wsP[k], ewP[k], jsel)),
-                                      __uint_as_float(msP[k] << 16));
-            else
-                r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(msP[k], emP[k], jsel)),
-                                      __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
+            r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(msP[k], emP[k], jsel)),
+                                  __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
             nan |= r[k] != r[k];
             if (k & 1) {
                 uint32_t hh = cvt_bf16x2(r[k - 1], r[k]);
@@ -1369,10 +1332,8 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             if (DEC) {
                 ewC[k] = (wkw << (enw & 31u)) | enw;
                 cw += (enw >> 8) & 0xFFu;
-                if (!DENSE) {
-                    emC[k] = (wkm << (enm & 31u)) | enm;
-                    cm += (enm >> 8) & 0xFFu;
-                }
+                emC[k] = (wkm << (enm & 31u)) | enm;
+                cm += (enm >> 8) & 0xFFu;
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1381,36 +1342,29 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         // needed here; a window that ran out is decoded again (with clamps).
         if (DEC) {
             rw.q += (int32_t)cw;
-            if (!DENSE) rm.q += (int32_t)cm;
+            rm.q += (int32_t)cm;
         }
         if (__builtin_expect(!wave_all((!DEC || max(cw, cm) <= 30) && !nan), 0)) {
             if (DEC && !wave_all(max(cw, cm) <= 30)) {
                 // a window ran out: group s again, one field per window
                 rw.q = qw0;
-                if (!DENSE) rm.q = qm0;
+                rm.q = qm0;
 #pragma unroll
                 for (uint32_t k = 0; k < 4; ++k) {
                     ewC[k] = rw.next(kSgdWTab);
                     rw.q = min(rw.q, qwmax);
-                    if (!DENSE) {
-                        emC[k] = rm.next(kSgdMTab);
-                        rm.q = min(rm.q, qmmax);
-                    }
+                    emC[k] = rm.next(kSgdMTab);
+                    rm.q = min(rm.q, qmmax);
                 }
             }
             // group s-1 with the integer rounding (same fields; a NaN's byte
             // becomes the canonical one's)
 #pragma unroll
             for (uint32_t k = 0; k < 4; k += 2) {
-                uint32_t R0, R1;
-                if (DENSE) {
-                    R0 = sgd_round(msP[k] << 16, join32s(wsP[k], ewP[k], jsel), p.mul);
-                    R1 = sgd_round(msP[k + 1] << 16, join32s(wsP[k + 1], ewP[k + 1], jsel), p.mul);
-                } else {
-                    R0 = sgd_round(join32s(wsP[k], ewP[k], jsel), join32s(msP[k], emP[k], jsel), p.mul);
-                    R1 = sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel), join32s(msP[k + 1], emP[k + 1], jsel),
-                                   p.mul);
-                }
+                const uint32_t R0 =
+                    sgd_round(join32s(wsP[k], ewP[k], jsel), join32s(msP[k], emP[k], jsel), p.mul);
+                const uint32_t R1 = sgd_round(join32s(wsP[k + 1], ewP[k + 1], jsel),
+                                              join32s(msP[k + 1], emP[k + 1], jsel), p.mul);
                 const uint32_t hh = (R0 >> 16) | (R1 & 0xFFFF0000u);
                 ep[k] = (hh >> 4) & 0x7F8u;
                 ep[k + 1] = (hh >> 20) & 0x7F8u;
@@ -1483,14 +1437,12 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 
 // Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
 // a lane, AGPRs included.
-// DENSE: the second operand is the dense BF16 tensor p.dense and the result
-// is p.mul * W + dense (the momentum step's first pass, W standing for M).
-template <uint32_t CAPT, bool GROUP, bool DENSE>
+template <uint32_t CAPT, bool GROUP>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
     if (!GROUP) {
         stage_dec(p.wdec, kSgdWTab);
-        if (!DENSE) stage_dec(p.mdec, kSgdMTab);
+        stage_dec(p.mdec, kSgdMTab);
         stage_enc(p.wenc, kSgdETab);
     }
     if (threadIdx.x < 2) st32(kSgdNone + 4 * threadIdx.x, 0);
@@ -1498,7 +1450,7 @@ void k_sgd(const SgdParams p) {
     uint64_t staged = ~0ull;   // the group tables in LDS: W's (and W''s) and M's, as table indices
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap, DENSE), DENSE);
+    const SgdLayout lay(cap, kSgdWave0 + wave_id() * sgd_wave_bytes(cap));
     st32(lay.z0 + 4 * l, 0);
     st32(lay.z1 + 4 * l, 0);
     st32(lay.z2 + 4 * l, 0);
@@ -1524,11 +1476,11 @@ void k_sgd(const SgdParams p) {
             // Tensors with identical tables share an index: a pair that moves
             // to another tensor stages tables only when they differ.
             k = p.gw.blk_tensor[b];
-            const uint32_t tw = p.gw.blk_tab[b], tm = DENSE ? 0u : p.gm.blk_tab[b];
+            const uint32_t tw = p.gw.blk_tab[b], tm = p.gm.blk_tab[b];
             const uint64_t key = ((uint64_t)tm << 32) | tw;
             if (key != staged) {
                 stage_dec(p.gw.dec[tw], kSgdWTab);
-                if (!DENSE) stage_dec(p.gm.dec[tm], kSgdMTab);
+                stage_dec(p.gm.dec[tm], kSgdMTab);
                 stage_enc(p.gw.enc[tw], kSgdETab);
                 __syncthreads();
                 staged = key;
@@ -1537,24 +1489,17 @@ void k_sgd(const SgdParams p) {
         // the block's overflow offsets are read along with the rows (one
         // memory round trip for both)
         const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
-        const uint64_t mob = DENSE ? 0 : p.m_obase[b], mob1 = DENSE ? 0 : p.m_obase[b + 1];
-        if (DENSE)
-            rows_to_lds<false>(p.w_pay, lay.w0, nullptr, 0, b, h, cap);
-        else
-            rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
+        const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
+        rows_to_lds<true>(p.w_pay, lay.w0, p.m_pay, lay.m0, b, h, cap);
         uint64_t r0;
         uint32_t nb;
-        const uint16_t *gu = nullptr;   // the dense operand's unit (DENSE)
         if (GROUP) {
             const BlockSpan sp = group_span(p.gw, k, p.block_elems, b);
             r0 = sp.sf0;
             nb = sp.nb;
-            // a group's dense operand: the buffers bound to p.gm, same sizes
-            if (DENSE) gu = group_span(p.gm, k, p.block_elems, b).dense + h * US;
         } else {
             r0 = (uint64_t)b * p.block_elems;
             nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
-            if (DENSE) gu = p.dense + r0 + h * US;
         }
         const uint32_t n_s = stream_len(nb, h * US + l);
         const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
@@ -1564,13 +1509,13 @@ void k_sgd(const SgdParams p) {
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
         if (fast) {
-            sgd_stream_full<CAPT, DENSE>(p, lay, st, r0 + h * US, gu);
+            sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
             ++nfull;
         } else {
-            uint32_t cw_s, cm_s = 0, wex, mex = 0;
+            uint32_t cw_s, cm_s, wex, mex;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
-            if (!DENSE) unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
-            sgd_stream_general<CAPT, DENSE>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
+            unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
+            sgd_stream_general<CAPT>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
         }
         // The result's counts overwrite W's when the update is in place:
         // other units of this block may still read W's (general path), so
@@ -1955,7 +1900,7 @@ void k_mom(const MomParams p) {
     uint64_t staged = ~0ull;
     const uint32_t l = lane();
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
-    const SgdLayout lay(cap, kMWave0 + wave_id() * sgd_wave_bytes(cap), false);
+    const SgdLayout lay(cap, kMWave0 + wave_id() * sgd_wave_bytes(cap));
     st32(lay.z0 + 4 * l, 0);
     st32(lay.z1 + 4 * l, 0);
     st32(lay.z2 + 4 * l, 0);
@@ -1964,6 +1909,7 @@ void k_mom(const MomParams p) {
     static_assert(kMomWaves == kMaxUnits, "a workgroup is one block's units");
     // Workgroups take blocks round-robin; the four waves meet at every block
     // (the units share sign-fraction lines and, in a group, the tables).
+    uint32_t nfull = 0;   // units done on the full-block path
     for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
         __builtin_amdgcn_s_barrier();
         const uint32_t h = wave_id();
@@ -2007,6 +1953,7 @@ void k_mom(const MomParams p) {
         stm.rows.init(p.om_pay, b, h, cap);
         if (fast) {
             mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
+            ++nfull;
         } else {
             uint32_t cw_s, cm_s, wex, mex;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
@@ -2019,6 +1966,10 @@ void k_mom(const MomParams p) {
         const UnitOut om{p.om_pay, (!fast && p.park_m) ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
                          p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m)};
         unit_finish(stm, n_s, u, b, h, 0, om);
+    }
+    if (l == 0 && nfull) {
+        atomicAdd(reinterpret_cast<uint32_t *>(p.ow_scratch + kScrFullUnits), nfull);
+        atomicAdd(reinterpret_cast<uint32_t *>(p.om_scratch + kScrFullUnits), nfull);
     }
 }
 
@@ -2049,16 +2000,14 @@ struct ByCap {
 };
 template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, false>); } };
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
-template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, false>); } };
-template <uint32_t C> struct SgdDK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, true>); } };
-template <uint32_t C> struct SgdGDK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, true>); } };
+template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false>); } };
 template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
 template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
-template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, false>); } };
+template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true>); } };
 
 // per kernel (encode, decode, update, the group encode, decode and update,
-// the update with a dense operand, alone and in a group) and capacity slot
-std::atomic<size_t> g_lds_granted[8][4];
+// and capacity slot
+std::atomic<size_t> g_lds_granted[6][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
@@ -2092,13 +2041,13 @@ int launch(const void *fn, uint64_t nunits, uint32_t waves, bool persistent, siz
 
 size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wave_bytes(cap); }
 size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
-size_t sgd_lds(uint32_t cap, bool dense) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap, dense); }
+size_t sgd_lds(uint32_t cap) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap); }
 
-int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream, const uint32_t *carry) {
+int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
     const uint32_t grid = (uint32_t)((words + 255) / 256);
     hipLaunchKernelGGL(k_clear, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                       reinterpret_cast<uint64_t *>(scratch), words, status, carry);
+                       reinterpret_cast<uint64_t *>(scratch), words, status);
     return (int)hipGetLastError();
 }
 
@@ -2139,12 +2088,10 @@ int launch_decode(const DecodeParams &p, void *stream, bool group) {
                   g_lds_granted[group ? 4 : 1][cap_slot(p.cap_words)]);
 }
 
-int launch_sgd(const SgdParams &p, void *stream, bool group, bool dense) {
-    const void *fn = group ? (dense ? ByCap<SgdGDK>::pick(p.cap_words) : ByCap<SgdGK>::pick(p.cap_words))
-                           : (dense ? ByCap<SgdDK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words));
-    const int slot = group ? (dense ? 7 : 5) : (dense ? 6 : 2);
-    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words, dense), p, stream,
-                  g_lds_granted[slot][cap_slot(p.cap_words)]);
+int launch_sgd(const SgdParams &p, void *stream, bool group) {
+    const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+                  g_lds_granted[group ? 5 : 2][cap_slot(p.cap_words)]);
 }
 
 

@@ -167,15 +167,10 @@ struct SgdParams {
     uint8_t *scratch;
     uint64_t n;
     uint32_t block_elems, cap_words, nblk;
-    // The product's factor: -eta for W - eta*M; mu for mu*M + g, where the
-    // decoded tensor (the W fields above) is M and the dense BF16 values
-    // below are g (the first pass of the momentum step).
-    float mul;
-    const uint16_t *dense;
+    float mul;           // the product's factor: -eta, for W - eta*M
     uint32_t park_cnt;   // the result's counts overwrite W's: park them in scratch
-    uint32_t pad1;
     GroupRef gw, gm;     // used by the group kernels only (W's codes for W and W';
-                         // M's for M, or the dense operand's buffers)
+                         // M's for M)
     EncTab wenc;
     DecTab wdec;
     DecTab mdec;
@@ -264,16 +259,12 @@ constexpr int kMaxDevices = 64;
 int noalloc_scratch(uint8_t **out);
 
 // Host-side launchers (kernels.hip).  Each returns the hipError_t of the launch.
-// carry (may be null): the cleared status word starts with carry's overflow bit
-int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream,
-                 const uint32_t *carry = nullptr);
+int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream);
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
                 uint32_t *status, uint16_t *cnt, void *stream);
 int launch_encode(const EncodeParams &p, void *stream, bool group = false);
 int launch_decode(const DecodeParams &p, void *stream, bool group = false);
-// dense: the second operand is dense (p.dense, or in a group the buffers
-// bound to p.gm); the product is p.mul * W + dense
-int launch_sgd(const SgdParams &p, void *stream, bool group = false, bool dense = false);
+int launch_sgd(const SgdParams &p, void *stream, bool group = false);
 int launch_mom(const MomParams &p, void *stream, bool group = false);
 int launch_gather(const uint16_t *x, uint64_t n, uint32_t m, void *stream, uint16_t *host_out);
 // The shift sample of a compressed tensor, copied to host_out; synchronises.

@@ -260,8 +260,8 @@ def narrow_values(orc, g, sigma, n, extra=0.01):
 def test_full_block_path_in_every_mode(L, orc, B, cw, inplace):
     """Full blocks whose inputs spill nothing in CLEAN, MEDIUM and HIGH: every
     unit of the update takes the full-block path (its own counter says so),
-    and W' equals the oracle's round trip; the momentum step's two passes
-    likewise."""
+    and W' equals the oracle's round trip; the fused momentum step likewise
+    (both outputs' counters)."""
     g = np.random.default_rng(B + 7 * cw)
     nblk = 6
     n = nblk * B
