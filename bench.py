@@ -282,7 +282,7 @@ def main():
         t_mom = float(np.mean([e[0].elapsed_time(e[1]) for e in mev])) / 1e3
         bytes_mom = float(np.mean(alg_mom))
         gbs = bytes_mom / t_mom / 1e9
-        mtraffic = load_traffic("momentum_step", wname)
+        mtraffic = load_traffic("k_mom", wname)
         next_ops = {"momentum": {"ms": round(t_mom * 1e3, 4), "alg_bytes": int(bytes_mom),
                                  "alg_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                                  "elems_per_s": float("%.4g" % (n / t_mom)), "mu": mu,
