@@ -313,7 +313,7 @@ def test_config3_gpt162m_flat(L, orc):
 
 # ------------------------------------------------------------------ momentum step
 
-def momentum_case(L, orc, w, m, gr, mw, mm, mu, eta, B, cw, inplace, what=""):
+def momentum_case(L, orc, w, m, gr, mw, mm, mu, eta, B, cw, inplace, what="", outs=None):
     cbw, ocw = check_codebook(L, orc, mw, w)
     cbm, ocm = check_codebook(L, orc, mm, m)
     lay = L.layout(B, cw)
@@ -330,6 +330,8 @@ def momentum_case(L, orc, w, m, gr, mw, mm, mu, eta, B, cw, inplace, what=""):
         ow.sf, ow.pay, ow.cnt, ow.obase = tw.sf, tw.pay, tw.cnt, tw.obase
         om.sf, om.pay, om.cnt, om.obase = tm.sf, tm.pay, tm.cnt, tm.obase
     L.lct_momentum_step(cbw, tw, cbm, tm, dev(gr), mu, eta, ow, om)
+    if outs is not None:
+        outs.extend([ow, om])
     for out, ref, cb, ocb, name in ((ow, ref_w, cbw, ocw, " W'"), (om, ref_m, cbm, ocm, " M'")):
         g = host_parts(out)
         assert_same(g, ref, what + name)
@@ -356,6 +358,61 @@ def test_momentum_small_with_spills(L, orc, B, cw, inplace):
                                  B, cw, inplace, what="B=%d cw=%d inplace=%s" % (B, cw, inplace))
     if cw == 1:
         assert ref_w.spilled > 0 and ref_m.spilled > 0
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_momentum_full_blocks_escapes_and_nans(L, orc, inplace):
+    """The fused momentum kernel's full-block path (no spilled input field):
+    runs of escapes that overrun a four-field window in W and in M, and NaNs
+    in W, M and the gradient, send single stages through the re-decode and
+    the integer rounding.  Every unit must take the full-block path."""
+    g = np.random.default_rng(78)
+    B, nblk = 65536, 4
+    n = nblk * B
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr = synth.to_bf16_bits(g.normal(0, 1e-4, n))
+    tiny = synth.to_bf16_bits(np.array([1e-30, -3e-33, 2e-35, -1e-36]))
+    for blk, s, j in [(0, 5, 40), (1, 130, 0), (2, 255, 252), (3, 64, 17), (0, 200, 128)]:
+        for t in range(4):
+            w[blk * B + (j + t) * 256 + s] = tiny[t]
+    for blk, s, j in [(1, 7, 30), (2, 100, 161), (3, 250, 9), (0, 63, 200)]:
+        for t in range(4):
+            m[blk * B + (j + t) * 256 + s] = tiny[t]
+    w[1 * B + 100 * 256 + 3] = 0x7FC0          # NaN in W
+    m[2 * B + 201 * 256 + 66] = 0xFFC1          # NaN in M (negative, payload)
+    gr[3 * B + 17 * 256 + 129] = 0x7F81         # NaN in g
+    gr[0 * B + 255 * 256 + 255] = 0xFF80        # -inf in g: M' and W' infinite
+    w[3 * B + 255 * 256 + 255] = 0x7F80         # +inf in W, last element
+    ocw = orc.codebook_build(0, 0.02, 0.0, w)
+    ocm = orc.codebook_build(0, 1e-3, 0.0, m)
+    assert orc.encode(ocw, w, B, 25).spilled == 0
+    assert orc.encode(ocm, m, B, 25).spilled == 0
+    outs = []
+    momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.9, 1e-3, B, 25, inplace,
+                  what="momentum escapes/nans inplace=%s" % inplace, outs=outs)
+    assert outs[0].full_path_units() == 4 * nblk and outs[1].full_path_units() == 4 * nblk
+
+
+@pytest.mark.parametrize("B,cw", [(65536, 25), (32768, 11)])
+def test_momentum_full_blocks_outputs_spill(L, orc, B, cw):
+    """Spill-free inputs on the full-block path whose outputs overflow: a
+    gradient far wider than M's codebook makes most of M''s fields escape and
+    W' = W - eta M' leave W's codebook too, so both writers run out of room
+    mid-stream and spill (the path's checked coding and overflow staging)."""
+    g = np.random.default_rng(B + cw + 1)
+    nblk = 3
+    n = nblk * B
+    w = narrow_values(orc, g, 0.02, n)
+    m = narrow_values(orc, g, 1e-3, n)
+    gr = synth.to_bf16_bits(g.normal(0, 0.5, n))
+    ocw, ocm = orc.codebook_build(0, 0.02, 0.0, w), orc.codebook_build(0, 1e-3, 0.0, m)
+    assert orc.encode(ocw, w, B, cw).spilled == 0 and orc.encode(ocm, m, B, cw).spilled == 0
+    outs = []
+    ref_w, ref_m = momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.9, 0.5, B, cw,
+                                 False, what="momentum output spills B=%d cw=%d" % (B, cw), outs=outs)
+    assert ref_m.spilled > n // 4 and ref_w.spilled > 0
+    assert outs[0].full_path_units() == 4 * nblk and outs[1].full_path_units() == 4 * nblk
 
 
 def test_momentum_zero_rates(L, orc):
