@@ -289,8 +289,9 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in,
  * buffer of SGD with momentum is stored compressed like the weights; paragraph
  * on training traffic: decode, update, re-encode in one pass).  Element by
  * element, m' = rne_bf16(fmaf(mu, f32(m), f32(g))), then
- * w' = rne_bf16(fmaf(-eta, f32(m'), f32(w))) with m' as stored; a NaN result
- * is written as 0x7FC0.  W' is encoded with cw, M' with cm.
+ * w' = rne_bf16(fmaf(-eta, f32(m'), f32(w))) with m' as rounded to BF16 (the
+ * value M' stores); a NaN result is written as 0x7FC0.  W' is encoded with
+ * cw, M' with cm.
  * d_g: the dense gradient, device BF16 bit patterns, n elements, 16-byte
  * aligned, overlapping no output.  w_in, m_in, w_out, m_out share n and
  * layout.  Each output's sf, pay, cnt and obase may be its own input's
@@ -407,11 +408,10 @@ lct_status lct_sgd_step_group(const lct_group *gw, const lct_tensor *w_all, cons
                               const lct_tensor *m_all, float eta, const lct_tensor *w_out,
                               void *stream);
 
-/* Momentum step on groups (lct_momentum_step per tensor, two launches of the
- * update kernel): gw's codebooks for W and W', gm's for M and M', and the
- * gradients are gg's dense buffers (gg's codebooks are not used).  The three
- * groups must have the same layout and sizes; the gradients must not overlap
- * an output.  Storage aliasing rules as lct_momentum_step.  Errors: as
+/* Momentum step on groups (lct_momentum_step per tensor, in one launch):
+ * gw's codebooks for W and W', gm's for M and M', and the gradients are gg's
+ * dense buffers (gg's codebooks are not used).  The three groups must have the
+ * same layout and sizes; the gradients must not overlap an output.  Storage aliasing rules as lct_momentum_step.  Errors: as
  * lct_momentum_step. */
 lct_status lct_momentum_step_group(const lct_group *gw, const lct_tensor *w_all, const lct_group *gm,
                                    const lct_tensor *m_all, const lct_group *gg, float mu, float eta,
