@@ -720,19 +720,24 @@ __global__ __launch_bounds__(64) void k_sample(const SampleParams p) {
 // (RFC 1951 order: by length, then field, the escape last as id 256), its
 // encode table and its 8-bit peek decode table, as the host builder does.
 __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
-    __shared__ uint32_t hist[256], base[256], lenf[256], code[257], cnt[16], key[4], wcount[4];
-    __shared__ uint32_t bins[256], syms[256], nbins, nsyms;
+    __shared__ uint32_t hist[256], base[256], lenf[256], code[257], cnt[17], key[4], wcount[4];
+    __shared__ uint32_t bins[256], syms[256], bylen[257], nbins, nsyms;
     const uint32_t t = threadIdx.x;
     hist[t] = 0;
     base[t] = p.base[t];
-    if (t < 16) cnt[t] = 0;
+    if (t < 17) cnt[t] = 0;   // codes per length in cnt[1..8], first codes in cnt[9..16]
     __syncthreads();
-    // the sample's 16 loads per thread all go out before any is counted
+    // the sample's 16 loads per thread all go out before any is counted;
+    // the position floor(i * n / m) without a 64-bit division in the usual
+    // cases (m = 4096 for n >= 4096, m = n below)
     uint32_t es[16];
+    const uint32_t mode = p.m == 4096u ? 0u : p.m == p.n ? 1u : 2u;
 #pragma unroll
     for (uint32_t j = 0; j < 16; ++j) {
         const uint32_t i = t + 256 * j;
-        es[j] = i < p.m ? (p.x[(uint64_t)i * p.n / p.m] >> 7) & 0xFFu : 256u;
+        const uint64_t at = mode == 0u ? ((uint64_t)i * p.n) >> 12 : mode == 1u ? (uint64_t)i
+                                                                                  : (uint64_t)i * p.n / p.m;
+        es[j] = i < p.m ? (p.x[at] >> 7) & 0xFFu : 256u;
     }
 #pragma unroll
     for (uint32_t j = 0; j < 16; ++j)
@@ -753,19 +758,30 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
     // the sample's fields (few for a tensor the model fits): field | count << 8
     compact(hist[t] != 0, t | (hist[t] << 8), bins, &nbins);
     const uint32_t esc_cost = p.esc_len + 8;
-    auto cost_key = [&](int32_t k) {
-        uint32_t c = 0;
-        for (uint32_t j = 0; j < nbins; ++j) {
-            const uint32_t v = bins[j];
-            const int32_t x = (int32_t)(v & 0xFFu) - k;
-            const uint32_t b = (x >= 0 && x < 256) ? base[x] : 0u;
-            c += (v >> 8) * (b ? b : esc_cost);
-        }
-        // cost first, then |k|, then the negative of a pair
+    // cost first, then |k|, then the negative of a pair
+    auto key_of = [](uint32_t c, int32_t k) {
         return (c << 10) | ((uint32_t)(k < 0 ? -k : k) << 1) | (k > 0 ? 1u : 0u);
     };
-    uint32_t best = cost_key((int32_t)t - 255);
-    if (t < 255) best = min(best, cost_key((int32_t)t + 1));
+    // Shifts k0 = t - 255 and k1 = t + 1 (t < 255) costed together, eight
+    // bins at a time so that the table reads of a batch are in flight at once
+    // (a bin past nbins reads as a zero count; j0 + 7 < 256 since j0 <= 248).
+    const int32_t k0 = (int32_t)t - 255, k1 = (int32_t)t + 1;
+    uint32_t c0 = 0, c1 = 0;
+    for (uint32_t j0 = 0; j0 < nbins; j0 += 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) v[i] = j0 + i < nbins ? bins[j0 + i] : 0u;
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            const int32_t x0 = (int32_t)(v[i] & 0xFFu) - k0, x1 = (int32_t)(v[i] & 0xFFu) - k1;
+            const uint32_t b0 = (x0 >= 0 && x0 < 256) ? base[x0] : 0u;
+            const uint32_t b1 = (x1 >= 0 && x1 < 256) ? base[x1] : 0u;
+            c0 += (v[i] >> 8) * (b0 ? b0 : esc_cost);
+            c1 += (v[i] >> 8) * (b1 ? b1 : esc_cost);
+        }
+    }
+    uint32_t best = key_of(c0, k0);
+    if (t < 255) best = min(best, key_of(c1, k1));
     for (uint32_t o = 32; o > 0; o >>= 1) best = min(best, (uint32_t)__shfl_xor((int)best, (int)o));
     if ((t & 63) == 0) key[t >> 6] = best;
     __syncthreads();
@@ -784,22 +800,36 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
         cnt[0] = 0;
         for (uint32_t bits = 1; bits <= 8; ++bits) {
             c = (c + cnt[bits - 1]) << 1;
-            cnt[8 + bits - 1] = c;      // first code of each length, in cnt[8..15]
+            cnt[8 + bits] = c;      // first code of each length
         }
     }
     __syncthreads();
-    auto first_code = [&](uint32_t len) { return cnt[8 + len - 1]; };
+    auto first_code = [&](uint32_t len) { return cnt[8 + len]; };
     // a code is its length's first code plus the coded fields before it of
     // that length; the escape comes after every field of its length
-    if (L) {
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < nsyms; ++j) rank += (syms[j] & 0x1FFu) < t && (syms[j] >> 9) == L;
-        code[t] = first_code(L) + rank;
-    }
-    if (t == 0) {
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < nsyms; ++j) rank += (syms[j] >> 9) == p.esc_len;
-        code[256] = first_code(p.esc_len) + rank;
+    // (eight entries of syms at a time; j0 + 7 < 256 as above)
+    {
+        uint32_t rank = 0, erank = 0;
+        for (uint32_t j0 = 0; j0 < nsyms; j0 += 8) {
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i) {
+                const uint32_t v = j0 + i < nsyms ? syms[j0 + i] : 0u;   // length 0: never counted
+                rank += (v & 0x1FFu) < t && (v >> 9) == L;
+                erank += (v >> 9) == p.esc_len;
+            }
+        }
+        if (L) code[t] = first_code(L) + rank;
+        if (t == 0) code[256] = first_code(p.esc_len) + erank;
+        // the symbols in canonical order: those of length L (the escape the
+        // last of its length) from the number of codes shorter than L
+        uint32_t before = 0;
+        for (uint32_t b = 1; b < 8; ++b) before += b < L ? cnt[b] : 0u;
+        if (L) bylen[before + rank] = t;
+        if (t == 0) {
+            uint32_t eb = 0;
+            for (uint32_t b = 1; b < p.esc_len; ++b) eb += cnt[b];
+            bylen[eb + erank] = 256;
+        }
     }
     __syncthreads();
     auto rev = [](uint32_t v, uint32_t n) { return __brev(v) >> (32 - n); };
@@ -811,13 +841,30 @@ __global__ __launch_bounds__(256) void k_fit(const FitParams p) {
         p.enc->bits[t] = rev(code[256], p.esc_len) | (t << p.esc_len);
         p.enc->len[t] = (uint8_t)(p.esc_len + 8);
     }
-    // decode table: the symbol whose reversed code the peek starts with
+    // decode table: the symbol whose code the peek t starts with.  The
+    // stream holds each code reversed, so the peek's first l bits read
+    // backwards are a code of length l when they fall in that length's range
+    // of canonical values; the shortest such l is the code (no code is a
+    // prefix of another).  Its symbol is bylen[codes shorter than l + offset
+    // in the range].
     uint32_t d = (8u << 8) | (1u << 14);
-    for (uint32_t j = 0; j <= nsyms; ++j) {
-        const uint32_t sj = j < nsyms ? (syms[j] & 0x1FFu) : 256u;
-        const uint32_t ls = j < nsyms ? (syms[j] >> 9) : p.esc_len;
-        if ((t & ((1u << ls) - 1)) == rev(code[sj], ls))
-            d = sj < 256 ? (sj | (ls << 8)) : (((ls + 8) << 8) | (1u << 13));
+    {
+        uint32_t before = 0, found = 0, at = 0, fl = 0;
+#pragma unroll
+        for (uint32_t l = 1; l <= 8; ++l) {
+            const uint32_t c = rev(t & ((1u << l) - 1), l);
+            const uint32_t f = first_code(l);
+            if (!found && cnt[l] && c >= f && c - f < cnt[l]) {
+                found = 1;
+                at = before + (c - f);
+                fl = l;
+            }
+            before += cnt[l];
+        }
+        if (found) {
+            const uint32_t s = bylen[at];
+            d = s < 256 ? (s | (fl << 8)) : (((fl + 8) << 8) | (1u << 13));
+        }
     }
     p.dec->dec[t] = (uint16_t)d;
     if (t == 0) {
