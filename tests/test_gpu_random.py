@@ -127,3 +127,100 @@ def test_random_case(L, orc, idx):  # noqa: F811
     L.lct_momentum_step(cbw, tw, cbm, tm, dev(gr), mu, eta, ow, om)
     for out, ref, name in ((ow, ref_w, " W'"), (om, ref_m, " M'")):
         same(host_parts(out), ref, what + name + " mu=%g eta=%g inplace=%s" % (mu, eta, inplace))
+
+
+# ------------------------------------------------------------------ groups
+
+NGROUPS = 40
+
+
+def lib_cb(L, c):
+    return L.lct_codebook_from_lengths(list(c.len_base), c.esc_len, c.shift)
+
+
+def todev(x):
+    return (dev(x).view(torch.bfloat16) if len(x)
+            else torch.empty(8, dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.parametrize("idx", range(NGROUPS))
+def test_random_group(L, orc, idx):  # noqa: F811
+    """Random groups (1 to 9 tensors of random sizes, empty ones included,
+    each with its own values and codebook) through the group encode, decode,
+    update and momentum calls, against the oracle's groups."""
+    from test_gpu_group import storage_equal
+    g = np.random.default_rng(77000 + idx)
+    B, cw = LAYOUTS[int(g.integers(0, len(LAYOUTS)))]
+    count = int(g.integers(1, 10))
+    ns = []
+    for _ in range(count):
+        kind = int(g.integers(0, 4))
+        ns.append([0, int(g.integers(1, 300)), int(g.integers(1, 2 * B)),
+                   B * int(g.integers(1, 3)) + int(g.integers(-200, 201))][kind])
+    ns = [max(0, min(n, 200000)) for n in ns]
+    op = ["encode", "sgd", "momentum"][int(g.integers(0, 3))]
+    what = "group case %d: %s ns=%s layout=(%d,%d)" % (idx, op, ns, B, cw)
+    lay = L.layout(B, cw)
+
+    def tensors():
+        xs, ocs = [], []
+        for n in ns:
+            x, model = draw_values(g, n)
+            xs.append(x)
+            ocs.append(orc.codebook_build(model.family, model.scale, model.shape, x))
+        return xs, ocs
+
+    ws, ocw = tensors()
+    gw = L.LctGroup(ns, lay, [lib_cb(L, c) for c in ocw], [todev(x) for x in ws])
+    rw = [orc.encode(c, x, B, cw) for c, x in zip(ocw, ws)]
+    full = sum(r.spilled for r in rw)
+    if op == "encode":
+        cap = out_cap(g, full)
+        cap = full + 64 if cap is None else cap
+        all_ = gw.alloc_storage(max(cap, 1))
+        L.lct_encode_group(gw, all_)
+        ref = orc.group(rw, max(cap, 1))
+        storage_equal(L, gw, all_, ref, ns, what)
+        if ref.status == 0:
+            for d in gw.dense:
+                d.zero_()
+            L.lct_decode_group(gw, all_)
+            for k, (x, d) in enumerate(zip(ws, gw.dense)):
+                torch.cuda.synchronize()
+                assert np.array_equal(d.view(torch.int16).cpu().numpy().view(np.uint16)[:len(x)], x), what + " %d" % k
+        return
+    ms, ocm = tensors()
+    gm = L.LctGroup(ns, lay, [lib_cb(L, c) for c in ocm], [todev(x) for x in ms])
+    rm = [orc.encode(c, x, B, cw) for c, x in zip(ocm, ms)]
+    big = sum(ns) + 64
+    w_all, m_all = gw.alloc_storage(big), gm.alloc_storage(big)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    storage_equal(L, gw, w_all, orc.group(rw, big), ns, what + " W")
+    storage_equal(L, gm, m_all, orc.group(rm, big), ns, what + " M")
+    inplace = bool(g.random() < 0.5)
+    eta = float([1e-3, 0.5, 0.0, -1e-2][int(g.integers(0, 4))])
+    if op == "sgd":
+        outs = [orc.sgd(ocw[k], rw[k], ocm[k], rm[k], eta) for k in range(count)]
+        cap = out_cap(g, sum(o.spilled for o in outs))
+        cap = big if cap is None else max(cap, 1)
+        out = gw.alloc_storage(cap)
+        if inplace:
+            out.sf, out.pay, out.cnt, out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+        L.lct_sgd_step_group(gw, w_all, gm, m_all, eta, out)
+        storage_equal(L, gw, out, orc.group(outs, cap), ns, what + " W' eta=%g inplace=%s" % (eta, inplace))
+        return
+    gs = [draw_values(g, n)[0] for n in ns]
+    gg = L.LctGroup(ns, lay, [lib_cb(L, c) for c in ocm], [todev(x) for x in gs])
+    mu = float([0.9, 0.0, 1.5][int(g.integers(0, 3))])
+    refs = [orc.momentum(ocw[k], rw[k], ocm[k], rm[k], gs[k], mu, eta) for k in range(count)]
+    cap = out_cap(g, max(sum(r[0].spilled for r in refs), sum(r[1].spilled for r in refs)))
+    cap = big if cap is None else max(cap, 1)
+    w_out, m_out = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    if inplace:
+        w_out.sf, w_out.pay, w_out.cnt, w_out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+        m_out.sf, m_out.pay, m_out.cnt, m_out.obase = m_all.sf, m_all.pay, m_all.cnt, m_all.obase
+    L.lct_momentum_step_group(gw, w_all, gm, m_all, gg, mu, eta, w_out, m_out)
+    tag = " mu=%g eta=%g inplace=%s" % (mu, eta, inplace)
+    storage_equal(L, gw, w_out, orc.group([r[0] for r in refs], cap), ns, what + " W'" + tag)
+    storage_equal(L, gm, m_out, orc.group([r[1] for r in refs], cap), ns, what + " M'" + tag)
