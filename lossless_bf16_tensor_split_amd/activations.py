@@ -25,6 +25,11 @@ Per saved tensor:
 Tensors that are not BF16, not on the GPU, not contiguous, smaller than
 `min_elems`, or leaves that require grad (parameters, which autograd saves by
 reference at no cost) are saved as they are.
+
+A codec keeps its staging pool, pinned words and base code across uses:
+a training loop makes one and enters it once per step (`with codec:`), so
+only the first step pays for the setup.  `compressed_activations` makes a
+fresh codec for one block.
 """
 from __future__ import annotations
 
@@ -74,6 +79,7 @@ class ActivationCodec:
         self.stored_bytes = 0    # their fixed sides plus spilled bytes
         self.pack_s = 0.0        # host time spent in pack (waits for the device included)
         self.unpack_s = 0.0      # host time spent in unpack
+        self._hooks = None
 
     def _wants(self, x: torch.Tensor) -> bool:
         return (x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
@@ -161,6 +167,23 @@ class ActivationCodec:
         while self._pending:
             self._reap(wait_one=True)
 
+    def __enter__(self):
+        """Install the pack/unpack hooks for the block (one step's forward;
+        backward may run inside or after it)."""
+        if self._hooks is not None:
+            raise RuntimeError("the codec is already entered")
+        self._hooks = torch.autograd.graph.saved_tensors_hooks(self.pack, self.unpack)
+        self._hooks.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        try:
+            self._hooks.__exit__(*exc)
+        finally:
+            self._hooks = None
+            self.close()
+        return False
+
     def ratio(self) -> float:
         return self.raw_bytes / self.stored_bytes if self.stored_bytes else 0.0
 
@@ -169,9 +192,5 @@ class ActivationCodec:
 def compressed_activations(model: Model | None = None, mode: int = CLEAN, min_elems: int = 1 << 16):
     """Within the block, tensors autograd saves for backward are stored
     compressed (see the module docstring); yields the codec for its counts."""
-    codec = ActivationCodec(model, mode, min_elems)
-    try:
-        with torch.autograd.graph.saved_tensors_hooks(codec.pack, codec.unpack):
-            yield codec
-    finally:
-        codec.close()
+    with ActivationCodec(model, mode, min_elems) as codec:
+        yield codec

@@ -49,3 +49,22 @@ def test_default_model_suits_gated_products(orc):
     sp_t, size_t = stored(prod, POWERLAW, 3.0)
     assert sp_t < 0.6 * sp_g and size_t < size_g
     assert stored(gate, POWERLAW, 3.0)[1] <= stored(gate, GAUSSIAN, 0.0)[1]
+
+
+def test_codec_reused_across_steps():
+    """One codec entered once per step: the hooks are installed only inside,
+    a second enter while inside is refused, and the counts add up."""
+    from lossless_bf16_tensor_split_amd.activations import ActivationCodec
+    import pytest
+    codec = ActivationCodec(min_elems=1)
+    x = torch.randn(32, 48, dtype=torch.bfloat16, requires_grad=True)
+    for step in range(3):
+        with codec:
+            with pytest.raises(RuntimeError):
+                codec.__enter__()
+            y = (torch.nn.functional.silu(x) * x).float().sum()
+        y.backward()
+        assert codec.passed > 0 and codec.saved == 0       # CPU tensors pass through
+    passed = codec.passed
+    (torch.nn.functional.silu(x) * x).float().sum().backward()  # outside: no hooks
+    assert codec.passed == passed
