@@ -41,8 +41,14 @@ METRIC = "encode/decode GB/s of BF16 input, fused SGD elems/s, % HBM peak, comp.
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernels' source with comments and blank space removed, so
+    that a change of comments alone keeps recorded counters valid."""
     p = os.path.join(ROOT, "lossless_bf16_tensor_split_amd", "csrc", "kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    src = open(p, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):

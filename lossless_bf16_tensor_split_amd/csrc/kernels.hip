@@ -1,5 +1,7 @@
-// kernels.hip -- encode, decode and fused SGD kernels of the LCT exponent
-// codec, written for CDNA4 (gfx950, wave64).
+// kernels.hip -- encode, decode, fused SGD and fused momentum kernels of the
+// LCT exponent codec, written for CDNA4 (gfx950, wave64), and the small
+// kernels around them (overflow scan and placement, shift sample, device
+// codebook fit).
 //
 // Format (explainer "LCT paper - Lossless Huffman coding of BF16 training
 // tensors", paragraphs on bits and on blocks and streams): a BF16 value splits
@@ -17,7 +19,9 @@
 // share the code tables in LDS and nothing else, so no wave ever waits for
 // another.  Encode and decode run one unit per wave (a workgroup is a block's
 // four units); the fused update's waves are persistent and take units
-// round-robin, so its three tables are staged once per workgroup.  The block's stream words are interleaved (word w of stream s at
+// round-robin, so its three tables are staged once per workgroup; the
+// momentum kernel's persistent workgroups are a block's four units at a time
+// and share its four tables.  The block's stream words are interleaved (word w of stream s at
 // w*256 + s): a unit's payload rows move between HBM and LDS with 16-byte
 // accesses and every lane works on its own column of the wave's LDS rows
 // (a row's lanes hit distinct banks).  Kernels are specialised on the stream
