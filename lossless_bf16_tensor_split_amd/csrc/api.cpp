@@ -170,10 +170,8 @@ lct_status check_group_dense(const lct_group &g, const Parts &p) {
     return LCT_OK;
 }
 
-// The buffers of an update: W (decoded, the product's other factor for a
-// dense operand), M (decoded second operand; null with a dense one), the
-// result.
-void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const lct_tensor &w_out,
+// The buffers of an update: W and M (both decoded) and the result.
+void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor &m, const lct_tensor &w_out,
                 uint64_t nb, float mul) {
     p.w_sf = w_in.sf;
     p.w_pay = w_in.pay;
@@ -181,14 +179,12 @@ void sgd_params(SgdParams &p, const lct_tensor &w_in, const lct_tensor *m, const
     p.w_obase = w_in.obase;
     p.w_ovf = w_in.ovf;
     p.w_ovf_cap = w_in.ovf_cap;
-    if (m) {
-        p.m_sf = m->sf;
-        p.m_pay = m->pay;
-        p.m_cnt = m->cnt;
-        p.m_obase = m->obase;
-        p.m_ovf = m->ovf;
-        p.m_ovf_cap = m->ovf_cap;
-    }
+    p.m_sf = m.sf;
+    p.m_pay = m.pay;
+    p.m_cnt = m.cnt;
+    p.m_obase = m.obase;
+    p.m_ovf = m.ovf;
+    p.m_ovf_cap = m.ovf_cap;
     p.o_sf = w_out.sf;
     p.o_pay = w_out.pay;
     p.o_cnt = w_out.cnt;
@@ -327,7 +323,7 @@ lct_status sgd_run(SgdParams &p, const lct_tensor &w_in, const lct_tensor &m, co
         if (overlaps_any(r, pw, false) || overlaps_any(r, pm, false)) return LCT_EALIAS;
     lct_status st = check_arch();
     if (st != LCT_OK) return st;
-    sgd_params(p, w_in, &m, w_out, nb, -eta);
+    sgd_params(p, w_in, m, w_out, nb, -eta);
     return sgd_launch(p, nb, group, stream);
 }
 
