@@ -37,6 +37,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, AMD's published figure
+# VALU: 256 CUs x 4 SIMDs x 16 lanes at the 2.4 GHz peak clock (a wave64
+# instruction takes four cycles of a 16-lane SIMD)
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 METRIC = "encode/decode GB/s of BF16 input, fused SGD elems/s, % HBM peak, comp. ratio"
 
 
@@ -49,6 +52,44 @@ def kernel_source_hash() -> str:
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
     return hashlib.sha256(src.encode()).hexdigest()[:16]
+
+
+def load_counters(kernel: str, workload: str):
+    """Issue counters per launch of a kernel from the committed rocprofv3
+    summary, if it exists for this workload and the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "sq_codec_kernels_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^counters_json:\s*(\{.*\})\s*$", open(path).read(), re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source") != kernel_source_hash():
+        return None
+    return d.get("per_dispatch", {}).get(kernel)
+
+
+def copy_ceiling(dev, mib=2048, reps=5):
+    """What a plain device copy reaches on this HBM (torch's copy of `mib` MiB,
+    read plus write bytes over the median time)."""
+    import numpy as np
+    import torch
+    nb = mib << 20
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    ms = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    t = float(np.median(ms[1:])) / 1e3
+    return {"GBps": round(2 * nb / t / 1e9, 1), "bytes": 2 * nb, "kind": "torch device copy, median of %d" % reps}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -219,6 +260,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    copy = copy_ceiling(dev)
     timed = ev[args.warmup:]
     t_enc = float(np.mean([e[0].elapsed_time(e[1]) for e in timed])) / 1e3
     t_sgd = float(np.mean([e[1].elapsed_time(e[2]) for e in timed])) / 1e3
@@ -238,12 +280,21 @@ def main():
         gbs = alg[op] / times[op] / 1e9
         per_op[op] = {"ms": round(times[op] * 1e3, 4), "alg_bytes": int(alg[op]),
                       "alg_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    for op in per_op:
+        per_op[op]["copy_frac"] = round(per_op[op]["alg_GBps"] / copy["GBps"], 4)
     per_op["encode"]["GBps_bf16_input"] = round(2 * n / t_enc / 1e9, 1)
     per_op["decode"]["GBps_bf16_output"] = round(2 * n / t_dec / 1e9, 1)
     per_op["sgd"]["elems_per_s"] = float("%.4g" % (n / t_sgd))
     dom = max(times, key=times.get)
     traffic = load_traffic(kname[dom], wname)
+    counters = load_counters(kname[dom], wname)
     achieved = alg[dom] / times[dom] / 1e9
+    valu = None
+    if counters and "SQ_INSTS_VALU" in counters:
+        lane_ops = 64.0 * counters["SQ_INSTS_VALU"] / times[dom]
+        valu = {"achieved": float("%.4g" % lane_ops), "peak": PEAK_VALU_LANE_OPS, "unit": "lane-ops/s",
+                "frac": round(lane_ops / PEAK_VALU_LANE_OPS, 4),
+                "source": "SQ_INSTS_VALU per launch from profiles/sq_codec_kernels_%s.md" % wname}
     # The momentum step (SGD with momentum) on the same workload, timed after
     # the headline step and outside `value`: W (the update's output; the
     # headline step's byte counts are taken above, before these calls rewrite
@@ -340,7 +391,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
+                     "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
+                     "secondary_valu": valu},
+        "hbm_copy": copy,
         "cpu_baseline": cpu,
         "next_ops": next_ops,
     }
