@@ -417,8 +417,9 @@ def configs_leg(L, dev, stream, reps=5):
     Each entry gives GB/s of BF16 input (output for decode), the algorithmic
     bytes (BF16 side, compressed sides, spilled bytes) over the time as a
     fraction of 8 TB/s, the compression ratio, the overflow fraction (spilled
-    fields per element) and the allocated bits per exponent ((payload +
-    overflow bits) / n)."""
+    fields per element), the allocated bits per exponent ((payload +
+    overflow bits) / n) and the occupancy the tensor gives the encode and
+    decode (their waves, and waves per SIMD of the chip)."""
     import numpy as np
     import torch
     import synth
@@ -454,8 +455,11 @@ def configs_leg(L, dev, stream, reps=5):
         t_dec = timed(lambda: L.lct_decode(cb, t, y))
         same = bool(torch.equal(y.view(torch.int16), x16.view(torch.int16)))
         fixed = t.sizes.fixed
+        nblk = (n + lay.block_elems - 1) // lay.block_elems
         out = {"n": n, "mode": {0: "CLEAN", 1: "MEDIUM", 2: "HIGH"}[mode],
                "layout": [lay.block_elems, lay.cap_words],
+               # one wave per 64 streams of a block, over the chip's 1,024 SIMDs
+               "waves": 4 * nblk, "waves_per_simd": round(4 * nblk / 1024.0, 3),
                "encode": entry(t, t_enc, 2 * n + fixed + sp, n, "GBps_bf16_input"),
                "decode": entry(t, t_dec, 2 * n + fixed + sp, n, "GBps_bf16_output"),
                "ratio": round(t.ratio(), 5), "overflow_fraction": round(sp / n, 6),
