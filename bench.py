@@ -447,7 +447,7 @@ def configs_leg(L, dev, stream, reps=5):
         n = x16.numel()
         lay = L.lct_layout_init(mode)
         cb = L.lct_codebook_build(L.Model(model.family, model.scale, model.shape), x16)
-        t = L.alloc_tensor(n, lay, n, dev)
+        t = L.alloc_tensor(n, lay, None, dev)
         y = torch.empty_like(x16)
         t_enc = timed(lambda: L.lct_encode(cb, x16, t))
         st = t.status_word()

@@ -126,7 +126,11 @@ typedef struct {
  *   obase      uint64[nblk + 1]  where block b's spilled bytes start in ovf;
  *              obase[nblk] = total spilled bytes (8-byte aligned)
  *   ovf        uint8[ovf_cap]  spilled exponent fields, raw, in (block,
- *              stream, position) order
+ *              stream, position) order.  ovf_cap = n always suffices; with
+ *              ovf_cap >= nblk * block_elems the writing calls stage spilled
+ *              fields at fixed places in scratch instead of claiming space
+ *              from one shared counter, which is much faster when many
+ *              streams spill
  *   status     uint32[1]  LCT_ST_* bits
  *   scratch    lct_sizes().scratch bytes of working memory (256-byte aligned);
  *              only lct_encode and the output of lct_sgd_step and

@@ -306,9 +306,18 @@ class LctTensor:
         return 2.0 * self.n / self.nbytes() if self.n else 0.0
 
 
+def full_ovf_cap(n: int, lay: Layout) -> int:
+    """An overflow region for every element of n rounded up to whole blocks:
+    no spill can exceed it, and with it the kernels stage spilled fields at
+    fixed places (no shared counter), which is faster when many streams spill."""
+    b = int(lay.block_elems)
+    return -(-n // b) * b if n else 0
+
+
 def alloc_tensor(n: int, lay: Layout, ovf_cap: int | None = None, device="cuda",
                  scratch=None, ovf=None) -> LctTensor:
-    return LctTensor(n, lay, n if ovf_cap is None else ovf_cap, device, scratch, ovf)
+    """Buffers of a compressed tensor (ovf_cap: full_ovf_cap(n, lay) when None)."""
+    return LctTensor(n, lay, full_ovf_cap(n, lay) if ovf_cap is None else ovf_cap, device, scratch, ovf)
 
 
 def _bits16(x: torch.Tensor) -> torch.Tensor:

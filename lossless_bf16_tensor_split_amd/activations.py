@@ -14,8 +14,8 @@ Per saved tensor:
     choice as lct_codebook_reshift_dense, made and turned into tables on the
     device (lct_group_fit), so a save never waits for the device;
   - buffers: the fixed side at its exact size; the spilled bytes land in a
-    staging region (large enough for every element to spill) taken from a
-    small pool.  The shift and the spilled total are copied to pinned host
+    staging region (large enough for every element, in whole blocks, to
+    spill) taken from a small pool.  The shift and the spilled total are copied to pinned host
     memory behind an event; once the event has passed, the spilled bytes move
     to a buffer of exactly their size, the staging region returns to the
     pool, and the host codebook for the decode is made from the shift.  A
@@ -40,7 +40,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (CLEAN, POWERLAW, Codebook, LctGroup, LctTensor, Model, lct_codebook_build,
+from . import (CLEAN, POWERLAW, Codebook, LctGroup, LctTensor, Model, full_ovf_cap, lct_codebook_build,
                lct_codebook_from_lengths, lct_decode, lct_encode_group, lct_layout_init, lct_sizes)
 
 
@@ -127,22 +127,25 @@ class ActivationCodec:
             self._pin_shift = torch.zeros(len(self._stage), dtype=torch.int32, pin_memory=True)
             self._pin_spill = torch.zeros(len(self._stage), dtype=torch.int64, pin_memory=True)
             self._shift = torch.zeros(len(self._stage), dtype=torch.int32, device=dev)
+        # room for every element in whole blocks: the encode stages spilled
+        # fields at fixed places (see full_ovf_cap)
+        cap = full_ovf_cap(n, self.layout)
         st = self._stage[slot]
-        if st is None or st.numel() < n or st.device != dev:
-            self._stage[slot] = st = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
-        sz = lct_sizes(n, self.layout, n)
+        if st is None or st.numel() < cap or st.device != dev:
+            self._stage[slot] = st = torch.empty(max(cap, 16), dtype=torch.uint8, device=dev)
+        sz = lct_sizes(n, self.layout, cap)
         if self._scratch is None or self._scratch.numel() < sz.scratch or self._scratch.device != dev:
             self._scratch = torch.empty(sz.scratch, dtype=torch.uint8, device=dev)
         # the codebook fitted on the device, then the encode with its tables
         grp = LctGroup([n], self.layout, [self.base], [xd], device=dev, fit=True,
                        shift=self._shift[slot:slot + 1], stream=stream)
-        all_ = grp.alloc_storage(n, dev, self._scratch, st)
+        all_ = grp.alloc_storage(cap, dev, self._scratch, st)
         lct_encode_group(grp, all_, stream)
         self._pin_shift[slot:slot + 1].copy_(self._shift[slot:slot + 1], non_blocking=True)
         self._pin_spill[slot:slot + 1].copy_(all_.obase[-1:], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(stream)
-        t = LctTensor.wrap(n, self.layout, n, lct_sizes(n, self.layout, n), all_.sf, all_.pay, all_.cnt,
+        t = LctTensor.wrap(n, self.layout, cap, lct_sizes(n, self.layout, cap), all_.sf, all_.pay, all_.cnt,
                            all_.obase, st, all_.status, None)
         h = _Saved(t, grp, x.shape)
         self._pending.append((h, slot, ev, stream))

@@ -79,6 +79,17 @@ constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kFlagVal = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 21;
+// Staging of spilled fields.  With room for every element in the overflow
+// region (ovf_cap >= nblk * block_elems) a stream's fields have a fixed place
+// in its unit's slice of each staging area (position j of stream s of unit u
+// at u * 64 * npos + s * npos + j), so no wave contends for a shared counter;
+// otherwise space is claimed from a counter as streams start to spill.
+constexpr uint64_t kClaim = ~0ull;
+// A unit's slice of a staging area under fixed staging, or 0 when the
+// region is too small for it (space is then claimed).
+__device__ __forceinline__ uint64_t fixed_stride(uint64_t nblk, uint32_t block_elems, uint64_t ovf_cap) {
+    return nblk * block_elems <= ovf_cap ? (uint64_t)(block_elems / kStreams) * kUnitStreams : 0;
+}
 
 extern __shared__ uint32_t lds[];
 
@@ -336,6 +347,7 @@ struct WriterT {
     uint32_t cs;      // coded prefix length
     uint32_t claimed; // staging space claimed for the spilled fields
     uint64_t soff;    // start of this stream's spilled fields in the staging area
+    uint64_t sbase;   // fixed staging: where the stream's position 0 would go (kClaim: claim space)
     Rows rows;
 
     // row0: address of the output's row 0 (a multiple of the row stride).
@@ -348,6 +360,7 @@ struct WriterT {
         cs = n_s;
         claimed = 0;
         soff = 0;
+        sbase = kClaim;
     }
     __device__ __forceinline__ void put(uint32_t bits, uint32_t len) {
         buf |= (uint64_t)bits << used;
@@ -369,7 +382,11 @@ using PayWriter = WriterT<PayRows>;
 
 // Code the CH fields at positions j0..j0+CH-1, given as encode-table offsets
 // e8[] (8 * field); with CHECKED, positions at or past n_s are absent.  One
-// capacity test per step in the common case.
+// capacity test per step in the common case.  When some lane's stream runs
+// out of room in this step, every lane codes the longest prefix of its
+// fields that fits (the greedy prefix: the first field that does not fit
+// and all after it spill), with the fields past its cut given no bits, so
+// that the wave takes one pass of pair puts instead of a test per field.
 template <bool CHECKED, class W>
 __device__ __forceinline__ void writer_chunk(W &st, const uint32_t (&e8)[CH], uint32_t j0,
                                              uint32_t n_s, uint32_t capbits, uint32_t etab) {
@@ -384,34 +401,40 @@ __device__ __forceinline__ void writer_chunk(W &st, const uint32_t (&e8)[CH], ui
             cl[i] = 0;
         }
     }
-    if (!st.live) return;
+    const bool live = st.live;
     const uint32_t tot = st.total();
     bool fits = tot + CH * 16 <= capbits;
-    if (!fits) {
+    if (live && !fits) {
         uint32_t sum = 0;
 #pragma unroll
         for (uint32_t i = 0; i < CH; ++i) sum += cl[i];
         fits = tot + sum <= capbits;
     }
-    if (fits) {
+    if (!wave_all(fits || !live)) {
+        // cut: the first field whose code does not fit (CH when all do)
+        const uint32_t room = capbits - tot;
+        uint32_t run = 0, cut = CH;
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) {
+            run += cl[i];
+            cut = (run > room && cut == CH) ? i : cut;
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) {
+            cb[i] = i < cut ? cb[i] : 0u;
+            cl[i] = i < cut ? cl[i] : 0u;
+        }
+        if (live && cut < CH) {
+            st.live = 0;
+            st.cs = j0 + cut;
+        }
+    }
+    if (live) {
 #pragma unroll
         for (uint32_t k = 0; k < CH; k += 2) {
             st.put(cb[k], cl[k]);
             st.put(cb[k + 1], cl[k + 1]);
             st.flush();
-        }
-    } else {
-#pragma unroll
-        for (uint32_t i = 0; i < CH; ++i) {
-            if (st.live) {
-                if (st.total() + cl[i] <= capbits) {
-                    st.put(cb[i], cl[i]);
-                    st.flush();
-                } else {
-                    st.live = 0;
-                    st.cs = j0 + i;
-                }
-            }
         }
     }
 }
@@ -424,7 +447,12 @@ __device__ __forceinline__ void writer_spill(W &st, const uint32_t (&e8)[N], uin
                                              uint32_t n_s, uint64_t *stage_ctr, uint8_t *stage,
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
-    if (__any(fresh)) {
+    if (st.sbase != kClaim) {
+        if (fresh) {
+            st.soff = st.sbase + st.cs;
+            st.claimed = 1;
+        }
+    } else if (__any(fresh)) {
         const uint32_t amt = fresh ? n_s - st.cs : 0;
         const uint32_t inc = wave_incl_scan(amt);
         const uint32_t tot = __shfl(inc, 63, 64);
@@ -528,6 +556,7 @@ struct UnitOut {
     uint8_t *scratch;
     uint64_t nblk, ovf_cap;
     uint32_t cap, parked;
+    uint64_t ustride;    // fixed staging: bytes of a unit's slice (0: claimed)
 };
 
 // After a unit's stream loop: its payload rows go out (LdsRows: the wave's
@@ -556,16 +585,30 @@ __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_
     }
     uint64_t base = 0;
     if (total) {
-        unsigned long long t = 0;
-        if (l == 0)
-            t = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
-                          (unsigned long long)total);
-        base = __shfl(t, 0, 64);
+        if (o.ustride) {
+            base = (uint64_t)u * o.ustride;
+        } else {
+            unsigned long long t = 0;
+            if (l == 0)
+                t = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
+                              (unsigned long long)total);
+            base = __shfl(t, 0, 64);
+        }
         const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
         uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
-        for (uint32_t k = 0; k < spill; ++k) {
-            const uint64_t from = st.soff + k, to = base + excl + k;
-            if (from < o.ovf_cap && to < o.ovf_cap) stage2[to] = stage[from];
+        // sixteen bytes a lane at a time, all loads out before any store
+        for (uint32_t k0 = 0; k0 < spill; k0 += 16) {
+            uint32_t v[16];
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) {
+                const uint64_t from = st.soff + k0 + i;
+                v[i] = (k0 + i < spill && from < o.ovf_cap) ? (uint32_t)stage[from] : 0u;
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) {
+                const uint64_t to = base + excl + k0 + i;
+                if (k0 + i < spill && st.soff + k0 + i < o.ovf_cap && to < o.ovf_cap) stage2[to] = (uint8_t)v[i];
+            }
         }
     }
     if (l == 0) {
@@ -1020,11 +1063,13 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode(const EncodeParams p)
     const uint32_t n_s = stream_len(nb, h * US + l);
     Writer st;
     st.init(out0, l, n_s);
+    const uint64_t ustride = fixed_stride(p.nblk, p.block_elems, p.ovf_cap);
+    if (ustride) st.sbase = (uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS);
     if (nb == p.block_elems)
         encode_stream<true, CAPT>(p, st, n_s, sp.dense + h * US, p.sf + sp.sf0 + h * US);
     else
         encode_stream<false, CAPT>(p, st, n_s, sp.dense + h * US, p.sf + sp.sf0 + h * US);
-    const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0};
+    const UnitOut o{p.pay, p.cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0, ustride};
     unit_finish(st, n_s, u, b, h, out0, o);
 }
 
@@ -1517,6 +1562,7 @@ void k_sgd(const SgdParams p) {
     // being even.
     static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
     uint32_t nfull = 0;   // units done on the full-block path
+    const uint64_t ustride = fixed_stride(p.nblk, p.block_elems, p.ovf_cap);
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
@@ -1559,6 +1605,7 @@ void k_sgd(const SgdParams p) {
         PayWriter st;
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
+        if (ustride) st.sbase = (uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS);
         if (fast) {
             sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
             ++nfull;
@@ -1572,7 +1619,7 @@ void k_sgd(const SgdParams p) {
         // other units of this block may still read W's (general path), so
         // they are parked and put in place by the placing kernel.
         const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
-                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt)};
+                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt), ustride};
         unit_finish(st, n_s, u, b, h, 0, o);
     }
     if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
@@ -1961,6 +2008,8 @@ void k_mom(const MomParams p) {
     // Workgroups take blocks round-robin; the four waves meet at every block
     // (the units share sign-fraction lines and, in a group, the tables).
     uint32_t nfull = 0;   // units done on the full-block path
+    const uint64_t wstride = fixed_stride(p.nblk, p.block_elems, p.ow_ovf_cap);
+    const uint64_t mstride = fixed_stride(p.nblk, p.block_elems, p.om_ovf_cap);
     for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
         __builtin_amdgcn_s_barrier();
         const uint32_t h = wave_id();
@@ -2002,6 +2051,8 @@ void k_mom(const MomParams p) {
         stw.rows.init(p.ow_pay, b, h, cap);
         stm.init(0, l, n_s);
         stm.rows.init(p.om_pay, b, h, cap);
+        if (wstride) stw.sbase = (uint64_t)u * wstride + (uint64_t)l * (p.block_elems / NS);
+        if (mstride) stm.sbase = (uint64_t)u * mstride + (uint64_t)l * (p.block_elems / NS);
         if (fast) {
             mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
             ++nfull;
@@ -2012,10 +2063,10 @@ void k_mom(const MomParams p) {
             mom_stream_general<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
         }
         const UnitOut ow{p.ow_pay, (!fast && p.park_w) ? wcnt_out : p.ow_cnt, p.ow_scratch, p.nblk,
-                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w)};
+                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w), wstride};
         unit_finish(stw, n_s, u, b, h, 0, ow);
         const UnitOut om{p.om_pay, (!fast && p.park_m) ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
-                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m)};
+                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m), mstride};
         unit_finish(stm, n_s, u, b, h, 0, om);
     }
     if (l == 0 && nfull) {
