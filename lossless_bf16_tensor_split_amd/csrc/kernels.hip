@@ -348,6 +348,7 @@ struct WriterT {
     uint32_t claimed; // staging space claimed for the spilled fields
     uint64_t soff;    // start of this stream's spilled fields in the staging area
     uint64_t sbase;   // fixed staging: where the stream's position 0 would go (kClaim: claim space)
+    uint32_t slot;    // fixed staging: positions of a stream's place
     Rows rows;
 
     // row0: address of the output's row 0 (a multiple of the row stride).
@@ -361,6 +362,12 @@ struct WriterT {
         claimed = 0;
         soff = 0;
         sbase = kClaim;
+        slot = 0;
+    }
+    // fixed staging: this lane's stream takes positions [base, base + npos)
+    __device__ __forceinline__ void fixed(uint64_t base, uint32_t npos) {
+        sbase = base;
+        slot = npos;
     }
     __device__ __forceinline__ void put(uint32_t bits, uint32_t len) {
         buf |= (uint64_t)bits << used;
@@ -448,10 +455,28 @@ __device__ __forceinline__ void writer_spill(W &st, const uint32_t (&e8)[N], uin
                                              uint64_t stage_cap) {
     const bool fresh = !st.live && !st.claimed;
     if (st.sbase != kClaim) {
+        // fixed places: the step's N fields go out in one store of N bytes
+        // at the stream's position j0 (aligned: j0, the unit's slice and the
+        // stream's share of it are multiples of N); the bytes before the
+        // stream's cut are never read
+        static_assert(N == 4 || N == 16, "one dword or one 16-byte store");
         if (fresh) {
             st.soff = st.sbase + st.cs;
             st.claimed = 1;
         }
+        if (!st.live && j0 + N <= st.slot) {
+            uint32_t wd[N / 4];
+#pragma unroll
+            for (uint32_t q = 0; q < N / 4; ++q)
+                wd[q] = ((e8[4 * q] >> 3) & 0xFFu) | (((e8[4 * q + 1] >> 3) & 0xFFu) << 8) |
+                        (((e8[4 * q + 2] >> 3) & 0xFFu) << 16) | (((e8[4 * q + 3] >> 3) & 0xFFu) << 24);
+            uint8_t *at = stage + st.sbase + j0;
+            if constexpr (N == 16)
+                *reinterpret_cast<u32x4 *>(at) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            else
+                *reinterpret_cast<uint32_t *>(at) = wd[0];
+        }
+        return;
     } else if (__any(fresh)) {
         const uint32_t amt = fresh ? n_s - st.cs : 0;
         const uint32_t inc = wave_incl_scan(amt);
@@ -584,16 +609,32 @@ __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_
             st.rows.store(w, 0);
     }
     uint64_t base = 0;
-    if (total) {
-        if (o.ustride) {
-            base = (uint64_t)u * o.ustride;
-        } else {
-            unsigned long long t = 0;
-            if (l == 0)
-                t = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
-                              (unsigned long long)total);
-            base = __shfl(t, 0, 64);
+    if (total && o.ustride) {
+        // fixed places: the unit's slice of the second staging area; the
+        // wave copies the piece together, a byte a lane, each destination
+        // byte d from the stream s whose range [excl_s, excl_s + spill_s)
+        // holds it (the last stream with excl_s <= d, found by halving)
+        base = (uint64_t)u * o.ustride;
+        const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
+        uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
+        const uint64_t src = spill ? st.soff : 0;
+        for (uint32_t d0 = 0; d0 < total; d0 += 64) {
+            const uint32_t d = d0 + l;
+            uint32_t sel = 0;
+#pragma unroll
+            for (uint32_t step = 32; step >= 1; step >>= 1) {
+                const uint32_t c = sel + step;
+                sel = (uint32_t)__shfl((int)excl, (int)c, 64) <= d ? c : sel;
+            }
+            const uint64_t from = __shfl(src, (int)sel, 64) + (d - (uint32_t)__shfl((int)excl, (int)sel, 64));
+            if (d < total && from < o.ovf_cap && base + d < o.ovf_cap) stage2[base + d] = stage[from];
         }
+    } else if (total) {
+        unsigned long long t = 0;
+        if (l == 0)
+            t = atomicAdd(reinterpret_cast<unsigned long long *>(o.scratch + kScrStage2),
+                          (unsigned long long)total);
+        base = __shfl(t, 0, 64);
         const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
         uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
         // sixteen bytes a lane at a time, all loads out before any store
@@ -1064,7 +1105,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode(const EncodeParams p)
     Writer st;
     st.init(out0, l, n_s);
     const uint64_t ustride = fixed_stride(p.nblk, p.block_elems, p.ovf_cap);
-    if (ustride) st.sbase = (uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS);
+    if (ustride) st.fixed((uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
     if (nb == p.block_elems)
         encode_stream<true, CAPT>(p, st, n_s, sp.dense + h * US, p.sf + sp.sf0 + h * US);
     else
@@ -1605,7 +1646,7 @@ void k_sgd(const SgdParams p) {
         PayWriter st;
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
-        if (ustride) st.sbase = (uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS);
+        if (ustride) st.fixed((uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
         if (fast) {
             sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
             ++nfull;
@@ -2051,8 +2092,8 @@ void k_mom(const MomParams p) {
         stw.rows.init(p.ow_pay, b, h, cap);
         stm.init(0, l, n_s);
         stm.rows.init(p.om_pay, b, h, cap);
-        if (wstride) stw.sbase = (uint64_t)u * wstride + (uint64_t)l * (p.block_elems / NS);
-        if (mstride) stm.sbase = (uint64_t)u * mstride + (uint64_t)l * (p.block_elems / NS);
+        if (wstride) stw.fixed((uint64_t)u * wstride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
+        if (mstride) stm.fixed((uint64_t)u * mstride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
         if (fast) {
             mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
             ++nfull;
