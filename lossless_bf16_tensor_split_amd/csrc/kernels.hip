@@ -79,11 +79,13 @@ constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kFlagVal = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 21;
-// Staging of spilled fields.  With room for every element in the overflow
-// region (ovf_cap >= nblk * block_elems) a stream's fields have a fixed place
-// in its unit's slice of each staging area (position j of stream s of unit u
-// at u * 64 * npos + s * npos + j), so no wave contends for a shared counter;
-// otherwise space is claimed from a counter as streams start to spill.
+// Staging of spilled fields.  In the encoder, with room for every element in
+// the overflow region (ovf_cap >= nblk * block_elems), a stream's fields have
+// a fixed place in its unit's slice of each staging area (position j of
+// stream s of unit u at u * 64 * npos + s * npos + j), so no wave contends
+// for a shared counter; otherwise (and in the updates, whose outputs rarely
+// spill and whose registers the extra code would cost) space is claimed from
+// a counter as streams start to spill.
 constexpr uint64_t kClaim = ~0ull;
 // A unit's slice of a staging area under fixed staging, or 0 when the
 // region is too small for it (space is then claimed).
@@ -394,7 +396,9 @@ using PayWriter = WriterT<PayRows>;
 // fields that fits (the greedy prefix: the first field that does not fit
 // and all after it spill), with the fields past its cut given no bits, so
 // that the wave takes one pass of pair puts instead of a test per field.
-template <bool CHECKED, class W>
+// Without GREEDY a stream that runs out of room tests its fields one by one
+// (fewer registers: the updates, whose outputs rarely run out, take this).
+template <bool CHECKED, bool GREEDY, class W>
 __device__ __forceinline__ void writer_chunk(W &st, const uint32_t (&e8)[CH], uint32_t j0,
                                              uint32_t n_s, uint32_t capbits, uint32_t etab) {
     uint32_t cb[CH], cl[CH];
@@ -407,6 +411,39 @@ __device__ __forceinline__ void writer_chunk(W &st, const uint32_t (&e8)[CH], ui
             cb[i] = 0;
             cl[i] = 0;
         }
+    }
+    if constexpr (!GREEDY) {
+        if (!st.live) return;
+        const uint32_t tot = st.total();
+        bool fits = tot + CH * 16 <= capbits;
+        if (!fits) {
+            uint32_t sum = 0;
+#pragma unroll
+            for (uint32_t i = 0; i < CH; ++i) sum += cl[i];
+            fits = tot + sum <= capbits;
+        }
+        if (fits) {
+#pragma unroll
+            for (uint32_t k = 0; k < CH; k += 2) {
+                st.put(cb[k], cl[k]);
+                st.put(cb[k + 1], cl[k + 1]);
+                st.flush();
+            }
+        } else {
+#pragma unroll
+            for (uint32_t i = 0; i < CH; ++i) {
+                if (st.live) {
+                    if (st.total() + cl[i] <= capbits) {
+                        st.put(cb[i], cl[i]);
+                        st.flush();
+                    } else {
+                        st.live = 0;
+                        st.cs = j0 + i;
+                    }
+                }
+            }
+        }
+        return;
     }
     const bool live = st.live;
     const uint32_t tot = st.total();
@@ -637,19 +674,11 @@ __device__ __forceinline__ void unit_finish(const WriterT<Rows> &st, uint32_t n_
         base = __shfl(t, 0, 64);
         const uint8_t *stage = o.scratch + scr_stage_offset(o.nblk);
         uint8_t *stage2 = o.scratch + scr_stage2_offset(o.nblk, o.ovf_cap);
-        // sixteen bytes a lane at a time, all loads out before any store
-        for (uint32_t k0 = 0; k0 < spill; k0 += 16) {
-            uint32_t v[16];
-#pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {
-                const uint64_t from = st.soff + k0 + i;
-                v[i] = (k0 + i < spill && from < o.ovf_cap) ? (uint32_t)stage[from] : 0u;
-            }
-#pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {
-                const uint64_t to = base + excl + k0 + i;
-                if (k0 + i < spill && st.soff + k0 + i < o.ovf_cap && to < o.ovf_cap) stage2[to] = (uint8_t)v[i];
-            }
+        // a byte at a time per lane: rare in the updates, whose outputs
+        // seldom spill, and cheap in registers there
+        for (uint32_t k = 0; k < spill; ++k) {
+            const uint64_t from = st.soff + k, to = base + excl + k;
+            if (from < o.ovf_cap && to < o.ovf_cap) stage2[to] = stage[from];
         }
     }
     if (l == 0) {
@@ -1061,7 +1090,7 @@ __device__ __forceinline__ void encode_stream(const EncodeParams &p, Writer &st,
                 e[i] = (bf.v[i] >> 4) & 0x7F8u;   // 8 * exponent field
                 if (FULL || j0 + i < n_s) o[i * NS] = (uint8_t)sf_of(bf.v[i]);
             }
-            writer_chunk<!FULL>(st, e, j0, n_s, capbits, kEncTab);
+            writer_chunk<!FULL, true>(st, e, j0, n_s, capbits, kEncTab);
             writer_spill<!FULL>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
 }
@@ -1315,7 +1344,7 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
                 if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
                 e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
             }
-            writer_chunk<true>(st, e, j0, n_s, capbits, kSgdETab);
+            writer_chunk<true, false>(st, e, j0, n_s, capbits, kSgdETab);
             writer_spill<true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
 }
@@ -1603,7 +1632,6 @@ void k_sgd(const SgdParams p) {
     // being even.
     static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
     uint32_t nfull = 0;   // units done on the full-block path
-    const uint64_t ustride = fixed_stride(p.nblk, p.block_elems, p.ovf_cap);
     for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
@@ -1646,7 +1674,6 @@ void k_sgd(const SgdParams p) {
         PayWriter st;
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
-        if (ustride) st.fixed((uint64_t)u * ustride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
         if (fast) {
             sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
             ++nfull;
@@ -1660,7 +1687,7 @@ void k_sgd(const SgdParams p) {
         // other units of this block may still read W's (general path), so
         // they are parked and put in place by the placing kernel.
         const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
-                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt), ustride};
+                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt), 0};
         unit_finish(st, n_s, u, b, h, 0, o);
     }
     if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
@@ -1758,9 +1785,9 @@ __device__ __forceinline__ void mom_stream_general(const MomParams &p, const Sgd
                 ew[i] = (Rw >> 20) & 0x7F8u;
                 em[i] = (Rm >> 20) & 0x7F8u;
             }
-            writer_chunk<true>(stw, ew, j0, n_s, capbits, kMWE);
+            writer_chunk<true, false>(stw, ew, j0, n_s, capbits, kMWE);
             writer_spill<true>(stw, ew, j0, n_s, wctr, wstage, p.ow_ovf_cap);
-            writer_chunk<true>(stm, em, j0, n_s, capbits, kMME);
+            writer_chunk<true, false>(stm, em, j0, n_s, capbits, kMME);
             writer_spill<true>(stm, em, j0, n_s, mctr, mstage, p.om_ovf_cap);
         });
 }
@@ -2049,8 +2076,6 @@ void k_mom(const MomParams p) {
     // Workgroups take blocks round-robin; the four waves meet at every block
     // (the units share sign-fraction lines and, in a group, the tables).
     uint32_t nfull = 0;   // units done on the full-block path
-    const uint64_t wstride = fixed_stride(p.nblk, p.block_elems, p.ow_ovf_cap);
-    const uint64_t mstride = fixed_stride(p.nblk, p.block_elems, p.om_ovf_cap);
     for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
         __builtin_amdgcn_s_barrier();
         const uint32_t h = wave_id();
@@ -2092,8 +2117,6 @@ void k_mom(const MomParams p) {
         stw.rows.init(p.ow_pay, b, h, cap);
         stm.init(0, l, n_s);
         stm.rows.init(p.om_pay, b, h, cap);
-        if (wstride) stw.fixed((uint64_t)u * wstride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
-        if (mstride) stm.fixed((uint64_t)u * mstride + (uint64_t)l * (p.block_elems / NS), p.block_elems / NS);
         if (fast) {
             mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
             ++nfull;
@@ -2104,10 +2127,10 @@ void k_mom(const MomParams p) {
             mom_stream_general<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
         }
         const UnitOut ow{p.ow_pay, (!fast && p.park_w) ? wcnt_out : p.ow_cnt, p.ow_scratch, p.nblk,
-                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w), wstride};
+                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w), 0};
         unit_finish(stw, n_s, u, b, h, 0, ow);
         const UnitOut om{p.om_pay, (!fast && p.park_m) ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
-                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m), mstride};
+                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m), 0};
         unit_finish(stm, n_s, u, b, h, 0, om);
     }
     if (l == 0 && nfull) {
