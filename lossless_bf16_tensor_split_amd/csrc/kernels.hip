@@ -1601,9 +1601,46 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     __builtin_amdgcn_raw_buffer_store_b128(outv, ros, (nh - 1) * kHalfB + g, 0, 0);
 }
 
+// A block takes the full-block path when it is whole and neither input has
+// a spilled field in it.  The update and the momentum step run that path and
+// the general one in kernels of their own (the general path's registers
+// would otherwise set the budget of the common one): the first skips the
+// other blocks, the second finds them with one test per lane for 64 blocks
+// at a time and does only those.
+template <bool GROUP, class P>
+__device__ __forceinline__ uint32_t block_len(const P &p, uint32_t b) {
+    if (GROUP) return group_span(p.gw, p.gw.blk_tensor[b], p.block_elems, b).nb;
+    return (uint32_t)min<uint64_t>(p.block_elems, p.n - (uint64_t)b * p.block_elems);
+}
+template <class P>
+__device__ __forceinline__ bool block_full(const P &p, uint32_t b, uint32_t nb, uint64_t wob, uint64_t wob1,
+                                           uint64_t mob, uint64_t mob1) {
+    return nb == p.block_elems && wob == wob1 && mob == mob1;
+}
+// The general kernel's walk: f(i) for every i < count taken by this
+// workgroup (i = blockIdx.x, + gridDim.x, ...) whose block is not full;
+// blk(i) names i's block.  Every wave of the workgroup takes the same i in
+// the same order.
+template <bool GROUP, class P, class Blk, class F>
+__device__ __forceinline__ void for_general(const P &p, uint32_t count, Blk blk, F f) {
+    const uint32_t G = gridDim.x;
+    for (uint64_t base = blockIdx.x; base < count; base += 64ull * G) {
+        const uint64_t i = base + (uint64_t)lane() * G;
+        bool gen = false;
+        if (i < count) {
+            const uint32_t b = blk((uint32_t)i);
+            gen = !block_full(p, b, block_len<GROUP>(p, b), p.w_obase[b], p.w_obase[b + 1], p.m_obase[b],
+                              p.m_obase[b + 1]);
+        }
+        for (uint64_t mask = __ballot(gen); mask; mask &= mask - 1)
+            f((uint32_t)(base + (uint64_t)__builtin_ctzll(mask) * G));
+    }
+}
+
 // Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
-// a lane, AGPRs included.
-template <uint32_t CAPT, bool GROUP>
+// a lane, AGPRs included.  GEN: the general kernel (blocks that are not
+// full); otherwise the full-block kernel.
+template <uint32_t CAPT, bool GROUP, bool GEN>
 __global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
     if (!GROUP) {
@@ -1623,7 +1660,6 @@ void k_sgd(const SgdParams p) {
     const uint32_t nunits = p.nblk * kMaxUnits;
     uint16_t *cnt_out = p.park_cnt ? reinterpret_cast<uint16_t *>(p.scratch + scr_cnt_offset(p.nblk))
                                    : p.o_cnt;
-    const uint32_t stride = gridDim.x * kSgdWaves;
     // The two waves of a workgroup take units 2i and 2i+1 of one block, whose
     // sign-fraction bytes share every 128-byte line.  Left free, the waves
     // drift apart over many units and the second read of a line misses L2, so
@@ -1632,7 +1668,8 @@ void k_sgd(const SgdParams p) {
     // being even.
     static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
     uint32_t nfull = 0;   // units done on the full-block path
-    for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) {
+    // One unit (the full-block kernel leaves the others to the general one).
+    auto unit = [&](uint32_t u) {
         __builtin_amdgcn_s_barrier();
         const uint32_t b = unit_block(u), h = unit_part(u);
         uint32_t k = 0;
@@ -1667,30 +1704,40 @@ void k_sgd(const SgdParams p) {
             r0 = (uint64_t)b * p.block_elems;
             nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
         }
+        if (!GEN && !block_full(p, b, nb, wob, wob1, mob, mob1)) return;
         const uint32_t n_s = stream_len(nb, h * US + l);
-        const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
         // The result's rows go straight to memory: W's rows, which an update
         // in place overwrites, are all in LDS by now.
         PayWriter st;
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
-        if (fast) {
+        if (!GEN) {
             sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
             ++nfull;
+            const UnitOut o{p.o_pay, p.o_cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0, 0};
+            unit_finish(st, n_s, u, b, h, 0, o);
         } else {
             uint32_t cw_s, cm_s, wex, mex;
             unit_spills(p.w_cnt + (uint64_t)b * NS, nb, h, cw_s, wex);
             unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
             sgd_stream_general<CAPT>(p, lay, st, n_s, cw_s, cm_s, r0 + h * US, wob + wex, mob + mex);
+            // The result's counts overwrite W's when the update is in place:
+            // other units of this block may still read W's, so they are
+            // parked and put in place by the placing kernel.  (The
+            // full-block kernel reads no counts.)
+            const UnitOut o{p.o_pay, cnt_out, p.scratch, p.nblk, p.ovf_cap, cap, p.park_cnt, 0};
+            unit_finish(st, n_s, u, b, h, 0, o);
         }
-        // The result's counts overwrite W's when the update is in place:
-        // other units of this block may still read W's (general path), so
-        // they are parked and put in place by the placing kernel.
-        const UnitOut o{p.o_pay, (!fast && p.park_cnt) ? cnt_out : p.o_cnt, p.scratch, p.nblk,
-                        p.ovf_cap, cap, (uint32_t)(!fast && p.park_cnt), 0};
-        unit_finish(st, n_s, u, b, h, 0, o);
+    };
+    if (!GEN) {
+        const uint32_t stride = gridDim.x * kSgdWaves;
+        for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) unit(u);
+        if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
+    } else {
+        // pairs of units: pair i is units 2i and 2i+1, of block i / 2
+        for_general<GROUP>(p, nunits / kSgdWaves, [](uint32_t i) { return i / 2; },
+                           [&](uint32_t i) { unit(kSgdWaves * i + wave_id()); });
     }
-    if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
 }
 
 // ------------------------------------------------------------------ fused momentum step
@@ -2052,7 +2099,8 @@ __device__ __forceinline__ void mom_stream_full(const MomParams &p, const SgdLay
     __builtin_amdgcn_raw_buffer_store_b128(outm, roms, (nh - 1) * kHalfB + piece, 0, 0);
 }
 
-template <uint32_t CAPT, bool GROUP>
+// GEN: the general kernel (blocks that are not full), as for the update.
+template <uint32_t CAPT, bool GROUP, bool GEN>
 __global__ __launch_bounds__(64 * kMomWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void k_mom(const MomParams p) {
     if (!GROUP) {
@@ -2076,7 +2124,7 @@ void k_mom(const MomParams p) {
     // Workgroups take blocks round-robin; the four waves meet at every block
     // (the units share sign-fraction lines and, in a group, the tables).
     uint32_t nfull = 0;   // units done on the full-block path
-    for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
+    auto block = [&](uint32_t b) {
         __builtin_amdgcn_s_barrier();
         const uint32_t h = wave_id();
         const uint32_t u = b * kMaxUnits + h;
@@ -2110,14 +2158,14 @@ void k_mom(const MomParams p) {
             nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
             gu = p.g + r0 + h * US;
         }
+        if (!GEN && !block_full(p, b, nb, wob, wob1, mob, mob1)) return;
         const uint32_t n_s = stream_len(nb, h * US + l);
-        const bool fast = nb == p.block_elems && wob == wob1 && mob == mob1;
         PayWriter stw, stm;
         stw.init(0, l, n_s);
         stw.rows.init(p.ow_pay, b, h, cap);
         stm.init(0, l, n_s);
         stm.rows.init(p.om_pay, b, h, cap);
-        if (fast) {
+        if (!GEN) {
             mom_stream_full<CAPT>(p, lay, stw, stm, r0 + h * US, gu);
             ++nfull;
         } else {
@@ -2126,16 +2174,23 @@ void k_mom(const MomParams p) {
             unit_spills(p.m_cnt + (uint64_t)b * NS, nb, h, cm_s, mex);
             mom_stream_general<CAPT>(p, lay, stw, stm, n_s, cw_s, cm_s, r0 + h * US, gu, wob + wex, mob + mex);
         }
-        const UnitOut ow{p.ow_pay, (!fast && p.park_w) ? wcnt_out : p.ow_cnt, p.ow_scratch, p.nblk,
-                         p.ow_ovf_cap, cap, (uint32_t)(!fast && p.park_w), 0};
+        // in place, the general kernel parks the counts (other units of the
+        // block still read the inputs'); the full-block kernel reads none
+        const UnitOut ow{p.ow_pay, GEN ? wcnt_out : p.ow_cnt, p.ow_scratch, p.nblk,
+                         p.ow_ovf_cap, cap, GEN ? p.park_w : 0u, 0};
         unit_finish(stw, n_s, u, b, h, 0, ow);
-        const UnitOut om{p.om_pay, (!fast && p.park_m) ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
-                         p.om_ovf_cap, cap, (uint32_t)(!fast && p.park_m), 0};
+        const UnitOut om{p.om_pay, GEN ? mcnt_out : p.om_cnt, p.om_scratch, p.nblk,
+                         p.om_ovf_cap, cap, GEN ? p.park_m : 0u, 0};
         unit_finish(stm, n_s, u, b, h, 0, om);
-    }
-    if (l == 0 && nfull) {
-        atomicAdd(reinterpret_cast<uint32_t *>(p.ow_scratch + kScrFullUnits), nfull);
-        atomicAdd(reinterpret_cast<uint32_t *>(p.om_scratch + kScrFullUnits), nfull);
+    };
+    if (!GEN) {
+        for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) block(b);
+        if (l == 0 && nfull) {
+            atomicAdd(reinterpret_cast<uint32_t *>(p.ow_scratch + kScrFullUnits), nfull);
+            atomicAdd(reinterpret_cast<uint32_t *>(p.om_scratch + kScrFullUnits), nfull);
+        }
+    } else {
+        for_general<GROUP>(p, p.nblk, [](uint32_t i) { return i; }, block);
     }
 }
 
@@ -2166,14 +2221,16 @@ struct ByCap {
 };
 template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, false>); } };
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
-template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false>); } };
+template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, false>); } };
+template <uint32_t C> struct SgdXK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, true>); } };
 template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
 template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
-template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true>); } };
+template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, false>); } };
+template <uint32_t C> struct SgdGXK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, true>); } };
 
 // per kernel (encode, decode, update, the group encode, decode and update,
-// and capacity slot
-std::atomic<size_t> g_lds_granted[6][4];
+// the update's general kernel, flat and group) and capacity slot
+std::atomic<size_t> g_lds_granted[8][4];
 
 int cap_slot(uint32_t cap) { return cap == 25 ? 0 : cap == 12 ? 1 : cap == 11 ? 2 : 3; }
 
@@ -2236,16 +2293,26 @@ int launch_encode(const EncodeParams &p, void *stream, bool group) {
                   g_lds_granted[group ? 3 : 0][cap_slot(p.cap_words)]);
 }
 
-template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, false>); } };
-template <uint32_t C> struct MomGK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, true>); } };
-std::atomic<size_t> g_mom_lds_granted[2][4];
+template <uint32_t C> struct MomK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, false, false>); } };
+template <uint32_t C> struct MomGK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, true, false>); } };
+template <uint32_t C> struct MomXK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, false, true>); } };
+template <uint32_t C> struct MomGXK { static const void *fn() { return reinterpret_cast<const void *>(&k_mom<C, true, true>); } };
+// flat, group, and their general kernels
+std::atomic<size_t> g_mom_lds_granted[4][4];
 
+// The full-block kernel, then the general one (which ends at once when every
+// block is full).
 int launch_mom(const MomParams &p, void *stream, bool group) {
-    const void *fn = group ? ByCap<MomGK>::pick(p.cap_words) : ByCap<MomK>::pick(p.cap_words);
     const size_t lds = kMWave0 + (size_t)kMomWaves * sgd_wave_bytes(p.cap_words);
+    const int slot = cap_slot(p.cap_words);
     // persistent: one workgroup is one block at a time
+    const void *fn = group ? ByCap<MomGK>::pick(p.cap_words) : ByCap<MomK>::pick(p.cap_words);
+    int e = launch(fn, (uint64_t)p.nblk * kMomWaves, kMomWaves, true, lds, p, stream,
+                   g_mom_lds_granted[group ? 1 : 0][slot]);
+    if (e != hipSuccess) return e;
+    fn = group ? ByCap<MomGXK>::pick(p.cap_words) : ByCap<MomXK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMomWaves, kMomWaves, true, lds, p, stream,
-                  g_mom_lds_granted[group ? 1 : 0][cap_slot(p.cap_words)]);
+                  g_mom_lds_granted[group ? 3 : 2][slot]);
 }
 
 int launch_decode(const DecodeParams &p, void *stream, bool group) {
@@ -2254,10 +2321,17 @@ int launch_decode(const DecodeParams &p, void *stream, bool group) {
                   g_lds_granted[group ? 4 : 1][cap_slot(p.cap_words)]);
 }
 
+// The full-block kernel, then the general one (which ends at once when every
+// block is full).
 int launch_sgd(const SgdParams &p, void *stream, bool group) {
+    const int slot = cap_slot(p.cap_words);
     const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
+    int e = launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+                   g_lds_granted[group ? 5 : 2][slot]);
+    if (e != hipSuccess) return e;
+    fn = group ? ByCap<SgdGXK>::pick(p.cap_words) : ByCap<SgdXK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
-                  g_lds_granted[group ? 5 : 2][cap_slot(p.cap_words)]);
+                  g_lds_granted[group ? 7 : 6][slot]);
 }
 
 
