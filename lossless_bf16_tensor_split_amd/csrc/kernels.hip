@@ -138,6 +138,20 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     return v;
 }
 
+// The wave's minimum of v, in every lane: within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8 lanes, then across rows by the broadcasts of
+// lanes 15 and 31, which leaves it in lane 63 (a lane whose shift source
+// lies outside its row keeps its own value).
+__device__ __forceinline__ int32_t wave_min(int32_t v) {
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -1296,6 +1310,117 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ---- The update at the CLEAN capacity with three waves per SIMD.
+//
+// At 25 words a stream, W's and M's rows and the sign-fraction regions take
+// 17.6 KB a wave, which leaves room for two waves per SIMD.  The ring kernel
+// keeps W's rows whole in LDS (an update in place overwrites them in memory)
+// but passes M's, which the update only reads, through a ring of kRing rows:
+// slot r % kRing holds row r, and a slot past the last repeats slot 0 so that
+// a window's second word never wraps.  At the start of every half the ring
+// takes the rows loaded during the previous half, and rows are loaded for
+// the slots whose rows lie below the wave's slowest reader.  A window that
+// reaches a row not yet in the ring is read from memory instead (rows past
+// the last read as zero).  M's sign-fraction bytes take one region.  With the
+// tables shared by four waves this is 12 KiB a wave: three waves per SIMD.
+constexpr uint32_t kRing = 8;
+constexpr uint32_t kRingMask = (kRing * ROWB - 1) & ~(ROWB - 1);
+constexpr uint32_t kRingFill = 2;   // rows loaded per half, at most
+constexpr uint32_t kRingCap = 25;
+constexpr uint32_t kRingWaves = 4;
+
+struct RingLayout {
+    uint32_t ring, z0, w0, z1, sw, sm, end;
+    __host__ __device__ constexpr RingLayout(uint32_t cap, uint32_t base)
+        : ring(base),
+          z0(base + (kRing + 1) * ROWB),
+          w0(z0 + ROWB),
+          z1(w0 + cap * ROWB),
+          sw(z1 + ROWB),
+          sm(sw + kSlabB),
+          end(sm + kRegB) {}
+};
+// a wave's bytes, a whole number of rings so that every ring is aligned to
+// its size (its slots are found by masking)
+constexpr uint32_t kRingWaveB = (RingLayout(kRingCap, 0).end + kRing * ROWB - 1) / (kRing * ROWB) * (kRing * ROWB);
+// the tables, at the update's offsets from here
+constexpr uint32_t kRingTab = kRingWaves * kRingWaveB;
+constexpr uint32_t kRingLds = kRingTab + kSgdWave0;
+static_assert(kRingLds * 3 <= 160 * 1024, "three four-wave workgroups per CU");
+
+struct RingReader {
+    int32_t q;          // stream bit position of the next code, minus 2
+    uint32_t tcol;      // the ring's address | this lane's byte in a row
+    int32_t hi;         // rows below hi have come in (those at or above the slowest reader's are held)
+    int32_t qlim;       // every lane's window is held while q < qlim
+    int32_t ncome;      // rows hi .. hi + ncome - 1 are on their way, in rr
+    int32_t cap;
+    uint32_t rr[kRingFill];
+    __amdgpu_buffer_rsrc_t src;   // the unit's rows in memory
+
+    // The ring holds rows 0 .. kRing-2, row -1 (zero) in slot kRing-1 and
+    // row 0 again in slot kRing.
+    __device__ __forceinline__ void init(uint32_t ring, uint32_t lane_, const uint32_t *rows, uint32_t cap_) {
+        q = -2;
+        tcol = ring | (4 * lane_);
+        hi = kRing - 1;
+        qlim = 32 * (hi - 1);
+        ncome = 0;
+        cap = (int32_t)cap_;
+        src = wave_rsrc(rows, (cap_ - 1) * 4 * NS + 4 * US);
+#pragma unroll
+        for (uint32_t k = 0; k < kRingFill; ++k) rr[k] = 0;
+    }
+    // this lane's word of row r >= 0 from memory (zero past the last row)
+    __device__ __forceinline__ uint32_t word(int32_t r) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(src, (uint32_t)r * (4 * NS) + (tcol & (ROWB - 1)), 0, 0);
+    }
+    __device__ __forceinline__ uint32_t window() const {
+        const uint32_t off = (((uint32_t)q << 3) & kRingMask) | tcol;
+        uint32_t a, b;
+        if (__builtin_expect(wave_all(q < qlim), 1)) {
+            a = ld32(off);
+            b = ld32(off + ROWB);
+        } else {
+            const int32_t r = q >> 5;
+            a = r < hi ? ld32(off) : word(r);
+            b = r + 1 < hi ? ld32(off + ROWB) : word(r + 1);
+            // wait for the two loads here (vmcnt(0), other counters left
+            // alone), so that the paths join with no load of theirs
+            // outstanding; otherwise every window after the join would wait
+            // for all of the wave's memory operations
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        return __builtin_amdgcn_alignbit(b, a, (uint32_t)q);
+    }
+    __device__ __forceinline__ uint32_t next(uint32_t tab) {
+        const uint32_t win = window();
+        const uint32_t en = ld32(tab + (win & 0x3FCu));
+        q += (en >> 8) & 0xFFu;
+        return (win << (en & 31u)) | en;
+    }
+    // The rows that came in go to their slots; then rows are loaded for the
+    // slots whose rows every reader has left (row r's slot held row r - kRing).
+    __device__ __forceinline__ void refill() {
+#pragma unroll
+        for (uint32_t k = 0; k < kRingFill; ++k) {
+            if ((int32_t)k < ncome) {
+                const uint32_t slot = (uint32_t)(hi + (int32_t)k) & (kRing - 1);
+                st32(tcol + slot * ROWB, rr[k]);
+                if (slot == 0) st32(tcol + kRing * ROWB, rr[k]);
+            }
+        }
+        hi += ncome;
+        int32_t lo = wave_min(q >> 5);
+        const int32_t n = max(0, min(min((int32_t)kRingFill, lo + (int32_t)kRing - hi), cap + 1 - hi));
+#pragma unroll
+        for (uint32_t k = 0; k < kRingFill; ++k)
+            if ((int32_t)k < n) rr[k] = word(hi + (int32_t)k);
+        ncome = n;
+        qlim = 32 * (hi - 1);
+    }
+};
+
 // General path: partial blocks and inputs with spilled fields; byte-wide
 // accesses with per-element checks.
 template <uint32_t CAPT>
@@ -1370,16 +1495,22 @@ struct HalfRegs {
     u32x4 w, m;
 };
 
-template <uint32_t CAPT>
-__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLayout &lay, PayWriter &st,
-                                                uint64_t r0) {
+// RING: M's rows come through a ring (the ring kernel's layout, Lay =
+// RingLayout, its tables from kRingTab); M's sign-fraction bytes then take
+// one region, refilled at the end of each half.  mrows: this unit's row 0 of
+// M's payload (ring only).
+template <uint32_t CAPT, bool RING, class Lay>
+__device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const Lay &lay, PayWriter &st,
+                                                uint64_t r0, const uint32_t *mrows) {
+    constexpr uint32_t TB = RING ? kRingTab : 0u;
+    constexpr uint32_t tabE = TB + kSgdETab, tabW = TB + kSgdWTab, tabM = TB + kSgdMTab;
     const uint32_t l = lane();
     const uint32_t npos = p.block_elems / NS;
     const uint32_t nh = npos / CH;                // halves (the block size is a multiple of 4096)
     const uint32_t cap = cap_of<CAPT>(p.cap_words);
     const uint32_t capbits = 32 * cap;
     const int32_t qwmax = Reader::bias(lay.w0) + (int32_t)capbits - 2;
-    const int32_t qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    int32_t qmmax;
     const uint32_t mine = 16 * l;                 // this lane's 16 bytes of a region
     const uint32_t lw = l & ~3u;                  // its sign-fraction byte's word in a region row
     const uint32_t jsel = (l & 3u) * 0x01010000u | 0x0C0Cu;
@@ -1396,21 +1527,31 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     const uint32_t g = (l >> 2) * NS + 16 * (l & 3);
     uint64_t *stage_ctr = reinterpret_cast<uint64_t *>(p.scratch + kScrStage);
     uint8_t *stage = p.scratch + scr_stage_offset(p.nblk);
-    Reader rw, rm;
+    Reader rw;
+    std::conditional_t<RING, RingReader, Reader> rm;
     rw.init(lay.w0, l);
-    rm.init(lay.m0, l);
+    if constexpr (RING) {
+        rm.init(lay.ring, l, mrows, cap);
+        qmmax = (int32_t)capbits - 2;
+    } else {
+        rm.init(lay.m0, l);
+        qmmax = Reader::bias(lay.m0) + (int32_t)capbits - 2;
+    }
 
-    auto load = [&](HalfRegs &r, uint32_t h) {
+    auto load_w = [&](HalfRegs &r, uint32_t h) {
         const uint32_t o = h < nh ? h * kHalfB + g : kNone;
         r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rws, o, 0, 0));
+    };
+    auto load_m = [&](HalfRegs &r, uint32_t h) {
+        const uint32_t o = h < nh ? h * kHalfB + g : kNone;
         r.m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rms, o, 0, 0));
     };
     auto region = [&](uint32_t h) { return (h & 1u) * kRegB; };
-    // a half's inputs into the region of half h
-    auto to_lds = [&](const HalfRegs &r, uint32_t h) {
-        st128(lay.sw + region(h) + mine, r.w);
-        st128(lay.sm + region(h) + mine, r.m);
-    };
+    // M's region of half h (one region in turn with the ring)
+    auto region_m = [&](uint32_t h) { return RING ? 0u : region(h); };
+    // a half's inputs into the regions of half h
+    auto to_lds_w = [&](const HalfRegs &r, uint32_t h) { st128(lay.sw + region(h) + mine, r.w); };
+    auto to_lds_m = [&](const HalfRegs &r, uint32_t h) { st128(lay.sm + region_m(h) + mine, r.m); };
 
     // Carried from stage to stage: the inputs of the group whose arithmetic
     // comes next (sign-fraction words and decoded fields), the codes (and
@@ -1451,6 +1592,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         constexpr bool DEC = decltype(DEC_)::value;
         constexpr uint32_t GS = decltype(GS_)::value;
         const uint32_t rc = region(h) + GS * 4 * US;                       // group s's rows
+        const uint32_t rcm = region_m(h) + GS * 4 * US;
         const uint32_t rp = (GS ? region(h) : region(h + 1)) + ((GS + 3) % 4) * 4 * US;   // group s-1's rows
         uint32_t wsC[4], msC[4], ewC[4], emC[4];
         uint32_t winw = 0, winm = 0, cw = 0, cm = 0;
@@ -1461,7 +1603,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
                 wsC[k] = ld32(lay.sw + rc + k * US + lw);
-                msC[k] = ld32(lay.sm + rc + k * US + lw);
+                msC[k] = ld32(lay.sm + rcm + k * US + lw);
             }
         }
         // the writer's group, with checks when some stream is near its end
@@ -1475,9 +1617,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
             uint32_t enw = 0, enm = 0, wkw = 0, wkm = 0;
             if (DEC) {
                 wkw = winw >> cw;
-                enw = ld32(kSgdWTab + (wkw & 0x3FCu));
+                enw = ld32(tabW + (wkw & 0x3FCu));
                 wkm = winm >> cm;
-                enm = ld32(kSgdMTab + (wkm & 0x3FCu));
+                enm = ld32(tabM + (wkm & 0x3FCu));
             }
             r[k] = __builtin_fmaf(p.mul, __uint_as_float(join32s(msP[k], emP[k], jsel)),
                                   __uint_as_float(join32s(wsP[k], ewP[k], jsel)));
@@ -1517,9 +1659,9 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
                 rm.q = qm0;
 #pragma unroll
                 for (uint32_t k = 0; k < 4; ++k) {
-                    ewC[k] = rw.next(kSgdWTab);
+                    ewC[k] = rw.next(tabW);
                     rw.q = min(rw.q, qwmax);
-                    emC[k] = rm.next(kSgdMTab);
+                    emC[k] = rm.next(tabM);
                     rm.q = min(rm.q, qmmax);
                 }
             }
@@ -1543,7 +1685,7 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         // the writer codes group s-1 next stage
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k) {
-            wc[k] = ld64(kSgdETab + ep[k]);
+            wc[k] = ld64(tabE + ep[k]);
             ew8[k] = ep[k];
         }
         jw = 4 * (4 * h + GS) - 4;
@@ -1561,8 +1703,11 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
     // of half h-1 has been split: that half's bytes are read out, its region
     // takes half h+1 (loaded two halves earlier into `next`), and the loads
     // of half h+3 go out into the same registers.  Half h-1's bytes leave in
-    // the third stage.
+    // the third stage.  With the ring, M's one region takes half h+1 after
+    // the half's last stage (which read the last of half h), and the ring
+    // takes the rows that came in during the previous half first.
     auto half = [&](uint32_t h, HalfRegs &next) {
+        if constexpr (RING) rm.refill();
         wall = __all(st.live && st.total() + CH * 16 <= capbits);
         stage_fn(std::true_type{}, std::integral_constant<uint32_t, 0>{}, h);
         if (h == 0) {
@@ -1576,18 +1721,30 @@ __device__ __forceinline__ void sgd_stream_full(const SgdParams &p, const SgdLay
         } else {
             outv = ld128(lay.sw + region(h - 1) + mine);
         }
-        to_lds(next, h + 1);
-        load(next, h + 3);
+        to_lds_w(next, h + 1);
+        load_w(next, h + 3);
+        if (!RING) {
+            to_lds_m(next, h + 1);
+            load_m(next, h + 3);
+        }
         stage_fn(std::true_type{}, std::integral_constant<uint32_t, 1>{}, h);
         if (h != 0) __builtin_amdgcn_raw_buffer_store_b128(outv, ros, (h - 1) * kHalfB + g, 0, 0);
         stage_fn(std::true_type{}, std::integral_constant<uint32_t, 2>{}, h);
         stage_fn(std::true_type{}, std::integral_constant<uint32_t, 3>{}, h);
+        if (RING) {
+            to_lds_m(next, h + 1);
+            load_m(next, h + 3);
+        }
     };
     HalfRegs a, b;
-    load(a, 0);
-    load(b, 1);
-    to_lds(a, 0);
-    load(a, 2);
+    load_w(a, 0);
+    load_m(a, 0);
+    load_w(b, 1);
+    load_m(b, 1);
+    to_lds_w(a, 0);
+    to_lds_m(a, 0);
+    load_w(a, 2);
+    load_m(a, 2);
     for (uint32_t h = 0; h < nh; h += 2) {
         half(h, b);
         if (h + 1 < nh) half(h + 1, a);
@@ -1712,7 +1869,7 @@ void k_sgd(const SgdParams p) {
         st.init(0, l, n_s);
         st.rows.init(p.o_pay, b, h, cap);
         if (!GEN) {
-            sgd_stream_full<CAPT>(p, lay, st, r0 + h * US);
+            sgd_stream_full<CAPT, false>(p, lay, st, r0 + h * US, nullptr);
             ++nfull;
             const UnitOut o{p.o_pay, p.o_cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0, 0};
             unit_finish(st, n_s, u, b, h, 0, o);
@@ -1738,6 +1895,107 @@ void k_sgd(const SgdParams p) {
         for_general<GROUP>(p, nunits / kSgdWaves, [](uint32_t i) { return i / 2; },
                            [&](uint32_t i) { unit(kSgdWaves * i + wave_id()); });
     }
+}
+
+// W's rows (cap) and M's first kRing-1 rows into the ring kernel's LDS with
+// one wait: row 0 goes to the ring's last slot too, and the slot before it
+// (row -1) is cleared.
+__device__ __forceinline__ void rows_ring_to_lds(const uint32_t *wpay, const uint32_t *mpay, const RingLayout &lay,
+                                                 uint32_t b, uint32_t h) {
+    constexpr uint32_t np = kRingCap * 16, nr = (kRing - 1) * 16;
+    constexpr uint32_t kw = (np + 63) / 64, km = (nr + 63) / 64;
+    const uint64_t u0 = (uint64_t)b * kRingCap * NS + h * US;
+    const uint32_t span = (kRingCap - 1) * 4 * NS + 4 * US;
+    const __amdgpu_buffer_rsrc_t rw = wave_rsrc(wpay + u0, span);
+    const __amdgpu_buffer_rsrc_t rm = wave_rsrc(mpay + u0, span);
+    u32x4 v[kw], m[km];
+#pragma unroll
+    for (uint32_t k = 0; k < kw; ++k) {
+        const uint32_t p = k * 64 + lane();
+        const uint32_t off = p < np ? (p / 16) * (4 * NS) + (p % 16) * 16 : 0x80000000u;
+        v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < km; ++k) {
+        const uint32_t p = k * 64 + lane();
+        const uint32_t off = p < nr ? (p / 16) * (4 * NS) + (p % 16) * 16 : 0x80000000u;
+        m[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0));
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kw; ++k) {
+        const uint32_t p = k * 64 + lane();
+        if (p < np) st128(lay.w0 + 16 * p, v[k]);
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < km; ++k) {
+        const uint32_t p = k * 64 + lane();
+        if (p < nr) st128(lay.ring + 16 * p, m[k]);
+        if (p < 16) st128(lay.ring + kRing * ROWB + 16 * p, m[k]);
+    }
+    st32(lay.ring + (kRing - 1) * ROWB + 4 * lane(), 0);
+}
+
+// The full-block update at the CLEAN capacity: four waves, one block's
+// units, per workgroup (they share the tables and meet at every block),
+// three waves per SIMD.  Blocks that are not full are left to the general
+// kernel.
+template <bool GROUP>
+__global__ __launch_bounds__(64 * kRingWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void k_sgd_ring(const SgdParams p) {
+    constexpr uint32_t cap = kRingCap;
+    if (!GROUP) {
+        stage_dec(p.wdec, kRingTab + kSgdWTab);
+        stage_dec(p.mdec, kRingTab + kSgdMTab);
+        stage_enc(p.wenc, kRingTab + kSgdETab);
+    }
+    if (threadIdx.x < 2) st32(kRingTab + kSgdNone + 4 * threadIdx.x, 0);
+    __syncthreads();
+    uint64_t staged = ~0ull;
+    const uint32_t l = lane(), h = wave_id();
+    const RingLayout lay(cap, h * kRingWaveB);
+    st32(lay.z0 + 4 * l, 0);
+    st32(lay.z1 + 4 * l, 0);
+    static_assert(kRingWaves == kMaxUnits, "a workgroup is one block's units");
+    uint32_t nfull = 0;
+    for (uint32_t b = blockIdx.x; b < p.nblk; b += gridDim.x) {
+        __builtin_amdgcn_s_barrier();
+        uint32_t k = 0;
+        if (GROUP) {
+            k = p.gw.blk_tensor[b];
+            const uint32_t tw = p.gw.blk_tab[b], tm = p.gm.blk_tab[b];
+            const uint64_t key = ((uint64_t)tm << 32) | tw;
+            if (key != staged) {
+                stage_dec(p.gw.dec[tw], kRingTab + kSgdWTab);
+                stage_dec(p.gm.dec[tm], kRingTab + kSgdMTab);
+                stage_enc(p.gw.enc[tw], kRingTab + kSgdETab);
+                __syncthreads();
+                staged = key;
+            }
+        }
+        const uint64_t wob = p.w_obase[b], wob1 = p.w_obase[b + 1];
+        const uint64_t mob = p.m_obase[b], mob1 = p.m_obase[b + 1];
+        rows_ring_to_lds(p.w_pay, p.m_pay, lay, b, h);
+        uint64_t r0;
+        uint32_t nb;
+        if (GROUP) {
+            const BlockSpan sp = group_span(p.gw, k, p.block_elems, b);
+            r0 = sp.sf0;
+            nb = sp.nb;
+        } else {
+            r0 = (uint64_t)b * p.block_elems;
+            nb = (uint32_t)min<uint64_t>(p.block_elems, p.n - r0);
+        }
+        if (!block_full(p, b, nb, wob, wob1, mob, mob1)) continue;
+        const uint32_t n_s = stream_len(nb, h * US + l);
+        PayWriter st;
+        st.init(0, l, n_s);
+        st.rows.init(p.o_pay, b, h, cap);
+        sgd_stream_full<cap, true>(p, lay, st, r0 + h * US, p.m_pay + ((uint64_t)b * cap * NS + h * US));
+        ++nfull;
+        const UnitOut o{p.o_pay, p.o_cnt, p.scratch, p.nblk, p.ovf_cap, cap, 0, 0};
+        unit_finish(st, n_s, b * kMaxUnits + h, b, h, 0, o);
+    }
+    if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
 }
 
 // ------------------------------------------------------------------ fused momentum step
@@ -2321,14 +2579,25 @@ int launch_decode(const DecodeParams &p, void *stream, bool group) {
                   g_lds_granted[group ? 4 : 1][cap_slot(p.cap_words)]);
 }
 
-// The full-block kernel, then the general one (which ends at once when every
-// block is full).
+std::atomic<size_t> g_ring_granted[2];
+
+// The full-block kernel (the ring kernel at the CLEAN capacity), then the
+// general one (which ends at once when every block is full).
 int launch_sgd(const SgdParams &p, void *stream, bool group) {
     const int slot = cap_slot(p.cap_words);
-    const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
-    int e = launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+    int e;
+    if (p.cap_words == kRingCap) {
+        const void *fn = group ? reinterpret_cast<const void *>(&k_sgd_ring<true>)
+                               : reinterpret_cast<const void *>(&k_sgd_ring<false>);
+        e = launch(fn, (uint64_t)p.nblk * kRingWaves, kRingWaves, true, kRingLds, p, stream,
+                   g_ring_granted[group ? 1 : 0]);
+    } else {
+        const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
+        e = launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
                    g_lds_granted[group ? 5 : 2][slot]);
+    }
     if (e != hipSuccess) return e;
+    const void *fn;
     fn = group ? ByCap<SgdGXK>::pick(p.cap_words) : ByCap<SgdXK>::pick(p.cap_words);
     return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
                   g_lds_granted[group ? 7 : 6][slot]);

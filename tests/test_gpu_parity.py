@@ -291,6 +291,47 @@ def test_full_block_path_in_every_mode(L, orc, B, cw, inplace):
     assert om.full_path_units() == 4 * nblk and ow.full_path_units() == 4 * nblk
 
 
+@pytest.mark.parametrize("inplace", [False, True])
+def test_sgd_readers_far_apart(L, orc, inplace):
+    """Full CLEAN blocks where some of M's streams open (or, in other blocks,
+    go on at mid-stream) with a run of escaped fields while their neighbours
+    keep two-bit codes: a wave's readers of M end up hundreds of bits apart,
+    farther than the rows the update holds of M at once, so the far readers'
+    windows come from memory.  No input field spills, so every unit takes the
+    full-block path; W' equals the oracle's round trip."""
+    g = np.random.default_rng(4242)
+    B, cw, nblk = 65536, 25, 4
+    n = nblk * B
+    w = narrow_values(orc, g, 0.02, n)
+    m = narrow_values(orc, g, 1e-3, n, extra=0.0)
+    tiny = synth.to_bf16_bits(np.array([1e-30, -3e-33, 2e-35, -1e-36]))
+    runs = [(0, 0), (1, 100), (2, 230), (3, 40)]      # (block, first position of the runs)
+    for blk, j0 in runs:
+        for s in range(0, 256, 4):                     # every fourth stream of every unit
+            for t in range(20):
+                m[blk * B + (j0 + t) * 256 + s] = tiny[(s + t) % 4]
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-3)
+    ocw = orc.codebook_build(0, 0.02, 0.0, w)
+    ocm = orc.codebook_build(0, 1e-3, 0.0, m)
+    assert orc.encode(ocw, w, B, cw).spilled == 0
+    assert orc.encode(ocm, m, B, cw).spilled == 0
+    # the readers' spread, from the code lengths: at some position of every
+    # block two streams of one unit are more than eight rows apart
+    esc = int(ocm.esc_len) + 8
+    lens = np.where(ocm.len[(m >> 7) & 0xFF] == 0, esc, ocm.len[(m >> 7) & 0xFF]).astype(np.int64)
+    bits = np.cumsum(lens.reshape(nblk, 256, 256), axis=1)        # [block, position, stream]
+    spread = (bits.reshape(nblk, 256, 4, 64).max(axis=3) - bits.reshape(nblk, 256, 4, 64).min(axis=3)).max(axis=(1, 2))
+    assert (spread > 8 * 32).all(), spread
+    sgd_case(L, orc, w, m, mw, mm, 1e-3, B, cw, inplace, what="far readers inplace=%s" % inplace)
+    cbw = L.lct_codebook_build(L.Model(0, 0.02, 0.0), dev(w))
+    cbm = L.lct_codebook_build(L.Model(0, 1e-3, 0.0), dev(m))
+    lay = L.layout(B, cw)
+    tw, tm = L.encode(cbw, dev(w), lay), L.encode(cbm, dev(m), lay)
+    out = L.alloc_tensor(n, lay)
+    L.lct_sgd_step(cbw, tw, cbm, tm, 1e-3, out)
+    assert out.full_path_units() == 4 * nblk
+
+
 def test_sgd_eta_zero_identity(L, orc):
     g = np.random.default_rng(3)
     n = 5 * 65536 + 7
