@@ -19,9 +19,12 @@
 // share the code tables in LDS and nothing else, so no wave ever waits for
 // another.  Encode and decode run one unit per wave (a workgroup is a block's
 // four units); the fused update's waves are persistent and take units
-// round-robin, so its three tables are staged once per workgroup; the
-// momentum kernel's persistent workgroups are a block's four units at a time
-// and share its four tables.  The block's stream words are interleaved (word w of stream s at
+// round-robin, so its three tables are staged once per workgroup (at the
+// CLEAN capacity a block's four units at a time, M's rows through an LDS
+// ring); the momentum kernel's persistent workgroups are a block's four units
+// at a time and share its four tables.  The updates' blocks that are partial
+// or have spilled input fields go to general kernels of their own.  The
+// block's stream words are interleaved (word w of stream s at
 // w*256 + s): a unit's payload rows move between HBM and LDS with 16-byte
 // accesses and every lane works on its own column of the wave's LDS rows
 // (a row's lanes hit distinct banks).  Kernels are specialised on the stream
@@ -34,7 +37,9 @@
 // and a shift (bits 4..0) that moves an escape's literal from the window to
 // bits 30..23 (31 for ordinary codes, which shifts everything out of that
 // range).  Several codes are read from one window; there is no refill logic.
-// Row -1 of each input column is zero for the first codes.
+// Row -1 of each input column is zero for the first codes.  (The ring kernel
+// reads M through slots of a ring and refills it by halves; a window past
+// the rows in the ring is read from memory.)
 //
 // Bit writer: a 64-bit buffer; after every second code it is stored at the
 // current row, and it advances by a word when the first one is full.  The
@@ -1254,6 +1259,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(const DecodeParams p)
 // ------------------------------------------------------------------ fused SGD
 
 constexpr uint32_t kSgdWaves = 2;
+// The general update kernel: a block's four units per workgroup, so that a
+// partial block's units walk at once.
+constexpr uint32_t kSgdGenWaves = 4;
+template <bool GEN> constexpr uint32_t sgd_waves() { return GEN ? kSgdGenWaves : kSgdWaves; }
 // Sign-fraction regions of the full-block path: per wave and tensor, two
 // regions of one half (CH positions of its 64 streams) each; W's also take
 // the result's bytes, written in place.
@@ -1798,7 +1807,7 @@ __device__ __forceinline__ void for_general(const P &p, uint32_t count, Blk blk,
 // a lane, AGPRs included.  GEN: the general kernel (blocks that are not
 // full); otherwise the full-block kernel.
 template <uint32_t CAPT, bool GROUP, bool GEN>
-__global__ __launch_bounds__(64 * kSgdWaves) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * sgd_waves<GEN>()) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
     if (!GROUP) {
         stage_dec(p.wdec, kSgdWTab);
@@ -1818,12 +1827,13 @@ void k_sgd(const SgdParams p) {
     uint16_t *cnt_out = p.park_cnt ? reinterpret_cast<uint16_t *>(p.scratch + scr_cnt_offset(p.nblk))
                                    : p.o_cnt;
     // The two waves of a workgroup take units 2i and 2i+1 of one block, whose
-    // sign-fraction bytes share every 128-byte line.  Left free, the waves
-    // drift apart over many units and the second read of a line misses L2, so
-    // they meet at the start of each unit (an execution barrier only: they
-    // share no data).  Both take the same number of trips, the unit count
-    // being even.
-    static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0, "pairs of units per workgroup");
+    // sign-fraction bytes share every 128-byte line (the general kernel's four
+    // waves a block's four units).  Left free, the waves drift apart over many
+    // units and the second read of a line misses L2, so they meet at the
+    // start of each unit (an execution barrier only: they share no data).
+    // All take the same number of trips, the unit count being even.
+    static_assert(kSgdWaves == 2 && kMaxUnits % kSgdWaves == 0 && kSgdGenWaves == kMaxUnits,
+                  "pairs of units per workgroup; the general kernel's: a block's units");
     uint32_t nfull = 0;   // units done on the full-block path
     // One unit (the full-block kernel leaves the others to the general one).
     auto unit = [&](uint32_t u) {
@@ -1891,9 +1901,8 @@ void k_sgd(const SgdParams p) {
         for (uint32_t u = first_unit(kSgdWaves); u < nunits; u += stride) unit(u);
         if (l == 0 && nfull) atomicAdd(reinterpret_cast<uint32_t *>(p.scratch + kScrFullUnits), nfull);
     } else {
-        // pairs of units: pair i is units 2i and 2i+1, of block i / 2
-        for_general<GROUP>(p, nunits / kSgdWaves, [](uint32_t i) { return i / 2; },
-                           [&](uint32_t i) { unit(kSgdWaves * i + wave_id()); });
+        for_general<GROUP>(p, p.nblk, [](uint32_t i) { return i; },
+                           [&](uint32_t b) { unit(kMaxUnits * b + wave_id()); });
     }
 }
 
@@ -2480,10 +2489,13 @@ struct ByCap {
 template <uint32_t C> struct EncK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, false>); } };
 template <uint32_t C> struct DecK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, false>); } };
 template <uint32_t C> struct SgdK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, false>); } };
+// the CLEAN capacity's full-block update is the ring kernel
+template <> struct SgdK<kRingCap> { static const void *fn() { return nullptr; } };
 template <uint32_t C> struct SgdXK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, false, true>); } };
 template <uint32_t C> struct EncGK { static const void *fn() { return reinterpret_cast<const void *>(&k_encode<C, true>); } };
 template <uint32_t C> struct DecGK { static const void *fn() { return reinterpret_cast<const void *>(&k_decode<C, true>); } };
 template <uint32_t C> struct SgdGK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, false>); } };
+template <> struct SgdGK<kRingCap> { static const void *fn() { return nullptr; } };
 template <uint32_t C> struct SgdGXK { static const void *fn() { return reinterpret_cast<const void *>(&k_sgd<C, true, true>); } };
 
 // per kernel (encode, decode, update, the group encode, decode and update,
@@ -2522,7 +2534,7 @@ int launch(const void *fn, uint64_t nunits, uint32_t waves, bool persistent, siz
 
 size_t encode_lds(uint32_t cap) { return kEncWave0 + (size_t)kEncWaves * enc_wave_bytes(cap); }
 size_t decode_lds(uint32_t cap) { return kDecWave0 + (size_t)kDecWaves * dec_wave_bytes(cap); }
-size_t sgd_lds(uint32_t cap) { return kSgdWave0 + (size_t)kSgdWaves * sgd_wave_bytes(cap); }
+size_t sgd_lds(uint32_t cap, uint32_t waves) { return kSgdWave0 + (size_t)waves * sgd_wave_bytes(cap); }
 
 int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream) {
     const uint64_t words = (scr_clear_bytes(nblk) + 7) / 8;
@@ -2593,13 +2605,14 @@ int launch_sgd(const SgdParams &p, void *stream, bool group) {
                    g_ring_granted[group ? 1 : 0]);
     } else {
         const void *fn = group ? ByCap<SgdGK>::pick(p.cap_words) : ByCap<SgdK>::pick(p.cap_words);
-        e = launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+        e = launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words, kSgdWaves), p, stream,
                    g_lds_granted[group ? 5 : 2][slot]);
     }
     if (e != hipSuccess) return e;
     const void *fn;
     fn = group ? ByCap<SgdGXK>::pick(p.cap_words) : ByCap<SgdXK>::pick(p.cap_words);
-    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdWaves, true, sgd_lds(p.cap_words), p, stream,
+    return launch(fn, (uint64_t)p.nblk * kMaxUnits, kSgdGenWaves, true, sgd_lds(p.cap_words, kSgdGenWaves), p,
+                  stream,
                   g_lds_granted[group ? 7 : 6][slot]);
 }
 

@@ -332,6 +332,39 @@ def test_sgd_readers_far_apart(L, orc, inplace):
     assert out.full_path_units() == 4 * nblk
 
 
+@pytest.mark.parametrize("B,cw,n", [(65536, 25, 16), (65536, 25, 65536 + 4096), (65536, 25, 2 * 65536 + 256 * 7),
+                                    (65536, 25, 3 * 65536 + 4096 * 5 + 16 * 7), (65536, 25, 65536 + 65520),
+                                    (32768, 12, 32768 + 16 * 999), (32768, 11, 2 * 32768 + 48)])
+def test_partial_last_block(L, orc, B, cw, n):
+    """Tensors whose last block is partial (streams of equal or of two
+    lengths) and whose inputs spill nothing: the whole blocks take the
+    full-block path and the partial one the general kernel (the counters say
+    so); the update and the momentum step equal the oracle's, in place and
+    not."""
+    g = np.random.default_rng(n + cw)
+    nfull = n // B
+    w = narrow_values(orc, g, 0.02, n)
+    m = narrow_values(orc, g, 1e-3, n)
+    gr = synth.to_bf16_bits(g.normal(0, 1e-6, n))
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-3)
+    ocw, ocm = orc.codebook_build(0, 0.02, 0.0, w), orc.codebook_build(0, 1e-3, 0.0, m)
+    assert orc.encode(ocw, w, B, cw).spilled == 0 and orc.encode(ocm, m, B, cw).spilled == 0
+    for inplace in (False, True):
+        what = "partial n=%d B=%d cw=%d inplace=%s" % (n, B, cw, inplace)
+        sgd_case(L, orc, w, m, mw, mm, 1e-3, B, cw, inplace, what=what)
+        momentum_case(L, orc, w, m, gr, mw, mm, 0.9, 1e-3, B, cw, inplace, what=what)
+    cbw = L.lct_codebook_build(L.Model(0, 0.02, 0.0), dev(w))
+    cbm = L.lct_codebook_build(L.Model(0, 1e-3, 0.0), dev(m))
+    lay = L.layout(B, cw)
+    out = L.alloc_tensor(n, lay)
+    L.lct_sgd_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), 1e-3, out)
+    assert out.full_path_units() == 4 * nfull
+    ow, om = L.alloc_tensor(n, lay), L.alloc_tensor(n, lay)
+    L.lct_momentum_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), dev(gr), 0.9, 1e-3,
+                        ow, om)
+    assert ow.full_path_units() == 4 * nfull and om.full_path_units() == 4 * nfull
+
+
 def test_sgd_eta_zero_identity(L, orc):
     g = np.random.default_rng(3)
     n = 5 * 65536 + 7
