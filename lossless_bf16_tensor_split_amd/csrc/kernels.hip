@@ -1210,18 +1210,29 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t ro
                 }
                 return;
             }
+            // chunks where no stream of the wave has a spilled field take a
+            // copy of the loop with no memory read in it (a read under a
+            // per-element branch makes every later element wait for all of
+            // the wave's memory operations)
+            auto elems = [&](auto SP_) {
+                constexpr bool SP = decltype(SP_)::value;
 #pragma unroll
-            for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + i;
-                uint32_t e23 = rd.next(kDecTab);
-                rd.q = min(rd.q, qmax);
-                if (j >= c_s && j < n_s) {
-                    const uint64_t k = sp0 + (j - c_s);
-                    e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
+                for (uint32_t i = 0; i < CH; ++i) {
+                    const uint32_t j = j0 + i;
+                    uint32_t e23 = rd.next(kDecTab);
+                    rd.q = min(rd.q, qmax);
+                    if (SP && j >= c_s && j < n_s) {
+                        const uint64_t k = sp0 + (j - c_s);
+                        e23 = (k < p.ovf_cap ? (uint32_t)p.ovf[k] : 0u) << 23;
+                    }
+                    // the BF16 value is the top half of its fp32 form
+                    if (j < n_s) out(i) = (uint16_t)(join32(bf.v[i], e23) >> 16);
                 }
-                // the BF16 value is the top half of its fp32 form
-                if (j < n_s) out(i) = (uint16_t)(join32(bf.v[i], e23) >> 16);
-            }
+            };
+            if (wave_all(j0 + CH <= c_s || j0 >= n_s))
+                elems(std::false_type{});
+            else
+                elems(std::true_type{});
         });
 }
 
@@ -1459,25 +1470,37 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
         [&](Buf2 &bf, uint32_t j0) {
             uint32_t e[CH];
             uint8_t *o = osf + (size_t)j0 * NS;
+            // SP: some stream of the wave has a spilled input field in this
+            // chunk.  The other chunks (nearly all) take a copy of the loop
+            // with no memory read in it: a read under a per-element branch
+            // makes every element after it wait for all of the wave's memory
+            // operations, the prefetched chunk and the stores included.
+            auto elems = [&](auto SP_) {
+                constexpr bool SP = decltype(SP_)::value;
 #pragma unroll
-            for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + i;
-                uint32_t ew = rw.next(kSgdWTab);
-                rw.q = min(rw.q, qwmax);
-                if (j >= cw_s && j < n_s) {
-                    const uint64_t k = wsp + (j - cw_s);
-                    ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                for (uint32_t i = 0; i < CH; ++i) {
+                    const uint32_t j = j0 + i;
+                    uint32_t ew = rw.next(kSgdWTab);
+                    rw.q = min(rw.q, qwmax);
+                    if (SP && j >= cw_s && j < n_s) {
+                        const uint64_t k = wsp + (j - cw_s);
+                        ew = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                    }
+                    uint32_t em = rm.next(kSgdMTab);
+                    rm.q = min(rm.q, qmmax);
+                    if (SP && j >= cm_s && j < n_s) {
+                        const uint64_t k = msp + (j - cm_s);
+                        em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                    }
+                    const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.mul);
+                    if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
+                    e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
                 }
-                uint32_t em = rm.next(kSgdMTab);
-                rm.q = min(rm.q, qmmax);
-                if (j >= cm_s && j < n_s) {
-                    const uint64_t k = msp + (j - cm_s);
-                    em = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                }
-                const uint32_t R = sgd_round(join32(bf.w[i], ew), join32(bf.m[i], em), p.mul);
-                if (j < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
-                e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
-            }
+            };
+            if (wave_all((j0 + CH <= cw_s || j0 >= n_s) && (j0 + CH <= cm_s || j0 >= n_s)))
+                elems(std::false_type{});
+            else
+                elems(std::true_type{});
             writer_chunk<true, false>(st, e, j0, n_s, capbits, kSgdETab);
             writer_spill<true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
@@ -2075,30 +2098,39 @@ __device__ __forceinline__ void mom_stream_general(const MomParams &p, const Sgd
             uint32_t ew[CH], em[CH];
             uint8_t *ow = owsf + (size_t)j0 * NS;
             uint8_t *om = omsf + (size_t)j0 * NS;
+            // as in the update: chunks with no spilled input field take a
+            // copy of the loop with no memory read in it
+            auto elems = [&](auto SP_) {
+                constexpr bool SP = decltype(SP_)::value;
 #pragma unroll
-            for (uint32_t i = 0; i < CH; ++i) {
-                const uint32_t j = j0 + i;
-                uint32_t fw = rw.next(kMWD);
-                rw.q = min(rw.q, qwmax);
-                if (j >= cw_s && j < n_s) {
-                    const uint64_t k = wsp + (j - cw_s);
-                    fw = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                for (uint32_t i = 0; i < CH; ++i) {
+                    const uint32_t j = j0 + i;
+                    uint32_t fw = rw.next(kMWD);
+                    rw.q = min(rw.q, qwmax);
+                    if (SP && j >= cw_s && j < n_s) {
+                        const uint64_t k = wsp + (j - cw_s);
+                        fw = (k < p.w_ovf_cap ? (uint32_t)p.w_ovf[k] : 0u) << 23;
+                    }
+                    uint32_t fm = rm.next(kMMD);
+                    rm.q = min(rm.q, qmmax);
+                    if (SP && j >= cm_s && j < n_s) {
+                        const uint64_t k = msp + (j - cm_s);
+                        fm = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
+                    }
+                    const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], fm), p.mu);
+                    const uint32_t Rw = sgd_round(join32(bf.w[i], fw), Rm & 0xFFFF0000u, p.neg_eta);
+                    if (j < n_s) {
+                        ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
+                        om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
+                    }
+                    ew[i] = (Rw >> 20) & 0x7F8u;
+                    em[i] = (Rm >> 20) & 0x7F8u;
                 }
-                uint32_t fm = rm.next(kMMD);
-                rm.q = min(rm.q, qmmax);
-                if (j >= cm_s && j < n_s) {
-                    const uint64_t k = msp + (j - cm_s);
-                    fm = (k < p.m_ovf_cap ? (uint32_t)p.m_ovf[k] : 0u) << 23;
-                }
-                const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], fm), p.mu);
-                const uint32_t Rw = sgd_round(join32(bf.w[i], fw), Rm & 0xFFFF0000u, p.neg_eta);
-                if (j < n_s) {
-                    ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
-                    om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
-                }
-                ew[i] = (Rw >> 20) & 0x7F8u;
-                em[i] = (Rm >> 20) & 0x7F8u;
-            }
+            };
+            if (wave_all((j0 + CH <= cw_s || j0 >= n_s) && (j0 + CH <= cm_s || j0 >= n_s)))
+                elems(std::false_type{});
+            else
+                elems(std::true_type{});
             writer_chunk<true, false>(stw, ew, j0, n_s, capbits, kMWE);
             writer_spill<true>(stw, ew, j0, n_s, wctr, wstage, p.ow_ovf_cap);
             writer_chunk<true, false>(stm, em, j0, n_s, capbits, kMME);
