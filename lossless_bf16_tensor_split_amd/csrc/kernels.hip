@@ -1826,9 +1826,11 @@ __device__ __forceinline__ void for_general(const P &p, uint32_t count, Blk blk,
     }
 }
 
-// Two waves per SIMD (eight per CU, what LDS allows): at most 256 registers
-// a lane, AGPRs included.  GEN: the general kernel (blocks that are not
-// full); otherwise the full-block kernel.
+// At least two waves per SIMD (at most 256 registers a lane, AGPRs
+// included); the full-block kernel of the MEDIUM and HIGH capacities needs
+// about 150, so LDS lets three share a SIMD.  GEN: the general kernel
+// (blocks that are not full); otherwise the full-block kernel (the CLEAN
+// capacity's is the ring kernel).
 template <uint32_t CAPT, bool GROUP, bool GEN>
 __global__ __launch_bounds__(64 * sgd_waves<GEN>()) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sgd(const SgdParams p) {
