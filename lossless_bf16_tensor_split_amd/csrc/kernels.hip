@@ -1229,7 +1229,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams &p, uint32_t ro
                     if (j < n_s) out(i) = (uint16_t)(join32(bf.v[i], e23) >> 16);
                 }
             };
-            if (wave_all(j0 + CH <= c_s || j0 >= n_s))
+            if (wave_all(j0 + CH <= c_s || c_s >= n_s))
                 elems(std::false_type{});
             else
                 elems(std::true_type{});
@@ -1497,7 +1497,7 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
                     e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
                 }
             };
-            if (wave_all((j0 + CH <= cw_s || j0 >= n_s) && (j0 + CH <= cm_s || j0 >= n_s)))
+            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s)))
                 elems(std::false_type{});
             else
                 elems(std::true_type{});
@@ -2129,7 +2129,7 @@ __device__ __forceinline__ void mom_stream_general(const MomParams &p, const Sgd
                     em[i] = (Rm >> 20) & 0x7F8u;
                 }
             };
-            if (wave_all((j0 + CH <= cw_s || j0 >= n_s) && (j0 + CH <= cm_s || j0 >= n_s)))
+            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s)))
                 elems(std::false_type{});
             else
                 elems(std::true_type{});
