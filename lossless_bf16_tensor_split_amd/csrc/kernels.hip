@@ -98,21 +98,20 @@ __device__ __forceinline__ uint64_t fixed_stride(uint64_t nblk, uint32_t block_e
     return nblk * block_elems <= ovf_cap ? (uint64_t)(block_elems / kStreams) * kUnitStreams : 0;
 }
 
-extern __shared__ uint32_t lds[];
+// The dynamic LDS region (named only to declare it: the kernels address it
+// by byte offset, below).
+extern __shared__ uint32_t lds[] __attribute__((unused));
 
 // LDS accessed by byte offset.  These kernels declare no static LDS, so the
 // dynamic region starts at LDS address 0 and an offset is an address: the
 // accesses take it (plus a constant folded into the instruction) directly.
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x2 lds_u64;
 typedef __attribute__((address_space(3))) u32x4 lds_u128;
 __device__ __forceinline__ uint32_t ld32(uint32_t off) { return *reinterpret_cast<lds_u32 *>(off); }
-__device__ __forceinline__ uint32_t ld8(uint32_t off) { return *reinterpret_cast<lds_u8 *>(off); }
-__device__ __forceinline__ uint32_t ld16(uint32_t off) { return *reinterpret_cast<lds_u16 *>(off); }
 __device__ __forceinline__ u32x2 ld64(uint32_t off) { return *reinterpret_cast<lds_u64 *>(off); }
 __device__ __forceinline__ u32x4 ld128(uint32_t off) { return *reinterpret_cast<lds_u128 *>(off); }
 __device__ __forceinline__ void st128(uint32_t off, u32x4 v) { *reinterpret_cast<lds_u128 *>(off) = v; }
