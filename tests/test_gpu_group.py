@@ -138,6 +138,47 @@ def test_group_sgd(L, orc, B, cw, inplace):
 
 
 @pytest.mark.parametrize("inplace", [False, True])
+def test_group_sgd_readers_far_apart(L, orc, inplace):
+    """The group update at the CLEAN capacity with M tensors whose streams
+    drift hundreds of bits apart (every fourth stream of a unit opens, or goes
+    on at mid-stream, with 20 escaped fields while its neighbours keep
+    two-bit codes), so that the far readers' windows come from memory rather
+    than the rows held of M; a second pair of tensors is ordinary.  W' equals
+    the oracle's, in place and not."""
+    from test_gpu_parity import narrow_values
+    B, cw = 65536, 25
+    ns = [3 * 65536, 2 * 65536]
+    g = np.random.default_rng(9650)
+    ws = [narrow_values(orc, g, 0.02, n) for n in ns]
+    ms = [narrow_values(orc, g, 1e-3, ns[0], extra=0.0), synth.to_bf16_bits(g.normal(0, 1e-3, ns[1]))]
+    tiny = synth.to_bf16_bits(np.array([1e-30, -3e-33, 2e-35, -1e-36]))
+    for blk, j0 in [(0, 0), (1, 100), (2, 230)]:
+        for s_ in range(0, 256, 4):
+            for t in range(20):
+                ms[0][blk * B + (j0 + t) * 256 + s_] = tiny[(s_ + t) % 4]
+    ocw = [orc.codebook_build(0, 0.02, 0.0, w) for w in ws]
+    ocm = [orc.codebook_build(0, 1e-3, 0.0, m) for m in ms]
+    rw = [orc.encode(c, w, B, cw) for c, w in zip(ocw, ws)]
+    rm = [orc.encode(c, m, B, cw) for c, m in zip(ocm, ms)]
+    assert rm[0].spilled == 0 and rw[0].spilled == 0
+    lib_cb = lambda c: L.lct_codebook_from_lengths(list(c.len_base), c.esc_len, c.shift)
+    lay = L.layout(B, cw)
+    gw = L.LctGroup(ns, lay, [lib_cb(c) for c in ocw], [dev(w).view(torch.bfloat16) for w in ws])
+    gm = L.LctGroup(ns, lay, [lib_cb(c) for c in ocm], [dev(m).view(torch.bfloat16) for m in ms])
+    cap = sum(ns)
+    w_all, m_all = gw.alloc_storage(cap), gm.alloc_storage(cap)
+    L.lct_encode_group(gw, w_all)
+    L.lct_encode_group(gm, m_all)
+    storage_equal(L, gm, m_all, orc.group(rm, cap), ns, "M")
+    ref = orc.group([orc.sgd(ocw[k], rw[k], ocm[k], rm[k], 1e-3) for k in range(len(ns))], cap)
+    out = gw.alloc_storage(cap)
+    if inplace:
+        out.sf, out.pay, out.cnt, out.obase = w_all.sf, w_all.pay, w_all.cnt, w_all.obase
+    L.lct_sgd_step_group(gw, w_all, gm, m_all, 1e-3, out)
+    storage_equal(L, gw, out, ref, ns, "W' far readers inplace=%s" % inplace)
+
+
+@pytest.mark.parametrize("inplace", [False, True])
 @pytest.mark.parametrize("B,cw", [(65536, 25), (8192, 3), (32768, 12), (32768, 11)])
 def test_group_momentum(L, orc, B, cw, inplace):
     """Momentum step on groups: W and M with per-tensor codebooks, the
