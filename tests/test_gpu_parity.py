@@ -365,6 +365,32 @@ def test_partial_last_block(L, orc, B, cw, n):
     assert ow.full_path_units() == 4 * nfull and om.full_path_units() == 4 * nfull
 
 
+@pytest.mark.parametrize("B", [4096, 16384, 32768])
+def test_ring_kernel_short_streams(L, orc, B):
+    """The 25-word capacity with blocks smaller than CLEAN's: the ring kernel
+    runs streams of 16 to 128 positions (the ring's first rows hold most or
+    all of a stream, and the refills reach rows past the stream's end, which
+    read as zero); whole blocks take it, a partial last block the general
+    kernel; the update and the momentum step equal the oracle's, in place and
+    not."""
+    g = np.random.default_rng(B + 25)
+    n = 5 * B + 4000
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr = synth.to_bf16_bits(g.normal(0, 4e-4, n))
+    mw, mm = synth.Model(0, 0.02), synth.Model(0, 1e-3)
+    for inplace in (False, True):
+        what = "ring B=%d inplace=%s" % (B, inplace)
+        sgd_case(L, orc, w, m, mw, mm, 1e-3, B, 25, inplace, what=what)
+        momentum_case(L, orc, w, m, gr, mw, mm, 0.9, 1e-3, B, 25, inplace, what=what)
+    cbw = L.lct_codebook_build(L.Model(0, 0.02, 0.0), dev(w))
+    cbm = L.lct_codebook_build(L.Model(0, 1e-3, 0.0), dev(m))
+    lay = L.layout(B, 25)
+    out = L.alloc_tensor(n, lay)
+    L.lct_sgd_step(cbw, L.encode(cbw, dev(w), lay), cbm, L.encode(cbm, dev(m), lay), 1e-3, out)
+    assert out.full_path_units() == 4 * (n // B)
+
+
 def test_sgd_eta_zero_identity(L, orc):
     g = np.random.default_rng(3)
     n = 5 * 65536 + 7
