@@ -1496,10 +1496,39 @@ __device__ __forceinline__ void sgd_stream_general(const SgdParams &p, const Sgd
                     e[i] = (R >> 20) & 0x7F8u;   // 8 * exponent field
                 }
             };
-            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s)))
-                elems(std::false_type{});
-            else
+            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s))) {
+                // no spilled field: four fields per window, a group of four
+                // positions at a time (a group whose window ran out is
+                // decoded again a field per window); fields past a stream's
+                // end decode to values that are not stored
+#pragma unroll
+                for (uint32_t g = 0; g < CH; g += 4) {
+                    const int32_t qw0 = rw.q, qm0 = rm.q;
+                    uint32_t ew[4], em[4];
+                    const uint32_t cw = rw.next_n<4>(kSgdWTab, qwmax, ew);
+                    const uint32_t cm = rm.next_n<4>(kSgdMTab, qmmax, em);
+                    if (__builtin_expect(!wave_all(max(cw, cm) <= 30), 0)) {
+                        rw.q = qw0;
+                        rm.q = qm0;
+#pragma unroll
+                        for (uint32_t k = 0; k < 4; ++k) {
+                            ew[k] = rw.next(kSgdWTab);
+                            rw.q = min(rw.q, qwmax);
+                            em[k] = rm.next(kSgdMTab);
+                            rm.q = min(rm.q, qmmax);
+                        }
+                    }
+#pragma unroll
+                    for (uint32_t k = 0; k < 4; ++k) {
+                        const uint32_t i = g + k;
+                        const uint32_t R = sgd_round(join32(bf.w[i], ew[k]), join32(bf.m[i], em[k]), p.mul);
+                        if (j0 + i < n_s) o[i * NS] = (uint8_t)(sgd_sf16(R) >> 16);
+                        e[i] = (R >> 20) & 0x7F8u;
+                    }
+                }
+            } else {
                 elems(std::true_type{});
+            }
             writer_chunk<true, false>(st, e, j0, n_s, capbits, kSgdETab);
             writer_spill<true>(st, e, j0, n_s, stage_ctr, stage, p.ovf_cap);
         });
@@ -2128,10 +2157,42 @@ __device__ __forceinline__ void mom_stream_general(const MomParams &p, const Sgd
                     em[i] = (Rm >> 20) & 0x7F8u;
                 }
             };
-            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s)))
-                elems(std::false_type{});
-            else
+            if (wave_all((j0 + CH <= cw_s || cw_s >= n_s) && (j0 + CH <= cm_s || cm_s >= n_s))) {
+                // no spilled field: four fields per window, a group of four
+                // positions at a time, as in the update's general path
+#pragma unroll
+                for (uint32_t g4 = 0; g4 < CH; g4 += 4) {
+                    const int32_t qw0 = rw.q, qm0 = rm.q;
+                    uint32_t fw[4], fm[4];
+                    const uint32_t cw = rw.next_n<4>(kMWD, qwmax, fw);
+                    const uint32_t cm = rm.next_n<4>(kMMD, qmmax, fm);
+                    if (__builtin_expect(!wave_all(max(cw, cm) <= 30), 0)) {
+                        rw.q = qw0;
+                        rm.q = qm0;
+#pragma unroll
+                        for (uint32_t k = 0; k < 4; ++k) {
+                            fw[k] = rw.next(kMWD);
+                            rw.q = min(rw.q, qwmax);
+                            fm[k] = rm.next(kMMD);
+                            rm.q = min(rm.q, qmmax);
+                        }
+                    }
+#pragma unroll
+                    for (uint32_t k = 0; k < 4; ++k) {
+                        const uint32_t i = g4 + k;
+                        const uint32_t Rm = sgd_round(bf.g[i] << 16, join32(bf.m[i], fm[k]), p.mu);
+                        const uint32_t Rw = sgd_round(join32(bf.w[i], fw[k]), Rm & 0xFFFF0000u, p.neg_eta);
+                        if (j0 + i < n_s) {
+                            ow[i * NS] = (uint8_t)(sgd_sf16(Rw) >> 16);
+                            om[i * NS] = (uint8_t)(sgd_sf16(Rm) >> 16);
+                        }
+                        ew[i] = (Rw >> 20) & 0x7F8u;
+                        em[i] = (Rm >> 20) & 0x7F8u;
+                    }
+                }
+            } else {
                 elems(std::true_type{});
+            }
             writer_chunk<true, false>(stw, ew, j0, n_s, capbits, kMWE);
             writer_spill<true>(stw, ew, j0, n_s, wctr, wstage, p.ow_ovf_cap);
             writer_chunk<true, false>(stm, em, j0, n_s, capbits, kMME);
