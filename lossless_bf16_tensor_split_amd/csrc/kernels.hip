@@ -716,9 +716,10 @@ __global__ void k_clear(uint64_t *words, uint64_t nwords, uint32_t *status) {
     if (i == 0) *status = 0u;
 }
 
-// Overflow offsets: an exclusive scan of the units' spill totals in unit
-// order (block, then its units), one unit per thread, groups chained by the
-// look-back.  Writes obase and flags a too-small overflow region.
+// Overflow offsets: an exclusive scan of the blocks' spill totals (each the
+// sum of its units' records), one block per thread, groups chained by the
+// look-back.  Writes obase and flags a too-small overflow region; the
+// placing kernel finds a unit's place within its block from the records.
 __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase,
                                                      uint64_t ovf_cap, uint32_t *status) {
     __shared__ uint32_t s_g;
@@ -727,12 +728,23 @@ __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t 
     if (t == 0) s_g = atomicAdd(reinterpret_cast<uint32_t *>(scratch + kScrTicket2), 1u);
     __syncthreads();
     const uint32_t g = s_g;
-    const uint64_t nunits = nblk * kMaxUnits;
-    const uint64_t u = (uint64_t)g * kScanGroup + t;
+    // one thread per block: its units' records are contiguous
+    const uint64_t b = (uint64_t)g * kScanGroup + t;
     const UnitRec *rec = reinterpret_cast<const UnitRec *>(scratch + scr_rec_offset(nblk));
-    const UnitRec r = u < nunits ? rec[u] : UnitRec{0, 0, 0};
+    uint64_t total = 0;
+    uint32_t parked = 0;
+    if (b < nblk) {
+        UnitRec r[kMaxUnits];
+#pragma unroll
+        for (uint32_t k = 0; k < kMaxUnits; ++k) r[k] = rec[b * kMaxUnits + k];
+#pragma unroll
+        for (uint32_t k = 0; k < kMaxUnits; ++k) {
+            total += r[k].total;
+            parked |= r[k].flags & 1u;
+        }
+    }
     // group scan of the totals (64-bit sums)
-    uint64_t inc = r.total;
+    uint64_t inc = total;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         const uint64_t x = __shfl_up(inc, d, 64);
@@ -753,14 +765,14 @@ __global__ __launch_bounds__(kScanGroup) void k_scan(uint8_t *scratch, uint64_t 
         if (t == 0) s_excl = ex;
     }
     __syncthreads();
-    const uint64_t ex = s_excl + inc - r.total;
-    if (u < nunits && u % kMaxUnits == 0) obase[u / kMaxUnits] = ex;
-    if (u + 1 == nunits) {
-        obase[nblk] = ex + r.total;
-        if (ex + r.total > ovf_cap) atomicOr(status, LCT_ST_OVF_FULL);
+    const uint64_t ex = s_excl + inc - total;
+    if (b < nblk) obase[b] = ex;
+    if (b + 1 == nblk) {
+        obase[nblk] = ex + total;
+        if (ex + total > ovf_cap) atomicOr(status, LCT_ST_OVF_FULL);
     }
     // parked counts are put in place by the placing kernel: tell it
-    if (__any(u < nunits && (r.flags & 1u)) && lane() == 0)
+    if (__any(parked != 0) && lane() == 0)
         atomicOr(reinterpret_cast<uint32_t *>(scratch + kScrParked), 1u);
 }
 
@@ -2640,7 +2652,7 @@ int launch_clear(uint8_t *scratch, uint64_t nblk, uint32_t *status, void *stream
 
 int launch_scan(uint8_t *scratch, uint64_t nblk, uint64_t *obase, uint8_t *ovf, uint64_t ovf_cap,
                 uint32_t *status, uint16_t *cnt, void *stream) {
-    const uint64_t groups = (nblk * kMaxUnits + kScanGroup - 1) / kScanGroup;
+    const uint64_t groups = (nblk + kScanGroup - 1) / kScanGroup;
     hipLaunchKernelGGL(k_scan, dim3((uint32_t)groups), dim3(kScanGroup), 0, (hipStream_t)stream,
                        scratch, nblk, obase, ovf_cap, status);
     hipError_t e = hipGetLastError();

@@ -35,7 +35,8 @@ constexpr uint64_t kScrParked = 24;   // uint32: nonzero when some unit parked i
 constexpr uint64_t kScrFullUnits = 28;  // uint32: units the update ran on its full-block path
                                         // (read by tests to show which path ran)
 constexpr uint64_t kScrFlags = 64;    // uint64[groups + 1]: the scan's look-back flags
-constexpr uint32_t kScanGroup = 256;  // units per scan workgroup
+constexpr uint32_t kScanGroup = 256;  // blocks per scan workgroup (the flags are sized for
+                                      // one group per 256 units, more than it needs)
 __host__ __device__ inline uint64_t scr_units(uint64_t nblk) { return kMaxUnits * nblk; }
 __host__ __device__ inline uint64_t scr_clear_bytes(uint64_t nblk) {
     return kScrFlags + 8 * ((scr_units(nblk) + kScanGroup - 1) / kScanGroup + 1);
