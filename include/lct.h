@@ -37,7 +37,9 @@
  *     aliasing, wrong device) are returned before anything is enqueued.
  *     The only data-dependent failure is a too-small overflow region: it is
  *     reported through the device status word (LCT_ST_* bits), never by a
- *     fault.  n == 0 is a no-op that returns LCT_OK.
+ *     fault.  n == 0 (for a group: no blocks) is a no-op that returns LCT_OK
+ *     and writes nothing; the empty encoding is obase = [0] with status 0, so
+ *     storage whose obase and status start zeroed already holds it.
  *   - Thread-safe: no global state beyond the sample array, which is guarded
  *     by a lock.
  */

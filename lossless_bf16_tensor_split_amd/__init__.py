@@ -254,7 +254,9 @@ class LctTensor:
         self.sf = torch.empty(max(sz.sf, 16), dtype=u8, device=dev)
         self.pay = torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev)
         self.cnt = torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev)
-        self.obase = torch.empty(sz.obase // 8, dtype=torch.int64, device=dev)
+        # zeroed: the calls write nothing for an empty tensor, whose encoding
+        # is obase = [0]
+        self.obase = torch.zeros(sz.obase // 8, dtype=torch.int64, device=dev)
         if ovf is None:
             ovf = torch.empty(max(ovf_cap, 16), dtype=u8, device=dev)
         elif ovf.numel() < ovf_cap:
@@ -475,7 +477,8 @@ class LctGroup:
         elif ovf.numel() < ovf_cap:
             raise ValueError("ovf too small: %d < %d" % (ovf.numel(), ovf_cap))
         # the padding after each member is zeroed once: no call writes it,
-        # so it stays zero
+        # so it stays zero; obase is zeroed because a group with no blocks
+        # is a no-op whose encoding is obase = [0]
         sf = torch.empty(max(sz.sf, 16), dtype=u8, device=dev)
         if self.count == 1:
             if int(self.ns[0]) % 256:
@@ -485,7 +488,7 @@ class LctGroup:
         return LctTensor.wrap(int(self.g.sf_bytes), self.layout, ovf_cap, sz, sf,
                               torch.empty(max(sz.pay // 4, 4), dtype=torch.int32, device=dev),
                               torch.empty(max(sz.cnt // 2, 2), dtype=torch.int16, device=dev),
-                              torch.empty(sz.obase // 8, dtype=torch.int64, device=dev),
+                              torch.zeros(sz.obase // 8, dtype=torch.int64, device=dev),
                               ovf, torch.zeros(4, dtype=torch.int32, device=dev), scratch)
 
     def tensor(self, all_: LctTensor, k: int) -> LctTensor:

@@ -137,6 +137,28 @@ def test_group_sgd(L, orc, B, cw, inplace):
         L.lct_sgd_step_group(gw, w_all, other, other.alloc_storage(cap), 1e-3, out)
 
 
+@pytest.mark.parametrize("ns", [[0], [0, 0, 0]])
+def test_group_all_empty(L, orc, ns):
+    """A group whose members are all empty has no blocks: every group call
+    writes nothing, and the storage as allocated already holds the empty
+    encoding (obase = [0], status 0)."""
+    B, cw = 65536, 25
+    xs, ocbs, cbs, dense, grp = make_group(L, orc, ns, B, cw, 9700 + len(ns))
+    ref = orc.encode_group(ocbs, xs, B, cw)
+    assert ref.obase.tolist() == [0] and ref.status == 0
+    all_ = grp.alloc_storage(16)
+    L.lct_encode_group(grp, all_)
+    storage_equal(L, grp, all_, ref, ns, "encode")
+    gm = L.LctGroup(ns, L.layout(B, cw), cbs, dense)
+    m_all = gm.alloc_storage(16)
+    L.lct_encode_group(gm, m_all)
+    out = grp.alloc_storage(16)
+    L.lct_sgd_step_group(grp, all_, gm, m_all, 1e-3, out)
+    storage_equal(L, grp, out, ref, ns, "update")
+    L.lct_decode_group(grp, out)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("inplace", [False, True])
 def test_group_sgd_readers_far_apart(L, orc, inplace):
     """The group update at the CLEAN capacity with M tensors whose streams

@@ -88,7 +88,7 @@ def test_config1_gaussian_clean(L, orc):
     assert ref.spilled == 0 and abs(t.ratio() - ref.ratio()) < 1e-12
 
 
-@pytest.mark.parametrize("n", [1, 255, 256, 257, 2047, 2048, 2049, 65535, 65537, 300001])
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 2047, 2048, 2049, 65535, 65537, 300001])
 def test_odd_sizes(L, orc, n):
     x = synth.draw(synth.TensorSpec("w", (n,), 500 + n % 89, "normal", {"sigma": 0.02}))
     for B, cw in [(65536, 25), (4096, 2), (4096, 1)]:
