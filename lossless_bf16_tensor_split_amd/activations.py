@@ -21,6 +21,11 @@ Per saved tensor:
     pool, and the host codebook for the decode is made from the shift.  A
     save that finds the pool empty waits for the oldest save's event; the
     block's end and a backward read of a save still in flight wait for it.
+  - streams: a save runs on the current stream.  Each staging slot has its
+    own scratch, and a slot taken again waits (on the device) for the trim
+    that last read it, so saves made on different streams do not race; a
+    restore on another stream than its save's waits for the trim and keeps
+    the saved buffers alive until its decode is done.
 
 Tensors that are not BF16, not on the GPU, not contiguous, smaller than
 `min_elems`, or leaves that require grad (parameters, which autograd saves by
@@ -50,6 +55,8 @@ class _Saved:
     grp: LctGroup | None         # its one-tensor group (device tables), until the encode is done
     shape: torch.Size
     cb: Codebook | None = None   # host codebook, once the shift is known
+    stream: torch.cuda.Stream | None = None   # the stream its buffers were made and written on
+    ready: torch.cuda.Event | None = None     # recorded on it once the spills are trimmed
 
 
 class ActivationCodec:
@@ -66,8 +73,9 @@ class ActivationCodec:
         self.len_base = list(self.base.len_base)
         self.layout = lct_layout_init(mode)
         self.min_elems = int(min_elems)
-        self._scratch = None
         self._stage = [None] * pool          # staging regions
+        self._scratch = [None] * pool        # each slot's scratch
+        self._slot_ev = [None] * pool        # recorded after the trim that last read each slot
         self._free = list(range(pool))
         self._shift = None                   # device int32 per slot: the fitted shift
         self._pin_shift = None               # pinned host copies: shift (int32) and
@@ -93,6 +101,9 @@ class ActivationCodec:
         h.grp = None                         # its table and the reference to the input go
         with torch.cuda.stream(stream):
             h.t.ovf = self._stage[slot][:max(spilled, 16)].clone()
+            h.ready = torch.cuda.Event()
+            h.ready.record(stream)
+        self._slot_ev[slot] = h.ready
         h.t.ovf_cap = spilled
         h.cb = lct_codebook_from_lengths(self.len_base, self.base.esc_len, shift)
         self.stored_bytes += int(h.t.sizes.fixed) + spilled
@@ -123,6 +134,9 @@ class ActivationCodec:
         if not self._free:
             self._reap(wait_one=True)
         slot = self._free.pop()
+        if self._slot_ev[slot] is not None:
+            # the slot's last trim may have run on another stream
+            stream.wait_event(self._slot_ev[slot])
         if self._shift is None:
             self._pin_shift = torch.zeros(len(self._stage), dtype=torch.int32, pin_memory=True)
             self._pin_spill = torch.zeros(len(self._stage), dtype=torch.int64, pin_memory=True)
@@ -134,12 +148,13 @@ class ActivationCodec:
         if st is None or st.numel() < cap or st.device != dev:
             self._stage[slot] = st = torch.empty(max(cap, 16), dtype=torch.uint8, device=dev)
         sz = lct_sizes(n, self.layout, cap)
-        if self._scratch is None or self._scratch.numel() < sz.scratch or self._scratch.device != dev:
-            self._scratch = torch.empty(sz.scratch, dtype=torch.uint8, device=dev)
+        scr = self._scratch[slot]
+        if scr is None or scr.numel() < sz.scratch or scr.device != dev:
+            self._scratch[slot] = scr = torch.empty(sz.scratch, dtype=torch.uint8, device=dev)
         # the codebook fitted on the device, then the encode with its tables
         grp = LctGroup([n], self.layout, [self.base], [xd], device=dev, fit=True,
                        shift=self._shift[slot:slot + 1], stream=stream)
-        all_ = grp.alloc_storage(cap, dev, self._scratch, st)
+        all_ = grp.alloc_storage(cap, dev, scr, st)
         lct_encode_group(grp, all_, stream)
         self._pin_shift[slot:slot + 1].copy_(self._shift[slot:slot + 1], non_blocking=True)
         self._pin_spill[slot:slot + 1].copy_(all_.obase[-1:], non_blocking=True)
@@ -147,7 +162,7 @@ class ActivationCodec:
         ev.record(stream)
         t = LctTensor.wrap(n, self.layout, cap, lct_sizes(n, self.layout, cap), all_.sf, all_.pay, all_.cnt,
                            all_.obase, st, all_.status, None)
-        h = _Saved(t, grp, x.shape)
+        h = _Saved(t, grp, x.shape, stream=stream)
         self._pending.append((h, slot, ev, stream))
         self.saved += 1
         self.raw_bytes += 2 * n
@@ -160,6 +175,11 @@ class ActivationCodec:
         t0 = time.perf_counter()
         while h.cb is None:                  # still in flight: finish saves up to it
             self._reap(wait_one=True)
+        cur = torch.cuda.current_stream(h.t.sf.device)
+        if cur != h.stream:
+            cur.wait_event(h.ready)
+            for b in (h.t.sf, h.t.pay, h.t.cnt, h.t.obase, h.t.ovf):
+                b.record_stream(cur)
         y = torch.empty(h.shape, dtype=torch.bfloat16, device=h.t.sf.device)
         lct_decode(h.cb, h.t, y.view(-1))
         self.unpack_s += time.perf_counter() - t0

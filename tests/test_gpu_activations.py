@@ -128,6 +128,34 @@ def test_consecutive_saves_trim_in_turn(L, orc):
     assert all(h.t.ovf_cap == h.t.spilled() for h in hs)
 
 
+def test_saves_on_two_streams(L, orc):
+    """Saves made in turn on two streams share the codec's staging pool
+    (three slots for eight saves, so slots change streams), and every save is
+    read back on a third stream: each comes back bit for bit."""
+    from lossless_bf16_tensor_split_amd.activations import ActivationCodec
+    codec = ActivationCodec(L.Model(0, 1.0, 0.0), min_elems=1)
+    g = np.random.default_rng(9120)
+    xs = [synth.to_bf16_bits(g.normal(0, 1.0, 90000 + 777 * k) * np.where(g.random(90000 + 777 * k) < 0.5,
+                                                                           1.0, 64.0)) for k in range(8)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    hs = []
+    for k, x in enumerate(xs):
+        xd = dev(x).view(torch.bfloat16)
+        s = streams[k % 2]
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            hs.append(codec.pack(xd))
+        xd.record_stream(s)
+    codec.close()
+    assert min(h.t.spilled() for h in hs) > 0
+    reader = torch.cuda.Stream()
+    with torch.cuda.stream(reader):
+        ys = [codec.unpack(h) for h in reversed(hs)]
+    reader.synchronize()
+    for x, y in zip(reversed(xs), ys):
+        assert np.array_equal(as_bits(y), x)
+
+
 def test_codec_reused_across_steps(L, orc):
     """One codec entered at every step of a small MLP: its staging pool and
     pinned words carry over, every step's saves are encoded and read back,
