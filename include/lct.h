@@ -364,8 +364,10 @@ lct_status lct_group_table_bytes(uint32_t count, const uint64_t *n, const lct_la
  * be NULL for a group that is only updated).  Dense buffers must not overlap
  * each other.  Writes the descriptor table to d_table (device,
  * lct_group_table_bytes bytes, 256-byte aligned) with a blocking copy and
- * fills *out, which keeps the n and d_dense pointers.  Errors: LCT_EINVAL,
- * LCT_EALIGN, LCT_EALIAS, LCT_EARCH, LCT_EHIP. */
+ * fills *out, which keeps the n and d_dense pointers.  The copy is not
+ * ordered with work queued on other streams: no such work may still use
+ * d_table's memory.  Errors: LCT_EINVAL, LCT_EALIGN, LCT_EALIAS, LCT_EARCH,
+ * LCT_EHIP. */
 lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *layout,
                           const lct_codebook *cbs, uint16_t *const *d_dense, void *d_table,
                           lct_group *out);

@@ -456,6 +456,10 @@ class LctGroup:
                                      _ptr(self.table), _ptr(shift), _stream(stream), C.byref(self.g)),
                    "lct_group_fit")
         else:
+            # the table's memory may come from a tensor freed while work that
+            # uses it is still queued on the current stream, and the bind's
+            # blocking copy is not ordered with that stream
+            torch.cuda.current_stream(self.table.device).synchronize()
             _check(lib.lct_group_bind(count, self.ns, C.byref(self.layout), self.codebooks,
                                       self.dense_ptrs, _ptr(self.table), C.byref(self.g)), "lct_group_bind")
 
