@@ -7,6 +7,7 @@ import ctypes as C
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -373,3 +374,18 @@ def test_group_host_side(L):
     assert L.lib.lct_momentum_step_group(C.byref(g), C.byref(all_), C.byref(g), C.byref(all_), C.byref(g),
                                          C.c_float(0.9), C.c_float(1e-3), C.byref(all_), C.byref(all_),
                                          None) == L.EINVAL
+
+
+def test_no_library_no_import(tmp_path):
+    """A copy of the package without liblct.so refuses to import: there is no
+    path around the HIP library."""
+    import shutil
+    pkg = os.path.join(ROOT, "lossless_bf16_tensor_split_amd")
+    dst = tmp_path / "lossless_bf16_tensor_split_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    assert not (dst / "liblct.so").exists()
+    r = subprocess.run([sys.executable, "-c", "import lossless_bf16_tensor_split_amd"], cwd=str(tmp_path),
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError: liblct.so is not built" in r.stderr
