@@ -43,57 +43,113 @@ constexpr int kLit = 8;          // literal bits after the escape code
 constexpr int kEsc = 256;        // escape symbol id
 
 // ---------------------------------------------------------------- model
+//
+// The probability of each exponent field's range of |x| under the model.
+// Gaussian and Laplace use their survival functions, P(|X| > t) = erfc(t /
+// (sigma sqrt 2)) and exp(-t / b).  Student-t integrates its density over
+// the range by Gauss-Legendre quadrature (no survival function, so no
+// difference of two nearly equal tails near zero): the range is cut into
+// pieces over each of which the log-density drops by at most one, so the
+// integrand is smooth on the scale of a piece and the rule is exact to
+// rounding; pieces whose mass is certainly below 2^-70 count as zero (their
+// weights are zero either way).
 
-double cont_frac_beta(double a, double b, double x) {
-    // 1 / (1 + d1 / (1 + d2 / (1 + ...))) for the regularized incomplete beta,
-    // with d_{2m+1} = -(a+m)(a+b+m)x / ((a+2m)(a+2m+1)) and
-    // d_{2m} = m(b-m)x / ((a+2m-1)(a+2m)); modified Lentz evaluation.
-    const double tiny = 1e-300;
-    double f = 1.0, c = 1.0, d = 0.0;
-    for (int j = 1; j <= 100000; ++j) {
-        const double m = j / 2;
-        const double num = (j & 1) ? -(a + m) * (a + b + m) * x
-                                   : m * (b - m) * x;
-        const double den = (j & 1) ? (a + 2.0 * m) * (a + 2.0 * m + 1.0)
-                                   : (a + 2.0 * m - 1.0) * (a + 2.0 * m);
-        const double dj = num / den;
-        d = 1.0 + dj * d;
-        if (fabs(d) < tiny) d = tiny;
-        d = 1.0 / d;
-        c = 1.0 + dj / c;
-        if (fabs(c) < tiny) c = tiny;
-        const double step = c * d;
-        f *= step;
-        if (fabs(step - 1.0) < 1e-16) break;
+// Gauss-Legendre rule with kGl nodes on [-1, 1]: the nodes are the roots of
+// the Legendre polynomial P_n, found by Newton's method from the estimates
+// cos(pi (i + 3/4) / (n + 1/2)), P_n and P_n' from the three-term recurrence;
+// the weights are 2 / ((1 - x^2) P_n'(x)^2).
+constexpr int kGl = 24;
+struct GaussLegendre {
+    double x[kGl], w[kGl];
+    GaussLegendre() {
+        const double pi = 3.14159265358979323846;
+        for (int i = 0; i < kGl; ++i) {
+            double z = cos(pi * (i + 0.75) / (kGl + 0.5)), dp = 0.0;
+            for (int it = 0; it < 100; ++it) {
+                double p0 = 1.0, p1 = z;          // P_{k-1}(z), P_k(z)
+                for (int k = 2; k <= kGl; ++k) {
+                    const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+                    p0 = p1;
+                    p1 = p2;
+                }
+                dp = kGl * (z * p1 - p0) / (z * z - 1.0);
+                const double dz = p1 / dp;
+                z -= dz;
+                if (fabs(dz) <= 1e-16) break;
+            }
+            double p0 = 1.0, p1 = z;
+            for (int k = 2; k <= kGl; ++k) {
+                const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+                p0 = p1;
+                p1 = p2;
+            }
+            dp = kGl * (z * p1 - p0) / (z * z - 1.0);
+            x[i] = z;
+            w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+        }
     }
-    return f;
+};
+const GaussLegendre &gauss_legendre() {
+    static const GaussLegendre rule;
+    return rule;
 }
 
-// I_x(a, b); y = 1 - x is given separately to keep its precision.
-double reg_inc_beta(double a, double b, double x, double y) {
-    if (x <= 0.0) return 0.0;
-    if (y <= 0.0) return 1.0;
-    const double lb = lgamma(a) + lgamma(b) - lgamma(a + b);
-    const double front = exp(a * log(x) + b * log(y) - lb);
-    if (x < (a + 1.0) / (a + b + 2.0)) return front / (a * cont_frac_beta(a, b, x));
-    return 1.0 - front / (b * cont_frac_beta(b, a, y));
+// log Gamma(x + 1/2) - log Gamma(x).  For x >= 15 from Stirling's series
+// log Gamma(z) = (z - 1/2) log z - z + log(2 pi)/2 + sum B_2k / (2k (2k-1)
+// z^(2k-1)), taken as one difference (five terms: error below 1e-16
+// relative), since the two lgamma values, each about x log x, would cancel
+// to about 1e-16 x log x of absolute error.
+double lgamma_half_step(double x) {
+    if (x < 15.0) return lgamma(x + 0.5) - lgamma(x);
+    auto series = [](double z) {
+        const double r = 1.0 / z, r2 = r * r;
+        return r * (1.0 / 12 - r2 * (1.0 / 360 - r2 * (1.0 / 1260 - r2 * (1.0 / 1680 - r2 / 1188))));
+    };
+    return x * log1p(0.5 / x) + 0.5 * log(x) - 0.5 + (series(x + 0.5) - series(x));
 }
 
-// P(|X| > t) under the model.
-double tail(const lct_model &m, double t) {
-    switch (m.family) {
-    case LCT_GAUSSIAN:
-        return erfc(t / (m.scale * sqrt(2.0)));
-    case LCT_LAPLACE:
-        return exp(-t / m.scale);
-    case LCT_POWERLAW: {
-        const double u = t / m.scale;
-        const double nu = m.shape;
-        return reg_inc_beta(0.5 * nu, 0.5, nu / (nu + u * u), (u * u) / (nu + u * u));
+// Student-t with nu degrees of freedom, unit scale: the density at u is
+// exp(lc - g(u)) with g(u) = (nu + 1)/2 log(1 + u^2/nu).
+struct StudentT {
+    double nu, lc;
+    explicit StudentT(double nu_)
+        : nu(nu_), lc(lgamma_half_step(0.5 * nu_) - 0.5 * log(nu_ * 3.14159265358979323846)) {}
+    double g(double u) const { return 0.5 * (nu + 1.0) * log1p(u * u / nu); }
+    double density(double u) const { return exp(lc - g(u)); }
+    // g' is largest at u = sqrt(nu)
+    double max_slope(double a, double b) const {
+        const double u = std::min(std::max(sqrt(nu), a), b);
+        return (nu + 1.0) * u / (nu + u * u);
     }
+    // P(a <= |T| < b), 0 <= a < b
+    double mass(double a, double b) const {
+        if (!(b > a)) return 0.0;
+        if (2.0 * density(a) * (b - a) < 0x1p-70) return 0.0;
+        const double drop = max_slope(a, b) * (b - a);
+        const int pieces = (int)std::min(65536.0, std::max(1.0, ceil(drop)));
+        const GaussLegendre &r = gauss_legendre();
+        const double h = (b - a) / pieces;
+        double sum = 0.0;
+        for (int j = 0; j < pieces; ++j) {
+            const double x0 = a + j * h, half = 0.5 * h, mid = x0 + half;
+            if (2.0 * density(x0) * h < 0x1p-70) break;      // the density decreases from here
+            double q = 0.0;
+            for (int i = 0; i < kGl; ++i) q += r.w[i] * density(mid + half * r.x[i]);
+            sum += q * half;
+        }
+        return 2.0 * sum;
     }
-    return 0.0;
-}
+    // P(|T| < b): octaves down to where the density is flat, then the rest
+    double below(double b) const {
+        const double flat = std::min(sqrt(nu), 1.0) / 8.0;
+        double sum = 0.0, hi = b;
+        while (hi > flat) {
+            sum += mass(0.5 * hi, hi);
+            hi *= 0.5;
+        }
+        return sum + mass(0.0, hi);
+    }
+};
 
 bool model_ok(const lct_model &m) {
     if (m.family < LCT_GAUSSIAN || m.family > LCT_POWERLAW) return false;
@@ -102,16 +158,38 @@ bool model_ok(const lct_model &m) {
     return true;
 }
 
+}  // namespace
+
+// Field e in 1..254 covers |x| in [2^(e-127), 2^(e-126)); field 0 zero and
+// the subnormals (|x| < 2^-126); field 255 has no mass.
+void model_pmf(const lct_model &m, double p[256]) {
+    const double r2 = sqrt(2.0);
+    auto edge = [&](int e) { return ldexp(1.0, e - 127) / m.scale; };   // in units of the scale
+    switch (m.family) {
+    case LCT_GAUSSIAN:
+        p[0] = erf(edge(1) / r2);
+        for (int e = 1; e <= 254; ++e) p[e] = erfc(edge(e) / r2) - erfc(edge(e + 1) / r2);
+        break;
+    case LCT_LAPLACE:
+        p[0] = -expm1(-edge(1));
+        for (int e = 1; e <= 254; ++e) p[e] = exp(-edge(e)) - exp(-edge(e + 1));
+        break;
+    default: {
+        const StudentT t(m.shape);
+        p[0] = t.below(edge(1));
+        for (int e = 1; e <= 254; ++e) p[e] = t.mass(edge(e), edge(e + 1));
+    }
+    }
+    for (int e = 0; e <= 254; ++e)
+        if (!(p[e] > 0.0)) p[e] = 0.0;
+    p[255] = 0.0;
+}
+
+namespace {
+
 void model_weights(const lct_model &m, uint64_t w[256]) {
     double p[256];
-    p[0] = 1.0 - tail(m, ldexp(1.0, -126));
-    for (int e = 1; e <= 254; ++e) {
-        const double lo = tail(m, ldexp(1.0, e - 127));
-        const double hi = tail(m, ldexp(1.0, e - 126));
-        const double q = lo - hi;
-        p[e] = q > 0.0 ? q : 0.0;
-    }
-    p[255] = 0.0;
+    model_pmf(m, p);
     for (int e = 0; e < 256; ++e) w[e] = (uint64_t)floor(p[e] * 1099511627776.0 + 0.5);
 }
 

@@ -274,6 +274,8 @@ int launch_sample(const SampleParams &p, void *stream, uint16_t *host_out);
 int launch_fit(const FitParams &p, void *stream);
 
 // Host codebook construction (codebook.cpp).
+// The model's probability of each exponent field (its range of |x|).
+void model_pmf(const lct_model &model, double p[256]);
 lct_status build_codebook(const lct_model &model, const uint16_t *sample, uint32_t m,
                           lct_codebook *out);
 lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, int32_t shift,

@@ -61,3 +61,18 @@ def test_host_codebook_under_sanitizers(tmp_path):
     assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
     assert "mismatches: 0" in out
+    assert "differing bins: 0" in out and "pmfs checked: 0" not in out
+    # the library's Student-t pmf at large nu against 50-digit values of the
+    # survival function I_{nu/(nu+u^2)}(nu/2, 1/2) (mpmath's regularized
+    # incomplete beta), bin by bin
+    import mpmath as mp
+    mp.mp.dps = 50
+    rows = [ln.split()[1:] for ln in out.splitlines() if ln.startswith("libpmf ")]
+    assert len(rows) > 20
+    def surv(nu, u):
+        return mp.betainc(nu / 2, mp.mpf(1) / 2, 0, nu / (nu + u * u), regularized=True)
+    for nu_s, scale_s, e_s, p_s in rows:
+        nu, scale, e = mp.mpf(nu_s), mp.mpf(scale_s), int(e_s)
+        lo = mp.ldexp(1, e - 127) / scale
+        exact = surv(nu, lo) - surv(nu, 2 * lo)
+        assert abs(float(p_s) - exact) <= 1e-13 * exact, (nu_s, scale_s, e, p_s, exact)
