@@ -19,10 +19,11 @@ LAYOUTS = [(65536, 25), (32768, 12), (32768, 11), (4096, 1), (8192, 3), (4096, 2
 SPECIALS = np.array([0x7FC0, 0xFFC1, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x7F7F,
                      0xFF7F, 0x0080, 0x7F81], np.uint16)
 NCASES = 200
+NUS = (1.0, 2.5, 3.0, 7.0, 30.0)   # Student-t degrees of freedom
 
 
 def draw_values(g, n):
-    """BF16 bits from a random family and scale, with the model the codebook
+    """BF16 bits from a random family, scale (and Student-t shape), with the model the codebook
     is built from (sometimes off by a power of two, so that fields shift or
     spill), and sometimes a sprinkle of special values."""
     fam = int(g.integers(0, 3))
@@ -32,13 +33,14 @@ def draw_values(g, n):
     elif fam == 1:
         x = g.laplace(0, scale, n)
     else:
-        x = g.standard_t(3, n) * scale
+        nu = float(NUS[int(g.integers(0, len(NUS)))])
+        x = g.standard_t(nu, n) * scale
     bits = synth.to_bf16_bits(x)
     if g.random() < 0.3 and n > 0:
         k = int(g.integers(1, max(2, n // 50)))
         bits[g.integers(0, n, k)] = SPECIALS[g.integers(0, SPECIALS.size, k)]
     model_scale = scale * float(2.0 ** int(g.integers(-3, 4))) if g.random() < 0.4 else scale
-    shape = 3.0 if fam == 2 else 0.0
+    shape = nu if fam == 2 else 0.0
     return bits, synth.Model(fam, model_scale, shape)
 
 
