@@ -35,6 +35,10 @@
  *     synchronise it.
  *   - Errors found on the host (null pointer, bad size, misalignment, illegal
  *     aliasing, wrong device) are returned before anything is enqueued.
+ *     Sizes are bounded so that nothing computed from them wraps: n (of a
+ *     tensor, a group member or a dense input) at most 2^48 elements, at
+ *     most 2^32 - 1 blocks, ovf_cap at most 2^56 bytes; larger ones give
+ *     LCT_EINVAL.
  *     The only data-dependent failure is a too-small overflow region: it is
  *     reported through the device status word (LCT_ST_* bits), never by a
  *     fault.  n == 0 (for a group: no blocks) is a no-op that returns LCT_OK
@@ -163,7 +167,8 @@ typedef struct {
 lct_status lct_layout_init(int32_t mode, lct_layout *out);
 
 /* Buffer sizes of an n-element tensor.  Errors: LCT_EINVAL for a layout
- * outside the accepted range or a null pointer. */
+ * outside the accepted range, a null pointer, or sizes past the limits that
+ * every call checks (see the conventions). */
 lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct_sizes_t *out);
 
 /* Codebook build (explainer, paragraph on bits: the code is fixed ahead of

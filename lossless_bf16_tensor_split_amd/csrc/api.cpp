@@ -47,6 +47,14 @@ bool layout_ok(const lct_layout &l) {
 
 uint64_t nblocks(uint64_t n, const lct_layout &l) { return (n + l.block_elems - 1) / l.block_elems; }
 
+// The largest sizes a call accepts, so that no size or address computed from
+// them wraps: n elements (blocks are indexed by 32 bits) and ovf_cap bytes.
+constexpr uint64_t kMaxElems = 1ull << 48;
+constexpr uint64_t kMaxOvfCap = 1ull << 56;
+bool sizes_ok(uint64_t n, const lct_layout &l, uint64_t ovf_cap) {
+    return n <= kMaxElems && nblocks(n, l) <= 0xFFFFFFFFull && ovf_cap <= kMaxOvfCap;
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 struct Range {
@@ -76,7 +84,8 @@ Parts parts(const lct_tensor &t, uint64_t nb = ~0ull) {
 
 // Pointers a call reads or writes must be non-null and aligned.
 lct_status check_tensor(const lct_tensor *t, bool writes, uint64_t nb = ~0ull) {
-    if (!t || !layout_ok(t->layout)) return LCT_EINVAL;
+    if (!t || !layout_ok(t->layout) || !sizes_ok(t->n, t->layout, t->ovf_cap)) return LCT_EINVAL;
+    if (nb != ~0ull && nb > 0xFFFFFFFFull) return LCT_EINVAL;
     if (!t->sf || !t->pay || !t->cnt || !t->obase) return LCT_EINVAL;
     if (t->ovf_cap && !t->ovf) return LCT_EINVAL;
     if (!aligned(t->sf, 16) || !aligned(t->pay, 16) || !aligned(t->cnt, 4) || !aligned(t->obase, 8))
@@ -127,11 +136,11 @@ uint64_t round256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 bool group_extent(uint32_t count, const uint64_t *n, const lct_layout &l, uint64_t *nblk, uint64_t *sf) {
     uint64_t nb = 0, s = 0;
     for (uint32_t k = 0; k < count; ++k) {
-        if (n[k] >= (1ull << 48)) return false;
+        if (n[k] > kMaxElems) return false;
         nb += nblocks(n[k], l);
+        if (nb > 0xFFFFFFFFull) return false;   // checked as it grows: it cannot wrap
         s += round256(n[k]);
     }
-    if (nb > 0xFFFFFFFFull) return false;
     *nblk = nb;
     *sf = s;
     return true;
@@ -342,7 +351,7 @@ lct_status lct_layout_init(int32_t mode, lct_layout *out) {
 }
 
 lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct_sizes_t *out) {
-    if (!layout || !out || !layout_ok(*layout)) return LCT_EINVAL;
+    if (!layout || !out || !layout_ok(*layout) || !sizes_ok(n, *layout, ovf_cap)) return LCT_EINVAL;
     const uint64_t nb = nblocks(n, *layout);
     out->nblk = nb;
     out->sf = n;
@@ -356,7 +365,7 @@ lct_status lct_sizes(uint64_t n, const lct_layout *layout, uint64_t ovf_cap, lct
 
 lct_status lct_codebook_build(const lct_model *model, const uint16_t *d_x, uint64_t n, void *stream,
                               lct_codebook *out) {
-    if (!model || !out || (n > 0 && !d_x)) return LCT_EINVAL;
+    if (!model || !out || (n > 0 && !d_x) || n > kMaxElems) return LCT_EINVAL;
     const uint32_t m = (uint32_t)std::min<uint64_t>(n, 4096);
     uint16_t sample[4096];
     if (m > 0) {
@@ -417,11 +426,10 @@ lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, voi
 
 lct_status lct_codebook_reshift_dense(const lct_codebook *cb, const uint16_t *d_x, uint64_t n,
                                       void *stream, lct_codebook *out) {
-    if (!cb || !out || (n > 0 && !d_x)) return LCT_EINVAL;
+    if (!cb || !out || (n > 0 && !d_x) || n > kMaxElems) return LCT_EINVAL;
     const uint32_t m = (uint32_t)std::min<uint64_t>(n, 4096);
     uint16_t sample[4096];
     if (m > 0) {
-        if (n >= (1ull << 52)) return LCT_EINVAL;
         lct_status st = check_arch();
         if (st != LCT_OK) return st;
         std::lock_guard<std::mutex> lock(g_sample_mu);
@@ -563,7 +571,7 @@ lct_status lct_sgd_step_noalloc(const lct_codebook *cw, const lct_tensor *w_in, 
                                 const lct_tensor *m, float eta, const lct_tensor *w_out, void *stream) {
     if (!cw || !cm || !w_in || !m || !w_out) return LCT_EINVAL;
     if (w_out->n == 0) return lct_sgd_step(cw, w_in, cm, m, eta, w_out, stream);
-    if (!layout_ok(w_out->layout)) return LCT_EINVAL;
+    if (!layout_ok(w_out->layout) || !sizes_ok(w_out->n, w_out->layout, w_out->ovf_cap)) return LCT_EINVAL;
     if (scr_bytes(nblocks(w_out->n, w_out->layout), w_out->ovf_cap) > kNoAllocScratch) return LCT_ESIZE;
     lct_status st = check_arch();
     if (st != LCT_OK) return st;
@@ -737,7 +745,8 @@ lct_status lct_group_fit(const lct_codebook *base, const uint64_t *n, uint16_t *
 }
 
 lct_status lct_group_sizes(const lct_group *g, uint64_t ovf_cap, lct_sizes_t *out) {
-    if (!g || !out || !layout_ok(g->layout)) return LCT_EINVAL;
+    if (!g || !out || !layout_ok(g->layout) || g->nblk > 0xFFFFFFFFull || ovf_cap > kMaxOvfCap)
+        return LCT_EINVAL;
     out->nblk = g->nblk;
     out->sf = g->sf_bytes;
     out->pay = g->nblk * g->layout.cap_words * kStreams * 4;

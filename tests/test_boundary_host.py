@@ -276,7 +276,8 @@ def test_reshift_and_recode_arguments_rejected_on_host(L):
     bad = _fake_tensor(L, n, lay, 0x1000_0000_0000)
     bad.layout = L.layout(4096, 65)
     assert rs(C.byref(cb), C.byref(bad), None, C.byref(out)) == L.EINVAL
-    big = _fake_tensor(L, 1 << 52, lay, 0x1000_0000_0000)
+    big = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    big.n = 1 << 52                     # past the size limit
     assert rs(C.byref(cb), C.byref(big), None, C.byref(out)) == L.EINVAL
     t0 = _fake_tensor(L, 0, lay, 0x1000_0000_0000)
     assert rs(C.byref(cb), C.byref(t0), None, C.byref(out)) == L.OK
@@ -389,3 +390,48 @@ def test_no_library_no_import(tmp_path):
                        env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError: liblct.so is not built" in r.stderr
+
+
+def test_sizes_past_the_limits_are_refused(L):
+    """n up to 2^48 elements in at most 2^32 - 1 blocks and ovf_cap up to
+    2^56 bytes; past them lct_sizes and every call refuse the tensor before
+    any launch (no size computed from them may wrap)."""
+    big = L.layout(65536, 25)
+    small = L.layout(4096, 2)
+    out = L.Sizes()
+    def sizes(n, lay, cap):
+        return L.lib.lct_sizes(C.c_uint64(n), C.byref(lay), C.c_uint64(cap), C.byref(out))
+    assert sizes((1 << 48) - 65536, big, 1 << 56) == L.OK
+    assert out.nblk == (1 << 32) - 1
+    assert out.pay == out.nblk * 25 * 256 * 4 and out.fixed == out.sf + out.pay + out.cnt + out.obase
+    for n, lay, cap in [(1 << 48, big, 0), ((1 << 48) + 1, big, 0), ((1 << 64) - 1, big, 0),
+                        (0, big, (1 << 56) + 1),
+                        (100, big, (1 << 64) - 1), ((1 << 32) * 4096, small, 0)]:
+        assert sizes(n, lay, cap) == L.EINVAL, (n, cap)
+    assert sizes((1 << 32) * 4096 - 4096, small, 0) == L.OK
+    # a descriptor with a wrapping n or ovf_cap is refused by the calls
+    cb = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    x = C.c_void_p(0x7000_0000_0000)
+    t = _fake_tensor(L, 100000, big, 0x1000_0000_0000)
+    m = _fake_tensor(L, 100000, big, 0x3000_0000_0000)
+    for n, cap in [((1 << 64) - 1, 64), ((1 << 48) + 4096, 64), (100000, (1 << 64) - 1)]:
+        bad = _fake_tensor(L, 100000, big, 0x1000_0000_0000)
+        bad.n, bad.ovf_cap = n, cap
+        assert L.lib.lct_encode(C.byref(cb), x, C.byref(bad), None) == L.EINVAL
+        assert L.lib.lct_decode(C.byref(cb), C.byref(bad), x, None) == L.EINVAL
+        assert L.lib.lct_sgd_step(C.byref(cb), C.byref(t), C.byref(cb), C.byref(m), C.c_float(1e-3),
+                                  C.byref(bad), None) == L.EINVAL
+        assert L.lib.lct_sgd_step_noalloc(C.byref(cb), C.byref(t), C.byref(cb), C.byref(m), C.c_float(1e-3),
+                                          C.byref(bad), None) == L.EINVAL
+    # dense inputs past 2^48 elements
+    model = L.Model(0, 0.02, 0.0)
+    got = L.Codebook()
+    assert L.lib.lct_codebook_build(C.byref(model), x, C.c_uint64((1 << 48) + 1), None, C.byref(got)) == L.EINVAL
+    assert L.lib.lct_codebook_reshift_dense(C.byref(cb), x, C.c_uint64((1 << 64) - 1), None,
+                                            C.byref(got)) == L.EINVAL
+    # group members past 2^48, and groups past 2^32 - 1 blocks in total
+    nbytes = C.c_uint64(0)
+    ns = (C.c_uint64 * 2)((1 << 48) + 1, 5)
+    assert L.lib.lct_group_table_bytes(2, ns, C.byref(big), C.byref(nbytes)) == L.EINVAL
+    many = (C.c_uint64 * 3)(1 << 47, 1 << 47, (1 << 32) * 4096)
+    assert L.lib.lct_group_table_bytes(3, many, C.byref(small), C.byref(nbytes)) == L.EINVAL
