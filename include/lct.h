@@ -105,7 +105,11 @@ typedef struct {
  * len_base[] is the base code the shift was applied to: len[e] =
  * len_base[e - shift] where 0 <= e - shift <= 255, else 0; shift re-estimation
  * keeps it.  The remaining members are lookup tables derived from
- * len/esc_len by the library: treat them as opaque. */
+ * len/esc_len by the library: treat them as opaque.  Every call that takes a
+ * codebook returns LCT_EINVAL for one whose tables break the ranges the
+ * kernels rely on (escape code of 1..8 bits, every field 1..16 bits with no
+ * bits past its length, decode lengths at most 16), such as a zeroed struct
+ * that was never built. */
 typedef struct {
     uint8_t  len[256];
     uint8_t  esc_len;

@@ -385,7 +385,7 @@ lct_status lct_codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_le
 
 lct_status lct_tensor_sample(const lct_codebook *cb, const lct_tensor *t, void *stream,
                              uint16_t *sample, uint32_t *m_out) {
-    if (!cb || !t || !sample) return LCT_EINVAL;
+    if (!cb || !t || !sample || !tables_ok(*cb)) return LCT_EINVAL;
     const uint32_t m = (uint32_t)std::min<uint64_t>(t->n, 4096);
     if (m > 0) {
         lct_status st = check_tensor(t, false);
@@ -416,7 +416,7 @@ lct_status lct_tensor_sample(const lct_codebook *cb, const lct_tensor *t, void *
 
 lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, void *stream,
                                 lct_codebook *out) {
-    if (!cb || !t || !out) return LCT_EINVAL;
+    if (!cb || !t || !out || !tables_ok(*cb)) return LCT_EINVAL;
     uint16_t sample[4096];
     uint32_t m = 0;
     const lct_status st = lct_tensor_sample(cb, t, stream, sample, &m);
@@ -426,7 +426,7 @@ lct_status lct_codebook_reshift(const lct_codebook *cb, const lct_tensor *t, voi
 
 lct_status lct_codebook_reshift_dense(const lct_codebook *cb, const uint16_t *d_x, uint64_t n,
                                       void *stream, lct_codebook *out) {
-    if (!cb || !out || (n > 0 && !d_x) || n > kMaxElems) return LCT_EINVAL;
+    if (!cb || !out || (n > 0 && !d_x) || n > kMaxElems || !tables_ok(*cb)) return LCT_EINVAL;
     const uint32_t m = (uint32_t)std::min<uint64_t>(n, 4096);
     uint16_t sample[4096];
     if (m > 0) {
@@ -441,7 +441,7 @@ lct_status lct_codebook_reshift_dense(const lct_codebook *cb, const uint16_t *d_
 
 lct_status lct_codebook_adapt(const lct_codebook *cb, const lct_tensor *t, double max_spill_per_elem,
                               void *stream, lct_codebook *out, int32_t *changed) {
-    if (!cb || !t || !out || !(max_spill_per_elem >= 0)) return LCT_EINVAL;
+    if (!cb || !t || !out || !(max_spill_per_elem >= 0) || !tables_ok(*cb)) return LCT_EINVAL;
     const lct_codebook in = *cb;   // out may be cb
     bool reshift = false;
     if (t->n > 0) {
@@ -469,7 +469,7 @@ lct_status lct_codebook_adapt(const lct_codebook *cb, const lct_tensor *t, doubl
 
 lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_tensor *out,
                       void *stream) {
-    if (!cb || !out) return LCT_EINVAL;
+    if (!cb || !out || !tables_ok(*cb)) return LCT_EINVAL;
     if (out->n == 0) return LCT_OK;
     lct_status st = check_tensor(out, true);
     if (st != LCT_OK) return st;
@@ -507,7 +507,7 @@ lct_status lct_encode(const lct_codebook *cb, const uint16_t *d_x, const lct_ten
 }
 
 lct_status lct_decode(const lct_codebook *cb, const lct_tensor *in, uint16_t *d_y, void *stream) {
-    if (!cb || !in) return LCT_EINVAL;
+    if (!cb || !in || !tables_ok(*cb)) return LCT_EINVAL;
     if (in->n == 0) return LCT_OK;
     lct_status st = check_tensor(in, false);
     if (st != LCT_OK) return st;
@@ -546,6 +546,7 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in, c
                                const lct_tensor *m, float eta, const lct_codebook *cw_out,
                                const lct_tensor *w_out, void *stream) {
     if (!cw || !cm || !cw_out || !w_in || !m || !w_out) return LCT_EINVAL;
+    if (!tables_ok(*cw) || !tables_ok(*cm) || !tables_ok(*cw_out)) return LCT_EINVAL;
     if (w_in->n != m->n || w_in->n != w_out->n) return LCT_EINVAL;
     if (w_in->layout.block_elems != m->layout.block_elems ||
         w_in->layout.block_elems != w_out->layout.block_elems ||
@@ -569,7 +570,7 @@ lct_status lct_sgd_step_recode(const lct_codebook *cw, const lct_tensor *w_in, c
 
 lct_status lct_sgd_step_noalloc(const lct_codebook *cw, const lct_tensor *w_in, const lct_codebook *cm,
                                 const lct_tensor *m, float eta, const lct_tensor *w_out, void *stream) {
-    if (!cw || !cm || !w_in || !m || !w_out) return LCT_EINVAL;
+    if (!cw || !cm || !w_in || !m || !w_out || !tables_ok(*cw) || !tables_ok(*cm)) return LCT_EINVAL;
     if (w_out->n == 0) return lct_sgd_step(cw, w_in, cm, m, eta, w_out, stream);
     if (!layout_ok(w_out->layout) || !sizes_ok(w_out->n, w_out->layout, w_out->ovf_cap)) return LCT_EINVAL;
     if (scr_bytes(nblocks(w_out->n, w_out->layout), w_out->ovf_cap) > kNoAllocScratch) return LCT_ESIZE;
@@ -595,6 +596,7 @@ lct_status lct_momentum_step_recode(const lct_codebook *cw, const lct_tensor *w_
                                     const lct_codebook *cw_out, const lct_codebook *cm_out,
                                     const lct_tensor *w_out, const lct_tensor *m_out, void *stream) {
     if (!cw || !cm || !cw_out || !cm_out || !w_in || !m_in || !w_out || !m_out) return LCT_EINVAL;
+    if (!tables_ok(*cw) || !tables_ok(*cm) || !tables_ok(*cw_out) || !tables_ok(*cm_out)) return LCT_EINVAL;
     const lct_tensor *all[] = {w_in, m_in, w_out, m_out};
     for (const lct_tensor *t : all)
         if (t->n != w_in->n || t->layout.block_elems != w_in->layout.block_elems ||
@@ -644,6 +646,8 @@ lct_status lct_group_bind(uint32_t count, const uint64_t *n, const lct_layout *l
                           lct_group *out) {
     if (!layout || !out || !cbs || !n || !d_table || count == 0 || !layout_ok(*layout))
         return LCT_EINVAL;
+    for (uint32_t k = 0; k < count; ++k)
+        if (!tables_ok(cbs[k])) return LCT_EINVAL;
     if (!aligned(d_table, 256)) return LCT_EALIGN;
     uint64_t nb = 0, sf = 0;
     if (!group_extent(count, n, *layout, &nb, &sf)) return LCT_EINVAL;
@@ -708,6 +712,9 @@ lct_status lct_group_fit(const lct_codebook *base, const uint64_t *n, uint16_t *
                          const lct_layout *layout, void *d_table, int32_t *d_shift, void *stream,
                          lct_group *out) {
     if (!base || !n || !d_dense || !layout || !d_table || !out || !layout_ok(*layout)) return LCT_EINVAL;
+    // the device builds the tables from the base code: its lengths must make one
+    lct_codebook check;
+    if (codebook_from_lengths(base->len_base, base->esc_len, 0, &check) != LCT_OK) return LCT_EINVAL;
     if (n[0] > 0 && !d_dense[0]) return LCT_EINVAL;
     if (!aligned(d_table, 256) || (n[0] > 0 && !aligned(d_dense[0], 16)) || (d_shift && !aligned(d_shift, 4)))
         return LCT_EALIGN;

@@ -417,6 +417,16 @@ lct_status reshift_codebook(const lct_codebook &cb, const uint16_t *sample, uint
     return st;
 }
 
+bool tables_ok(const lct_codebook &cb) {
+    if (cb.esc_len < 1 || cb.esc_len > kCap) return false;
+    for (int e = 0; e < 256; ++e) {
+        const uint32_t L = cb.enc_len[e];
+        if (L < 1 || L > kCap + kLit || (cb.enc_bits[e] >> L) != 0) return false;
+        if (((cb.dec[e] >> 8) & 0x1F) > kCap + kLit) return false;
+    }
+    return true;
+}
+
 void fill_enc(const lct_codebook &cb, EncTab *t) {
     memcpy(t->bits, cb.enc_bits, sizeof t->bits);
     memcpy(t->len, cb.enc_len, sizeof t->len);

@@ -283,6 +283,11 @@ lct_status codebook_from_lengths(const uint8_t len_base[256], uint8_t esc_len, i
 // cb's base code with the shift that minimises the sample's coded bits.
 lct_status reshift_codebook(const lct_codebook &cb, const uint16_t *sample, uint32_t m,
                             lct_codebook *out);
+// The ranges the kernels rely on hold in cb's lookup tables: an escape code
+// of 1..8 bits, every field costing 1..16 bits with no bits past its length,
+// every decode entry's length at most 16 (a codebook not made by the
+// library, e.g. one left zeroed, fails).
+bool tables_ok(const lct_codebook &cb);
 void fill_enc(const lct_codebook &cb, EncTab *t);
 void fill_enc_packed(const lct_codebook &cb, uint32_t t[256]);
 void fill_dec(const lct_codebook &cb, DecTab *t);

@@ -435,3 +435,60 @@ def test_sizes_past_the_limits_are_refused(L):
     assert L.lib.lct_group_table_bytes(2, ns, C.byref(big), C.byref(nbytes)) == L.EINVAL
     many = (C.c_uint64 * 3)(1 << 47, 1 << 47, (1 << 32) * 4096)
     assert L.lib.lct_group_table_bytes(3, many, C.byref(small), C.byref(nbytes)) == L.EINVAL
+
+
+def test_codebooks_not_made_by_the_library_are_refused(L):
+    """A zeroed codebook (never built) or one whose lookup tables were
+    altered is refused by every call that takes one, before any launch."""
+    lay = L.layout(65536, 25)
+    good = L.lct_codebook_build(L.Model(0, 0.02, 0.0), None)
+    zero = L.Codebook()
+    long_code = L.Codebook.from_buffer_copy(bytes(good))
+    long_code.enc_len[7] = 40
+    stray_bits = L.Codebook.from_buffer_copy(bytes(good))
+    e = next(i for i in range(256) if stray_bits.enc_len[i] < 16)
+    stray_bits.enc_bits[e] |= 1 << stray_bits.enc_len[e]
+    long_dec = L.Codebook.from_buffer_copy(bytes(good))
+    long_dec.dec[3] = (long_dec.dec[3] & ~0x1F00) | (20 << 8)
+    x = C.c_void_p(0x7000_0000_0000)
+    n = 100000
+    t = _fake_tensor(L, n, lay, 0x1000_0000_0000)
+    m = _fake_tensor(L, n, lay, 0x3000_0000_0000)
+    o = _fake_tensor(L, n, lay, 0x5000_0000_0000)
+    mo = _fake_tensor(L, n, lay, 0x6000_0000_0000)
+    out = L.Codebook()
+    smp = (C.c_uint16 * 4096)()
+    mm = C.c_uint32(0)
+    lib, f = L.lib, C.c_float
+    for bad in (zero, long_code, stray_bits, long_dec):
+        b = C.byref(bad)
+        g = C.byref(good)
+        assert lib.lct_encode(b, x, C.byref(o), None) == L.EINVAL
+        assert lib.lct_decode(b, C.byref(t), x, None) == L.EINVAL
+        assert lib.lct_sgd_step(b, C.byref(t), g, C.byref(m), f(1e-3), C.byref(o), None) == L.EINVAL
+        assert lib.lct_sgd_step(g, C.byref(t), b, C.byref(m), f(1e-3), C.byref(o), None) == L.EINVAL
+        assert lib.lct_sgd_step_recode(g, C.byref(t), g, C.byref(m), f(1e-3), b, C.byref(o), None) == L.EINVAL
+        assert lib.lct_sgd_step_noalloc(b, C.byref(t), g, C.byref(m), f(1e-3), C.byref(o), None) == L.EINVAL
+        assert lib.lct_momentum_step(b, C.byref(t), g, C.byref(m), x, f(0.9), f(1e-3), C.byref(o), C.byref(mo),
+                                     None) == L.EINVAL
+        assert lib.lct_tensor_sample(b, C.byref(t), None, smp, C.byref(mm)) == L.EINVAL
+        assert lib.lct_codebook_reshift(b, C.byref(t), None, C.byref(out)) == L.EINVAL
+        assert lib.lct_codebook_reshift_dense(b, x, C.c_uint64(n), None, C.byref(out)) == L.EINVAL
+        assert lib.lct_codebook_adapt(b, C.byref(t), C.c_double(0.01), None, C.byref(out), None) == L.EINVAL
+        ns = (C.c_uint64 * 2)(n, 5)
+        cbs = (L.Codebook * 2)(good, bad)
+        grp = L.Group()
+        assert lib.lct_group_bind(2, ns, C.byref(lay), cbs, None, C.c_void_p(0x7100_0000_0000),
+                                  C.byref(grp)) == L.EINVAL
+    # a base code whose lengths break the Kraft inequality, for the device fit
+    over = L.Codebook.from_buffer_copy(bytes(good))
+    for i in range(256):
+        over.len_base[i] = 1
+    grp = L.Group()
+    ns1 = (C.c_uint64 * 1)(n)
+    dense = (C.c_void_p * 1)(0x7000_0000_0000)
+    assert lib.lct_group_fit(C.byref(over), ns1, dense, C.byref(lay), C.c_void_p(0x7100_0000_0000), None, None,
+                             C.byref(grp)) == L.EINVAL
+    # n == 0 stays a no-op with a good codebook
+    t0 = _fake_tensor(L, 0, lay, 0x1000_0000_0000)
+    assert lib.lct_encode(C.byref(good), None, C.byref(t0), None) == L.OK
