@@ -30,11 +30,15 @@
  *     lct_sgd_step_noalloc() (LCT_NOALLOC_SCRATCH_BYTES).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     lct_encode, lct_decode and the update calls (lct_sgd_step*,
- *     lct_momentum_step*) only enqueue work on it and return at once;
- *     lct_codebook_build, lct_codebook_reshift and lct_codebook_adapt
- *     synchronise it.
+ *     lct_momentum_step*) only enqueue work on it and return at once, as do
+ *     the group calls and lct_group_fit; lct_codebook_build,
+ *     lct_codebook_reshift, lct_codebook_reshift_dense, lct_tensor_sample
+ *     and lct_codebook_adapt synchronise it (they read a sample back), and
+ *     lct_group_bind copies its table with a blocking copy.
  *   - Errors found on the host (null pointer, bad size, misalignment, illegal
- *     aliasing, wrong device) are returned before anything is enqueued.
+ *     aliasing, a current device that is not gfx950) are returned before
+ *     anything is enqueued.  Which device a buffer lives on is not checked:
+ *     every buffer must be on the current device.
  *     Sizes are bounded so that nothing computed from them wraps: n (of a
  *     tensor, a group member or a dense input) at most 2^48 elements, at
  *     most 2^32 - 1 blocks, ovf_cap at most 2^56 bytes; larger ones give
@@ -44,8 +48,9 @@
  *     fault.  n == 0 (for a group: no blocks) is a no-op that returns LCT_OK
  *     and writes nothing; the empty encoding is obase = [0] with status 0, so
  *     storage whose obase and status start zeroed already holds it.
- *   - Thread-safe: no global state beyond the sample array, which is guarded
- *     by a lock.
+ *   - Thread-safe: the global state is the sample array (guarded by a lock),
+ *     per-device caches of constants (guarded), and the working memory of
+ *     lct_sgd_step_noalloc, which calls overlapping on one device share.
  */
 #ifndef LCT_H
 #define LCT_H
