@@ -180,8 +180,8 @@ def lct_codebook_build(model: Model, x: torch.Tensor | None, stream=None) -> Cod
     """Codebook for model, shift sampled from x (BF16 or 16-bit tensor on the GPU)."""
     out = Codebook()
     n = 0 if x is None else x.numel()
-    if x is not None and not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    if n:
+        _bits16(x)
     st = _stream(stream) if n else None     # no sample: nothing runs on the device
     _check(lib.lct_codebook_build(C.byref(model), _ptr(x), n, st, C.byref(out)),
            "lct_codebook_build")
@@ -220,10 +220,10 @@ def lct_codebook_reshift(cb: Codebook, t: "LctTensor", stream=None) -> Codebook:
 
 def lct_codebook_reshift_dense(cb: Codebook, x: torch.Tensor, stream=None) -> Codebook:
     """cb's base code with the shift re-estimated from the dense tensor x."""
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
-    out = Codebook()
     n = x.numel()
+    if n:
+        _bits16(x)
+    out = Codebook()
     st = _stream(stream) if n else None
     _check(lib.lct_codebook_reshift_dense(C.byref(cb), _ptr(x), n, st, C.byref(out)),
            "lct_codebook_reshift_dense")
@@ -278,7 +278,20 @@ class LctTensor:
         t.sf, t.pay, t.cnt, t.obase, t.ovf, t.status, t.scratch = sf, pay, cnt, obase, ovf, status, scratch
         return t
 
-    def c(self) -> _Tensor:
+    def c(self, need_scratch: bool = True) -> _Tensor:
+        """The C descriptor.  Every buffer must be a contiguous device tensor
+        of at least the bytes lct_sizes gives (the library cannot see a
+        buffer's size; a missing one is left to the call to refuse)."""
+        sz = self.sizes
+        for name, need in (("sf", sz.sf), ("pay", sz.pay), ("cnt", sz.cnt), ("obase", sz.obase),
+                           ("ovf", self.ovf_cap), ("status", 4), ("scratch", sz.scratch if need_scratch else 0)):
+            b = getattr(self, name)
+            if b is None:
+                continue
+            if not b.is_cuda or not b.is_contiguous():
+                raise ValueError("%s must be a contiguous device tensor" % name)
+            if b.numel() * b.element_size() < need:
+                raise ValueError("%s holds %d bytes; the tensor needs %d" % (name, b.numel() * b.element_size(), need))
         return _Tensor(self.n, self.layout, _ptr(self.sf), _ptr(self.pay), _ptr(self.cnt),
                        _ptr(self.obase), _ptr(self.ovf), self.ovf_cap, _ptr(self.status),
                        _ptr(self.scratch))
@@ -327,7 +340,16 @@ def _bits16(x: torch.Tensor) -> torch.Tensor:
         raise TypeError("expected BF16 (or 16-bit pattern) tensor, got %s" % x.dtype)
     if not x.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    if not x.is_cuda:
+        raise ValueError("tensor must be on the GPU")
     return x
+
+
+def _gradient(g: torch.Tensor, n: int) -> torch.Tensor:
+    _bits16(g)
+    if g.numel() != n:
+        raise ValueError("g has %d elements, the tensors %d" % (g.numel(), n))
+    return g
 
 
 def lct_encode(cb: Codebook, x: torch.Tensor, out: LctTensor, stream=None) -> None:
@@ -357,7 +379,7 @@ def lct_sgd_step_noalloc(cw: Codebook, w_in: LctTensor, cm: Codebook, m: LctTens
                          w_out: LctTensor, stream=None) -> None:
     """lct_sgd_step with the library's static working memory (w_out's
     scratch is not used)."""
-    a, b, o = w_in.c(), m.c(), w_out.c()
+    a, b, o = w_in.c(), m.c(), w_out.c(need_scratch=False)
     _check(lib.lct_sgd_step_noalloc(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), eta, C.byref(o),
                                     _stream(stream)), "lct_sgd_step_noalloc")
 
@@ -374,6 +396,7 @@ def lct_momentum_step_recode(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: 
                              g: torch.Tensor, mu: float, eta: float, cw_out: Codebook,
                              cm_out: Codebook, w_out: LctTensor, m_out: LctTensor,
                              stream=None) -> None:
+    _gradient(g, w_in.n)
     a, b, ow, om = w_in.c(), m_in.c(), w_out.c(), m_out.c()
     _check(lib.lct_momentum_step_recode(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), _ptr(g),
                                         mu, eta, C.byref(cw_out), C.byref(cm_out), C.byref(ow),
@@ -382,6 +405,7 @@ def lct_momentum_step_recode(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: 
 
 def lct_momentum_step(cw: Codebook, w_in: LctTensor, cm: Codebook, m_in: LctTensor, g: torch.Tensor,
                       mu: float, eta: float, w_out: LctTensor, m_out: LctTensor, stream=None) -> None:
+    _gradient(g, w_in.n)
     a, b, ow, om = w_in.c(), m_in.c(), w_out.c(), m_out.c()
     _check(lib.lct_momentum_step(C.byref(cw), C.byref(a), C.byref(cm), C.byref(b), _ptr(g), mu, eta,
                                  C.byref(ow), C.byref(om), _stream(stream)), "lct_momentum_step")
@@ -441,8 +465,10 @@ class LctGroup:
         self.dense = list(dense) if dense is not None else None
         self.dense_ptrs = None
         if dense is not None:
-            for t in dense:
+            for t, nk in zip(dense, ns):
                 _bits16(t)
+                if t.numel() < int(nk):
+                    raise ValueError("a dense tensor has %d elements, its member %d" % (t.numel(), int(nk)))
             self.dense_ptrs = (C.c_void_p * count)(*[t.data_ptr() for t in dense])
         nbytes = C.c_uint64(0)
         _check(lib.lct_group_table_bytes(count, self.ns, C.byref(self.layout), C.byref(nbytes)),
