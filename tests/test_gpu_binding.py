@@ -76,3 +76,39 @@ def test_dense_inputs_are_checked(L):
     torch.cuda.synchronize()
     assert wo.status_word() == 0 and mo.status_word() == 0 and y.numel() == n
     assert np.isfinite(y.float().cpu().numpy()).all()
+
+
+def test_calls_on_a_side_stream_match_the_default_stream(L):
+    """Encode, update, momentum step and decode enqueued on a side stream
+    (default priority) give the same bytes as on the default stream: every
+    launch goes to the caller's stream and waits for nothing else."""
+    n = 5 * 65536 + 999
+    lay = L.layout(65536, 25)
+    torch.manual_seed(9400)
+    w = (torch.randn(n, device="cuda") * 0.02).to(torch.bfloat16)
+    m = (torch.randn(n, device="cuda") * 1e-3).to(torch.bfloat16)
+    g = (torch.randn(n, device="cuda") * 1e-3).to(torch.bfloat16)
+    cbw = L.lct_codebook_build(L.Model(0, 0.02, 0.0), w)
+    cbm = L.lct_codebook_build(L.Model(0, 1e-3, 0.0), m)
+
+    def run():
+        tw, tm = L.encode(cbw, w, lay), L.encode(cbm, m, lay)
+        out = L.alloc_tensor(n, lay)
+        L.lct_sgd_step(cbw, tw, cbm, tm, 1e-3, out)
+        wo, mo = L.alloc_tensor(n, lay), L.alloc_tensor(n, lay)
+        L.lct_momentum_step(cbw, out, cbm, tm, g, 0.9, 1e-3, wo, mo)
+        return out, wo, mo, L.decode(cbw, wo)
+
+    ref = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    side.synchronize()
+    for a, b in zip(ref[:3], got[:3]):
+        sz = a.sizes
+        assert torch.equal(a.sf[:sz.sf], b.sf[:sz.sf]) and torch.equal(a.pay[:sz.pay // 4], b.pay[:sz.pay // 4])
+        assert torch.equal(a.cnt[:sz.cnt // 2], b.cnt[:sz.cnt // 2]) and torch.equal(a.obase, b.obase)
+        assert a.status_word() == b.status_word() == 0
+    assert torch.equal(ref[3].view(torch.int16), got[3].view(torch.int16))
