@@ -19,6 +19,7 @@ LAYOUTS = [(65536, 25), (32768, 12), (32768, 11), (4096, 1), (8192, 3), (4096, 2
 SPECIALS = np.array([0x7FC0, 0xFFC1, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x7F7F,
                      0xFF7F, 0x0080, 0x7F81], np.uint16)
 NCASES = 200
+NLARGE = 24
 NUS = (1.0, 2.5, 3.0, 7.0, 30.0)   # Student-t degrees of freedom
 
 
@@ -80,7 +81,27 @@ def same(gp, ref, what):
 
 @pytest.mark.parametrize("idx", range(NCASES))
 def test_random_case(L, orc, idx):  # noqa: F811
-    g, B, cw, n, op = draw_case(idx)
+    run_case(L, orc, idx, *draw_case(idx))
+
+
+def draw_large_case(idx):
+    """A case of 8 to 48 blocks (ragged by up to 300 elements either way), in
+    any layout: many blocks at once in the update's full-block and general
+    kernels, with spills where the layout is small."""
+    g = np.random.default_rng(777000 + idx)
+    B, cw = LAYOUTS[int(g.integers(0, len(LAYOUTS)))]
+    n = B * int(g.integers(8, 49)) + int(g.integers(-300, 301))
+    n = max(1, min(n, 3_200_000))
+    op = ["roundtrip", "sgd", "momentum"][int(g.integers(0, 3))]
+    return g, B, cw, n, op
+
+
+@pytest.mark.parametrize("idx", range(NLARGE))
+def test_random_large_case(L, orc, idx):  # noqa: F811
+    run_case(L, orc, idx, *draw_large_case(idx))
+
+
+def run_case(L, orc, idx, g, B, cw, n, op):
     what = "case %d: %s n=%d layout=(%d,%d)" % (idx, op, n, B, cw)
     lay = L.layout(B, cw)
     w, mw = draw_values(g, n)
