@@ -49,6 +49,19 @@ from . import (CLEAN, POWERLAW, Codebook, LctGroup, LctTensor, Model, full_ovf_c
                lct_codebook_from_lengths, lct_decode, lct_encode_group, lct_layout_init, lct_sizes)
 
 
+_BASE = {}
+
+
+def _base_code(model: Model) -> Codebook:
+    """The model's base code (shift 0), built once per model: it depends on
+    the model alone, and codecs only read it."""
+    key = (int(model.family), float(model.scale), float(model.shape))
+    cb = _BASE.get(key)
+    if cb is None:
+        cb = _BASE[key] = lct_codebook_build(model, None)
+    return cb
+
+
 @dataclass
 class _Saved:
     t: LctTensor                 # the tensor (n elements) over the group storage's buffers
@@ -69,7 +82,7 @@ class ActivationCodec:
         # to the escape and, past a stream's capacity, to the overflow region;
         # the t code keeps near-Gaussian tensors at the same size.
         self.model = Model(POWERLAW, 1.0, 3.0) if model is None else model
-        self.base = lct_codebook_build(self.model, None)
+        self.base = _base_code(self.model)
         self.len_base = list(self.base.len_base)
         self.layout = lct_layout_init(mode)
         self.min_elems = int(min_elems)
