@@ -589,3 +589,34 @@ def test_updates_at_odd_sizes(L, orc, n):
                  what="n=%d inplace=%s" % (n, inplace))
         momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), 0.9, 1e-3, 65536, 25,
                       inplace, what="n=%d inplace=%s" % (n, inplace))
+
+
+@pytest.mark.parametrize("eta", [float("inf"), float("-inf"), float("nan")])
+@pytest.mark.parametrize("B,cw", [(65536, 25), (32768, 12)])
+def test_sgd_with_a_non_finite_learning_rate(L, orc, eta, B, cw):
+    """eta = +-inf or NaN: every result is an infinity or NaN (inf * 0 where
+    M is zero), each element through the rounding with the NaN check, and
+    most exponent fields spill; the bytes are the oracle's."""
+    n = 2 * B + 777
+    g = np.random.default_rng(9800)
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    m[::97] = 0
+    ref = sgd_case(L, orc, w, m, synth.Model(0, 0.02), synth.Model(0, 1e-3), eta, B, cw, False,
+                   what="eta=%g" % eta)
+    assert ref.spilled > n // 2
+
+
+def test_momentum_with_non_finite_coefficients(L, orc):
+    """mu = NaN makes M' NaN everywhere and W' NaN through it; mu = inf makes
+    M' infinite (NaN where M is zero), and then W' = fmaf(-0, M', W) is NaN;
+    eta = NaN leaves M' finite and makes W' NaN.  The bytes are the
+    oracle's."""
+    n = 65536 + 3001
+    g = np.random.default_rng(9810)
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    gr = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    for mu, eta in [(float("nan"), 1e-3), (float("inf"), 0.0), (0.9, float("nan"))]:
+        momentum_case(L, orc, w, m, gr, synth.Model(0, 0.02), synth.Model(0, 1e-3), mu, eta, 65536, 25, False,
+                      what="mu=%g eta=%g" % (mu, eta))
