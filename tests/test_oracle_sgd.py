@@ -165,3 +165,24 @@ def test_compressed_sgd_is_naive_round_trip(orc):
             r = exact_fmaf(float(np.float32(-eta)), mi, wi)
             if r != 0 and np.isfinite(r):
                 assert f32_of(int(dense[i]) << 16) == round_exact(Fraction(r), 8, -126, 127)
+
+
+def test_non_finite_learning_rate_gives_the_canonical_nan_or_infinities(orc):
+    """eta = NaN: every W' is the canonical quiet NaN 0x7FC0.  eta = +inf:
+    W' = fmaf(-inf, m, w) is -inf where m > 0, +inf where m < 0 and NaN
+    where m is zero (inf * 0); the compressed step decodes to exactly that."""
+    g = np.random.default_rng(31)
+    n = 2 * 4096 + 5
+    w = synth.to_bf16_bits(g.normal(0, 0.02, n))
+    m = synth.to_bf16_bits(g.normal(0, 1e-3, n))
+    m[::7] = 0
+    m[1::7] = 0x8000
+    cw = orc.codebook_build(0, 0.02, 0.0, w)
+    cm = orc.codebook_build(0, 1e-3, 0.0, m)
+    tw, tm = orc.encode(cw, w, 4096, 25), orc.encode(cm, m, 4096, 25)
+    y = orc.decode(cw, orc.sgd(cw, tw, cm, tm, float("nan")))
+    assert (y == 0x7FC0).all()
+    y = orc.decode(cw, orc.sgd(cw, tw, cm, tm, float("inf")))
+    mf = (m.astype(np.uint32) << 16).view(np.float32)
+    want = np.where(mf > 0, 0xFF80, np.where(mf < 0, 0x7F80, 0x7FC0)).astype(np.uint16)
+    assert np.array_equal(y, want)
